@@ -1,0 +1,82 @@
+"""The five workloads the op is checked and measured on.
+
+Shapes follow the pages' two trainers: the DiT adapter trainer (self-attention
+at a 1542-token crop with GQA, cross-attention over up to 512 encoder tokens with
+key padding), a causal GQA language-model layer, and the long-window exact walk
+of the llama.cpp pull request (a 32768-token cached K/V window walked in 512-token
+query chunks, each chunk attending causally to every earlier window position).
+
+Config ``k`` (1-based) draws its inputs with seed ``1000 + k``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+from .inputs import BF16, F32, Case, make_case
+
+
+@dataclass(frozen=True)
+class Workload:
+    key: str
+    title: str
+    index: int
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", "tiny parity case, fp32, B=1 H=2 S=64 D=64", 1),
+    "dit_sa": Workload("dit_sa", "DiT self-attention, B=1 Hq=16 Hkv=8 S=1542 D=128 bf16, pad mask", 2),
+    "dit_ca": Workload("dit_ca", "DiT cross-attention, B=2 H=16 Sq=1542 Sk=512 D=128 bf16, key-pad mask", 3),
+    "lm_causal": Workload("lm_causal", "LM causal GQA, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 4),
+    "long_window": Workload("long_window",
+                            "long-window chunked walk, W=32768, 64 chunks of 512, Hq=16 Hkv=4 D=128 bf16", 5),
+}
+
+LONG_WINDOW = 32768
+LONG_CHUNK = 512
+
+
+def seed_of(key: str) -> int:
+    return 1000 + WORKLOADS[key].index
+
+
+def make(key: str, **shrink) -> Case:
+    """Build the seeded case for a workload. Keyword overrides (e.g. ``Hq=2``) shrink
+    a workload for a fast test while keeping its structure and its seed."""
+    s = seed_of(key)
+    if key == "tiny":
+        a = dict(B=1, Hq=2, Hkv=2, Sq=64, Sk=64, D=64, dtype=F32)
+        a.update(shrink)
+        return make_case(key, seed=s, **a)
+    if key == "dit_sa":
+        a = dict(B=1, Hq=16, Hkv=8, Sq=1542, Sk=1542, D=128, dtype=BF16)
+        a.update(shrink)
+        return make_case(key, seed=s, mask="sa_pad", **a)
+    if key == "dit_ca":
+        a = dict(B=2, Hq=16, Hkv=16, Sq=1542, Sk=512, D=128, dtype=BF16)
+        lo_hi = {"lo": 128, "hi": 512, "masked_rows": 2}
+        if "Sk" in shrink:  # keep the valid lengths inside the shrunk key count, below its end
+            lo_hi["hi"] = max(1, (3 * shrink["Sk"]) // 4)
+            lo_hi["lo"] = max(1, shrink["Sk"] // 4)
+        a.update(shrink)
+        return make_case(key, seed=s, mask="ca_keypad", mask_args=lo_hi, **a)
+    if key == "lm_causal":
+        a = dict(B=1, Hq=32, Hkv=8, Sq=4096, Sk=4096, D=128, dtype=BF16, do_std=0.1)
+        a.update(shrink)
+        return make_case(key, seed=s, causal=True, q_offset=0, **a)
+    if key == "long_window":
+        W = shrink.pop("W", LONG_WINDOW)
+        a = dict(B=1, Hq=16, Hkv=4, Sq=W, Sk=W, D=128, dtype=BF16)
+        a.update(shrink)
+        return make_case(key, seed=s, causal=True, q_offset=0, **a)
+    raise KeyError(key)
+
+
+def chunk_plan(W: int = LONG_WINDOW, chunk: int = LONG_CHUNK) -> list[tuple[int, int, int]]:
+    """The exact walk's fixed plan: (row start p0, rows, keys visible) per chunk.
+
+    Chunk c covers query rows [p0, p0 + chunk) with p0 = c * chunk and sees window
+    keys [0, p0 + chunk); its causal offset is p0.
+    """
+    if W % chunk:
+        raise ValueError("window must be a whole number of chunks")
+    return [(c * chunk, chunk, (c + 1) * chunk) for c in range(W // chunk)]

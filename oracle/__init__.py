@@ -1,0 +1,146 @@
+"""CPU oracle for softmax attention with an LSE side output and its gradient.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the package's smoke check and the
+bench's ``cpu_baseline`` leg may import this module; the op never does. It is a
+plain float64 C implementation (``fa_oracle.c``) that materialises every score
+row, plus this thin ctypes wrapper. It shares no code with the HIP library.
+
+Every function takes float64 arrays in contiguous ``[B, H, S, D]`` layout and an
+optional additive mask ``[Bm, Sq, Sk]`` (``Bm`` 1 or B, ``-inf`` = masked).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fa_oracle.c")
+_LIB = os.path.join(_HERE, "libfa_oracle.so")
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math: sums keep their order)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", "-O2", "-std=c99", "-D_POSIX_C_SOURCE=200809L", "-fPIC", "-shared",
+                        "-fno-fast-math", "-ffp-contract=off", "-o", tmp, _SRC, "-lm", "-lpthread"],
+                       check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("Sq", ctypes.c_int32), ("Sk", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("mask_b", ctypes.c_int32),
+                ("q_offset", ctypes.c_int64), ("scale", ctypes.c_double)]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        _lib = ctypes.CDLL(build())
+        dp = ctypes.POINTER(ctypes.c_double)
+        ip = ctypes.POINTER(ctypes.c_int64)
+        pp = ctypes.POINTER(_Problem)
+        _lib.ora_forward.argtypes = [pp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+        _lib.ora_backward.argtypes = [pp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+        _lib.ora_rows.argtypes = [pp, dp, dp, dp, dp, dp, ctypes.c_int64, ip, dp, dp, dp, dp, ctypes.c_int]
+        _lib.ora_cols.argtypes = [pp, dp, dp, dp, dp, dp, ctypes.c_int64, ip, dp, dp, ctypes.c_int]
+        for f in (_lib.ora_forward, _lib.ora_backward, _lib.ora_rows, _lib.ora_cols):
+            f.restype = ctypes.c_int
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _problem(q, k, mask, scale, causal, q_offset):
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Sk, _ = k.shape
+    if q_offset is None:
+        q_offset = Sk - Sq if causal else 0
+    mb = 0 if mask is None else int(mask.shape[0])
+    if mask is not None and tuple(mask.shape[1:]) != (Sq, Sk):
+        raise ValueError("mask must be [Bm, Sq, Sk]")
+    return _Problem(B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), mb, int(q_offset), float(scale))
+
+
+def forward(q, k, v, mask=None, *, scale: float, causal: bool = False, q_offset: Optional[int] = None,
+            threads: Optional[int] = None):
+    """Returns (O [B,Hq,Sq,D], LSE [B,Hq,Sq]) in float64."""
+    q, k, v, mask = _f64(q), _f64(k), _f64(v), _f64(mask)
+    p = _problem(q, k, mask, scale, causal, q_offset)
+    O = np.zeros(q.shape, np.float64)
+    L = np.zeros(q.shape[:3], np.float64)
+    rc = _load().ora_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(O), _ptr(L),
+                             threads or default_threads())
+    if rc:
+        raise ValueError(f"oracle rejected the problem (code {rc})")
+    return O, L
+
+
+def backward(q, k, v, do, mask=None, *, scale: float, causal: bool = False, q_offset: Optional[int] = None,
+             threads: Optional[int] = None) -> dict:
+    """The full forward and backward. Returns a dict with O, LSE, Delta, dQ, dK, dV (float64)."""
+    q, k, v, do, mask = _f64(q), _f64(k), _f64(v), _f64(do), _f64(mask)
+    p = _problem(q, k, mask, scale, causal, q_offset)
+    out = {"O": np.zeros(q.shape), "LSE": np.zeros(q.shape[:3]), "Delta": np.zeros(q.shape[:3]),
+           "dQ": np.zeros(q.shape), "dK": np.zeros(k.shape), "dV": np.zeros(k.shape)}
+    rc = _load().ora_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(do),
+                              *(_ptr(out[n]) for n in ("O", "LSE", "Delta", "dQ", "dK", "dV")),
+                              threads or default_threads())
+    if rc:
+        raise ValueError(f"oracle rejected the problem (code {rc})")
+    return out
+
+
+def rows(q, k, v, do, row_ids, mask=None, *, scale: float, causal: bool = False,
+         q_offset: Optional[int] = None, threads: Optional[int] = None) -> dict:
+    """Selected rows, ids (b*Hq + h)*Sq + i. Returns O [n,D], LSE [n], Delta [n], dQ [n,D]."""
+    q, k, v, do, mask = _f64(q), _f64(k), _f64(v), _f64(do), _f64(mask)
+    p = _problem(q, k, mask, scale, causal, q_offset)
+    ids = np.ascontiguousarray(row_ids, dtype=np.int64)
+    n, D = ids.size, q.shape[3]
+    out = {"O": np.zeros((n, D)), "LSE": np.zeros(n), "Delta": np.zeros(n), "dQ": np.zeros((n, D))}
+    rc = _load().ora_rows(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(do), n,
+                          ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                          *(_ptr(out[x]) for x in ("O", "LSE", "Delta", "dQ")), threads or default_threads())
+    if rc:
+        raise ValueError(f"oracle rejected the problem (code {rc})")
+    return out
+
+
+def cols(q, k, v, do, col_ids, mask=None, *, scale: float, causal: bool = False,
+         q_offset: Optional[int] = None, threads: Optional[int] = None) -> dict:
+    """Selected key columns, ids (b*Hkv + g)*Sk + j. Returns dK [n,D], dV [n,D]."""
+    q, k, v, do, mask = _f64(q), _f64(k), _f64(v), _f64(do), _f64(mask)
+    p = _problem(q, k, mask, scale, causal, q_offset)
+    ids = np.ascontiguousarray(col_ids, dtype=np.int64)
+    n, D = ids.size, q.shape[3]
+    out = {"dK": np.zeros((n, D)), "dV": np.zeros((n, D))}
+    rc = _load().ora_cols(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(do), n,
+                          ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                          _ptr(out["dK"]), _ptr(out["dV"]), threads or default_threads())
+    if rc:
+        raise ValueError(f"oracle rejected the problem (code {rc})")
+    return out

@@ -1,0 +1,75 @@
+"""Host-side checks of the input generators, mask builders, the chunk plan and the
+work accounting (no GPU)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from flash_attention_train_amd import accounting as A
+from flash_attention_train_amd import configs
+from flash_attention_train_amd.inputs import bf16_bits_to_f32, f32_to_bf16_bits, make_case
+
+
+def test_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10.0 ** rng.integers(-6, 6, 100000),
+                        np.array([0.0, -0.0, 1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 65504.0], np.float32)])
+    mine = f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)
+    back = bf16_bits_to_f32(mine)
+    assert np.array_equal(back, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_generators_are_deterministic_and_seeded():
+    a = configs.make("dit_ca", B=2, Hq=2, Hkv=2, Sq=33, Sk=20, D=8)
+    b = configs.make("dit_ca", B=2, Hq=2, Hkv=2, Sq=33, Sk=20, D=8)
+    for n in ("q", "k", "v", "do", "mask"):
+        assert np.array_equal(getattr(a, n), getattr(b, n))
+    c = make_case("x", B=1, Hq=1, Hkv=1, Sq=4, Sk=4, D=8, dtype="bf16", seed=1)
+    d = make_case("x", B=1, Hq=1, Hkv=1, Sq=4, Sk=4, D=8, dtype="bf16", seed=2)
+    assert not np.array_equal(c.q, d.q)
+
+
+def test_full_size_masks_follow_the_workload_description():
+    sa = configs.make("dit_sa", Hq=2, Hkv=1, D=8)
+    assert sa.mask.shape == (1, 1542, 1542) and sa.meta["valid_len"] == 1388
+    fin = np.isfinite(sa.mask[0])
+    assert fin[:1388, :1388].all() and not fin[:1388, 1388:].any() and fin[1388:].all()
+    ca = configs.make("dit_ca", Hq=2, Hkv=2, D=8)
+    assert ca.mask.shape == (2, 1542, 512)
+    for b, (L, rows) in enumerate(zip(ca.meta["valid_lens"], ca.meta["masked_rows"])):
+        assert 128 <= L <= 512 and len(rows) == 2
+        fin = np.isfinite(ca.mask[b])
+        assert not fin[rows].any()
+        keep = np.setdiff1d(np.arange(1542), rows)
+        assert fin[keep, :L].all() and not fin[:, L:].any()
+
+
+def test_pair_counts_match_brute_force():
+    for causal, q_offset in ((False, 0), (True, 0), (True, 5)):
+        c = make_case("x", B=2, Hq=3, Hkv=1, Sq=9, Sk=14, D=4, dtype="f32", seed=7, mask="random",
+                      mask_args={"Bm": 2}, causal=causal, q_offset=q_offset)
+        n = 0
+        for b in range(c.B):
+            for i in range(c.Sq):
+                for j in range(c.Sk):
+                    if np.isfinite(c.mask[b, i, j]) and (not causal or j <= q_offset + i):
+                        n += 1
+        assert A.case_pairs(c) == n * c.Hq
+
+
+def test_headline_pair_counts():
+    assert A.unmasked_pairs(1, 16, 1542, 1542, False, 0, configs.make("dit_sa", Hq=1, Hkv=1, D=8).mask) == 34_624_192
+    assert A.unmasked_pairs(1, 32, 4096, 4096, True, 0, None) == 268_500_992
+    assert A.chunked_pairs(16, 32768, 512) == 8_590_196_736
+    assert A.unmasked_pairs(1, 16, 32768, 32768, True, 0, None) == 8_590_196_736
+
+
+def test_chunk_plan():
+    plan = configs.chunk_plan()
+    assert len(plan) == 64
+    assert plan[0] == (0, 512, 512) and plan[-1] == (32256, 512, 32768)
+    with pytest.raises(ValueError):
+        configs.chunk_plan(1000, 512)

@@ -1,0 +1,329 @@
+"""Pins of the CPU oracle to things other than itself (no GPU involved).
+
+Each check is chosen so that a plausible slip in the oracle -- a dropped scale, a
+wrong sign, a transposed operand, a wrong GQA head index, a mishandled mask --
+fails at least one of them:
+
+* a hand-worked example whose every value was derived on paper (golden file);
+* central finite differences, in float64, of L = <O, dO> with respect to Q, K, V;
+* PyTorch CPU float64 autograd through an explicitly materialised softmax;
+* closed forms (one key, uniform scores, first causal row) and invariants;
+* exact zeros for fully masked rows and fully masked key columns;
+* GQA equal to the group sum over the head-expanded problem;
+* the chunked walk equal to the one-shot problem.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from flash_attention_train_amd import configs
+from flash_attention_train_amd.inputs import make_case
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _problem(seed, B=1, Hq=2, Hkv=1, Sq=6, Sk=7, D=4, mask="none", causal=False, q_offset=None,
+             mask_args=None, scale=None):
+    c = make_case("pin", B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, Sk=Sk, D=D, dtype="f32", seed=seed, mask=mask,
+                  causal=causal, q_offset=q_offset, mask_args=mask_args, scale=scale)
+    return c
+
+
+def _arrays(c):
+    return c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), (None if c.mask is None else c.mask.astype(np.float64))
+
+
+def _full(c):
+    q, k, v, do, m = _arrays(c)
+    return oracle.backward(q, k, v, do, m, scale=c.scale, causal=c.causal, q_offset=c.q_offset)
+
+
+def _fully_masked_rows(c):
+    """Boolean [B, Sq]: rows with no visible key (mask and causal)."""
+    vis = np.ones((c.B, c.Sq, c.Sk), bool)
+    if c.mask is not None:
+        vis &= np.isfinite(c.mask) if c.mask.shape[0] == c.B else np.isfinite(c.mask[[0] * c.B])
+    if c.causal:
+        vis &= np.arange(c.Sk)[None, None, :] <= (c.q_offset + np.arange(c.Sq))[None, :, None]
+    return ~vis.any(axis=2), vis
+
+
+# ---------------------------------------------------------------------------
+# golden: a worked example derived by hand
+# ---------------------------------------------------------------------------
+def test_golden_worked_example():
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        g = json.load(f)
+
+    def arr(x):
+        return np.array([[(-np.inf if e == "-inf" else e) for e in row] for row in x], dtype=np.float64)
+
+    q = arr(g["q"])[None, None]
+    k = arr(g["k"])[None, None]
+    v = arr(g["v"])[None, None]
+    do = arr(g["do"])[None, None]
+    m = arr(g["mask"])[None]
+    r = oracle.backward(q, k, v, do, m, scale=g["scale"])
+    for name, want in g["expect"].items():
+        got = r[name][0, 0]
+        np.testing.assert_allclose(got, np.array(want), rtol=1e-14, atol=1e-14, err_msg=name)
+    # the fully masked row and column are exactly zero, not merely small
+    assert np.all(r["O"][0, 0, 2] == 0) and r["LSE"][0, 0, 2] == 0 and np.all(r["dQ"][0, 0, 2] == 0)
+    assert np.all(r["dK"][0, 0, 3] == 0) and np.all(r["dV"][0, 0, 3] == 0)
+
+
+# ---------------------------------------------------------------------------
+# finite differences of L = <O, dO>
+# ---------------------------------------------------------------------------
+FD_CASES = {
+    "plain": dict(seed=11),
+    "gqa2_sa_pad": dict(seed=12, Hq=4, Hkv=2, Sq=8, Sk=8, mask="sa_pad", mask_args={"pad_frac": 0.25}),
+    "ca_keypad_rows": dict(seed=13, B=2, Hq=2, Hkv=2, Sq=7, Sk=6, mask="ca_keypad",
+                           mask_args={"lo": 2, "hi": 6, "masked_rows": 1}),
+    "causal_offset": dict(seed=14, Hq=2, Hkv=1, Sq=5, Sk=9, causal=True, q_offset=3),
+    "gqa4_random_bias": dict(seed=15, Hq=4, Hkv=1, Sq=6, Sk=7, mask="random",
+                             mask_args={"Bm": 1, "p_masked": 0.25, "full_rows": 1, "full_cols": 1}),
+    "causal_gqa_batch": dict(seed=16, B=2, Hq=4, Hkv=2, Sq=6, Sk=6, causal=True, q_offset=0),
+}
+
+
+@pytest.mark.parametrize("name", list(FD_CASES))
+def test_finite_differences(name):
+    c = _problem(**FD_CASES[name])
+    q, k, v, do, m = _arrays(c)
+    r = oracle.backward(q, k, v, do, m, scale=c.scale, causal=c.causal, q_offset=c.q_offset)
+    assert np.abs(r["dQ"]).max() > 0 and np.abs(r["dK"]).max() > 0 and np.abs(r["dV"]).max() > 0
+
+    def loss(a):
+        O, _ = oracle.forward(a["q"], a["k"], a["v"], m, scale=c.scale, causal=c.causal,
+                              q_offset=c.q_offset, threads=1)
+        return float(np.sum(O * do))
+
+    h = 1e-6
+    for name_t, t, grad in (("q", q, r["dQ"]), ("k", k, r["dK"]), ("v", v, r["dV"])):
+        fd = np.zeros_like(t)
+        for idx in np.ndindex(t.shape):
+            tp = t.copy()
+            tp[idx] += h
+            tm = t.copy()
+            tm[idx] -= h
+            fd[idx] = (loss({"q": q, "k": k, "v": v, name_t: tp})
+                       - loss({"q": q, "k": k, "v": v, name_t: tm})) / (2 * h)
+        err = np.abs(fd - grad).max() / max(np.abs(grad).max(), 1e-30)
+        assert err < 1e-7, (name, name_t, err)
+
+
+# ---------------------------------------------------------------------------
+# an independent library routine: torch CPU float64 autograd, materialised softmax
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(FD_CASES))
+def test_torch_autograd_crosscheck(name):
+    torch = pytest.importorskip("torch")
+    c = _problem(**FD_CASES[name])
+    q, k, v, do, m = _arrays(c)
+    r = oracle.backward(q, k, v, do, m, scale=c.scale, causal=c.causal, q_offset=c.q_offset)
+    full, vis = _fully_masked_rows(c)
+    G = c.Hq // c.Hkv
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    tv = torch.tensor(v, requires_grad=True)
+    ke = tk.repeat_interleave(G, dim=1)
+    ve = tv.repeat_interleave(G, dim=1)
+    bias = torch.zeros((c.B, 1, c.Sq, c.Sk), dtype=torch.float64)
+    if m is not None:
+        bias = bias + torch.tensor(m)[:, None] if m.shape[0] == c.B else bias + torch.tensor(m)[None]
+    bias = bias.masked_fill(~torch.tensor(vis)[:, None], float("-inf"))
+    # keep fully masked rows finite for the library (it would give NaN there); they are
+    # excluded from the comparison and from the loss below
+    bias = bias.masked_fill(torch.tensor(full)[:, None, :, None], 0.0)
+    s = torch.matmul(tq, ke.transpose(-1, -2).contiguous()) * c.scale + bias
+    p = torch.softmax(s, dim=-1)
+    o = torch.matmul(p, ve)
+    lse = torch.logsumexp(s, dim=-1)
+    keep = torch.tensor(~full)[:, None, :, None].to(torch.float64)
+    (o * torch.tensor(do) * keep).sum().backward()
+    keep_np = ~full[:, None, :]
+    np.testing.assert_allclose(r["O"][np.broadcast_to(keep_np, r["LSE"].shape)],
+                               o.detach().numpy()[np.broadcast_to(keep_np, r["LSE"].shape)], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["LSE"][np.broadcast_to(keep_np, r["LSE"].shape)],
+                               lse.detach().numpy()[np.broadcast_to(keep_np, r["LSE"].shape)], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["dQ"], tq.grad.numpy(), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(r["dK"], tk.grad.numpy(), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(r["dV"], tv.grad.numpy(), rtol=1e-11, atol=1e-11)
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+def test_single_key_closed_form():
+    c = _problem(21, Hq=2, Hkv=1, Sq=5, Sk=1, D=4)
+    q, k, v, do, _ = _arrays(c)
+    r = oracle.backward(q, k, v, do, scale=c.scale)
+    np.testing.assert_allclose(r["O"], np.broadcast_to(v.repeat(2, axis=1), r["O"].shape), rtol=0, atol=1e-15)
+    lse = c.scale * np.einsum("bhid,bjd->bhi", q, k[:, 0])
+    np.testing.assert_allclose(r["LSE"], lse, rtol=1e-14, atol=1e-14)
+    assert np.abs(r["dQ"]).max() < 1e-14 and np.abs(r["dK"]).max() < 1e-14
+    np.testing.assert_allclose(r["dV"][0, 0, 0], do[0].sum(axis=(0, 1)), rtol=1e-13, atol=1e-13)
+
+
+def test_uniform_scores_closed_form():
+    c = _problem(22, B=2, Hq=2, Hkv=2, Sq=4, Sk=9, D=3, mask="ca_keypad",
+                 mask_args={"lo": 3, "hi": 8, "masked_rows": 1})
+    q, k, v, do, m = _arrays(c)
+    q = np.zeros_like(q)
+    O, L = oracle.forward(q, k, v, m, scale=c.scale)
+    full, vis = _fully_masked_rows(c)
+    for b in range(c.B):
+        for h in range(c.Hq):
+            for i in range(c.Sq):
+                if full[b, i]:
+                    assert np.all(O[b, h, i] == 0) and L[b, h, i] == 0
+                    continue
+                js = np.nonzero(vis[b, i])[0]
+                np.testing.assert_allclose(O[b, h, i], v[b, h][js].mean(axis=0), rtol=1e-14, atol=1e-14)
+                assert abs(L[b, h, i] - math.log(len(js))) < 1e-14
+
+
+def test_first_causal_row_closed_form():
+    c = _problem(23, Hq=2, Hkv=2, Sq=6, Sk=6, D=5, causal=True, q_offset=0)
+    q, k, v, _, _ = _arrays(c)
+    O, L = oracle.forward(q, k, v, scale=c.scale, causal=True, q_offset=0)
+    for h in range(2):
+        np.testing.assert_allclose(O[0, h, 0], v[0, h, 0], rtol=0, atol=1e-15)
+        assert abs(L[0, h, 0] - c.scale * float(q[0, h, 0] @ k[0, h, 0])) < 1e-14
+
+
+def test_rows_sum_to_one_via_constant_values():
+    c = _problem(24, B=2, Hq=4, Hkv=2, Sq=7, Sk=8, mask="random", mask_args={"Bm": 2})
+    q, k, v, _, m = _arrays(c)
+    O, _ = oracle.forward(q, k, np.ones_like(v), m, scale=c.scale)
+    full, _ = _fully_masked_rows(c)
+    for b in range(c.B):
+        for i in range(c.Sq):
+            want = 0.0 if full[b, i] else 1.0
+            assert np.abs(O[b, :, i] - want).max() < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+def test_gradient_sum_invariants():
+    c = _problem(31, B=2, Hq=4, Hkv=2, Sq=9, Sk=11, mask="random", mask_args={"Bm": 2, "full_rows": 2})
+    r = _full(c)
+    full, _ = _fully_masked_rows(c)
+    do = c.f64("do")
+    assert np.abs(r["dK"].sum(axis=2)).max() < 1e-13 * max(1.0, np.abs(r["dK"]).max())
+    G = c.Hq // c.Hkv
+    for b in range(c.B):
+        for g in range(c.Hkv):
+            want = sum(do[b, h][~full[b]].sum(axis=0) for h in range(g * G, (g + 1) * G))
+            np.testing.assert_allclose(r["dV"][b, g].sum(axis=0), want, rtol=1e-12, atol=1e-12)
+    # Delta equals sum_j P_ij dP_ij, i.e. <dO_i, O_i>
+    np.testing.assert_allclose(r["Delta"], np.einsum("bhid,bhid->bhi", do, r["O"]), rtol=1e-13, atol=1e-13)
+
+
+def test_mask_row_shift_and_key_permutation_and_linearity():
+    c = _problem(32, B=1, Hq=2, Hkv=1, Sq=5, Sk=8, mask="random", mask_args={"Bm": 1, "full_rows": 0})
+    q, k, v, do, m = _arrays(c)
+    base = oracle.backward(q, k, v, do, m, scale=c.scale)
+    # a constant added to one row's unmasked mask entries shifts that row's LSE only
+    m2 = m.copy()
+    m2[0, 2][np.isfinite(m2[0, 2])] += 3.25
+    O2, L2 = oracle.forward(q, k, v, m2, scale=c.scale)
+    np.testing.assert_allclose(O2, base["O"], rtol=1e-13, atol=1e-13)
+    dl = L2 - base["LSE"]
+    assert np.abs(dl[0, :, 2] - 3.25).max() < 1e-12 and np.abs(np.delete(dl, 2, axis=2)).max() < 1e-13
+    # permuting keys permutes dK/dV and leaves O/LSE/dQ alone
+    perm = np.random.default_rng(0).permutation(c.Sk)
+    r = oracle.backward(q, k[:, :, perm], v[:, :, perm], do, m[:, :, perm], scale=c.scale)
+    for n in ("O", "LSE", "dQ"):
+        np.testing.assert_allclose(r[n], base[n], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["dK"], base["dK"][:, :, perm], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["dV"], base["dV"][:, :, perm], rtol=1e-12, atol=1e-12)
+    # O is linear in V
+    O3, _ = oracle.forward(q, k, 2.0 * v + 1.5 * np.flip(v, axis=3), m, scale=c.scale)
+    O4, _ = oracle.forward(q, k, np.flip(v, axis=3), m, scale=c.scale)
+    np.testing.assert_allclose(O3, 2.0 * base["O"] + 1.5 * O4, rtol=1e-12, atol=1e-12)
+
+
+def test_exact_zeros_fully_masked_rows_and_columns():
+    c = configs.make("dit_ca", B=2, Hq=2, Hkv=2, Sq=40, Sk=24, D=8)
+    r = _full(c)
+    full, vis = _fully_masked_rows(c)
+    assert full.any() and (~vis.any(axis=1)).any()
+    for b in range(c.B):
+        rows = np.nonzero(full[b])[0]
+        assert np.all(r["O"][b][:, rows] == 0) and np.all(r["LSE"][b][:, rows] == 0)
+        assert np.all(r["dQ"][b][:, rows] == 0)
+        cols = np.nonzero(~vis[b].any(axis=0))[0]
+        assert cols.size > 0
+        assert np.all(r["dK"][b][:, cols] == 0) and np.all(r["dV"][b][:, cols] == 0)
+    assert np.abs(r["dK"]).max() > 0 and np.abs(r["dV"]).max() > 0
+
+
+def test_sa_pad_mask_has_no_fully_masked_key_column():
+    c = configs.make("dit_sa", Hq=2, Hkv=1, Sq=50, Sk=50, D=8)
+    _, vis = _fully_masked_rows(c)
+    assert vis.any(axis=1).all()
+    assert c.meta["valid_len"] == 45
+
+
+# ---------------------------------------------------------------------------
+# GQA and the chunked walk
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("G", [2, 4])
+def test_gqa_equals_group_sum_of_expanded_heads(G):
+    c = _problem(41 + G, B=2, Hq=2 * G, Hkv=2, Sq=6, Sk=9, mask="random", mask_args={"Bm": 1})
+    q, k, v, do, m = _arrays(c)
+    r = oracle.backward(q, k, v, do, m, scale=c.scale)
+    ke, ve = k.repeat(G, axis=1), v.repeat(G, axis=1)
+    e = oracle.backward(q, ke, ve, do, m, scale=c.scale)
+    for n in ("O", "LSE", "dQ"):
+        np.testing.assert_allclose(r[n], e[n], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(r["dK"], e["dK"].reshape(2, 2, G, 9, -1).sum(axis=2), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(r["dV"], e["dV"].reshape(2, 2, G, 9, -1).sum(axis=2), rtol=1e-12, atol=1e-13)
+
+
+def test_chunked_walk_equals_one_shot():
+    W, C = 96, 16
+    c = configs.make("long_window", W=W, Hq=4, Hkv=2, D=8)
+    q, k, v, do, _ = _arrays(c)
+    one = oracle.backward(q, k, v, do, scale=c.scale, causal=True, q_offset=0)
+    dk = np.zeros_like(one["dK"])
+    dv = np.zeros_like(one["dV"])
+    for p0, n, sk in configs.chunk_plan(W, C):
+        r = oracle.backward(q[:, :, p0:p0 + n], k[:, :, :sk], v[:, :, :sk], do[:, :, p0:p0 + n],
+                            scale=c.scale, causal=True, q_offset=p0)
+        for name in ("O", "LSE", "Delta", "dQ"):
+            np.testing.assert_allclose(r[name], one[name][:, :, p0:p0 + n], rtol=1e-12, atol=1e-13)
+        dk[:, :, :sk] += r["dK"]
+        dv[:, :, :sk] += r["dV"]
+    scale_k = np.abs(one["dK"]).max()
+    assert np.abs(dk - one["dK"]).max() <= 1e-12 * scale_k
+    assert np.abs(dv - one["dV"]).max() <= 1e-12 * np.abs(one["dV"]).max()
+
+
+# ---------------------------------------------------------------------------
+# the sampled entry points agree with the whole-problem entry point
+# ---------------------------------------------------------------------------
+def test_sampled_rows_and_columns_match_full():
+    c = _problem(51, B=2, Hq=4, Hkv=2, Sq=10, Sk=12, mask="random", mask_args={"Bm": 2}, causal=True, q_offset=2)
+    q, k, v, do, m = _arrays(c)
+    full = oracle.backward(q, k, v, do, m, scale=c.scale, causal=True, q_offset=2)
+    rng = np.random.default_rng(3)
+    rows = rng.choice(c.B * c.Hq * c.Sq, 17, replace=False)
+    rr = oracle.rows(q, k, v, do, rows, m, scale=c.scale, causal=True, q_offset=2)
+    for n in ("O", "dQ"):
+        np.testing.assert_allclose(rr[n], full[n].reshape(-1, c.D)[rows], rtol=1e-14, atol=1e-14)
+    for n in ("LSE", "Delta"):
+        np.testing.assert_allclose(rr[n], full[n].reshape(-1)[rows], rtol=1e-14, atol=1e-14)
+    cols = rng.choice(c.B * c.Hkv * c.Sk, 13, replace=False)
+    cc = oracle.cols(q, k, v, do, cols, m, scale=c.scale, causal=True, q_offset=2)
+    np.testing.assert_allclose(cc["dK"], full["dK"].reshape(-1, c.D)[cols], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(cc["dV"], full["dV"].reshape(-1, c.D)[cols], rtol=1e-13, atol=1e-14)
