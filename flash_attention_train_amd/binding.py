@@ -1,0 +1,217 @@
+"""Python binding over the C ABI in ``include/fa_train.h`` (argument marshalling only).
+
+PyTorch provides device memory and the stream; every step of the op runs in the
+HIP kernels of ``libfa_train.so``. There is no CPU or PyTorch fallback: if the
+library is missing or a call fails, an exception says so.
+
+Tensors are ``[B, H, S, D]`` views with the last dimension contiguous (any batch,
+head and sequence strides that are multiples of 16 bytes). LSE and Delta are
+fp32 ``[B, Hq, S]`` with a contiguous last dimension.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa_train.so")
+
+FA_F32, FA_BF16 = 0, 1
+
+
+class FaView(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+                ("stride_s", ctypes.c_int64)]
+
+
+class FaAttnParams(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("Sq", ctypes.c_int32),
+                ("Sk", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("q_offset", ctypes.c_int64), ("scale", ctypes.c_float), ("mask", ctypes.c_void_p),
+                ("mask_stride_b", ctypes.c_int64), ("mask_stride_q", ctypes.c_int64)]
+
+
+class FaError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn} failed with status {status}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+# exported symbol -> (argtypes, restype)
+_VP = ctypes.c_void_p
+_PV = ctypes.POINTER(FaView)
+_PP = ctypes.POINTER(FaAttnParams)
+SIGNATURES = {
+    "fa_train_fwd": ([_PP, _PV, _PV, _PV, _PV, _PV, _VP], ctypes.c_int),
+    "fa_train_bwd_preprocess": ([_PP, _PV, _PV, _PV, _VP], ctypes.c_int),
+    "fa_train_bwd_workspace_bytes": ([_PP], ctypes.c_size_t),
+    "fa_train_bwd": ([_PP, _PV, _PV, _PV, _PV, _PV, _PV, _PV, _PV, _PV, _VP, ctypes.c_size_t, _VP], ctypes.c_int),
+    "fa_train_bwd_chunked": ([_PP, _PV, _PV, _PV, _PV, _PV, _PV, _PV, _PV, _PV, _VP, ctypes.c_size_t, _VP],
+                             ctypes.c_int),
+    "fa_train_status_str": ([ctypes.c_int], ctypes.c_char_p),
+    "fa_train_last_error": ([], ctypes.c_char_p),
+    "fa_train_version": ([], ctypes.c_int),
+    "fa_train_probe_mfma": ([ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP], ctypes.c_int),
+    "fa_train_probe_ds_read_tr16": ([ctypes.c_int32, _VP, _VP, _VP], ctypes.c_int),
+}
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def lib():
+    """Load libfa_train.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m flash_attention_train_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (argt, rest) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.argtypes = argt
+            f.restype = rest
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise FaError(fn, status, lib().fa_train_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def view4(t: torch.Tensor) -> FaView:
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [B, H, S, D] tensor with a contiguous last dimension")
+    return FaView(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def view3(t: torch.Tensor) -> FaView:
+    if t.dim() != 3 or t.dtype != torch.float32:
+        raise ValueError("expected an fp32 [B, H, S] tensor")
+    return FaView(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream_handle(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], causal: bool,
+                q_offset: Optional[int], mask: Optional[torch.Tensor]) -> FaAttnParams:
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Sk, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise ValueError("q and k disagree on B or D")
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    if q_offset is None:
+        q_offset = Sk - Sq if causal else 0
+    p = FaAttnParams(B, Hq, Hkv, Sq, Sk, D, _dtype_code(q), int(bool(causal)), int(q_offset), float(scale),
+                     None, 0, 0)
+    if mask is not None:
+        if mask.dtype != torch.float32 or mask.dim() != 3 or mask.stride(2) != 1:
+            raise ValueError("mask must be an fp32 [Bm, Sq, Sk] tensor with a contiguous last dimension")
+        if mask.shape[1] != Sq or mask.shape[2] != Sk or mask.shape[0] not in (1, B):
+            raise ValueError("mask must be [1 or B, Sq, Sk]")
+        p.mask = mask.data_ptr()
+        p.mask_stride_b = 0 if mask.shape[0] == 1 else mask.stride(0)
+        p.mask_stride_q = mask.stride(1)
+    return p
+
+
+def fwd(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, out=None, lse=None, stream=None):
+    """Forward: returns (O, LSE). O has q's dtype and shape; LSE is fp32 [B, Hq, Sq]."""
+    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _check("fa_train_fwd", lib().fa_train_fwd(ctypes.byref(p), view4(q), view4(k), view4(v), view4(out), view3(lse),
+                                              _stream_handle(stream)))
+    return out, lse
+
+
+def bwd_preprocess(o, dout, *, delta=None, stream=None):
+    """Delta = rowsum(dO * O) in fp32, [B, Hq, Sq]."""
+    B, Hq, Sq, D = o.shape
+    if delta is None:
+        delta = torch.empty((B, Hq, Sq), dtype=torch.float32, device=o.device)
+    p = FaAttnParams(B, Hq, Hq, Sq, Sq, D, _dtype_code(o), 0, 0, 1.0, None, 0, 0)
+    _check("fa_train_bwd_preprocess",
+           lib().fa_train_bwd_preprocess(ctypes.byref(p), view4(o), view4(dout), view3(delta), _stream_handle(stream)))
+    return delta
+
+
+def bwd_workspace_bytes(q, k, *, scale=None, causal=False, q_offset=None, mask=None) -> int:
+    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask)
+    return int(lib().fa_train_bwd_workspace_bytes(ctypes.byref(p)))
+
+
+def _workspace(p: FaAttnParams, device, workspace):
+    need = int(lib().fa_train_bwd_workspace_bytes(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_offset=None, dq=None, dk=None,
+        dv=None, workspace=None, stream=None):
+    """Backward: returns (dQ, dK, dV), each in q's dtype, overwritten."""
+    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask)
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    ws, nbytes = _workspace(p, q.device, workspace)
+    _check("fa_train_bwd", lib().fa_train_bwd(ctypes.byref(p), view4(q), view4(k), view4(v), view4(dout), view3(lse),
+                                              view3(delta), view4(dq), view4(dk), view4(dv), ws.data_ptr(), nbytes,
+                                              _stream_handle(stream)))
+    return dq, dk, dv
+
+
+def bwd_chunked(q, k, v, dout, lse, delta, dk_acc, dv_acc, *, mask=None, scale=None, causal=True, q_offset=None,
+                dq=None, workspace=None, stream=None):
+    """Chunked backward: returns dQ for the chunk; ADDS dK/dV into the fp32 window
+    accumulators ``dk_acc`` / ``dv_acc`` ([B, Hkv, >= Sk, D])."""
+    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask)
+    if dk_acc.dtype != torch.float32 or dv_acc.dtype != torch.float32:
+        raise TypeError("the window accumulators must be float32")
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    ws, nbytes = _workspace(p, q.device, workspace)
+    _check("fa_train_bwd_chunked",
+           lib().fa_train_bwd_chunked(ctypes.byref(p), view4(q), view4(k), view4(v), view4(dout), view3(lse),
+                                      view3(delta), view4(dq), view4(dk_acc), view4(dv_acc), ws.data_ptr(), nbytes,
+                                      _stream_handle(stream)))
+    return dq
+
+
+def probe_mfma(kind: int, a: torch.Tensor, b: torch.Tensor) -> torch.Tensor:
+    """Run the matrix-core layout probe; a, b: fp32 [waves, 64, k]; returns [waves, 64, regs]."""
+    waves = a.shape[0]
+    regs = 16 if kind in (0, 2) else 4
+    c = torch.empty((waves, 64, regs), dtype=torch.float32, device=a.device)
+    _check("fa_train_probe_mfma", lib().fa_train_probe_mfma(kind, waves, a.data_ptr(), b.data_ptr(), c.data_ptr(),
+                                                            _stream_handle(None)))
+    return c
+
+
+def probe_ds_read_tr16(byte_addr: torch.Tensor) -> torch.Tensor:
+    """Run the LDS transpose-read probe; byte_addr: int32 [waves, 64]; returns int32 [waves, 64, 4]."""
+    waves = byte_addr.shape[0]
+    out = torch.empty((waves, 64, 4), dtype=torch.int16, device=byte_addr.device)
+    _check("fa_train_probe_ds_read_tr16", lib().fa_train_probe_ds_read_tr16(waves, byte_addr.data_ptr(),
+                                                                            out.data_ptr(), _stream_handle(None)))
+    return out.to(torch.int32) & 0xFFFF

@@ -1,0 +1,333 @@
+// fa_api.hip -- the C ABI declared in include/fa_train.h: host-side argument
+// checks, then kernel launches on the caller's stream. Nothing here allocates,
+// synchronizes or reads device memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "fa_kernels.h"
+#include "fa_train.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fa_status fail(fa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+struct Extent {
+  uintptr_t lo, hi;  // byte range [lo, hi)
+};
+
+bool overlaps(const Extent& x, const Extent& y) { return x.lo < y.hi && y.lo < x.hi; }
+
+// Checks one strided view of [B, H, S, W] elements of `elt` bytes (W contiguous).
+// `align16` demands 16-byte aligned data and row strides; `out` demands that no two
+// (b, h, s) rows overlap. Fills the byte extent for the alias checks.
+fa_status check_view(const fa_view* v, const char* name, int64_t B, int64_t H, int64_t S, int64_t W, int elt,
+                     bool align16, bool out, Extent* ext) {
+  if (!v || !v->data) return fail(FA_ERR_NULL, "%s: view or data pointer is NULL", name);
+  if (v->stride_b < 0 || v->stride_h < 0 || v->stride_s < 0)
+    return fail(FA_ERR_STRIDE, "%s: negative stride", name);
+  const uintptr_t base = reinterpret_cast<uintptr_t>(v->data);
+  if (align16) {
+    if (base % 16) return fail(FA_ERR_ALIGN, "%s: data pointer is not 16-byte aligned", name);
+    if ((v->stride_b * elt) % 16 || (v->stride_h * elt) % 16 || (v->stride_s * elt) % 16)
+      return fail(FA_ERR_ALIGN, "%s: strides must be multiples of 16 bytes", name);
+  } else if (base % elt) {
+    return fail(FA_ERR_ALIGN, "%s: data pointer is not %d-byte aligned", name, elt);
+  }
+  if (out) {
+    // classic non-overlap test: sort the dims by stride, each stride must clear
+    // the extent of the dims below it
+    struct Dim {
+      int64_t stride, n;
+    } d[3] = {{v->stride_b, B}, {v->stride_h, H}, {v->stride_s, S}};
+    std::sort(d, d + 3, [](const Dim& x, const Dim& y) { return x.stride < y.stride; });
+    int64_t extent = W;
+    for (int i = 0; i < 3; ++i) {
+      if (d[i].n <= 1) continue;
+      if (d[i].stride < extent) return fail(FA_ERR_STRIDE, "%s: output rows overlap", name);
+      extent = d[i].stride * (d[i].n - 1) + extent;
+    }
+  }
+  const int64_t last = (B - 1) * v->stride_b + (H - 1) * v->stride_h + (S - 1) * v->stride_s + W;
+  ext->lo = base;
+  ext->hi = base + (uintptr_t)(last * elt);
+  return FA_OK;
+}
+
+fa_status check_params(const fa_attn_params* p) {
+  if (!p) return fail(FA_ERR_NULL, "params pointer is NULL");
+  if (p->B < 1 || p->Hq < 1 || p->Hkv < 1 || p->Sq < 1 || p->Sk < 1 || p->D < 1)
+    return fail(FA_ERR_SHAPE, "sizes must be positive (B=%d Hq=%d Hkv=%d Sq=%d Sk=%d D=%d)", p->B, p->Hq, p->Hkv,
+                p->Sq, p->Sk, p->D);
+  if (p->Hq % p->Hkv) return fail(FA_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", p->Hq, p->Hkv);
+  if (p->B > 65535 || p->Hq > 65535) return fail(FA_ERR_SHAPE, "B and Hq must be at most 65535");
+  if (p->dtype != FA_F32 && p->dtype != FA_BF16) return fail(FA_ERR_DTYPE, "unknown dtype %d", p->dtype);
+  if (p->D != 64 && p->D != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", p->D);
+  if (p->causal != 0 && p->causal != 1) return fail(FA_ERR_SHAPE, "causal must be 0 or 1");
+  if (p->q_offset < -(int64_t(1) << 40) || p->q_offset > (int64_t(1) << 40))
+    return fail(FA_ERR_SHAPE, "q_offset out of range");
+  if (!isfinite(p->scale)) return fail(FA_ERR_SHAPE, "scale must be finite");
+  if (p->mask) {
+    if (p->mask_stride_q < p->Sk) return fail(FA_ERR_STRIDE, "mask_stride_q (%lld) < Sk", (long long)p->mask_stride_q);
+    if (p->mask_stride_b < 0) return fail(FA_ERR_STRIDE, "mask_stride_b is negative");
+    if (reinterpret_cast<uintptr_t>(p->mask) % 4) return fail(FA_ERR_ALIGN, "mask pointer is not 4-byte aligned");
+  }
+  return FA_OK;
+}
+
+Extent mask_extent(const fa_attn_params* p) {
+  const uintptr_t base = reinterpret_cast<uintptr_t>(p->mask);
+  const int64_t last = (int64_t)(p->B - 1) * p->mask_stride_b + (int64_t)(p->Sq - 1) * p->mask_stride_q + p->Sk;
+  return {base, base + (uintptr_t)(last * 4)};
+}
+
+fa::AttnShape shape_of(const fa_attn_params* p) {
+  fa::AttnShape a;
+  a.B = p->B;
+  a.Hq = p->Hq;
+  a.Hkv = p->Hkv;
+  a.Sq = p->Sq;
+  a.Sk = p->Sk;
+  a.D = p->D;
+  a.G = p->Hq / p->Hkv;
+  a.causal = p->causal;
+  a.q_offset = p->q_offset;
+  a.scale = p->scale;
+  a.mask = p->mask;
+  a.mask_sb = p->mask_stride_b;
+  a.mask_sq = p->mask_stride_q;
+  return a;
+}
+
+fa::Strides strides_of(const fa_view* v) { return {v->stride_b, v->stride_h, v->stride_s}; }
+
+int elt_of(const fa_attn_params* p) { return p->dtype == FA_BF16 ? 2 : 4; }
+
+fa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return FA_OK;
+  return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+fa_status check_alias(const Extent* outs, int n_out, const char* const* out_names, const Extent* ins, int n_in,
+                      const char* const* in_names) {
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlaps(outs[i], ins[j]))
+        return fail(FA_ERR_ALIAS, "output %s overlaps input %s", out_names[i], in_names[j]);
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlaps(outs[i], outs[j]))
+        return fail(FA_ERR_ALIAS, "outputs %s and %s overlap", out_names[i], out_names[j]);
+  }
+  return FA_OK;
+}
+
+size_t workspace_bytes(const fa_attn_params* p) {
+  const size_t n = (size_t)p->B * p->Hq * p->Sq * p->D * sizeof(float);
+  return (n + 255) / 256 * 256;
+}
+
+// Shared body of the two backward entry points.
+fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,
+                     const fa_view* dout, const fa_view* lse, const fa_view* delta, const fa_view* dq,
+                     const fa_view* dk, const fa_view* dv, void* workspace, size_t workspace_bytes_given,
+                     hipStream_t stream, bool accumulate) {
+  fa_status s = check_params(p);
+  if (s) return s;
+  const int elt = elt_of(p);
+  Extent eq, ek, ev, edo, el, ed, edq, edk, edv;
+  if ((s = check_view(q, "q", p->B, p->Hq, p->Sq, p->D, elt, true, false, &eq))) return s;
+  if ((s = check_view(k, "k", p->B, p->Hkv, p->Sk, p->D, elt, true, false, &ek))) return s;
+  if ((s = check_view(v, "v", p->B, p->Hkv, p->Sk, p->D, elt, true, false, &ev))) return s;
+  if ((s = check_view(dout, "dout", p->B, p->Hq, p->Sq, p->D, elt, true, false, &edo))) return s;
+  if (!lse || !delta) return fail(FA_ERR_NULL, "lse or delta view is NULL");
+  if (lse->stride_s != 1 || delta->stride_s != 1) return fail(FA_ERR_STRIDE, "lse / delta stride_s must be 1");
+  if ((s = check_view(lse, "lse", p->B, p->Hq, p->Sq, 1, 4, false, false, &el))) return s;
+  if ((s = check_view(delta, "delta", p->B, p->Hq, p->Sq, 1, 4, false, false, &ed))) return s;
+  if ((s = check_view(dq, "dq", p->B, p->Hq, p->Sq, p->D, elt, true, true, &edq))) return s;
+  const int gelt = accumulate ? 4 : elt;
+  if ((s = check_view(dk, accumulate ? "dk_acc" : "dk", p->B, p->Hkv, p->Sk, p->D, gelt, true, true, &edk))) return s;
+  if ((s = check_view(dv, accumulate ? "dv_acc" : "dv", p->B, p->Hkv, p->Sk, p->D, gelt, true, true, &edv))) return s;
+  const size_t need = workspace_bytes(p);
+  if (!workspace) return fail(FA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (workspace_bytes_given < need)
+    return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_given, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(FA_ERR_ALIGN, "workspace is not 256-byte aligned");
+  const uintptr_t wlo = reinterpret_cast<uintptr_t>(workspace);
+  Extent ews = {wlo, wlo + need};
+  Extent ins[8] = {eq, ek, ev, edo, el, ed, {0, 0}, {0, 0}};
+  const char* in_names[8] = {"q", "k", "v", "dout", "lse", "delta", "mask", "-"};
+  int n_in = 6;
+  if (p->mask) ins[n_in++] = mask_extent(p);
+  Extent outs[4] = {edq, edk, edv, ews};
+  const char* out_names[4] = {"dq", accumulate ? "dk_acc" : "dk", accumulate ? "dv_acc" : "dv", "workspace"};
+  if ((s = check_alias(outs, 4, out_names, ins, n_in, in_names))) return s;
+
+  fa::BwdArgs a;
+  a.a = shape_of(p);
+  a.q = q->data;
+  a.k = k->data;
+  a.v = v->data;
+  a.dout = dout->data;
+  a.lse = static_cast<const float*>(lse->data);
+  a.delta = static_cast<const float*>(delta->data);
+  a.dk = dk->data;
+  a.dv = dv->data;
+  a.dq_acc = static_cast<float*>(workspace);
+  a.sq = strides_of(q);
+  a.sk = strides_of(k);
+  a.sv = strides_of(v);
+  a.sdo = strides_of(dout);
+  a.sdk = strides_of(dk);
+  a.sdv = strides_of(dv);
+  a.lse_sb = lse->stride_b;
+  a.lse_sh = lse->stride_h;
+  a.delta_sb = delta->stride_b;
+  a.delta_sh = delta->stride_h;
+  a.accumulate = accumulate ? 1 : 0;
+  const int is_bf16 = p->dtype == FA_BF16;
+  fa_status st;
+  if ((st = hip_status(fa::launch_zero_f32(a.dq_acc, (int64_t)p->B * p->Hq * p->Sq * p->D, stream), "dq clear")))
+    return st;
+  if ((st = hip_status(fa::launch_bwd(a, is_bf16, stream), "backward"))) return st;
+  fa::DqArgs c;
+  c.B = p->B;
+  c.Hq = p->Hq;
+  c.Sq = p->Sq;
+  c.D = p->D;
+  c.dq_acc = a.dq_acc;
+  c.dq = dq->data;
+  c.sdq = strides_of(dq);
+  c.scale = p->scale;
+  return hip_status(fa::launch_dq_convert(c, is_bf16, stream), "dq convert");
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_train_fwd(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,
+                       const fa_view* o, const fa_view* lse, hipStream_t stream) {
+  g_err[0] = 0;
+  fa_status s = check_params(p);
+  if (s) return s;
+  const int elt = elt_of(p);
+  Extent eq, ek, ev, eo, el;
+  if ((s = check_view(q, "q", p->B, p->Hq, p->Sq, p->D, elt, true, false, &eq))) return s;
+  if ((s = check_view(k, "k", p->B, p->Hkv, p->Sk, p->D, elt, true, false, &ek))) return s;
+  if ((s = check_view(v, "v", p->B, p->Hkv, p->Sk, p->D, elt, true, false, &ev))) return s;
+  if ((s = check_view(o, "o", p->B, p->Hq, p->Sq, p->D, elt, true, true, &eo))) return s;
+  if (!lse) return fail(FA_ERR_NULL, "lse view is NULL");
+  if (lse->stride_s != 1) return fail(FA_ERR_STRIDE, "lse stride_s must be 1");
+  if ((s = check_view(lse, "lse", p->B, p->Hq, p->Sq, 1, 4, false, true, &el))) return s;
+  Extent ins[4] = {eq, ek, ev, {0, 0}};
+  const char* in_names[4] = {"q", "k", "v", "mask"};
+  int n_in = 3;
+  if (p->mask) ins[n_in++] = mask_extent(p);
+  Extent outs[2] = {eo, el};
+  const char* out_names[2] = {"o", "lse"};
+  if ((s = check_alias(outs, 2, out_names, ins, n_in, in_names))) return s;
+
+  fa::FwdArgs a;
+  a.a = shape_of(p);
+  a.q = q->data;
+  a.k = k->data;
+  a.v = v->data;
+  a.o = o->data;
+  a.lse = static_cast<float*>(lse->data);
+  a.sq = strides_of(q);
+  a.sk = strides_of(k);
+  a.sv = strides_of(v);
+  a.so = strides_of(o);
+  a.lse_sb = lse->stride_b;
+  a.lse_sh = lse->stride_h;
+  return hip_status(fa::launch_fwd(a, p->dtype == FA_BF16, stream), "forward");
+}
+
+fa_status fa_train_bwd_preprocess(const fa_attn_params* p, const fa_view* o, const fa_view* dout,
+                                  const fa_view* delta, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!p) return fail(FA_ERR_NULL, "params pointer is NULL");
+  if (p->B < 1 || p->Hq < 1 || p->Sq < 1) return fail(FA_ERR_SHAPE, "sizes must be positive");
+  if (p->dtype != FA_F32 && p->dtype != FA_BF16) return fail(FA_ERR_DTYPE, "unknown dtype %d", p->dtype);
+  if (p->D != 64 && p->D != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", p->D);
+  const int elt = elt_of(p);
+  Extent eo, edo, ed;
+  fa_status s;
+  if ((s = check_view(o, "o", p->B, p->Hq, p->Sq, p->D, elt, true, false, &eo))) return s;
+  if ((s = check_view(dout, "dout", p->B, p->Hq, p->Sq, p->D, elt, true, false, &edo))) return s;
+  if (!delta) return fail(FA_ERR_NULL, "delta view is NULL");
+  if (delta->stride_s != 1) return fail(FA_ERR_STRIDE, "delta stride_s must be 1");
+  if ((s = check_view(delta, "delta", p->B, p->Hq, p->Sq, 1, 4, false, true, &ed))) return s;
+  Extent ins[2] = {eo, edo};
+  const char* in_names[2] = {"o", "dout"};
+  const char* out_names[1] = {"delta"};
+  if ((s = check_alias(&ed, 1, out_names, ins, 2, in_names))) return s;
+  fa::PreArgs a;
+  a.B = p->B;
+  a.Hq = p->Hq;
+  a.Sq = p->Sq;
+  a.D = p->D;
+  a.o = o->data;
+  a.dout = dout->data;
+  a.delta = static_cast<float*>(delta->data);
+  a.so = strides_of(o);
+  a.sdo = strides_of(dout);
+  a.delta_sb = delta->stride_b;
+  a.delta_sh = delta->stride_h;
+  return hip_status(fa::launch_preprocess(a, p->dtype == FA_BF16, stream), "preprocess");
+}
+
+size_t fa_train_bwd_workspace_bytes(const fa_attn_params* p) {
+  if (check_params(p) != FA_OK) return 0;
+  return workspace_bytes(p);
+}
+
+fa_status fa_train_bwd(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,
+                       const fa_view* dout, const fa_view* lse, const fa_view* delta, const fa_view* dq,
+                       const fa_view* dk, const fa_view* dv, void* workspace, size_t workspace_bytes_given,
+                       hipStream_t stream) {
+  g_err[0] = 0;
+  return bwd_common(p, q, k, v, dout, lse, delta, dq, dk, dv, workspace, workspace_bytes_given, stream, false);
+}
+
+fa_status fa_train_bwd_chunked(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,
+                               const fa_view* dout, const fa_view* lse, const fa_view* delta, const fa_view* dq,
+                               const fa_view* dk_acc, const fa_view* dv_acc, void* workspace,
+                               size_t workspace_bytes_given, hipStream_t stream) {
+  g_err[0] = 0;
+  return bwd_common(p, q, k, v, dout, lse, delta, dq, dk_acc, dv_acc, workspace, workspace_bytes_given, stream,
+                    true);
+}
+
+const char* fa_train_status_str(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "null pointer";
+    case FA_ERR_SHAPE: return "bad shape";
+    case FA_ERR_DTYPE: return "bad dtype";
+    case FA_ERR_STRIDE: return "bad stride";
+    case FA_ERR_ALIGN: return "misaligned pointer or stride";
+    case FA_ERR_ALIAS: return "output aliases another buffer";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+const char* fa_train_last_error(void) { return g_err; }
+
+int fa_train_version(void) { return FA_TRAIN_ABI_VERSION; }
+
+}  // extern "C"

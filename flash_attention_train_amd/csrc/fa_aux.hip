@@ -1,0 +1,108 @@
+// fa_aux.hip -- the memory-bound helpers of the backward:
+//   * the preprocess Delta_i = sum_d dO_id * O_id (llama.cpp pull request 57,
+//     commit 86c140d: the tiled backward computes the LSE, then D, then the
+//     gradients per tile);
+//   * clearing the fp32 dQ accumulator;
+//   * converting the accumulated dQ to its output dtype with the softmax scale.
+// All three stream their operands once with 16-byte loads and stores.
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+namespace {
+
+// One query row per D/8 consecutive lanes, 8 elements per lane, fp32 products,
+// reduced with lane shuffles inside the row's lane group.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void preprocess_kernel(const PreArgs p) {
+  constexpr int LPR = D / 8;       // lanes per row
+  constexpr int RPB = 256 / LPR;   // rows per workgroup
+  const int sub = threadIdx.x % LPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int64_t nrows = (int64_t)p.B * p.Hq * p.Sq;
+  float acc = 0.f;
+  int b = 0, h = 0, i = 0;
+  if (row < nrows) {
+    i = (int)(row % p.Sq);
+    h = (int)((row / p.Sq) % p.Hq);
+    b = (int)(row / ((int64_t)p.Sq * p.Hq));
+    Frag<T> o, d;
+    load8(o, static_cast<const T*>(p.o) + b * p.so.b + h * p.so.h + (int64_t)i * p.so.s + 8 * sub);
+    load8(d, static_cast<const T*>(p.dout) + b * p.sdo.b + h * p.sdo.h + (int64_t)i * p.sdo.s + 8 * sub);
+    for (int j = 0; j < 8; ++j) acc += elem(o, j) * elem(d, j);
+  }
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < nrows && sub == 0) p.delta[b * p.delta_sb + h * p.delta_sh + i] = acc;
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(f32x4* p, int64_t n4) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) p[i] = z;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void dq_convert_kernel(const DqArgs p) {
+  constexpr int CPR = D / 8;  // 8-element chunks per row
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nrows = (int64_t)p.B * p.Hq * p.Sq;
+  if (c >= nrows * CPR) return;
+  const int64_t row = c / CPR;
+  const int d0 = (int)(c % CPR) * 8;
+  const int i = (int)(row % p.Sq);
+  const int h = (int)((row / p.Sq) % p.Hq);
+  const int b = (int)(row / ((int64_t)p.Sq * p.Hq));
+  const float* src = p.dq_acc + row * D + d0;
+  const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+  const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
+  T* dst = static_cast<T*>(p.dq) + b * p.sdq.b + h * p.sdq.h + (int64_t)i * p.sdq.s + d0;
+  Frag<T> out;
+  f32x16 tmp;
+  for (int j = 0; j < 4; ++j) {
+    tmp[j] = lo[j] * p.scale;
+    tmp[4 + j] = hi[j] * p.scale;
+  }
+  pack8(out, tmp, 0);
+  store8(dst, out);
+}
+
+template <typename T, int D>
+hipError_t launch_pre_t(const PreArgs& p, hipStream_t stream) {
+  constexpr int RPB = 256 / (D / 8);
+  const int64_t nrows = (int64_t)p.B * p.Hq * p.Sq;
+  const dim3 grid((unsigned)((nrows + RPB - 1) / RPB));
+  hipLaunchKernelGGL((preprocess_kernel<T, D>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_dq_t(const DqArgs& p, hipStream_t stream) {
+  const int64_t chunks = (int64_t)p.B * p.Hq * p.Sq * (D / 8);
+  const dim3 grid((unsigned)((chunks + 255) / 256));
+  hipLaunchKernelGGL((dq_convert_kernel<T, D>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_preprocess(const PreArgs& p, int is_bf16, hipStream_t stream) {
+  if (is_bf16) return p.D == 64 ? launch_pre_t<bf16, 64>(p, stream) : launch_pre_t<bf16, 128>(p, stream);
+  return p.D == 64 ? launch_pre_t<float, 64>(p, stream) : launch_pre_t<float, 128>(p, stream);
+}
+
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream) {
+  // n is a multiple of 4 (whole rows of D = 64 or 128 floats)
+  const int64_t n4 = n / 4;
+  int64_t blocks = (n4 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, reinterpret_cast<f32x4*>(p), n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_convert(const DqArgs& p, int is_bf16, hipStream_t stream) {
+  if (is_bf16) return p.D == 64 ? launch_dq_t<bf16, 64>(p, stream) : launch_dq_t<bf16, 128>(p, stream);
+  return p.D == 64 ? launch_dq_t<float, 64>(p, stream) : launch_dq_t<float, 128>(p, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,203 @@
+// fa_fwd.hip -- forward of the fused attention op: O and the per-row LSE.
+//
+// Tiled online-softmax attention (the forward half of the flash-attention
+// training op on the "Flash Attn Training" skill page, section 6, trap 3: the
+// forward emits O together with the LSE the backward recomputes P from).
+//
+// Work split: one workgroup of 4 waves per (batch, query head, 128-row query
+// tile); each wave owns 32 query rows and walks the key tiles (64 keys each) that
+// can be visible to its tile. K and V^T tiles are staged in LDS and shared by the
+// four waves; Q stays in registers for the whole walk.
+//
+// Layout trick: the wave computes S^T = K Q^T (keys as rows), so in the
+// accumulator every lane holds ONE query row and 16 keys of it. The row max/sum
+// then need a single cross-lane step (lane l with lane l ^ 32), the probabilities
+// feed the next product straight from registers as its B operand, and the
+// output is accumulated transposed, O^T = V^T P^T, so the per-row rescale is a
+// per-lane scalar.
+//
+// Numerics: scores are scaled by scale * log2(e) and exponentiated with the
+// hardware exp2; the LSE is converted back to natural log on output. A row that
+// has seen no visible key keeps m = -inf; its exponent base is taken as 0 so that
+// exp2(-inf) = 0 flows through without NaN, and the epilogue writes O = 0 and
+// LSE = 0 for it (skill page, section 6, trap 9).
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+namespace {
+
+__device__ __forceinline__ f32x16 zeros16() {
+  f32x16 z;
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ bf16 elem_t(const bf16x8& f, int j) { return f[j]; }
+__device__ __forceinline__ float elem_t(const f32x8& f, int j) { return j < 4 ? f.lo[j] : f.hi[j - 4]; }
+
+template <typename T, int D, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(256, 1) void fwd_kernel(const FwdArgs args) {
+  constexpr int BM = 128;              // query rows per workgroup (32 per wave)
+  constexpr int BN = 64;               // keys per tile
+  constexpr int PAD = 16 / sizeof(T);  // 16 bytes of row padding against bank conflicts
+  constexpr int KS = D + PAD;          // row stride of the K tile [BN][D]
+  constexpr int VS = BN + PAD;         // row stride of the V^T tile [D][BN]
+  constexpr int DS = D / 16;           // k-slot groups along the head dim
+  constexpr int DB = D / 32;           // 32-wide output blocks along the head dim
+  __shared__ __attribute__((aligned(16))) T k_lds[BN * KS];
+  __shared__ __attribute__((aligned(16))) T vt_lds[D * VS];
+
+  const AttnShape& a = args.a;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, r32 = lane & 31;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int qt = gridDim.x - 1 - blockIdx.x;  // the longest causal tiles start first
+  const int q0 = qt * BM;
+  const int qrow = q0 + wave * 32 + r32;
+  const int hk = h / a.G;
+  const float cs = a.scale * kLog2e;
+
+  const T* Q = static_cast<const T*>(args.q) + b * args.sq.b + h * args.sq.h;
+  const T* K = static_cast<const T*>(args.k) + b * args.sk.b + hk * args.sk.h;
+  const T* V = static_cast<const T*>(args.v) + b * args.sv.b + hk * args.sv.h;
+  const float* Mrow = nullptr;
+  if (MASK && qrow < a.Sq) Mrow = a.mask + b * a.mask_sb + (int64_t)qrow * a.mask_sq;
+
+  // Q as the B operand of S^T = K Q^T: lane (row r32, half g) holds d = 16 s + 8 g + j
+  Frag<T> qf[DS];
+  for (int s = 0; s < DS; ++s) {
+    if (qrow < a.Sq)
+      load8(qf[s], Q + (int64_t)qrow * args.sq.s + 16 * s + 8 * g);
+    else
+      zero(qf[s]);
+  }
+
+  f32x16 oacc[DB];
+  for (int db = 0; db < DB; ++db) oacc[db] = zeros16();
+  float m = neg_inf();  // running row max (log2 units), identical in lanes l and l ^ 32
+  float l = 0.f;        // this lane's share of the running row sum
+
+  const int nkt = (a.Sk + BN - 1) / BN;
+  int kt_end = nkt;
+  if (CAUSAL) {
+    const int64_t last_key = a.q_offset + q0 + BM - 1;  // highest key the tile can see
+    kt_end = last_key < 0 ? 0 : (int)((last_key / BN + 1) < nkt ? (last_key / BN + 1) : nkt);
+  }
+
+  for (int kt = 0; kt < kt_end; ++kt) {
+    __syncthreads();  // every wave is done with the previous tile
+    for (int c = tid; c < BN * D / 8; c += 256) {
+      const int key = c / (D / 8), d0 = (c % (D / 8)) * 8;
+      const int kg = kt * BN + key;
+      Frag<T> kv, vv;
+      if (kg < a.Sk) {
+        load8(kv, K + (int64_t)kg * args.sk.s + d0);
+        load8(vv, V + (int64_t)kg * args.sv.s + d0);
+      } else {
+        zero(kv);
+        zero(vv);
+      }
+      store8(k_lds + key * KS + d0, kv);
+      for (int i = 0; i < 8; ++i) vt_lds[(d0 + i) * VS + key] = elem_t(vv, i);
+    }
+    __syncthreads();
+
+    // S^T for two 32-key blocks: lane (query r32, half g), register r -> key 8 (r/4) + 4 g + r%4
+    f32x16 st[2];
+    for (int kb = 0; kb < 2; ++kb) {
+      st[kb] = zeros16();
+      for (int s = 0; s < DS; ++s) {
+        Frag<T> kf;
+        load8(kf, k_lds + (32 * kb + r32) * KS + 16 * s + 8 * g);
+        mma(st[kb], kf, qf[s]);
+      }
+    }
+
+    float mx = neg_inf();
+    for (int kb = 0; kb < 2; ++kb) {
+      for (int r = 0; r < 16; ++r) {
+        const int key = kt * BN + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+        float x = st[kb][r] * cs;
+        bool vis = key < a.Sk;
+        if (CAUSAL) vis = vis && ((int64_t)key <= a.q_offset + qrow);
+        if (MASK && vis && Mrow) x += Mrow[key] * kLog2e;
+        x = vis ? x : neg_inf();
+        st[kb][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, xor32(mx));
+    const float m_new = fmaxf(m, mx);
+    const float base = (m_new == neg_inf()) ? 0.f : m_new;
+    const float alpha = fast_exp2(m - base);  // 0 while nothing was visible yet
+    m = m_new;
+
+    float ls = 0.f;
+    for (int kb = 0; kb < 2; ++kb) {
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(st[kb][r] - base);
+        st[kb][r] = p;
+        ls += p;
+      }
+    }
+    l = l * alpha + ls;
+    for (int db = 0; db < DB; ++db)
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+
+    // O^T += V^T P^T. Registers 8 hh .. 8 hh + 7 of key block kb hold keys
+    // 32 kb + 16 hh + {4 g .. 4 g + 3} and 32 kb + 16 hh + 8 + {4 g .. 4 g + 3};
+    // the V^T operand reads the same keys for its output row d.
+    for (int kb = 0; kb < 2; ++kb) {
+      for (int hh = 0; hh < 2; ++hh) {
+        Frag<T> pf;
+        pack8(pf, st[kb], 8 * hh);
+        for (int db = 0; db < DB; ++db) {
+          const T* row = vt_lds + (32 * db + r32) * VS + 32 * kb + 16 * hh + 4 * g;
+          Frag<T> vf;
+          load4x2(vf, row, row + 8);
+          mma(oacc[db], vf, pf);
+        }
+      }
+    }
+  }
+
+  // epilogue: O = acc / l, LSE = ln(sum) + max; fully masked rows -> 0 and 0
+  const float lt = l + xor32(l);
+  const bool full = (m == neg_inf());
+  const float inv = full ? 0.f : 1.f / lt;
+  const float lse = full ? 0.f : (m + log2f(lt)) * kLn2;
+  if (qrow < a.Sq) {
+    T* O = static_cast<T*>(args.o) + b * args.so.b + h * args.so.h + (int64_t)qrow * args.so.s;
+    for (int db = 0; db < DB; ++db)
+      for (int r = 0; r < 16; ++r) O[32 * db + 8 * (r >> 2) + 4 * g + (r & 3)] = from_f32<T>(oacc[db][r] * inv);
+    if (g == 0) args.lse[b * args.lse_sb + h * args.lse_sh + qrow] = lse;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_fwd_t(const FwdArgs& args, hipStream_t stream) {
+  const dim3 grid((args.a.Sq + 127) / 128, args.a.Hq, args.a.B);
+  const dim3 block(256);
+  const bool causal = args.a.causal != 0, mask = args.a.mask != nullptr;
+  if (causal && mask)
+    hipLaunchKernelGGL((fwd_kernel<T, D, true, true>), grid, block, 0, stream, args);
+  else if (causal)
+    hipLaunchKernelGGL((fwd_kernel<T, D, true, false>), grid, block, 0, stream, args);
+  else if (mask)
+    hipLaunchKernelGGL((fwd_kernel<T, D, false, true>), grid, block, 0, stream, args);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, false, false>), grid, block, 0, stream, args);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& args, int is_bf16, hipStream_t stream) {
+  if (is_bf16) return args.a.D == 64 ? launch_fwd_t<bf16, 64>(args, stream) : launch_fwd_t<bf16, 128>(args, stream);
+  return args.a.D == 64 ? launch_fwd_t<float, 64>(args, stream) : launch_fwd_t<float, 128>(args, stream);
+}
+
+}  // namespace fa

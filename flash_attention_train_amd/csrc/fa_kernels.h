@@ -1,0 +1,79 @@
+// fa_kernels.h -- kernel argument blocks and launcher declarations (internal).
+//
+// The C ABI layer validates every argument on the host, fills one of these
+// blocks and calls the matching launcher; the launchers pick a template instance
+// and enqueue it on the caller's stream. Strides are in elements of each tensor's
+// own type.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct Strides {
+  int64_t b, h, s;
+};
+
+struct AttnShape {
+  int B, Hq, Hkv, Sq, Sk, D;
+  int G;             // Hq / Hkv
+  int causal;
+  int64_t q_offset;  // key position of query row 0
+  float scale;       // multiplies <q, k>
+  const float* mask; // additive [b][i][j] fp32 or nullptr
+  int64_t mask_sb, mask_sq;
+};
+
+struct FwdArgs {
+  AttnShape a;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  Strides sq, sk, sv, so;
+  int64_t lse_sb, lse_sh;
+};
+
+struct PreArgs {
+  int B, Hq, Sq, D;
+  const void* o;
+  const void* dout;
+  float* delta;
+  Strides so, sdo;
+  int64_t delta_sb, delta_sh;
+};
+
+struct BwdArgs {
+  AttnShape a;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse;
+  const float* delta;
+  void* dk;        // dtype output (plain) or fp32 accumulator (chunked)
+  void* dv;
+  float* dq_acc;   // fp32 [B, Hq, Sq, D] contiguous workspace, zeroed before the launch
+  Strides sq, sk, sv, sdo, sdk, sdv;
+  int64_t lse_sb, lse_sh, delta_sb, delta_sh;
+  int accumulate;  // 1: dK/dV are fp32 accumulators and receive +=, 0: overwrite in dtype
+};
+
+struct DqArgs {
+  int B, Hq, Sq, D;
+  const float* dq_acc;
+  void* dq;
+  Strides sdq;
+  float scale;
+};
+
+// launchers: return hipSuccess or the launch error
+hipError_t launch_fwd(const FwdArgs& args, int is_bf16, hipStream_t stream);
+hipError_t launch_preprocess(const PreArgs& args, int is_bf16, hipStream_t stream);
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& args, int is_bf16, hipStream_t stream);
+hipError_t launch_dq_convert(const DqArgs& args, int is_bf16, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,145 @@
+/*
+ * fa_train.h -- C ABI of the fused flash-attention training op for MI355X (gfx950).
+ *
+ * The op is exact softmax attention with a per-row log-sum-exp (LSE) side output,
+ * and its gradient, split the way the pages split it:
+ *
+ *   fa_train_fwd             O and LSE                         (forward)
+ *   fa_train_bwd_preprocess  Delta_i = sum_d dO_id * O_id      ("LSE, D, then grads")
+ *   fa_train_bwd             dQ, dK, dV from Q, K, V, dO, LSE, Delta
+ *   fa_train_bwd_chunked     the same, but dK/dV are ADDED into caller-owned fp32
+ *                            accumulators over a cached K/V window (exact walk)
+ *
+ * Definitions (natural log; s = scale; G = Hq / Hkv; query head h reads KV head h / G):
+ *   S_ij  = s * <q_i, k_j> + M_ij, or -inf when masked (mask entry -inf, causal
+ *           j > q_offset + i)
+ *   LSE_i = ln sum_j exp(S_ij);  P_ij = exp(S_ij - LSE_i);  O_i = sum_j P_ij v_j
+ *   a query row with no visible key is "fully masked": O_i = 0 and LSE_i = 0
+ *   dS_ij = P_ij (<dO_i, v_j> - Delta_i);  dQ_i = s sum_j dS_ij k_j
+ *   dK_j  = s sum_{h in group} sum_i dS_ij q_i;  dV_j = sum_{h in group} sum_i P_ij dO_i
+ *
+ * Sources: "Flash Attn Training" skill page, section 6 (trap 3: the forward emits
+ * O and the LSE and the LSE receives no gradient; trap 4: the backward refuses to
+ * write over the forward's buffers; trap 5: native GQA without head expansion;
+ * traps 8 and 9: fully masked rows give O = 0, LSE = 0 and fully masked key columns
+ * get zero gradient); llama.cpp pull request 57, commit 86c140d (a backward tiled
+ * over the KV window: LSE, D, then per-tile grads, GQA group-sum; the exact walk
+ * adds dL/d(cached K/V) into a caller-owned accumulator) and the commit that makes
+ * the training graph the serving graph (attention reads the cache in place).
+ *
+ * Conventions shared by every entry point
+ *   - Device pointers throughout. Q, O, dO, dQ are [B, Hq, Sq, D]; K, V, dK, dV are
+ *     [B, Hkv, Sk, D]; each is described by an fa_view: element strides for the
+ *     batch, head and sequence dimensions, with D contiguous. LSE and Delta are fp32
+ *     [B, Hq, Sq] views whose sequence stride must be 1.
+ *   - dtype applies to Q, K, V, O, dO, dQ, dK, dV. Accumulation is fp32 for both
+ *     dtypes; with FA_BF16 the probabilities and dS are rounded to bf16 before
+ *     their matrix products.
+ *   - Rows need 16-byte alignment: data pointers 16-byte aligned and every stride a
+ *     multiple of 16 bytes' worth of elements.
+ *   - The mask is optional, fp32, additive, indexed [b][i][j] (j contiguous), with
+ *     values 0, finite biases or -inf. mask_stride_b = 0 shares one mask across the
+ *     batch. It is broadcast over heads.
+ *   - Work is enqueued on `stream` (NULL = the null stream). The library never
+ *     allocates, frees, synchronizes or reads results back; outputs are valid once
+ *     the stream's work has completed. Entry points are reentrant.
+ *   - Every argument check runs on the host before any launch; on error nothing is
+ *     launched, outputs are untouched, and fa_train_last_error() describes the
+ *     problem (thread-local text).
+ */
+#ifndef FA_TRAIN_H
+#define FA_TRAIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_TRAIN_ABI_VERSION 1
+
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,        /* a required pointer is NULL */
+    FA_ERR_SHAPE = 2,       /* non-positive size, Hq % Hkv != 0, bad q_offset, ... */
+    FA_ERR_DTYPE = 3,       /* unknown dtype */
+    FA_ERR_STRIDE = 4,      /* stride too small / overlapping rows, LSE stride_s != 1 */
+    FA_ERR_ALIGN = 5,       /* pointer or stride not 16-byte aligned */
+    FA_ERR_ALIAS = 6,       /* an output overlaps an input or another output */
+    FA_ERR_UNSUPPORTED = 7, /* head dim other than 64 or 128 */
+    FA_ERR_WORKSPACE = 8,   /* workspace missing or smaller than fa_train_bwd_workspace_bytes */
+    FA_ERR_HIP = 9          /* a kernel launch failed; detail in fa_train_last_error() */
+} fa_status;
+
+typedef enum fa_dtype { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+/* A strided view of a [B, H, S, D] tensor (or [B, H, S] for LSE / Delta).
+ * Strides count elements of the view's own type. D is contiguous. */
+typedef struct fa_view {
+    void* data;
+    int64_t stride_b;
+    int64_t stride_h;
+    int64_t stride_s;
+} fa_view;
+
+typedef struct fa_attn_params {
+    int32_t B, Hq, Hkv, Sq, Sk, D;
+    int32_t dtype;        /* fa_dtype */
+    int32_t causal;       /* 0 or 1: key j visible to query i only if j <= q_offset + i */
+    int64_t q_offset;     /* key position of query row 0 (>= 0; Sk - Sq for bottom-right causal) */
+    float scale;          /* multiplies <q, k>; usually 1/sqrt(D) */
+    const float* mask;    /* optional additive mask [b][i][j], fp32; NULL = none */
+    int64_t mask_stride_b;/* elements between batch entries; 0 = shared by the batch */
+    int64_t mask_stride_q;/* elements between query rows (>= Sk) */
+} fa_attn_params;
+
+/* Forward: writes O (dtype) and LSE (fp32, natural log). Fully masked rows get
+ * O = 0 and LSE = 0. O must not overlap Q, K or V. */
+fa_status fa_train_fwd(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,
+                       const fa_view* o, const fa_view* lse, hipStream_t stream);
+
+/* Preprocess for the backward: Delta_i = sum_d dO_id * O_id in fp32, from the stored
+ * O and dO. Only B, Hq, Sq, D and dtype of p are used. */
+fa_status fa_train_bwd_preprocess(const fa_attn_params* p, const fa_view* o, const fa_view* dout,
+                                  const fa_view* delta, hipStream_t stream);
+
+/* Bytes of device workspace fa_train_bwd / fa_train_bwd_chunked need for p
+ * (an fp32 dQ accumulator). 0 if p is invalid. */
+size_t fa_train_bwd_workspace_bytes(const fa_attn_params* p);
+
+/* Backward: OVERWRITES dQ, dK, dV (dtype). Reads Q, K, V, dO, the forward's LSE and
+ * the preprocess's Delta. dQ/dK/dV must not overlap any input or each other (in
+ * particular not the forward's O / LSE buffers). `workspace` is caller-owned device
+ * memory of at least fa_train_bwd_workspace_bytes(p) bytes, 256-byte aligned; its
+ * contents on entry do not matter. dK/dV rows of keys no query can see are zero. */
+fa_status fa_train_bwd(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,
+                       const fa_view* dout, const fa_view* lse, const fa_view* delta, const fa_view* dq,
+                       const fa_view* dk, const fa_view* dv, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* Chunked backward for the exact walk over a cached K/V window: the query chunk
+ * (Sq rows at key positions q_offset ...) attends to window rows [0, Sk). OVERWRITES
+ * dQ for the chunk and ADDS the chunk's dK/dV contributions into fp32 accumulators
+ * dk_acc / dv_acc, views over the window ([B, Hkv, >= Sk, D], fp32 element strides).
+ * The accumulators are never cleared by the library; the caller zeroes them before
+ * the first chunk. Chunks may run in any order (the result is a sum). */
+fa_status fa_train_bwd_chunked(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,
+                               const fa_view* dout, const fa_view* lse, const fa_view* delta,
+                               const fa_view* dq, const fa_view* dk_acc, const fa_view* dv_acc,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* fa_train_status_str(fa_status s);
+/* Detail text of the calling thread's last error ("" if none). */
+const char* fa_train_last_error(void);
+/* FA_TRAIN_ABI_VERSION of the loaded library. */
+int fa_train_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_TRAIN_H */

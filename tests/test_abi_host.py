@@ -1,0 +1,138 @@
+"""The C ABI on the host, no GPU: the library loads, exports every symbol the
+headers declare, and rejects bad arguments before any launch. Pointers here are
+fake addresses; every call below is invalid in exactly one way, so validation
+returns before anything touches a device."""
+from __future__ import annotations
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from flash_attention_train_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libfa_train.so not built")
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(fa_train_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    L = B.lib()
+    names = declared_functions()
+    assert "fa_train_fwd" in names and "fa_train_bwd_chunked" in names
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in B.SIGNATURES, f"{n} has no ctypes signature in the binding"
+    assert L.fa_train_version() == 1
+
+
+BASE = 0x7F0000000000  # fake, 256-byte aligned device addresses
+
+
+def params(**kw):
+    a = dict(B=1, Hq=4, Hkv=2, Sq=64, Sk=64, D=64, dtype=B.FA_BF16, causal=0, q_offset=0, scale=0.125, mask=None,
+             mask_stride_b=0, mask_stride_q=0)
+    a.update(kw)
+    return B.FaAttnParams(*(a[f] for f, _ in B.FaAttnParams._fields_))
+
+
+def view(i, H=4, S=64, D=64, elt=2, **kw):
+    a = dict(data=BASE + i * (1 << 24), stride_b=H * S * D, stride_h=S * D, stride_s=D)
+    a.update(kw)
+    return B.FaView(a["data"], a["stride_b"], a["stride_h"], a["stride_s"])
+
+
+def lse_view(i, H=4, S=64):
+    return B.FaView(BASE + i * (1 << 24), H * S, S, 1)
+
+
+def fwd_call(p, q=None, k=None, v=None, o=None, lse=None):
+    q = q or view(0)
+    k = k or view(1, H=2)
+    v = v or view(2, H=2)
+    o = o or view(3)
+    lse = lse or lse_view(4)
+    return B.lib().fa_train_fwd(ctypes.byref(p) if p is not None else None, q, k, v, o, lse, None)
+
+
+FWD_ERRORS = [
+    ("null params", None, {}, 1),
+    ("Hq not a multiple of Hkv", params(Hq=3), {}, 2),
+    ("zero length", params(Sq=0), {}, 2),
+    ("bad dtype", params(dtype=7), {}, 3),
+    ("head dim 96", params(D=96), {}, 7),
+    ("misaligned q", params(), {"q": view(0, data=BASE + 8)}, 5),
+    ("stride not 16B", params(), {"k": view(1, H=2, stride_s=68)}, 5),
+    ("o rows overlap", params(), {"o": view(3, stride_s=32)}, 4),
+    ("o aliases q", params(), {"o": view(0)}, 6),
+    ("lse aliases o", params(), {"lse": B.FaView(BASE + 3 * (1 << 24), 256, 64, 1)}, 6),
+    ("lse not contiguous", params(), {"lse": B.FaView(BASE + 4 * (1 << 24), 512, 128, 2)}, 4),
+    ("null data", params(), {"v": view(2, H=2, data=0)}, 1),
+    ("causal flag 2", params(causal=2), {}, 2),
+    ("mask stride too small", params(mask=BASE + 9 * (1 << 24), mask_stride_q=32), {}, 4),
+]
+
+
+@pytest.mark.parametrize("name,p,over,code", FWD_ERRORS, ids=[e[0] for e in FWD_ERRORS])
+def test_forward_rejects(name, p, over, code):
+    st = fwd_call(p, **over)
+    assert st == code, (st, B.lib().fa_train_last_error())
+    assert B.lib().fa_train_last_error() != b""
+    assert B.lib().fa_train_status_str(st) not in (b"", b"ok")
+
+
+def bwd_call(p, accumulate=False, ws=None, ws_bytes=None, **over):
+    L = B.lib()
+    v = {"q": view(0), "k": view(1, H=2), "v": view(2, H=2), "do": view(3), "lse": lse_view(4), "delta": lse_view(5),
+         "dq": view(6), "dk": view(7, H=2, elt=4 if accumulate else 2), "dv": view(8, H=2)}
+    v.update(over)
+    need = L.fa_train_bwd_workspace_bytes(ctypes.byref(p))
+    ws = BASE + 12 * (1 << 24) if ws is None else ws
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    f = L.fa_train_bwd_chunked if accumulate else L.fa_train_bwd
+    return f(ctypes.byref(p), v["q"], v["k"], v["v"], v["do"], v["lse"], v["delta"], v["dq"], v["dk"], v["dv"], ws,
+             ws_bytes, None)
+
+
+def test_backward_rejects():
+    p = params()
+    assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(p)) == 1 * 4 * 64 * 64 * 4
+    assert bwd_call(p, ws=0) == 8
+    assert bwd_call(p, ws_bytes=100) == 8
+    assert bwd_call(p, ws=BASE + 12 * (1 << 24) + 16) == 5
+    assert bwd_call(p, dq=view(0)) == 6          # dQ over Q
+    assert bwd_call(p, dk=view(8, H=2)) == 6     # dK over dV
+    assert bwd_call(p, dv=view(4, H=2)) == 6  # dV over the LSE input
+    assert bwd_call(p, ws=BASE + 4 * (1 << 24)) == 6  # workspace over LSE
+    assert bwd_call(p, dk=view(7, H=2, stride_h=0)) == 4  # dK heads collapse onto each other
+    assert bwd_call(params(Hkv=3)) == 2
+    assert bwd_call(p, accumulate=True, dk=view(7, H=2, data=BASE + 7 * (1 << 24) + 4)) == 5
+    assert B.lib().fa_train_bwd_workspace_bytes(None) == 0
+
+
+def test_preprocess_rejects():
+    L = B.lib()
+    p = params()
+    assert L.fa_train_bwd_preprocess(ctypes.byref(p), view(0), view(1), B.FaView(BASE + 0 * (1 << 24), 256, 64, 1),
+                                     None) == 6
+    assert L.fa_train_bwd_preprocess(ctypes.byref(params(D=32)), view(0), view(1), lse_view(2), None) == 7
+    assert L.fa_train_bwd_preprocess(None, view(0), view(1), lse_view(2), None) == 1
+
+
+def test_probe_rejects_bad_arguments():
+    L = B.lib()
+    assert L.fa_train_probe_mfma(9, 1, BASE, BASE, BASE, None) == 2
+    assert L.fa_train_probe_mfma(0, 0, BASE, BASE, BASE, None) == 2
+    assert L.fa_train_probe_mfma(0, 1, None, BASE, BASE, None) == 1
+    assert L.fa_train_probe_ds_read_tr16(0, BASE, BASE, None) == 2

@@ -1,0 +1,143 @@
+"""GPU parity at sizes the oracle finishes in seconds: every output of the HIP
+path (O, LSE, Delta, dQ, dK, dV) against the oracle, element by element, on
+shapes that span several tiles and end in a ragged tail; plus the degenerate and
+structural cases (fully masked rows and columns, GQA, causal offsets, strided
+views, broadcast masks, fp32 and bf16, D = 64 and 128)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from flash_attention_train_amd import binding, configs
+from flash_attention_train_amd.inputs import make_case
+from parity_util import TOL, compare_full, dev, host64, run_gpu, say, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_full(c):
+    m = None if c.mask is None else c.mask.astype(np.float64)
+    return oracle.backward(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), m, scale=c.scale, causal=c.causal,
+                           q_offset=c.q_offset)
+
+
+CASES = {
+    # the tiny fp32 workload, exactly as specified
+    "tiny_f32": lambda: configs.make("tiny"),
+    # workload structures at reduced head counts and ragged lengths
+    "dit_sa_ragged": lambda: configs.make("dit_sa", Hq=4, Hkv=2, Sq=300, Sk=300),
+    "dit_ca_ragged": lambda: configs.make("dit_ca", B=2, Hq=2, Hkv=2, Sq=300, Sk=160),
+    "lm_causal_gqa4": lambda: configs.make("lm_causal", Hq=4, Hkv=1, Sq=333, Sk=333),
+    "chunk_offset": lambda: make_case("chunk_offset", B=1, Hq=4, Hkv=2, Sq=100, Sk=356, D=128, dtype="bf16",
+                                      seed=61, causal=True, q_offset=256),
+    "random_bias_bcast": lambda: make_case("random_bias_bcast", B=2, Hq=2, Hkv=1, Sq=130, Sk=70, D=128,
+                                           dtype="bf16", seed=62, mask="random",
+                                           mask_args={"Bm": 1, "full_rows": 3, "full_cols": 2}),
+    "d64_bf16": lambda: make_case("d64_bf16", B=2, Hq=4, Hkv=4, Sq=200, Sk=129, D=64, dtype="bf16", seed=63,
+                                  mask="random", mask_args={"Bm": 2, "p_masked": 0.5}),
+    "d128_f32_causal": lambda: make_case("d128_f32_causal", B=1, Hq=2, Hkv=1, Sq=150, Sk=150, D=128, dtype="f32",
+                                         seed=64, causal=True),
+    "f32_d64_gqa_mask": lambda: make_case("f32_d64_gqa_mask", B=2, Hq=4, Hkv=2, Sq=70, Sk=90, D=64, dtype="f32",
+                                          seed=65, mask="ca_keypad", mask_args={"lo": 10, "hi": 60,
+                                                                                "masked_rows": 2}),
+    "single_query_single_key": lambda: make_case("one_one", B=1, Hq=2, Hkv=1, Sq=1, Sk=1, D=128, dtype="bf16",
+                                                 seed=66),
+    "causal_q_before_keys": lambda: make_case("causal_negative_offset", B=1, Hq=2, Hkv=2, Sq=80, Sk=40, D=64,
+                                              dtype="f32", seed=67, causal=True),  # q_offset = -40
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_parity_small(name):
+    c = CASES[name]()
+    say(f"case {name}: B={c.B} Hq={c.Hq} Hkv={c.Hkv} Sq={c.Sq} Sk={c.Sk} D={c.D} {c.dtype} causal={c.causal} "
+        f"q_offset={c.q_offset} mask={c.meta['mask_kind']}")
+    got = run_gpu(c)
+    ref = oracle_full(c)
+    compare_full(c, got, ref, zero_ok=("dQ", "dK") if c.Sk == 1 else ())
+
+
+def test_deterministic_outputs():
+    """O, LSE, Delta, dK, dV are written without atomics: two runs agree bitwise."""
+    c = CASES["dit_ca_ragged"]()
+    t = upload(c)
+    a = run_gpu(c, t)
+    b = run_gpu(c, t)
+    for n in ("O", "LSE", "Delta", "dK", "dV"):
+        assert np.array_equal(a[n], b[n]), n
+
+
+def test_pad_invariance_bitwise():
+    """Changing K/V at pad keys leaves every real row's O and LSE bitwise unchanged
+    (the pages' dirty-padding check, HOT-Step TRAINING.md, batching paragraph)."""
+    c = configs.make("dit_sa", Hq=2, Hkv=1, Sq=200, Sk=200)
+    L = c.meta["valid_len"]
+    t = upload(c)
+    o1, l1 = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale)
+    k2, v2 = t["k"].clone(), t["v"].clone()
+    k2[:, :, L:] = 7.0
+    v2[:, :, L:] = -3.0
+    o2, l2 = binding.fwd(t["q"], k2, v2, mask=t["mask"], scale=c.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, :, :L], o2[:, :, :L]) and torch.equal(l1[:, :, :L], l2[:, :, :L])
+
+
+def test_strided_views():
+    """[B, S, H, D] memory order (permuted views) gives the same results as contiguous."""
+    c = configs.make("dit_sa", Hq=4, Hkv=2, Sq=150, Sk=150)
+    t = upload(c)
+
+    def bshd(x):
+        return x.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+
+    q, k, v, do = (bshd(t[n]) for n in ("q", "k", "v", "do"))
+    assert q.stride(1) == c.D and not q.is_contiguous()
+    o, lse = binding.fwd(q, k, v, mask=t["mask"], scale=c.scale, out=bshd(torch.empty_like(t["q"])))
+    delta = binding.bwd_preprocess(o, do)
+    dq, dk, dv = binding.bwd(q, k, v, do, lse, delta, mask=t["mask"], scale=c.scale,
+                             dq=bshd(torch.empty_like(t["q"])), dk=bshd(torch.empty_like(t["k"])),
+                             dv=bshd(torch.empty_like(t["v"])))
+    torch.cuda.synchronize()
+    ref = run_gpu(c, t)
+    for n, x in (("O", o), ("LSE", lse), ("Delta", delta), ("dK", dk), ("dV", dv)):
+        assert np.array_equal(host64(x), ref[n]), n
+    assert np.abs(host64(dq) - ref["dQ"]).max() <= 1e-2 * np.abs(ref["dQ"]).max()
+
+
+def test_chunked_walk_small():
+    """Eight 128-row chunks over a 1024-key window, dK/dV accumulated in fp32 on the
+    device, against the one-shot oracle (the exact walk, llama.cpp PR 57)."""
+    W, C = 1024, 128
+    c = configs.make("long_window", W=W, Hq=4, Hkv=2)
+    t = upload(c)
+    dk_acc = torch.zeros((1, c.Hkv, W, c.D), dtype=torch.float32, device="cuda")
+    dv_acc = torch.zeros_like(dk_acc)
+    O = torch.empty_like(t["q"])
+    LSE = torch.empty((1, c.Hq, W), dtype=torch.float32, device="cuda")
+    Delta = torch.empty_like(LSE)
+    dQ = torch.empty_like(t["q"])
+    for p0, n, sk in configs.chunk_plan(W, C):
+        q = t["q"][:, :, p0:p0 + n]
+        do = t["do"][:, :, p0:p0 + n]
+        kk, vv = t["k"][:, :, :sk], t["v"][:, :, :sk]
+        o, lse = binding.fwd(q, kk, vv, scale=c.scale, causal=True, q_offset=p0, out=O[:, :, p0:p0 + n],
+                             lse=LSE[:, :, p0:p0 + n])
+        delta = binding.bwd_preprocess(o, do, delta=Delta[:, :, p0:p0 + n])
+        binding.bwd_chunked(q, kk, vv, do, lse, delta, dk_acc, dv_acc, scale=c.scale, causal=True, q_offset=p0,
+                            dq=dQ[:, :, p0:p0 + n])
+    torch.cuda.synchronize()
+    ref = oracle_full(c)
+    got = {"O": host64(O), "LSE": host64(LSE), "Delta": host64(Delta), "dQ": host64(dQ),
+           "dK": dk_acc.cpu().numpy().astype(np.float64), "dV": dv_acc.cpu().numpy().astype(np.float64)}
+    compare_full(c, got, ref)
+    # the accumulated gradient is a sum over chunks: the same walk in another order agrees
+    dk2 = torch.zeros_like(dk_acc)
+    dv2 = torch.zeros_like(dv_acc)
+    for p0, n, sk in reversed(configs.chunk_plan(W, C)):
+        binding.bwd_chunked(t["q"][:, :, p0:p0 + n], t["k"][:, :, :sk], t["v"][:, :, :sk], t["do"][:, :, p0:p0 + n],
+                            LSE[:, :, p0:p0 + n], Delta[:, :, p0:p0 + n], dk2, dv2, scale=c.scale, causal=True,
+                            q_offset=p0)
+    torch.cuda.synchronize()
+    assert np.abs(dk2.cpu().numpy() - dk_acc.cpu().numpy()).max() <= 1e-5 * np.abs(got["dK"]).max()
