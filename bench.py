@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention training op on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+forward (O, LSE) -> preprocess (Delta) -> backward (dQ, dK, dV), back to back on
+one stream, through the C ABI. Inputs are resident in HBM before timing starts.
+
+The headline line is the DiT self-attention workload (B=1, Hq=16, Hkv=8,
+S=1542, D=128, bf16, pad mask): mask-adjusted fwd+bwd TFLOP/s (14 * D * N FLOPs
+per step, N = unmasked score pairs). Other workloads are reported under "extra".
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload dit_sa]
+                    [--extra lm_causal,dit_ca] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+METRIC = "attention fwd+bwd TFLOP/s (mask-adjusted) and % of MI355X bf16 MFMA peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dit_sa")
+    ap.add_argument("--extra", default="lm_causal,dit_ca")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Workload:
+    """Device buffers and the three calls of one step for a seeded case."""
+
+    def __init__(self, key: str):
+        import torch
+
+        from flash_attention_train_amd import accounting, binding, configs
+        self.key = key
+        self.case = c = configs.make(key)
+        self.pairs = accounting.case_pairs(c)
+        self.fwd_flops = accounting.fwd_flops(self.pairs, c.D)
+        self.bwd_flops = accounting.bwd_flops(self.pairs, c.D)
+        self.pre_bytes = accounting.preprocess_bytes(c.B, c.Hq, c.Sq, c.D, c.dtype)
+        dev = "cuda"
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.q, self.k, self.v, self.do = up(c.q), up(c.k), up(c.v), up(c.do)
+        self.mask = None if c.mask is None else torch.from_numpy(c.mask).to(dev)
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty(c.B, c.Hq, c.Sq, dtype=torch.float32, device=dev)
+        self.delta = torch.empty_like(self.lse)
+        self.dq = torch.empty_like(self.q)
+        self.dk = torch.empty_like(self.k)
+        self.dv = torch.empty_like(self.v)
+        nws = binding.bwd_workspace_bytes(self.q, self.k, scale=c.scale, causal=c.causal, q_offset=c.q_offset,
+                                          mask=self.mask)
+        self.ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+        self.B = binding
+
+    def fwd(self):
+        c = self.case
+        self.B.fwd(self.q, self.k, self.v, mask=self.mask, scale=c.scale, causal=c.causal, q_offset=c.q_offset,
+                   out=self.o, lse=self.lse)
+
+    def pre(self):
+        self.B.bwd_preprocess(self.o, self.do, delta=self.delta)
+
+    def bwd(self):
+        c = self.case
+        self.B.bwd(self.q, self.k, self.v, self.do, self.lse, self.delta, mask=self.mask, scale=c.scale,
+                   causal=c.causal, q_offset=c.q_offset, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
+
+    def step(self):
+        self.fwd()
+        self.pre()
+        self.bwd()
+
+
+def time_workload(w: Workload, steps: int, warmup: int) -> dict:
+    """Times `steps` whole steps (wall clock around synchronizes) and, inside the
+    same timed region, each call with HIP events on the stream it is launched on."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        w.step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        e = ev[i]
+        e[0].record(stream)
+        w.fwd()
+        e[1].record(stream)
+        w.pre()
+        e[2].record(stream)
+        w.bwd()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    pre_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    bwd_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    step_ms = wall * 1e3 / steps
+    total_flops = w.fwd_flops + w.bwd_flops
+    return {
+        "ms_per_step": step_ms,
+        "tflops": total_flops / (step_ms * 1e-3) / 1e12,
+        "fwd_ms_mean": float(fwd_ms.mean()), "pre_ms_mean": float(pre_ms.mean()), "bwd_ms_mean": float(bwd_ms.mean()),
+        "fwd_ms_median": float(np.median(fwd_ms)), "bwd_ms_median": float(np.median(bwd_ms)),
+        "fwd_tflops": w.fwd_flops / (fwd_ms.mean() * 1e-3) / 1e12,
+        "bwd_tflops": w.bwd_flops / (bwd_ms.mean() * 1e-3) / 1e12,
+        "fwdbwd_event_tflops": total_flops / ((fwd_ms + pre_ms + bwd_ms).mean() * 1e-3) / 1e12,
+        "pre_gbs": w.pre_bytes / (pre_ms.mean() * 1e-3) / 1e9,
+        "pairs": w.pairs,
+        "gflop_per_step": total_flops / 1e9,
+    }
+
+
+def cpu_baseline(key: str) -> dict:
+    """The oracle as it stands (fp64 C, all host cores) on one whole step of the
+    workload: fwd + bwd, mask-adjusted FLOPs per second."""
+    import oracle
+    from flash_attention_train_amd import accounting, configs
+    c = configs.make(key)
+    threads = oracle.default_threads()
+    m = None if c.mask is None else c.mask.astype(np.float64)
+    args = (c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), m)
+    t0 = time.perf_counter()
+    oracle.backward(*args, scale=c.scale, causal=c.causal, q_offset=c.q_offset, threads=threads)
+    dt = time.perf_counter() - t0
+    n = accounting.case_pairs(c)
+    flops = accounting.fwd_flops(n, c.D) + accounting.bwd_flops(n, c.D)
+    cpu = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"one whole fwd+bwd step of the {key} workload (all heads), float64, {dt:.1f} s",
+            "seconds": dt, "cpu": cpu}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the op and its measurement are single-device "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from flash_attention_train_amd import accounting, binding, configs
+    binding.lib()  # fail loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    log(f"[bench] device {torch.cuda.get_device_name(0)}; workload {args.workload}")
+    w = Workload(args.workload)
+    r = time_workload(w, args.steps, args.warmup)
+    log(f"[bench] {args.workload}: {r['ms_per_step']:.3f} ms/step, {r['tflops']:.1f} TFLOP/s")
+
+    extra = {}
+    for key in [k for k in args.extra.split(",") if k and k != args.workload]:
+        we = Workload(key)
+        re_ = time_workload(we, max(5, args.steps // 2), args.warmup)
+        re_["pct_of_peak"] = 100.0 * re_["tflops"] / accounting.MI355X_BF16_DENSE_TFLOPS
+        extra[key] = re_
+        log(f"[bench] {key}: {re_['ms_per_step']:.3f} ms/step, {re_['tflops']:.1f} TFLOP/s")
+        del we
+        torch.cuda.empty_cache()
+
+    peak = accounting.MI355X_BF16_DENSE_TFLOPS
+    achieved = r["bwd_tflops"]
+    line = {
+        "metric": METRIC,
+        "value": round(r["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs shaped like the workload; no datasets or weights)",
+        "config": {"workload": configs.WORKLOADS[args.workload].title, "global_batch": w.case.B,
+                   "seq_len": w.case.Sq, "unmasked_pairs": w.pairs, "gflop_per_step": round(r["gflop_per_step"], 3)},
+        "pct_of_peak": round(100.0 * r["tflops"] / peak, 2),
+        "roofline": {"kernel": "fa_train_bwd (dQ clear + backward + dQ convert)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None},
+        "breakdown": {k: round(v, 4) if isinstance(v, float) else v for k, v in r.items()},
+        "extra": extra,
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on the host cores ...")
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -31,7 +31,7 @@ class FaAttnParams(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("Sq", ctypes.c_int32),
                 ("Sk", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("q_offset", ctypes.c_int64), ("scale", ctypes.c_float), ("mask", ctypes.c_void_p),
-                ("mask_stride_b", ctypes.c_int64), ("mask_stride_q", ctypes.c_int64)]
+                ("mask_stride_b", ctypes.c_int64), ("mask_stride_q", ctypes.c_int64), ("config", ctypes.c_int32)]
 
 
 class FaError(RuntimeError):
@@ -111,7 +111,7 @@ def _stream_handle(stream) -> int:
 
 
 def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], causal: bool,
-                q_offset: Optional[int], mask: Optional[torch.Tensor]) -> FaAttnParams:
+                q_offset: Optional[int], mask: Optional[torch.Tensor], config: int = 0) -> FaAttnParams:
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Sk, Dk = k.shape
     if Bk != B or Dk != D:
@@ -121,7 +121,7 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
     if q_offset is None:
         q_offset = Sk - Sq if causal else 0
     p = FaAttnParams(B, Hq, Hkv, Sq, Sk, D, _dtype_code(q), int(bool(causal)), int(q_offset), float(scale),
-                     None, 0, 0)
+                     None, 0, 0, int(config))
     if mask is not None:
         if mask.dtype != torch.float32 or mask.dim() != 3 or mask.stride(2) != 1:
             raise ValueError("mask must be an fp32 [Bm, Sq, Sk] tensor with a contiguous last dimension")
@@ -133,9 +133,10 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
     return p
 
 
-def fwd(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, out=None, lse=None, stream=None):
+def fwd(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, out=None, lse=None, stream=None,
+        config=0):
     """Forward: returns (O, LSE). O has q's dtype and shape; LSE is fp32 [B, Hq, Sq]."""
-    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask)
+    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, config=config)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
@@ -150,7 +151,7 @@ def bwd_preprocess(o, dout, *, delta=None, stream=None):
     B, Hq, Sq, D = o.shape
     if delta is None:
         delta = torch.empty((B, Hq, Sq), dtype=torch.float32, device=o.device)
-    p = FaAttnParams(B, Hq, Hq, Sq, Sq, D, _dtype_code(o), 0, 0, 1.0, None, 0, 0)
+    p = FaAttnParams(B, Hq, Hq, Sq, Sq, D, _dtype_code(o), 0, 0, 1.0, None, 0, 0, 0)
     _check("fa_train_bwd_preprocess",
            lib().fa_train_bwd_preprocess(ctypes.byref(p), view4(o), view4(dout), view3(delta), _stream_handle(stream)))
     return delta

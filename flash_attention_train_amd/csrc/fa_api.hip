@@ -77,7 +77,8 @@ fa_status check_params(const fa_attn_params* p) {
   if (p->causal != 0 && p->causal != 1) return fail(FA_ERR_SHAPE, "causal must be 0 or 1");
   if (p->q_offset < -(int64_t(1) << 40) || p->q_offset > (int64_t(1) << 40))
     return fail(FA_ERR_SHAPE, "q_offset out of range");
-  if (!isfinite(p->scale)) return fail(FA_ERR_SHAPE, "scale must be finite");
+  if (!(p->scale > 0.f) || !isfinite(p->scale)) return fail(FA_ERR_SHAPE, "scale must be positive and finite");
+  if (p->config < 0 || p->config > 2) return fail(FA_ERR_SHAPE, "unknown kernel configuration %d", p->config);
   if (p->mask) {
     if (p->mask_stride_q < p->Sk) return fail(FA_ERR_STRIDE, "mask_stride_q (%lld) < Sk", (long long)p->mask_stride_q);
     if (p->mask_stride_b < 0) return fail(FA_ERR_STRIDE, "mask_stride_b is negative");
@@ -251,7 +252,17 @@ fa_status fa_train_fwd(const fa_attn_params* p, const fa_view* q, const fa_view*
   a.so = strides_of(o);
   a.lse_sb = lse->stride_b;
   a.lse_sh = lse->stride_h;
-  return hip_status(fa::launch_fwd(a, p->dtype == FA_BF16, stream), "forward");
+  a.inv_scale = 1.f / p->scale;
+  const uintptr_t mp = reinterpret_cast<uintptr_t>(p->mask);
+  a.mask_vec4 = p->mask && mp % 16 == 0 && p->mask_stride_q % 4 == 0 && p->mask_stride_b % 4 == 0;
+  if (p->dtype == FA_BF16) {
+    // variant 1 (32 query rows per wave, 64-key tiles, two waves per SIMD) measured
+    // faster than variant 2 (64 rows per wave, 32-key tiles, one wave per SIMD) on
+    // every workload shape tried; variant 2 stays selectable for tuning
+    const int variant = p->config ? p->config : 1;
+    return hip_status(fa::launch_fwd_bf16(a, variant, stream), "forward");
+  }
+  return hip_status(fa::launch_fwd(a, 0, stream), "forward");
 }
 
 fa_status fa_train_bwd_preprocess(const fa_attn_params* p, const fa_view* o, const fa_view* dout,

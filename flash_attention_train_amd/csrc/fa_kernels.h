@@ -34,6 +34,8 @@ struct FwdArgs {
   float* lse;
   Strides sq, sk, sv, so;
   int64_t lse_sb, lse_sh;
+  float inv_scale;  // 1 / scale (scale > 0)
+  int mask_vec4;    // the mask can be read 4 floats at a time (16-byte aligned rows)
 };
 
 struct PreArgs {
@@ -71,6 +73,7 @@ struct DqArgs {
 
 // launchers: return hipSuccess or the launch error
 hipError_t launch_fwd(const FwdArgs& args, int is_bf16, hipStream_t stream);
+hipError_t launch_fwd_bf16(const FwdArgs& args, int qb, hipStream_t stream);
 hipError_t launch_preprocess(const PreArgs& args, int is_bf16, hipStream_t stream);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& args, int is_bf16, hipStream_t stream);

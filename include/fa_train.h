@@ -89,11 +89,14 @@ typedef struct fa_attn_params {
     int32_t B, Hq, Hkv, Sq, Sk, D;
     int32_t dtype;        /* fa_dtype */
     int32_t causal;       /* 0 or 1: key j visible to query i only if j <= q_offset + i */
-    int64_t q_offset;     /* key position of query row 0 (>= 0; Sk - Sq for bottom-right causal) */
-    float scale;          /* multiplies <q, k>; usually 1/sqrt(D) */
+    int64_t q_offset;     /* key position of query row 0 (Sk - Sq for bottom-right causal; rows with
+                             q_offset + i < 0 see no key under causal masking) */
+    float scale;          /* multiplies <q, k>; must be > 0; usually 1/sqrt(D) */
     const float* mask;    /* optional additive mask [b][i][j], fp32; NULL = none */
     int64_t mask_stride_b;/* elements between batch entries; 0 = shared by the batch */
     int64_t mask_stride_q;/* elements between query rows (>= Sk) */
+    int32_t config;       /* kernel configuration: 0 = automatic choice; 1, 2 = query rows
+                             per wave in units of 32 for the bf16 forward (for tuning) */
 } fa_attn_params;
 
 /* Forward: writes O (dtype) and LSE (fp32, natural log). Fully masked rows get

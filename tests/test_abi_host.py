@@ -42,7 +42,7 @@ BASE = 0x7F0000000000  # fake, 256-byte aligned device addresses
 
 def params(**kw):
     a = dict(B=1, Hq=4, Hkv=2, Sq=64, Sk=64, D=64, dtype=B.FA_BF16, causal=0, q_offset=0, scale=0.125, mask=None,
-             mask_stride_b=0, mask_stride_q=0)
+             mask_stride_b=0, mask_stride_q=0, config=0)
     a.update(kw)
     return B.FaAttnParams(*(a[f] for f, _ in B.FaAttnParams._fields_))
 
@@ -80,6 +80,8 @@ FWD_ERRORS = [
     ("lse not contiguous", params(), {"lse": B.FaView(BASE + 4 * (1 << 24), 512, 128, 2)}, 4),
     ("null data", params(), {"v": view(2, H=2, data=0)}, 1),
     ("causal flag 2", params(causal=2), {}, 2),
+    ("negative scale", params(scale=-0.5), {}, 2),
+    ("unknown config", params(config=9), {}, 2),
     ("mask stride too small", params(mask=BASE + 9 * (1 << 24), mask_stride_q=32), {}, 4),
 ]
 

@@ -141,3 +141,18 @@ def test_chunked_walk_small():
                             q_offset=p0)
     torch.cuda.synchronize()
     assert np.abs(dk2.cpu().numpy() - dk_acc.cpu().numpy()).max() <= 1e-5 * np.abs(got["dK"]).max()
+
+
+@pytest.mark.parametrize("config", [1, 2])
+@pytest.mark.parametrize("name", ["dit_sa_ragged", "lm_causal_gqa4", "chunk_offset", "random_bias_bcast", "d64_bf16"])
+def test_forward_variants(name, config):
+    """Both bf16 forward configurations (32 or 64 query rows per wave) against the oracle."""
+    c = CASES[name]()
+    t = upload(c)
+    o, lse = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
+                         q_offset=c.q_offset, config=config)
+    torch.cuda.synchronize()
+    m = None if c.mask is None else c.mask.astype(np.float64)
+    O, L = oracle.forward(c.f64("q"), c.f64("k"), c.f64("v"), m, scale=c.scale, causal=c.causal,
+                          q_offset=c.q_offset)
+    compare_full(c, {"O": host64(o), "LSE": host64(lse)}, {"O": O, "LSE": L}, names=("O", "LSE"))
