@@ -31,7 +31,8 @@ class FaAttnParams(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("Sq", ctypes.c_int32),
                 ("Sk", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("q_offset", ctypes.c_int64), ("scale", ctypes.c_float), ("mask", ctypes.c_void_p),
-                ("mask_stride_b", ctypes.c_int64), ("mask_stride_q", ctypes.c_int64), ("config", ctypes.c_int32)]
+                ("mask_stride_b", ctypes.c_int64), ("mask_stride_q", ctypes.c_int64),
+                ("fwd_variant", ctypes.c_int32), ("kv_split", ctypes.c_int32), ("q_split", ctypes.c_int32)]
 
 
 class FaError(RuntimeError):
@@ -111,7 +112,8 @@ def _stream_handle(stream) -> int:
 
 
 def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], causal: bool,
-                q_offset: Optional[int], mask: Optional[torch.Tensor], config: int = 0) -> FaAttnParams:
+                q_offset: Optional[int], mask: Optional[torch.Tensor], fwd_variant: int = 0, kv_split: int = 0,
+                q_split: int = 0) -> FaAttnParams:
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Sk, Dk = k.shape
     if Bk != B or Dk != D:
@@ -121,7 +123,7 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
     if q_offset is None:
         q_offset = Sk - Sq if causal else 0
     p = FaAttnParams(B, Hq, Hkv, Sq, Sk, D, _dtype_code(q), int(bool(causal)), int(q_offset), float(scale),
-                     None, 0, 0, int(config))
+                     None, 0, 0, int(fwd_variant), int(kv_split), int(q_split))
     if mask is not None:
         if mask.dtype != torch.float32 or mask.dim() != 3 or mask.stride(2) != 1:
             raise ValueError("mask must be an fp32 [Bm, Sq, Sk] tensor with a contiguous last dimension")
@@ -134,9 +136,9 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
 
 
 def fwd(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, out=None, lse=None, stream=None,
-        config=0):
+        variant=0):
     """Forward: returns (O, LSE). O has q's dtype and shape; LSE is fp32 [B, Hq, Sq]."""
-    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, config=config)
+    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, fwd_variant=variant)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
@@ -151,28 +153,32 @@ def bwd_preprocess(o, dout, *, delta=None, stream=None):
     B, Hq, Sq, D = o.shape
     if delta is None:
         delta = torch.empty((B, Hq, Sq), dtype=torch.float32, device=o.device)
-    p = FaAttnParams(B, Hq, Hq, Sq, Sq, D, _dtype_code(o), 0, 0, 1.0, None, 0, 0, 0)
+    p = FaAttnParams(B, Hq, Hq, Sq, Sq, D, _dtype_code(o), 0, 0, 1.0, None, 0, 0, 0, 0, 0)
     _check("fa_train_bwd_preprocess",
            lib().fa_train_bwd_preprocess(ctypes.byref(p), view4(o), view4(dout), view3(delta), _stream_handle(stream)))
     return delta
 
 
-def bwd_workspace_bytes(q, k, *, scale=None, causal=False, q_offset=None, mask=None) -> int:
-    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask)
+def bwd_workspace_bytes(q, k, *, scale=None, causal=False, q_offset=None, mask=None, kv_split=0, q_split=0) -> int:
+    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
+                    q_split=q_split)
     return int(lib().fa_train_bwd_workspace_bytes(ctypes.byref(p)))
 
 
 def _workspace(p: FaAttnParams, device, workspace):
     need = int(lib().fa_train_bwd_workspace_bytes(ctypes.byref(p)))
+    if need == ctypes.c_size_t(-1).value:
+        need = 0  # invalid parameters: the call itself reports why
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
     return workspace, workspace.numel() * workspace.element_size()
 
 
 def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_offset=None, dq=None, dk=None,
-        dv=None, workspace=None, stream=None):
+        dv=None, workspace=None, stream=None, kv_split=0, q_split=0):
     """Backward: returns (dQ, dK, dV), each in q's dtype, overwritten."""
-    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask)
+    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
+                    q_split=q_split)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
@@ -184,10 +190,11 @@ def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_off
 
 
 def bwd_chunked(q, k, v, dout, lse, delta, dk_acc, dv_acc, *, mask=None, scale=None, causal=True, q_offset=None,
-                dq=None, workspace=None, stream=None):
+                dq=None, workspace=None, stream=None, kv_split=0, q_split=0):
     """Chunked backward: returns dQ for the chunk; ADDS dK/dV into the fp32 window
     accumulators ``dk_acc`` / ``dv_acc`` ([B, Hkv, >= Sk, D])."""
-    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask)
+    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
+                    q_split=q_split)
     if dk_acc.dtype != torch.float32 or dv_acc.dtype != torch.float32:
         raise TypeError("the window accumulators must be float32")
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq

@@ -78,7 +78,9 @@ fa_status check_params(const fa_attn_params* p) {
   if (p->q_offset < -(int64_t(1) << 40) || p->q_offset > (int64_t(1) << 40))
     return fail(FA_ERR_SHAPE, "q_offset out of range");
   if (!(p->scale > 0.f) || !isfinite(p->scale)) return fail(FA_ERR_SHAPE, "scale must be positive and finite");
-  if (p->config < 0 || p->config > 2) return fail(FA_ERR_SHAPE, "unknown kernel configuration %d", p->config);
+  if (p->fwd_variant < 0 || p->fwd_variant > 2) return fail(FA_ERR_SHAPE, "unknown forward variant %d", p->fwd_variant);
+  if (p->kv_split < 0 || p->kv_split > 64 || p->q_split < 0 || p->q_split > 64)
+    return fail(FA_ERR_SHAPE, "split hints must be in 0 .. 64");
   if (p->mask) {
     if (p->mask_stride_q < p->Sk) return fail(FA_ERR_STRIDE, "mask_stride_q (%lld) < Sk", (long long)p->mask_stride_q);
     if (p->mask_stride_b < 0) return fail(FA_ERR_STRIDE, "mask_stride_b is negative");
@@ -133,10 +135,55 @@ fa_status check_alias(const Extent* outs, int n_out, const char* const* out_name
   return FA_OK;
 }
 
-size_t workspace_bytes(const fa_attn_params* p) {
-  const size_t n = (size_t)p->B * p->Hq * p->Sq * p->D * sizeof(float);
-  return (n + 255) / 256 * 256;
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Split factors of the bf16 backward. Each split > 1 spreads one tile's walk over
+// several workgroups whose partial sums meet in fp32 atomics, so splits are only
+// used when the unsplit grid would leave compute units idle.
+void choose_splits(const fa_attn_params* p, bool accumulate, int* kv_split, int* q_split) {
+  const int64_t target = 512;  // about two workgroups per compute unit
+  const int64_t kv_units = (int64_t)((p->Sk + 127) / 128) * p->B * p->Hkv;
+  const int64_t q_units = (int64_t)((p->Sq + 127) / 128) * p->B * p->Hq;
+  const int64_t kv_pairs = (int64_t)((p->Sq + 63) / 64) * (p->Hq / p->Hkv);  // walk length of one key tile
+  const int64_t q_tiles = (p->Sk + 63) / 64;                                  // walk length of one query tile
+  int kv = 1, q = 1;
+  if (kv_units + q_units < target) {
+    kv = (int)std::min<int64_t>(std::min<int64_t>(kv_pairs, 64), (target + kv_units - 1) / kv_units);
+    q = (int)std::min<int64_t>(std::min<int64_t>(q_tiles, 64), (target + q_units - 1) / q_units);
+  }
+  (void)accumulate;
+  *kv_split = p->kv_split ? p->kv_split : std::max(kv, 1);
+  *q_split = p->q_split ? p->q_split : std::max(q, 1);
 }
+
+struct WsLayout {
+  size_t dq_off, dk_off, dv_off, total;
+  bool need_dq, need_dkdv;
+};
+
+// Workspace of the backward: fp32 accumulators for whatever the chosen
+// decomposition adds with atomics (dQ always for fp32 inputs).
+WsLayout workspace_layout(const fa_attn_params* p, bool accumulate) {
+  WsLayout w;
+  const size_t nq = (size_t)p->B * p->Hq * p->Sq * p->D * sizeof(float);
+  const size_t nk = (size_t)p->B * p->Hkv * p->Sk * p->D * sizeof(float);
+  if (p->dtype == FA_BF16) {
+    int kv, q;
+    choose_splits(p, accumulate, &kv, &q);
+    w.need_dq = q > 1;
+    w.need_dkdv = kv > 1 && !accumulate;
+  } else {
+    w.need_dq = true;
+    w.need_dkdv = false;
+  }
+  w.dq_off = 0;
+  w.dk_off = w.need_dq ? round256(nq) : 0;
+  w.dv_off = w.dk_off + (w.need_dkdv ? round256(nk) : 0);
+  w.total = w.dv_off + (w.need_dkdv ? round256(nk) : 0);
+  return w;
+}
+
+size_t workspace_bytes(const fa_attn_params* p) { return workspace_layout(p, false).total; }
 
 // Shared body of the two backward entry points.
 fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,
@@ -159,11 +206,14 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   const int gelt = accumulate ? 4 : elt;
   if ((s = check_view(dk, accumulate ? "dk_acc" : "dk", p->B, p->Hkv, p->Sk, p->D, gelt, true, true, &edk))) return s;
   if ((s = check_view(dv, accumulate ? "dv_acc" : "dv", p->B, p->Hkv, p->Sk, p->D, gelt, true, true, &edv))) return s;
-  const size_t need = workspace_bytes(p);
-  if (!workspace) return fail(FA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
-  if (workspace_bytes_given < need)
-    return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_given, need);
-  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(FA_ERR_ALIGN, "workspace is not 256-byte aligned");
+  const WsLayout wl = workspace_layout(p, accumulate);
+  const size_t need = wl.total;
+  if (need > 0) {
+    if (!workspace) return fail(FA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes_given < need)
+      return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_given, need);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(FA_ERR_ALIGN, "workspace is not 256-byte aligned");
+  }
   const uintptr_t wlo = reinterpret_cast<uintptr_t>(workspace);
   Extent ews = {wlo, wlo + need};
   Extent ins[8] = {eq, ek, ev, edo, el, ed, {0, 0}, {0, 0}};
@@ -184,7 +234,6 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   a.delta = static_cast<const float*>(delta->data);
   a.dk = dk->data;
   a.dv = dv->data;
-  a.dq_acc = static_cast<float*>(workspace);
   a.sq = strides_of(q);
   a.sk = strides_of(k);
   a.sv = strides_of(v);
@@ -196,8 +245,42 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   a.delta_sb = delta->stride_b;
   a.delta_sh = delta->stride_h;
   a.accumulate = accumulate ? 1 : 0;
+  a.inv_scale = 1.f / p->scale;
+  const uintptr_t mp = reinterpret_cast<uintptr_t>(p->mask);
+  a.mask_vec4 = p->mask && mp % 16 == 0 && p->mask_stride_q % 4 == 0 && p->mask_stride_b % 4 == 0;
   const int is_bf16 = p->dtype == FA_BF16;
   fa_status st;
+  if (is_bf16) {
+    char* ws = static_cast<char*>(workspace);
+    fa::BwdPlan plan;
+    int kv, q;
+    choose_splits(p, accumulate, &kv, &q);
+    fa::plan_bwd_bf16(a.a, kv, q, &plan);
+    a.dq_acc = wl.need_dq ? reinterpret_cast<float*>(ws + wl.dq_off) : nullptr;
+    plan.dk_acc = wl.need_dkdv ? reinterpret_cast<float*>(ws + wl.dk_off) : nullptr;
+    plan.dv_acc = wl.need_dkdv ? reinterpret_cast<float*>(ws + wl.dv_off) : nullptr;
+    plan.dq = dq->data;
+    plan.sdq = strides_of(dq);
+    const int64_t nq = (int64_t)p->B * p->Hq * p->Sq * p->D, nk = (int64_t)p->B * p->Hkv * p->Sk * p->D;
+    if (wl.need_dq && (st = hip_status(fa::launch_zero_f32(a.dq_acc, nq, stream), "dq clear"))) return st;
+    if (wl.need_dkdv) {
+      if ((st = hip_status(fa::launch_zero_f32(plan.dk_acc, nk, stream), "dk clear"))) return st;
+      if ((st = hip_status(fa::launch_zero_f32(plan.dv_acc, nk, stream), "dv clear"))) return st;
+    }
+    if ((st = hip_status(fa::launch_bwd_bf16(a, plan, stream), "backward"))) return st;
+    if (wl.need_dq) {
+      fa::DqArgs c = {p->B, p->Hq, p->Sq, p->D, a.dq_acc, dq->data, strides_of(dq), p->scale};
+      if ((st = hip_status(fa::launch_dq_convert(c, 1, stream), "dq convert"))) return st;
+    }
+    if (wl.need_dkdv) {
+      fa::DqArgs ck = {p->B, p->Hkv, p->Sk, p->D, plan.dk_acc, dk->data, strides_of(dk), 1.f};
+      fa::DqArgs cv = {p->B, p->Hkv, p->Sk, p->D, plan.dv_acc, dv->data, strides_of(dv), 1.f};
+      if ((st = hip_status(fa::launch_dq_convert(ck, 1, stream), "dk convert"))) return st;
+      if ((st = hip_status(fa::launch_dq_convert(cv, 1, stream), "dv convert"))) return st;
+    }
+    return FA_OK;
+  }
+  a.dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.dq_off);
   if ((st = hip_status(fa::launch_zero_f32(a.dq_acc, (int64_t)p->B * p->Hq * p->Sq * p->D, stream), "dq clear")))
     return st;
   if ((st = hip_status(fa::launch_bwd(a, is_bf16, stream), "backward"))) return st;
@@ -259,7 +342,7 @@ fa_status fa_train_fwd(const fa_attn_params* p, const fa_view* q, const fa_view*
     // variant 1 (32 query rows per wave, 64-key tiles, two waves per SIMD) measured
     // faster than variant 2 (64 rows per wave, 32-key tiles, one wave per SIMD) on
     // every workload shape tried; variant 2 stays selectable for tuning
-    const int variant = p->config ? p->config : 1;
+    const int variant = p->fwd_variant ? p->fwd_variant : 1;
     return hip_status(fa::launch_fwd_bf16(a, variant, stream), "forward");
   }
   return hip_status(fa::launch_fwd(a, 0, stream), "forward");
@@ -300,7 +383,7 @@ fa_status fa_train_bwd_preprocess(const fa_attn_params* p, const fa_view* o, con
 }
 
 size_t fa_train_bwd_workspace_bytes(const fa_attn_params* p) {
-  if (check_params(p) != FA_OK) return 0;
+  if (check_params(p) != FA_OK) return (size_t)-1;
   return workspace_bytes(p);
 }
 

@@ -1,0 +1,489 @@
+// fa_bwd_bf16.hip -- the bf16 backward: dQ, dK, dV in one launch.
+//
+// The backward recomputes P from the forward's LSE tile by tile and sums dK/dV
+// over each query-head group (llama.cpp pull request 57, commit 86c140d: "LSE,
+// D, then grads per tile; GQA group-sum"). On gfx950 it is split into two kinds
+// of workgroups that run side by side in one grid, so that neither needs the
+// other's results and no score tile ever travels through LDS or memory:
+//
+//  dK/dV workgroups (KV-stationary): 4 waves x 32 keys own a 128-key tile of one
+//    KV head. They walk the (query head of the group, 64-row query tile) pairs
+//    that can see the keys, with the Q and dO tiles staged in LDS (double-
+//    buffered through registers) and shared by the waves. Per 32-row block:
+//      S  = Q K^T, dP = dO V^T   (A: Q / dO rows from LDS, B: K / V in registers)
+//      P  = exp2(S c + M log2e - LSE log2e), dS = P (dP - Delta)
+//      dV += P^T dO, dK += dS^T Q  (A: P / dS straight from the accumulators,
+//                                   B: dO^T / Q^T by LDS transpose reads)
+//  dQ workgroups (Q-stationary): 4 waves x 32 rows own a 128-row query tile of
+//    one head and walk its visible 64-key tiles (K and V staged in LDS, double-
+//    buffered), computing S^T = K Q^T and dP^T = V dO^T so that each lane holds
+//    one query row; dS^T then feeds dQ += dS K directly as the A operand, with
+//    the K operand read by LDS transpose reads.
+//
+// When a problem has too few tiles to fill the GPU, the dK/dV walk is split over
+// several workgroups per key tile and the dQ walk over several per query tile;
+// split partial sums are added with fp32 atomics into fp32 accumulators (a
+// workspace that a convert pass turns into the output dtype, or, for the chunked
+// walk, the caller's window accumulators). Unsplit work stores its results
+// directly. Masked entries get P = 0 exactly, so fully masked rows and key
+// columns end with exactly zero gradients ("Flash Attn Training" skill page,
+// section 6, traps 8 and 9).
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+namespace {
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr int KV_BN = 128;  // keys per dK/dV workgroup
+constexpr int KV_BM = 64;   // query rows per staged tile of the dK/dV walk
+constexpr int Q_BM = 128;   // query rows per dQ workgroup
+constexpr int Q_BN = 64;    // keys per staged tile of the dQ walk
+
+__device__ __forceinline__ f32x16 zeros16() {
+  f32x16 z;
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ bf16x4 tr_read(const bf16* lds_base, int elem_offset) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)((__attribute__((address_space(3))) bf16*)lds_base + elem_offset));
+}
+
+__device__ __forceinline__ void atomic_add_f32(float* p, float v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV workgroup
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, bool MASK>
+__device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
+  constexpr int RS = D + 8;  // LDS row stride (elements)
+  constexpr int DS = D / 16, DB = D / 32;
+  constexpr int CPT = KV_BM * D / 8 / 256;  // 16-byte chunks per thread per tensor
+  bf16* q_lds = reinterpret_cast<bf16*>(smem);                 // [2][KV_BM * RS]
+  bf16* do_lds = q_lds + 2 * KV_BM * RS;                       // [2][KV_BM * RS]
+  float* lse_lds = reinterpret_cast<float*>(do_lds + 2 * KV_BM * RS);  // [2][KV_BM]
+  float* dlt_lds = lse_lds + 2 * KV_BM;                        // [2][KV_BM]
+
+  const AttnShape& a = args.a;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, r32 = lane & 31;
+  // unit -> (key tile, batch, kv head, split); key tiles vary slowest so that the
+  // long causal tiles (small key index) are dispatched first
+  const int per_tile = a.B * a.Hkv * plan.kv_split;
+  const int kt = unit / per_tile;
+  int rem = unit % per_tile;
+  const int split = rem % plan.kv_split;
+  rem /= plan.kv_split;
+  const int hk = rem % a.Hkv, b = rem / a.Hkv;
+  const int n0 = kt * KV_BN;
+  const int key = n0 + 32 * wave + r32;
+  const float cs = a.scale * kLog2e;
+
+  const bf16* K = static_cast<const bf16*>(args.k) + b * args.sk.b + hk * args.sk.h;
+  const bf16* V = static_cast<const bf16*>(args.v) + b * args.sv.b + hk * args.sv.h;
+  bf16x8 kf[DS], vf[DS];
+  for (int s = 0; s < DS; ++s) {
+    if (key < a.Sk) {
+      kf[s] = *reinterpret_cast<const bf16x8*>(K + (int64_t)key * args.sk.s + 16 * s + 8 * g);
+      vf[s] = *reinterpret_cast<const bf16x8*>(V + (int64_t)key * args.sv.s + 16 * s + 8 * g);
+    } else {
+      zero(kf[s]);
+      zero(vf[s]);
+    }
+  }
+  f32x16 dk[DB], dv[DB];
+  for (int db = 0; db < DB; ++db) {
+    dk[db] = zeros16();
+    dv[db] = zeros16();
+  }
+
+  // the (head, query tile) pairs this workgroup walks: query tiles qt0 .. nqt - 1 of
+  // every head of the group, pair p = (qt - qt0) * G + (h - hk G), p = split (mod kv_split)
+  const int nqt = (a.Sq + KV_BM - 1) / KV_BM;
+  int qt0 = 0;
+  if (CAUSAL) {
+    const int64_t first_row = (int64_t)n0 - a.q_offset;  // rows i >= n0 - q_offset see a key here
+    qt0 = first_row <= 0 ? 0 : (int)((first_row / KV_BM) < nqt ? first_row / KV_BM : nqt);
+  }
+  const int npairs = (nqt - qt0) * a.G;
+
+  bf16x8 qpre[CPT], dpre[CPT];
+  float lpre = 0.f;
+  auto pair_of = [&](int p, int& h, int& q0) {
+    h = hk * a.G + p % a.G;
+    q0 = (qt0 + p / a.G) * KV_BM;
+  };
+  auto load_pair = [&](int p) {
+    int h, q0;
+    pair_of(p, h, q0);
+    const bf16* Q = static_cast<const bf16*>(args.q) + b * args.sq.b + h * args.sq.h;
+    const bf16* dO = static_cast<const bf16*>(args.dout) + b * args.sdo.b + h * args.sdo.h;
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      const int row = q0 + c / (D / 8), d0 = (c % (D / 8)) * 8;
+      if (row < a.Sq) {
+        qpre[i] = *reinterpret_cast<const bf16x8*>(Q + (int64_t)row * args.sq.s + d0);
+        dpre[i] = *reinterpret_cast<const bf16x8*>(dO + (int64_t)row * args.sdo.s + d0);
+      } else {
+        zero(qpre[i]);
+        zero(dpre[i]);
+      }
+    }
+    if (tid < 2 * KV_BM) {
+      const int row = q0 + (tid % KV_BM);
+      if (row < a.Sq)
+        lpre = tid < KV_BM ? args.lse[b * args.lse_sb + h * args.lse_sh + row] * kLog2e
+                           : args.delta[b * args.delta_sb + h * args.delta_sh + row];
+      else
+        lpre = 0.f;
+    }
+  };
+  auto store_pair = [&](int buf) {
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c / (D / 8), d0 = (c % (D / 8)) * 8;
+      *reinterpret_cast<bf16x8*>(q_lds + buf * KV_BM * RS + row * RS + d0) = qpre[i];
+      *reinterpret_cast<bf16x8*>(do_lds + buf * KV_BM * RS + row * RS + d0) = dpre[i];
+    }
+    if (tid < KV_BM)
+      lse_lds[buf * KV_BM + tid] = lpre;
+    else if (tid < 2 * KV_BM)
+      dlt_lds[buf * KV_BM + tid - KV_BM] = lpre;
+  };
+
+  const int G16 = lane >> 4, L16 = lane & 15;
+  const int tr_row = L16 >> 2, tr_col = 16 * (G16 & 1) + 4 * (L16 & 3);
+
+  int p = split;
+  if (p < npairs) {
+    load_pair(p);
+    store_pair(0);
+  }
+  __syncthreads();
+  for (int it = 0; p < npairs; ++it, p += plan.kv_split) {
+    const int buf = it & 1;
+    const int pn = p + plan.kv_split;
+    if (pn < npairs) load_pair(pn);
+    int h, q0;
+    pair_of(p, h, q0);
+    const bf16* qb_lds = q_lds + buf * KV_BM * RS;
+    const bf16* db_lds = do_lds + buf * KV_BM * RS;
+    const float* lse_b = lse_lds + buf * KV_BM;
+    const float* dlt_b = dlt_lds + buf * KV_BM;
+    bool edge = q0 + KV_BM > a.Sq || n0 + KV_BN > a.Sk;
+    if (CAUSAL) edge = edge || ((int64_t)n0 + KV_BN - 1 > a.q_offset + q0);
+
+    for (int qb = 0; qb < KV_BM / 32; ++qb) {
+      f32x16 sacc = zeros16(), dpacc = zeros16();
+      for (int s = 0; s < DS; ++s) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb_lds + (32 * qb + r32) * RS + 16 * s + 8 * g);
+        const bf16x8 da = *reinterpret_cast<const bf16x8*>(db_lds + (32 * qb + r32) * RS + 16 * s + 8 * g);
+        mma(sacc, qa, kf[s]);
+        mma(dpacc, da, vf[s]);
+      }
+      // lane (key, half g), register r -> query row 32 qb + 8 (r/4) + 4 g + r%4
+      for (int rr = 0; rr < 4; ++rr) {
+        const int ql4 = 32 * qb + 8 * rr + 4 * g;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_b + ql4);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt_b + ql4);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rr + e;
+          float x = sacc[r];
+          bool vis = true;
+          if (MASK || edge) {
+            const int qi = q0 + ql4 + e;
+            vis = key < a.Sk && qi < a.Sq;
+            if (CAUSAL) vis = vis && ((int64_t)key <= a.q_offset + qi);
+            if (MASK && vis) x += a.mask[b * a.mask_sb + (int64_t)qi * a.mask_sq + key] * args.inv_scale;
+          }
+          const float pv = vis ? fast_exp2(fmaf(x, cs, -l4[e])) : 0.f;
+          sacc[r] = pv;
+          dpacc[r] = pv * (dpacc[r] - d4[e]);
+        }
+      }
+      // dV += P^T dO, dK += dS^T Q; registers 8 hh .. 8 hh + 7 hold rows
+      // 32 qb + 16 hh + 8 t + 4 g + e, exactly the rows each transpose read returns
+      for (int hh = 0; hh < 2; ++hh) {
+        bf16x8 pa, dsa;
+        pack8(pa, sacc, 8 * hh);
+        pack8(dsa, dpacc, 8 * hh);
+        const int rbase = 32 * qb + 16 * hh + 4 * g + tr_row;
+        for (int db = 0; db < DB; ++db) {
+          const int col = 32 * db + tr_col;
+          const bf16x4 d0 = tr_read(db_lds, rbase * RS + col);
+          const bf16x4 d1 = tr_read(db_lds, (rbase + 8) * RS + col);
+          const bf16x4 q0v = tr_read(qb_lds, rbase * RS + col);
+          const bf16x4 q1v = tr_read(qb_lds, (rbase + 8) * RS + col);
+          const bf16x8 dob = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+          const bf16x8 qbt = {q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
+          mma(dv[db], pa, dob);
+          mma(dk[db], dsa, qbt);
+        }
+      }
+    }
+    if (pn < npairs) store_pair(buf ^ 1);
+    __syncthreads();
+  }
+
+  // results: accumulator row = key 8 (r/4) + 4 g + r%4 of this wave, column d = 32 db + r32
+  const bool atomic = plan.kv_split > 1;
+  for (int db = 0; db < DB; ++db) {
+    for (int r = 0; r < 16; ++r) {
+      const int kk = n0 + 32 * wave + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (kk >= a.Sk) continue;
+      const int d = 32 * db + r32;
+      const float vk = dk[db][r] * a.scale, vv = dv[db][r];
+      if (args.accumulate || atomic) {
+        float* pk;
+        float* pv;
+        if (args.accumulate) {
+          pk = static_cast<float*>(args.dk) + b * args.sdk.b + hk * args.sdk.h + (int64_t)kk * args.sdk.s + d;
+          pv = static_cast<float*>(args.dv) + b * args.sdv.b + hk * args.sdv.h + (int64_t)kk * args.sdv.s + d;
+        } else {
+          const int64_t o = (((int64_t)b * a.Hkv + hk) * a.Sk + kk) * D + d;
+          pk = plan.dk_acc + o;
+          pv = plan.dv_acc + o;
+        }
+        if (atomic) {
+          atomic_add_f32(pk, vk);
+          atomic_add_f32(pv, vv);
+        } else {
+          *pk += vk;
+          *pv += vv;
+        }
+      } else {
+        bf16* pk = static_cast<bf16*>(args.dk) + b * args.sdk.b + hk * args.sdk.h + (int64_t)kk * args.sdk.s + d;
+        bf16* pv = static_cast<bf16*>(args.dv) + b * args.sdv.b + hk * args.sdv.h + (int64_t)kk * args.sdv.s + d;
+        *pk = (bf16)vk;
+        *pv = (bf16)vv;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ workgroup
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, bool MASK>
+__device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
+  constexpr int RS = D + 8;
+  constexpr int DS = D / 16, DB = D / 32;
+  constexpr int CPT = Q_BN * D / 8 / 256;
+  bf16* k_lds = reinterpret_cast<bf16*>(smem);  // [2][Q_BN * RS]
+  bf16* v_lds = k_lds + 2 * Q_BN * RS;          // [2][Q_BN * RS]
+
+  const AttnShape& a = args.a;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, r32 = lane & 31;
+  // unit -> (query tile, batch, head, split); the last query tiles (longest under
+  // a causal mask) are dispatched first
+  const int nqt = (a.Sq + Q_BM - 1) / Q_BM;
+  const int per_tile = a.B * a.Hq * plan.q_split;
+  const int qt = nqt - 1 - unit / per_tile;
+  int rem = unit % per_tile;
+  const int split = rem % plan.q_split;
+  rem /= plan.q_split;
+  const int h = rem % a.Hq, b = rem / a.Hq;
+  const int hk = h / a.G;
+  const int q0 = qt * Q_BM;
+  const int qw = q0 + 32 * wave;
+  const int row = qw + r32;
+  const float cs = a.scale * kLog2e;
+
+  const bf16* Q = static_cast<const bf16*>(args.q) + b * args.sq.b + h * args.sq.h;
+  const bf16* dO = static_cast<const bf16*>(args.dout) + b * args.sdo.b + h * args.sdo.h;
+  const bf16* K = static_cast<const bf16*>(args.k) + b * args.sk.b + hk * args.sk.h;
+  const bf16* V = static_cast<const bf16*>(args.v) + b * args.sv.b + hk * args.sv.h;
+  bf16x8 qf[DS], df[DS];
+  for (int s = 0; s < DS; ++s) {
+    if (row < a.Sq) {
+      qf[s] = *reinterpret_cast<const bf16x8*>(Q + (int64_t)row * args.sq.s + 16 * s + 8 * g);
+      df[s] = *reinterpret_cast<const bf16x8*>(dO + (int64_t)row * args.sdo.s + 16 * s + 8 * g);
+    } else {
+      zero(qf[s]);
+      zero(df[s]);
+    }
+  }
+  float lse2 = 0.f, dlt = 0.f;
+  if (row < a.Sq) {
+    lse2 = args.lse[b * args.lse_sb + h * args.lse_sh + row] * kLog2e;
+    dlt = args.delta[b * args.delta_sb + h * args.delta_sh + row];
+  }
+  const float* Mrow = nullptr;
+  if (MASK && row < a.Sq) Mrow = a.mask + b * a.mask_sb + (int64_t)row * a.mask_sq;
+
+  f32x16 dq[DB];
+  for (int db = 0; db < DB; ++db) dq[db] = zeros16();
+
+  const int nkt = (a.Sk + Q_BN - 1) / Q_BN;
+  int kt_end = nkt;
+  if (CAUSAL) {
+    const int64_t last_key = a.q_offset + q0 + Q_BM - 1;
+    kt_end = last_key < 0 ? 0 : (int)((last_key / Q_BN + 1) < nkt ? (last_key / Q_BN + 1) : nkt);
+  }
+
+  bf16x8 kpre[CPT], vpre[CPT];
+  auto load_tile = [&](int kt) {
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      const int kk = kt * Q_BN + c / (D / 8), d0 = (c % (D / 8)) * 8;
+      if (kk < a.Sk) {
+        kpre[i] = *reinterpret_cast<const bf16x8*>(K + (int64_t)kk * args.sk.s + d0);
+        vpre[i] = *reinterpret_cast<const bf16x8*>(V + (int64_t)kk * args.sv.s + d0);
+      } else {
+        zero(kpre[i]);
+        zero(vpre[i]);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      const int rr = c / (D / 8), d0 = (c % (D / 8)) * 8;
+      *reinterpret_cast<bf16x8*>(k_lds + buf * Q_BN * RS + rr * RS + d0) = kpre[i];
+      *reinterpret_cast<bf16x8*>(v_lds + buf * Q_BN * RS + rr * RS + d0) = vpre[i];
+    }
+  };
+
+  const int G16 = lane >> 4, L16 = lane & 15;
+  const int tr_row = L16 >> 2, tr_col = 16 * (G16 & 1) + 4 * (L16 & 3);
+
+  int kt = split;
+  if (kt < kt_end) {
+    load_tile(kt);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int it = 0; kt < kt_end; ++it, kt += plan.q_split) {
+    const int buf = it & 1;
+    const int ktn = kt + plan.q_split;
+    if (ktn < kt_end) load_tile(ktn);
+    const bf16* kb_lds = k_lds + buf * Q_BN * RS;
+    const bf16* vb_lds = v_lds + buf * Q_BN * RS;
+    const int key0 = kt * Q_BN;
+    bool edge = key0 + Q_BN > a.Sk || qw + 32 > a.Sq;
+    if (CAUSAL) edge = edge || ((int64_t)key0 + Q_BN - 1 > a.q_offset + qw);
+
+    f32x16 st[2], dpt[2];
+    for (int kb = 0; kb < 2; ++kb) {
+      st[kb] = zeros16();
+      dpt[kb] = zeros16();
+      for (int s = 0; s < DS; ++s) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb_lds + (32 * kb + r32) * RS + 16 * s + 8 * g);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vb_lds + (32 * kb + r32) * RS + 16 * s + 8 * g);
+        mma(st[kb], ka, qf[s]);
+        mma(dpt[kb], va, df[s]);
+      }
+    }
+    // lane (query row, half g), register r -> key 32 kb + 8 (r/4) + 4 g + r%4
+    bf16x8 dsf[2][2];
+    for (int kb = 0; kb < 2; ++kb) {
+      for (int rr = 0; rr < 4; ++rr) {
+        const int k4 = key0 + 32 * kb + 8 * rr + 4 * g;
+        float mv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (MASK && Mrow) {
+          if (k4 + 3 < a.Sk && args.mask_vec4) {
+            const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mrow + k4);
+            mv[0] = m4[0]; mv[1] = m4[1]; mv[2] = m4[2]; mv[3] = m4[3];
+          } else {
+            for (int e = 0; e < 4; ++e) mv[e] = (k4 + e < a.Sk) ? Mrow[k4 + e] : 0.f;
+          }
+        }
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rr + e;
+          float x = st[kb][r];
+          bool vis = true;
+          if (MASK || edge) {
+            vis = k4 + e < a.Sk && row < a.Sq;
+            if (CAUSAL) vis = vis && ((int64_t)(k4 + e) <= a.q_offset + row);
+            if (MASK) x += mv[e] * args.inv_scale;
+          }
+          const float pv = vis ? fast_exp2(fmaf(x, cs, -lse2)) : 0.f;
+          st[kb][r] = pv * (dpt[kb][r] - dlt);
+        }
+      }
+      pack8(dsf[kb][0], st[kb], 0);
+      pack8(dsf[kb][1], st[kb], 8);
+    }
+    // dQ += dS K: A = dS (registers 8 hh .. of key block kb: keys 32 kb + 16 hh + 8 t + 4 g + e),
+    // B = K rows of the same keys, column d, by transpose reads
+    for (int kb = 0; kb < 2; ++kb) {
+      for (int hh = 0; hh < 2; ++hh) {
+        const int rbase = 32 * kb + 16 * hh + 4 * g + tr_row;
+        for (int db = 0; db < DB; ++db) {
+          const bf16x4 lo = tr_read(kb_lds, rbase * RS + 32 * db + tr_col);
+          const bf16x4 hi = tr_read(kb_lds, (rbase + 8) * RS + 32 * db + tr_col);
+          const bf16x8 kbt = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          mma(dq[db], dsf[kb][hh], kbt);
+        }
+      }
+    }
+    if (ktn < kt_end) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // dQ accumulator: lane (d = 32 db + r32, half g), register r -> row 8 (r/4) + 4 g + r%4 of the wave
+  for (int db = 0; db < DB; ++db) {
+    for (int r = 0; r < 16; ++r) {
+      const int qi = qw + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (qi >= a.Sq) continue;
+      const int d = 32 * db + r32;
+      if (plan.q_split > 1) {
+        atomic_add_f32(args.dq_acc + (((int64_t)b * a.Hq + h) * a.Sq + qi) * D + d, dq[db][r]);
+      } else {
+        bf16* pq = static_cast<bf16*>(plan.dq) + b * plan.sdq.b + h * plan.sdq.h + (int64_t)qi * plan.sdq.s + d;
+        *pq = (bf16)(dq[db][r] * a.scale);
+      }
+    }
+  }
+}
+
+template <int D, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(const BwdArgs args, const BwdPlan plan) {
+  constexpr int KV_LDS = 2 * 2 * KV_BM * (D + 8) * 2 + 4 * KV_BM * 4;
+  constexpr int Q_LDS = 2 * 2 * Q_BN * (D + 8) * 2;
+  __shared__ __attribute__((aligned(16))) char smem[KV_LDS > Q_LDS ? KV_LDS : Q_LDS];
+  const int blk = blockIdx.x;
+  if (blk < plan.n_kv_units)
+    dkdv_unit<D, CAUSAL, MASK>(args, plan, blk, smem);
+  else
+    dq_unit<D, CAUSAL, MASK>(args, plan, blk - plan.n_kv_units, smem);
+}
+
+template <int D>
+hipError_t launch_t(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream) {
+  const dim3 grid(plan.n_kv_units + plan.n_q_units);
+  const bool causal = args.a.causal != 0, mask = args.a.mask != nullptr;
+  if (causal && mask)
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, true, true>), grid, dim3(256), 0, stream, args, plan);
+  else if (causal)
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, true, false>), grid, dim3(256), 0, stream, args, plan);
+  else if (mask)
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, false, true>), grid, dim3(256), 0, stream, args, plan);
+  else
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, false, false>), grid, dim3(256), 0, stream, args, plan);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, BwdPlan* plan) {
+  const int nkt = (a.Sk + KV_BN - 1) / KV_BN;
+  const int nqt = (a.Sq + Q_BM - 1) / Q_BM;
+  plan->kv_split = kv_split;
+  plan->q_split = q_split;
+  plan->n_kv_units = nkt * a.B * a.Hkv * kv_split;
+  plan->n_q_units = nqt * a.B * a.Hq * q_split;
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream) {
+  return args.a.D == 64 ? launch_t<64>(args, plan, stream) : launch_t<128>(args, plan, stream);
+}
+
+}  // namespace fa

@@ -61,6 +61,20 @@ struct BwdArgs {
   Strides sq, sk, sv, sdo, sdk, sdv;
   int64_t lse_sb, lse_sh, delta_sb, delta_sh;
   int accumulate;  // 1: dK/dV are fp32 accumulators and receive +=, 0: overwrite in dtype
+  float inv_scale; // 1 / scale
+  int mask_vec4;   // the mask can be read 4 floats at a time
+};
+
+// Work decomposition of the bf16 backward (one launch, two kinds of workgroups).
+struct BwdPlan {
+  int kv_split;    // workgroups sharing one 128-key tile's dK/dV walk (> 1: fp32 atomics)
+  int q_split;     // workgroups sharing one 128-row query tile's dQ walk (> 1: fp32 atomics)
+  int n_kv_units;  // dK/dV workgroups (launched first)
+  int n_q_units;   // dQ workgroups
+  float* dk_acc;   // fp32 [B, Hkv, Sk, D] workspace when kv_split > 1 and not accumulating
+  float* dv_acc;
+  void* dq;        // dQ output (dtype) written directly when q_split == 1
+  Strides sdq;
 };
 
 struct DqArgs {
@@ -78,5 +92,7 @@ hipError_t launch_preprocess(const PreArgs& args, int is_bf16, hipStream_t strea
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& args, int is_bf16, hipStream_t stream);
 hipError_t launch_dq_convert(const DqArgs& args, int is_bf16, hipStream_t stream);
+void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, BwdPlan* plan);
+hipError_t launch_bwd_bf16(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream);
 
 }  // namespace fa

@@ -95,8 +95,13 @@ typedef struct fa_attn_params {
     const float* mask;    /* optional additive mask [b][i][j], fp32; NULL = none */
     int64_t mask_stride_b;/* elements between batch entries; 0 = shared by the batch */
     int64_t mask_stride_q;/* elements between query rows (>= Sk) */
-    int32_t config;       /* kernel configuration: 0 = automatic choice; 1, 2 = query rows
-                             per wave in units of 32 for the bf16 forward (for tuning) */
+    /* Work decomposition hints, 0 = automatic (the normal setting; other values are
+     * for tuning and give the same results up to fp32 summation order): */
+    int32_t fwd_variant;  /* bf16 forward: 1 = 32 query rows per wave, 2 = 64 rows */
+    int32_t kv_split;     /* bf16 backward: workgroups sharing one 128-key tile's dK/dV
+                             walk, 1 .. 64 (> 1 adds partial sums with fp32 atomics) */
+    int32_t q_split;      /* bf16 backward: workgroups sharing one 128-row query tile's dQ
+                             walk, 1 .. 64 (> 1 adds partial sums with fp32 atomics) */
 } fa_attn_params;
 
 /* Forward: writes O (dtype) and LSE (fp32, natural log). Fully masked rows get
@@ -109,8 +114,8 @@ fa_status fa_train_fwd(const fa_attn_params* p, const fa_view* q, const fa_view*
 fa_status fa_train_bwd_preprocess(const fa_attn_params* p, const fa_view* o, const fa_view* dout,
                                   const fa_view* delta, hipStream_t stream);
 
-/* Bytes of device workspace fa_train_bwd / fa_train_bwd_chunked need for p
- * (an fp32 dQ accumulator). 0 if p is invalid. */
+/* Bytes of device workspace fa_train_bwd / fa_train_bwd_chunked need for p (fp32
+ * accumulators for split work; may be 0). Returns (size_t)-1 if p is invalid. */
 size_t fa_train_bwd_workspace_bytes(const fa_attn_params* p);
 
 /* Backward: OVERWRITES dQ, dK, dV (dtype). Reads Q, K, V, dO, the forward's LSE and

@@ -41,14 +41,14 @@ def upload(c: Case) -> dict:
     return d
 
 
-def run_gpu(c: Case, t: dict | None = None) -> dict:
+def run_gpu(c: Case, t: dict | None = None, **bwd_kw) -> dict:
     """fwd -> preprocess -> bwd on the GPU; returns float64 host copies."""
     t = t or upload(c)
     o, lse = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
                          q_offset=c.q_offset)
     delta = binding.bwd_preprocess(o, t["do"])
     dq, dk, dv = binding.bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, mask=t["mask"], scale=c.scale,
-                             causal=c.causal, q_offset=c.q_offset)
+                             causal=c.causal, q_offset=c.q_offset, **bwd_kw)
     torch.cuda.synchronize()
     return {"O": host64(o), "LSE": host64(lse), "Delta": host64(delta), "dQ": host64(dq), "dK": host64(dk),
             "dV": host64(dv)}

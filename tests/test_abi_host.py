@@ -42,7 +42,7 @@ BASE = 0x7F0000000000  # fake, 256-byte aligned device addresses
 
 def params(**kw):
     a = dict(B=1, Hq=4, Hkv=2, Sq=64, Sk=64, D=64, dtype=B.FA_BF16, causal=0, q_offset=0, scale=0.125, mask=None,
-             mask_stride_b=0, mask_stride_q=0, config=0)
+             mask_stride_b=0, mask_stride_q=0, fwd_variant=0, kv_split=0, q_split=0)
     a.update(kw)
     return B.FaAttnParams(*(a[f] for f, _ in B.FaAttnParams._fields_))
 
@@ -81,7 +81,8 @@ FWD_ERRORS = [
     ("null data", params(), {"v": view(2, H=2, data=0)}, 1),
     ("causal flag 2", params(causal=2), {}, 2),
     ("negative scale", params(scale=-0.5), {}, 2),
-    ("unknown config", params(config=9), {}, 2),
+    ("unknown forward variant", params(fwd_variant=9), {}, 2),
+    ("split out of range", params(kv_split=65), {}, 2),
     ("mask stride too small", params(mask=BASE + 9 * (1 << 24), mask_stride_q=32), {}, 4),
 ]
 
@@ -108,8 +109,10 @@ def bwd_call(p, accumulate=False, ws=None, ws_bytes=None, **over):
 
 
 def test_backward_rejects():
-    p = params()
+    p = params(q_split=2, kv_split=1)
     assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(p)) == 1 * 4 * 64 * 64 * 4
+    assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(params(q_split=1, kv_split=1))) == 0
+    assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(params(q_split=1, kv_split=2))) == 2 * 2 * 64 * 64 * 4
     assert bwd_call(p, ws=0) == 8
     assert bwd_call(p, ws_bytes=100) == 8
     assert bwd_call(p, ws=BASE + 12 * (1 << 24) + 16) == 5
@@ -120,7 +123,7 @@ def test_backward_rejects():
     assert bwd_call(p, dk=view(7, H=2, stride_h=0)) == 4  # dK heads collapse onto each other
     assert bwd_call(params(Hkv=3)) == 2
     assert bwd_call(p, accumulate=True, dk=view(7, H=2, data=BASE + 7 * (1 << 24) + 4)) == 5
-    assert B.lib().fa_train_bwd_workspace_bytes(None) == 0
+    assert B.lib().fa_train_bwd_workspace_bytes(None) == ctypes.c_size_t(-1).value
 
 
 def test_preprocess_rejects():
