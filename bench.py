@@ -71,11 +71,18 @@ class Workload:
                                           mask=self.mask)
         self.ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
         self.B = binding
+        self.tiles = None
+
+    def classify(self):
+        """The mask tile map (dead / open / mixed 64 x 64 blocks), part of every step
+        that has a dense mask."""
+        if self.mask is not None:
+            self.tiles = self.B.mask_tile_map(self.mask, self.q, self.k)
 
     def fwd(self):
         c = self.case
         self.B.fwd(self.q, self.k, self.v, mask=self.mask, scale=c.scale, causal=c.causal, q_offset=c.q_offset,
-                   out=self.o, lse=self.lse)
+                   out=self.o, lse=self.lse, mask_tiles=self.tiles)
 
     def pre(self):
         self.B.bwd_preprocess(self.o, self.do, delta=self.delta)
@@ -83,9 +90,11 @@ class Workload:
     def bwd(self):
         c = self.case
         self.B.bwd(self.q, self.k, self.v, self.do, self.lse, self.delta, mask=self.mask, scale=c.scale,
-                   causal=c.causal, q_offset=c.q_offset, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
+                   causal=c.causal, q_offset=c.q_offset, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws,
+                   mask_tiles=self.tiles)
 
     def step(self):
+        self.classify()
         self.fwd()
         self.pre()
         self.bwd()
@@ -105,6 +114,7 @@ def time_workload(w: Workload, steps: int, warmup: int) -> dict:
     for i in range(steps):
         e = ev[i]
         e[0].record(stream)
+        w.classify()
         w.fwd()
         e[1].record(stream)
         w.pre()
@@ -180,7 +190,7 @@ def main():
     log(f"[bench] {args.workload}: {r['ms_per_step']:.3f} ms/step, {r['tflops']:.1f} TFLOP/s")
 
     extra = {}
-    for key in [k for k in args.extra.split(",") if k and k != args.workload]:
+    for key in [k for k in args.extra.split(",") if k and k not in (args.workload, "none")]:
         we = Workload(key)
         re_ = time_workload(we, max(5, args.steps // 2), args.warmup)
         re_["pct_of_peak"] = 100.0 * re_["tflops"] / accounting.MI355X_BF16_DENSE_TFLOPS

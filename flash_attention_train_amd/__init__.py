@@ -6,7 +6,7 @@ C ABI in ``include/fa_train.h``; this package is the Python binding over it.
 """
 from __future__ import annotations
 
-__all__ = ["fwd", "bwd_preprocess", "bwd", "bwd_chunked", "bwd_workspace_bytes", "library_path"]
+__all__ = ["fwd", "bwd_preprocess", "bwd", "bwd_chunked", "bwd_workspace_bytes", "mask_tile_map", "library_path"]
 
 
 def __getattr__(name):  # the binding (and the HIP library) is loaded on first use

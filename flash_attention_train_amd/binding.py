@@ -31,7 +31,7 @@ class FaAttnParams(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("Sq", ctypes.c_int32),
                 ("Sk", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("q_offset", ctypes.c_int64), ("scale", ctypes.c_float), ("mask", ctypes.c_void_p),
-                ("mask_stride_b", ctypes.c_int64), ("mask_stride_q", ctypes.c_int64),
+                ("mask_stride_b", ctypes.c_int64), ("mask_stride_q", ctypes.c_int64), ("mask_tiles", ctypes.c_void_p),
                 ("fwd_variant", ctypes.c_int32), ("kv_split", ctypes.c_int32), ("q_split", ctypes.c_int32)]
 
 
@@ -57,6 +57,8 @@ SIGNATURES = {
     "fa_train_status_str": ([ctypes.c_int], ctypes.c_char_p),
     "fa_train_last_error": ([], ctypes.c_char_p),
     "fa_train_version": ([], ctypes.c_int),
+    "fa_train_mask_tiles_bytes": ([_PP], ctypes.c_size_t),
+    "fa_train_mask_tiles": ([_PP, _VP, _VP], ctypes.c_int),
     "fa_train_probe_mfma": ([ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP], ctypes.c_int),
     "fa_train_probe_ds_read_tr16": ([ctypes.c_int32, _VP, _VP, _VP], ctypes.c_int),
 }
@@ -113,7 +115,7 @@ def _stream_handle(stream) -> int:
 
 def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], causal: bool,
                 q_offset: Optional[int], mask: Optional[torch.Tensor], fwd_variant: int = 0, kv_split: int = 0,
-                q_split: int = 0) -> FaAttnParams:
+                q_split: int = 0, mask_tiles: Optional[torch.Tensor] = None) -> FaAttnParams:
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Sk, Dk = k.shape
     if Bk != B or Dk != D:
@@ -123,7 +125,7 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
     if q_offset is None:
         q_offset = Sk - Sq if causal else 0
     p = FaAttnParams(B, Hq, Hkv, Sq, Sk, D, _dtype_code(q), int(bool(causal)), int(q_offset), float(scale),
-                     None, 0, 0, int(fwd_variant), int(kv_split), int(q_split))
+                     None, 0, 0, None, int(fwd_variant), int(kv_split), int(q_split))
     if mask is not None:
         if mask.dtype != torch.float32 or mask.dim() != 3 or mask.stride(2) != 1:
             raise ValueError("mask must be an fp32 [Bm, Sq, Sk] tensor with a contiguous last dimension")
@@ -132,13 +134,30 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
         p.mask = mask.data_ptr()
         p.mask_stride_b = 0 if mask.shape[0] == 1 else mask.stride(0)
         p.mask_stride_q = mask.stride(1)
+        if mask_tiles is not None:
+            if mask_tiles.dtype != torch.uint8 or not mask_tiles.is_contiguous():
+                raise ValueError("mask_tiles must be a contiguous uint8 tensor from mask_tile_map()")
+            p.mask_tiles = mask_tiles.data_ptr()
+    elif mask_tiles is not None:
+        raise ValueError("mask_tiles given without a mask")
     return p
 
 
+def mask_tile_map(mask: torch.Tensor, q: torch.Tensor, k: torch.Tensor, *, stream=None) -> torch.Tensor:
+    """Classify every 64 x 64 block of an additive mask (0 dead, 1 open, 2 mixed) for
+    reuse by fwd/bwd/bwd_chunked through their ``mask_tiles`` argument."""
+    p = make_params(q, k, scale=None, causal=False, q_offset=0, mask=mask)
+    n = int(lib().fa_train_mask_tiles_bytes(ctypes.byref(p)))
+    tiles = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    _check("fa_train_mask_tiles", lib().fa_train_mask_tiles(ctypes.byref(p), tiles.data_ptr(), _stream_handle(stream)))
+    return tiles[:n]
+
+
 def fwd(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, out=None, lse=None, stream=None,
-        variant=0):
+        variant=0, mask_tiles=None):
     """Forward: returns (O, LSE). O has q's dtype and shape; LSE is fp32 [B, Hq, Sq]."""
-    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, fwd_variant=variant)
+    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, fwd_variant=variant,
+                    mask_tiles=mask_tiles)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
@@ -153,7 +172,7 @@ def bwd_preprocess(o, dout, *, delta=None, stream=None):
     B, Hq, Sq, D = o.shape
     if delta is None:
         delta = torch.empty((B, Hq, Sq), dtype=torch.float32, device=o.device)
-    p = FaAttnParams(B, Hq, Hq, Sq, Sq, D, _dtype_code(o), 0, 0, 1.0, None, 0, 0, 0, 0, 0)
+    p = FaAttnParams(B, Hq, Hq, Sq, Sq, D, _dtype_code(o), 0, 0, 1.0, None, 0, 0, None, 0, 0, 0)
     _check("fa_train_bwd_preprocess",
            lib().fa_train_bwd_preprocess(ctypes.byref(p), view4(o), view4(dout), view3(delta), _stream_handle(stream)))
     return delta
@@ -175,10 +194,10 @@ def _workspace(p: FaAttnParams, device, workspace):
 
 
 def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_offset=None, dq=None, dk=None,
-        dv=None, workspace=None, stream=None, kv_split=0, q_split=0):
+        dv=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None):
     """Backward: returns (dQ, dK, dV), each in q's dtype, overwritten."""
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
-                    q_split=q_split)
+                    q_split=q_split, mask_tiles=mask_tiles)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
@@ -190,11 +209,11 @@ def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_off
 
 
 def bwd_chunked(q, k, v, dout, lse, delta, dk_acc, dv_acc, *, mask=None, scale=None, causal=True, q_offset=None,
-                dq=None, workspace=None, stream=None, kv_split=0, q_split=0):
+                dq=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None):
     """Chunked backward: returns dQ for the chunk; ADDS dK/dV into the fp32 window
     accumulators ``dk_acc`` / ``dv_acc`` ([B, Hkv, >= Sk, D])."""
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
-                    q_split=q_split)
+                    q_split=q_split, mask_tiles=mask_tiles)
     if dk_acc.dtype != torch.float32 or dv_acc.dtype != torch.float32:
         raise TypeError("the window accumulators must be float32")
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq

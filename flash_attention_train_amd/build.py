@@ -34,6 +34,12 @@ def hipcc() -> str:
 def _flags() -> list[str]:
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
             "-Wno-unused-variable", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # no NaN quieting around min/max: the kernels never form NaNs (-inf is
+            # handled explicitly), so IEEE-mode canonicalization would be pure overhead
+            "-fno-honor-nans",
+            # MFMA accumulators in arch VGPRs: the softmax reads them, and the AGPR form
+            # cost a v_accvgpr_read per element in the hot loops
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

@@ -95,6 +95,10 @@ Extent mask_extent(const fa_attn_params* p) {
   return {base, base + (uintptr_t)(last * 4)};
 }
 
+int64_t tile_rows(const fa_attn_params* p) { return (p->Sq + 63) / 64; }
+int64_t tile_cols(const fa_attn_params* p) { return (p->Sk + 63) / 64; }
+int64_t tile_batches(const fa_attn_params* p) { return p->mask_stride_b == 0 ? 1 : p->B; }
+
 fa::AttnShape shape_of(const fa_attn_params* p) {
   fa::AttnShape a;
   a.B = p->B;
@@ -110,6 +114,9 @@ fa::AttnShape shape_of(const fa_attn_params* p) {
   a.mask = p->mask;
   a.mask_sb = p->mask_stride_b;
   a.mask_sq = p->mask_stride_q;
+  a.tiles = p->mask ? p->mask_tiles : nullptr;
+  a.tiles_ncol = (int)tile_cols(p);
+  a.tiles_bstride = p->mask_stride_b == 0 ? 0 : (int)(tile_rows(p) * tile_cols(p));
   return a;
 }
 
@@ -402,6 +409,24 @@ fa_status fa_train_bwd_chunked(const fa_attn_params* p, const fa_view* q, const 
   g_err[0] = 0;
   return bwd_common(p, q, k, v, dout, lse, delta, dq, dk_acc, dv_acc, workspace, workspace_bytes_given, stream,
                     true);
+}
+
+size_t fa_train_mask_tiles_bytes(const fa_attn_params* p) {
+  if (check_params(p) != FA_OK || !p->mask) return 0;
+  return (size_t)(tile_batches(p) * tile_rows(p) * tile_cols(p));
+}
+
+fa_status fa_train_mask_tiles(const fa_attn_params* p, uint8_t* tiles, hipStream_t stream) {
+  g_err[0] = 0;
+  fa_status s = check_params(p);
+  if (s) return s;
+  if (!p->mask) return fail(FA_ERR_NULL, "the params carry no mask");
+  if (!tiles) return fail(FA_ERR_NULL, "tiles is NULL");
+  const uintptr_t t = reinterpret_cast<uintptr_t>(tiles);
+  const Extent et = {t, t + (uintptr_t)fa_train_mask_tiles_bytes(p)};
+  const Extent em = mask_extent(p);
+  if (overlaps(et, em)) return fail(FA_ERR_ALIAS, "tiles overlaps the mask");
+  return hip_status(fa::launch_mask_tiles(shape_of(p), tiles, stream), "mask tiles");
 }
 
 const char* fa_train_status_str(fa_status s) {

@@ -66,6 +66,26 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const DqArgs p) {
   store8(dst, out);
 }
 
+// One workgroup per 64 x 64 mask block: dead if every entry is -inf, open if every
+// entry is 0, mixed otherwise (blocks are clipped at Sq and Sk).
+__global__ __launch_bounds__(256) void mask_tiles_kernel(const AttnShape a, uint8_t* tiles) {
+  const int ct = blockIdx.x, rt = blockIdx.y, bm = blockIdx.z;
+  const float* M = a.mask + bm * a.mask_sb;
+  const int rows = min(kMaskTile, a.Sq - rt * kMaskTile), cols = min(kMaskTile, a.Sk - ct * kMaskTile);
+  int dead = 1, open = 1;
+  for (int e = threadIdx.x; e < kMaskTile * kMaskTile; e += 256) {
+    const int r = e / kMaskTile, c = e % kMaskTile;
+    if (r < rows && c < cols) {
+      const float v = M[(int64_t)(rt * kMaskTile + r) * a.mask_sq + ct * kMaskTile + c];
+      dead &= (v == neg_inf());
+      open &= (v == 0.f);
+    }
+  }
+  dead = __syncthreads_and(dead);
+  open = __syncthreads_and(open);
+  if (threadIdx.x == 0) tiles[((int64_t)bm * gridDim.y + rt) * gridDim.x + ct] = dead ? kTileDead : (open ? kTileOpen : kTileMixed);
+}
+
 template <typename T, int D>
 hipError_t launch_pre_t(const PreArgs& p, hipStream_t stream) {
   constexpr int RPB = 256 / (D / 8);
@@ -88,6 +108,13 @@ hipError_t launch_dq_t(const DqArgs& p, hipStream_t stream) {
 hipError_t launch_preprocess(const PreArgs& p, int is_bf16, hipStream_t stream) {
   if (is_bf16) return p.D == 64 ? launch_pre_t<bf16, 64>(p, stream) : launch_pre_t<bf16, 128>(p, stream);
   return p.D == 64 ? launch_pre_t<float, 64>(p, stream) : launch_pre_t<float, 128>(p, stream);
+}
+
+hipError_t launch_mask_tiles(const AttnShape& a, uint8_t* tiles, hipStream_t stream) {
+  const int nrt = (a.Sq + kMaskTile - 1) / kMaskTile, nct = (a.Sk + kMaskTile - 1) / kMaskTile;
+  const int bm = a.mask_sb == 0 ? 1 : a.B;
+  hipLaunchKernelGGL(mask_tiles_kernel, dim3(nct, nrt, bm), dim3(256), 0, stream, a, tiles);
+  return hipGetLastError();
 }
 
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream) {

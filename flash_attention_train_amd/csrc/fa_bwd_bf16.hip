@@ -44,6 +44,7 @@ constexpr int Q_BN = 64;    // keys per staged tile of the dQ walk
 
 __device__ __forceinline__ f32x16 zeros16() {
   f32x16 z;
+  #pragma unroll
   for (int r = 0; r < 16; ++r) z[r] = 0.f;
   return z;
 }
@@ -88,6 +89,7 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
   const bf16* K = static_cast<const bf16*>(args.k) + b * args.sk.b + hk * args.sk.h;
   const bf16* V = static_cast<const bf16*>(args.v) + b * args.sv.b + hk * args.sv.h;
   bf16x8 kf[DS], vf[DS];
+  #pragma unroll
   for (int s = 0; s < DS; ++s) {
     if (key < a.Sk) {
       kf[s] = *reinterpret_cast<const bf16x8*>(K + (int64_t)key * args.sk.s + 16 * s + 8 * g);
@@ -98,6 +100,7 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
     }
   }
   f32x16 dk[DB], dv[DB];
+  #pragma unroll
   for (int db = 0; db < DB; ++db) {
     dk[db] = zeros16();
     dv[db] = zeros16();
@@ -124,27 +127,22 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
     pair_of(p, h, q0);
     const bf16* Q = static_cast<const bf16*>(args.q) + b * args.sq.b + h * args.sq.h;
     const bf16* dO = static_cast<const bf16*>(args.dout) + b * args.sdo.b + h * args.sdo.h;
+    // rows past the end load the last row: they are masked (P = 0) on the tail tile
+    #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + 256 * i;
-      const int row = q0 + c / (D / 8), d0 = (c % (D / 8)) * 8;
-      if (row < a.Sq) {
-        qpre[i] = *reinterpret_cast<const bf16x8*>(Q + (int64_t)row * args.sq.s + d0);
-        dpre[i] = *reinterpret_cast<const bf16x8*>(dO + (int64_t)row * args.sdo.s + d0);
-      } else {
-        zero(qpre[i]);
-        zero(dpre[i]);
-      }
+      const int row = min(q0 + c / (D / 8), a.Sq - 1), d0 = (c % (D / 8)) * 8;
+      qpre[i] = *reinterpret_cast<const bf16x8*>(Q + (int64_t)row * args.sq.s + d0);
+      dpre[i] = *reinterpret_cast<const bf16x8*>(dO + (int64_t)row * args.sdo.s + d0);
     }
     if (tid < 2 * KV_BM) {
-      const int row = q0 + (tid % KV_BM);
-      if (row < a.Sq)
-        lpre = tid < KV_BM ? args.lse[b * args.lse_sb + h * args.lse_sh + row] * kLog2e
-                           : args.delta[b * args.delta_sb + h * args.delta_sh + row];
-      else
-        lpre = 0.f;
+      const int row = min(q0 + (tid % KV_BM), a.Sq - 1);
+      lpre = tid < KV_BM ? args.lse[b * args.lse_sb + h * args.lse_sh + row] * kLog2e
+                         : args.delta[b * args.delta_sb + h * args.delta_sh + row];
     }
   };
   auto store_pair = [&](int buf) {
+    #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + 256 * i;
       const int row = c / (D / 8), d0 = (c % (D / 8)) * 8;
@@ -160,27 +158,60 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
   const int G16 = lane >> 4, L16 = lane & 15;
   const int tr_row = L16 >> 2, tr_col = 16 * (G16 & 1) + 4 * (L16 & 3);
 
-  int p = split;
+  // With a mask tile map, pairs whose mask blocks are dead for both 64-key halves of
+  // this workgroup are skipped; per wave, a dead block skips the products and an open
+  // block skips the mask reads.
+  const int nct = (a.Sk + kMaskTile - 1) / kMaskTile;
+  const int ct0 = n0 / kMaskTile;
+  auto live = [&](int pp) -> bool {
+    if (!MASK || !a.tiles) return true;
+    const int rt = qt0 + pp / a.G;  // 64-row query tiles are the mask's row blocks
+    for (int ct = ct0; ct < ct0 + KV_BN / kMaskTile && ct < nct; ++ct)
+      if (tile_class(a, b, rt, ct) != kTileDead) return true;
+    return false;
+  };
+  auto next_live = [&](int pp) {
+    while (pp < npairs && !live(pp)) pp += plan.kv_split;
+    return pp;
+  };
+  const int ct_w = ct0 + (32 * wave) / kMaskTile;  // this wave's 32 keys lie in one 64-key block
+
+  int p = next_live(split);
   if (p < npairs) {
     load_pair(p);
     store_pair(0);
   }
   __syncthreads();
-  for (int it = 0; p < npairs; ++it, p += plan.kv_split) {
+  for (int it = 0; p < npairs; ++it) {
     const int buf = it & 1;
-    const int pn = p + plan.kv_split;
-    if (pn < npairs) load_pair(pn);
+    const int pn = next_live(p + plan.kv_split);
+    load_pair(pn < npairs ? pn : p);  // the last pair reloads itself: no branch around the loads
     int h, q0;
     pair_of(p, h, q0);
+    int cls = kTileMixed;
+    if (MASK) cls = ct_w < nct ? tile_class(a, b, q0 / kMaskTile, ct_w) : kTileDead;
+    const bool mixed = MASK && cls == kTileMixed;
     const bf16* qb_lds = q_lds + buf * KV_BM * RS;
     const bf16* db_lds = do_lds + buf * KV_BM * RS;
     const float* lse_b = lse_lds + buf * KV_BM;
     const float* dlt_b = dlt_lds + buf * KV_BM;
     bool edge = q0 + KV_BM > a.Sq || n0 + KV_BN > a.Sk;
     if (CAUSAL) edge = edge || ((int64_t)n0 + KV_BN - 1 > a.q_offset + q0);
+    // visible local rows of this lane's key: qlo <= ql < qhi (ql = row - q0), shifted by
+    // this lane's 4 g so that each test compares a constant
+    int qlo = 0, qhi = key < a.Sk ? a.Sq - q0 : 0;
+    if (CAUSAL) {
+      const int64_t lo = (int64_t)key - a.q_offset - q0;  // key <= q_offset + row
+      qlo = (int)(lo < 0 ? 0 : (lo > KV_BM ? KV_BM : lo));
+    }
+    qlo -= 4 * g;
+    qhi -= 4 * g;
 
+    #pragma unroll
     for (int qb = 0; qb < KV_BM / 32; ++qb) {
+      if (cls == kTileDead) break;
       f32x16 sacc = zeros16(), dpacc = zeros16();
+      #pragma unroll
       for (int s = 0; s < DS; ++s) {
         const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb_lds + (32 * qb + r32) * RS + 16 * s + 8 * g);
         const bf16x8 da = *reinterpret_cast<const bf16x8*>(db_lds + (32 * qb + r32) * RS + 16 * s + 8 * g);
@@ -188,19 +219,20 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
         mma(dpacc, da, vf[s]);
       }
       // lane (key, half g), register r -> query row 32 qb + 8 (r/4) + 4 g + r%4
+      #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int ql4 = 32 * qb + 8 * rr + 4 * g;
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_b + ql4);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt_b + ql4);
+        #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rr + e;
           float x = sacc[r];
           bool vis = true;
-          if (MASK || edge) {
-            const int qi = q0 + ql4 + e;
-            vis = key < a.Sk && qi < a.Sq;
-            if (CAUSAL) vis = vis && ((int64_t)key <= a.q_offset + qi);
-            if (MASK && vis) x += a.mask[b * a.mask_sb + (int64_t)qi * a.mask_sq + key] * args.inv_scale;
+          if (mixed || edge) {
+            const int c = 32 * qb + 8 * rr + e;  // ql - 4 g
+            vis = c >= qlo && c < qhi;
+            if (mixed && vis) x += a.mask[b * a.mask_sb + (int64_t)(q0 + ql4 + e) * a.mask_sq + key] * args.inv_scale;
           }
           const float pv = vis ? fast_exp2(fmaf(x, cs, -l4[e])) : 0.f;
           sacc[r] = pv;
@@ -209,11 +241,13 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
       }
       // dV += P^T dO, dK += dS^T Q; registers 8 hh .. 8 hh + 7 hold rows
       // 32 qb + 16 hh + 8 t + 4 g + e, exactly the rows each transpose read returns
+      #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         bf16x8 pa, dsa;
         pack8(pa, sacc, 8 * hh);
         pack8(dsa, dpacc, 8 * hh);
         const int rbase = 32 * qb + 16 * hh + 4 * g + tr_row;
+        #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const int col = 32 * db + tr_col;
           const bf16x4 d0 = tr_read(db_lds, rbase * RS + col);
@@ -229,11 +263,14 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
     }
     if (pn < npairs) store_pair(buf ^ 1);
     __syncthreads();
+    p = pn;
   }
 
   // results: accumulator row = key 8 (r/4) + 4 g + r%4 of this wave, column d = 32 db + r32
   const bool atomic = plan.kv_split > 1;
+  #pragma unroll
   for (int db = 0; db < DB; ++db) {
+    #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kk = n0 + 32 * wave + 8 * (r >> 2) + 4 * g + (r & 3);
       if (kk >= a.Sk) continue;
@@ -301,6 +338,7 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
   const bf16* K = static_cast<const bf16*>(args.k) + b * args.sk.b + hk * args.sk.h;
   const bf16* V = static_cast<const bf16*>(args.v) + b * args.sv.b + hk * args.sv.h;
   bf16x8 qf[DS], df[DS];
+  #pragma unroll
   for (int s = 0; s < DS; ++s) {
     if (row < a.Sq) {
       qf[s] = *reinterpret_cast<const bf16x8*>(Q + (int64_t)row * args.sq.s + 16 * s + 8 * g);
@@ -319,6 +357,7 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
   if (MASK && row < a.Sq) Mrow = a.mask + b * a.mask_sb + (int64_t)row * a.mask_sq;
 
   f32x16 dq[DB];
+  #pragma unroll
   for (int db = 0; db < DB; ++db) dq[db] = zeros16();
 
   const int nkt = (a.Sk + Q_BN - 1) / Q_BN;
@@ -330,19 +369,17 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
 
   bf16x8 kpre[CPT], vpre[CPT];
   auto load_tile = [&](int kt) {
+    // keys past the end load the last key: they are masked (P = 0) on the tail tile
+    #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + 256 * i;
-      const int kk = kt * Q_BN + c / (D / 8), d0 = (c % (D / 8)) * 8;
-      if (kk < a.Sk) {
-        kpre[i] = *reinterpret_cast<const bf16x8*>(K + (int64_t)kk * args.sk.s + d0);
-        vpre[i] = *reinterpret_cast<const bf16x8*>(V + (int64_t)kk * args.sv.s + d0);
-      } else {
-        zero(kpre[i]);
-        zero(vpre[i]);
-      }
+      const int kk = min(kt * Q_BN + c / (D / 8), a.Sk - 1), d0 = (c % (D / 8)) * 8;
+      kpre[i] = *reinterpret_cast<const bf16x8*>(K + (int64_t)kk * args.sk.s + d0);
+      vpre[i] = *reinterpret_cast<const bf16x8*>(V + (int64_t)kk * args.sv.s + d0);
     }
   };
   auto store_tile = [&](int buf) {
+    #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + 256 * i;
       const int rr = c / (D / 8), d0 = (c % (D / 8)) * 8;
@@ -354,82 +391,110 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
   const int G16 = lane >> 4, L16 = lane & 15;
   const int tr_row = L16 >> 2, tr_col = 16 * (G16 & 1) + 4 * (L16 & 3);
 
-  int kt = split;
+  // mask tile map: skip key tiles dead for both 64-row blocks of this workgroup
+  const int nrt = (a.Sq + kMaskTile - 1) / kMaskTile;
+  auto live = [&](int k) -> bool {
+    if (!MASK || !a.tiles) return true;
+    for (int rt = q0 / kMaskTile; rt <= (q0 + Q_BM - 1) / kMaskTile && rt < nrt; ++rt)
+      if (tile_class(a, b, rt, k) != kTileDead) return true;  // Q_BN = kMaskTile: key tile = block
+    return false;
+  };
+  auto next_live = [&](int k) {
+    while (k < kt_end && !live(k)) k += plan.q_split;
+    return k;
+  };
+  const int rt_w = qw / kMaskTile;
+
+  int kt = next_live(split);
   if (kt < kt_end) {
     load_tile(kt);
     store_tile(0);
   }
   __syncthreads();
-  for (int it = 0; kt < kt_end; ++it, kt += plan.q_split) {
+  for (int it = 0; kt < kt_end; ++it) {
     const int buf = it & 1;
-    const int ktn = kt + plan.q_split;
-    if (ktn < kt_end) load_tile(ktn);
+    const int ktn = next_live(kt + plan.q_split);
+    load_tile(ktn < kt_end ? ktn : kt);  // the last tile reloads itself: no branch around the loads
+    int cls = kTileMixed;
+    if (MASK) cls = rt_w < nrt ? tile_class(a, b, rt_w, kt) : kTileDead;
+    const bool mixed = MASK && cls == kTileMixed;
     const bf16* kb_lds = k_lds + buf * Q_BN * RS;
     const bf16* vb_lds = v_lds + buf * Q_BN * RS;
     const int key0 = kt * Q_BN;
     bool edge = key0 + Q_BN > a.Sk || qw + 32 > a.Sq;
     if (CAUSAL) edge = edge || ((int64_t)key0 + Q_BN - 1 > a.q_offset + qw);
+    // visible local keys of this lane's row: kl < klim, shifted by 4 g
+    int64_t kl64 = row < a.Sq ? (int64_t)a.Sk - key0 : 0;
+    if (CAUSAL) {
+      const int64_t c = a.q_offset + row + 1 - key0;
+      kl64 = c < kl64 ? c : kl64;
+    }
+    const int klim = (int)(kl64 < 0 ? 0 : (kl64 > Q_BN ? Q_BN : kl64)) - 4 * g;
 
-    f32x16 st[2], dpt[2];
+    // one 32-key block at a time keeps the live accumulators small
+    #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      st[kb] = zeros16();
-      dpt[kb] = zeros16();
+      if (cls == kTileDead) break;
+      f32x16 st = zeros16(), dpt = zeros16();
+      #pragma unroll
       for (int s = 0; s < DS; ++s) {
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb_lds + (32 * kb + r32) * RS + 16 * s + 8 * g);
         const bf16x8 va = *reinterpret_cast<const bf16x8*>(vb_lds + (32 * kb + r32) * RS + 16 * s + 8 * g);
-        mma(st[kb], ka, qf[s]);
-        mma(dpt[kb], va, df[s]);
+        mma(st, ka, qf[s]);
+        mma(dpt, va, df[s]);
       }
-    }
-    // lane (query row, half g), register r -> key 32 kb + 8 (r/4) + 4 g + r%4
-    bf16x8 dsf[2][2];
-    for (int kb = 0; kb < 2; ++kb) {
+      // lane (query row, half g), register r -> key 32 kb + 8 (r/4) + 4 g + r%4
+      #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int k4 = key0 + 32 * kb + 8 * rr + 4 * g;
         float mv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (MASK && Mrow) {
+        if (mixed && Mrow) {
           if (k4 + 3 < a.Sk && args.mask_vec4) {
             const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mrow + k4);
             mv[0] = m4[0]; mv[1] = m4[1]; mv[2] = m4[2]; mv[3] = m4[3];
           } else {
+            #pragma unroll
             for (int e = 0; e < 4; ++e) mv[e] = (k4 + e < a.Sk) ? Mrow[k4 + e] : 0.f;
           }
         }
+        #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rr + e;
-          float x = st[kb][r];
+          float x = st[r];
           bool vis = true;
-          if (MASK || edge) {
-            vis = k4 + e < a.Sk && row < a.Sq;
-            if (CAUSAL) vis = vis && ((int64_t)(k4 + e) <= a.q_offset + row);
-            if (MASK) x += mv[e] * args.inv_scale;
+          if (mixed || edge) {
+            vis = 32 * kb + 8 * rr + e < klim;
+            if (MASK) x += mv[e] * args.inv_scale;  // mv = 0 unless the block is mixed
           }
           const float pv = vis ? fast_exp2(fmaf(x, cs, -lse2)) : 0.f;
-          st[kb][r] = pv * (dpt[kb][r] - dlt);
+          st[r] = pv * (dpt[r] - dlt);
         }
       }
-      pack8(dsf[kb][0], st[kb], 0);
-      pack8(dsf[kb][1], st[kb], 8);
-    }
-    // dQ += dS K: A = dS (registers 8 hh .. of key block kb: keys 32 kb + 16 hh + 8 t + 4 g + e),
-    // B = K rows of the same keys, column d, by transpose reads
-    for (int kb = 0; kb < 2; ++kb) {
+      // dQ += dS K: A = dS (registers 8 hh .. of this key block: keys 32 kb + 16 hh + 8 t + 4 g + e),
+      // B = K rows of the same keys, column d, by transpose reads
+      #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
+        bf16x8 dsf;
+        pack8(dsf, st, 8 * hh);
         const int rbase = 32 * kb + 16 * hh + 4 * g + tr_row;
+        #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const bf16x4 lo = tr_read(kb_lds, rbase * RS + 32 * db + tr_col);
           const bf16x4 hi = tr_read(kb_lds, (rbase + 8) * RS + 32 * db + tr_col);
           const bf16x8 kbt = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          mma(dq[db], dsf[kb][hh], kbt);
+          mma(dq[db], dsf, kbt);
         }
       }
     }
     if (ktn < kt_end) store_tile(buf ^ 1);
     __syncthreads();
+    kt = ktn;
   }
 
   // dQ accumulator: lane (d = 32 db + r32, half g), register r -> row 8 (r/4) + 4 g + r%4 of the wave
+  #pragma unroll
   for (int db = 0; db < DB; ++db) {
+    #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qi = qw + 8 * (r >> 2) + 4 * g + (r & 3);
       if (qi >= a.Sq) continue;

@@ -67,6 +67,7 @@ __device__ __forceinline__ void mma(f32x16& c, const f32x8& a, const f32x8& b) {
 // fragment loads (8 consecutive elements, or two runs of 4) and conversions
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void zero(bf16x8& f) {
+  #pragma unroll
   for (int j = 0; j < 8; ++j) f[j] = (bf16)0.0f;
 }
 __device__ __forceinline__ void zero(f32x8& f) {
@@ -102,6 +103,7 @@ __device__ __forceinline__ float elem(const f32x8& f, int j) { return j < 4 ? f.
 
 // 8 fp32 values (register slots r0 .. r0 + 7 of an accumulator) to an operand fragment
 __device__ __forceinline__ void pack8(bf16x8& f, const f32x16& c, int r0) {
+  #pragma unroll
   for (int j = 0; j < 8; ++j) f[j] = (bf16)c[r0 + j];
 }
 __device__ __forceinline__ void pack8(f32x8& f, const f32x16& c, int r0) {

@@ -35,6 +35,7 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 __device__ __forceinline__ f32x16 zeros16() {
   f32x16 z;
+  #pragma unroll
   for (int r = 0; r < 16; ++r) z[r] = 0.f;
   return z;
 }
@@ -74,8 +75,10 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
 
   // Q rows as B operands: lane (row r32, half g) holds d = 16 s + 8 g .. + 7
   bf16x8 qf[QB][DS];
+  #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qw + 32 * qb + r32;
+    #pragma unroll
     for (int s = 0; s < DS; ++s) {
       if (row < a.Sq)
         qf[qb][s] = *reinterpret_cast<const bf16x8*>(Q + (int64_t)row * args.sq.s + 16 * s + 8 * g);
@@ -86,7 +89,9 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
 
   f32x16 oacc[QB][DB];
   float base[QB], lsum[QB];
+  #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
+    #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[qb][db] = zeros16();
     base[qb] = neg_inf();
     lsum[qb] = 0.f;
@@ -99,22 +104,40 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     kt_end = last_key < 0 ? 0 : (int)((last_key / BN + 1) < nkt ? (last_key / BN + 1) : nkt);
   }
 
-  // tile loader: thread tid moves chunks tid + 256 i (row = chunk / (D/8))
+  // tile loader: thread tid moves chunks tid + 256 i (row = chunk / (D/8)). Rows past
+  // the end of K / V load the last row instead: those keys are masked (P = 0) on the
+  // tail tile, so any finite values do, and the loads need no branch.
   bf16x8 kpre[CPT], vpre[CPT];
+  // per-thread element offsets inside a tile (row c / (D/8), column d0), tile bases are scalar
+  int koff[CPT], voff[CPT], krow[CPT];
+  #pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + 256 * i;
+    krow[i] = c / (D / 8);
+    koff[i] = krow[i] * (int)args.sk.s + (c % (D / 8)) * 8;
+    voff[i] = krow[i] * (int)args.sv.s + (c % (D / 8)) * 8;
+  }
   auto load_tile = [&](int kt) {
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i;
-      const int key = kt * BN + c / (D / 8), d0 = (c % (D / 8)) * 8;
-      if (key < a.Sk) {
-        kpre[i] = *reinterpret_cast<const bf16x8*>(K + (int64_t)key * args.sk.s + d0);
-        vpre[i] = *reinterpret_cast<const bf16x8*>(V + (int64_t)key * args.sv.s + d0);
-      } else {
-        zero(kpre[i]);
-        zero(vpre[i]);
+    const int key0 = kt * BN;
+    const bf16* Kt = K + (int64_t)key0 * args.sk.s;
+    const bf16* Vt = V + (int64_t)key0 * args.sv.s;
+    if (key0 + BN <= a.Sk) {
+      #pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        kpre[i] = *reinterpret_cast<const bf16x8*>(Kt + koff[i]);
+        vpre[i] = *reinterpret_cast<const bf16x8*>(Vt + voff[i]);
+      }
+    } else {
+      #pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int dr = min(krow[i], a.Sk - 1 - key0) - krow[i];  // clamp to the last row
+        kpre[i] = *reinterpret_cast<const bf16x8*>(Kt + koff[i] + dr * (int)args.sk.s);
+        vpre[i] = *reinterpret_cast<const bf16x8*>(Vt + voff[i] + dr * (int)args.sv.s);
       }
     }
   };
   auto store_tile = [&](int buf) {
+    #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + 256 * i;
       const int row = c / (D / 8), d0 = (c % (D / 8)) * 8;
@@ -123,8 +146,26 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     }
   };
 
-  if (kt_end > 0) {
-    load_tile(0);
+  // With a mask tile map, key tiles whose mask blocks are dead for every row block
+  // of this workgroup are skipped outright (no load, no products); per wave, a dead
+  // block skips the products and an open block skips the mask reads.
+  const int nrt = (a.Sq + kMaskTile - 1) / kMaskTile;
+  const int rt_w = qw / kMaskTile;  // the wave's QB * 32 rows lie in one 64-row block
+  auto live = [&](int kt) -> bool {
+    if (!MASK || !a.tiles) return true;
+    const int ct = (kt * BN) / kMaskTile;
+    for (int rt = q0 / kMaskTile; rt <= (q0 + BM - 1) / kMaskTile && rt < nrt; ++rt)
+      if (tile_class(a, b, rt, ct) != kTileDead) return true;
+    return false;
+  };
+  auto next_live = [&](int kt) {
+    while (kt < kt_end && !live(kt)) ++kt;
+    return kt;
+  };
+
+  int kt = next_live(0);
+  if (kt < kt_end) {
+    load_tile(kt);
     store_tile(0);
   }
   __syncthreads();
@@ -133,20 +174,29 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
   const int G16 = lane >> 4, L16 = lane & 15;
   const int tr_row = L16 >> 2, tr_col = 16 * (G16 & 1) + 4 * (L16 & 3);
 
-  for (int kt = 0; kt < kt_end; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < kt_end;
-    if (more) load_tile(kt + 1);
+  for (int it = 0; kt < kt_end; ++it) {
+    const int buf = it & 1;
+    const int ktn = next_live(kt + 1);
+    const bool more = ktn < kt_end;
+    load_tile(more ? ktn : kt);  // the last iteration reloads its own tile: no branch around loads
     const bf16* kb_lds = k_lds[buf];
     const bf16* vb_lds = v_lds[buf];
+    int cls = kTileMixed;
+    if (MASK) cls = rt_w < nrt ? tile_class(a, b, rt_w, (kt * BN) / kMaskTile) : kTileDead;
+    if (cls != kTileDead) {
 
     // S^T = K Q^T for both 32-key blocks; each K fragment serves all QB query blocks
     f32x16 st[QB][KB];
+    #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
+      #pragma unroll
       for (int kb = 0; kb < KB; ++kb) st[qb][kb] = zeros16();
+    #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      #pragma unroll
       for (int s = 0; s < DS; ++s) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb_lds + (32 * kb + r32) * KS + 16 * s + 8 * g);
+        #pragma unroll
         for (int qb = 0; qb < QB; ++qb) mma(st[qb][kb], kf, qf[qb][s]);
       }
     }
@@ -155,14 +205,29 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     const int key0 = kt * BN;
     bool edge = key0 + BN > a.Sk;
     if (CAUSAL) edge = edge || ((int64_t)key0 + BN - 1 > a.q_offset + qw);
+    // visible local keys of this lane's rows are kl < lim[qb] (kl = key - key0)
+    int lim[QB];
+    #pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      int64_t l = (int64_t)a.Sk - key0;
+      if (CAUSAL) {
+        const int64_t c = a.q_offset + qw + 32 * qb + r32 + 1 - key0;
+        l = c < l ? c : l;
+      }
+      lim[qb] = (int)(l < 0 ? 0 : (l > BN ? BN : l));
+    }
 
     bf16x8 pf[QB][KB][2];
+    #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int row = qw + 32 * qb + r32;
-      if (MASK || edge) {
+      const bool mixed = MASK && cls == kTileMixed;
+      if (mixed || edge) {
         const float* Mrow = nullptr;
-        if (MASK && row < a.Sq) Mrow = a.mask + b * a.mask_sb + (int64_t)row * a.mask_sq;
+        if (mixed && row < a.Sq) Mrow = a.mask + b * a.mask_sb + (int64_t)row * a.mask_sq;
+        #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
+          #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const int k4 = key0 + 32 * kb + 8 * rr + 4 * g;  // 4 consecutive keys k4 .. k4 + 3
             float mv[4] = {0.f, 0.f, 0.f, 0.f};
@@ -171,16 +236,16 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
                 const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mrow + k4);
                 mv[0] = m4[0]; mv[1] = m4[1]; mv[2] = m4[2]; mv[3] = m4[3];
               } else {
+                #pragma unroll
                 for (int e = 0; e < 4; ++e) mv[e] = (k4 + e < a.Sk) ? Mrow[k4 + e] : 0.f;
               }
             }
+            #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int key = k4 + e;
-              bool vis = key < a.Sk;
-              if (CAUSAL) vis = vis && ((int64_t)key <= a.q_offset + row);
+              const bool vis = 32 * kb + 8 * rr + 4 * g + e < lim[qb];
               // the mask enters the raw score as M / scale so that one fma applies both later
               float x = st[qb][kb][4 * rr + e];
-              if (MASK) x += mv[e] * args.inv_scale;
+              if (MASK) x += mv[e] * args.inv_scale;  // mv = 0 unless the block is mixed
               st[qb][kb][4 * rr + e] = vis ? x : neg_inf();
             }
           }
@@ -188,7 +253,9 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
       }
       // row max of this tile (raw score units), shared by lanes l and l ^ 32
       float mx = neg_inf();
+      #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
+        #pragma unroll
         for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(st[qb][kb][r], st[qb][kb][r + 1]));
       mx = fmaxf(mx, xor32(mx));
       const float mscaled = mx * cs;
@@ -200,12 +267,16 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
         const float nb = need ? mscaled : base[qb];
         base[qb] = nb;
         lsum[qb] *= alpha;
+        #pragma unroll
         for (int db = 0; db < DB; ++db)
+          #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
       }
       const float nbase = (base[qb] == neg_inf()) ? 0.f : -base[qb];
       float ls = 0.f;
+      #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
+        #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = fast_exp2(fmaf(st[qb][kb][r], cs, nbase));
           st[qb][kb][r] = p;
@@ -219,23 +290,30 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
 
     // O^T += V^T P^T: registers 8 hh .. 8 hh + 7 of key block kb hold keys
     // 32 kb + 16 hh + 8 t + 4 g + e (t = 0, 1; e = 0..3) -- the rows each transpose read returns
+    #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int rbase = 32 * kb + 16 * hh + 4 * g + tr_row;
+        #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const bf16x4 lo = tr_read(vb_lds, rbase * KS + 32 * db + tr_col);
           const bf16x4 hi = tr_read(vb_lds, (rbase + 8) * KS + 32 * db + tr_col);
           const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          #pragma unroll
           for (int qb = 0; qb < QB; ++qb) mma(oacc[qb][db], vf, pf[qb][kb][hh]);
         }
       }
     }
 
+    }  // cls != dead
     if (more) store_tile(buf ^ 1);
     __syncthreads();
+    kt = ktn;
   }
 
   // epilogue: O = acc / l, LSE = (base + log2 l) ln 2; fully masked rows -> 0, 0
+  #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qw + 32 * qb + r32;
     const float lt = lsum[qb] + xor32(lsum[qb]);
@@ -244,9 +322,12 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     const float lse = full ? 0.f : (base[qb] + log2f(lt)) * kLn2;
     if (row < a.Sq) {
       bf16* O = static_cast<bf16*>(args.o) + b * args.so.b + h * args.so.h + (int64_t)row * args.so.s;
+      #pragma unroll
       for (int db = 0; db < DB; ++db) {
+        #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           bf16x4 o4;
+          #pragma unroll
           for (int e = 0; e < 4; ++e) o4[e] = (bf16)(oacc[qb][db][4 * rr + e] * inv);
           *reinterpret_cast<bf16x4*>(O + 32 * db + 8 * rr + 4 * g) = o4;
         }

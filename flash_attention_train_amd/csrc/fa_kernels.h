@@ -23,7 +23,18 @@ struct AttnShape {
   float scale;       // multiplies <q, k>
   const float* mask; // additive [b][i][j] fp32 or nullptr
   int64_t mask_sb, mask_sq;
+  const uint8_t* tiles;  // mask block classes [Bm][ceil(Sq/64)][ceil(Sk/64)] or nullptr
+  int tiles_bstride;     // blocks per mask batch entry (0 when the mask is shared)
+  int tiles_ncol;        // ceil(Sk / 64)
 };
+
+constexpr int kTileDead = 0, kTileOpen = 1, kTileMixed = 2, kMaskTile = 64;
+
+// class of mask block (b, row block rt, key block ct); mixed when no map is given
+__device__ __forceinline__ int tile_class(const AttnShape& a, int b, int rt, int ct) {
+  if (!a.tiles) return kTileMixed;
+  return a.tiles[b * a.tiles_bstride + rt * a.tiles_ncol + ct];
+}
 
 struct FwdArgs {
   AttnShape a;
@@ -90,6 +101,7 @@ hipError_t launch_fwd(const FwdArgs& args, int is_bf16, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& args, int qb, hipStream_t stream);
 hipError_t launch_preprocess(const PreArgs& args, int is_bf16, hipStream_t stream);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
+hipError_t launch_mask_tiles(const AttnShape& a, uint8_t* tiles, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& args, int is_bf16, hipStream_t stream);
 hipError_t launch_dq_convert(const DqArgs& args, int is_bf16, hipStream_t stream);
 void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, BwdPlan* plan);

@@ -95,6 +95,11 @@ typedef struct fa_attn_params {
     const float* mask;    /* optional additive mask [b][i][j], fp32; NULL = none */
     int64_t mask_stride_b;/* elements between batch entries; 0 = shared by the batch */
     int64_t mask_stride_q;/* elements between query rows (>= Sk) */
+    const uint8_t* mask_tiles; /* optional classification of the mask's 64 x 64 blocks made by
+                             fa_train_mask_tiles for this very mask (same pointer, strides and
+                             shape); NULL = every block is read elementwise. With it, blocks
+                             that are entirely -inf are skipped and blocks that are entirely
+                             0 are not read. */
     /* Work decomposition hints, 0 = automatic (the normal setting; other values are
      * for tuning and give the same results up to fp32 summation order): */
     int32_t fwd_variant;  /* bf16 forward: 1 = 32 query rows per wave, 2 = 64 rows */
@@ -138,6 +143,23 @@ fa_status fa_train_bwd_chunked(const fa_attn_params* p, const fa_view* q, const 
                                const fa_view* dout, const fa_view* lse, const fa_view* delta,
                                const fa_view* dq, const fa_view* dk_acc, const fa_view* dv_acc,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Mask block classes written by fa_train_mask_tiles. */
+#define FA_TILE_DEAD 0  /* every entry of the block is -inf */
+#define FA_TILE_OPEN 1  /* every entry of the block is exactly 0 */
+#define FA_TILE_MIXED 2 /* anything else (finite biases, partly masked) */
+#define FA_MASK_TILE 64 /* block edge, in query rows and keys */
+
+/* Bytes of the mask tile map for p: Bm * ceil(Sq/64) * ceil(Sk/64), Bm = 1 when
+ * mask_stride_b == 0, else B. 0 if p has no mask or is invalid. */
+size_t fa_train_mask_tiles_bytes(const fa_attn_params* p);
+
+/* Classifies every 64 x 64 block of p's mask (clipped at Sq and Sk) into the
+ * FA_TILE_* classes, one byte per block at tiles[(bm * ceil(Sq/64) + rt) * ceil(Sk/64) + ct].
+ * The map depends only on the mask, so one map serves the forward and the backward and
+ * every layer that shares the mask. Errors: FA_ERR_NULL (no mask, NULL tiles), the
+ * shape and stride errors of the other entry points, FA_ERR_HIP. */
+fa_status fa_train_mask_tiles(const fa_attn_params* p, uint8_t* tiles, hipStream_t stream);
 
 /* Static text for a status code. */
 const char* fa_train_status_str(fa_status s);

@@ -42,7 +42,7 @@ BASE = 0x7F0000000000  # fake, 256-byte aligned device addresses
 
 def params(**kw):
     a = dict(B=1, Hq=4, Hkv=2, Sq=64, Sk=64, D=64, dtype=B.FA_BF16, causal=0, q_offset=0, scale=0.125, mask=None,
-             mask_stride_b=0, mask_stride_q=0, fwd_variant=0, kv_split=0, q_split=0)
+             mask_stride_b=0, mask_stride_q=0, mask_tiles=None, fwd_variant=0, kv_split=0, q_split=0)
     a.update(kw)
     return B.FaAttnParams(*(a[f] for f, _ in B.FaAttnParams._fields_))
 
@@ -133,6 +133,18 @@ def test_preprocess_rejects():
                                      None) == 6
     assert L.fa_train_bwd_preprocess(ctypes.byref(params(D=32)), view(0), view(1), lse_view(2), None) == 7
     assert L.fa_train_bwd_preprocess(None, view(0), view(1), lse_view(2), None) == 1
+
+
+def test_mask_tiles_host_checks():
+    L = B.lib()
+    assert L.fa_train_mask_tiles_bytes(ctypes.byref(params())) == 0  # no mask
+    m = params(Sq=130, Sk=70, mask=BASE + 9 * (1 << 24), mask_stride_q=72, mask_stride_b=0)
+    assert L.fa_train_mask_tiles_bytes(ctypes.byref(m)) == 3 * 2
+    mb = params(B=2, Sq=130, Sk=70, mask=BASE + 9 * (1 << 24), mask_stride_q=72, mask_stride_b=130 * 72)
+    assert L.fa_train_mask_tiles_bytes(ctypes.byref(mb)) == 2 * 3 * 2
+    assert L.fa_train_mask_tiles(ctypes.byref(params()), BASE, None) == 1
+    assert L.fa_train_mask_tiles(ctypes.byref(m), None, None) == 1
+    assert L.fa_train_mask_tiles(ctypes.byref(m), BASE + 9 * (1 << 24) + 64, None) == 6
 
 
 def test_probe_rejects_bad_arguments():

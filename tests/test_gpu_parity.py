@@ -202,3 +202,63 @@ def test_chunked_decompositions(kv_split, q_split):
     got = {"dQ": host64(dQ), "dK": dk_acc.cpu().numpy().astype(np.float64),
            "dV": dv_acc.cpu().numpy().astype(np.float64)}
     compare_full(c, got, ref, names=("dQ", "dK", "dV"))
+
+
+def numpy_tile_map(mask: np.ndarray) -> np.ndarray:
+    Bm, Sq, Sk = mask.shape
+    nr, nc = (Sq + 63) // 64, (Sk + 63) // 64
+    out = np.zeros((Bm, nr, nc), np.uint8)
+    for b in range(Bm):
+        for r in range(nr):
+            for c in range(nc):
+                blk = mask[b, 64 * r:64 * r + 64, 64 * c:64 * c + 64]
+                out[b, r, c] = 0 if np.all(blk == -np.inf) else (1 if np.all(blk == 0) else 2)
+    return out.reshape(-1)
+
+
+TILE_CASES = {
+    "dit_sa_ragged": lambda: configs.make("dit_sa", Hq=4, Hkv=2, Sq=300, Sk=300),
+    "dit_ca_ragged": lambda: configs.make("dit_ca", B=2, Hq=2, Hkv=2, Sq=300, Sk=400),
+    "random_blocks": lambda: _block_mask_case(),
+    "causal_plus_pad": lambda: make_case("causal_pad", B=1, Hq=4, Hkv=1, Sq=260, Sk=260, D=128, dtype="bf16",
+                                         seed=71, causal=True, mask="sa_pad", mask_args={"pad_frac": 0.2}),
+}
+
+
+def _block_mask_case():
+    """Mask with whole dead blocks, whole open blocks, bias blocks and ragged edges."""
+    c = make_case("random_blocks", B=2, Hq=2, Hkv=1, Sq=200, Sk=330, D=128, dtype="bf16", seed=72)
+    rng = np.random.default_rng(73)
+    m = np.zeros((2, 200, 330), np.float32)
+    for b in range(2):
+        for r in range(0, 200, 64):
+            for cc in range(0, 330, 64):
+                kind = rng.integers(0, 3)
+                if kind == 0:
+                    m[b, r:r + 64, cc:cc + 64] = -np.inf
+                elif kind == 2:
+                    m[b, r:r + 64, cc:cc + 64] = rng.standard_normal(m[b, r:r + 64, cc:cc + 64].shape)
+    m[0, 5, :] = -np.inf  # a fully masked row
+    c.mask = m
+    c.meta["mask_kind"] = "blocks"
+    return c
+
+
+@pytest.mark.parametrize("name", list(TILE_CASES))
+def test_mask_tile_map_and_skipping(name):
+    """The mask block classification matches numpy, and fwd + bwd that use it (skipping
+    dead blocks, not reading open ones) still match the oracle."""
+    c = TILE_CASES[name]()
+    t = upload(c)
+    tiles = binding.mask_tile_map(t["mask"], t["q"], t["k"])
+    torch.cuda.synchronize()
+    assert np.array_equal(tiles.cpu().numpy(), numpy_tile_map(c.mask))
+    o, lse = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
+                         q_offset=c.q_offset, mask_tiles=tiles)
+    delta = binding.bwd_preprocess(o, t["do"])
+    dq, dk, dv = binding.bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, mask=t["mask"], scale=c.scale,
+                             causal=c.causal, q_offset=c.q_offset, mask_tiles=tiles)
+    torch.cuda.synchronize()
+    got = {"O": host64(o), "LSE": host64(lse), "Delta": host64(delta), "dQ": host64(dq), "dK": host64(dk),
+           "dV": host64(dv)}
+    compare_full(c, got, oracle_full(c))
