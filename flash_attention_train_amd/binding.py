@@ -144,13 +144,20 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
 
 
 def mask_tile_map(mask: torch.Tensor, q: torch.Tensor, k: torch.Tensor, *, stream=None) -> torch.Tensor:
-    """Classify every 64 x 64 block of an additive mask (0 dead, 1 open, 2 mixed) for
-    reuse by fwd/bwd/bwd_chunked through their ``mask_tiles`` argument."""
+    """Classify every 64 x 64 block of an additive mask (0 dead, 1 open, 2 visibility bits,
+    3 finite biases) and record its visibility bits, for reuse by fwd/bwd/bwd_chunked
+    through their ``mask_tiles`` argument. The first ``mask_tile_count`` bytes are the classes."""
     p = make_params(q, k, scale=None, causal=False, q_offset=0, mask=mask)
     n = int(lib().fa_train_mask_tiles_bytes(ctypes.byref(p)))
     tiles = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
     _check("fa_train_mask_tiles", lib().fa_train_mask_tiles(ctypes.byref(p), tiles.data_ptr(), _stream_handle(stream)))
-    return tiles[:n]
+    return tiles
+
+
+def mask_tile_count(mask: torch.Tensor) -> int:
+    """Number of 64 x 64 blocks (and class bytes) of a [Bm, Sq, Sk] mask."""
+    Bm, Sq, Sk = mask.shape
+    return Bm * ((Sq + 63) // 64) * ((Sk + 63) // 64)
 
 
 def fwd(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, out=None, lse=None, stream=None,

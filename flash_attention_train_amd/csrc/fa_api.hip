@@ -115,6 +115,10 @@ fa::AttnShape shape_of(const fa_attn_params* p) {
   a.mask_sb = p->mask_stride_b;
   a.mask_sq = p->mask_stride_q;
   a.tiles = p->mask ? p->mask_tiles : nullptr;
+  const int64_t nblk = tile_batches(p) * tile_rows(p) * tile_cols(p);
+  const int64_t rowbits_off = (nblk + 255) / 256 * 256;
+  a.rowbits = a.tiles ? reinterpret_cast<const uint64_t*>(a.tiles + rowbits_off) : nullptr;
+  a.colbits = a.tiles ? a.rowbits + nblk * 64 : nullptr;
   a.tiles_ncol = (int)tile_cols(p);
   a.tiles_bstride = p->mask_stride_b == 0 ? 0 : (int)(tile_rows(p) * tile_cols(p));
   return a;
@@ -148,7 +152,10 @@ size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 // several workgroups whose partial sums meet in fp32 atomics, so splits are only
 // used when the unsplit grid would leave compute units idle.
 void choose_splits(const fa_attn_params* p, bool accumulate, int* kv_split, int* q_split) {
-  const int64_t target = 512;  // about two workgroups per compute unit
+  // Splitting pays only when the unsplit grid cannot give every compute unit a
+  // workgroup; measured on the workloads at hand, beyond that the atomics and the
+  // extra clear / convert passes cost more than the better balance gains.
+  const int64_t target = 256;
   const int64_t kv_units = (int64_t)((p->Sk + 127) / 128) * p->B * p->Hkv;
   const int64_t q_units = (int64_t)((p->Sq + 127) / 128) * p->B * p->Hq;
   const int64_t kv_pairs = (int64_t)((p->Sq + 63) / 64) * (p->Hq / p->Hkv);  // walk length of one key tile
@@ -413,7 +420,8 @@ fa_status fa_train_bwd_chunked(const fa_attn_params* p, const fa_view* q, const 
 
 size_t fa_train_mask_tiles_bytes(const fa_attn_params* p) {
   if (check_params(p) != FA_OK || !p->mask) return 0;
-  return (size_t)(tile_batches(p) * tile_rows(p) * tile_cols(p));
+  const int64_t nblk = tile_batches(p) * tile_rows(p) * tile_cols(p);
+  return (size_t)((nblk + 255) / 256 * 256 + 2 * nblk * 64 * 8);  // classes, row words, column words
 }
 
 fa_status fa_train_mask_tiles(const fa_attn_params* p, uint8_t* tiles, hipStream_t stream) {
@@ -423,10 +431,13 @@ fa_status fa_train_mask_tiles(const fa_attn_params* p, uint8_t* tiles, hipStream
   if (!p->mask) return fail(FA_ERR_NULL, "the params carry no mask");
   if (!tiles) return fail(FA_ERR_NULL, "tiles is NULL");
   const uintptr_t t = reinterpret_cast<uintptr_t>(tiles);
+  if (t % 8) return fail(FA_ERR_ALIGN, "tiles is not 8-byte aligned");
   const Extent et = {t, t + (uintptr_t)fa_train_mask_tiles_bytes(p)};
   const Extent em = mask_extent(p);
   if (overlaps(et, em)) return fail(FA_ERR_ALIAS, "tiles overlaps the mask");
-  return hip_status(fa::launch_mask_tiles(shape_of(p), tiles, stream), "mask tiles");
+  fa_attn_params q = *p;
+  q.mask_tiles = tiles;
+  return hip_status(fa::launch_mask_tiles(shape_of(&q), tiles, stream), "mask tiles");
 }
 
 const char* fa_train_status_str(fa_status s) {

@@ -3,8 +3,9 @@
 //     commit 86c140d: the tiled backward computes the LSE, then D, then the
 //     gradients per tile);
 //   * clearing the fp32 dQ accumulator;
-//   * converting the accumulated dQ to its output dtype with the softmax scale.
-// All three stream their operands once with 16-byte loads and stores.
+//   * converting the accumulated dQ to its output dtype with the softmax scale;
+//   * classifying the additive mask's 64 x 64 blocks for the forward and backward.
+// The first three stream their operands once with 16-byte loads and stores.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -66,24 +67,42 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const DqArgs p) {
   store8(dst, out);
 }
 
-// One workgroup per 64 x 64 mask block: dead if every entry is -inf, open if every
-// entry is 0, mixed otherwise (blocks are clipped at Sq and Sk).
-__global__ __launch_bounds__(256) void mask_tiles_kernel(const AttnShape a, uint8_t* tiles) {
+// One workgroup per 64 x 64 mask block (clipped at Sq and Sk; entries outside count as
+// masked for the bits and are ignored by the class): the visibility bits of every
+// row come from one wave ballot each, the column words from a bit transpose in LDS,
+// and the class from workgroup-wide votes.
+__global__ __launch_bounds__(256) void mask_tiles_kernel(const AttnShape a, uint8_t* tiles, uint64_t* rowbits,
+                                                         uint64_t* colbits) {
+  __shared__ uint64_t rows_lds[kMaskTile];
   const int ct = blockIdx.x, rt = blockIdx.y, bm = blockIdx.z;
+  const int64_t blk = ((int64_t)bm * gridDim.y + rt) * gridDim.x + ct;
   const float* M = a.mask + bm * a.mask_sb;
-  const int rows = min(kMaskTile, a.Sq - rt * kMaskTile), cols = min(kMaskTile, a.Sk - ct * kMaskTile);
-  int dead = 1, open = 1;
-  for (int e = threadIdx.x; e < kMaskTile * kMaskTile; e += 256) {
-    const int r = e / kMaskTile, c = e % kMaskTile;
-    if (r < rows && c < cols) {
-      const float v = M[(int64_t)(rt * kMaskTile + r) * a.mask_sq + ct * kMaskTile + c];
-      dead &= (v == neg_inf());
-      open &= (v == 0.f);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int any_vis = 0, any_masked = 0, any_bias = 0;
+  for (int r = wave; r < kMaskTile; r += 4) {
+    const int row = rt * kMaskTile + r, key = ct * kMaskTile + lane;
+    const bool in = row < a.Sq && key < a.Sk;
+    const float v = in ? M[(int64_t)row * a.mask_sq + key] : neg_inf();
+    const bool vis = in && v != neg_inf();
+    any_vis |= vis;
+    any_masked |= in && !vis;
+    any_bias |= vis && v != 0.f;
+    const uint64_t word = __ballot(vis);
+    if (lane == 0) {
+      rowbits[blk * kMaskTile + r] = word;
+      rows_lds[r] = word;
     }
   }
-  dead = __syncthreads_and(dead);
-  open = __syncthreads_and(open);
-  if (threadIdx.x == 0) tiles[((int64_t)bm * gridDim.y + rt) * gridDim.x + ct] = dead ? kTileDead : (open ? kTileOpen : kTileMixed);
+  any_vis = __syncthreads_or(any_vis);
+  any_masked = __syncthreads_or(any_masked);
+  any_bias = __syncthreads_or(any_bias);
+  if (wave == 0) {
+    uint64_t col = 0;
+    for (int i = 0; i < kMaskTile; ++i) col |= ((rows_lds[i] >> lane) & 1ull) << i;
+    colbits[blk * kMaskTile + lane] = col;
+  }
+  if (threadIdx.x == 0)
+    tiles[blk] = !any_vis ? kTileDead : any_bias ? kTileBias : any_masked ? kTileBits : kTileOpen;
 }
 
 template <typename T, int D>
@@ -113,7 +132,8 @@ hipError_t launch_preprocess(const PreArgs& p, int is_bf16, hipStream_t stream) 
 hipError_t launch_mask_tiles(const AttnShape& a, uint8_t* tiles, hipStream_t stream) {
   const int nrt = (a.Sq + kMaskTile - 1) / kMaskTile, nct = (a.Sk + kMaskTile - 1) / kMaskTile;
   const int bm = a.mask_sb == 0 ? 1 : a.B;
-  hipLaunchKernelGGL(mask_tiles_kernel, dim3(nct, nrt, bm), dim3(256), 0, stream, a, tiles);
+  hipLaunchKernelGGL(mask_tiles_kernel, dim3(nct, nrt, bm), dim3(256), 0, stream, a, tiles,
+                     const_cast<uint64_t*>(a.rowbits), const_cast<uint64_t*>(a.colbits));
   return hipGetLastError();
 }
 

@@ -188,9 +188,13 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
     load_pair(pn < npairs ? pn : p);  // the last pair reloads itself: no branch around the loads
     int h, q0;
     pair_of(p, h, q0);
-    int cls = kTileMixed;
+    int cls = kTileBias;
     if (MASK) cls = ct_w < nct ? tile_class(a, b, q0 / kMaskTile, ct_w) : kTileDead;
-    const bool mixed = MASK && cls == kTileMixed;
+    const bool bias = MASK && cls == kTileBias;  // read mask values
+    const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
+    uint64_t vword = 0;  // this lane's key: bit i = row q0 + i visible
+    if (bits)
+      vword = a.colbits[(int64_t)tile_index(a, b, q0 / kMaskTile, ct_w) * kMaskTile + (key - ct_w * kMaskTile)];
     const bf16* qb_lds = q_lds + buf * KV_BM * RS;
     const bf16* db_lds = do_lds + buf * KV_BM * RS;
     const float* lse_b = lse_lds + buf * KV_BM;
@@ -218,6 +222,7 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
         mma(sacc, qa, kf[s]);
         mma(dpacc, da, vf[s]);
       }
+      const uint32_t vb = (uint32_t)(vword >> (32 * qb)) >> (4 * g);
       // lane (key, half g), register r -> query row 32 qb + 8 (r/4) + 4 g + r%4
       #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
@@ -229,10 +234,11 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
           const int r = 4 * rr + e;
           float x = sacc[r];
           bool vis = true;
-          if (mixed || edge) {
+          if (bias || bits || edge) {
             const int c = 32 * qb + 8 * rr + e;  // ql - 4 g
             vis = c >= qlo && c < qhi;
-            if (mixed && vis) x += a.mask[b * a.mask_sb + (int64_t)(q0 + ql4 + e) * a.mask_sq + key] * args.inv_scale;
+            if (bits) vis = vis && ((vb >> (8 * rr + e)) & 1u);
+            if (bias && vis) x += a.mask[b * a.mask_sb + (int64_t)(q0 + ql4 + e) * a.mask_sq + key] * args.inv_scale;
           }
           const float pv = vis ? fast_exp2(fmaf(x, cs, -l4[e])) : 0.f;
           sacc[r] = pv;
@@ -415,9 +421,12 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
     const int buf = it & 1;
     const int ktn = next_live(kt + plan.q_split);
     load_tile(ktn < kt_end ? ktn : kt);  // the last tile reloads itself: no branch around the loads
-    int cls = kTileMixed;
+    int cls = kTileBias;
     if (MASK) cls = rt_w < nrt ? tile_class(a, b, rt_w, kt) : kTileDead;
-    const bool mixed = MASK && cls == kTileMixed;
+    const bool bias = MASK && cls == kTileBias;  // read mask values
+    const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
+    uint64_t vword = 0;  // this lane's row: bit j = key kt * 64 + j visible
+    if (bits) vword = a.rowbits[(int64_t)tile_index(a, b, rt_w, kt) * kMaskTile + (row - rt_w * kMaskTile)];
     const bf16* kb_lds = k_lds + buf * Q_BN * RS;
     const bf16* vb_lds = v_lds + buf * Q_BN * RS;
     const int key0 = kt * Q_BN;
@@ -443,12 +452,13 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
         mma(st, ka, qf[s]);
         mma(dpt, va, df[s]);
       }
+      const uint32_t vb = (uint32_t)(vword >> (32 * kb)) >> (4 * g);
       // lane (query row, half g), register r -> key 32 kb + 8 (r/4) + 4 g + r%4
       #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int k4 = key0 + 32 * kb + 8 * rr + 4 * g;
         float mv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (mixed && Mrow) {
+        if (bias && Mrow) {
           if (k4 + 3 < a.Sk && args.mask_vec4) {
             const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mrow + k4);
             mv[0] = m4[0]; mv[1] = m4[1]; mv[2] = m4[2]; mv[3] = m4[3];
@@ -462,9 +472,10 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
           const int r = 4 * rr + e;
           float x = st[r];
           bool vis = true;
-          if (mixed || edge) {
+          if (bias || bits || edge) {
             vis = 32 * kb + 8 * rr + e < klim;
-            if (MASK) x += mv[e] * args.inv_scale;  // mv = 0 unless the block is mixed
+            if (bits) vis = vis && ((vb >> (8 * rr + e)) & 1u);
+            if (MASK) x += mv[e] * args.inv_scale;  // mv = 0 unless the block has biases
           }
           const float pv = vis ? fast_exp2(fmaf(x, cs, -lse2)) : 0.f;
           st[r] = pv * (dpt[r] - dlt);

@@ -181,9 +181,25 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     load_tile(more ? ktn : kt);  // the last iteration reloads its own tile: no branch around loads
     const bf16* kb_lds = k_lds[buf];
     const bf16* vb_lds = v_lds[buf];
-    int cls = kTileMixed;
+    int cls = kTileBias;
     if (MASK) cls = rt_w < nrt ? tile_class(a, b, rt_w, (kt * BN) / kMaskTile) : kTileDead;
     if (cls != kTileDead) {
+    const bool bias = MASK && cls == kTileBias;  // read mask values
+    const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
+    // this lane's visibility bits for the tile's keys, shifted down by 4 g
+    uint32_t vb[QB][KB];
+    if (bits) {
+      const int64_t base = (int64_t)tile_index(a, b, rt_w, (kt * BN) / kMaskTile) * kMaskTile;
+      #pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const uint64_t w = a.rowbits[base + (qw + 32 * qb + r32 - rt_w * kMaskTile)];
+        #pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int half = BN == 64 ? kb : (kt & 1);
+          vb[qb][kb] = (uint32_t)(w >> (32 * half)) >> (4 * g);
+        }
+      }
+    }
 
     // S^T = K Q^T for both 32-key blocks; each K fragment serves all QB query blocks
     f32x16 st[QB][KB];
@@ -221,10 +237,9 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int row = qw + 32 * qb + r32;
-      const bool mixed = MASK && cls == kTileMixed;
-      if (mixed || edge) {
+      if (bias || bits || edge) {
         const float* Mrow = nullptr;
-        if (mixed && row < a.Sq) Mrow = a.mask + b * a.mask_sb + (int64_t)row * a.mask_sq;
+        if (bias && row < a.Sq) Mrow = a.mask + b * a.mask_sb + (int64_t)row * a.mask_sq;
         #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           #pragma unroll
@@ -242,10 +257,11 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
             }
             #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const bool vis = 32 * kb + 8 * rr + 4 * g + e < lim[qb];
+              bool vis = 32 * kb + 8 * rr + 4 * g + e < lim[qb];
+              if (bits) vis = vis && ((vb[qb][kb] >> (8 * rr + e)) & 1u);
               // the mask enters the raw score as M / scale so that one fma applies both later
               float x = st[qb][kb][4 * rr + e];
-              if (MASK) x += mv[e] * args.inv_scale;  // mv = 0 unless the block is mixed
+              if (MASK) x += mv[e] * args.inv_scale;  // mv = 0 unless the block has biases
               st[qb][kb][4 * rr + e] = vis ? x : neg_inf();
             }
           }

@@ -23,17 +23,23 @@ struct AttnShape {
   float scale;       // multiplies <q, k>
   const float* mask; // additive [b][i][j] fp32 or nullptr
   int64_t mask_sb, mask_sq;
-  const uint8_t* tiles;  // mask block classes [Bm][ceil(Sq/64)][ceil(Sk/64)] or nullptr
-  int tiles_bstride;     // blocks per mask batch entry (0 when the mask is shared)
-  int tiles_ncol;        // ceil(Sk / 64)
+  const uint8_t* tiles;      // mask block classes [Bm][ceil(Sq/64)][ceil(Sk/64)] or nullptr
+  const uint64_t* rowbits;   // per block, 64 words: bit j of word i = entry (i, j) visible
+  const uint64_t* colbits;   // per block, 64 words: bit i of word j = entry (i, j) visible
+  int tiles_bstride;         // blocks per mask batch entry (0 when the mask is shared)
+  int tiles_ncol;            // ceil(Sk / 64)
 };
 
-constexpr int kTileDead = 0, kTileOpen = 1, kTileMixed = 2, kMaskTile = 64;
+// block classes: dead = all -inf, open = all 0, bits = only 0 / -inf, bias = finite biases
+constexpr int kTileDead = 0, kTileOpen = 1, kTileBits = 2, kTileBias = 3, kMaskTile = 64;
 
-// class of mask block (b, row block rt, key block ct); mixed when no map is given
+__device__ __forceinline__ int tile_index(const AttnShape& a, int b, int rt, int ct) {
+  return b * a.tiles_bstride + rt * a.tiles_ncol + ct;
+}
+// class of mask block (b, row block rt, key block ct); "bias" (read every value) without a map
 __device__ __forceinline__ int tile_class(const AttnShape& a, int b, int rt, int ct) {
-  if (!a.tiles) return kTileMixed;
-  return a.tiles[b * a.tiles_bstride + rt * a.tiles_ncol + ct];
+  if (!a.tiles) return kTileBias;
+  return a.tiles[tile_index(a, b, rt, ct)];
 }
 
 struct FwdArgs {

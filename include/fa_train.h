@@ -147,18 +147,23 @@ fa_status fa_train_bwd_chunked(const fa_attn_params* p, const fa_view* q, const 
 /* Mask block classes written by fa_train_mask_tiles. */
 #define FA_TILE_DEAD 0  /* every entry of the block is -inf */
 #define FA_TILE_OPEN 1  /* every entry of the block is exactly 0 */
-#define FA_TILE_MIXED 2 /* anything else (finite biases, partly masked) */
+#define FA_TILE_BITS 2  /* entries are 0 or -inf, both present: a visibility pattern */
+#define FA_TILE_BIAS 3  /* some entry is a finite non-zero bias */
 #define FA_MASK_TILE 64 /* block edge, in query rows and keys */
 
-/* Bytes of the mask tile map for p: Bm * ceil(Sq/64) * ceil(Sk/64), Bm = 1 when
- * mask_stride_b == 0, else B. 0 if p has no mask or is invalid. */
+/* Bytes of the mask tile map for p (0 if p has no mask or is invalid). With
+ * nblk = Bm * ceil(Sq/64) * ceil(Sk/64) (Bm = 1 when mask_stride_b == 0, else B), the
+ * map starts with nblk class bytes, block (bm, rt, ct) at (bm * ceil(Sq/64) + rt) *
+ * ceil(Sk/64) + ct, followed by per-block visibility bit words for the kernels. */
 size_t fa_train_mask_tiles_bytes(const fa_attn_params* p);
 
-/* Classifies every 64 x 64 block of p's mask (clipped at Sq and Sk) into the
- * FA_TILE_* classes, one byte per block at tiles[(bm * ceil(Sq/64) + rt) * ceil(Sk/64) + ct].
- * The map depends only on the mask, so one map serves the forward and the backward and
- * every layer that shares the mask. Errors: FA_ERR_NULL (no mask, NULL tiles), the
- * shape and stride errors of the other entry points, FA_ERR_HIP. */
+/* Classifies every 64 x 64 block of p's mask (clipped at Sq and Sk) into the FA_TILE_*
+ * classes and records each block's visibility bits (rows and columns of 64 bits).
+ * The map depends only on the mask, so one map serves the forward and the backward
+ * and every layer that shares the mask. `tiles`: device memory of
+ * fa_train_mask_tiles_bytes(p) bytes, 8-byte aligned. Errors: FA_ERR_NULL (no mask,
+ * NULL tiles), FA_ERR_ALIGN, the shape and stride errors of the other entry points,
+ * FA_ERR_HIP. */
 fa_status fa_train_mask_tiles(const fa_attn_params* p, uint8_t* tiles, hipStream_t stream);
 
 /* Static text for a status code. */

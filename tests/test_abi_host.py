@@ -139,12 +139,13 @@ def test_mask_tiles_host_checks():
     L = B.lib()
     assert L.fa_train_mask_tiles_bytes(ctypes.byref(params())) == 0  # no mask
     m = params(Sq=130, Sk=70, mask=BASE + 9 * (1 << 24), mask_stride_q=72, mask_stride_b=0)
-    assert L.fa_train_mask_tiles_bytes(ctypes.byref(m)) == 3 * 2
+    assert L.fa_train_mask_tiles_bytes(ctypes.byref(m)) == 256 + 2 * (3 * 2) * 64 * 8
     mb = params(B=2, Sq=130, Sk=70, mask=BASE + 9 * (1 << 24), mask_stride_q=72, mask_stride_b=130 * 72)
-    assert L.fa_train_mask_tiles_bytes(ctypes.byref(mb)) == 2 * 3 * 2
+    assert L.fa_train_mask_tiles_bytes(ctypes.byref(mb)) == 256 + 2 * (2 * 3 * 2) * 64 * 8
     assert L.fa_train_mask_tiles(ctypes.byref(params()), BASE, None) == 1
     assert L.fa_train_mask_tiles(ctypes.byref(m), None, None) == 1
     assert L.fa_train_mask_tiles(ctypes.byref(m), BASE + 9 * (1 << 24) + 64, None) == 6
+    assert L.fa_train_mask_tiles(ctypes.byref(m), BASE + 3, None) == 5
 
 
 def test_probe_rejects_bad_arguments():

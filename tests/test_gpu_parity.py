@@ -212,7 +212,13 @@ def numpy_tile_map(mask: np.ndarray) -> np.ndarray:
         for r in range(nr):
             for c in range(nc):
                 blk = mask[b, 64 * r:64 * r + 64, 64 * c:64 * c + 64]
-                out[b, r, c] = 0 if np.all(blk == -np.inf) else (1 if np.all(blk == 0) else 2)
+                fin = np.isfinite(blk)
+                if not fin.any():
+                    out[b, r, c] = 0
+                elif np.any(blk[fin] != 0):
+                    out[b, r, c] = 3
+                else:
+                    out[b, r, c] = 1 if fin.all() else 2
     return out.reshape(-1)
 
 
@@ -252,7 +258,20 @@ def test_mask_tile_map_and_skipping(name):
     t = upload(c)
     tiles = binding.mask_tile_map(t["mask"], t["q"], t["k"])
     torch.cuda.synchronize()
-    assert np.array_equal(tiles.cpu().numpy(), numpy_tile_map(c.mask))
+    nblk = binding.mask_tile_count(t["mask"])
+    assert np.array_equal(tiles[:nblk].cpu().numpy(), numpy_tile_map(c.mask))
+    # the visibility words: bit j of row word i / bit i of column word j = entry (i, j) finite
+    Bm, Sq, Sk = c.mask.shape
+    nr, nc = (Sq + 63) // 64, (Sk + 63) // 64
+    off = (nblk + 255) // 256 * 256
+    words = tiles[off:off + 2 * nblk * 64 * 8].cpu().numpy().view(np.uint64).reshape(2, Bm, nr, nc, 64)
+    vis = np.zeros((Bm, nr * 64, nc * 64), bool)
+    vis[:, :Sq, :Sk] = np.isfinite(c.mask)
+    blocks = vis.reshape(Bm, nr, 64, nc, 64).transpose(0, 1, 3, 2, 4)  # [Bm, nr, nc, row, col]
+    weights = (np.uint64(1) << np.arange(64, dtype=np.uint64))
+    rows = (blocks.astype(np.uint64) * weights[None, None, None, None, :]).sum(axis=4, dtype=np.uint64)
+    cols = (blocks.astype(np.uint64) * weights[None, None, None, :, None]).sum(axis=3, dtype=np.uint64)
+    assert np.array_equal(words[0], rows) and np.array_equal(words[1], cols)
     o, lse = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
                          q_offset=c.q_offset, mask_tiles=tiles)
     delta = binding.bwd_preprocess(o, t["do"])
