@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--workload", default="dit_sa")
     ap.add_argument("--extra", default="lm_causal,dit_ca")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (the reference kernel that "
+                         "scales the HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -69,6 +72,7 @@ class Workload:
         self.dv = torch.empty_like(self.v)
         nws = binding.bwd_workspace_bytes(self.q, self.k, scale=c.scale, causal=c.causal, q_offset=c.q_offset,
                                           mask=self.mask)
+        self.ws_bytes = nws
         self.ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
         self.B = binding
         self.tiles = None
@@ -142,6 +146,45 @@ def time_workload(w: Workload, steps: int, warmup: int) -> dict:
     }
 
 
+KERNEL_SOURCES = ("flash_attention_train_amd/csrc/fa_bwd_bf16.hip", "flash_attention_train_amd/csrc/fa_device.h",
+                  "flash_attention_train_amd/csrc/fa_kernels.h")
+
+
+def source_digest(paths=KERNEL_SOURCES) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for p in paths:
+        with open(os.path.join(root, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the backward kernel from the committed counter summary,
+    or None when there is none for this workload or the kernel source changed since."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic_bwd.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("workloads", {}).get(workload)
+    if not entry or rec.get("source_sha256") != source_digest():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(mib: int):
+    import torch
+    src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": mib << 20, "launches": 5}), flush=True)
+
+
 def cpu_baseline(key: str) -> dict:
     """The oracle as it stands (fp64 C, all host cores) on one whole step of the
     workload: fwd + bwd, mask-adjusted FLOPs per second."""
@@ -183,6 +226,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     log(f"[bench] device {torch.cuda.get_device_name(0)}; workload {args.workload}")
     w = Workload(args.workload)
@@ -200,6 +246,8 @@ def main():
         torch.cuda.empty_cache()
 
     peak = accounting.MI355X_BF16_DENSE_TFLOPS
+    # the backward call is a single kernel launch when it needs no workspace (no split work)
+    single = w.ws_bytes == 0
     achieved = r["bwd_tflops"]
     line = {
         "metric": METRIC,
@@ -217,9 +265,11 @@ def main():
         "config": {"workload": configs.WORKLOADS[args.workload].title, "global_batch": w.case.B,
                    "seq_len": w.case.Sq, "unmasked_pairs": w.pairs, "gflop_per_step": round(r["gflop_per_step"], 3)},
         "pct_of_peak": round(100.0 * r["tflops"] / peak, 2),
-        "roofline": {"kernel": "fa_train_bwd (dQ clear + backward + dQ convert)", "bound": "mfma",
+        "roofline": {"kernel": "bwd_bf16_kernel (fa_train_bwd)" if single else
+                     "fa_train_bwd (clear + bwd_bf16_kernel + convert)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None},
+                     "frac": round(achieved / peak, 4), "traffic": measured_traffic(args.workload),
+                     "flop_per_launch": w.bwd_flops, "launch_ms": round(r["bwd_ms_mean"], 5)},
         "breakdown": {k: round(v, 4) if isinstance(v, float) else v for k, v in r.items()},
         "extra": extra,
         "gpu": torch.cuda.get_device_name(0),

@@ -1,9 +1,10 @@
 // fa_bwd.hip -- backward of the fused attention op: dQ, dK, dV.
 //
 // The backward recomputes P from the forward's LSE, tile by tile over the KV
-// window, and sums the GQA group inside the kernel (llama.cpp pull request 57,
-// commit 86c140d: "LSE, D, then grads per tile; GQA group-sum"; native GQA
-// without head expansion, "Flash Attn Training" skill page, section 6, trap 5).
+// window, and adds the dK/dV of every query head of a group into the group's KV
+// head inside the kernel (llama.cpp pull request 57, commit 86c140d, the tiled
+// backward; native GQA without head expansion, "Flash Attn Training" skill page,
+// section 6, trap 5).
 //
 // Work split (KV-stationary): one workgroup per (batch, KV head, BN-key tile),
 // NW waves of 32 keys each. The workgroup walks every query head of its group and

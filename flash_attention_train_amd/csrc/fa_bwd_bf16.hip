@@ -1,24 +1,26 @@
 // fa_bwd_bf16.hip -- the bf16 backward: dQ, dK, dV in one launch.
 //
-// The backward recomputes P from the forward's LSE tile by tile and sums dK/dV
-// over each query-head group (llama.cpp pull request 57, commit 86c140d: "LSE,
-// D, then grads per tile; GQA group-sum"). On gfx950 it is split into two kinds
-// of workgroups that run side by side in one grid, so that neither needs the
-// other's results and no score tile ever travels through LDS or memory:
+// The backward rebuilds P tile by tile from the forward's per-row LSE, uses the
+// preprocessed Delta = rowsum(dO o O), and adds the dK/dV contributions of every
+// query head of a group into the group's one KV head (llama.cpp pull request 57,
+// commit 86c140d, the tiled backward). On gfx950 it is split into two kinds of
+// workgroups that run side by side in one grid, so that neither needs the other's
+// results and no score tile ever travels through LDS or memory:
 //
 //  dK/dV workgroups (KV-stationary): 4 waves x 32 keys own a 128-key tile of one
 //    KV head. They walk the (query head of the group, 64-row query tile) pairs
-//    that can see the keys, with the Q and dO tiles staged in LDS (double-
-//    buffered through registers) and shared by the waves. Per 32-row block:
+//    that can see the keys, with the Q and dO tiles copied straight from global
+//    memory into LDS (double-buffered, XOR-swizzled rows) and shared by the waves.
+//    Per 32-row block:
 //      S  = Q K^T, dP = dO V^T   (A: Q / dO rows from LDS, B: K / V in registers)
 //      P  = exp2(S c + M log2e - LSE log2e), dS = P (dP - Delta)
 //      dV += P^T dO, dK += dS^T Q  (A: P / dS straight from the accumulators,
 //                                   B: dO^T / Q^T by LDS transpose reads)
 //  dQ workgroups (Q-stationary): 4 waves x 32 rows own a 128-row query tile of
-//    one head and walk its visible 64-key tiles (K and V staged in LDS, double-
-//    buffered), computing S^T = K Q^T and dP^T = V dO^T so that each lane holds
-//    one query row; dS^T then feeds dQ += dS K directly as the A operand, with
-//    the K operand read by LDS transpose reads.
+//    one head and walk its visible 64-key tiles (K and V staged in LDS the same
+//    way), computing S^T = K Q^T and dP^T = V dO^T so that each lane holds one
+//    query row; dS^T then feeds dQ += dS K directly as the A operand, with the K
+//    operand read by LDS transpose reads.
 //
 // When a problem has too few tiles to fill the GPU, the dK/dV walk is split over
 // several workgroups per key tile and the dQ walk over several per query tile;
@@ -30,12 +32,11 @@
 // section 6, traps 8 and 9).
 #include "fa_device.h"
 #include "fa_kernels.h"
+#include "fa_tile.h"
 
 namespace fa {
 
 namespace {
-
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int KV_BN = 128;  // keys per dK/dV workgroup
 constexpr int KV_BM = 64;   // query rows per staged tile of the dK/dV walk
@@ -49,11 +50,6 @@ __device__ __forceinline__ f32x16 zeros16() {
   return z;
 }
 
-__device__ __forceinline__ bf16x4 tr_read(const bf16* lds_base, int elem_offset) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (lds_bf16x4*)((__attribute__((address_space(3))) bf16*)lds_base + elem_offset));
-}
-
 __device__ __forceinline__ void atomic_add_f32(float* p, float v) {
   __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -63,12 +59,11 @@ __device__ __forceinline__ void atomic_add_f32(float* p, float v) {
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool MASK>
 __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
-  constexpr int RS = D + 8;  // LDS row stride (elements)
   constexpr int DS = D / 16, DB = D / 32;
-  constexpr int CPT = KV_BM * D / 8 / 256;  // 16-byte chunks per thread per tensor
-  bf16* q_lds = reinterpret_cast<bf16*>(smem);                 // [2][KV_BM * RS]
-  bf16* do_lds = q_lds + 2 * KV_BM * RS;                       // [2][KV_BM * RS]
-  float* lse_lds = reinterpret_cast<float*>(do_lds + 2 * KV_BM * RS);  // [2][KV_BM]
+  using TL = Tile<D>;
+  bf16* q_lds = reinterpret_cast<bf16*>(smem);                 // [2][KV_BM * D]
+  bf16* do_lds = q_lds + 2 * KV_BM * D;                        // [2][KV_BM * D]
+  float* lse_lds = reinterpret_cast<float*>(do_lds + 2 * KV_BM * D);  // [2][KV_BM]
   float* dlt_lds = lse_lds + 2 * KV_BM;                        // [2][KV_BM]
 
   const AttnShape& a = args.a;
@@ -116,39 +111,27 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
   }
   const int npairs = (nqt - qt0) * a.G;
 
-  bf16x8 qpre[CPT], dpre[CPT];
   float lpre = 0.f;
   auto pair_of = [&](int p, int& h, int& q0) {
     h = hk * a.G + p % a.G;
     q0 = (qt0 + p / a.G) * KV_BM;
   };
-  auto load_pair = [&](int p) {
+  // stage a pair's Q and dO tiles straight into LDS (rows past the end repeat the last
+  // row, masked out on the tail tile) and fetch its LSE / Delta into a register
+  auto stage_pair = [&](int p, int buf) {
     int h, q0;
     pair_of(p, h, q0);
-    const bf16* Q = static_cast<const bf16*>(args.q) + b * args.sq.b + h * args.sq.h;
-    const bf16* dO = static_cast<const bf16*>(args.dout) + b * args.sdo.b + h * args.sdo.h;
-    // rows past the end load the last row: they are masked (P = 0) on the tail tile
-    #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i;
-      const int row = min(q0 + c / (D / 8), a.Sq - 1), d0 = (c % (D / 8)) * 8;
-      qpre[i] = *reinterpret_cast<const bf16x8*>(Q + (int64_t)row * args.sq.s + d0);
-      dpre[i] = *reinterpret_cast<const bf16x8*>(dO + (int64_t)row * args.sdo.s + d0);
-    }
+    const bf16* Q = static_cast<const bf16*>(args.q) + b * args.sq.b + h * args.sq.h + (int64_t)q0 * args.sq.s;
+    const bf16* dO = static_cast<const bf16*>(args.dout) + b * args.sdo.b + h * args.sdo.h + (int64_t)q0 * args.sdo.s;
+    TL::template stage<KV_BM, 256>(q_lds + buf * KV_BM * D, Q, args.sq.s, a.Sq - q0);
+    TL::template stage<KV_BM, 256>(do_lds + buf * KV_BM * D, dO, args.sdo.s, a.Sq - q0);
     if (tid < 2 * KV_BM) {
       const int row = min(q0 + (tid % KV_BM), a.Sq - 1);
       lpre = tid < KV_BM ? args.lse[b * args.lse_sb + h * args.lse_sh + row] * kLog2e
                          : args.delta[b * args.delta_sb + h * args.delta_sh + row];
     }
   };
-  auto store_pair = [&](int buf) {
-    #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / (D / 8), d0 = (c % (D / 8)) * 8;
-      *reinterpret_cast<bf16x8*>(q_lds + buf * KV_BM * RS + row * RS + d0) = qpre[i];
-      *reinterpret_cast<bf16x8*>(do_lds + buf * KV_BM * RS + row * RS + d0) = dpre[i];
-    }
+  auto store_stats = [&](int buf) {
     if (tid < KV_BM)
       lse_lds[buf * KV_BM + tid] = lpre;
     else if (tid < 2 * KV_BM)
@@ -178,14 +161,15 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
 
   int p = next_live(split);
   if (p < npairs) {
-    load_pair(p);
-    store_pair(0);
+    stage_pair(p, 0);
+    wait_vm();
+    store_stats(0);
   }
   __syncthreads();
   for (int it = 0; p < npairs; ++it) {
     const int buf = it & 1;
     const int pn = next_live(p + plan.kv_split);
-    load_pair(pn < npairs ? pn : p);  // the last pair reloads itself: no branch around the loads
+    if (pn < npairs) stage_pair(pn, buf ^ 1);  // lands while this pair is being processed
     int h, q0;
     pair_of(p, h, q0);
     int cls = kTileBias;
@@ -195,8 +179,8 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
     uint64_t vword = 0;  // this lane's key: bit i = row q0 + i visible
     if (bits)
       vword = a.colbits[(int64_t)tile_index(a, b, q0 / kMaskTile, ct_w) * kMaskTile + (key - ct_w * kMaskTile)];
-    const bf16* qb_lds = q_lds + buf * KV_BM * RS;
-    const bf16* db_lds = do_lds + buf * KV_BM * RS;
+    const bf16* qb_lds = q_lds + buf * KV_BM * D;
+    const bf16* db_lds = do_lds + buf * KV_BM * D;
     const float* lse_b = lse_lds + buf * KV_BM;
     const float* dlt_b = dlt_lds + buf * KV_BM;
     bool edge = q0 + KV_BM > a.Sq || n0 + KV_BN > a.Sk;
@@ -212,17 +196,17 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
     qhi -= 4 * g;
 
     #pragma unroll
-    for (int qb = 0; qb < KV_BM / 32; ++qb) {
-      if (cls == kTileDead) break;
+    for (int qb = 0; qb < KV_BM / 32 && cls != kTileDead; ++qb) {
       f32x16 sacc = zeros16(), dpacc = zeros16();
       #pragma unroll
       for (int s = 0; s < DS; ++s) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb_lds + (32 * qb + r32) * RS + 16 * s + 8 * g);
-        const bf16x8 da = *reinterpret_cast<const bf16x8*>(db_lds + (32 * qb + r32) * RS + 16 * s + 8 * g);
+        const bf16x8 qa = TL::read_chunk(qb_lds, 32 * qb + r32, 2 * s + g);
+        const bf16x8 da = TL::read_chunk(db_lds, 32 * qb + r32, 2 * s + g);
         mma(sacc, qa, kf[s]);
         mma(dpacc, da, vf[s]);
       }
-      const uint32_t vb = (uint32_t)(vword >> (32 * qb)) >> (4 * g);
+      uint32_t vb = 0;
+      if (MASK) vb = (uint32_t)(vword >> (32 * qb)) >> (4 * g);
       // lane (key, half g), register r -> query row 32 qb + 8 (r/4) + 4 g + r%4
       #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
@@ -234,12 +218,13 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
           const int r = 4 * rr + e;
           float x = sacc[r];
           bool vis = true;
-          if (bias || bits || edge) {
+          if (edge || bits) {
             const int c = 32 * qb + 8 * rr + e;  // ql - 4 g
             vis = c >= qlo && c < qhi;
             if (bits) vis = vis && ((vb >> (8 * rr + e)) & 1u);
-            if (bias && vis) x += a.mask[b * a.mask_sb + (int64_t)(q0 + ql4 + e) * a.mask_sq + key] * args.inv_scale;
           }
+          if (MASK && bias && vis)
+            x += a.mask[b * a.mask_sb + (int64_t)(q0 + ql4 + e) * a.mask_sq + key] * args.inv_scale;
           const float pv = vis ? fast_exp2(fmaf(x, cs, -l4[e])) : 0.f;
           sacc[r] = pv;
           dpacc[r] = pv * (dpacc[r] - d4[e]);
@@ -256,10 +241,10 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
         #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const int col = 32 * db + tr_col;
-          const bf16x4 d0 = tr_read(db_lds, rbase * RS + col);
-          const bf16x4 d1 = tr_read(db_lds, (rbase + 8) * RS + col);
-          const bf16x4 q0v = tr_read(qb_lds, rbase * RS + col);
-          const bf16x4 q1v = tr_read(qb_lds, (rbase + 8) * RS + col);
+          const bf16x4 d0 = TL::read_tr(db_lds, rbase, col);
+          const bf16x4 d1 = TL::read_tr(db_lds, rbase + 8, col);
+          const bf16x4 q0v = TL::read_tr(qb_lds, rbase, col);
+          const bf16x4 q1v = TL::read_tr(qb_lds, rbase + 8, col);
           const bf16x8 dob = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
           const bf16x8 qbt = {q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
           mma(dv[db], pa, dob);
@@ -267,7 +252,8 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
         }
       }
     }
-    if (pn < npairs) store_pair(buf ^ 1);
+    wait_vm();
+    if (pn < npairs) store_stats(buf ^ 1);
     __syncthreads();
     p = pn;
   }
@@ -315,11 +301,10 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool MASK>
 __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
-  constexpr int RS = D + 8;
   constexpr int DS = D / 16, DB = D / 32;
-  constexpr int CPT = Q_BN * D / 8 / 256;
-  bf16* k_lds = reinterpret_cast<bf16*>(smem);  // [2][Q_BN * RS]
-  bf16* v_lds = k_lds + 2 * Q_BN * RS;          // [2][Q_BN * RS]
+  using TL = Tile<D>;
+  bf16* k_lds = reinterpret_cast<bf16*>(smem);  // [2][Q_BN * D]
+  bf16* v_lds = k_lds + 2 * Q_BN * D;           // [2][Q_BN * D]
 
   const AttnShape& a = args.a;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -373,25 +358,12 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
     kt_end = last_key < 0 ? 0 : (int)((last_key / Q_BN + 1) < nkt ? (last_key / Q_BN + 1) : nkt);
   }
 
-  bf16x8 kpre[CPT], vpre[CPT];
-  auto load_tile = [&](int kt) {
-    // keys past the end load the last key: they are masked (P = 0) on the tail tile
-    #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i;
-      const int kk = min(kt * Q_BN + c / (D / 8), a.Sk - 1), d0 = (c % (D / 8)) * 8;
-      kpre[i] = *reinterpret_cast<const bf16x8*>(K + (int64_t)kk * args.sk.s + d0);
-      vpre[i] = *reinterpret_cast<const bf16x8*>(V + (int64_t)kk * args.sv.s + d0);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i;
-      const int rr = c / (D / 8), d0 = (c % (D / 8)) * 8;
-      *reinterpret_cast<bf16x8*>(k_lds + buf * Q_BN * RS + rr * RS + d0) = kpre[i];
-      *reinterpret_cast<bf16x8*>(v_lds + buf * Q_BN * RS + rr * RS + d0) = vpre[i];
-    }
+  // stage K and V rows [key0, key0 + Q_BN) straight into LDS (keys past the end repeat
+  // the last key, masked out on the tail tile)
+  auto stage_tile = [&](int kt, int buf) {
+    const int key0 = kt * Q_BN;
+    TL::template stage<Q_BN, 256>(k_lds + buf * Q_BN * D, K + (int64_t)key0 * args.sk.s, args.sk.s, a.Sk - key0);
+    TL::template stage<Q_BN, 256>(v_lds + buf * Q_BN * D, V + (int64_t)key0 * args.sv.s, args.sv.s, a.Sk - key0);
   };
 
   const int G16 = lane >> 4, L16 = lane & 15;
@@ -412,23 +384,21 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
   const int rt_w = qw / kMaskTile;
 
   int kt = next_live(split);
-  if (kt < kt_end) {
-    load_tile(kt);
-    store_tile(0);
-  }
+  if (kt < kt_end) stage_tile(kt, 0);
+  wait_vm();
   __syncthreads();
   for (int it = 0; kt < kt_end; ++it) {
     const int buf = it & 1;
     const int ktn = next_live(kt + plan.q_split);
-    load_tile(ktn < kt_end ? ktn : kt);  // the last tile reloads itself: no branch around the loads
+    if (ktn < kt_end) stage_tile(ktn, buf ^ 1);  // lands while this tile is being processed
     int cls = kTileBias;
     if (MASK) cls = rt_w < nrt ? tile_class(a, b, rt_w, kt) : kTileDead;
     const bool bias = MASK && cls == kTileBias;  // read mask values
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
     uint64_t vword = 0;  // this lane's row: bit j = key kt * 64 + j visible
     if (bits) vword = a.rowbits[(int64_t)tile_index(a, b, rt_w, kt) * kMaskTile + (row - rt_w * kMaskTile)];
-    const bf16* kb_lds = k_lds + buf * Q_BN * RS;
-    const bf16* vb_lds = v_lds + buf * Q_BN * RS;
+    const bf16* kb_lds = k_lds + buf * Q_BN * D;
+    const bf16* vb_lds = v_lds + buf * Q_BN * D;
     const int key0 = kt * Q_BN;
     bool edge = key0 + Q_BN > a.Sk || qw + 32 > a.Sq;
     if (CAUSAL) edge = edge || ((int64_t)key0 + Q_BN - 1 > a.q_offset + qw);
@@ -442,23 +412,23 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
 
     // one 32-key block at a time keeps the live accumulators small
     #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (cls == kTileDead) break;
+    for (int kb = 0; kb < 2 && cls != kTileDead; ++kb) {
       f32x16 st = zeros16(), dpt = zeros16();
       #pragma unroll
       for (int s = 0; s < DS; ++s) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb_lds + (32 * kb + r32) * RS + 16 * s + 8 * g);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vb_lds + (32 * kb + r32) * RS + 16 * s + 8 * g);
+        const bf16x8 ka = TL::read_chunk(kb_lds, 32 * kb + r32, 2 * s + g);
+        const bf16x8 va = TL::read_chunk(vb_lds, 32 * kb + r32, 2 * s + g);
         mma(st, ka, qf[s]);
         mma(dpt, va, df[s]);
       }
-      const uint32_t vb = (uint32_t)(vword >> (32 * kb)) >> (4 * g);
+      uint32_t vb = 0;
+      if (MASK) vb = (uint32_t)(vword >> (32 * kb)) >> (4 * g);
       // lane (query row, half g), register r -> key 32 kb + 8 (r/4) + 4 g + r%4
       #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int k4 = key0 + 32 * kb + 8 * rr + 4 * g;
         float mv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (bias && Mrow) {
+        if (MASK && bias && Mrow) {
           if (k4 + 3 < a.Sk && args.mask_vec4) {
             const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mrow + k4);
             mv[0] = m4[0]; mv[1] = m4[1]; mv[2] = m4[2]; mv[3] = m4[3];
@@ -471,12 +441,9 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rr + e;
           float x = st[r];
-          bool vis = true;
-          if (bias || bits || edge) {
-            vis = 32 * kb + 8 * rr + e < klim;
-            if (bits) vis = vis && ((vb >> (8 * rr + e)) & 1u);
-            if (MASK) x += mv[e] * args.inv_scale;  // mv = 0 unless the block has biases
-          }
+          bool vis = 32 * kb + 8 * rr + e < klim;
+          if (bits) vis = vis && ((vb >> (8 * rr + e)) & 1u);
+          if (MASK) x += mv[e] * args.inv_scale;  // mv = 0 unless the block has biases
           const float pv = vis ? fast_exp2(fmaf(x, cs, -lse2)) : 0.f;
           st[r] = pv * (dpt[r] - dlt);
         }
@@ -490,14 +457,14 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
         const int rbase = 32 * kb + 16 * hh + 4 * g + tr_row;
         #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x4 lo = tr_read(kb_lds, rbase * RS + 32 * db + tr_col);
-          const bf16x4 hi = tr_read(kb_lds, (rbase + 8) * RS + 32 * db + tr_col);
+          const bf16x4 lo = TL::read_tr(kb_lds, rbase, 32 * db + tr_col);
+          const bf16x4 hi = TL::read_tr(kb_lds, rbase + 8, 32 * db + tr_col);
           const bf16x8 kbt = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           mma(dq[db], dsf, kbt);
         }
       }
     }
-    if (ktn < kt_end) store_tile(buf ^ 1);
+    wait_vm();
     __syncthreads();
     kt = ktn;
   }
@@ -522,8 +489,8 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
 
 template <int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(const BwdArgs args, const BwdPlan plan) {
-  constexpr int KV_LDS = 2 * 2 * KV_BM * (D + 8) * 2 + 4 * KV_BM * 4;
-  constexpr int Q_LDS = 2 * 2 * Q_BN * (D + 8) * 2;
+  constexpr int KV_LDS = 2 * 2 * KV_BM * D * 2 + 4 * KV_BM * 4;
+  constexpr int Q_LDS = 2 * 2 * Q_BN * D * 2;
   __shared__ __attribute__((aligned(16))) char smem[KV_LDS > Q_LDS ? KV_LDS : Q_LDS];
   const int blk = blockIdx.x;
   if (blk < plan.n_kv_units)

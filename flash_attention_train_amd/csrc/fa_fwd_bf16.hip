@@ -7,9 +7,9 @@
 //  * one workgroup of 4 waves per (batch, head, 32*4*QB-row query tile); each
 //    wave owns QB blocks of 32 query rows, held in registers as the B operand
 //    of S^T = K Q^T for the whole walk;
-//  * K and V tiles of BN keys are staged row-major in LDS, double-buffered: the
-//    next tile's global loads are issued before the current tile's products and
-//    written to the other buffer afterwards, so one barrier per tile suffices;
+//  * K and V tiles of BN keys are copied row-major into LDS by direct global-to-LDS
+//    loads (no registers), double-buffered: the next tile's loads are issued into the
+//    other buffer before the current tile's products, so one barrier per tile suffices;
 //  * K fragments are 16-byte row reads; the V^T operand of O^T = V^T P^T comes
 //    from the row-major V tile through the LDS transpose read
 //    (ds_read_b64_tr_b16: in each 16-lane group, lane L addresses row
@@ -26,12 +26,11 @@
 // page, section 6, trap 9).
 #include "fa_device.h"
 #include "fa_kernels.h"
+#include "fa_tile.h"
 
 namespace fa {
 
 namespace {
-
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 __device__ __forceinline__ f32x16 zeros16() {
   f32x16 z;
@@ -40,23 +39,15 @@ __device__ __forceinline__ f32x16 zeros16() {
   return z;
 }
 
-// One transposed 4 x 16 read: lane i of each 16-lane group gets column c0 + i of rows r0 .. r0 + 3.
-__device__ __forceinline__ bf16x4 tr_read(const bf16* lds_base, int elem_offset) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (lds_bf16x4*)((__attribute__((address_space(3))) bf16*)lds_base + elem_offset));
-}
-
 template <int D, int QB, int BN, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const FwdArgs args) {
   constexpr int NW = 4;
   constexpr int BM = NW * QB * 32;  // query rows per workgroup
   constexpr int KB = BN / 32;       // 32-key blocks per tile
-  constexpr int KS = D + 8;         // LDS row stride (elements): 16 bytes of padding
   constexpr int DS = D / 16, DB = D / 32;
-  constexpr int CH = BN * D / 8;    // 16-byte chunks per tile
-  constexpr int CPT = CH / 256;     // chunks per thread
-  __shared__ __attribute__((aligned(16))) bf16 k_lds[2][BN * KS];
-  __shared__ __attribute__((aligned(16))) bf16 v_lds[2][BN * KS];
+  using TL = Tile<D>;
+  __shared__ __attribute__((aligned(16))) bf16 k_lds[2][BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 v_lds[2][BN * D];
 
   const AttnShape& a = args.a;
   const int tid = threadIdx.x;
@@ -104,46 +95,12 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     kt_end = last_key < 0 ? 0 : (int)((last_key / BN + 1) < nkt ? (last_key / BN + 1) : nkt);
   }
 
-  // tile loader: thread tid moves chunks tid + 256 i (row = chunk / (D/8)). Rows past
-  // the end of K / V load the last row instead: those keys are masked (P = 0) on the
-  // tail tile, so any finite values do, and the loads need no branch.
-  bf16x8 kpre[CPT], vpre[CPT];
-  // per-thread element offsets inside a tile (row c / (D/8), column d0), tile bases are scalar
-  int koff[CPT], voff[CPT], krow[CPT];
-  #pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int c = tid + 256 * i;
-    krow[i] = c / (D / 8);
-    koff[i] = krow[i] * (int)args.sk.s + (c % (D / 8)) * 8;
-    voff[i] = krow[i] * (int)args.sv.s + (c % (D / 8)) * 8;
-  }
-  auto load_tile = [&](int kt) {
+  // tile staging: K and V rows [key0, key0 + BN) straight into LDS; keys past the end
+  // repeat the last key (masked out, P = 0, on the tail tile)
+  auto stage_tile = [&](int kt, int buf) {
     const int key0 = kt * BN;
-    const bf16* Kt = K + (int64_t)key0 * args.sk.s;
-    const bf16* Vt = V + (int64_t)key0 * args.sv.s;
-    if (key0 + BN <= a.Sk) {
-      #pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        kpre[i] = *reinterpret_cast<const bf16x8*>(Kt + koff[i]);
-        vpre[i] = *reinterpret_cast<const bf16x8*>(Vt + voff[i]);
-      }
-    } else {
-      #pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        const int dr = min(krow[i], a.Sk - 1 - key0) - krow[i];  // clamp to the last row
-        kpre[i] = *reinterpret_cast<const bf16x8*>(Kt + koff[i] + dr * (int)args.sk.s);
-        vpre[i] = *reinterpret_cast<const bf16x8*>(Vt + voff[i] + dr * (int)args.sv.s);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / (D / 8), d0 = (c % (D / 8)) * 8;
-      *reinterpret_cast<bf16x8*>(&k_lds[buf][row * KS + d0]) = kpre[i];
-      *reinterpret_cast<bf16x8*>(&v_lds[buf][row * KS + d0]) = vpre[i];
-    }
+    TL::template stage<BN, 256>(k_lds[buf], K + (int64_t)key0 * args.sk.s, args.sk.s, a.Sk - key0);
+    TL::template stage<BN, 256>(v_lds[buf], V + (int64_t)key0 * args.sv.s, args.sv.s, a.Sk - key0);
   };
 
   // With a mask tile map, key tiles whose mask blocks are dead for every row block
@@ -164,10 +121,8 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
   };
 
   int kt = next_live(0);
-  if (kt < kt_end) {
-    load_tile(kt);
-    store_tile(0);
-  }
+  if (kt < kt_end) stage_tile(kt, 0);
+  wait_vm();
   __syncthreads();
 
   // transpose-read addressing inside a 16-lane group
@@ -178,7 +133,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     const int buf = it & 1;
     const int ktn = next_live(kt + 1);
     const bool more = ktn < kt_end;
-    load_tile(more ? ktn : kt);  // the last iteration reloads its own tile: no branch around loads
+    if (more) stage_tile(ktn, buf ^ 1);  // lands while this tile is being processed
     const bf16* kb_lds = k_lds[buf];
     const bf16* vb_lds = v_lds[buf];
     int cls = kTileBias;
@@ -211,7 +166,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     for (int kb = 0; kb < KB; ++kb) {
       #pragma unroll
       for (int s = 0; s < DS; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb_lds + (32 * kb + r32) * KS + 16 * s + 8 * g);
+        const bf16x8 kf = TL::read_chunk(kb_lds, 32 * kb + r32, 2 * s + g);
         #pragma unroll
         for (int qb = 0; qb < QB; ++qb) mma(st[qb][kb], kf, qf[qb][s]);
       }
@@ -313,8 +268,8 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
         const int rbase = 32 * kb + 16 * hh + 4 * g + tr_row;
         #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x4 lo = tr_read(vb_lds, rbase * KS + 32 * db + tr_col);
-          const bf16x4 hi = tr_read(vb_lds, (rbase + 8) * KS + 32 * db + tr_col);
+          const bf16x4 lo = TL::read_tr(vb_lds, rbase, 32 * db + tr_col);
+          const bf16x4 hi = TL::read_tr(vb_lds, rbase + 8, 32 * db + tr_col);
           const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           #pragma unroll
           for (int qb = 0; qb < QB; ++qb) mma(oacc[qb][db], vf, pf[qb][kb][hh]);
@@ -323,7 +278,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     }
 
     }  // cls != dead
-    if (more) store_tile(buf ^ 1);
+    wait_vm();
     __syncthreads();
     kt = ktn;
   }

@@ -5,7 +5,8 @@
  * and its gradient, split the way the pages split it:
  *
  *   fa_train_fwd             O and LSE                         (forward)
- *   fa_train_bwd_preprocess  Delta_i = sum_d dO_id * O_id      ("LSE, D, then grads")
+ *   fa_train_bwd_preprocess  Delta_i = sum_d dO_id * O_id      (the step between the
+ *                            forward's LSE and the gradients)
  *   fa_train_bwd             dQ, dK, dV from Q, K, V, dO, LSE, Delta
  *   fa_train_bwd_chunked     the same, but dK/dV are ADDED into caller-owned fp32
  *                            accumulators over a cached K/V window (exact walk)
@@ -22,9 +23,10 @@
  * O and the LSE and the LSE receives no gradient; trap 4: the backward refuses to
  * write over the forward's buffers; trap 5: native GQA without head expansion;
  * traps 8 and 9: fully masked rows give O = 0, LSE = 0 and fully masked key columns
- * get zero gradient); llama.cpp pull request 57, commit 86c140d (a backward tiled
- * over the KV window: LSE, D, then per-tile grads, GQA group-sum; the exact walk
- * adds dL/d(cached K/V) into a caller-owned accumulator) and the commit that makes
+ * get zero gradient); llama.cpp pull request 57, commit 86c140d (the backward runs
+ * over KV-window tiles, first the per-row LSE, then Delta, then the gradients of each
+ * tile, and adds each query group's dK/dV into its one KV head; the exact walk adds
+ * the gradient of the cached K/V into an accumulator that the caller owns) and the commit that makes
  * the training graph the serving graph (attention reads the cache in place).
  *
  * Conventions shared by every entry point
