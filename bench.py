@@ -147,7 +147,7 @@ def time_workload(w: Workload, steps: int, warmup: int) -> dict:
 
 
 KERNEL_SOURCES = ("flash_attention_train_amd/csrc/fa_bwd_bf16.hip", "flash_attention_train_amd/csrc/fa_device.h",
-                  "flash_attention_train_amd/csrc/fa_kernels.h")
+                  "flash_attention_train_amd/csrc/fa_kernels.h", "flash_attention_train_amd/csrc/fa_tile.h")
 
 
 def source_digest(paths=KERNEL_SOURCES) -> str:
@@ -185,20 +185,24 @@ def copy_calibration(mib: int):
     print(json.dumps({"copy_calibration_bytes": mib << 20, "launches": 5}), flush=True)
 
 
-def cpu_baseline(key: str) -> dict:
-    """The oracle as it stands (fp64 C, all host cores) on one whole step of the
-    workload: fwd + bwd, mask-adjusted FLOPs per second."""
+def cpu_baseline(key: str, min_seconds: float = 10.0, max_reps: int = 8) -> dict:
+    """The oracle as it stands (fp64 C, all host cores) on whole steps of the workload
+    (fwd + bwd), repeated until about `min_seconds` of CPU work: mask-adjusted FLOPs
+    per second."""
     import oracle
     from flash_attention_train_amd import accounting, configs
     c = configs.make(key)
     threads = oracle.default_threads()
     m = None if c.mask is None else c.mask.astype(np.float64)
     args = (c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), m)
-    t0 = time.perf_counter()
-    oracle.backward(*args, scale=c.scale, causal=c.causal, q_offset=c.q_offset, threads=threads)
-    dt = time.perf_counter() - t0
+    reps, dt = 0, 0.0
+    while reps < max_reps and (reps == 0 or dt < min_seconds):
+        t0 = time.perf_counter()
+        oracle.backward(*args, scale=c.scale, causal=c.causal, q_offset=c.q_offset, threads=threads)
+        dt += time.perf_counter() - t0
+        reps += 1
     n = accounting.case_pairs(c)
-    flops = accounting.fwd_flops(n, c.D) + accounting.bwd_flops(n, c.D)
+    flops = reps * (accounting.fwd_flops(n, c.D) + accounting.bwd_flops(n, c.D))
     cpu = platform.processor() or "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -209,7 +213,7 @@ def cpu_baseline(key: str) -> dict:
     except OSError:
         pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"one whole fwd+bwd step of the {key} workload (all heads), float64, {dt:.1f} s",
+            "sample": f"{reps} whole fwd+bwd step(s) of the {key} workload (all heads), float64, {dt:.1f} s",
             "seconds": dt, "cpu": cpu}
 
 
