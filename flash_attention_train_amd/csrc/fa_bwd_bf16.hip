@@ -176,24 +176,28 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
     if (MASK) cls = ct_w < nct ? tile_class(a, b, q0 / kMaskTile, ct_w) : kTileDead;
     const bool bias = MASK && cls == kTileBias;  // read mask values
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
-    uint64_t vword = 0;  // this lane's key: bit i = row q0 + i visible
-    if (bits)
-      vword = a.colbits[(int64_t)tile_index(a, b, q0 / kMaskTile, ct_w) * kMaskTile + (key - ct_w * kMaskTile)];
     const bf16* qb_lds = q_lds + buf * KV_BM * D;
     const bf16* db_lds = do_lds + buf * KV_BM * D;
     const float* lse_b = lse_lds + buf * KV_BM;
     const float* dlt_b = dlt_lds + buf * KV_BM;
     bool edge = q0 + KV_BM > a.Sq || n0 + KV_BN > a.Sk;
     if (CAUSAL) edge = edge || ((int64_t)n0 + KV_BN - 1 > a.q_offset + q0);
-    // visible local rows of this lane's key: qlo <= ql < qhi (ql = row - q0), shifted by
-    // this lane's 4 g so that each test compares a constant
-    int qlo = 0, qhi = key < a.Sk ? a.Sq - q0 : 0;
-    if (CAUSAL) {
-      const int64_t lo = (int64_t)key - a.q_offset - q0;  // key <= q_offset + row
-      qlo = (int)(lo < 0 ? 0 : (lo > KV_BM ? KV_BM : lo));
+    // Rows of the tile this lane's key can see, as a bit word (bit i: row q0 + i): the
+    // sequence tail, the causal diagonal and the block's visibility bits. Blocks with
+    // none of these (wave-uniform `masked` false) skip the masking altogether.
+    const bool masked = edge || bits;
+    uint64_t vis = ~0ull;
+    if (masked) {
+      int qlo = 0;
+      const int qhi = key < a.Sk ? min(a.Sq - q0, KV_BM) : 0;
+      if (CAUSAL) {
+        const int64_t lo = (int64_t)key - a.q_offset - q0;  // key <= q_offset + row
+        qlo = (int)(lo < 0 ? 0 : (lo > KV_BM ? KV_BM : lo));
+      }
+      vis = bit_range64(qlo, qhi);
+      if (bits)
+        vis &= a.colbits[(int64_t)tile_index(a, b, q0 / kMaskTile, ct_w) * kMaskTile + (key - ct_w * kMaskTile)];
     }
-    qlo -= 4 * g;
-    qhi -= 4 * g;
 
     #pragma unroll
     for (int qb = 0; qb < KV_BM / 32 && cls != kTileDead; ++qb) {
@@ -205,30 +209,31 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
         mma(sacc, qa, kf[s]);
         mma(dpacc, da, vf[s]);
       }
-      uint32_t vb = 0;
-      if (MASK) vb = (uint32_t)(vword >> (32 * qb)) >> (4 * g);
       // lane (key, half g), register r -> query row 32 qb + 8 (r/4) + 4 g + r%4
+      if (MASK && bias) {  // additive mask values (rows past the end read the last row)
+        const float* mk = a.mask + b * a.mask_sb + min(key, a.Sk - 1);
+        #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = min(q0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3), a.Sq - 1);
+          sacc[r] += mk[(int64_t)row * a.mask_sq] * args.inv_scale;
+        }
+      }
       #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int ql4 = 32 * qb + 8 * rr + 4 * g;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_b + ql4);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt_b + ql4);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_b + 32 * qb + 8 * rr + 4 * g);
         #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * rr + e;
-          float x = sacc[r];
-          bool vis = true;
-          if (edge || bits) {
-            const int c = 32 * qb + 8 * rr + e;  // ql - 4 g
-            vis = c >= qlo && c < qhi;
-            if (bits) vis = vis && ((vb >> (8 * rr + e)) & 1u);
-          }
-          if (MASK && bias && vis)
-            x += a.mask[b * a.mask_sb + (int64_t)(q0 + ql4 + e) * a.mask_sq + key] * args.inv_scale;
-          const float pv = vis ? fast_exp2(fmaf(x, cs, -l4[e])) : 0.f;
-          sacc[r] = pv;
-          dpacc[r] = pv * (dpacc[r] - d4[e]);
-        }
+        for (int e = 0; e < 4; ++e) sacc[4 * rr + e] = fast_exp2(fmaf(sacc[4 * rr + e], cs, -l4[e]));
+      }
+      if (masked) {  // bit 8 rr + e of w <-> register 4 rr + e
+        const uint32_t w = (uint32_t)(vis >> (32 * qb + 4 * g));
+        #pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = keep_if_bit(sacc[r], w, 8 * (r >> 2) + (r & 3));
+      }
+      #pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt_b + 32 * qb + 8 * rr + 4 * g);
+        #pragma unroll
+        for (int e = 0; e < 4; ++e) dpacc[4 * rr + e] = sacc[4 * rr + e] * (dpacc[4 * rr + e] - d4[e]);
       }
       // dV += P^T dO, dK += dS^T Q; registers 8 hh .. 8 hh + 7 hold rows
       // 32 qb + 16 hh + 8 t + 4 g + e, exactly the rows each transpose read returns
@@ -344,8 +349,6 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
     lse2 = args.lse[b * args.lse_sb + h * args.lse_sh + row] * kLog2e;
     dlt = args.delta[b * args.delta_sb + h * args.delta_sh + row];
   }
-  const float* Mrow = nullptr;
-  if (MASK && row < a.Sq) Mrow = a.mask + b * a.mask_sb + (int64_t)row * a.mask_sq;
 
   f32x16 dq[DB];
   #pragma unroll
@@ -395,20 +398,25 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
     if (MASK) cls = rt_w < nrt ? tile_class(a, b, rt_w, kt) : kTileDead;
     const bool bias = MASK && cls == kTileBias;  // read mask values
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
-    uint64_t vword = 0;  // this lane's row: bit j = key kt * 64 + j visible
-    if (bits) vword = a.rowbits[(int64_t)tile_index(a, b, rt_w, kt) * kMaskTile + (row - rt_w * kMaskTile)];
     const bf16* kb_lds = k_lds + buf * Q_BN * D;
     const bf16* vb_lds = v_lds + buf * Q_BN * D;
     const int key0 = kt * Q_BN;
     bool edge = key0 + Q_BN > a.Sk || qw + 32 > a.Sq;
     if (CAUSAL) edge = edge || ((int64_t)key0 + Q_BN - 1 > a.q_offset + qw);
-    // visible local keys of this lane's row: kl < klim, shifted by 4 g
-    int64_t kl64 = row < a.Sq ? (int64_t)a.Sk - key0 : 0;
-    if (CAUSAL) {
-      const int64_t c = a.q_offset + row + 1 - key0;
-      kl64 = c < kl64 ? c : kl64;
+    // Keys of the tile this lane's row can see, as a bit word (bit j: key key0 + j):
+    // the sequence tail, the causal diagonal and the block's visibility bits. Blocks
+    // with none of these (wave-uniform `masked` false) skip the masking altogether.
+    const bool masked = edge || bits;
+    uint64_t vis = ~0ull;
+    if (masked) {
+      int64_t kl64 = row < a.Sq ? (int64_t)a.Sk - key0 : 0;
+      if (CAUSAL) {
+        const int64_t c = a.q_offset + row + 1 - key0;
+        kl64 = c < kl64 ? c : kl64;
+      }
+      vis = bit_range64(0, (int)(kl64 < 0 ? 0 : (kl64 > Q_BN ? Q_BN : kl64)));
+      if (bits) vis &= a.rowbits[(int64_t)tile_index(a, b, rt_w, kt) * kMaskTile + (row - rt_w * kMaskTile)];
     }
-    const int klim = (int)(kl64 < 0 ? 0 : (kl64 > Q_BN ? Q_BN : kl64)) - 4 * g;
 
     // one 32-key block at a time keeps the live accumulators small
     #pragma unroll
@@ -421,33 +429,33 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
         mma(st, ka, qf[s]);
         mma(dpt, va, df[s]);
       }
-      uint32_t vb = 0;
-      if (MASK) vb = (uint32_t)(vword >> (32 * kb)) >> (4 * g);
       // lane (query row, half g), register r -> key 32 kb + 8 (r/4) + 4 g + r%4
-      #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int k4 = key0 + 32 * kb + 8 * rr + 4 * g;
-        float mv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (MASK && bias && Mrow) {
+      if (MASK && bias) {  // additive mask values, 4 keys at a time (keys past the end read 0)
+        const float* mr = a.mask + b * a.mask_sb + (int64_t)min(row, a.Sq - 1) * a.mask_sq;
+        #pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int k4 = key0 + 32 * kb + 8 * rr + 4 * g;
+          float mv[4];
           if (k4 + 3 < a.Sk && args.mask_vec4) {
-            const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mrow + k4);
+            const f32x4 m4 = *reinterpret_cast<const f32x4*>(mr + k4);
             mv[0] = m4[0]; mv[1] = m4[1]; mv[2] = m4[2]; mv[3] = m4[3];
           } else {
             #pragma unroll
-            for (int e = 0; e < 4; ++e) mv[e] = (k4 + e < a.Sk) ? Mrow[k4 + e] : 0.f;
+            for (int e = 0; e < 4; ++e) mv[e] = (k4 + e < a.Sk) ? mr[k4 + e] : 0.f;
           }
-        }
-        #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * rr + e;
-          float x = st[r];
-          bool vis = 32 * kb + 8 * rr + e < klim;
-          if (bits) vis = vis && ((vb >> (8 * rr + e)) & 1u);
-          if (MASK) x += mv[e] * args.inv_scale;  // mv = 0 unless the block has biases
-          const float pv = vis ? fast_exp2(fmaf(x, cs, -lse2)) : 0.f;
-          st[r] = pv * (dpt[r] - dlt);
+          #pragma unroll
+          for (int e = 0; e < 4; ++e) st[4 * rr + e] += mv[e] * args.inv_scale;
         }
       }
+      #pragma unroll
+      for (int r = 0; r < 16; ++r) st[r] = fast_exp2(fmaf(st[r], cs, -lse2));
+      if (masked) {  // bit 8 rr + e of w <-> register 4 rr + e
+        const uint32_t w = (uint32_t)(vis >> (32 * kb + 4 * g));
+        #pragma unroll
+        for (int r = 0; r < 16; ++r) st[r] = keep_if_bit(st[r], w, 8 * (r >> 2) + (r & 3));
+      }
+      #pragma unroll
+      for (int r = 0; r < 16; ++r) st[r] = st[r] * (dpt[r] - dlt);
       // dQ += dS K: A = dS (registers 8 hh .. of this key block: keys 32 kb + 16 hh + 8 t + 4 g + e),
       // B = K rows of the same keys, column d, by transpose reads
       #pragma unroll

@@ -131,4 +131,17 @@ __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); 
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// x where bit `bit` of `word` is set, +0.0 where it is clear (a sign-extended one-bit
+// field ANDed into the float's bits: two VALU instructions, no compare or select)
+__device__ __forceinline__ float keep_if_bit(float x, uint32_t word, int bit) {
+  return __int_as_float(__float_as_int(x) & __builtin_amdgcn_sbfe((int)word, bit, 1));
+}
+
+// bits [lo, hi) of a 64-bit word set (0 <= lo, hi <= 64)
+__device__ __forceinline__ uint64_t bit_range64(int lo, int hi) {
+  const uint64_t below_hi = hi >= 64 ? ~0ull : ((1ull << hi) - 1ull);
+  const uint64_t from_lo = lo >= 64 ? 0ull : (~0ull << lo);
+  return below_hi & from_lo;
+}
+
 }  // namespace fa
