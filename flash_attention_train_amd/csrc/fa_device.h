@@ -137,6 +137,13 @@ __device__ __forceinline__ float keep_if_bit(float x, uint32_t word, int bit) {
   return __int_as_float(__float_as_int(x) & __builtin_amdgcn_sbfe((int)word, bit, 1));
 }
 
+// x where bit `bit` of `word` is set, -inf where it is clear (bit-field insert under a
+// sign-extended one-bit field)
+__device__ __forceinline__ float ninf_unless_bit(float x, uint32_t word, int bit) {
+  const int m = __builtin_amdgcn_sbfe((int)word, bit, 1);
+  return __int_as_float((__float_as_int(x) & m) | (~m & (int)0xff800000u));
+}
+
 // bits [lo, hi) of a 64-bit word set (0 <= lo, hi <= 64)
 __device__ __forceinline__ uint64_t bit_range64(int lo, int hi) {
   const uint64_t below_hi = hi >= 64 ? ~0ull : ((1ull << hi) - 1ull);

@@ -141,20 +141,6 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     if (cls != kTileDead) {
     const bool bias = MASK && cls == kTileBias;  // read mask values
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
-    // this lane's visibility bits for the tile's keys, shifted down by 4 g
-    uint32_t vb[QB][KB];
-    if (bits) {
-      const int64_t base = (int64_t)tile_index(a, b, rt_w, (kt * BN) / kMaskTile) * kMaskTile;
-      #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const uint64_t w = a.rowbits[base + (qw + 32 * qb + r32 - rt_w * kMaskTile)];
-        #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const int half = BN == 64 ? kb : (kt & 1);
-          vb[qb][kb] = (uint32_t)(w >> (32 * half)) >> (4 * g);
-        }
-      }
-    }
 
     // S^T = K Q^T for both 32-key blocks; each K fragment serves all QB query blocks
     f32x16 st[QB][KB];
@@ -172,54 +158,57 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
       }
     }
 
-    // does this tile need per-element masking (sequence tail / causal diagonal)?
+    // does this tile need per-element masking (sequence tail / causal diagonal / bits)?
     const int key0 = kt * BN;
     bool edge = key0 + BN > a.Sk;
     if (CAUSAL) edge = edge || ((int64_t)key0 + BN - 1 > a.q_offset + qw);
-    // visible local keys of this lane's rows are kl < lim[qb] (kl = key - key0)
-    int lim[QB];
-    #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      int64_t l = (int64_t)a.Sk - key0;
-      if (CAUSAL) {
-        const int64_t c = a.q_offset + qw + 32 * qb + r32 + 1 - key0;
-        l = c < l ? c : l;
-      }
-      lim[qb] = (int)(l < 0 ? 0 : (l > BN ? BN : l));
-    }
+    const bool masked = edge || bits;
 
     bf16x8 pf[QB][KB][2];
     #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int row = qw + 32 * qb + r32;
-      if (bias || bits || edge) {
-        const float* Mrow = nullptr;
-        if (bias && row < a.Sq) Mrow = a.mask + b * a.mask_sb + (int64_t)row * a.mask_sq;
+      if (MASK && bias) {
+        // the mask enters the raw score as M / scale so that one fma applies both later;
+        // keys past the end read 0 (the tail is masked below), rows past the end the last row
+        const float* mr = a.mask + b * a.mask_sb + (int64_t)min(row, a.Sq - 1) * a.mask_sq;
         #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const int k4 = key0 + 32 * kb + 8 * rr + 4 * g;  // 4 consecutive keys k4 .. k4 + 3
-            float mv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (MASK && Mrow) {
-              if (k4 + 3 < a.Sk && args.mask_vec4) {
-                const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mrow + k4);
-                mv[0] = m4[0]; mv[1] = m4[1]; mv[2] = m4[2]; mv[3] = m4[3];
-              } else {
-                #pragma unroll
-                for (int e = 0; e < 4; ++e) mv[e] = (k4 + e < a.Sk) ? Mrow[k4 + e] : 0.f;
-              }
+            float mv[4];
+            if (k4 + 3 < a.Sk && args.mask_vec4) {
+              const f32x4 m4 = *reinterpret_cast<const f32x4*>(mr + k4);
+              mv[0] = m4[0]; mv[1] = m4[1]; mv[2] = m4[2]; mv[3] = m4[3];
+            } else {
+              #pragma unroll
+              for (int e = 0; e < 4; ++e) mv[e] = (k4 + e < a.Sk) ? mr[k4 + e] : 0.f;
             }
             #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              bool vis = 32 * kb + 8 * rr + 4 * g + e < lim[qb];
-              if (bits) vis = vis && ((vb[qb][kb] >> (8 * rr + e)) & 1u);
-              // the mask enters the raw score as M / scale so that one fma applies both later
-              float x = st[qb][kb][4 * rr + e];
-              if (MASK) x += mv[e] * args.inv_scale;  // mv = 0 unless the block has biases
-              st[qb][kb][4 * rr + e] = vis ? x : neg_inf();
-            }
+            for (int e = 0; e < 4; ++e) st[qb][kb][4 * rr + e] += mv[e] * args.inv_scale;
           }
+        }
+      }
+      if (masked) {
+        // keys of the tile this lane's row can see (bit j: key key0 + j); masked scores
+        // become -inf (bit-field insert of -inf under a sign-extended bit: two VALU ops)
+        int64_t l = (int64_t)a.Sk - key0;
+        if (CAUSAL) {
+          const int64_t c = a.q_offset + row + 1 - key0;
+          l = c < l ? c : l;
+        }
+        uint64_t vis = bit_range64(0, (int)(l < 0 ? 0 : (l > BN ? BN : l)));
+        if (bits) {
+          const uint64_t w = a.rowbits[(int64_t)tile_index(a, b, rt_w, key0 / kMaskTile) * kMaskTile +
+                                       (row - rt_w * kMaskTile)];
+          vis &= BN == 64 ? w : (w >> (key0 % kMaskTile));
+        }
+        #pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const uint32_t wv = (uint32_t)(vis >> (32 * kb + 4 * g));  // bit 8 rr + e <-> register 4 rr + e
+          #pragma unroll
+          for (int r = 0; r < 16; ++r) st[qb][kb][r] = ninf_unless_bit(st[qb][kb][r], wv, 8 * (r >> 2) + (r & 3));
         }
       }
       // row max of this tile (raw score units), shared by lanes l and l ^ 32
