@@ -218,16 +218,16 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
           sacc[r] += mk[(int64_t)row * a.mask_sq] * args.inv_scale;
         }
       }
+      if (masked) {  // hidden scores -> -inf (P = 0); bit 8 rr + e of w <-> register 4 rr + e
+        const uint32_t w = (uint32_t)(vis >> (32 * qb + 4 * g));
+        #pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = ninf_unless_bit(sacc[r], w, 8 * (r >> 2) + (r & 3));
+      }
       #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_b + 32 * qb + 8 * rr + 4 * g);
         #pragma unroll
         for (int e = 0; e < 4; ++e) sacc[4 * rr + e] = fast_exp2(fmaf(sacc[4 * rr + e], cs, -l4[e]));
-      }
-      if (masked) {  // bit 8 rr + e of w <-> register 4 rr + e
-        const uint32_t w = (uint32_t)(vis >> (32 * qb + 4 * g));
-        #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = keep_if_bit(sacc[r], w, 8 * (r >> 2) + (r & 3));
       }
       #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
@@ -447,13 +447,13 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
           for (int e = 0; e < 4; ++e) st[4 * rr + e] += mv[e] * args.inv_scale;
         }
       }
-      #pragma unroll
-      for (int r = 0; r < 16; ++r) st[r] = fast_exp2(fmaf(st[r], cs, -lse2));
-      if (masked) {  // bit 8 rr + e of w <-> register 4 rr + e
+      if (masked) {  // hidden scores -> -inf (P = 0); bit 8 rr + e of w <-> register 4 rr + e
         const uint32_t w = (uint32_t)(vis >> (32 * kb + 4 * g));
         #pragma unroll
-        for (int r = 0; r < 16; ++r) st[r] = keep_if_bit(st[r], w, 8 * (r >> 2) + (r & 3));
+        for (int r = 0; r < 16; ++r) st[r] = ninf_unless_bit(st[r], w, 8 * (r >> 2) + (r & 3));
       }
+      #pragma unroll
+      for (int r = 0; r < 16; ++r) st[r] = fast_exp2(fmaf(st[r], cs, -lse2));
       #pragma unroll
       for (int r = 0; r < 16; ++r) st[r] = st[r] * (dpt[r] - dlt);
       // dQ += dS K: A = dS (registers 8 hh .. of this key block: keys 32 kb + 16 hh + 8 t + 4 g + e),

@@ -131,14 +131,8 @@ __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); 
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
-// x where bit `bit` of `word` is set, +0.0 where it is clear (a sign-extended one-bit
-// field ANDed into the float's bits: two VALU instructions, no compare or select)
-__device__ __forceinline__ float keep_if_bit(float x, uint32_t word, int bit) {
-  return __int_as_float(__float_as_int(x) & __builtin_amdgcn_sbfe((int)word, bit, 1));
-}
-
-// x where bit `bit` of `word` is set, -inf where it is clear (bit-field insert under a
-// sign-extended one-bit field)
+// x where bit `bit` of `word` is set, -inf where it is clear: a sign-extended one-bit
+// field selects between x and -inf bitwise (v_bfe_i32 + v_bitop3, no compare)
 __device__ __forceinline__ float ninf_unless_bit(float x, uint32_t word, int bit) {
   const int m = __builtin_amdgcn_sbfe((int)word, bit, 1);
   return __int_as_float((__float_as_int(x) & m) | (~m & (int)0xff800000u));
