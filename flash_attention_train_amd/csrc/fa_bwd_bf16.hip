@@ -50,15 +50,70 @@ __device__ __forceinline__ f32x16 zeros16() {
   return z;
 }
 
+// acc += a b with the accumulator in AGPRs (the dK/dV and dQ sums live there for the
+// whole walk, which leaves the arch VGPRs to the operands in flight). The s_nop gives
+// the two wait states a VALU write of a source operand needs before a matrix product.
+__device__ __forceinline__ void mma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// the last products into AGPR accumulators must have written them before VALU reads
+// them (the matrix core's result latency, with margin)
+template <int N>
+__device__ __forceinline__ void settle_acc(f32x16 (&acc)[N]) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+  #pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+a"(acc[i]));
+}
+
 __device__ __forceinline__ void atomic_add_f32(float* p, float v) {
   __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// unit -> (key tile, batch, kv head, split); key tiles vary slowest so that the long
+// causal tiles (small key index) are dispatched first
+struct KvUnit {
+  int kt, b, hk, split;
+};
+__device__ __forceinline__ KvUnit kv_unit_of(const AttnShape& a, const BwdPlan& plan, int unit) {
+  const int per_tile = a.B * a.Hkv * plan.kv_split;
+  int rem = unit % per_tile;
+  const int split = rem % plan.kv_split;
+  rem /= plan.kv_split;
+  return {unit / per_tile, rem / a.Hkv, rem % a.Hkv, split};
+}
+
+// unit -> (query tile, batch, head, split); the last query tiles (longest under a
+// causal mask) are dispatched first
+struct QUnit {
+  int qt, b, h, split;
+};
+__device__ __forceinline__ QUnit q_unit_of(const AttnShape& a, const BwdPlan& plan, int unit) {
+  const int nqt = (a.Sq + Q_BM - 1) / Q_BM;
+  const int per_tile = a.B * a.Hq * plan.q_split;
+  int rem = unit % per_tile;
+  const int split = rem % plan.q_split;
+  rem /= plan.q_split;
+  return {nqt - 1 - unit / per_tile, rem / a.Hq, rem % a.Hq, split};
+}
+
+// Does any mask block of rows [r0, r0 + nr) x keys [c0, c0 + nc) (in 64-blocks) carry
+// additive values? Units whose blocks are all dead / open / 0-or--inf run a body
+// compiled without the mask-value reads, which keeps their loop free of that code.
+__device__ __forceinline__ bool any_bias_block(const AttnShape& a, int b, int rb0, int nrb, int cb0, int ncb) {
+  if (!a.tiles) return true;
+  const int nrt = (a.Sq + kMaskTile - 1) / kMaskTile, nct = (a.Sk + kMaskTile - 1) / kMaskTile;
+  for (int rt = rb0; rt < rb0 + nrb && rt < nrt; ++rt)
+    for (int ct = cb0; ct < cb0 + ncb && ct < nct; ++ct)
+      if (tile_class(a, b, rt, ct) == kTileBias) return true;
+  return false;
 }
 
 // ---------------------------------------------------------------------------
 // dK / dV workgroup
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool MASK>
-__device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
+template <int D, bool CAUSAL, bool MASK, bool BIAS>
+__device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
   constexpr int DS = D / 16, DB = D / 32;
   using TL = Tile<D>;
   bf16* q_lds = reinterpret_cast<bf16*>(smem);                 // [2][KV_BM * D]
@@ -69,14 +124,8 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
   const AttnShape& a = args.a;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, r32 = lane & 31;
-  // unit -> (key tile, batch, kv head, split); key tiles vary slowest so that the
-  // long causal tiles (small key index) are dispatched first
-  const int per_tile = a.B * a.Hkv * plan.kv_split;
-  const int kt = unit / per_tile;
-  int rem = unit % per_tile;
-  const int split = rem % plan.kv_split;
-  rem /= plan.kv_split;
-  const int hk = rem % a.Hkv, b = rem / a.Hkv;
+  const KvUnit u = kv_unit_of(a, plan, unit);
+  const int kt = u.kt, b = u.b, hk = u.hk, split = u.split;
   const int n0 = kt * KV_BN;
   const int key = n0 + 32 * wave + r32;
   const float cs = a.scale * kLog2e;
@@ -183,11 +232,14 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
     bool edge = q0 + KV_BM > a.Sq || n0 + KV_BN > a.Sk;
     if (CAUSAL) edge = edge || ((int64_t)n0 + KV_BN - 1 > a.q_offset + q0);
     // Rows of the tile this lane's key can see, as a bit word (bit i: row q0 + i): the
-    // sequence tail, the causal diagonal and the block's visibility bits. Blocks with
-    // none of these (wave-uniform `masked` false) skip the masking altogether.
-    const bool masked = edge || bits;
-    uint64_t vis = ~0ull;
-    if (masked) {
+    // sequence tail, the causal diagonal and the block's visibility bits (none for a
+    // dead block, whose products then contribute exact zeros: skipping them per wave
+    // costs more in registers than it saves). Blocks with none of these (wave-uniform
+    // `masked` false) skip the masking altogether.
+    const bool dead = MASK && cls == kTileDead;
+    const bool masked = edge || bits || dead;
+    uint64_t vis = dead ? 0ull : ~0ull;
+    if (masked && !dead) {
       int qlo = 0;
       const int qhi = key < a.Sk ? min(a.Sq - q0, KV_BM) : 0;
       if (CAUSAL) {
@@ -200,17 +252,43 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
     }
 
     #pragma unroll
-    for (int qb = 0; qb < KV_BM / 32 && cls != kTileDead; ++qb) {
+    for (int qb = 0; qb < KV_BM / 32; ++qb) {
+      // S = Q K^T, dP = dO V^T: the block's Q and dO row chunks are all requested before
+      // the first product, so only the first read's latency is exposed
+      bf16x8 qa[DS], da[DS];
+      #pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        qa[s] = TL::read_chunk(qb_lds, 32 * qb + r32, 2 * s + g);
+        da[s] = TL::read_chunk(db_lds, 32 * qb + r32, 2 * s + g);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 sacc = zeros16(), dpacc = zeros16();
       #pragma unroll
       for (int s = 0; s < DS; ++s) {
-        const bf16x8 qa = TL::read_chunk(qb_lds, 32 * qb + r32, 2 * s + g);
-        const bf16x8 da = TL::read_chunk(db_lds, 32 * qb + r32, 2 * s + g);
-        mma(sacc, qa, kf[s]);
-        mma(dpacc, da, vf[s]);
+        mma(sacc, qa[s], kf[s]);
+        mma(dpacc, da[s], vf[s]);
       }
+      // the dO^T / Q^T operands of dV += P^T dO and dK += dS^T Q are requested now and
+      // land during the softmax; registers 8 hh .. 8 hh + 7 of the accumulators hold rows
+      // 32 qb + 16 hh + 8 t + 4 g + e, exactly the rows each transpose read returns
+      bf16x8 dob[2][DB], qbt[2][DB];
+      #pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int rbase = 32 * qb + 16 * hh + 4 * g + tr_row;
+        #pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int col = 32 * db + tr_col;
+          const bf16x4 d0 = TL::read_tr(db_lds, rbase, col);
+          const bf16x4 d1 = TL::read_tr(db_lds, rbase + 8, col);
+          const bf16x4 q0v = TL::read_tr(qb_lds, rbase, col);
+          const bf16x4 q1v = TL::read_tr(qb_lds, rbase + 8, col);
+          dob[hh][db] = bf16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+          qbt[hh][db] = bf16x8{q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
       // lane (key, half g), register r -> query row 32 qb + 8 (r/4) + 4 g + r%4
-      if (MASK && bias) {  // additive mask values (rows past the end read the last row)
+      if (BIAS && bias) {  // additive mask values (rows past the end read the last row)
         const float* mk = a.mask + b * a.mask_sb + min(key, a.Sk - 1);
         #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -235,25 +313,15 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
         #pragma unroll
         for (int e = 0; e < 4; ++e) dpacc[4 * rr + e] = sacc[4 * rr + e] * (dpacc[4 * rr + e] - d4[e]);
       }
-      // dV += P^T dO, dK += dS^T Q; registers 8 hh .. 8 hh + 7 hold rows
-      // 32 qb + 16 hh + 8 t + 4 g + e, exactly the rows each transpose read returns
       #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         bf16x8 pa, dsa;
         pack8(pa, sacc, 8 * hh);
         pack8(dsa, dpacc, 8 * hh);
-        const int rbase = 32 * qb + 16 * hh + 4 * g + tr_row;
         #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int col = 32 * db + tr_col;
-          const bf16x4 d0 = TL::read_tr(db_lds, rbase, col);
-          const bf16x4 d1 = TL::read_tr(db_lds, rbase + 8, col);
-          const bf16x4 q0v = TL::read_tr(qb_lds, rbase, col);
-          const bf16x4 q1v = TL::read_tr(qb_lds, rbase + 8, col);
-          const bf16x8 dob = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-          const bf16x8 qbt = {q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
-          mma(dv[db], pa, dob);
-          mma(dk[db], dsa, qbt);
+          mma_acc(dv[db], pa, dob[hh][db]);
+          mma_acc(dk[db], dsa, qbt[hh][db]);
         }
       }
     }
@@ -263,6 +331,8 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
     p = pn;
   }
 
+  settle_acc(dk);
+  settle_acc(dv);
   // results: accumulator row = key 8 (r/4) + 4 g + r%4 of this wave, column d = 32 db + r32
   const bool atomic = plan.kv_split > 1;
   #pragma unroll
@@ -304,8 +374,8 @@ __device__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, ch
 // ---------------------------------------------------------------------------
 // dQ workgroup
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool MASK>
-__device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
+template <int D, bool CAUSAL, bool MASK, bool BIAS>
+__device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
   constexpr int DS = D / 16, DB = D / 32;
   using TL = Tile<D>;
   bf16* k_lds = reinterpret_cast<bf16*>(smem);  // [2][Q_BN * D]
@@ -314,15 +384,8 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
   const AttnShape& a = args.a;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, r32 = lane & 31;
-  // unit -> (query tile, batch, head, split); the last query tiles (longest under
-  // a causal mask) are dispatched first
-  const int nqt = (a.Sq + Q_BM - 1) / Q_BM;
-  const int per_tile = a.B * a.Hq * plan.q_split;
-  const int qt = nqt - 1 - unit / per_tile;
-  int rem = unit % per_tile;
-  const int split = rem % plan.q_split;
-  rem /= plan.q_split;
-  const int h = rem % a.Hq, b = rem / a.Hq;
+  const QUnit u = q_unit_of(a, plan, unit);
+  const int qt = u.qt, b = u.b, h = u.h, split = u.split;
   const int hk = h / a.G;
   const int q0 = qt * Q_BM;
   const int qw = q0 + 32 * wave;
@@ -404,11 +467,13 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
     bool edge = key0 + Q_BN > a.Sk || qw + 32 > a.Sq;
     if (CAUSAL) edge = edge || ((int64_t)key0 + Q_BN - 1 > a.q_offset + qw);
     // Keys of the tile this lane's row can see, as a bit word (bit j: key key0 + j):
-    // the sequence tail, the causal diagonal and the block's visibility bits. Blocks
-    // with none of these (wave-uniform `masked` false) skip the masking altogether.
-    const bool masked = edge || bits;
-    uint64_t vis = ~0ull;
-    if (masked) {
+    // the sequence tail, the causal diagonal and the block's visibility bits (none for
+    // a dead block, computed to exact zeros like in the dK/dV walk). Blocks with none
+    // of these (wave-uniform `masked` false) skip the masking altogether.
+    const bool dead = MASK && cls == kTileDead;
+    const bool masked = edge || bits || dead;
+    uint64_t vis = dead ? 0ull : ~0ull;
+    if (masked && !dead) {
       int64_t kl64 = row < a.Sq ? (int64_t)a.Sk - key0 : 0;
       if (CAUSAL) {
         const int64_t c = a.q_offset + row + 1 - key0;
@@ -420,17 +485,37 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
 
     // one 32-key block at a time keeps the live accumulators small
     #pragma unroll
-    for (int kb = 0; kb < 2 && cls != kTileDead; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
+      // S^T = K Q^T, dP^T = V dO^T: all K / V row chunks of the block requested up front
+      bf16x8 ka[DS], va[DS];
+      #pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        ka[s] = TL::read_chunk(kb_lds, 32 * kb + r32, 2 * s + g);
+        va[s] = TL::read_chunk(vb_lds, 32 * kb + r32, 2 * s + g);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 st = zeros16(), dpt = zeros16();
       #pragma unroll
       for (int s = 0; s < DS; ++s) {
-        const bf16x8 ka = TL::read_chunk(kb_lds, 32 * kb + r32, 2 * s + g);
-        const bf16x8 va = TL::read_chunk(vb_lds, 32 * kb + r32, 2 * s + g);
-        mma(st, ka, qf[s]);
-        mma(dpt, va, df[s]);
+        mma(st, ka[s], qf[s]);
+        mma(dpt, va[s], df[s]);
       }
+      // K operands of dQ += dS K (transpose reads), landing during the softmax: registers
+      // 8 hh .. of this key block hold keys 32 kb + 16 hh + 8 t + 4 g + e
+      bf16x8 kbt[2][DB];
+      #pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int rbase = 32 * kb + 16 * hh + 4 * g + tr_row;
+        #pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x4 lo = TL::read_tr(kb_lds, rbase, 32 * db + tr_col);
+          const bf16x4 hi = TL::read_tr(kb_lds, rbase + 8, 32 * db + tr_col);
+          kbt[hh][db] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
       // lane (query row, half g), register r -> key 32 kb + 8 (r/4) + 4 g + r%4
-      if (MASK && bias) {  // additive mask values, 4 keys at a time (keys past the end read 0)
+      if (BIAS && bias) {  // additive mask values, 4 keys at a time (keys past the end read 0)
         const float* mr = a.mask + b * a.mask_sb + (int64_t)min(row, a.Sq - 1) * a.mask_sq;
         #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -456,20 +541,12 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
       for (int r = 0; r < 16; ++r) st[r] = fast_exp2(fmaf(st[r], cs, -lse2));
       #pragma unroll
       for (int r = 0; r < 16; ++r) st[r] = st[r] * (dpt[r] - dlt);
-      // dQ += dS K: A = dS (registers 8 hh .. of this key block: keys 32 kb + 16 hh + 8 t + 4 g + e),
-      // B = K rows of the same keys, column d, by transpose reads
       #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         bf16x8 dsf;
         pack8(dsf, st, 8 * hh);
-        const int rbase = 32 * kb + 16 * hh + 4 * g + tr_row;
         #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x4 lo = TL::read_tr(kb_lds, rbase, 32 * db + tr_col);
-          const bf16x4 hi = TL::read_tr(kb_lds, rbase + 8, 32 * db + tr_col);
-          const bf16x8 kbt = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          mma(dq[db], dsf, kbt);
-        }
+        for (int db = 0; db < DB; ++db) mma_acc(dq[db], dsf, kbt[hh][db]);
       }
     }
     wait_vm();
@@ -477,6 +554,7 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
     kt = ktn;
   }
 
+  settle_acc(dq);
   // dQ accumulator: lane (d = 32 db + r32, half g), register r -> row 8 (r/4) + 4 g + r%4 of the wave
   #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -495,16 +573,32 @@ __device__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char
   }
 }
 
+// Units whose mask blocks carry additive values run a body compiled with the
+// mask-value reads; all others (dead / open / 0-or--inf blocks) a body without them,
+// which keeps that code and its registers out of the common loop.
 template <int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(const BwdArgs args, const BwdPlan plan) {
   constexpr int KV_LDS = 2 * 2 * KV_BM * D * 2 + 4 * KV_BM * 4;
   constexpr int Q_LDS = 2 * 2 * Q_BN * D * 2;
   __shared__ __attribute__((aligned(16))) char smem[KV_LDS > Q_LDS ? KV_LDS : Q_LDS];
   const int blk = blockIdx.x;
-  if (blk < plan.n_kv_units)
-    dkdv_unit<D, CAUSAL, MASK>(args, plan, blk, smem);
-  else
-    dq_unit<D, CAUSAL, MASK>(args, plan, blk - plan.n_kv_units, smem);
+  const AttnShape& a = args.a;
+  if (blk < plan.n_kv_units) {
+    const KvUnit u = kv_unit_of(a, plan, blk);
+    if (MASK && any_bias_block(a, u.b, 0, (a.Sq + kMaskTile - 1) / kMaskTile, u.kt * (KV_BN / kMaskTile),
+                               KV_BN / kMaskTile))
+      dkdv_unit<D, CAUSAL, MASK, true>(args, plan, blk, smem);
+    else
+      dkdv_unit<D, CAUSAL, MASK, false>(args, plan, blk, smem);
+  } else {
+    const int unit = blk - plan.n_kv_units;
+    const QUnit u = q_unit_of(a, plan, unit);
+    if (MASK && any_bias_block(a, u.b, u.qt * (Q_BM / kMaskTile), Q_BM / kMaskTile, 0,
+                               (a.Sk + kMaskTile - 1) / kMaskTile))
+      dq_unit<D, CAUSAL, MASK, true>(args, plan, unit, smem);
+    else
+      dq_unit<D, CAUSAL, MASK, false>(args, plan, unit, smem);
+  }
 }
 
 template <int D>
