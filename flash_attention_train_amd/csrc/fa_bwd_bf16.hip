@@ -122,7 +122,8 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
   float* dlt_lds = lse_lds + 2 * KV_BM;                        // [2][KV_BM]
 
   const AttnShape& a = args.a;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) from here on
   const int g = lane >> 5, r32 = lane & 31;
   const KvUnit u = kv_unit_of(a, plan, unit);
   const int kt = u.kt, b = u.b, hk = u.hk, split = u.split;
@@ -176,13 +177,14 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     TL::template stage<KV_BM, 256>(do_lds + buf * KV_BM * D, dO, args.sdo.s, a.Sq - q0);
     if (tid < 2 * KV_BM) {
       const int row = min(q0 + (tid % KV_BM), a.Sq - 1);
-      lpre = tid < KV_BM ? args.lse[b * args.lse_sb + h * args.lse_sh + row] * kLog2e
+      // (scaled when stored, so that nothing waits for the load before the tile's work)
+      lpre = tid < KV_BM ? args.lse[b * args.lse_sb + h * args.lse_sh + row]
                          : args.delta[b * args.delta_sb + h * args.delta_sh + row];
     }
   };
   auto store_stats = [&](int buf) {
     if (tid < KV_BM)
-      lse_lds[buf * KV_BM + tid] = lpre;
+      lse_lds[buf * KV_BM + tid] = lpre * kLog2e;
     else if (tid < 2 * KV_BM)
       dlt_lds[buf * KV_BM + tid - KV_BM] = lpre;
   };
@@ -382,7 +384,8 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
   bf16* v_lds = k_lds + 2 * Q_BN * D;           // [2][Q_BN * D]
 
   const AttnShape& a = args.a;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) from here on
   const int g = lane >> 5, r32 = lane & 31;
   const QUnit u = q_unit_of(a, plan, unit);
   const int qt = u.qt, b = u.b, h = u.h, split = u.split;

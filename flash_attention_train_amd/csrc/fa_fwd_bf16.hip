@@ -51,7 +51,8 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
 
   const AttnShape& a = args.a;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) from here on
   const int g = lane >> 5, r32 = lane & 31;
   const int b = blockIdx.z, h = blockIdx.y;
   const int qt = gridDim.x - 1 - blockIdx.x;  // longest causal tiles first
@@ -115,13 +116,55 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
       if (tile_class(a, b, rt, ct) != kTileDead) return true;
     return false;
   };
+  // The live key tiles of the workgroup, 256 at a time, as bit words in LDS: found by
+  // all threads at once, so that the walk never waits on a class load per tile.
+  __shared__ uint64_t live_lds[4];
+  int live_base = -256;
+  auto refill = [&](int base) {  // called by the whole workgroup at the same point
+    const int t = base + tid;
+    const uint64_t w = __ballot(t < kt_end && live(t));
+    __syncthreads();  // the previous words are no longer read
+    if (lane == 0) live_lds[wave] = w;
+    __syncthreads();
+    live_base = base;
+  };
   auto next_live = [&](int kt) {
-    while (kt < kt_end && !live(kt)) ++kt;
-    return kt;
+    if (!MASK || !a.tiles) return kt < kt_end ? kt : kt_end;
+    while (kt < kt_end) {
+      if (kt >= live_base + 256) refill(kt & ~255);
+      const int off = kt - live_base;
+      const uint64_t bits = live_lds[off >> 6] >> (off & 63);
+      if (bits) return kt + (int)__builtin_ctzll(bits);
+      kt = live_base + 64 * ((off >> 6) + 1);
+    }
+    return kt_end;
+  };
+
+  // Per-tile mask state of this wave, fetched one tile ahead (its loads then complete
+  // under the end-of-iteration wait instead of stalling the tile): the block class and
+  // this lane's row visibility words.
+  auto mask_state = [&](int kt, int& cls, uint64_t (&w)[QB]) {
+    cls = kTileBias;
+    #pragma unroll
+    for (int qb = 0; qb < QB; ++qb) w[qb] = ~0ull;
+    if (MASK && a.tiles) {
+      const int ct = (kt * BN) / kMaskTile;
+      cls = rt_w < nrt ? tile_class(a, b, rt_w, ct) : kTileDead;
+      if (rt_w < nrt) {
+        const int64_t base = (int64_t)tile_index(a, b, rt_w, ct) * kMaskTile - rt_w * kMaskTile;
+        #pragma unroll
+        for (int qb = 0; qb < QB; ++qb) w[qb] = a.rowbits[base + qw + 32 * qb + r32];
+      }
+    }
   };
 
   int kt = next_live(0);
-  if (kt < kt_end) stage_tile(kt, 0);
+  int cls_cur = kTileBias;
+  uint64_t wb_cur[QB];
+  if (kt < kt_end) {
+    stage_tile(kt, 0);
+    mask_state(kt, cls_cur, wb_cur);
+  }
   wait_vm();
   __syncthreads();
 
@@ -133,11 +176,15 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     const int buf = it & 1;
     const int ktn = next_live(kt + 1);
     const bool more = ktn < kt_end;
-    if (more) stage_tile(ktn, buf ^ 1);  // lands while this tile is being processed
+    int cls_next = kTileBias;
+    uint64_t wb_next[QB];
+    if (more) {
+      mask_state(ktn, cls_next, wb_next);
+      stage_tile(ktn, buf ^ 1);  // lands while this tile is being processed
+    }
     const bf16* kb_lds = k_lds[buf];
     const bf16* vb_lds = v_lds[buf];
-    int cls = kTileBias;
-    if (MASK) cls = rt_w < nrt ? tile_class(a, b, rt_w, (kt * BN) / kMaskTile) : kTileDead;
+    const int cls = cls_cur;
     if (cls != kTileDead) {
     const bool bias = MASK && cls == kTileBias;  // read mask values
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
@@ -199,11 +246,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
           l = c < l ? c : l;
         }
         uint64_t vis = bit_range64(0, (int)(l < 0 ? 0 : (l > BN ? BN : l)));
-        if (bits) {
-          const uint64_t w = a.rowbits[(int64_t)tile_index(a, b, rt_w, key0 / kMaskTile) * kMaskTile +
-                                       (row - rt_w * kMaskTile)];
-          vis &= BN == 64 ? w : (w >> (key0 % kMaskTile));
-        }
+        if (bits) vis &= BN == 64 ? wb_cur[qb] : (wb_cur[qb] >> (key0 % kMaskTile));
         #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           const uint32_t wv = (uint32_t)(vis >> (32 * kb + 4 * g));  // bit 8 rr + e <-> register 4 rr + e
@@ -270,6 +313,9 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     wait_vm();
     __syncthreads();
     kt = ktn;
+    cls_cur = cls_next;
+    #pragma unroll
+    for (int qb = 0; qb < QB; ++qb) wb_cur[qb] = wb_next[qb];
   }
 
   // epilogue: O = acc / l, LSE = (base + log2 l) ln 2; fully masked rows -> 0, 0

@@ -36,10 +36,17 @@ constexpr int kTileDead = 0, kTileOpen = 1, kTileBits = 2, kTileBias = 3, kMaskT
 __device__ __forceinline__ int tile_index(const AttnShape& a, int b, int rt, int ct) {
   return b * a.tiles_bstride + rt * a.tiles_ncol + ct;
 }
-// class of mask block (b, row block rt, key block ct); "bias" (read every value) without a map
+// class of mask block (b, row block rt, key block ct); "bias" (read every value) without a
+// map. The index is wave-uniform, so the class is read with a scalar load (through the
+// constant address space, one aligned dword: the class array is 256-byte aligned and
+// padded to a multiple of 256 bytes); scalar loads are tracked apart from the vector
+// memory counter that orders the direct-to-LDS tile loads.
 __device__ __forceinline__ int tile_class(const AttnShape& a, int b, int rt, int ct) {
   if (!a.tiles) return kTileBias;
-  return a.tiles[tile_index(a, b, rt, ct)];
+  const int i = tile_index(a, b, rt, ct);
+  const auto* w = reinterpret_cast<const __attribute__((address_space(4))) uint32_t*>(
+      reinterpret_cast<uintptr_t>(a.tiles) + (uintptr_t)(i & ~3));
+  return (int)((*w >> (8 * (i & 3))) & 0xffu);
 }
 
 struct FwdArgs {

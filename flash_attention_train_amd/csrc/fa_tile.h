@@ -60,8 +60,20 @@ struct Tile {
       const int c = p ^ swz(row);
       const int grow = row < valid ? row : valid - 1;
       const bf16* g = src + (int64_t)grow * stride + 8 * c;
-      __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds + 8 * n0), 16, 0, 0);
+      dma16(g, lds + 8 * n0);
     }
+  }
+
+  // One wave-instruction of global_load_lds_dwordx4: lane l's 16 bytes from g land at
+  // LDS byte address m0 + 16 l, m0 = dst (wave-uniform). Written as asm so that the
+  // compiler does not treat the asynchronous LDS write as possibly aliasing every later
+  // LDS read (it would wait for the load before the current tile's reads, serialising
+  // the prefetch); the callers order the loads with an explicit wait and barrier.
+  __device__ static __forceinline__ void dma16(const bf16* g, bf16* dst) {
+    const uint32_t m0 =
+        __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) bf16*)dst);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0)
+                 : "memory", "m0");
   }
 };
 
