@@ -210,21 +210,41 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
   };
   const int ct_w = ct0 + (32 * wave) / kMaskTile;  // this wave's 32 keys lie in one 64-key block
 
+  // Per-pair mask state of this wave, fetched one pair ahead (its loads complete under
+  // the end-of-iteration wait instead of stalling the pair): the block class and this
+  // lane's key column visibility word.
+  auto mask_state = [&](int pp, int& cls, uint64_t& w) {
+    cls = kTileBias;
+    w = ~0ull;
+    if (MASK && a.tiles) {
+      const int rt = qt0 + pp / a.G;
+      cls = ct_w < nct ? tile_class(a, b, rt, ct_w) : kTileDead;
+      if (ct_w < nct) w = a.colbits[(int64_t)tile_index(a, b, rt, ct_w) * kMaskTile + (key - ct_w * kMaskTile)];
+    }
+  };
+
   int p = next_live(split);
+  int cls_cur = kTileBias;
+  uint64_t wb_cur = ~0ull;
   if (p < npairs) {
     stage_pair(p, 0);
-    wait_vm();
-    store_stats(0);
+    mask_state(p, cls_cur, wb_cur);
   }
+  wait_vm();  // on every path: the K / V fragments are complete before the walk
+  if (p < npairs) store_stats(0);
   __syncthreads();
   for (int it = 0; p < npairs; ++it) {
     const int buf = it & 1;
     const int pn = next_live(p + plan.kv_split);
-    if (pn < npairs) stage_pair(pn, buf ^ 1);  // lands while this pair is being processed
+    int cls_next = kTileBias;
+    uint64_t wb_next = ~0ull;
+    if (pn < npairs) {
+      mask_state(pn, cls_next, wb_next);
+      stage_pair(pn, buf ^ 1);  // lands while this pair is being processed
+    }
     int h, q0;
     pair_of(p, h, q0);
-    int cls = kTileBias;
-    if (MASK) cls = ct_w < nct ? tile_class(a, b, q0 / kMaskTile, ct_w) : kTileDead;
+    const int cls = cls_cur;
     const bool bias = MASK && cls == kTileBias;  // read mask values
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
     const bf16* qb_lds = q_lds + buf * KV_BM * D;
@@ -249,8 +269,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
         qlo = (int)(lo < 0 ? 0 : (lo > KV_BM ? KV_BM : lo));
       }
       vis = bit_range64(qlo, qhi);
-      if (bits)
-        vis &= a.colbits[(int64_t)tile_index(a, b, q0 / kMaskTile, ct_w) * kMaskTile + (key - ct_w * kMaskTile)];
+      if (bits) vis &= wb_cur;
     }
 
     #pragma unroll
@@ -331,6 +350,8 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     if (pn < npairs) store_stats(buf ^ 1);
     __syncthreads();
     p = pn;
+    cls_cur = cls_next;
+    wb_cur = wb_next;
   }
 
   settle_acc(dk);
@@ -452,16 +473,36 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
   };
   const int rt_w = qw / kMaskTile;
 
+  // per-tile mask state of this wave, fetched one tile ahead: the block class and this
+  // lane's row visibility word
+  auto mask_state = [&](int k, int& cls, uint64_t& w) {
+    cls = kTileBias;
+    w = ~0ull;
+    if (MASK && a.tiles) {
+      cls = rt_w < nrt ? tile_class(a, b, rt_w, k) : kTileDead;
+      if (rt_w < nrt) w = a.rowbits[(int64_t)tile_index(a, b, rt_w, k) * kMaskTile + (row - rt_w * kMaskTile)];
+    }
+  };
+
   int kt = next_live(split);
-  if (kt < kt_end) stage_tile(kt, 0);
+  int cls_cur = kTileBias;
+  uint64_t wb_cur = ~0ull;
+  if (kt < kt_end) {
+    stage_tile(kt, 0);
+    mask_state(kt, cls_cur, wb_cur);
+  }
   wait_vm();
   __syncthreads();
   for (int it = 0; kt < kt_end; ++it) {
     const int buf = it & 1;
     const int ktn = next_live(kt + plan.q_split);
-    if (ktn < kt_end) stage_tile(ktn, buf ^ 1);  // lands while this tile is being processed
-    int cls = kTileBias;
-    if (MASK) cls = rt_w < nrt ? tile_class(a, b, rt_w, kt) : kTileDead;
+    int cls_next = kTileBias;
+    uint64_t wb_next = ~0ull;
+    if (ktn < kt_end) {
+      mask_state(ktn, cls_next, wb_next);
+      stage_tile(ktn, buf ^ 1);  // lands while this tile is being processed
+    }
+    const int cls = cls_cur;
     const bool bias = MASK && cls == kTileBias;  // read mask values
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
     const bf16* kb_lds = k_lds + buf * Q_BN * D;
@@ -483,7 +524,7 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
         kl64 = c < kl64 ? c : kl64;
       }
       vis = bit_range64(0, (int)(kl64 < 0 ? 0 : (kl64 > Q_BN ? Q_BN : kl64)));
-      if (bits) vis &= a.rowbits[(int64_t)tile_index(a, b, rt_w, kt) * kMaskTile + (row - rt_w * kMaskTile)];
+      if (bits) vis &= wb_cur;
     }
 
     // one 32-key block at a time keeps the live accumulators small
@@ -555,6 +596,8 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
     wait_vm();
     __syncthreads();
     kt = ktn;
+    cls_cur = cls_next;
+    wb_cur = wb_next;
   }
 
   settle_acc(dq);
