@@ -38,6 +38,7 @@ def parse():
     ap.add_argument("--workload", default="dit_sa")
     ap.add_argument("--extra", default="lm_causal,dit_ca")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference kernel that "
                          "scales the HBM byte counters) and exit")
@@ -76,12 +77,14 @@ class Workload:
         self.ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
         self.B = binding
         self.tiles = None
+        if self.mask is not None:
+            self.tiles = binding.mask_tile_map(self.mask, self.q, self.k)  # sized once, refilled every step
 
     def classify(self):
         """The mask tile map (dead / open / mixed 64 x 64 blocks), part of every step
         that has a dense mask."""
         if self.mask is not None:
-            self.tiles = self.B.mask_tile_map(self.mask, self.q, self.k)
+            self.B.mask_tile_map(self.mask, self.q, self.k, out=self.tiles)
 
     def fwd(self):
         c = self.case
@@ -104,9 +107,35 @@ class Workload:
         self.bwd()
 
 
-def time_workload(w: Workload, steps: int, warmup: int) -> dict:
-    """Times `steps` whole steps (wall clock around synchronizes) and, inside the
-    same timed region, each call with HIP events on the stream it is launched on."""
+def time_graph(w: Workload, steps: int, warmup: int) -> float:
+    """Captures one whole step (mask map, forward, preprocess, backward: the same launches
+    as the eager step) in a HIP graph and times `steps` replays between synchronizes.
+    Returns ms per step. The graph removes the host's per-launch cost, which a training
+    loop that captures its attention layer does not pay either."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        w.step()  # one eager step on the capture stream before capturing
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        w.step()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def time_workload(w: Workload, steps: int, warmup: int, graph: bool = True) -> dict:
+    """Times `steps` whole eager steps (wall clock around synchronizes) and, inside the
+    same timed region, each call with HIP events on the stream it is launched on; then
+    (graph=True) the same step replayed from a captured graph."""
     import torch
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -130,10 +159,14 @@ def time_workload(w: Workload, steps: int, warmup: int) -> dict:
     fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     pre_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     bwd_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
-    step_ms = wall * 1e3 / steps
+    eager_ms = wall * 1e3 / steps
+    step_ms = time_graph(w, steps, warmup) if graph else eager_ms
     total_flops = w.fwd_flops + w.bwd_flops
     return {
         "ms_per_step": step_ms,
+        "timing": "hip graph replay of the whole step" if graph else "eager launches",
+        "eager_ms_per_step": eager_ms,
+        "eager_tflops": total_flops / (eager_ms * 1e-3) / 1e12,
         "tflops": total_flops / (step_ms * 1e-3) / 1e12,
         "fwd_ms_mean": float(fwd_ms.mean()), "pre_ms_mean": float(pre_ms.mean()), "bwd_ms_mean": float(bwd_ms.mean()),
         "fwd_ms_median": float(np.median(fwd_ms)), "bwd_ms_median": float(np.median(bwd_ms)),
@@ -236,13 +269,13 @@ def main():
 
     log(f"[bench] device {torch.cuda.get_device_name(0)}; workload {args.workload}")
     w = Workload(args.workload)
-    r = time_workload(w, args.steps, args.warmup)
+    r = time_workload(w, args.steps, args.warmup, graph=not args.eager)
     log(f"[bench] {args.workload}: {r['ms_per_step']:.3f} ms/step, {r['tflops']:.1f} TFLOP/s")
 
     extra = {}
     for key in [k for k in args.extra.split(",") if k and k not in (args.workload, "none")]:
         we = Workload(key)
-        re_ = time_workload(we, max(5, args.steps // 2), args.warmup)
+        re_ = time_workload(we, max(5, args.steps // 2), args.warmup, graph=not args.eager)
         re_["pct_of_peak"] = 100.0 * re_["tflops"] / accounting.MI355X_BF16_DENSE_TFLOPS
         extra[key] = re_
         log(f"[bench] {key}: {re_['ms_per_step']:.3f} ms/step, {re_['tflops']:.1f} TFLOP/s")

@@ -143,13 +143,20 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
     return p
 
 
-def mask_tile_map(mask: torch.Tensor, q: torch.Tensor, k: torch.Tensor, *, stream=None) -> torch.Tensor:
+def mask_tile_map(mask: torch.Tensor, q: torch.Tensor, k: torch.Tensor, *, stream=None,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Classify every 64 x 64 block of an additive mask (0 dead, 1 open, 2 visibility bits,
     3 finite biases) and record its visibility bits, for reuse by fwd/bwd/bwd_chunked
-    through their ``mask_tiles`` argument. The first ``mask_tile_count`` bytes are the classes."""
+    through their ``mask_tiles`` argument. The first ``mask_tile_count`` bytes are the classes.
+    ``out`` (uint8, at least the map's size) is filled instead of a new tensor."""
     p = make_params(q, k, scale=None, causal=False, q_offset=0, mask=mask)
     n = int(lib().fa_train_mask_tiles_bytes(ctypes.byref(p)))
-    tiles = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    if out is not None:
+        if out.dtype != torch.uint8 or not out.is_contiguous() or out.numel() < n:
+            raise ValueError(f"out must be a contiguous uint8 tensor of at least {n} bytes")
+        tiles = out
+    else:
+        tiles = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
     _check("fa_train_mask_tiles", lib().fa_train_mask_tiles(ctypes.byref(p), tiles.data_ptr(), _stream_handle(stream)))
     return tiles
 

@@ -68,41 +68,69 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const DqArgs p) {
 }
 
 // One workgroup per 64 x 64 mask block (clipped at Sq and Sk; entries outside count as
-// masked for the bits and are ignored by the class): the visibility bits of every
-// row come from one wave ballot each, the column words from a bit transpose in LDS,
-// and the class from workgroup-wide votes.
+// masked for the bits and are ignored by the class). Each wave takes 16 consecutive
+// rows with all 16 loads in flight at once; a wave ballot per row gives the row word,
+// a 64 x 64 bit transpose across the lanes of wave 0 (six butterfly rounds of lane
+// exchanges) gives the column words, and the class comes from OR-ed flags.
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t x, int m) {
+  const int lo = __shfl_xor((int)(uint32_t)x, m, 64), hi = __shfl_xor((int)(uint32_t)(x >> 32), m, 64);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
 __global__ __launch_bounds__(256) void mask_tiles_kernel(const AttnShape a, uint8_t* tiles, uint64_t* rowbits,
                                                          uint64_t* colbits) {
   __shared__ uint64_t rows_lds[kMaskTile];
+  __shared__ int flags_lds;
   const int ct = blockIdx.x, rt = blockIdx.y, bm = blockIdx.z;
   const int64_t blk = ((int64_t)bm * gridDim.y + rt) * gridDim.x + ct;
   const float* M = a.mask + bm * a.mask_sb;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int any_vis = 0, any_masked = 0, any_bias = 0;
-  for (int r = wave; r < kMaskTile; r += 4) {
-    const int row = rt * kMaskTile + r, key = ct * kMaskTile + lane;
-    const bool in = row < a.Sq && key < a.Sk;
-    const float v = in ? M[(int64_t)row * a.mask_sq + key] : neg_inf();
-    const bool vis = in && v != neg_inf();
-    any_vis |= vis;
-    any_masked |= in && !vis;
-    any_bias |= vis && v != 0.f;
-    const uint64_t word = __ballot(vis);
+  const int key = ct * kMaskTile + lane;
+  const int row0 = rt * kMaskTile + wave * 16;
+  if (threadIdx.x == 0) flags_lds = 0;
+  float v[16];
+  #pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const bool in = row0 + i < a.Sq && key < a.Sk;
+    v[i] = in ? M[(int64_t)(row0 + i) * a.mask_sq + key] : neg_inf();
+  }
+  int fl = 0;  // 1: a visible entry, 2: a masked entry inside the block, 4: a nonzero visible value
+  #pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const bool in = row0 + i < a.Sq && key < a.Sk;
+    const bool vis = v[i] != neg_inf();
+    fl |= (vis ? 1 : 0) | (in && !vis ? 2 : 0) | (vis && v[i] != 0.f ? 4 : 0);
+    const uint64_t w = __ballot(vis);
     if (lane == 0) {
-      rowbits[blk * kMaskTile + r] = word;
-      rows_lds[r] = word;
+      rows_lds[wave * 16 + i] = w;
+      rowbits[blk * kMaskTile + wave * 16 + i] = w;
     }
   }
-  any_vis = __syncthreads_or(any_vis);
-  any_masked = __syncthreads_or(any_masked);
-  any_bias = __syncthreads_or(any_bias);
+  const int wf = (__any(fl & 1) ? 1 : 0) | (__any(fl & 2) ? 2 : 0) | (__any(fl & 4) ? 4 : 0);
+  __syncthreads();  // flags cleared, row words in LDS
+  if (lane == 0) atomicOr(&flags_lds, wf);
   if (wave == 0) {
-    uint64_t col = 0;
-    for (int i = 0; i < kMaskTile; ++i) col |= ((rows_lds[i] >> lane) & 1ull) << i;
-    colbits[blk * kMaskTile + lane] = col;
+    // lane r holds row r's word (bit c: key c); after the rounds lane c holds column c's
+    // word (bit r: row r)
+    uint64_t x = rows_lds[lane];
+    const uint64_t masks[6] = {0x00000000FFFFFFFFull, 0x0000FFFF0000FFFFull, 0x00FF00FF00FF00FFull,
+                               0x0F0F0F0F0F0F0F0Full, 0x3333333333333333ull, 0x5555555555555555ull};
+    #pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      const int j = 32 >> k;
+      const uint64_t other = shfl_xor64(x, j);
+      if (lane & j)
+        x ^= ((other >> j) ^ x) & masks[k];
+      else
+        x ^= (((x >> j) ^ other) & masks[k]) << j;
+    }
+    colbits[blk * kMaskTile + lane] = x;
   }
-  if (threadIdx.x == 0)
-    tiles[blk] = !any_vis ? kTileDead : any_bias ? kTileBias : any_masked ? kTileBits : kTileOpen;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int f = flags_lds;
+    tiles[blk] = !(f & 1) ? kTileDead : (f & 4) ? kTileBias : (f & 2) ? kTileBits : kTileOpen;
+  }
 }
 
 template <typename T, int D>

@@ -256,8 +256,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     // Rows of the tile this lane's key can see, as a bit word (bit i: row q0 + i): the
     // sequence tail, the causal diagonal and the block's visibility bits (none for a
     // dead block, whose products then contribute exact zeros: skipping them per wave
-    // costs more in registers than it saves). Blocks with none of these (wave-uniform
-    // `masked` false) skip the masking altogether.
+    // costs more in registers than it saves).
     const bool dead = MASK && cls == kTileDead;
     const bool masked = edge || bits || dead;
     uint64_t vis = dead ? 0ull : ~0ull;
@@ -272,43 +271,29 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
       if (bits) vis &= wb_cur;
     }
 
-    #pragma unroll
-    for (int qb = 0; qb < KV_BM / 32; ++qb) {
-      // S = Q K^T, dP = dO V^T: the block's Q and dO row chunks are all requested before
-      // the first product, so only the first read's latency is exposed
+    // The pair is two 32-row blocks, each in three steps: products S = Q K^T and
+    // dP = dO V^T (A), the softmax gradient (B) and the products dV += P^T dO,
+    // dK += dS^T Q (C). They are issued as A0 A1 B0 C0 B1 C1 so that each block's
+    // VALU work (B) has the other block's matrix products beside it to overlap with;
+    // masking is applied unconditionally (a no-op word on open blocks) to keep the
+    // whole pair one straight-line region for the scheduler.
+    auto step_a = [&](int qb, f32x16& sacc, f32x16& dpacc) {
       bf16x8 qa[DS], da[DS];
       #pragma unroll
       for (int s = 0; s < DS; ++s) {
         qa[s] = TL::read_chunk(qb_lds, 32 * qb + r32, 2 * s + g);
         da[s] = TL::read_chunk(db_lds, 32 * qb + r32, 2 * s + g);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 sacc = zeros16(), dpacc = zeros16();
+      sacc = zeros16();
+      dpacc = zeros16();
       #pragma unroll
       for (int s = 0; s < DS; ++s) {
         mma(sacc, qa[s], kf[s]);
         mma(dpacc, da[s], vf[s]);
       }
-      // the dO^T / Q^T operands of dV += P^T dO and dK += dS^T Q are requested now and
-      // land during the softmax; registers 8 hh .. 8 hh + 7 of the accumulators hold rows
-      // 32 qb + 16 hh + 8 t + 4 g + e, exactly the rows each transpose read returns
-      bf16x8 dob[2][DB], qbt[2][DB];
-      #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int rbase = 32 * qb + 16 * hh + 4 * g + tr_row;
-        #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int col = 32 * db + tr_col;
-          const bf16x4 d0 = TL::read_tr(db_lds, rbase, col);
-          const bf16x4 d1 = TL::read_tr(db_lds, rbase + 8, col);
-          const bf16x4 q0v = TL::read_tr(qb_lds, rbase, col);
-          const bf16x4 q1v = TL::read_tr(qb_lds, rbase + 8, col);
-          dob[hh][db] = bf16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-          qbt[hh][db] = bf16x8{q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // lane (key, half g), register r -> query row 32 qb + 8 (r/4) + 4 g + r%4
+    };
+    // lane (key, half g), register r -> query row 32 qb + 8 (r/4) + 4 g + r%4
+    auto step_b = [&](int qb, f32x16& sacc, f32x16& dpacc, bf16x8 (&pa)[2], bf16x8 (&dsa)[2]) {
       if (BIAS && bias) {  // additive mask values (rows past the end read the last row)
         const float* mk = a.mask + b * a.mask_sb + min(key, a.Sk - 1);
         #pragma unroll
@@ -317,35 +302,59 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
           sacc[r] += mk[(int64_t)row * a.mask_sq] * args.inv_scale;
         }
       }
-      if (masked) {  // hidden scores -> -inf (P = 0); bit 8 rr + e of w <-> register 4 rr + e
-        const uint32_t w = (uint32_t)(vis >> (32 * qb + 4 * g));
-        #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = ninf_unless_bit(sacc[r], w, 8 * (r >> 2) + (r & 3));
-      }
+      // hidden scores -> -inf (P = 0); bit 8 rr + e of w <-> register 4 rr + e
+      const uint32_t w = (uint32_t)(vis >> (32 * qb + 4 * g));
+      #pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = ninf_unless_bit(sacc[r], w, 8 * (r >> 2) + (r & 3));
       #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_b + 32 * qb + 8 * rr + 4 * g);
-        #pragma unroll
-        for (int e = 0; e < 4; ++e) sacc[4 * rr + e] = fast_exp2(fmaf(sacc[4 * rr + e], cs, -l4[e]));
-      }
-      #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt_b + 32 * qb + 8 * rr + 4 * g);
         #pragma unroll
-        for (int e = 0; e < 4; ++e) dpacc[4 * rr + e] = sacc[4 * rr + e] * (dpacc[4 * rr + e] - d4[e]);
+        for (int e = 0; e < 4; ++e) {
+          const float pv = fast_exp2(fmaf(sacc[4 * rr + e], cs, -l4[e]));
+          sacc[4 * rr + e] = pv;
+          dpacc[4 * rr + e] = pv * (dpacc[4 * rr + e] - d4[e]);
+        }
       }
       #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        bf16x8 pa, dsa;
-        pack8(pa, sacc, 8 * hh);
-        pack8(dsa, dpacc, 8 * hh);
+        pack8(pa[hh], sacc, 8 * hh);
+        pack8(dsa[hh], dpacc, 8 * hh);
+      }
+    };
+    // registers 8 hh .. 8 hh + 7 of the accumulators hold rows 32 qb + 16 hh + 8 t + 4 g + e,
+    // exactly the rows each transpose read of dO^T / Q^T returns
+    auto step_c = [&](int qb, const bf16x8 (&pa)[2], const bf16x8 (&dsa)[2]) {
+      #pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int rbase = 32 * qb + 16 * hh + 4 * g + tr_row;
+        bf16x8 dob[DB], qbt[DB];
         #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          mma_acc(dv[db], pa, dob[hh][db]);
-          mma_acc(dk[db], dsa, qbt[hh][db]);
+          const int col = 32 * db + tr_col;
+          const bf16x4 d0 = TL::read_tr(db_lds, rbase, col);
+          const bf16x4 d1 = TL::read_tr(db_lds, rbase + 8, col);
+          const bf16x4 q0v = TL::read_tr(qb_lds, rbase, col);
+          const bf16x4 q1v = TL::read_tr(qb_lds, rbase + 8, col);
+          dob[db] = bf16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+          qbt[db] = bf16x8{q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
+        }
+        #pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          mma_acc(dv[db], pa[hh], dob[db]);
+          mma_acc(dk[db], dsa[hh], qbt[db]);
         }
       }
-    }
+    };
+    f32x16 s0, dp0, s1, dp1;
+    bf16x8 pa0[2], ds0[2], pa1[2], ds1[2];
+    step_a(0, s0, dp0);
+    step_a(1, s1, dp1);
+    step_b(0, s0, dp0, pa0, ds0);
+    step_c(0, pa0, ds0);
+    step_b(1, s1, dp1, pa1, ds1);
+    step_c(1, pa1, ds1);
     wait_vm();
     if (pn < npairs) store_stats(buf ^ 1);
     __syncthreads();

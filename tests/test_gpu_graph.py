@@ -1,0 +1,80 @@
+"""The whole step (mask tile map, forward, preprocess, backward) captured in a HIP graph
+and replayed: every replay, with eager work and synchronizations between replays, must
+reproduce the eager step's outputs bit for bit (the walks are pinned to one workgroup
+per tile so that no fp32 atomics reorder sums), and the eager step itself matches the
+oracle. This is the launch sequence the benchmark times."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from flash_attention_train_amd import binding, configs
+from parity_util import compare_full, host64, say, upload
+
+pytestmark = pytest.mark.gpu
+
+
+class Step:
+    def __init__(self, c, t):
+        self.c, self.t = c, t
+        q = t["q"]
+        self.o = torch.empty_like(q)
+        self.lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+        self.delta = torch.empty_like(self.lse)
+        self.dq, self.dk, self.dv = torch.empty_like(q), torch.empty_like(t["k"]), torch.empty_like(t["v"])
+        self.ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+        self.tiles = None if t["mask"] is None else binding.mask_tile_map(t["mask"], q, t["k"])
+
+    def __call__(self):
+        c, t = self.c, self.t
+        if self.tiles is not None:
+            binding.mask_tile_map(t["mask"], t["q"], t["k"], out=self.tiles)
+        binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal, q_offset=c.q_offset,
+                    out=self.o, lse=self.lse, mask_tiles=self.tiles)
+        binding.bwd_preprocess(self.o, t["do"], delta=self.delta)
+        binding.bwd(t["q"], t["k"], t["v"], t["do"], self.lse, self.delta, mask=t["mask"], scale=c.scale,
+                    causal=c.causal, q_offset=c.q_offset, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws,
+                    kv_split=1, q_split=1, mask_tiles=self.tiles)
+
+    def outputs(self):
+        return [x.clone() for x in (self.o, self.lse, self.delta, self.dq, self.dk, self.dv)]
+
+
+@pytest.mark.parametrize("key,shrink", [("dit_sa", dict(Hq=4, Hkv=2, Sq=300, Sk=300)),
+                                        ("dit_ca", dict(B=2, Hq=2, Hkv=2, Sq=300, Sk=160)),
+                                        ("lm_causal", dict(Hq=4, Hkv=1, Sq=333, Sk=333))])
+def test_graph_replays_match_eager(key, shrink):
+    c = configs.make(key, **shrink)
+    say(f"{key}: graph capture of the whole step, B={c.B} Hq={c.Hq} Sq={c.Sq} Sk={c.Sk}")
+    step = Step(c, upload(c))
+    step()
+    torch.cuda.synchronize()
+    eager = step.outputs()
+    got = dict(zip(("O", "LSE", "Delta", "dQ", "dK", "dV"), (host64(x) for x in eager)))
+    m = None if c.mask is None else c.mask.astype(np.float64)
+    ref = oracle.backward(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), m, scale=c.scale, causal=c.causal,
+                          q_offset=c.q_offset)
+    compare_full(c, got, ref)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    scratch = torch.zeros(1 << 16, device="cuda")
+    for rep in range(4):
+        for x in (step.o, step.lse, step.delta, step.dq, step.dk, step.dv):
+            x.fill_(float("nan"))  # eager work between replays; every output must be rewritten
+        scratch.add_(1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("O", "LSE", "Delta", "dQ", "dK", "dV"), eager, step.outputs()):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager step"
+    say(f"    4 replays equal to the eager step")
