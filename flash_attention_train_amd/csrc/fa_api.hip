@@ -155,9 +155,9 @@ void choose_splits(const fa_attn_params* p, bool accumulate, int* kv_split, int*
   // Splitting pays only when the unsplit grid cannot give every compute unit a
   // workgroup; measured on the workloads at hand, beyond that the atomics and the
   // extra clear / convert passes cost more than the better balance gains.
-  const int64_t target = 256;
-  const int64_t kv_units = (int64_t)((p->Sk + 127) / 128) * p->B * p->Hkv;
-  const int64_t q_units = (int64_t)((p->Sq + 127) / 128) * p->B * p->Hq;
+  const int64_t target = 1024 / fa::kBwdWaves;  // workgroups that fill the GPU (one wave per SIMD)
+  const int64_t kv_units = (int64_t)((p->Sk + fa::kBwdUnit - 1) / fa::kBwdUnit) * p->B * p->Hkv;
+  const int64_t q_units = (int64_t)((p->Sq + fa::kBwdUnit - 1) / fa::kBwdUnit) * p->B * p->Hq;
   const int64_t kv_pairs = (int64_t)((p->Sq + 63) / 64) * (p->Hq / p->Hkv);  // walk length of one key tile
   const int64_t q_tiles = (p->Sk + 63) / 64;                                  // walk length of one query tile
   int kv = 1, q = 1;

@@ -38,10 +38,12 @@ namespace fa {
 
 namespace {
 
-constexpr int KV_BN = 128;  // keys per dK/dV workgroup
-constexpr int KV_BM = 64;   // query rows per staged tile of the dK/dV walk
-constexpr int Q_BM = 128;   // query rows per dQ workgroup
-constexpr int Q_BN = 64;    // keys per staged tile of the dQ walk
+constexpr int NT = kBwdThreads;  // threads per workgroup (kBwdWaves waves of 32 keys or rows)
+constexpr int KV_BN = kBwdUnit;  // keys per dK/dV workgroup
+constexpr int KV_BM = 64;        // query rows per staged tile of the dK/dV walk
+constexpr int Q_BM = kBwdUnit;   // query rows per dQ workgroup
+constexpr int Q_BN = 64;         // keys per staged tile of the dQ walk
+static_assert(2 * KV_BM <= NT, "one thread per LSE / Delta value of a staged tile");
 
 __device__ __forceinline__ f32x16 zeros16() {
   f32x16 z;
@@ -173,8 +175,8 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     pair_of(p, h, q0);
     const bf16* Q = static_cast<const bf16*>(args.q) + b * args.sq.b + h * args.sq.h + (int64_t)q0 * args.sq.s;
     const bf16* dO = static_cast<const bf16*>(args.dout) + b * args.sdo.b + h * args.sdo.h + (int64_t)q0 * args.sdo.s;
-    TL::template stage<KV_BM, 256>(q_lds + buf * KV_BM * D, Q, args.sq.s, a.Sq - q0);
-    TL::template stage<KV_BM, 256>(do_lds + buf * KV_BM * D, dO, args.sdo.s, a.Sq - q0);
+    TL::template stage<KV_BM, NT>(q_lds + buf * KV_BM * D, Q, args.sq.s, a.Sq - q0);
+    TL::template stage<KV_BM, NT>(do_lds + buf * KV_BM * D, dO, args.sdo.s, a.Sq - q0);
     if (tid < 2 * KV_BM) {
       const int row = min(q0 + (tid % KV_BM), a.Sq - 1);
       // (scaled when stored, so that nothing waits for the load before the tile's work)
@@ -461,8 +463,8 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
   // the last key, masked out on the tail tile)
   auto stage_tile = [&](int kt, int buf) {
     const int key0 = kt * Q_BN;
-    TL::template stage<Q_BN, 256>(k_lds + buf * Q_BN * D, K + (int64_t)key0 * args.sk.s, args.sk.s, a.Sk - key0);
-    TL::template stage<Q_BN, 256>(v_lds + buf * Q_BN * D, V + (int64_t)key0 * args.sv.s, args.sv.s, a.Sk - key0);
+    TL::template stage<Q_BN, NT>(k_lds + buf * Q_BN * D, K + (int64_t)key0 * args.sk.s, args.sk.s, a.Sk - key0);
+    TL::template stage<Q_BN, NT>(v_lds + buf * Q_BN * D, V + (int64_t)key0 * args.sv.s, args.sv.s, a.Sk - key0);
   };
 
   const int G16 = lane >> 4, L16 = lane & 15;
@@ -632,7 +634,7 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
 // mask-value reads; all others (dead / open / 0-or--inf blocks) a body without them,
 // which keeps that code and its registers out of the common loop.
 template <int D, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(const BwdArgs args, const BwdPlan plan) {
+__global__ __launch_bounds__(NT) void bwd_bf16_kernel(const BwdArgs args, const BwdPlan plan) {
   constexpr int KV_LDS = 2 * 2 * KV_BM * D * 2 + 4 * KV_BM * 4;
   constexpr int Q_LDS = 2 * 2 * Q_BN * D * 2;
   __shared__ __attribute__((aligned(16))) char smem[KV_LDS > Q_LDS ? KV_LDS : Q_LDS];
@@ -661,13 +663,13 @@ hipError_t launch_t(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream
   const dim3 grid(plan.n_kv_units + plan.n_q_units);
   const bool causal = args.a.causal != 0, mask = args.a.mask != nullptr;
   if (causal && mask)
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, true, true>), grid, dim3(256), 0, stream, args, plan);
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, true, true>), grid, dim3(NT), 0, stream, args, plan);
   else if (causal)
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, true, false>), grid, dim3(256), 0, stream, args, plan);
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, true, false>), grid, dim3(NT), 0, stream, args, plan);
   else if (mask)
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, false, true>), grid, dim3(256), 0, stream, args, plan);
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, false, true>), grid, dim3(NT), 0, stream, args, plan);
   else
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, false, false>), grid, dim3(256), 0, stream, args, plan);
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, false, false>), grid, dim3(NT), 0, stream, args, plan);
   return hipGetLastError();
 }
 

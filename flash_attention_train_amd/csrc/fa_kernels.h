@@ -49,6 +49,12 @@ __device__ __forceinline__ int tile_class(const AttnShape& a, int b, int rt, int
   return (int)((*w >> (8 * (i & 3))) & 0xffu);
 }
 
+// bf16 backward decomposition: waves per workgroup (one wave per SIMD: 1024 / kBwdWaves
+// workgroups fill the GPU), keys per dK/dV workgroup and query rows per dQ workgroup
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kBwdUnit = 32 * kBwdWaves;
+
 struct FwdArgs {
   AttnShape a;
   const void* q;
