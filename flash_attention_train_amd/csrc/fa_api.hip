@@ -7,6 +7,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <functional>
+#include <queue>
+#include <vector>
 
 #include "fa_kernels.h"
 #include "fa_train.h"
@@ -151,23 +154,104 @@ size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 // Split factors of the bf16 backward. Each split > 1 spreads one tile's walk over
 // several workgroups whose partial sums meet in fp32 atomics, so splits are only
 // used when the unsplit grid would leave compute units idle.
-void choose_splits(const fa_attn_params* p, bool accumulate, int* kv_split, int* q_split) {
-  // Splitting pays only when the unsplit grid cannot give every compute unit a
-  // workgroup; measured on the workloads at hand, beyond that the atomics and the
-  // extra clear / convert passes cost more than the better balance gains.
-  const int64_t target = 1024 / fa::kBwdWaves;  // workgroups that fill the GPU (one wave per SIMD)
-  const int64_t kv_units = (int64_t)((p->Sk + fa::kBwdUnit - 1) / fa::kBwdUnit) * p->B * p->Hkv;
-  const int64_t q_units = (int64_t)((p->Sq + fa::kBwdUnit - 1) / fa::kBwdUnit) * p->B * p->Hq;
-  const int64_t kv_pairs = (int64_t)((p->Sq + 63) / 64) * (p->Hq / p->Hkv);  // walk length of one key tile
-  const int64_t q_tiles = (p->Sk + 63) / 64;                                  // walk length of one query tile
-  int kv = 1, q = 1;
-  if (kv_units + q_units < target) {
-    kv = (int)std::min<int64_t>(std::min<int64_t>(kv_pairs, 64), (target + kv_units - 1) / kv_units);
-    q = (int)std::min<int64_t>(std::min<int64_t>(q_tiles, 64), (target + q_units - 1) / q_units);
+// Predicted time (us) of the bf16 backward for one split choice. The workgroups are
+// taken in dispatch order (dK/dV units by key tile, longest causal walks first, then
+// dQ units, longest first), each costed by its walk length, and placed greedily on
+// the compute units the way the dispatcher fills whichever frees first; split
+// choices add the reduce pass over their fp32 slices.
+double predict_bwd_us(const fa_attn_params* p, int kv, int q) {
+  // measured on MI355X with both workgroup kinds running side by side
+  constexpr double kPairUs = 2.7;         // one 64-row x 128-key dK/dV step
+  constexpr double kTileUs = 2.2;         // one 128-row x 64-key dQ step
+  constexpr double kPassUs = 2.0;         // one more kernel on the stream
+  constexpr double kBytesPerUs = 5.0e6;   // streaming rate of the reduce pass
+  const int U = fa::kBwdUnit, slots = 1024 / fa::kBwdWaves;
+  const int64_t nkt = (p->Sk + U - 1) / U, nqt = (p->Sq + U - 1) / U;
+  const int64_t nr64 = (p->Sq + 63) / 64, nk64 = (p->Sk + 63) / 64;
+  const int G = p->Hq / p->Hkv;
+  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+  for (int i = 0; i < slots; ++i) free_at.push(0.0);
+  double end = 0.0;
+  auto place = [&](double cost) {
+    const double t = free_at.top() + cost;
+    free_at.pop();
+    free_at.push(t);
+    end = std::max(end, t);
+  };
+  for (int64_t kt = 0; kt < nkt; ++kt) {
+    int64_t qt0 = 0;  // first 64-row tile that sees this key tile
+    if (p->causal) {
+      const int64_t first_row = kt * U - p->q_offset;
+      qt0 = first_row <= 0 ? 0 : std::min<int64_t>(first_row / 64, nr64);
+    }
+    const int64_t pairs = G * (nr64 - qt0);
+    const double cost = kPairUs * (double)((pairs + kv - 1) / kv);
+    for (int64_t u = 0; u < (int64_t)p->B * p->Hkv * kv; ++u) place(cost);
   }
+  for (int64_t qt = nqt - 1; qt >= 0; --qt) {
+    int64_t tiles = nk64;
+    if (p->causal) {
+      const int64_t last_key = p->q_offset + (qt + 1) * U - 1;
+      tiles = last_key < 0 ? 0 : std::min<int64_t>(last_key / 64 + 1, nk64);
+    }
+    const double cost = kTileUs * (double)((tiles + q - 1) / q);
+    for (int64_t u = 0; u < (int64_t)p->B * p->Hq * q; ++u) place(cost);
+  }
+  const double nk = (double)p->B * p->Hkv * p->Sk * p->D, nq = (double)p->B * p->Hq * p->Sq * p->D;
+  if (kv > 1) end += kPassUs + (2.0 * kv * nk * 4.0 + 2.0 * nk * 2.0) / kBytesPerUs;
+  if (q > 1) end += kPassUs + (q * nq * 4.0 + nq * 2.0) / kBytesPerUs;
+  return end;
+}
+
+// Split choice of the bf16 backward: the candidate with the least predicted time, kept
+// per shape in a small per-thread cache (the prediction walks every workgroup). Calls
+// with the same shape always get the same choice, so the workspace size the caller
+// was given matches the launch.
+void choose_splits(const fa_attn_params* p, bool accumulate, int* kv_split, int* q_split) {
   (void)accumulate;
-  *kv_split = p->kv_split ? p->kv_split : std::max(kv, 1);
-  *q_split = p->q_split ? p->q_split : std::max(q, 1);
+  int kv = 1, q = 1;
+  const int64_t units = (int64_t)((p->Sk + fa::kBwdUnit - 1) / fa::kBwdUnit) * p->B * p->Hkv +
+                        (int64_t)((p->Sq + fa::kBwdUnit - 1) / fa::kBwdUnit) * p->B * p->Hq;
+  if (units < 8 * 1024) {
+    struct Entry {
+      int64_t key[8];
+      int kv, q;
+    };
+    thread_local Entry cache[16];
+    thread_local int next = 0;
+    const int64_t key[8] = {p->B, p->Hq, p->Hkv, p->Sq, p->Sk, p->D, p->causal, p->q_offset};
+    bool hit = false;
+    for (const Entry& e : cache)
+      if (e.kv > 0 && std::equal(key, key + 8, e.key)) {
+        kv = e.kv;
+        q = e.q;
+        hit = true;
+        break;
+      }
+    if (!hit) {
+      const int64_t kv_pairs = (int64_t)((p->Sq + 63) / 64) * (p->Hq / p->Hkv);  // walk length, one key tile
+      const int64_t q_tiles = (p->Sk + 63) / 64;                                  // walk length, one query tile
+      double best = predict_bwd_us(p, 1, 1);
+      for (int ckv : {1, 2, 4, 8})
+        for (int cq : {1, 2, 4, 8, 16}) {
+          if ((ckv == 1 && cq == 1) || ckv > std::max<int64_t>(kv_pairs, 1) || cq > std::max<int64_t>(q_tiles, 1))
+            continue;
+          const double t = predict_bwd_us(p, ckv, cq);
+          if (t < 0.98 * best) {  // a split must pay for itself clearly
+            best = t;
+            kv = ckv;
+            q = cq;
+          }
+        }
+      Entry& e = cache[next];
+      next = (next + 1) % 16;
+      std::copy(key, key + 8, e.key);
+      e.kv = kv;
+      e.q = q;
+    }
+  }
+  *kv_split = p->kv_split ? p->kv_split : kv;
+  *q_split = p->q_split ? p->q_split : q;
 }
 
 struct WsLayout {
@@ -175,25 +259,28 @@ struct WsLayout {
   bool need_dq, need_dkdv;
 };
 
-// Workspace of the backward: fp32 accumulators for whatever the chosen
-// decomposition adds with atomics (dQ always for fp32 inputs).
+// Workspace of the backward: the fp32 partial slices of the chosen split (bf16), or the
+// fp32 dQ accumulator (fp32 inputs).
 WsLayout workspace_layout(const fa_attn_params* p, bool accumulate) {
   WsLayout w;
   const size_t nq = (size_t)p->B * p->Hq * p->Sq * p->D * sizeof(float);
   const size_t nk = (size_t)p->B * p->Hkv * p->Sk * p->D * sizeof(float);
+  size_t dq_bytes = nq, dk_bytes = 0;
   if (p->dtype == FA_BF16) {
     int kv, q;
     choose_splits(p, accumulate, &kv, &q);
     w.need_dq = q > 1;
-    w.need_dkdv = kv > 1 && !accumulate;
+    w.need_dkdv = kv > 1;
+    dq_bytes = w.need_dq ? q * nq : 0;
+    dk_bytes = w.need_dkdv ? kv * nk : 0;
   } else {
     w.need_dq = true;
     w.need_dkdv = false;
   }
   w.dq_off = 0;
-  w.dk_off = w.need_dq ? round256(nq) : 0;
-  w.dv_off = w.dk_off + (w.need_dkdv ? round256(nk) : 0);
-  w.total = w.dv_off + (w.need_dkdv ? round256(nk) : 0);
+  w.dk_off = w.need_dq ? round256(dq_bytes) : 0;
+  w.dv_off = w.dk_off + (w.need_dkdv ? round256(dk_bytes) : 0);
+  w.total = w.dv_off + (w.need_dkdv ? round256(dk_bytes) : 0);
   return w;
 }
 
@@ -270,27 +357,27 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
     int kv, q;
     choose_splits(p, accumulate, &kv, &q);
     fa::plan_bwd_bf16(a.a, kv, q, &plan);
-    a.dq_acc = wl.need_dq ? reinterpret_cast<float*>(ws + wl.dq_off) : nullptr;
-    plan.dk_acc = wl.need_dkdv ? reinterpret_cast<float*>(ws + wl.dk_off) : nullptr;
-    plan.dv_acc = wl.need_dkdv ? reinterpret_cast<float*>(ws + wl.dv_off) : nullptr;
+    // split walks write every element of their fp32 slices (zeros included), so the
+    // slices need no clearing; the reduce passes sum them into the outputs
+    a.dq_acc = nullptr;
+    plan.dq_part = wl.need_dq ? reinterpret_cast<float*>(ws + wl.dq_off) : nullptr;
+    plan.dk_part = wl.need_dkdv ? reinterpret_cast<float*>(ws + wl.dk_off) : nullptr;
+    plan.dv_part = wl.need_dkdv ? reinterpret_cast<float*>(ws + wl.dv_off) : nullptr;
     plan.dq = dq->data;
     plan.sdq = strides_of(dq);
     const int64_t nq = (int64_t)p->B * p->Hq * p->Sq * p->D, nk = (int64_t)p->B * p->Hkv * p->Sk * p->D;
-    if (wl.need_dq && (st = hip_status(fa::launch_zero_f32(a.dq_acc, nq, stream), "dq clear"))) return st;
-    if (wl.need_dkdv) {
-      if ((st = hip_status(fa::launch_zero_f32(plan.dk_acc, nk, stream), "dk clear"))) return st;
-      if ((st = hip_status(fa::launch_zero_f32(plan.dv_acc, nk, stream), "dv clear"))) return st;
-    }
     if ((st = hip_status(fa::launch_bwd_bf16(a, plan, stream), "backward"))) return st;
     if (wl.need_dq) {
-      fa::DqArgs c = {p->B, p->Hq, p->Sq, p->D, a.dq_acc, dq->data, strides_of(dq), p->scale};
-      if ((st = hip_status(fa::launch_dq_convert(c, 1, stream), "dq convert"))) return st;
+      fa::ReduceArgs r = {p->B, p->Hq, p->Sq, p->D, plan.dq_part, q, nq, dq->data, strides_of(dq), p->scale, 0};
+      if ((st = hip_status(fa::launch_reduce_parts(r, 1, stream), "dq reduce"))) return st;
     }
     if (wl.need_dkdv) {
-      fa::DqArgs ck = {p->B, p->Hkv, p->Sk, p->D, plan.dk_acc, dk->data, strides_of(dk), 1.f};
-      fa::DqArgs cv = {p->B, p->Hkv, p->Sk, p->D, plan.dv_acc, dv->data, strides_of(dv), 1.f};
-      if ((st = hip_status(fa::launch_dq_convert(ck, 1, stream), "dk convert"))) return st;
-      if ((st = hip_status(fa::launch_dq_convert(cv, 1, stream), "dv convert"))) return st;
+      // the chunked walk adds into its fp32 window accumulators; otherwise bf16 outputs
+      const int out_bf16 = accumulate ? 0 : 1, acc = accumulate ? 1 : 0;
+      fa::ReduceArgs rk = {p->B, p->Hkv, p->Sk, p->D, plan.dk_part, kv, nk, dk->data, strides_of(dk), p->scale, acc};
+      fa::ReduceArgs rv = {p->B, p->Hkv, p->Sk, p->D, plan.dv_part, kv, nk, dv->data, strides_of(dv), 1.f, acc};
+      if ((st = hip_status(fa::launch_reduce_parts(rk, out_bf16, stream), "dk reduce"))) return st;
+      if ((st = hip_status(fa::launch_reduce_parts(rv, out_bf16, stream), "dv reduce"))) return st;
     }
     return FA_OK;
   }

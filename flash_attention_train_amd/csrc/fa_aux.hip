@@ -67,6 +67,46 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const DqArgs p) {
   store8(dst, out);
 }
 
+// Sum of the backward's fp32 partial slices, 8 consecutive elements per thread: each
+// slice element is read once, the result written once (or added to an fp32 output).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void reduce_parts_kernel(const ReduceArgs p) {
+  constexpr int CPR = D / 8;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nrows = (int64_t)p.B * p.H * p.S;
+  if (c >= nrows * CPR) return;
+  const int64_t row = c / CPR;
+  const int d0 = (int)(c % CPR) * 8;
+  const int i = (int)(row % p.S);
+  const int h = (int)((row / p.S) % p.H);
+  const int b = (int)(row / ((int64_t)p.S * p.H));
+  const float* src = p.parts + row * D + d0;
+  f32x16 acc;
+  #pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  for (int s = 0; s < p.nparts; ++s) {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(src + s * p.part_stride);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(src + s * p.part_stride + 4);
+    #pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[j] += lo[j];
+      acc[4 + j] += hi[j];
+    }
+  }
+  T* dst = static_cast<T*>(p.out) + b * p.so.b + h * p.so.h + (int64_t)i * p.so.s + d0;
+  if (p.accumulate) {  // fp32 output only (checked by the caller)
+    float* f = reinterpret_cast<float*>(dst);
+    #pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] += acc[j] * p.scale;
+    return;
+  }
+  #pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] *= p.scale;
+  Frag<T> out;
+  pack8(out, acc, 0);
+  store8(dst, out);
+}
+
 // One workgroup per 64 x 64 mask block (clipped at Sq and Sk; entries outside count as
 // masked for the bits and are ignored by the class). Each wave takes 16 consecutive
 // rows with all 16 loads in flight at once; a wave ballot per row gives the row word,
@@ -173,6 +213,19 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream) {
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, reinterpret_cast<f32x4*>(p), n4);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_reduce_t(const ReduceArgs& p, hipStream_t stream) {
+  const int64_t chunks = (int64_t)p.B * p.H * p.S * (D / 8);
+  const dim3 grid((unsigned)((chunks + 255) / 256));
+  hipLaunchKernelGGL((reduce_parts_kernel<T, D>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_parts(const ReduceArgs& p, int is_bf16, hipStream_t stream) {
+  if (is_bf16) return p.D == 64 ? launch_reduce_t<bf16, 64>(p, stream) : launch_reduce_t<bf16, 128>(p, stream);
+  return p.D == 64 ? launch_reduce_t<float, 64>(p, stream) : launch_reduce_t<float, 128>(p, stream);
 }
 
 hipError_t launch_dq_convert(const DqArgs& p, int is_bf16, hipStream_t stream) {

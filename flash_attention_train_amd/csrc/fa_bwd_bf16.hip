@@ -22,12 +22,11 @@
 //    query row; dS^T then feeds dQ += dS K directly as the A operand, with the K
 //    operand read by LDS transpose reads.
 //
-// When a problem has too few tiles to fill the GPU, the dK/dV walk is split over
-// several workgroups per key tile and the dQ walk over several per query tile;
-// split partial sums are added with fp32 atomics into fp32 accumulators (a
-// workspace that a convert pass turns into the output dtype, or, for the chunked
-// walk, the caller's window accumulators). Unsplit work stores its results
-// directly. Masked entries get P = 0 exactly, so fully masked rows and key
+// When the launch balances better that way, the dK/dV walk is split over several
+// workgroups per key tile and the dQ walk over several per query tile; each split
+// stores its fp32 partial sums into a slice of its own (no atomics), and a reduce
+// pass sums the slices into the output dtype (or adds them to the chunked walk's
+// window accumulators). Unsplit work stores its results directly. Masked entries get P = 0 exactly, so fully masked rows and key
 // columns end with exactly zero gradients ("Flash Attn Training" skill page,
 // section 6, traps 8 and 9).
 #include "fa_device.h"
@@ -68,9 +67,6 @@ __device__ __forceinline__ void settle_acc(f32x16 (&acc)[N]) {
   for (int i = 0; i < N; ++i) asm volatile("" : "+a"(acc[i]));
 }
 
-__device__ __forceinline__ void atomic_add_f32(float* p, float v) {
-  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // unit -> (key tile, batch, kv head, split); key tiles vary slowest so that the long
 // causal tiles (small key index) are dispatched first
@@ -367,8 +363,11 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
 
   settle_acc(dk);
   settle_acc(dv);
-  // results: accumulator row = key 8 (r/4) + 4 g + r%4 of this wave, column d = 32 db + r32
-  const bool atomic = plan.kv_split > 1;
+  // results: accumulator row = key 8 (r/4) + 4 g + r%4 of this wave, column d = 32 db + r32.
+  // Split walks store their partial sums (unscaled) into their own fp32 slice, which a
+  // reduce pass sums; a workgroup with no live pair still stores its zeros.
+  const bool part = plan.kv_split > 1;
+  const int64_t part_off = (int64_t)split * a.B * a.Hkv * a.Sk * D;
   #pragma unroll
   for (int db = 0; db < DB; ++db) {
     #pragma unroll
@@ -376,30 +375,20 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
       const int kk = n0 + 32 * wave + 8 * (r >> 2) + 4 * g + (r & 3);
       if (kk >= a.Sk) continue;
       const int d = 32 * db + r32;
-      const float vk = dk[db][r] * a.scale, vv = dv[db][r];
-      if (args.accumulate || atomic) {
-        float* pk;
-        float* pv;
-        if (args.accumulate) {
-          pk = static_cast<float*>(args.dk) + b * args.sdk.b + hk * args.sdk.h + (int64_t)kk * args.sdk.s + d;
-          pv = static_cast<float*>(args.dv) + b * args.sdv.b + hk * args.sdv.h + (int64_t)kk * args.sdv.s + d;
-        } else {
-          const int64_t o = (((int64_t)b * a.Hkv + hk) * a.Sk + kk) * D + d;
-          pk = plan.dk_acc + o;
-          pv = plan.dv_acc + o;
-        }
-        if (atomic) {
-          atomic_add_f32(pk, vk);
-          atomic_add_f32(pv, vv);
-        } else {
-          *pk += vk;
-          *pv += vv;
-        }
+      if (part) {
+        const int64_t o = part_off + (((int64_t)b * a.Hkv + hk) * a.Sk + kk) * D + d;
+        plan.dk_part[o] = dk[db][r];
+        plan.dv_part[o] = dv[db][r];
+      } else if (args.accumulate) {
+        float* pk = static_cast<float*>(args.dk) + b * args.sdk.b + hk * args.sdk.h + (int64_t)kk * args.sdk.s + d;
+        float* pv = static_cast<float*>(args.dv) + b * args.sdv.b + hk * args.sdv.h + (int64_t)kk * args.sdv.s + d;
+        *pk += dk[db][r] * a.scale;
+        *pv += dv[db][r];
       } else {
         bf16* pk = static_cast<bf16*>(args.dk) + b * args.sdk.b + hk * args.sdk.h + (int64_t)kk * args.sdk.s + d;
         bf16* pv = static_cast<bf16*>(args.dv) + b * args.sdv.b + hk * args.sdv.h + (int64_t)kk * args.sdv.s + d;
-        *pk = (bf16)vk;
-        *pv = (bf16)vv;
+        *pk = (bf16)(dk[db][r] * a.scale);
+        *pv = (bf16)dv[db][r];
       }
     }
   }
@@ -620,8 +609,9 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
       const int qi = qw + 8 * (r >> 2) + 4 * g + (r & 3);
       if (qi >= a.Sq) continue;
       const int d = 32 * db + r32;
-      if (plan.q_split > 1) {
-        atomic_add_f32(args.dq_acc + (((int64_t)b * a.Hq + h) * a.Sq + qi) * D + d, dq[db][r]);
+      if (plan.q_split > 1) {  // this split's fp32 slice, summed by a reduce pass
+        plan.dq_part[(int64_t)split * a.B * a.Hq * a.Sq * D + (((int64_t)b * a.Hq + h) * a.Sq + qi) * D + d] =
+            dq[db][r];
       } else {
         bf16* pq = static_cast<bf16*>(plan.dq) + b * plan.sdq.b + h * plan.sdq.h + (int64_t)qi * plan.sdq.s + d;
         *pq = (bf16)(dq[db][r] * a.scale);

@@ -97,14 +97,28 @@ struct BwdArgs {
 
 // Work decomposition of the bf16 backward (one launch, two kinds of workgroups).
 struct BwdPlan {
-  int kv_split;    // workgroups sharing one 128-key tile's dK/dV walk (> 1: fp32 atomics)
-  int q_split;     // workgroups sharing one 128-row query tile's dQ walk (> 1: fp32 atomics)
+  int kv_split;    // workgroups sharing one key tile's dK/dV walk (> 1: fp32 partial slices)
+  int q_split;     // workgroups sharing one query tile's dQ walk (> 1: fp32 partial slices)
   int n_kv_units;  // dK/dV workgroups (launched first)
   int n_q_units;   // dQ workgroups
-  float* dk_acc;   // fp32 [B, Hkv, Sk, D] workspace when kv_split > 1 and not accumulating
-  float* dv_acc;
+  float* dk_part;  // fp32 [kv_split][B, Hkv, Sk, D] partial sums when kv_split > 1
+  float* dv_part;
+  float* dq_part;  // fp32 [q_split][B, Hq, Sq, D] partial sums when q_split > 1
   void* dq;        // dQ output (dtype) written directly when q_split == 1
   Strides sdq;
+};
+
+// out = scale * sum of nparts fp32 slices [B, H, S, D] (slice s at parts + s * part_stride),
+// stored in the output dtype, or added to an fp32 output when accumulate is set
+struct ReduceArgs {
+  int B, H, S, D;
+  const float* parts;
+  int nparts;
+  int64_t part_stride;
+  void* out;
+  Strides so;
+  float scale;
+  int accumulate;
 };
 
 struct DqArgs {
@@ -123,6 +137,7 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_mask_tiles(const AttnShape& a, uint8_t* tiles, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& args, int is_bf16, hipStream_t stream);
 hipError_t launch_dq_convert(const DqArgs& args, int is_bf16, hipStream_t stream);
+hipError_t launch_reduce_parts(const ReduceArgs& args, int is_bf16, hipStream_t stream);
 void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, BwdPlan* plan);
 hipError_t launch_bwd_bf16(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream);
 

@@ -109,10 +109,12 @@ def bwd_call(p, accumulate=False, ws=None, ws_bytes=None, **over):
 
 
 def test_backward_rejects():
+    # split walks keep one fp32 slice per split: dQ slices [q_split][B, Hq, Sq, D], dK and
+    # dV slices [kv_split][B, Hkv, Sk, D] each
     p = params(q_split=2, kv_split=1)
-    assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(p)) == 1 * 4 * 64 * 64 * 4
+    assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(p)) == 2 * (1 * 4 * 64 * 64 * 4)
     assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(params(q_split=1, kv_split=1))) == 0
-    assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(params(q_split=1, kv_split=2))) == 2 * 2 * 64 * 64 * 4
+    assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(params(q_split=1, kv_split=2))) == 2 * 2 * (2 * 64 * 64 * 4)
     assert bwd_call(p, ws=0) == 8
     assert bwd_call(p, ws_bytes=100) == 8
     assert bwd_call(p, ws=BASE + 12 * (1 << 24) + 16) == 5
