@@ -54,8 +54,10 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) from here on
   const int g = lane >> 5, r32 = lane & 31;
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int qt = gridDim.x - 1 - blockIdx.x;  // longest causal tiles first
+  // Workgroups are dispatched in linear order with x fastest: x walks (batch, head) and y
+  // the query tiles from the last, so every head's longest causal walks go out first.
+  const int h = blockIdx.x % a.Hq, b = blockIdx.x / a.Hq;
+  const int qt = gridDim.y - 1 - blockIdx.y;
   const int q0 = qt * BM;
   const int qw = q0 + wave * QB * 32;          // first row of this wave
   const int hk = h / a.G;
@@ -346,7 +348,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
 template <int D, int QB, int BN>
 hipError_t launch_t(const FwdArgs& args, hipStream_t stream) {
   constexpr int BM = 4 * QB * 32;
-  const dim3 grid((args.a.Sq + BM - 1) / BM, args.a.Hq, args.a.B);
+  const dim3 grid(args.a.Hq * args.a.B, (args.a.Sq + BM - 1) / BM);
   const bool causal = args.a.causal != 0, mask = args.a.mask != nullptr;
   if (causal && mask)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BN, true, true>), grid, dim3(256), 0, stream, args);
