@@ -159,16 +159,34 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
   }
   const int npairs = (nqt - qt0) * a.G;
 
+  // Pair p is (query tile qt0 + p / G, head hk G + p % G); this workgroup walks
+  // p = split, split + kv_split, ..., carried as a running (quotient, remainder) so that
+  // no step divides.
+  struct Pos {
+    int p, qi, hi;
+  };
+  const int step_q = plan.kv_split / a.G, step_h = plan.kv_split % a.G;
+  auto advance = [&](Pos x) {
+    x.p += plan.kv_split;
+    x.qi += step_q;
+    x.hi += step_h;
+    if (x.hi >= a.G) {
+      x.hi -= a.G;
+      ++x.qi;
+    }
+    return x;
+  };
+
   float lpre = 0.f;
-  auto pair_of = [&](int p, int& h, int& q0) {
-    h = hk * a.G + p % a.G;
-    q0 = (qt0 + p / a.G) * KV_BM;
+  auto pair_of = [&](const Pos& x, int& h, int& q0) {
+    h = hk * a.G + x.hi;
+    q0 = (qt0 + x.qi) * KV_BM;
   };
   // stage a pair's Q and dO tiles straight into LDS (rows past the end repeat the last
   // row, masked out on the tail tile) and fetch its LSE / Delta into a register
-  auto stage_pair = [&](int p, int buf) {
+  auto stage_pair = [&](const Pos& x, int buf) {
     int h, q0;
-    pair_of(p, h, q0);
+    pair_of(x, h, q0);
     const bf16* Q = static_cast<const bf16*>(args.q) + b * args.sq.b + h * args.sq.h + (int64_t)q0 * args.sq.s;
     const bf16* dO = static_cast<const bf16*>(args.dout) + b * args.sdo.b + h * args.sdo.h + (int64_t)q0 * args.sdo.s;
     TL::template stage<KV_BM, NT>(q_lds + buf * KV_BM * D, Q, args.sq.s, a.Sq - q0);
@@ -195,53 +213,54 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
   // block skips the mask reads.
   const int nct = (a.Sk + kMaskTile - 1) / kMaskTile;
   const int ct0 = n0 / kMaskTile;
-  auto live = [&](int pp) -> bool {
+  auto live = [&](const Pos& x) -> bool {
     if (!MASK || !a.tiles) return true;
-    const int rt = qt0 + pp / a.G;  // 64-row query tiles are the mask's row blocks
+    const int rt = qt0 + x.qi;  // 64-row query tiles are the mask's row blocks
     for (int ct = ct0; ct < ct0 + KV_BN / kMaskTile && ct < nct; ++ct)
       if (tile_class(a, b, rt, ct) != kTileDead) return true;
     return false;
   };
-  auto next_live = [&](int pp) {
-    while (pp < npairs && !live(pp)) pp += plan.kv_split;
-    return pp;
+  auto next_live = [&](Pos x) {
+    while (x.p < npairs && !live(x)) x = advance(x);
+    return x;
   };
   const int ct_w = ct0 + (32 * wave) / kMaskTile;  // this wave's 32 keys lie in one 64-key block
 
   // Per-pair mask state of this wave, fetched one pair ahead (its loads complete under
   // the end-of-iteration wait instead of stalling the pair): the block class and this
   // lane's key column visibility word.
-  auto mask_state = [&](int pp, int& cls, uint64_t& w) {
+  auto mask_state = [&](const Pos& x, int& cls, uint64_t& w) {
     cls = kTileBias;
     w = ~0ull;
     if (MASK && a.tiles) {
-      const int rt = qt0 + pp / a.G;
+      const int rt = qt0 + x.qi;
       cls = ct_w < nct ? tile_class(a, b, rt, ct_w) : kTileDead;
       if (ct_w < nct) w = a.colbits[(int64_t)tile_index(a, b, rt, ct_w) * kMaskTile + (key - ct_w * kMaskTile)];
     }
   };
 
-  int p = next_live(split);
+  Pos cur = next_live(Pos{split, split / a.G, split % a.G});
   int cls_cur = kTileBias;
   uint64_t wb_cur = ~0ull;
-  if (p < npairs) {
-    stage_pair(p, 0);
-    mask_state(p, cls_cur, wb_cur);
+  if (cur.p < npairs) {
+    stage_pair(cur, 0);
+    mask_state(cur, cls_cur, wb_cur);
   }
   wait_vm();  // on every path: the K / V fragments are complete before the walk
-  if (p < npairs) store_stats(0);
+  if (cur.p < npairs) store_stats(0);
   __syncthreads();
-  for (int it = 0; p < npairs; ++it) {
+  for (int it = 0; cur.p < npairs; ++it) {
     const int buf = it & 1;
-    const int pn = next_live(p + plan.kv_split);
+    const Pos nxt = next_live(advance(cur));
+    const bool more = nxt.p < npairs;
     int cls_next = kTileBias;
     uint64_t wb_next = ~0ull;
-    if (pn < npairs) {
-      mask_state(pn, cls_next, wb_next);
-      stage_pair(pn, buf ^ 1);  // lands while this pair is being processed
+    if (more) {
+      mask_state(nxt, cls_next, wb_next);
+      stage_pair(nxt, buf ^ 1);  // lands while this pair is being processed
     }
     int h, q0;
-    pair_of(p, h, q0);
+    pair_of(cur, h, q0);
     const int cls = cls_cur;
     const bool bias = MASK && cls == kTileBias;  // read mask values
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
@@ -354,9 +373,9 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     step_b(1, s1, dp1, pa1, ds1);
     step_c(1, pa1, ds1);
     wait_vm();
-    if (pn < npairs) store_stats(buf ^ 1);
+    if (more) store_stats(buf ^ 1);
     __syncthreads();
-    p = pn;
+    cur = nxt;
     cls_cur = cls_next;
     wb_cur = wb_next;
   }
