@@ -40,6 +40,9 @@ fa_status check_view(const fa_view* v, const char* name, int64_t B, int64_t H, i
   if (!v || !v->data) return fail(FA_ERR_NULL, "%s: view or data pointer is NULL", name);
   if (v->stride_b < 0 || v->stride_h < 0 || v->stride_s < 0)
     return fail(FA_ERR_STRIDE, "%s: negative stride", name);
+  // the tile loads address a tile's rows with 32-bit byte offsets from the tile's start
+  if (v->stride_s >= (int64_t(1) << 24))
+    return fail(FA_ERR_STRIDE, "%s: stride_s (%lld) must be below 2^24 elements", name, (long long)v->stride_s);
   const uintptr_t base = reinterpret_cast<uintptr_t>(v->data);
   if (align16) {
     if (base % 16) return fail(FA_ERR_ALIGN, "%s: data pointer is not 16-byte aligned", name);

@@ -189,8 +189,8 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     pair_of(x, h, q0);
     const bf16* Q = static_cast<const bf16*>(args.q) + b * args.sq.b + h * args.sq.h + (int64_t)q0 * args.sq.s;
     const bf16* dO = static_cast<const bf16*>(args.dout) + b * args.sdo.b + h * args.sdo.h + (int64_t)q0 * args.sdo.s;
-    TL::template stage<KV_BM, NT>(q_lds + buf * KV_BM * D, Q, args.sq.s, a.Sq - q0);
-    TL::template stage<KV_BM, NT>(do_lds + buf * KV_BM * D, dO, args.sdo.s, a.Sq - q0);
+    TL::template stage<KV_BM, NT, false>(q_lds + buf * KV_BM * D, Q, args.sq.s, a.Sq - q0);
+    TL::template stage<KV_BM, NT, false>(do_lds + buf * KV_BM * D, dO, args.sdo.s, a.Sq - q0);
     if (tid < 2 * KV_BM) {
       const int row = min(q0 + (tid % KV_BM), a.Sq - 1);
       // (scaled when stored, so that nothing waits for the load before the tile's work)
@@ -471,8 +471,8 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
   // the last key, masked out on the tail tile)
   auto stage_tile = [&](int kt, int buf) {
     const int key0 = kt * Q_BN;
-    TL::template stage<Q_BN, NT>(k_lds + buf * Q_BN * D, K + (int64_t)key0 * args.sk.s, args.sk.s, a.Sk - key0);
-    TL::template stage<Q_BN, NT>(v_lds + buf * Q_BN * D, V + (int64_t)key0 * args.sv.s, args.sv.s, a.Sk - key0);
+    TL::template stage<Q_BN, NT, false>(k_lds + buf * Q_BN * D, K + (int64_t)key0 * args.sk.s, args.sk.s, a.Sk - key0);
+    TL::template stage<Q_BN, NT, false>(v_lds + buf * Q_BN * D, V + (int64_t)key0 * args.sv.s, args.sv.s, a.Sk - key0);
   };
 
   const int G16 = lane >> 4, L16 = lane & 15;

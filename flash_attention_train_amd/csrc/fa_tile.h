@@ -47,20 +47,36 @@ struct Tile {
   // Stage rows [0, ROWS) of a tile whose row i is at src + i * stride (elements), rows
   // at or beyond `valid` replaced by row valid - 1 (the callers mask those rows out).
   // NT threads, NT / 64 waves; every thread issues ROWS * NCH / NT loads. The caller
-  // waits (vmcnt) and synchronises before reading the tile.
-  template <int ROWS, int NT>
+  // waits (vmcnt) and synchronises before reading the tile. A full tile (valid >= ROWS,
+  // the common case) costs no vector ALU work per load: a thread loads the same chunk of
+  // every row it touches (its loads are RSTEP rows apart and the swizzle repeats every 16
+  // rows), so one 32-bit byte offset serves all of them and the row step goes into the
+  // scalar base address. The row stride is below 2^24 elements (checked on the host).
+  // FAST_FULL = false keeps the per-lane addressing for every tile (the backward's walks,
+  // measured faster that way).
+  template <int ROWS, int NT, bool FAST_FULL = true>
   __device__ static __forceinline__ void stage(bf16* lds, const bf16* src, int64_t stride, int valid) {
+    constexpr int W = NT / 64, PER = ROWS * NCH / NT, RSTEP = 64 * W / NCH;
     static_assert((ROWS * NCH) % NT == 0, "tile must split evenly over the threads");
+    static_assert(RSTEP % 16 == 0, "a thread's rows must share their swizzle");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int i = 0; i < ROWS * NCH / NT; ++i) {
-      const int n0 = 64 * (wave + (NT / 64) * i);  // first chunk of this wave-instruction
+    if (FAST_FULL && valid >= ROWS) {
+      const int row0 = (64 * wave + lane) / NCH;
+      const int c = (lane % NCH) ^ swz(row0);
+      const uint32_t voff = ((uint32_t)row0 * (uint32_t)stride + 8u * (uint32_t)c) * 2u;
+      #pragma unroll
+      for (int i = 0; i < PER; ++i)
+        dma16(src + (int64_t)RSTEP * i * stride, voff, lds + 8 * 64 * (__builtin_amdgcn_readfirstlane(wave) + W * i));
+      return;
+    }
+    #pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int n0 = 64 * (wave + W * i);  // first chunk of this wave-instruction
       const int n = n0 + lane;
       const int row = n / NCH, p = n % NCH;
       const int c = p ^ swz(row);
       const int grow = row < valid ? row : valid - 1;
-      const bf16* g = src + (int64_t)grow * stride + 8 * c;
-      dma16(g, lds + 8 * n0);
+      dma16(src + (int64_t)grow * stride + 8 * c, lds + 8 * n0);
     }
   }
 
@@ -73,6 +89,13 @@ struct Tile {
     const uint32_t m0 =
         __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) bf16*)dst);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0)
+                 : "memory", "m0");
+  }
+  // the same with a wave-uniform base address and a per-lane 32-bit byte offset
+  __device__ static __forceinline__ void dma16(const bf16* sbase, uint32_t voff, bf16* dst) {
+    const uint32_t m0 =
+        __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) bf16*)dst);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
                  : "memory", "m0");
   }
 };

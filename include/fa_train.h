@@ -38,7 +38,7 @@
  *     dtypes; with FA_BF16 the probabilities and dS are rounded to bf16 before
  *     their matrix products.
  *   - Rows need 16-byte alignment: data pointers 16-byte aligned and every stride a
- *     multiple of 16 bytes' worth of elements.
+ *     multiple of 16 bytes' worth of elements; stride_s must be below 2^24 elements.
  *   - The mask is optional, fp32, additive, indexed [b][i][j] (j contiguous), with
  *     values 0, finite biases or -inf. mask_stride_b = 0 shares one mask across the
  *     batch. It is broadcast over heads.

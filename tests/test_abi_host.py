@@ -84,6 +84,8 @@ FWD_ERRORS = [
     ("unknown forward variant", params(fwd_variant=9), {}, 2),
     ("split out of range", params(kv_split=65), {}, 2),
     ("mask stride too small", params(mask=BASE + 9 * (1 << 24), mask_stride_q=32), {}, 4),
+    ("row stride 2^24", params(), {"k": view(1, H=2, stride_s=1 << 24, stride_h=(1 << 24) * 64,
+                                                stride_b=(1 << 24) * 128)}, 4),
 ]
 
 
