@@ -84,7 +84,7 @@ fa_status check_params(const fa_attn_params* p) {
   if (p->q_offset < -(int64_t(1) << 40) || p->q_offset > (int64_t(1) << 40))
     return fail(FA_ERR_SHAPE, "q_offset out of range");
   if (!(p->scale > 0.f) || !isfinite(p->scale)) return fail(FA_ERR_SHAPE, "scale must be positive and finite");
-  if (p->fwd_variant < 0 || p->fwd_variant > 2) return fail(FA_ERR_SHAPE, "unknown forward variant %d", p->fwd_variant);
+  if (p->fwd_variant < 0 || p->fwd_variant > 3) return fail(FA_ERR_SHAPE, "unknown forward variant %d", p->fwd_variant);
   if (p->kv_split < 0 || p->kv_split > 64 || p->q_split < 0 || p->q_split > 64)
     return fail(FA_ERR_SHAPE, "split hints must be in 0 .. 64");
   if (p->mask) {

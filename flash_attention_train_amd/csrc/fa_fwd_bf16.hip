@@ -39,27 +39,34 @@ __device__ __forceinline__ f32x16 zeros16() {
   return z;
 }
 
-template <int D, int QB, int BN, bool CAUSAL, bool MASK>
+// KS = 2 splits the keys of a query tile over two halves of the workgroup (for problems
+// with too few query tiles to fill the GPU): waves 0-1 and 2-3 own the same 64 rows, take
+// alternate live key tiles, and merge their (max, sum, O) in LDS at the end.
+template <int D, int QB, int BN, bool CAUSAL, bool MASK, int KS>
 __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const FwdArgs args) {
   constexpr int NW = 4;
-  constexpr int BM = NW * QB * 32;  // query rows per workgroup
+  constexpr int RB = NW / KS;       // waves (row blocks) per key half
+  constexpr int BM = RB * QB * 32;  // query rows per workgroup
   constexpr int KB = BN / 32;       // 32-key blocks per tile
   constexpr int DS = D / 16, DB = D / 32;
+  constexpr int NTS = 64 * RB;      // threads staging one key half's tiles
   using TL = Tile<D>;
-  __shared__ __attribute__((aligned(16))) bf16 k_lds[2][BN * D];
-  __shared__ __attribute__((aligned(16))) bf16 v_lds[2][BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 kv_lds[2][KS][2][BN * D];  // K and V: [key half][buffer]
+  bf16(&k_lds)[KS][2][BN * D] = kv_lds[0];
+  bf16(&v_lds)[KS][2][BN * D] = kv_lds[1];
 
   const AttnShape& a = args.a;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) from here on
+  const int rb = wave % RB, kh = wave / RB;                    // row block, key half
   const int g = lane >> 5, r32 = lane & 31;
   // Workgroups are dispatched in linear order with x fastest: x walks (batch, head) and y
   // the query tiles from the last, so every head's longest causal walks go out first.
   const int h = blockIdx.x % a.Hq, b = blockIdx.x / a.Hq;
   const int qt = gridDim.y - 1 - blockIdx.y;
   const int q0 = qt * BM;
-  const int qw = q0 + wave * QB * 32;          // first row of this wave
+  const int qw = q0 + rb * QB * 32;            // first row of this wave
   const int hk = h / a.G;
   const float cs = a.scale * kLog2e;           // scale > 0 (checked on the host)
 
@@ -100,10 +107,11 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
 
   // tile staging: K and V rows [key0, key0 + BN) straight into LDS; keys past the end
   // repeat the last key (masked out, P = 0, on the tail tile)
+  // (with KS = 2 each key half stages its own tile with its own two waves)
   auto stage_tile = [&](int kt, int buf) {
     const int key0 = kt * BN;
-    TL::template stage<BN, 256>(k_lds[buf], K + (int64_t)key0 * args.sk.s, args.sk.s, a.Sk - key0);
-    TL::template stage<BN, 256>(v_lds[buf], V + (int64_t)key0 * args.sv.s, args.sv.s, a.Sk - key0);
+    TL::template stage<BN, NTS, KS == 1>(k_lds[kh][buf], K + (int64_t)key0 * args.sk.s, args.sk.s, a.Sk - key0, rb);
+    TL::template stage<BN, NTS, KS == 1>(v_lds[kh][buf], V + (int64_t)key0 * args.sv.s, args.sv.s, a.Sk - key0, rb);
   };
 
   // With a mask tile map, key tiles whose mask blocks are dead for every row block
@@ -160,9 +168,16 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     }
   };
 
-  int kt = next_live(0);
+  // The walk goes in steps of KS live tiles (tk[0] < tk[1] ...); this wave's tile is tk[kh].
+  int tk[KS];
+  tk[0] = next_live(0);
+  #pragma unroll
+  for (int j = 1; j < KS; ++j) tk[j] = tk[j - 1] < kt_end ? next_live(tk[j - 1] + 1) : kt_end;
+  int kt = tk[kh];
   int cls_cur = kTileBias;
   uint64_t wb_cur[QB];
+  #pragma unroll
+  for (int qb = 0; qb < QB; ++qb) wb_cur[qb] = ~0ull;
   if (kt < kt_end) {
     stage_tile(kt, 0);
     mask_state(kt, cls_cur, wb_cur);
@@ -174,19 +189,25 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
   const int G16 = lane >> 4, L16 = lane & 15;
   const int tr_row = L16 >> 2, tr_col = 16 * (G16 & 1) + 4 * (L16 & 3);
 
-  for (int it = 0; kt < kt_end; ++it) {
+  for (int it = 0; tk[0] < kt_end; ++it) {
     const int buf = it & 1;
-    const int ktn = next_live(kt + 1);
+    int tn[KS];
+    tn[0] = tk[KS - 1] < kt_end ? next_live(tk[KS - 1] + 1) : kt_end;
+    #pragma unroll
+    for (int j = 1; j < KS; ++j) tn[j] = tn[j - 1] < kt_end ? next_live(tn[j - 1] + 1) : kt_end;
+    const int ktn = tn[kh];
     const bool more = ktn < kt_end;
     int cls_next = kTileBias;
     uint64_t wb_next[QB];
+    #pragma unroll
+    for (int qb = 0; qb < QB; ++qb) wb_next[qb] = ~0ull;
     if (more) {
       mask_state(ktn, cls_next, wb_next);
       stage_tile(ktn, buf ^ 1);  // lands while this tile is being processed
     }
-    const bf16* kb_lds = k_lds[buf];
-    const bf16* vb_lds = v_lds[buf];
-    const int cls = cls_cur;
+    const bf16* kb_lds = k_lds[kh][buf];
+    const bf16* vb_lds = v_lds[kh][buf];
+    const int cls = kt < kt_end ? cls_cur : kTileDead;  // a key half may sit out the last step
     if (cls != kTileDead) {
     const bool bias = MASK && cls == kTileBias;  // read mask values
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
@@ -314,10 +335,41 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     }  // cls != dead
     wait_vm();
     __syncthreads();
+    #pragma unroll
+    for (int j = 0; j < KS; ++j) tk[j] = tn[j];
     kt = ktn;
     cls_cur = cls_next;
     #pragma unroll
     for (int qb = 0; qb < QB; ++qb) wb_cur[qb] = wb_next[qb];
+  }
+
+  if constexpr (KS > 1) {
+    // merge the key halves: half 1 leaves (base, sum, O) per lane in LDS (the tile buffers
+    // are free after the last barrier), half 0 rescales both to the larger base and adds
+    static_assert(KS == 2 && QB == 1, "the key split pairs two halves of one-block waves");
+    constexpr int NV = DB * 16 + 2;  // floats per lane
+    static_assert(RB * NV * 64 * 4 <= (int)sizeof(kv_lds), "merge buffer fits in the tile buffers");
+    float* mrg = reinterpret_cast<float*>(&kv_lds[0][0][0][0]) + rb * NV * 64;
+    if (kh == 1) {
+      #pragma unroll
+      for (int db = 0; db < DB; ++db)
+        #pragma unroll
+        for (int r = 0; r < 16; ++r) mrg[(db * 16 + r) * 64 + lane] = oacc[0][db][r];
+      mrg[(DB * 16) * 64 + lane] = base[0];
+      mrg[(DB * 16 + 1) * 64 + lane] = lsum[0];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float b1 = mrg[(DB * 16) * 64 + lane], l1 = mrg[(DB * 16 + 1) * 64 + lane];
+    const float nb = fmaxf(base[0], b1);
+    const float f0 = base[0] == neg_inf() ? 0.f : fast_exp2(base[0] - nb);
+    const float f1 = b1 == neg_inf() ? 0.f : fast_exp2(b1 - nb);
+    #pragma unroll
+    for (int db = 0; db < DB; ++db)
+      #pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[0][db][r] = oacc[0][db][r] * f0 + mrg[(db * 16 + r) * 64 + lane] * f1;
+    lsum[0] = lsum[0] * f0 + l1 * f1;
+    base[0] = nb;
   }
 
   // epilogue: O = acc / l, LSE = (base + log2 l) ln 2; fully masked rows -> 0, 0
@@ -345,28 +397,35 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
   }
 }
 
-template <int D, int QB, int BN>
+template <int D, int QB, int BN, int KS>
 hipError_t launch_t(const FwdArgs& args, hipStream_t stream) {
-  constexpr int BM = 4 * QB * 32;
+  constexpr int BM = 4 / KS * QB * 32;
   const dim3 grid(args.a.Hq * args.a.B, (args.a.Sq + BM - 1) / BM);
   const bool causal = args.a.causal != 0, mask = args.a.mask != nullptr;
   if (causal && mask)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BN, true, true>), grid, dim3(256), 0, stream, args);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BN, true, true, KS>), grid, dim3(256), 0, stream, args);
   else if (causal)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BN, true, false>), grid, dim3(256), 0, stream, args);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BN, true, false, KS>), grid, dim3(256), 0, stream, args);
   else if (mask)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BN, false, true>), grid, dim3(256), 0, stream, args);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BN, false, true, KS>), grid, dim3(256), 0, stream, args);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BN, false, false>), grid, dim3(256), 0, stream, args);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BN, false, false, KS>), grid, dim3(256), 0, stream, args);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const FwdArgs& args, int variant, hipStream_t stream) {
+  if (variant == 2) return launch_t<D, 2, 32, 1>(args, stream);
+  if (variant == 3) return launch_t<D, 1, 32, 2>(args, stream);
+  return launch_t<D, 1, 64, 1>(args, stream);
 }
 
 }  // namespace
 
-// variant: 1 = 32 query rows per wave, 64-key tiles; 2 = 64 rows per wave, 32-key tiles
+// variant: 1 = 32 query rows per wave, 64-key tiles; 2 = 64 rows per wave, 32-key tiles;
+// 3 = 32 rows per wave, keys split over two halves of the workgroup, 32-key tiles
 hipError_t launch_fwd_bf16(const FwdArgs& args, int variant, hipStream_t stream) {
-  if (args.a.D == 64) return variant == 2 ? launch_t<64, 2, 32>(args, stream) : launch_t<64, 1, 64>(args, stream);
-  return variant == 2 ? launch_t<128, 2, 32>(args, stream) : launch_t<128, 1, 64>(args, stream);
+  return args.a.D == 64 ? launch_d<64>(args, variant, stream) : launch_d<128>(args, variant, stream);
 }
 
 }  // namespace fa

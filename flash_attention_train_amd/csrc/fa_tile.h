@@ -55,11 +55,14 @@ struct Tile {
   // FAST_FULL = false keeps the per-lane addressing for every tile (the backward's walks,
   // measured faster that way).
   template <int ROWS, int NT, bool FAST_FULL = true>
-  __device__ static __forceinline__ void stage(bf16* lds, const bf16* src, int64_t stride, int valid) {
+  __device__ static __forceinline__ void stage(bf16* lds, const bf16* src, int64_t stride, int valid,
+                                               int group_wave = -1) {
     constexpr int W = NT / 64, PER = ROWS * NCH / NT, RSTEP = 64 * W / NCH;
     static_assert((ROWS * NCH) % NT == 0, "tile must split evenly over the threads");
-    static_assert(RSTEP % 16 == 0, "a thread's rows must share their swizzle");
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    static_assert(!FAST_FULL || RSTEP % 16 == 0, "a thread's rows must share their swizzle");
+    // group_wave: this wave's index among the NT / 64 staging waves (default: its index
+    // in the workgroup)
+    const int lane = threadIdx.x & 63, wave = group_wave < 0 ? (int)(threadIdx.x >> 6) : group_wave;
     if (FAST_FULL && valid >= ROWS) {
       const int row0 = (64 * wave + lane) / NCH;
       const int c = (lane % NCH) ^ swz(row0);

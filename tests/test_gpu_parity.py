@@ -150,10 +150,12 @@ def test_chunked_walk_small():
     assert np.abs(dk2.cpu().numpy() - dk_acc.cpu().numpy()).max() <= 1e-5 * np.abs(got["dK"]).max()
 
 
-@pytest.mark.parametrize("config", [1, 2])
-@pytest.mark.parametrize("name", ["dit_sa_ragged", "lm_causal_gqa4", "chunk_offset", "random_bias_bcast", "d64_bf16"])
+@pytest.mark.parametrize("config", [1, 2, 3])
+@pytest.mark.parametrize("name", ["dit_sa_ragged", "dit_ca_ragged", "lm_causal_gqa4", "chunk_offset",
+                                  "random_bias_bcast", "d64_bf16", "single_query_single_key"])
 def test_forward_variants(name, config):
-    """Both bf16 forward configurations (32 or 64 query rows per wave) against the oracle."""
+    """Every bf16 forward configuration (32 or 64 query rows per wave; keys split over two
+    halves of the workgroup, merged at the end) against the oracle."""
     c = CASES[name]()
     t = upload(c)
     o, lse = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
@@ -272,6 +274,12 @@ def test_mask_tile_map_and_skipping(name):
     rows = (blocks.astype(np.uint64) * weights[None, None, None, None, :]).sum(axis=4, dtype=np.uint64)
     cols = (blocks.astype(np.uint64) * weights[None, None, None, :, None]).sum(axis=3, dtype=np.uint64)
     assert np.array_equal(words[0], rows) and np.array_equal(words[1], cols)
+    for variant in (1, 3):  # the key-split forward walks the live tiles in pairs
+        o3, lse3 = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
+                               q_offset=c.q_offset, mask_tiles=tiles, variant=variant)
+        torch.cuda.synchronize()
+        ref = oracle_full(c)
+        compare_full(c, {"O": host64(o3), "LSE": host64(lse3)}, ref, names=("O", "LSE"))
     o, lse = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
                          q_offset=c.q_offset, mask_tiles=tiles)
     delta = binding.bwd_preprocess(o, t["do"])
