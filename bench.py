@@ -304,7 +304,7 @@ def main():
                    "seq_len": w.case.Sq, "unmasked_pairs": w.pairs, "gflop_per_step": round(r["gflop_per_step"], 3)},
         "pct_of_peak": round(100.0 * r["tflops"] / peak, 2),
         "roofline": {"kernel": "bwd_bf16_kernel (fa_train_bwd)" if single else
-                     "fa_train_bwd (bwd_bf16_kernel + reduce_parts_kernel x2)", "bound": "mfma",
+                     "fa_train_bwd (bwd_bf16_kernel + reduce_parts_kernel)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": measured_traffic(args.workload),
                      "flop_per_launch": w.bwd_flops, "launch_ms": round(r["bwd_ms_mean"], 5)},

@@ -372,15 +372,14 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
     if ((st = hip_status(fa::launch_bwd_bf16(a, plan, stream), "backward"))) return st;
     if (wl.need_dq) {
       fa::ReduceArgs r = {p->B, p->Hq, p->Sq, p->D, plan.dq_part, q, nq, dq->data, strides_of(dq), p->scale, 0};
-      if ((st = hip_status(fa::launch_reduce_parts(r, 1, stream), "dq reduce"))) return st;
+      if ((st = hip_status(fa::launch_reduce_parts(r, nullptr, 1, stream), "dq reduce"))) return st;
     }
     if (wl.need_dkdv) {
       // the chunked walk adds into its fp32 window accumulators; otherwise bf16 outputs
       const int out_bf16 = accumulate ? 0 : 1, acc = accumulate ? 1 : 0;
       fa::ReduceArgs rk = {p->B, p->Hkv, p->Sk, p->D, plan.dk_part, kv, nk, dk->data, strides_of(dk), p->scale, acc};
       fa::ReduceArgs rv = {p->B, p->Hkv, p->Sk, p->D, plan.dv_part, kv, nk, dv->data, strides_of(dv), 1.f, acc};
-      if ((st = hip_status(fa::launch_reduce_parts(rk, out_bf16, stream), "dk reduce"))) return st;
-      if ((st = hip_status(fa::launch_reduce_parts(rv, out_bf16, stream), "dv reduce"))) return st;
+      if ((st = hip_status(fa::launch_reduce_parts(rk, &rv, out_bf16, stream), "dk / dv reduce"))) return st;
     }
     return FA_OK;
   }

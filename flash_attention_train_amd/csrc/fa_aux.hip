@@ -70,7 +70,8 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const DqArgs p) {
 // Sum of the backward's fp32 partial slices, 8 consecutive elements per thread: each
 // slice element is read once, the result written once (or added to an fp32 output).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void reduce_parts_kernel(const ReduceArgs p) {
+__global__ __launch_bounds__(256) void reduce_parts_kernel(const ReduceArgs p0, const ReduceArgs p1) {
+  const ReduceArgs& p = blockIdx.y ? p1 : p0;  // one launch reduces up to two tensors (dK and dV)
   constexpr int CPR = D / 8;
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t nrows = (int64_t)p.B * p.H * p.S;
@@ -84,6 +85,7 @@ __global__ __launch_bounds__(256) void reduce_parts_kernel(const ReduceArgs p) {
   f32x16 acc;
   #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  #pragma unroll 4
   for (int s = 0; s < p.nparts; ++s) {
     const f32x4 lo = *reinterpret_cast<const f32x4*>(src + s * p.part_stride);
     const f32x4 hi = *reinterpret_cast<const f32x4*>(src + s * p.part_stride + 4);
@@ -216,16 +218,17 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream) {
 }
 
 template <typename T, int D>
-hipError_t launch_reduce_t(const ReduceArgs& p, hipStream_t stream) {
-  const int64_t chunks = (int64_t)p.B * p.H * p.S * (D / 8);
-  const dim3 grid((unsigned)((chunks + 255) / 256));
-  hipLaunchKernelGGL((reduce_parts_kernel<T, D>), grid, dim3(256), 0, stream, p);
+hipError_t launch_reduce_t(const ReduceArgs& p, const ReduceArgs* p1, hipStream_t stream) {
+  const int64_t chunks = (int64_t)p.B * p.H * p.S * (D / 8);  // p1 has the same shape
+  const dim3 grid((unsigned)((chunks + 255) / 256), p1 ? 2 : 1);
+  hipLaunchKernelGGL((reduce_parts_kernel<T, D>), grid, dim3(256), 0, stream, p, p1 ? *p1 : p);
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_parts(const ReduceArgs& p, int is_bf16, hipStream_t stream) {
-  if (is_bf16) return p.D == 64 ? launch_reduce_t<bf16, 64>(p, stream) : launch_reduce_t<bf16, 128>(p, stream);
-  return p.D == 64 ? launch_reduce_t<float, 64>(p, stream) : launch_reduce_t<float, 128>(p, stream);
+hipError_t launch_reduce_parts(const ReduceArgs& p, const ReduceArgs* p1, int is_bf16, hipStream_t stream) {
+  if (is_bf16)
+    return p.D == 64 ? launch_reduce_t<bf16, 64>(p, p1, stream) : launch_reduce_t<bf16, 128>(p, p1, stream);
+  return p.D == 64 ? launch_reduce_t<float, 64>(p, p1, stream) : launch_reduce_t<float, 128>(p, p1, stream);
 }
 
 hipError_t launch_dq_convert(const DqArgs& p, int is_bf16, hipStream_t stream) {

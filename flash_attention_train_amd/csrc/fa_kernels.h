@@ -137,7 +137,8 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_mask_tiles(const AttnShape& a, uint8_t* tiles, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& args, int is_bf16, hipStream_t stream);
 hipError_t launch_dq_convert(const DqArgs& args, int is_bf16, hipStream_t stream);
-hipError_t launch_reduce_parts(const ReduceArgs& args, int is_bf16, hipStream_t stream);
+// reduces args, and args1 too when given (same shape and dtype: one launch for dK and dV)
+hipError_t launch_reduce_parts(const ReduceArgs& args, const ReduceArgs* args1, int is_bf16, hipStream_t stream);
 void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, BwdPlan* plan);
 hipError_t launch_bwd_bf16(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream);
 
