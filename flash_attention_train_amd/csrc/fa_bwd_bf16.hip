@@ -98,21 +98,55 @@ __device__ __forceinline__ QUnit q_unit_of(const AttnShape& a, const BwdPlan& pl
 // Does any mask block of rows [r0, r0 + nr) x keys [c0, c0 + nc) (in 64-blocks) carry
 // additive values? Units whose blocks are all dead / open / 0-or--inf run a body
 // compiled without the mask-value reads, which keeps their loop free of that code.
+// Called by the whole workgroup: the threads test the blocks together.
 __device__ __forceinline__ bool any_bias_block(const AttnShape& a, int b, int rb0, int nrb, int cb0, int ncb) {
   if (!a.tiles) return true;
   const int nrt = (a.Sq + kMaskTile - 1) / kMaskTile, nct = (a.Sk + kMaskTile - 1) / kMaskTile;
-  for (int rt = rb0; rt < rb0 + nrb && rt < nrt; ++rt)
-    for (int ct = cb0; ct < cb0 + ncb && ct < nct; ++ct)
-      if (tile_class(a, b, rt, ct) == kTileBias) return true;
-  return false;
+  nrb = min(nrb, nrt - rb0);
+  ncb = min(ncb, nct - cb0);
+  int any = 0;
+  for (int i = threadIdx.x; i < nrb * ncb; i += NT) {
+    const int rt = rb0 + i / ncb, ct = cb0 + i % ncb;
+    any |= tile_class(a, b, rt, ct) == kTileBias;
+  }
+  return __syncthreads_or(any) != 0;
 }
 
 // ---------------------------------------------------------------------------
 // dK / dV workgroup
 // ---------------------------------------------------------------------------
+// The live candidates of a walk (candidate j = 0 .. n - 1), NT at a time as bit words in
+// LDS: every thread tests one candidate, so that no step of the walk waits on a class
+// load. The walk is workgroup-uniform, and every call is made by the whole workgroup at
+// the same point.
+struct LiveWords {
+  uint64_t* words;  // [kBwdWaves] in LDS
+  int base;
+  template <class F>
+  __device__ __forceinline__ int next(int j, int n, int tid, F&& live) {
+    static_assert(NT == 64 * kBwdWaves && (NT & (NT - 1)) == 0, "one bit word per wave");
+    while (j < n) {
+      if (j >= base + NT) {
+        const int c = (j & ~(NT - 1)) + tid;
+        const uint64_t w = __ballot(c < n && live(c));
+        __syncthreads();  // the previous words are no longer read
+        if ((tid & 63) == 0) words[tid >> 6] = w;
+        __syncthreads();
+        base = j & ~(NT - 1);
+      }
+      const int off = j - base;
+      const uint64_t bits = words[off >> 6] >> (off & 63);
+      if (bits) return j + (int)__builtin_ctzll(bits);
+      j = base + 64 * ((off >> 6) + 1);
+    }
+    return n;
+  }
+};
+
 template <int D, bool CAUSAL, bool MASK, bool BIAS>
 __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
   constexpr int DS = D / 16, DB = D / 32;
+  static_assert(8 % DS == 0 && 8 % (2 * DB) == 0, "each woven slice holds whole product pairs");
   using TL = Tile<D>;
   bf16* q_lds = reinterpret_cast<bf16*>(smem);                 // [2][KV_BM * D]
   bf16* do_lds = q_lds + 2 * KV_BM * D;                        // [2][KV_BM * D]
@@ -142,6 +176,10 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
       zero(vf[s]);
     }
   }
+  // the K / V operand fragments live in accumulation registers for the whole walk (matrix
+  // instructions read their A / B operands from there), leaving the vector file to the pairs
+  #pragma unroll
+  for (int s = 0; s < DS; ++s) asm volatile("" : "+a"(kf[s]), "+a"(vf[s]));
   f32x16 dk[DB], dv[DB];
   #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -163,11 +201,12 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
   // p = split, split + kv_split, ..., carried as a running (quotient, remainder) so that
   // no step divides.
   struct Pos {
-    int p, qi, hi;
+    int p, qi, hi, j;  // j: the candidate's number in this walk
   };
   const int step_q = plan.kv_split / a.G, step_h = plan.kv_split % a.G;
   auto advance = [&](Pos x) {
     x.p += plan.kv_split;
+    ++x.j;
     x.qi += step_q;
     x.hi += step_h;
     if (x.hi >= a.G) {
@@ -213,34 +252,43 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
   // block skips the mask reads.
   const int nct = (a.Sk + kMaskTile - 1) / kMaskTile;
   const int ct0 = n0 / kMaskTile;
-  auto live = [&](const Pos& x) -> bool {
-    if (!MASK || !a.tiles) return true;
-    const int rt = qt0 + x.qi;  // 64-row query tiles are the mask's row blocks
+  auto live = [&](int j) -> bool {  // candidate j: pair split + j kv_split
+    const int rt = qt0 + (split + j * plan.kv_split) / a.G;  // 64-row query tiles are the mask's row blocks
     for (int ct = ct0; ct < ct0 + KV_BN / kMaskTile && ct < nct; ++ct)
       if (tile_class(a, b, rt, ct) != kTileDead) return true;
     return false;
   };
+  __shared__ uint64_t live_lds[kBwdWaves];
+  LiveWords lw{live_lds, -NT};
+  const int ncand = npairs > split ? (npairs - split + plan.kv_split - 1) / plan.kv_split : 0;
   auto next_live = [&](Pos x) {
-    while (x.p < npairs && !live(x)) x = advance(x);
-    return x;
+    if (!MASK || !a.tiles || x.p >= npairs) return x;
+    const int j = lw.next(x.j, ncand, tid, live);
+    if (j == x.j) return x;
+    if (j >= ncand) return Pos{npairs, 0, 0, ncand};
+    const int p = split + j * plan.kv_split;  // after a skip only
+    return Pos{p, p / a.G, p % a.G, j};
   };
   const int ct_w = ct0 + (32 * wave) / kMaskTile;  // this wave's 32 keys lie in one 64-key block
 
   // Per-pair mask state of this wave, fetched one pair ahead (its loads complete under
   // the end-of-iteration wait instead of stalling the pair): the block class and this
   // lane's key column visibility word.
-  auto mask_state = [&](const Pos& x, int& cls, uint64_t& w) {
-    cls = kTileBias;
+  auto mask_state = [&](const Pos& x, ClassAhead& cls, uint64_t& w) {
+    cls = ClassAhead{0u, kSelBias};
     w = ~0ull;
     if (MASK && a.tiles) {
-      const int rt = qt0 + x.qi;
-      cls = ct_w < nct ? tile_class(a, b, rt, ct_w) : kTileDead;
-      if (ct_w < nct) w = a.colbits[(int64_t)tile_index(a, b, rt, ct_w) * kMaskTile + (key - ct_w * kMaskTile)];
+      cls.sel = kSelDead;
+      if (ct_w < nct) {
+        const int i = tile_index(a, b, qt0 + x.qi, ct_w);
+        cls = class_ahead(a, i);
+        w = a.colbits[(int64_t)i * kMaskTile + (key - ct_w * kMaskTile)];
+      }
     }
   };
 
-  Pos cur = next_live(Pos{split, split / a.G, split % a.G});
-  int cls_cur = kTileBias;
+  Pos cur = next_live(Pos{split, split / a.G, split % a.G, 0});
+  ClassAhead cls_cur{0u, kSelBias};
   uint64_t wb_cur = ~0ull;
   if (cur.p < npairs) {
     stage_pair(cur, 0);
@@ -253,7 +301,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     const int buf = it & 1;
     const Pos nxt = next_live(advance(cur));
     const bool more = nxt.p < npairs;
-    int cls_next = kTileBias;
+    ClassAhead cls_next{0u, kSelBias};
     uint64_t wb_next = ~0ull;
     if (more) {
       mask_state(nxt, cls_next, wb_next);
@@ -261,7 +309,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     }
     int h, q0;
     pair_of(cur, h, q0);
-    const int cls = cls_cur;
+    const int cls = class_of(cls_cur);
     const bool bias = MASK && cls == kTileBias;  // read mask values
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
     const bf16* qb_lds = q_lds + buf * KV_BM * D;
@@ -290,10 +338,9 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
 
     // The pair is two 32-row blocks, each in three steps: products S = Q K^T and
     // dP = dO V^T (A), the softmax gradient (B) and the products dV += P^T dO,
-    // dK += dS^T Q (C). They are issued as A0 A1 B0 C0 B1 C1 so that each block's
-    // VALU work (B) has the other block's matrix products beside it to overlap with;
-    // masking is applied unconditionally (a no-op word on open blocks) to keep the
-    // whole pair one straight-line region for the scheduler.
+    // dK += dS^T Q (C). They run as A0, A1 with B0, C0 with B1, C1, so that each
+    // block's vector work (B) has the other block's matrix products beside it;
+    // masking is applied unconditionally (a no-op word on open blocks).
     auto step_a = [&](int qb, f32x16& sacc, f32x16& dpacc) {
       bf16x8 qa[DS], da[DS];
       #pragma unroll
@@ -309,54 +356,27 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
         mma(dpacc, da[s], vf[s]);
       }
     };
-    // lane (key, half g), register r -> query row 32 qb + 8 (r/4) + 4 g + r%4
-    auto step_b = [&](int qb, f32x16& sacc, f32x16& dpacc, bf16x8 (&pa)[2], bf16x8 (&dsa)[2]) {
-      if (BIAS && bias) {  // additive mask values (rows past the end read the last row)
-        const float* mk = a.mask + b * a.mask_sb + min(key, a.Sk - 1);
-        #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = min(q0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3), a.Sq - 1);
-          sacc[r] += mk[(int64_t)row * a.mask_sq] * args.inv_scale;
-        }
-      }
-      // hidden scores -> -inf (P = 0); bit 8 rr + e of w <-> register 4 rr + e
-      const uint32_t w = (uint32_t)(vis >> (32 * qb + 4 * g));
+    // transpose reads of dO^T / Q^T for half hh of block qb (the operands of step C):
+    // registers 8 hh .. 8 hh + 7 of the score accumulators hold rows
+    // 32 qb + 16 hh + 8 t + 4 g + e, exactly the rows each read returns
+    auto read_c = [&](int qb, int hh, bf16x8 (&dob)[DB], bf16x8 (&qbt)[DB]) {
+      const int rbase = 32 * qb + 16 * hh + 4 * g + tr_row;
       #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = ninf_unless_bit(sacc[r], w, 8 * (r >> 2) + (r & 3));
-      #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_b + 32 * qb + 8 * rr + 4 * g);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt_b + 32 * qb + 8 * rr + 4 * g);
-        #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pv = fast_exp2(fmaf(sacc[4 * rr + e], cs, -l4[e]));
-          sacc[4 * rr + e] = pv;
-          dpacc[4 * rr + e] = pv * (dpacc[4 * rr + e] - d4[e]);
-        }
-      }
-      #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        pack8(pa[hh], sacc, 8 * hh);
-        pack8(dsa[hh], dpacc, 8 * hh);
+      for (int db = 0; db < DB; ++db) {
+        const int col = 32 * db + tr_col;
+        const bf16x4 d0 = TL::read_tr(db_lds, rbase, col);
+        const bf16x4 d1 = TL::read_tr(db_lds, rbase + 8, col);
+        const bf16x4 q0v = TL::read_tr(qb_lds, rbase, col);
+        const bf16x4 q1v = TL::read_tr(qb_lds, rbase + 8, col);
+        dob[db] = bf16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+        qbt[db] = bf16x8{q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
       }
     };
-    // registers 8 hh .. 8 hh + 7 of the accumulators hold rows 32 qb + 16 hh + 8 t + 4 g + e,
-    // exactly the rows each transpose read of dO^T / Q^T returns
     auto step_c = [&](int qb, const bf16x8 (&pa)[2], const bf16x8 (&dsa)[2]) {
       #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const int rbase = 32 * qb + 16 * hh + 4 * g + tr_row;
         bf16x8 dob[DB], qbt[DB];
-        #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int col = 32 * db + tr_col;
-          const bf16x4 d0 = TL::read_tr(db_lds, rbase, col);
-          const bf16x4 d1 = TL::read_tr(db_lds, rbase + 8, col);
-          const bf16x4 q0v = TL::read_tr(qb_lds, rbase, col);
-          const bf16x4 q1v = TL::read_tr(qb_lds, rbase + 8, col);
-          dob[db] = bf16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-          qbt[db] = bf16x8{q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
-        }
+        read_c(qb, hh, dob, qbt);
         #pragma unroll
         for (int db = 0; db < DB; ++db) {
           mma_acc(dv[db], pa[hh], dob[db]);
@@ -364,13 +384,101 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
         }
       }
     };
+    // step B for block qb, scores in sacc / dpacc (lane = key, half g; register r = query
+    // row 32 qb + 8 (r/4) + 4 g + r%4): additive mask values and the row statistics
+    // first, then slice i finishes registers 2 i and 2 i + 1 (hidden scores -> -inf,
+    // P = 0; bit 8 rr + e of the visibility word <-> register 4 rr + e)
+    struct RowStats {
+      uint32_t w;
+      f32x4 l4[4], d4[4];
+    };
+    auto stats_b = [&](int qb, f32x16& sacc, RowStats& st) {
+      if (BIAS && bias) {
+        const float* mk = a.mask + b * a.mask_sb + min(key, a.Sk - 1);
+        #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = min(q0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3), a.Sq - 1);
+          sacc[r] += mk[(int64_t)row * a.mask_sq] * args.inv_scale;
+        }
+      }
+      st.w = (uint32_t)(vis >> (32 * qb + 4 * g));
+      #pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        st.l4[rr] = *reinterpret_cast<const f32x4*>(lse_b + 32 * qb + 8 * rr + 4 * g);
+        st.d4[rr] = *reinterpret_cast<const f32x4*>(dlt_b + 32 * qb + 8 * rr + 4 * g);
+      }
+    };
+    auto slice_b = [&](int i, const RowStats& st, f32x16& sacc, f32x16& dpacc) {
+      #pragma unroll
+      for (int r = 2 * i; r < 2 * i + 2; ++r) {
+        const float sv = ninf_unless_bit(sacc[r], st.w, 8 * (r >> 2) + (r & 3));
+        const float pv = fast_exp2(fmaf(sv, cs, -st.l4[r >> 2][r & 3]));
+        sacc[r] = pv;
+        dpacc[r] = pv * (dpacc[r] - st.d4[r >> 2][r & 3]);
+      }
+    };
     f32x16 s0, dp0, s1, dp1;
     bf16x8 pa0[2], ds0[2], pa1[2], ds1[2];
     step_a(0, s0, dp0);
-    step_a(1, s1, dp1);
-    step_b(0, s0, dp0, pa0, ds0);
-    step_c(0, pa0, ds0);
-    step_b(1, s1, dp1, pa1, ds1);
+    // Step A of block 1 woven with step B of block 0, then step C of block 0 woven with
+    // step B of block 1: each two are independent, and one wave per SIMD only overlaps
+    // vector work with matrix products when its instruction stream alternates them. Each
+    // slice is two products and two scores, fenced so that the scheduler keeps the
+    // alternation; the operands of both are loaded before the weave.
+    {
+      bf16x8 qa[DS], da[DS];
+      #pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        qa[s] = TL::read_chunk(qb_lds, 32 + r32, 2 * s + g);
+        da[s] = TL::read_chunk(db_lds, 32 + r32, 2 * s + g);
+      }
+      RowStats st;
+      stats_b(0, s0, st);
+      s1 = zeros16();
+      dp1 = zeros16();
+      __builtin_amdgcn_sched_barrier(0);
+      // DS product pairs spread over the 8 slices
+      #pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        constexpr int EVERY = 8 / DS;
+        if (i % EVERY == 0) {
+          mma(s1, qa[i / EVERY], kf[i / EVERY]);
+          mma(dp1, da[i / EVERY], vf[i / EVERY]);
+        }
+        slice_b(i, st, s0, dp0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      #pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        pack8(pa0[hh], s0, 8 * hh);
+        pack8(ds0[hh], dp0, 8 * hh);
+      }
+    }
+    {
+      bf16x8 dob[2][DB], qbt[2][DB];
+      read_c(0, 0, dob[0], qbt[0]);
+      read_c(0, 1, dob[1], qbt[1]);
+      RowStats st;
+      stats_b(1, s1, st);
+      __builtin_amdgcn_sched_barrier(0);
+      // 2 DB product pairs spread over the 8 slices
+      #pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        constexpr int EVERY = 8 / (2 * DB);
+        if (i % EVERY == 0) {
+          const int j = i / EVERY, hh = j / DB, db = j % DB;
+          mma_acc(dv[db], pa0[hh], dob[hh][db]);
+          mma_acc(dk[db], ds0[hh], qbt[hh][db]);
+        }
+        slice_b(i, st, s1, dp1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      #pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        pack8(pa1[hh], s1, 8 * hh);
+        pack8(ds1[hh], dp1, 8 * hh);
+      }
+    }
     step_c(1, pa1, ds1);
     wait_vm();
     if (more) store_stats(buf ^ 1);
@@ -480,31 +588,41 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
 
   // mask tile map: skip key tiles dead for both 64-row blocks of this workgroup
   const int nrt = (a.Sq + kMaskTile - 1) / kMaskTile;
-  auto live = [&](int k) -> bool {
-    if (!MASK || !a.tiles) return true;
+  // candidate j: key tile split + j q_split
+  auto live = [&](int j) -> bool {
+    const int k = split + j * plan.q_split;
     for (int rt = q0 / kMaskTile; rt <= (q0 + Q_BM - 1) / kMaskTile && rt < nrt; ++rt)
       if (tile_class(a, b, rt, k) != kTileDead) return true;  // Q_BN = kMaskTile: key tile = block
     return false;
   };
-  auto next_live = [&](int k) {
-    while (k < kt_end && !live(k)) k += plan.q_split;
-    return k;
+  __shared__ uint64_t live_lds[kBwdWaves];
+  LiveWords lw{live_lds, -NT};
+  const int ncand = kt_end > split ? (kt_end - split + plan.q_split - 1) / plan.q_split : 0;
+  auto next_live = [&](int j) {  // candidate j -> the first live one from j (ncand: none)
+    if (j >= ncand) return ncand;
+    return MASK && a.tiles ? lw.next(j, ncand, tid, live) : j;
   };
+  auto tile_of = [&](int j) { return j < ncand ? split + j * plan.q_split : kt_end; };
   const int rt_w = qw / kMaskTile;
 
   // per-tile mask state of this wave, fetched one tile ahead: the block class and this
   // lane's row visibility word
-  auto mask_state = [&](int k, int& cls, uint64_t& w) {
-    cls = kTileBias;
+  auto mask_state = [&](int k, ClassAhead& cls, uint64_t& w) {
+    cls = ClassAhead{0u, kSelBias};
     w = ~0ull;
     if (MASK && a.tiles) {
-      cls = rt_w < nrt ? tile_class(a, b, rt_w, k) : kTileDead;
-      if (rt_w < nrt) w = a.rowbits[(int64_t)tile_index(a, b, rt_w, k) * kMaskTile + (row - rt_w * kMaskTile)];
+      cls.sel = kSelDead;
+      if (rt_w < nrt) {
+        const int i = tile_index(a, b, rt_w, k);
+        cls = class_ahead(a, i);
+        w = a.rowbits[(int64_t)i * kMaskTile + (row - rt_w * kMaskTile)];
+      }
     }
   };
 
-  int kt = next_live(split);
-  int cls_cur = kTileBias;
+  int kj = next_live(0);
+  int kt = tile_of(kj);
+  ClassAhead cls_cur{0u, kSelBias};
   uint64_t wb_cur = ~0ull;
   if (kt < kt_end) {
     stage_tile(kt, 0);
@@ -514,14 +632,15 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
   __syncthreads();
   for (int it = 0; kt < kt_end; ++it) {
     const int buf = it & 1;
-    const int ktn = next_live(kt + plan.q_split);
-    int cls_next = kTileBias;
+    const int kjn = next_live(kj + 1);
+    const int ktn = tile_of(kjn);
+    ClassAhead cls_next{0u, kSelBias};
     uint64_t wb_next = ~0ull;
     if (ktn < kt_end) {
       mask_state(ktn, cls_next, wb_next);
       stage_tile(ktn, buf ^ 1);  // lands while this tile is being processed
     }
-    const int cls = cls_cur;
+    const int cls = class_of(cls_cur);
     const bool bias = MASK && cls == kTileBias;  // read mask values
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
     const bf16* kb_lds = k_lds + buf * Q_BN * D;
@@ -615,6 +734,7 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
     wait_vm();
     __syncthreads();
     kt = ktn;
+    kj = kjn;
     cls_cur = cls_next;
     wb_cur = wb_next;
   }

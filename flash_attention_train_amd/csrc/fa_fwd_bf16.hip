@@ -153,15 +153,17 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
   // Per-tile mask state of this wave, fetched one tile ahead (its loads then complete
   // under the end-of-iteration wait instead of stalling the tile): the block class and
   // this lane's row visibility words.
-  auto mask_state = [&](int kt, int& cls, uint64_t (&w)[QB]) {
-    cls = kTileBias;
+  auto mask_state = [&](int kt, ClassAhead& cls, uint64_t (&w)[QB]) {
+    cls = ClassAhead{0u, kSelBias};
     #pragma unroll
     for (int qb = 0; qb < QB; ++qb) w[qb] = ~0ull;
     if (MASK && a.tiles) {
       const int ct = (kt * BN) / kMaskTile;
-      cls = rt_w < nrt ? tile_class(a, b, rt_w, ct) : kTileDead;
+      cls.sel = kSelDead;
       if (rt_w < nrt) {
-        const int64_t base = (int64_t)tile_index(a, b, rt_w, ct) * kMaskTile - rt_w * kMaskTile;
+        const int i = tile_index(a, b, rt_w, ct);
+        cls = class_ahead(a, i);
+        const int64_t base = (int64_t)i * kMaskTile - rt_w * kMaskTile;
         #pragma unroll
         for (int qb = 0; qb < QB; ++qb) w[qb] = a.rowbits[base + qw + 32 * qb + r32];
       }
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
   #pragma unroll
   for (int j = 1; j < KS; ++j) tk[j] = tk[j - 1] < kt_end ? next_live(tk[j - 1] + 1) : kt_end;
   int kt = tk[kh];
-  int cls_cur = kTileBias;
+  ClassAhead cls_cur{0u, kSelBias};
   uint64_t wb_cur[QB];
   #pragma unroll
   for (int qb = 0; qb < QB; ++qb) wb_cur[qb] = ~0ull;
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     for (int j = 1; j < KS; ++j) tn[j] = tn[j - 1] < kt_end ? next_live(tn[j - 1] + 1) : kt_end;
     const int ktn = tn[kh];
     const bool more = ktn < kt_end;
-    int cls_next = kTileBias;
+    ClassAhead cls_next{0u, kSelBias};
     uint64_t wb_next[QB];
     #pragma unroll
     for (int qb = 0; qb < QB; ++qb) wb_next[qb] = ~0ull;
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     }
     const bf16* kb_lds = k_lds[kh][buf];
     const bf16* vb_lds = v_lds[kh][buf];
-    const int cls = kt < kt_end ? cls_cur : kTileDead;  // a key half may sit out the last step
+    const int cls = kt < kt_end ? class_of(cls_cur) : kTileDead;  // a key half may sit out the last step
     if (cls != kTileDead) {
     const bool bias = MASK && cls == kTileBias;  // read mask values
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits

@@ -37,16 +37,36 @@ __device__ __forceinline__ int tile_index(const AttnShape& a, int b, int rt, int
   return b * a.tiles_bstride + rt * a.tiles_ncol + ct;
 }
 // class of mask block (b, row block rt, key block ct); "bias" (read every value) without a
-// map. The index is wave-uniform, so the class is read with a scalar load (through the
-// constant address space, one aligned dword: the class array is 256-byte aligned and
-// padded to a multiple of 256 bytes); scalar loads are tracked apart from the vector
-// memory counter that orders the direct-to-LDS tile loads.
+// map. Read through the constant address space, one aligned dword (the class array is
+// 256-byte aligned and padded to a multiple of 256 bytes): a wave-uniform index becomes a
+// scalar load, tracked apart from the vector memory counter that orders the
+// direct-to-LDS tile loads; a per-lane index becomes a vector load.
 __device__ __forceinline__ int tile_class(const AttnShape& a, int b, int rt, int ct) {
   if (!a.tiles) return kTileBias;
   const int i = tile_index(a, b, rt, ct);
   const auto* w = reinterpret_cast<const __attribute__((address_space(4))) uint32_t*>(
       reinterpret_cast<uintptr_t>(a.tiles) + (uintptr_t)(i & ~3));
   return (int)((*w >> (8 * (i & 3))) & 0xffu);
+}
+
+// A block class fetched ahead of its use by a vector load: every lane loads one byte of
+// the 64-block window holding block i (inside the class array's 256-byte padding), and
+// class_of() takes lane i % 64's byte, wave-uniform, after the walk's wait for its tile
+// loads. (A scalar load shares its counter with the LDS reads and completes out of
+// order, so every LDS wait until it landed would have to wait for it as well.)
+constexpr int kSelDead = -1, kSelBias = -2;
+struct ClassAhead {
+  uint32_t win;
+  int sel;  // i % 64, or kSelDead / kSelBias
+};
+__device__ __forceinline__ ClassAhead class_ahead(const AttnShape& a, int i) {
+  const auto* t = reinterpret_cast<const __attribute__((address_space(1))) uint8_t*>(reinterpret_cast<uintptr_t>(a.tiles));
+  return ClassAhead{t[(i & ~63) + (int)(threadIdx.x & 63)], i & 63};
+}
+__device__ __forceinline__ int class_of(const ClassAhead& c) {
+  if (c.sel == kSelBias) return kTileBias;
+  if (c.sel == kSelDead) return kTileDead;
+  return __builtin_amdgcn_readlane((int)c.win, c.sel);
 }
 
 // bf16 backward decomposition: waves per workgroup (one wave per SIMD: 1024 / kBwdWaves
