@@ -115,6 +115,54 @@ __device__ __forceinline__ bool any_bias_block(const AttnShape& a, int b, int rb
 // ---------------------------------------------------------------------------
 // dK / dV workgroup
 // ---------------------------------------------------------------------------
+// Store a wave's 32 x D fp32 accumulator block (lane (column 32 db + r32, half g),
+// register r -> row 8 (r/4) + 4 g + r%4) through LDS: staged row-major, with the 32-column
+// halves of every second group of 4 rows swapped so that the two lane halves of a write
+// hit different banks, then read back as 16-byte row chunks and handed to
+// sink.put(row, column, 4 values). One 16-byte store per chunk replaces one 2- or 4-byte
+// store per element. `stage` is this wave's 32 x D floats of LDS, idle around the call;
+// the wave reads back only what it wrote itself, in order.
+template <int D, class Sink>
+__device__ __forceinline__ void store_block(const f32x16 (&acc)[D / 32], float mul, float* stage, int lane,
+                                            const Sink& sink) {
+  const int g = lane >> 5, r32 = lane & 31;
+  #pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    #pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * g + (r & 3);
+      stage[row * D + ((32 * db + r32) ^ (((row >> 2) & 1) << 5))] = acc[db][r] * mul;
+    }
+  }
+  constexpr int CH = D / 4;  // 16-byte chunks per row
+  #pragma unroll
+  for (int i = 0; i < 32 * CH / 64; ++i) {
+    const int e = 64 * i + lane, row = e / CH, col = 4 * (e % CH);
+    sink.put(row, col, *reinterpret_cast<const f32x4*>(stage + row * D + (col ^ (((row >> 2) & 1) << 5))));
+  }
+}
+
+// Destination of a wave's 32-row result block: row 0's address and the row pitch in
+// bytes, the rows that exist, and the element kind: bf16 (stored), fp32 (stored, a
+// partial slice) or fp32 added to (an accumulator). Built once before the stores, so
+// that a chunk's store is an address add and a store.
+struct RowSink {
+  char* base;
+  int64_t pitch;
+  int rows;
+  int kind;  // 0 bf16, 1 fp32 store, 2 fp32 add
+  __device__ __forceinline__ void put(int row, int col, const f32x4& v) const {
+    if (row >= rows) return;
+    char* p = base + row * pitch;
+    if (kind == 0) {
+      *reinterpret_cast<bf16x4*>(p + 2 * col) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+    } else {
+      f32x4* q = reinterpret_cast<f32x4*>(p + 4 * col);
+      *q = kind == 2 ? *q + v : v;
+    }
+  }
+};
+
 // The live candidates of a walk (candidate j = 0 .. n - 1), NT at a time as bit words in
 // LDS: every thread tests one candidate, so that no step of the walk waits on a class
 // load. The walk is workgroup-uniform, and every call is made by the whole workgroup at
@@ -176,10 +224,6 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
       zero(vf[s]);
     }
   }
-  // the K / V operand fragments live in accumulation registers for the whole walk (matrix
-  // instructions read their A / B operands from there), leaving the vector file to the pairs
-  #pragma unroll
-  for (int s = 0; s < DS; ++s) asm volatile("" : "+a"(kf[s]), "+a"(vf[s]));
   f32x16 dk[DB], dv[DB];
   #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -294,6 +338,11 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     stage_pair(cur, 0);
     mask_state(cur, cls_cur, wb_cur);
   }
+  // The K / V operand fragments live in accumulation registers for the whole walk (matrix
+  // instructions read their A / B operands from there), leaving the vector file to the
+  // pairs. Moved there only now, so that their loads and the first pair's land together.
+  #pragma unroll
+  for (int s = 0; s < DS; ++s) asm volatile("" : "+a"(kf[s]), "+a"(vf[s]));
   wait_vm();  // on every path: the K / V fragments are complete before the walk
   if (cur.p < npairs) store_stats(0);
   __syncthreads();
@@ -490,35 +539,26 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
 
   settle_acc(dk);
   settle_acc(dv);
-  // results: accumulator row = key 8 (r/4) + 4 g + r%4 of this wave, column d = 32 db + r32.
   // Split walks store their partial sums (unscaled) into their own fp32 slice, which a
-  // reduce pass sums; a workgroup with no live pair still stores its zeros.
+  // reduce pass sums; a workgroup with no live pair still stores its zeros. The pair
+  // buffers stage the results once every wave has left the walk.
   const bool part = plan.kv_split > 1;
-  const int64_t part_off = (int64_t)split * a.B * a.Hkv * a.Sk * D;
-  #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kk = n0 + 32 * wave + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (kk >= a.Sk) continue;
-      const int d = 32 * db + r32;
-      if (part) {
-        const int64_t o = part_off + (((int64_t)b * a.Hkv + hk) * a.Sk + kk) * D + d;
-        plan.dk_part[o] = dk[db][r];
-        plan.dv_part[o] = dv[db][r];
-      } else if (args.accumulate) {
-        float* pk = static_cast<float*>(args.dk) + b * args.sdk.b + hk * args.sdk.h + (int64_t)kk * args.sdk.s + d;
-        float* pv = static_cast<float*>(args.dv) + b * args.sdv.b + hk * args.sdv.h + (int64_t)kk * args.sdv.s + d;
-        *pk += dk[db][r] * a.scale;
-        *pv += dv[db][r];
-      } else {
-        bf16* pk = static_cast<bf16*>(args.dk) + b * args.sdk.b + hk * args.sdk.h + (int64_t)kk * args.sdk.s + d;
-        bf16* pv = static_cast<bf16*>(args.dv) + b * args.sdv.b + hk * args.sdv.h + (int64_t)kk * args.sdv.s + d;
-        *pk = (bf16)(dk[db][r] * a.scale);
-        *pv = (bf16)dv[db][r];
-      }
-    }
-  }
+  const int kbase = n0 + 32 * wave;
+  const int rows = max(0, min(32, a.Sk - kbase));
+  auto sink = [&](float* part_base, void* out, const Strides& so) {
+    if (part)
+      return RowSink{reinterpret_cast<char*>(part_base + (int64_t)split * a.B * a.Hkv * a.Sk * D +
+                                             (((int64_t)b * a.Hkv + hk) * a.Sk + kbase) * D),
+                     (int64_t)D * 4, rows, 1};
+    const int64_t esz = args.accumulate ? 4 : 2;
+    return RowSink{static_cast<char*>(out) + (b * so.b + hk * so.h + (int64_t)kbase * so.s) * esz, so.s * esz, rows,
+                   args.accumulate ? 2 : 0};
+  };
+  const RowSink sk = sink(plan.dk_part, args.dk, args.sdk), sv = sink(plan.dv_part, args.dv, args.sdv);
+  float* stage = reinterpret_cast<float*>(smem) + wave * 32 * D;
+  __syncthreads();
+  store_block<D>(dk, part ? 1.f : a.scale, stage, lane, sk);
+  store_block<D>(dv, 1.f, stage, lane, sv);
 }
 
 // ---------------------------------------------------------------------------
@@ -740,23 +780,20 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
   }
 
   settle_acc(dq);
-  // dQ accumulator: lane (d = 32 db + r32, half g), register r -> row 8 (r/4) + 4 g + r%4 of the wave
-  #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qi = qw + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (qi >= a.Sq) continue;
-      const int d = 32 * db + r32;
-      if (plan.q_split > 1) {  // this split's fp32 slice, summed by a reduce pass
-        plan.dq_part[(int64_t)split * a.B * a.Hq * a.Sq * D + (((int64_t)b * a.Hq + h) * a.Sq + qi) * D + d] =
-            dq[db][r];
-      } else {
-        bf16* pq = static_cast<bf16*>(plan.dq) + b * plan.sdq.b + h * plan.sdq.h + (int64_t)qi * plan.sdq.s + d;
-        *pq = (bf16)(dq[db][r] * a.scale);
-      }
-    }
-  }
+  // split walks store this split's fp32 slice (unscaled), summed by a reduce pass; the
+  // tile buffers stage the results once every wave has left the walk
+  const int rows = max(0, min(32, a.Sq - qw));
+  const RowSink sq =
+      plan.q_split > 1
+          ? RowSink{reinterpret_cast<char*>(plan.dq_part + (int64_t)split * a.B * a.Hq * a.Sq * D +
+                                            (((int64_t)b * a.Hq + h) * a.Sq + qw) * D),
+                    (int64_t)D * 4, rows, 1}
+          : RowSink{reinterpret_cast<char*>(static_cast<bf16*>(plan.dq) + b * plan.sdq.b + h * plan.sdq.h +
+                                            (int64_t)qw * plan.sdq.s),
+                    plan.sdq.s * 2, rows, 0};
+  float* stage = reinterpret_cast<float*>(smem) + wave * 32 * D;
+  __syncthreads();
+  store_block<D>(dq, plan.q_split > 1 ? 1.f : a.scale, stage, lane, sq);
 }
 
 // Units whose mask blocks carry additive values run a body compiled with the
