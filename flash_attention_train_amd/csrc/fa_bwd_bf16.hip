@@ -134,12 +134,18 @@ __device__ __forceinline__ void store_block(const f32x16 (&acc)[D / 32], float m
       stage[row * D + ((32 * db + r32) ^ (((row >> 2) & 1) << 5))] = acc[db][r] * mul;
     }
   }
-  constexpr int CH = D / 4;  // 16-byte chunks per row
+  // all chunks are read back before any is stored (the stores skip rows past the end,
+  // and a read under that branch would wait on its own)
+  constexpr int CH = D / 4, N = 32 * CH / 64;  // 16-byte chunks per row, per lane
+  const int r0 = lane / CH, col = 4 * (lane % CH);
+  f32x4 v[N];
   #pragma unroll
-  for (int i = 0; i < 32 * CH / 64; ++i) {
-    const int e = 64 * i + lane, row = e / CH, col = 4 * (e % CH);
-    sink.put(row, col, *reinterpret_cast<const f32x4*>(stage + row * D + (col ^ (((row >> 2) & 1) << 5))));
+  for (int i = 0; i < N; ++i) {
+    const int row = r0 + i * (64 / CH);
+    v[i] = *reinterpret_cast<const f32x4*>(stage + row * D + (col ^ (((row >> 2) & 1) << 5)));
   }
+  #pragma unroll
+  for (int i = 0; i < N; ++i) sink.put(r0 + i * (64 / CH), col, v[i]);
 }
 
 // Destination of a wave's 32-row result block: row 0's address and the row pitch in
@@ -213,16 +219,14 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
 
   const bf16* K = static_cast<const bf16*>(args.k) + b * args.sk.b + hk * args.sk.h;
   const bf16* V = static_cast<const bf16*>(args.v) + b * args.sv.b + hk * args.sv.h;
+  // (keys past the end read the last key: their scores are hidden on the tail tile and
+  // their rows are never stored; a zeroing branch would make the loads wait here)
+  const int64_t key_c = min(key, a.Sk - 1);
   bf16x8 kf[DS], vf[DS];
   #pragma unroll
   for (int s = 0; s < DS; ++s) {
-    if (key < a.Sk) {
-      kf[s] = *reinterpret_cast<const bf16x8*>(K + (int64_t)key * args.sk.s + 16 * s + 8 * g);
-      vf[s] = *reinterpret_cast<const bf16x8*>(V + (int64_t)key * args.sv.s + 16 * s + 8 * g);
-    } else {
-      zero(kf[s]);
-      zero(vf[s]);
-    }
+    kf[s] = *reinterpret_cast<const bf16x8*>(K + key_c * args.sk.s + 16 * s + 8 * g);
+    vf[s] = *reinterpret_cast<const bf16x8*>(V + key_c * args.sv.s + 16 * s + 8 * g);
   }
   f32x16 dk[DB], dv[DB];
   #pragma unroll
@@ -587,22 +591,17 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
   const bf16* dO = static_cast<const bf16*>(args.dout) + b * args.sdo.b + h * args.sdo.h;
   const bf16* K = static_cast<const bf16*>(args.k) + b * args.sk.b + hk * args.sk.h;
   const bf16* V = static_cast<const bf16*>(args.v) + b * args.sv.b + hk * args.sv.h;
+  // (rows past the end read the last row: their scores are hidden on the tail tile and
+  // their dQ rows are never stored; a zeroing branch would make the loads wait here)
+  const int64_t row_c = min(row, a.Sq - 1);
   bf16x8 qf[DS], df[DS];
   #pragma unroll
   for (int s = 0; s < DS; ++s) {
-    if (row < a.Sq) {
-      qf[s] = *reinterpret_cast<const bf16x8*>(Q + (int64_t)row * args.sq.s + 16 * s + 8 * g);
-      df[s] = *reinterpret_cast<const bf16x8*>(dO + (int64_t)row * args.sdo.s + 16 * s + 8 * g);
-    } else {
-      zero(qf[s]);
-      zero(df[s]);
-    }
+    qf[s] = *reinterpret_cast<const bf16x8*>(Q + row_c * args.sq.s + 16 * s + 8 * g);
+    df[s] = *reinterpret_cast<const bf16x8*>(dO + row_c * args.sdo.s + 16 * s + 8 * g);
   }
-  float lse2 = 0.f, dlt = 0.f;
-  if (row < a.Sq) {
-    lse2 = args.lse[b * args.lse_sb + h * args.lse_sh + row] * kLog2e;
-    dlt = args.delta[b * args.delta_sb + h * args.delta_sh + row];
-  }
+  const float lse2 = args.lse[b * args.lse_sb + h * args.lse_sh + row_c] * kLog2e;
+  const float dlt = args.delta[b * args.delta_sb + h * args.delta_sh + row_c];
 
   f32x16 dq[DB];
   #pragma unroll

@@ -78,14 +78,12 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
   bf16x8 qf[QB][DS];
   #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int row = qw + 32 * qb + r32;
+    // (rows past the end read the last row and are never stored; a zeroing branch would
+    // make the loads wait here)
+    const int64_t row_c = min(qw + 32 * qb + r32, a.Sq - 1);
     #pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      if (row < a.Sq)
-        qf[qb][s] = *reinterpret_cast<const bf16x8*>(Q + (int64_t)row * args.sq.s + 16 * s + 8 * g);
-      else
-        zero(qf[qb][s]);
-    }
+    for (int s = 0; s < DS; ++s)
+      qf[qb][s] = *reinterpret_cast<const bf16x8*>(Q + row_c * args.sq.s + 16 * s + 8 * g);
   }
 
   f32x16 oacc[QB][DB];
