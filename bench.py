@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--extra", default="lm_causal,dit_ca")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--splits", default="tune",
+                    help="backward split: 'tune' (time a few settings once at setup, untimed), 'model' (the "
+                         "library's cost model) or KVxQ (e.g. 2x1)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference kernel that "
                          "scales the HBM byte counters) and exit")
@@ -48,7 +51,7 @@ def parse():
 class Workload:
     """Device buffers and the three calls of one step for a seeded case."""
 
-    def __init__(self, key: str):
+    def __init__(self, key: str, splits: str = "tune"):
         import torch
 
         from flash_attention_train_amd import accounting, binding, configs
@@ -71,14 +74,28 @@ class Workload:
         self.dq = torch.empty_like(self.q)
         self.dk = torch.empty_like(self.k)
         self.dv = torch.empty_like(self.v)
-        nws = binding.bwd_workspace_bytes(self.q, self.k, scale=c.scale, causal=c.causal, q_offset=c.q_offset,
-                                          mask=self.mask)
-        self.ws_bytes = nws
-        self.ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
         self.B = binding
         self.tiles = None
         if self.mask is not None:
             self.tiles = binding.mask_tile_map(self.mask, self.q, self.k)  # sized once, refilled every step
+        # backward split: the library's cost model, or (tune) the fastest of a few
+        # settings timed once here on this workload, outside every timed region
+        self.kv_split = self.q_split = 0
+        self.splits_from = "library cost model"
+        if "x" in splits:
+            self.kv_split, self.q_split = (int(x) for x in splits.split("x"))
+            self.splits_from = "given"
+        elif splits == "tune":
+            self.splits_from = "tuned once at setup"
+            self.fwd()
+            self.pre()
+            self.kv_split, self.q_split = binding.tune_bwd_splits(
+                self.q, self.k, self.v, self.do, self.lse, self.delta, mask=self.mask, scale=c.scale,
+                causal=c.causal, q_offset=c.q_offset, mask_tiles=self.tiles)
+        nws = binding.bwd_workspace_bytes(self.q, self.k, scale=c.scale, causal=c.causal, q_offset=c.q_offset,
+                                          mask=self.mask, kv_split=self.kv_split, q_split=self.q_split)
+        self.ws_bytes = nws
+        self.ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
 
     def classify(self):
         """The mask tile map (dead / open / mixed 64 x 64 blocks), part of every step
@@ -98,7 +115,7 @@ class Workload:
         c = self.case
         self.B.bwd(self.q, self.k, self.v, self.do, self.lse, self.delta, mask=self.mask, scale=c.scale,
                    causal=c.causal, q_offset=c.q_offset, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws,
-                   mask_tiles=self.tiles)
+                   kv_split=self.kv_split, q_split=self.q_split, mask_tiles=self.tiles)
 
     def step(self):
         self.classify()
@@ -175,6 +192,8 @@ def time_workload(w: Workload, steps: int, warmup: int, graph: bool = True) -> d
         "fwdbwd_event_tflops": total_flops / ((fwd_ms + pre_ms + bwd_ms).mean() * 1e-3) / 1e12,
         "pre_gbs": w.pre_bytes / (pre_ms.mean() * 1e-3) / 1e9,
         "pairs": w.pairs,
+        "bwd_splits": [w.kv_split, w.q_split],
+        "bwd_splits_from": w.splits_from,
         "gflop_per_step": total_flops / 1e9,
     }
 
@@ -268,13 +287,13 @@ def main():
         return
 
     log(f"[bench] device {torch.cuda.get_device_name(0)}; workload {args.workload}")
-    w = Workload(args.workload)
+    w = Workload(args.workload, args.splits)
     r = time_workload(w, args.steps, args.warmup, graph=not args.eager)
     log(f"[bench] {args.workload}: {r['ms_per_step']:.3f} ms/step, {r['tflops']:.1f} TFLOP/s")
 
     extra = {}
     for key in [k for k in args.extra.split(",") if k and k not in (args.workload, "none")]:
-        we = Workload(key)
+        we = Workload(key, args.splits if "x" not in args.splits else "tune")
         re_ = time_workload(we, max(5, args.steps // 2), args.warmup, graph=not args.eager)
         re_["pct_of_peak"] = 100.0 * re_["tflops"] / accounting.MI355X_BF16_DENSE_TFLOPS
         extra[key] = re_

@@ -222,6 +222,42 @@ def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_off
     return dq, dk, dv
 
 
+BWD_SPLIT_CANDIDATES = ((0, 0), (1, 1), (2, 1), (4, 1), (8, 1), (1, 2), (2, 2), (4, 2))
+
+
+def tune_bwd_splits(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_offset=None,
+                    mask_tiles=None, candidates=BWD_SPLIT_CANDIDATES, reps=5, rounds=3, stream=None):
+    """Times the backward on these inputs for each (kv_split, q_split) candidate ((0, 0):
+    the library's own choice) and returns the fastest pair: `rounds` passes over the
+    candidates, interleaved, each candidate keeping its best pass of `reps` calls. The
+    library chooses with a cost model that sees the shape but not the mask's content (key
+    padding makes many key tiles dead), so a caller that runs one shape many times can
+    tune once and pass the result to bwd(). Outputs go to scratch buffers; every pass
+    synchronizes."""
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    need = max(bwd_workspace_bytes(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv,
+                                   q_split=qs) for kv, qs in candidates)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    best = {}
+    for _ in range(rounds):
+        for kv, qs in candidates:
+            def call():
+                bwd(q, k, v, dout, lse, delta, mask=mask, scale=scale, causal=causal, q_offset=q_offset, dq=dq,
+                    dk=dk, dv=dv, workspace=ws, stream=s, kv_split=kv, q_split=qs, mask_tiles=mask_tiles)
+            call()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for _ in range(reps):
+                call()
+            e1.record(s)
+            e1.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            best[(kv, qs)] = min(ms, best.get((kv, qs), ms))
+    return min(best, key=best.get)
+
+
 def bwd_chunked(q, k, v, dout, lse, delta, dk_acc, dv_acc, *, mask=None, scale=None, causal=True, q_offset=None,
                 dq=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None):
     """Chunked backward: returns dQ for the chunk; ADDS dK/dV into the fp32 window

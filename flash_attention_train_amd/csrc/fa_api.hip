@@ -163,10 +163,11 @@ size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 // the compute units the way the dispatcher fills whichever frees first; split
 // choices add the reduce pass over their fp32 slices.
 double predict_bwd_us(const fa_attn_params* p, int kv, int q) {
-  // measured on MI355X with both workgroup kinds running side by side
+  // fitted to MI355X timings of the three bf16 workloads over the split grid
   constexpr double kPairUs = 2.7;         // one 64-row x 128-key dK/dV step
-  constexpr double kTileUs = 2.2;         // one 128-row x 64-key dQ step
-  constexpr double kPassUs = 2.0;         // one more kernel on the stream
+  constexpr double kTileUs = 1.8;         // one 128-row x 64-key dQ step
+  constexpr double kKvUnitUs = 8.0;       // a dK/dV workgroup's first loads and its stores
+  constexpr double kPassUs = 4.0;         // one more kernel on the stream
   constexpr double kBytesPerUs = 5.0e6;   // streaming rate of the reduce pass
   const int U = fa::kBwdUnit, slots = 1024 / fa::kBwdWaves;
   const int64_t nkt = (p->Sk + U - 1) / U, nqt = (p->Sq + U - 1) / U;
@@ -188,7 +189,7 @@ double predict_bwd_us(const fa_attn_params* p, int kv, int q) {
       qt0 = first_row <= 0 ? 0 : std::min<int64_t>(first_row / 64, nr64);
     }
     const int64_t pairs = G * (nr64 - qt0);
-    const double cost = kPairUs * (double)((pairs + kv - 1) / kv);
+    const double cost = kKvUnitUs + kPairUs * (double)((pairs + kv - 1) / kv);
     for (int64_t u = 0; u < (int64_t)p->B * p->Hkv * kv; ++u) place(cost);
   }
   for (int64_t qt = nqt - 1; qt >= 0; --qt) {

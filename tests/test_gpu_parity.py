@@ -170,7 +170,8 @@ def test_forward_variants(name, config):
 @pytest.mark.parametrize("kv_split,q_split", [(1, 1), (3, 1), (1, 2), (2, 5)])
 @pytest.mark.parametrize("name", ["dit_sa_ragged", "lm_causal_gqa4", "random_bias_bcast", "d64_bf16"])
 def test_backward_decompositions(name, kv_split, q_split):
-    """Every split of the bf16 backward's work (direct stores or fp32 atomics) gives the oracle's gradients."""
+    """Every split of the bf16 backward's work (direct stores, or fp32 partial slices summed by a reduce
+    pass) gives the oracle's gradients."""
     c = CASES[name]()
     t = upload(c)
     o, lse = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
@@ -181,6 +182,25 @@ def test_backward_decompositions(name, kv_split, q_split):
     torch.cuda.synchronize()
     ref = oracle_full(c)
     compare_full(c, {"dQ": host64(dq), "dK": host64(dk), "dV": host64(dv)}, ref, names=("dQ", "dK", "dV"))
+
+
+def test_tuned_split_is_a_candidate_and_exact():
+    """The split tuner returns one of its candidates, and the backward run with that split (and the mask
+    tile map) gives the oracle's gradients."""
+    c = CASES["dit_ca_ragged"]()
+    t = upload(c)
+    tiles = binding.mask_tile_map(t["mask"], t["q"], t["k"])
+    o, lse = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
+                         q_offset=c.q_offset, mask_tiles=tiles)
+    delta = binding.bwd_preprocess(o, t["do"])
+    kv, qs = binding.tune_bwd_splits(t["q"], t["k"], t["v"], t["do"], lse, delta, mask=t["mask"], scale=c.scale,
+                                     causal=c.causal, q_offset=c.q_offset, mask_tiles=tiles, reps=2)
+    assert (kv, qs) in binding.BWD_SPLIT_CANDIDATES
+    say(f"    tuned split kv {kv} q {qs}")
+    dq, dk, dv = binding.bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, mask=t["mask"], scale=c.scale,
+                             causal=c.causal, q_offset=c.q_offset, kv_split=kv, q_split=qs, mask_tiles=tiles)
+    torch.cuda.synchronize()
+    compare_full(c, {"dQ": host64(dq), "dK": host64(dk), "dV": host64(dv)}, oracle_full(c), names=("dQ", "dK", "dV"))
 
 
 @pytest.mark.parametrize("kv_split,q_split", [(1, 1), (2, 3)])
