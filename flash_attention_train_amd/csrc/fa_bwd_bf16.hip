@@ -51,22 +51,6 @@ __device__ __forceinline__ f32x16 zeros16() {
   return z;
 }
 
-// acc += a b with the accumulator in AGPRs (the dK/dV and dQ sums live there for the
-// whole walk, which leaves the arch VGPRs to the operands in flight). The s_nop gives
-// the two wait states a VALU write of a source operand needs before a matrix product.
-__device__ __forceinline__ void mma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
-// the last products into AGPR accumulators must have written them before VALU reads
-// them (the matrix core's result latency, with margin)
-template <int N>
-__device__ __forceinline__ void settle_acc(f32x16 (&acc)[N]) {
-  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
-  #pragma unroll
-  for (int i = 0; i < N; ++i) asm volatile("" : "+a"(acc[i]));
-}
-
 
 // unit -> (key tile, batch, kv head, split); key tiles vary slowest so that the long
 // causal tiles (small key index) are dispatched first

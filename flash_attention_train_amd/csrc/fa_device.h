@@ -52,6 +52,20 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ void mma(f32x16& c, const bf16x8& a, const bf16x8& b) {
   c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// acc += a b with the accumulator in AGPRs (sums that live there for a whole walk, which
+// leaves the arch VGPRs to the operands in flight). The s_nop gives the two wait states
+// a VALU write of a source operand needs before a matrix product.
+__device__ __forceinline__ void mma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// the last products into AGPR accumulators must have written them before VALU reads
+// them (the matrix core's result latency, with margin)
+template <int N>
+__device__ __forceinline__ void settle_acc(f32x16 (&acc)[N]) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+  #pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+a"(acc[i]));
+}
 __device__ __forceinline__ void mma(f32x16& c, const f32x8& a, const f32x8& b) {
   c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[0], b.lo[0], c, 0, 0, 0);
   c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[1], b.lo[1], c, 0, 0, 0);

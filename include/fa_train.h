@@ -104,11 +104,14 @@ typedef struct fa_attn_params {
                              0 are not read. */
     /* Work decomposition hints, 0 = automatic (the normal setting; other values are
      * for tuning and give the same results up to fp32 summation order): */
-    int32_t fwd_variant;  /* bf16 forward: 1 = 32 query rows per wave, 2 = 64 rows */
+    int32_t fwd_variant;  /* bf16 forward: 1 = 32 query rows per wave, 64-key tiles;
+                             2 = 64 rows per wave, 32-key tiles; 3 = keys split over two
+                             halves of the workgroup, merged at the end */
     int32_t kv_split;     /* bf16 backward: workgroups sharing one 128-key tile's dK/dV
-                             walk, 1 .. 64 (> 1 adds partial sums with fp32 atomics) */
+                             walk, 1 .. 64 (> 1: each writes an fp32 partial slice in the
+                             workspace, summed by a reduce pass) */
     int32_t q_split;      /* bf16 backward: workgroups sharing one 128-row query tile's dQ
-                             walk, 1 .. 64 (> 1 adds partial sums with fp32 atomics) */
+                             walk, 1 .. 64 (> 1: fp32 partial slices, as for kv_split) */
 } fa_attn_params;
 
 /* Forward: writes O (dtype) and LSE (fp32, natural log). Fully masked rows get
