@@ -39,9 +39,9 @@ def parse():
     ap.add_argument("--extra", default="lm_causal,dit_ca")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
-    ap.add_argument("--splits", default="tune",
-                    help="backward split: 'tune' (time a few settings once at setup, untimed), 'model' (the "
-                         "library's cost model) or KVxQ (e.g. 2x1)")
+    ap.add_argument("--splits", default="table",
+                    help="backward split: 'table' (the workload's measured setting), 'tune' (time a few settings "
+                         "once at setup, untimed), 'model' (the library's cost model) or KVxQ (e.g. 2x1)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference kernel that "
                          "scales the HBM byte counters) and exit")
@@ -51,7 +51,7 @@ def parse():
 class Workload:
     """Device buffers and the three calls of one step for a seeded case."""
 
-    def __init__(self, key: str, splits: str = "tune"):
+    def __init__(self, key: str, splits: str = "table"):
         import torch
 
         from flash_attention_train_amd import accounting, binding, configs
@@ -82,7 +82,10 @@ class Workload:
         # settings timed once here on this workload, outside every timed region
         self.kv_split = self.q_split = 0
         self.splits_from = "library cost model"
-        if "x" in splits:
+        if splits == "table" and configs.WORKLOADS[key].bwd_splits:
+            self.kv_split, self.q_split = configs.WORKLOADS[key].bwd_splits
+            self.splits_from = "workload table"
+        elif "x" in splits:
             self.kv_split, self.q_split = (int(x) for x in splits.split("x"))
             self.splits_from = "given"
         elif splits == "tune":
@@ -212,9 +215,9 @@ def source_digest(paths=KERNEL_SOURCES) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the backward kernel from the committed counter summary,
-    or None when there is none for this workload or the kernel source changed since."""
+def measured_traffic(workload: str, splits):
+    """HBM bytes per backward call from the committed counter summary, or None when
+    there is none for this workload and split, or the kernel source changed since."""
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic_bwd.json")
     try:
         with open(path) as f:
@@ -222,7 +225,7 @@ def measured_traffic(workload: str):
     except (OSError, ValueError):
         return None
     entry = rec.get("workloads", {}).get(workload)
-    if not entry or rec.get("source_sha256") != source_digest():
+    if not entry or rec.get("source_sha256") != source_digest() or entry.get("bwd_splits") != list(splits):
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -293,7 +296,7 @@ def main():
 
     extra = {}
     for key in [k for k in args.extra.split(",") if k and k not in (args.workload, "none")]:
-        we = Workload(key, args.splits if "x" not in args.splits else "tune")
+        we = Workload(key, args.splits if "x" not in args.splits else "table")
         re_ = time_workload(we, max(5, args.steps // 2), args.warmup, graph=not args.eager)
         re_["pct_of_peak"] = 100.0 * re_["tflops"] / accounting.MI355X_BF16_DENSE_TFLOPS
         extra[key] = re_
@@ -325,7 +328,8 @@ def main():
         "roofline": {"kernel": "bwd_bf16_kernel (fa_train_bwd)" if single else
                      "fa_train_bwd (bwd_bf16_kernel + reduce_parts_kernel)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": measured_traffic(args.workload),
+                     "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(args.workload, [w.kv_split, w.q_split]),
                      "flop_per_launch": w.bwd_flops, "launch_ms": round(r["bwd_ms_mean"], 5)},
         "breakdown": {k: round(v, 4) if isinstance(v, float) else v for k, v in r.items()},
         "extra": extra,

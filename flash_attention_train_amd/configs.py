@@ -20,13 +20,18 @@ class Workload:
     key: str
     title: str
     index: int
+    # the bf16 backward's (kv_split, q_split) for this workload: the fastest or within
+    # noise of the fastest on MI355X over kv in {1, 2, 4} x q in {1, 2, 4}; None: the
+    # library's cost model
+    bwd_splits: tuple | None = None
 
 
 WORKLOADS = {
     "tiny": Workload("tiny", "tiny parity case, fp32, B=1 H=2 S=64 D=64", 1),
-    "dit_sa": Workload("dit_sa", "DiT self-attention, B=1 Hq=16 Hkv=8 S=1542 D=128 bf16, pad mask", 2),
-    "dit_ca": Workload("dit_ca", "DiT cross-attention, B=2 H=16 Sq=1542 Sk=512 D=128 bf16, key-pad mask", 3),
-    "lm_causal": Workload("lm_causal", "LM causal GQA, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 4),
+    "dit_sa": Workload("dit_sa", "DiT self-attention, B=1 Hq=16 Hkv=8 S=1542 D=128 bf16, pad mask", 2, (2, 1)),
+    "dit_ca": Workload("dit_ca", "DiT cross-attention, B=2 H=16 Sq=1542 Sk=512 D=128 bf16, key-pad mask", 3,
+                       (2, 1)),
+    "lm_causal": Workload("lm_causal", "LM causal GQA, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 4, (2, 1)),
     "long_window": Workload("long_window",
                             "long-window chunked walk, W=32768, 64 chunks of 512, Hq=16 Hkv=4 D=128 bf16", 5),
 }
