@@ -36,7 +36,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dit_sa")
-    ap.add_argument("--extra", default="lm_causal,dit_ca")
+    ap.add_argument("--extra", default="lm_causal,dit_ca,long_window",
+                    help="other workloads to time, comma separated ('none' for none); long_window is the "
+                         "64-chunk walk over a 32768-long window")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--splits", default="table",
@@ -78,6 +80,11 @@ class Workload:
         self.tiles = None
         if self.mask is not None:
             self.tiles = binding.mask_tile_map(self.mask, self.q, self.k)  # sized once, refilled every step
+        # forward workspace: the split-key walk's partial rows when the grid is short
+        self.fws_bytes = binding.fwd_workspace_bytes(self.q, self.k, scale=c.scale, causal=c.causal,
+                                                     q_offset=c.q_offset, mask=self.mask)
+        self.fws = torch.empty(max(self.fws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.fwd_split = self.fws_bytes // (4 * c.B * c.Hq * c.Sq * (c.D + 2)) if self.fws_bytes else 1
         # backward split: the library's cost model, or (tune) the fastest of a few
         # settings timed once here on this workload, outside every timed region
         self.kv_split = self.q_split = 0
@@ -109,7 +116,7 @@ class Workload:
     def fwd(self):
         c = self.case
         self.B.fwd(self.q, self.k, self.v, mask=self.mask, scale=c.scale, causal=c.causal, q_offset=c.q_offset,
-                   out=self.o, lse=self.lse, mask_tiles=self.tiles)
+                   out=self.o, lse=self.lse, mask_tiles=self.tiles, workspace=self.fws)
 
     def pre(self):
         self.B.bwd_preprocess(self.o, self.do, delta=self.delta)
@@ -195,10 +202,77 @@ def time_workload(w: Workload, steps: int, warmup: int, graph: bool = True) -> d
         "fwdbwd_event_tflops": total_flops / ((fwd_ms + pre_ms + bwd_ms).mean() * 1e-3) / 1e12,
         "pre_gbs": w.pre_bytes / (pre_ms.mean() * 1e-3) / 1e9,
         "pairs": w.pairs,
+        "fwd_split": w.fwd_split,
         "bwd_splits": [w.kv_split, w.q_split],
         "bwd_splits_from": w.splits_from,
         "gflop_per_step": total_flops / 1e9,
     }
+
+
+def time_long_window(steps: int, warmup: int) -> dict:
+    """The long-window exact walk at full size: 64 query chunks of 512 rows over a
+    32768-long cached K/V window, each chunk forward -> preprocess -> chunked backward
+    (dK/dV added into fp32 window accumulators, zeroed at the start of the walk). The
+    whole walk (192 launches) is captured in one HIP graph and replayed; FLOPs are the
+    walk's exact causal pairs, which equal the one-shot causal run's."""
+    import torch
+
+    from flash_attention_train_amd import accounting, binding, configs
+    W, C = configs.LONG_WINDOW, configs.LONG_CHUNK
+    c = configs.make("long_window")
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+    q, k, v, do = up(c.q), up(c.k), up(c.v), up(c.do)
+    dk_acc = torch.zeros((1, c.Hkv, W, c.D), dtype=torch.float32, device="cuda")
+    dv_acc = torch.zeros_like(dk_acc)
+    O, dQ = torch.empty_like(q), torch.empty_like(q)
+    LSE = torch.empty((1, c.Hq, W), dtype=torch.float32, device="cuda")
+    Delta = torch.empty_like(LSE)
+    plan = configs.chunk_plan(W, C)
+    need = max(binding.bwd_workspace_bytes(q[:, :, p0:p0 + n], k[:, :, :sk], scale=c.scale, causal=True,
+                                           q_offset=p0) for p0, n, sk in plan)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    fneed = max(binding.fwd_workspace_bytes(q[:, :, p0:p0 + n], k[:, :, :sk], scale=c.scale, causal=True,
+                                            q_offset=p0) for p0, n, sk in plan)
+    fws = torch.empty(max(fneed, 256), dtype=torch.uint8, device="cuda")
+
+    def walk():
+        dk_acc.zero_()
+        dv_acc.zero_()
+        for p0, n, sk in plan:
+            qc, doc = q[:, :, p0:p0 + n], do[:, :, p0:p0 + n]
+            kc, vc = k[:, :, :sk], v[:, :, :sk]
+            binding.fwd(qc, kc, vc, scale=c.scale, causal=True, q_offset=p0, out=O[:, :, p0:p0 + n],
+                        lse=LSE[:, :, p0:p0 + n], workspace=fws)
+            binding.bwd_preprocess(O[:, :, p0:p0 + n], doc, delta=Delta[:, :, p0:p0 + n])
+            binding.bwd_chunked(qc, kc, vc, doc, LSE[:, :, p0:p0 + n], Delta[:, :, p0:p0 + n], dk_acc, dv_acc,
+                                scale=c.scale, causal=True, q_offset=p0, dq=dQ[:, :, p0:p0 + n], workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        walk()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        walk()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    pairs = accounting.chunked_pairs(c.Hq, W, C)
+    flops = accounting.fwd_flops(pairs, c.D) + accounting.bwd_flops(pairs, c.D)
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"ms_per_walk": ms, "tflops": tflops, "pct_of_peak": 100.0 * tflops / accounting.MI355X_BF16_DENSE_TFLOPS,
+            "chunks": len(plan), "pairs": pairs, "gflop_per_walk": flops / 1e9,
+            "timing": "hip graph replay of the whole 64-chunk walk"}
 
 
 KERNEL_SOURCES = ("flash_attention_train_amd/csrc/fa_bwd_bf16.hip", "flash_attention_train_amd/csrc/fa_device.h",
@@ -296,6 +370,11 @@ def main():
 
     extra = {}
     for key in [k for k in args.extra.split(",") if k and k not in (args.workload, "none")]:
+        if key == "long_window":
+            extra[key] = time_long_window(max(2, args.steps // 8), 1)
+            log(f"[bench] {key}: {extra[key]['ms_per_walk']:.2f} ms/walk, {extra[key]['tflops']:.1f} TFLOP/s")
+            torch.cuda.empty_cache()
+            continue
         we = Workload(key, args.splits if "x" not in args.splits else "table")
         re_ = time_workload(we, max(5, args.steps // 2), args.warmup, graph=not args.eager)
         re_["pct_of_peak"] = 100.0 * re_["tflops"] / accounting.MI355X_BF16_DENSE_TFLOPS

@@ -32,7 +32,8 @@ class FaAttnParams(ctypes.Structure):
                 ("Sk", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("q_offset", ctypes.c_int64), ("scale", ctypes.c_float), ("mask", ctypes.c_void_p),
                 ("mask_stride_b", ctypes.c_int64), ("mask_stride_q", ctypes.c_int64), ("mask_tiles", ctypes.c_void_p),
-                ("fwd_variant", ctypes.c_int32), ("kv_split", ctypes.c_int32), ("q_split", ctypes.c_int32)]
+                ("fwd_variant", ctypes.c_int32), ("kv_split", ctypes.c_int32), ("q_split", ctypes.c_int32),
+                ("fwd_split", ctypes.c_int32)]
 
 
 class FaError(RuntimeError):
@@ -49,6 +50,8 @@ _PV = ctypes.POINTER(FaView)
 _PP = ctypes.POINTER(FaAttnParams)
 SIGNATURES = {
     "fa_train_fwd": ([_PP, _PV, _PV, _PV, _PV, _PV, _VP], ctypes.c_int),
+    "fa_train_fwd_workspace_bytes": ([_PP], ctypes.c_size_t),
+    "fa_train_fwd_ws": ([_PP, _PV, _PV, _PV, _PV, _PV, _VP, ctypes.c_size_t, _VP], ctypes.c_int),
     "fa_train_bwd_preprocess": ([_PP, _PV, _PV, _PV, _VP], ctypes.c_int),
     "fa_train_bwd_workspace_bytes": ([_PP], ctypes.c_size_t),
     "fa_train_bwd": ([_PP, _PV, _PV, _PV, _PV, _PV, _PV, _PV, _PV, _PV, _VP, ctypes.c_size_t, _VP], ctypes.c_int),
@@ -115,7 +118,7 @@ def _stream_handle(stream) -> int:
 
 def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], causal: bool,
                 q_offset: Optional[int], mask: Optional[torch.Tensor], fwd_variant: int = 0, kv_split: int = 0,
-                q_split: int = 0, mask_tiles: Optional[torch.Tensor] = None) -> FaAttnParams:
+                q_split: int = 0, mask_tiles: Optional[torch.Tensor] = None, fwd_split: int = 0) -> FaAttnParams:
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Sk, Dk = k.shape
     if Bk != B or Dk != D:
@@ -125,7 +128,7 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
     if q_offset is None:
         q_offset = Sk - Sq if causal else 0
     p = FaAttnParams(B, Hq, Hkv, Sq, Sk, D, _dtype_code(q), int(bool(causal)), int(q_offset), float(scale),
-                     None, 0, 0, None, int(fwd_variant), int(kv_split), int(q_split))
+                     None, 0, 0, None, int(fwd_variant), int(kv_split), int(q_split), int(fwd_split))
     if mask is not None:
         if mask.dtype != torch.float32 or mask.dim() != 3 or mask.stride(2) != 1:
             raise ValueError("mask must be an fp32 [Bm, Sq, Sk] tensor with a contiguous last dimension")
@@ -167,17 +170,31 @@ def mask_tile_count(mask: torch.Tensor) -> int:
     return Bm * ((Sq + 63) // 64) * ((Sk + 63) // 64)
 
 
+def fwd_workspace_bytes(q, k, *, scale=None, causal=False, q_offset=None, mask=None, split=0) -> int:
+    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, fwd_split=split)
+    return int(lib().fa_train_fwd_workspace_bytes(ctypes.byref(p)))
+
+
 def fwd(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, out=None, lse=None, stream=None,
-        variant=0, mask_tiles=None):
-    """Forward: returns (O, LSE). O has q's dtype and shape; LSE is fp32 [B, Hq, Sq]."""
+        variant=0, mask_tiles=None, workspace=None, split=0):
+    """Forward: returns (O, LSE). O has q's dtype and shape; LSE is fp32 [B, Hq, Sq].
+    Runs fa_train_fwd_ws: a short grid may split the key walks (split = 0: the library's
+    choice; 1: never), with `workspace` (allocated here when None and needed)."""
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, fwd_variant=variant,
-                    mask_tiles=mask_tiles)
+                    mask_tiles=mask_tiles, fwd_split=split)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    _check("fa_train_fwd", lib().fa_train_fwd(ctypes.byref(p), view4(q), view4(k), view4(v), view4(out), view3(lse),
-                                              _stream_handle(stream)))
+    need = int(lib().fa_train_fwd_workspace_bytes(ctypes.byref(p)))
+    if need == ctypes.c_size_t(-1).value:
+        need = 0  # invalid parameters: the call itself reports why
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("fa_train_fwd_ws", lib().fa_train_fwd_ws(ctypes.byref(p), view4(q), view4(k), view4(v), view4(out),
+                                                    view3(lse), ws_ptr, ws_bytes, _stream_handle(stream)))
     return out, lse
 
 

@@ -85,7 +85,8 @@ fa_status check_params(const fa_attn_params* p) {
     return fail(FA_ERR_SHAPE, "q_offset out of range");
   if (!(p->scale > 0.f) || !isfinite(p->scale)) return fail(FA_ERR_SHAPE, "scale must be positive and finite");
   if (p->fwd_variant < 0 || p->fwd_variant > 3) return fail(FA_ERR_SHAPE, "unknown forward variant %d", p->fwd_variant);
-  if (p->kv_split < 0 || p->kv_split > 64 || p->q_split < 0 || p->q_split > 64)
+  if (p->kv_split < 0 || p->kv_split > 64 || p->q_split < 0 || p->q_split > 64 || p->fwd_split < 0 ||
+      p->fwd_split > 64)
     return fail(FA_ERR_SHAPE, "split hints must be in 0 .. 64");
   if (p->mask) {
     if (p->mask_stride_q < p->Sk) return fail(FA_ERR_STRIDE, "mask_stride_q (%lld) < Sk", (long long)p->mask_stride_q);
@@ -400,15 +401,39 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   return hip_status(fa::launch_dq_convert(c, is_bf16, stream), "dq convert");
 }
 
-}  // namespace
+// Split of the bf16 forward's key walks: fwd_split when given, else 1 unless the grid has
+// fewer than 256 query-tile workgroups (one per CU at most: a CU holds two), then as many
+// as bring it near 512 while every split keeps at least 12 key tiles (capped at 16): the
+// merge and each workgroup's first loads cost about as much as 12 tiles of walk
+// (measured: 16 heads x 1542 rows gains 10% at 2 splits and loses at 3; a 512-row
+// chunk over a 32768-key window runs 4x faster at 8).
+int choose_fwd_split(const fa_attn_params* p) {
+  if (p->dtype != FA_BF16) return 1;
+  const int64_t wgs = (int64_t)p->B * p->Hq * ((p->Sq + 127) / 128);
+  int64_t nkt = (p->Sk + 63) / 64;
+  if (p->causal) {  // the longest walk: the last query tile's
+    const int64_t last_key = p->q_offset + p->Sq - 1;
+    nkt = last_key < 0 ? 0 : std::min<int64_t>(last_key / 64 + 1, nkt);
+  }
+  if (p->fwd_split) return (int)std::max<int64_t>(1, std::min<int64_t>(p->fwd_split, std::max<int64_t>(nkt, 1)));
+  if (wgs >= 256) return 1;
+  const int64_t s = std::min<int64_t>({16, (512 + wgs - 1) / wgs, nkt / 12});
+  return (int)std::max<int64_t>(1, s);
+}
 
-extern "C" {
+size_t fwd_workspace_bytes(const fa_attn_params* p) {
+  const int s = choose_fwd_split(p);
+  if (s <= 1) return 0;
+  return round256((size_t)s * p->B * p->Hq * p->Sq * (p->D + 2) * sizeof(float));
+}
 
-fa_status fa_train_fwd(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,
-                       const fa_view* o, const fa_view* lse, hipStream_t stream) {
-  g_err[0] = 0;
+fa_status fwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,
+                     const fa_view* o, const fa_view* lse, void* workspace, size_t workspace_bytes_given,
+                     bool with_ws, hipStream_t stream) {
   fa_status s = check_params(p);
   if (s) return s;
+  if (!with_ws && p->fwd_split > 1)
+    return fail(FA_ERR_WORKSPACE, "fwd_split %d needs a workspace: call fa_train_fwd_ws", p->fwd_split);
   const int elt = elt_of(p);
   Extent eq, ek, ev, eo, el;
   if ((s = check_view(q, "q", p->B, p->Hq, p->Sq, p->D, elt, true, false, &eq))) return s;
@@ -422,9 +447,18 @@ fa_status fa_train_fwd(const fa_attn_params* p, const fa_view* q, const fa_view*
   const char* in_names[4] = {"q", "k", "v", "mask"};
   int n_in = 3;
   if (p->mask) ins[n_in++] = mask_extent(p);
-  Extent outs[2] = {eo, el};
-  const char* out_names[2] = {"o", "lse"};
-  if ((s = check_alias(outs, 2, out_names, ins, n_in, in_names))) return s;
+  const int splits = with_ws ? choose_fwd_split(p) : 1;
+  const size_t need = splits > 1 ? fwd_workspace_bytes(p) : 0;
+  if (need > 0) {
+    if (!workspace) return fail(FA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes_given < need)
+      return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_given, need);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(FA_ERR_ALIGN, "workspace is not 256-byte aligned");
+  }
+  const uintptr_t wlo = reinterpret_cast<uintptr_t>(workspace);
+  Extent outs[3] = {eo, el, {wlo, wlo + need}};
+  const char* out_names[3] = {"o", "lse", "workspace"};
+  if ((s = check_alias(outs, need > 0 ? 3 : 2, out_names, ins, n_in, in_names))) return s;
 
   fa::FwdArgs a;
   a.a = shape_of(p);
@@ -442,7 +476,15 @@ fa_status fa_train_fwd(const fa_attn_params* p, const fa_view* q, const fa_view*
   a.inv_scale = 1.f / p->scale;
   const uintptr_t mp = reinterpret_cast<uintptr_t>(p->mask);
   a.mask_vec4 = p->mask && mp % 16 == 0 && p->mask_stride_q % 4 == 0 && p->mask_stride_b % 4 == 0;
+  a.splits = splits;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
   if (p->dtype == FA_BF16) {
+    if (splits > 1) {  // the split walk runs the default configuration
+      a.part_o = static_cast<float*>(workspace);
+      a.part_ml = a.part_o + (size_t)splits * p->B * p->Hq * p->Sq * p->D;
+      return hip_status(fa::launch_fwd_bf16_split(a, stream), "split forward");
+    }
     // variant 1 (32 query rows per wave, 64-key tiles, two waves per SIMD) measured
     // faster than variant 2 (64 rows per wave, 32-key tiles, one wave per SIMD) on
     // every workload shape tried; variant 2 stays selectable for tuning
@@ -450,6 +492,28 @@ fa_status fa_train_fwd(const fa_attn_params* p, const fa_view* q, const fa_view*
     return hip_status(fa::launch_fwd_bf16(a, variant, stream), "forward");
   }
   return hip_status(fa::launch_fwd(a, 0, stream), "forward");
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_train_fwd(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,
+                       const fa_view* o, const fa_view* lse, hipStream_t stream) {
+  g_err[0] = 0;
+  return fwd_common(p, q, k, v, o, lse, nullptr, 0, false, stream);
+}
+
+size_t fa_train_fwd_workspace_bytes(const fa_attn_params* p) {
+  if (check_params(p) != FA_OK) return (size_t)-1;
+  return fwd_workspace_bytes(p);
+}
+
+fa_status fa_train_fwd_ws(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,
+                          const fa_view* o, const fa_view* lse, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  g_err[0] = 0;
+  return fwd_common(p, q, k, v, o, lse, workspace, workspace_bytes, true, stream);
 }
 
 fa_status fa_train_bwd_preprocess(const fa_attn_params* p, const fa_view* o, const fa_view* dout,

@@ -42,7 +42,9 @@ __device__ __forceinline__ f32x16 zeros16() {
 // KS = 2 splits the keys of a query tile over two halves of the workgroup (for problems
 // with too few query tiles to fill the GPU): waves 0-1 and 2-3 own the same 64 rows, take
 // alternate live key tiles, and merge their (max, sum, O) in LDS at the end.
-template <int D, int QB, int BN, bool CAUSAL, bool MASK, int KS>
+// SPLIT: workgroup blockIdx.z walks only the blockIdx.z-th contiguous share of the live
+// range's key tiles and leaves its unnormalised rows to the merge pass.
+template <int D, int QB, int BN, bool CAUSAL, bool MASK, int KS, bool SPLIT = false>
 __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const FwdArgs args) {
   constexpr int NW = 4;
   constexpr int RB = NW / KS;       // waves (row blocks) per key half
@@ -101,6 +103,12 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
   if (CAUSAL) {
     const int64_t last_key = a.q_offset + q0 + BM - 1;
     kt_end = last_key < 0 ? 0 : (int)((last_key / BN + 1) < nkt ? (last_key / BN + 1) : nkt);
+  }
+  int kt_begin = 0;
+  if constexpr (SPLIT) {  // this workgroup's share of [0, kt_end)
+    const int per = (kt_end + (int)gridDim.z - 1) / (int)gridDim.z;
+    kt_begin = min(kt_end, (int)blockIdx.z * per);
+    kt_end = min(kt_end, kt_begin + per);
   }
 
   // tile staging: K and V rows [key0, key0 + BN) straight into LDS; keys past the end
@@ -170,7 +178,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
 
   // The walk goes in steps of KS live tiles (tk[0] < tk[1] ...); this wave's tile is tk[kh].
   int tk[KS];
-  tk[0] = next_live(0);
+  tk[0] = next_live(kt_begin);
   #pragma unroll
   for (int j = 1; j < KS; ++j) tk[j] = tk[j - 1] < kt_end ? next_live(tk[j - 1] + 1) : kt_end;
   int kt = tk[kh];
@@ -372,6 +380,23 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     base[0] = nb;
   }
 
+  if constexpr (SPLIT) {  // unnormalised rows, their base and row sum, for the merge
+    static_assert(QB == 1 && KS == 1, "the split walk runs the one-block, one-half configuration");
+    const int row = qw + r32;
+    const float lt = lsum[0] + xor32(lsum[0]);
+    if (row < a.Sq) {
+      const int64_t r = (((int64_t)blockIdx.z * a.B + b) * a.Hq + h) * a.Sq + row;
+      float* po = args.part_o + r * D;
+      #pragma unroll
+      for (int db = 0; db < DB; ++db)
+        #pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          *reinterpret_cast<f32x4*>(po + 32 * db + 8 * rr + 4 * g) =
+              f32x4{oacc[0][db][4 * rr], oacc[0][db][4 * rr + 1], oacc[0][db][4 * rr + 2], oacc[0][db][4 * rr + 3]};
+      if (g == 0) *reinterpret_cast<float2*>(args.part_ml + 2 * r) = float2{base[0], lt};
+    }
+    return;
+  }
   // epilogue: O = acc / l, LSE = (base + log2 l) ln 2; fully masked rows -> 0, 0
   #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -395,6 +420,62 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
       if (g == 0) args.lse[b * args.lse_sb + h * args.lse_sh + row] = lse;
     }
   }
+}
+
+// Merge of a split forward: per row, the partial rows are rescaled to the largest base
+// and summed, O = sum / (rescaled row sums), LSE = (base + log2 sum) ln 2; a row no split
+// saw a key for (every base -inf) gets O = 0, LSE = 0. One thread per 4 columns of a row.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(const FwdArgs args) {
+  constexpr int TPR = D / 4;  // threads per row
+  const AttnShape& a = args.a;
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
+  const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;
+  const int c = 4 * (threadIdx.x % TPR);
+  if (r >= rows) return;
+  const int S = args.splits;
+  const int64_t stride = rows;  // rows per split slice
+  float mx = neg_inf();
+  for (int z = 0; z < S; ++z) mx = fmaxf(mx, args.part_ml[2 * (z * stride + r)]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  if (mx != neg_inf()) {
+    for (int z = 0; z < S; ++z) {
+      const float2 ml = *reinterpret_cast<const float2*>(args.part_ml + 2 * (z * stride + r));
+      if (ml.x == neg_inf()) continue;
+      const float w = fast_exp2(ml.x - mx);
+      l += w * ml.y;
+      const f32x4 po = *reinterpret_cast<const f32x4*>(args.part_o + (z * stride + r) * D + c);
+      acc += w * po;
+    }
+  }
+  const bool full = mx == neg_inf();
+  const float inv = full ? 0.f : 1.f / l;
+  const int i = (int)(r % a.Sq);
+  const int h = (int)((r / a.Sq) % a.Hq), b = (int)(r / ((int64_t)a.Sq * a.Hq));
+  bf16* O = static_cast<bf16*>(args.o) + b * args.so.b + h * args.so.h + (int64_t)i * args.so.s + c;
+  *reinterpret_cast<bf16x4*>(O) = bf16x4{(bf16)(acc[0] * inv), (bf16)(acc[1] * inv), (bf16)(acc[2] * inv),
+                                         (bf16)(acc[3] * inv)};
+  if (c == 0) args.lse[b * args.lse_sb + h * args.lse_sh + i] = full ? 0.f : (mx + log2f(l)) * kLn2;
+}
+
+template <int D>
+hipError_t launch_split_d(const FwdArgs& args, hipStream_t stream) {
+  const dim3 grid(args.a.Hq * args.a.B, (args.a.Sq + 127) / 128, args.splits);
+  const bool causal = args.a.causal != 0, mask = args.a.mask != nullptr;
+  if (causal && mask)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, 64, true, true, 1, true>), grid, dim3(256), 0, stream, args);
+  else if (causal)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, 64, true, false, 1, true>), grid, dim3(256), 0, stream, args);
+  else if (mask)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, 64, false, true, 1, true>), grid, dim3(256), 0, stream, args);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, 64, false, false, 1, true>), grid, dim3(256), 0, stream, args);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t threads = (int64_t)args.a.B * args.a.Hq * args.a.Sq * (D / 4);
+  hipLaunchKernelGGL((fwd_merge_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, args);
+  return hipGetLastError();
 }
 
 template <int D, int QB, int BN, int KS>
@@ -426,6 +507,10 @@ hipError_t launch_d(const FwdArgs& args, int variant, hipStream_t stream) {
 // 3 = 32 rows per wave, keys split over two halves of the workgroup, 32-key tiles
 hipError_t launch_fwd_bf16(const FwdArgs& args, int variant, hipStream_t stream) {
   return args.a.D == 64 ? launch_d<64>(args, variant, stream) : launch_d<128>(args, variant, stream);
+}
+
+hipError_t launch_fwd_bf16_split(const FwdArgs& args, hipStream_t stream) {
+  return args.a.D == 64 ? launch_split_d<64>(args, stream) : launch_split_d<128>(args, stream);
 }
 
 }  // namespace fa

@@ -86,6 +86,11 @@ struct FwdArgs {
   int64_t lse_sb, lse_sh;
   float inv_scale;  // 1 / scale (scale > 0)
   int mask_vec4;    // the mask can be read 4 floats at a time (16-byte aligned rows)
+  // split key walks (splits > 1): workgroup z walks the z-th share of the key tiles and
+  // stores its unnormalised fp32 O rows and (base, row sum) per row, merged afterwards
+  int splits;
+  float* part_o;    // [splits][B][Hq][Sq][D]
+  float* part_ml;   // [splits][B][Hq][Sq][2]: exponent base (log2 units, -inf: no key), row sum
 };
 
 struct PreArgs {
@@ -152,6 +157,8 @@ struct DqArgs {
 // launchers: return hipSuccess or the launch error
 hipError_t launch_fwd(const FwdArgs& args, int is_bf16, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& args, int qb, hipStream_t stream);
+// the split forward (args.splits > 1) followed by the merge of its partial rows
+hipError_t launch_fwd_bf16_split(const FwdArgs& args, hipStream_t stream);
 hipError_t launch_preprocess(const PreArgs& args, int is_bf16, hipStream_t stream);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_mask_tiles(const AttnShape& a, uint8_t* tiles, hipStream_t stream);

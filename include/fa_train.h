@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FA_TRAIN_ABI_VERSION 1
+#define FA_TRAIN_ABI_VERSION 2
 
 typedef enum fa_status {
     FA_OK = 0,
@@ -112,12 +112,36 @@ typedef struct fa_attn_params {
                              workspace, summed by a reduce pass) */
     int32_t q_split;      /* bf16 backward: workgroups sharing one 128-row query tile's dQ
                              walk, 1 .. 64 (> 1: fp32 partial slices, as for kv_split) */
+    int32_t fwd_split;    /* bf16 forward through fa_train_fwd_ws: workgroups sharing one
+                             128-row query tile's key walk, 1 .. 64 (> 1: each stores its
+                             unnormalised fp32 rows in the workspace and a merge pass
+                             combines them). fa_train_fwd never splits and rejects > 1. */
 } fa_attn_params;
 
 /* Forward: writes O (dtype) and LSE (fp32, natural log). Fully masked rows get
  * O = 0 and LSE = 0. O must not overlap Q, K or V. */
 fa_status fa_train_fwd(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,
                        const fa_view* o, const fa_view* lse, hipStream_t stream);
+
+/* Bytes of device workspace fa_train_fwd_ws needs for p: 0 when the forward is not
+ * split, else splits * B * Hq * Sq * (D + 2) * 4 rounded up to 256 (the partial rows,
+ * their exponent bases and row sums). The split is fwd_split when set, else chosen
+ * from the shape: only grids with fewer than 256 query-tile workgroups and key walks of
+ * at least 24 tiles of 64 keys are split. Returns (size_t)-1 if p is invalid. */
+size_t fa_train_fwd_workspace_bytes(const fa_attn_params* p);
+
+/* Forward with a caller-owned workspace: the same results as fa_train_fwd (O, LSE,
+ * fully masked rows O = 0 and LSE = 0) for the same inputs, up to the order of fp32
+ * summation, but a short grid may split each query tile's key walk over several
+ * workgroups (the split-key reading of the pages' tiled forward; the partial rows are
+ * merged exactly by rescaling to the largest exponent base). `workspace`: at least
+ * fa_train_fwd_workspace_bytes(p) bytes of device memory, 256-byte aligned (NULL
+ * allowed when 0 bytes are needed), overlapping no input or output; contents on entry
+ * do not matter. Errors: those of fa_train_fwd, FA_ERR_WORKSPACE, FA_ERR_ALIGN and
+ * FA_ERR_ALIAS for the workspace. */
+fa_status fa_train_fwd_ws(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,
+                          const fa_view* o, const fa_view* lse, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 /* Preprocess for the backward: Delta_i = sum_d dO_id * O_id in fp32, from the stored
  * O and dO. Only B, Hq, Sq, D and dtype of p are used. */

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(L, n), n
         assert n in B.SIGNATURES, f"{n} has no ctypes signature in the binding"
-    assert L.fa_train_version() == 1
+    assert L.fa_train_version() == 2
 
 
 BASE = 0x7F0000000000  # fake, 256-byte aligned device addresses
@@ -42,7 +42,7 @@ BASE = 0x7F0000000000  # fake, 256-byte aligned device addresses
 
 def params(**kw):
     a = dict(B=1, Hq=4, Hkv=2, Sq=64, Sk=64, D=64, dtype=B.FA_BF16, causal=0, q_offset=0, scale=0.125, mask=None,
-             mask_stride_b=0, mask_stride_q=0, mask_tiles=None, fwd_variant=0, kv_split=0, q_split=0)
+             mask_stride_b=0, mask_stride_q=0, mask_tiles=None, fwd_variant=0, kv_split=0, q_split=0, fwd_split=0)
     a.update(kw)
     return B.FaAttnParams(*(a[f] for f, _ in B.FaAttnParams._fields_))
 
@@ -95,6 +95,34 @@ def test_forward_rejects(name, p, over, code):
     assert st == code, (st, B.lib().fa_train_last_error())
     assert B.lib().fa_train_last_error() != b""
     assert B.lib().fa_train_status_str(st) not in (b"", b"ok")
+
+
+def test_split_forward_workspace_and_rejects():
+    L = B.lib()
+    # splits x B x Hq x Sq x (D + 2) fp32: the partial rows plus their base and row sum
+    p2 = params(Sk=640, fwd_split=2)
+    assert L.fa_train_fwd_workspace_bytes(ctypes.byref(p2)) == 2 * 1 * 4 * 64 * 66 * 4
+    # automatic: 4 query-tile workgroups, 64 key tiles -> 5 splits (each at least 12 tiles)
+    assert L.fa_train_fwd_workspace_bytes(ctypes.byref(params(Sk=4096))) == 5 * 1 * 4 * 64 * 66 * 4
+    assert L.fa_train_fwd_workspace_bytes(ctypes.byref(params())) == 0  # one key tile: nothing to split
+    assert L.fa_train_fwd_workspace_bytes(ctypes.byref(params(Sk=640, fwd_split=1))) == 0
+    assert L.fa_train_fwd_workspace_bytes(None) == ctypes.c_size_t(-1).value
+    assert L.fa_train_fwd_workspace_bytes(ctypes.byref(params(fwd_split=65))) == ctypes.c_size_t(-1).value
+    kk, vv = view(1, H=2, S=640), view(2, H=2, S=640)
+    need = 2 * 1 * 4 * 64 * 66 * 4
+    ws = BASE + 12 * (1 << 24)
+
+    def fws(p, ws=ws, nbytes=need, **over):
+        v = {"q": view(0), "k": kk, "v": vv, "o": view(3), "lse": lse_view(4)}
+        v.update(over)
+        return L.fa_train_fwd_ws(ctypes.byref(p), v["q"], v["k"], v["v"], v["o"], v["lse"], ws, nbytes, None)
+
+    assert fwd_call(p2, k=kk, v=vv) == 8  # the plain forward never splits
+    assert fws(p2, ws=None) == 8
+    assert fws(p2, nbytes=need - 1) == 8
+    assert fws(p2, ws=ws + 64) == 5
+    assert fws(p2, ws=BASE) == 6  # workspace over Q
+    assert fws(params(Sk=640, fwd_split=65)) == 2
 
 
 def bwd_call(p, accumulate=False, ws=None, ws_bytes=None, **over):

@@ -11,15 +11,21 @@ import torch
 
 import oracle
 from flash_attention_train_amd import binding, configs
+from flash_attention_train_amd.inputs import make_case
 from parity_util import compare_full, host64, say, upload
 
 pytestmark = pytest.mark.gpu
 
 
 class Step:
-    def __init__(self, c, t):
+    def __init__(self, c, t, fwd_split=0):
         self.c, self.t = c, t
         q = t["q"]
+        self.fwd_split = fwd_split
+        self.fws = torch.empty(max(256, binding.fwd_workspace_bytes(q, t["k"], scale=c.scale, causal=c.causal,
+                                                                    q_offset=c.q_offset, mask=t["mask"],
+                                                                    split=fwd_split)),
+                               dtype=torch.uint8, device="cuda")
         self.o = torch.empty_like(q)
         self.lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
         self.delta = torch.empty_like(self.lse)
@@ -32,7 +38,7 @@ class Step:
         if self.tiles is not None:
             binding.mask_tile_map(t["mask"], t["q"], t["k"], out=self.tiles)
         binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal, q_offset=c.q_offset,
-                    out=self.o, lse=self.lse, mask_tiles=self.tiles)
+                    out=self.o, lse=self.lse, mask_tiles=self.tiles, workspace=self.fws, split=self.fwd_split)
         binding.bwd_preprocess(self.o, t["do"], delta=self.delta)
         binding.bwd(t["q"], t["k"], t["v"], t["do"], self.lse, self.delta, mask=t["mask"], scale=c.scale,
                     causal=c.causal, q_offset=c.q_offset, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws,
@@ -42,13 +48,18 @@ class Step:
         return [x.clone() for x in (self.o, self.lse, self.delta, self.dq, self.dk, self.dv)]
 
 
-@pytest.mark.parametrize("key,shrink", [("dit_sa", dict(Hq=4, Hkv=2, Sq=300, Sk=300)),
-                                        ("dit_ca", dict(B=2, Hq=2, Hkv=2, Sq=300, Sk=160)),
-                                        ("lm_causal", dict(Hq=4, Hkv=1, Sq=333, Sk=333))])
-def test_graph_replays_match_eager(key, shrink):
-    c = configs.make(key, **shrink)
-    say(f"{key}: graph capture of the whole step, B={c.B} Hq={c.Hq} Sq={c.Sq} Sk={c.Sk}")
-    step = Step(c, upload(c))
+@pytest.mark.parametrize("key,shrink,fwd_split", [("dit_sa", dict(Hq=4, Hkv=2, Sq=300, Sk=300), 0),
+                                                  ("dit_ca", dict(B=2, Hq=2, Hkv=2, Sq=300, Sk=160), 0),
+                                                  ("lm_causal", dict(Hq=4, Hkv=1, Sq=333, Sk=333), 0),
+                                                  ("chunk", None, 4)])
+def test_graph_replays_match_eager(key, shrink, fwd_split):
+    if key == "chunk":  # a query chunk late in a causal window: the split-key forward and its merge
+        c = make_case("graph_chunk", B=1, Hq=4, Hkv=2, Sq=200, Sk=1800, D=128, dtype="bf16", seed=71, causal=True,
+                      q_offset=1600)
+    else:
+        c = configs.make(key, **shrink)
+    say(f"{key}: graph capture of the whole step, B={c.B} Hq={c.Hq} Sq={c.Sq} Sk={c.Sk} fwd_split={fwd_split}")
+    step = Step(c, upload(c), fwd_split)
     step()
     torch.cuda.synchronize()
     eager = step.outputs()

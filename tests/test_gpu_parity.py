@@ -159,7 +159,27 @@ def test_forward_variants(name, config):
     c = CASES[name]()
     t = upload(c)
     o, lse = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
-                         q_offset=c.q_offset, variant=config)
+                         q_offset=c.q_offset, variant=config, split=1)
+    torch.cuda.synchronize()
+    m = None if c.mask is None else c.mask.astype(np.float64)
+    O, L = oracle.forward(c.f64("q"), c.f64("k"), c.f64("v"), m, scale=c.scale, causal=c.causal,
+                          q_offset=c.q_offset)
+    compare_full(c, {"O": host64(o), "LSE": host64(lse)}, {"O": O, "LSE": L}, names=("O", "LSE"))
+
+
+@pytest.mark.parametrize("split", [2, 3, 7])
+@pytest.mark.parametrize("name", ["dit_sa_ragged", "dit_ca_ragged", "lm_causal_gqa4", "chunk_offset",
+                                  "random_bias_bcast", "d64_bf16", "single_query_single_key"])
+def test_forward_splits(name, split):
+    """The split-key forward (each query tile's key walk over `split` workgroups, partial rows merged)
+    against the oracle, fully masked rows exact; splits that see no key contribute nothing."""
+    c = CASES[name]()
+    t = upload(c)
+    ws = torch.empty(max(1, binding.fwd_workspace_bytes(t["q"], t["k"], scale=c.scale, causal=c.causal,
+                                                        q_offset=c.q_offset, mask=t["mask"], split=split)),
+                     dtype=torch.uint8, device="cuda")
+    o, lse = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
+                         q_offset=c.q_offset, workspace=ws, split=split)
     torch.cuda.synchronize()
     m = None if c.mask is None else c.mask.astype(np.float64)
     O, L = oracle.forward(c.f64("q"), c.f64("k"), c.f64("v"), m, scale=c.scale, causal=c.causal,
@@ -294,9 +314,10 @@ def test_mask_tile_map_and_skipping(name):
     rows = (blocks.astype(np.uint64) * weights[None, None, None, None, :]).sum(axis=4, dtype=np.uint64)
     cols = (blocks.astype(np.uint64) * weights[None, None, None, :, None]).sum(axis=3, dtype=np.uint64)
     assert np.array_equal(words[0], rows) and np.array_equal(words[1], cols)
-    for variant in (1, 3):  # the key-split forward walks the live tiles in pairs
+    # the key-split forward walks the live tiles in pairs; the split forward a share of them
+    for variant, split in ((1, 1), (3, 1), (1, 3)):
         o3, lse3 = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
-                               q_offset=c.q_offset, mask_tiles=tiles, variant=variant)
+                               q_offset=c.q_offset, mask_tiles=tiles, variant=variant, split=split)
         torch.cuda.synchronize()
         ref = oracle_full(c)
         compare_full(c, {"O": host64(o3), "LSE": host64(lse3)}, ref, names=("O", "LSE"))
