@@ -188,8 +188,11 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
   using TL = Tile<D>;
   bf16* q_lds = reinterpret_cast<bf16*>(smem);                 // [2][KV_BM * D]
   bf16* do_lds = q_lds + 2 * KV_BM * D;                        // [2][KV_BM * D]
-  float* lse_lds = reinterpret_cast<float*>(do_lds + 2 * KV_BM * D);  // [2][KV_BM]
-  float* dlt_lds = lse_lds + 2 * KV_BM;                        // [2][KV_BM]
+  // one extra 16-wide k-chunk per staged Q and dO row: (-LSE / scale) and (-Delta), each as
+  // three bf16 terms (hi + mid + lo carry the fp32 value) and zeros; with K and V extended by
+  // (1, 1, 1, 0 ...) the products give S - LSE / scale and dP - Delta directly, so the row
+  // statistics are never broadcast to every lane through LDS
+  bf16* aug_lds = do_lds + 2 * KV_BM * D;                      // [Q', dO'][2 buffers][KV_BM][16]
 
   const AttnShape& a = args.a;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -206,6 +209,10 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
   // (keys past the end read the last key: their scores are hidden on the tail tile and
   // their rows are never stored; a zeroing branch would make the loads wait here)
   const int64_t key_c = min(key, a.Sk - 1);
+  // the K / V extension of the augmented chunk: (1, 1, 1, 0 ...) in half 0, zeros in half 1
+  bf16x8 ones3;
+  #pragma unroll
+  for (int e = 0; e < 8; ++e) ones3[e] = (bf16)(g == 0 && e < 3 ? 1.f : 0.f);
   bf16x8 kf[DS], vf[DS];
   #pragma unroll
   for (int s = 0; s < DS; ++s) {
@@ -249,6 +256,16 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
   };
 
   float lpre = 0.f;
+  // each of the first 2 KV_BM threads owns one augmented row in both buffers: zeroed once here
+  // by the thread that later writes its three terms (so no barrier orders the two)
+  if (tid < 2 * KV_BM) {
+    #pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      bf16x8* z = reinterpret_cast<bf16x8*>(aug_lds + (((tid / KV_BM) * 2 + bb) * KV_BM + tid % KV_BM) * 16);
+      zero(z[0]);
+      zero(z[1]);
+    }
+  }
   auto pair_of = [&](const Pos& x, int& h, int& q0) {
     h = hk * a.G + x.hi;
     q0 = (qt0 + x.qi) * KV_BM;
@@ -264,16 +281,21 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     TL::template stage<KV_BM, NT, false>(do_lds + buf * KV_BM * D, dO, args.sdo.s, a.Sq - q0);
     if (tid < 2 * KV_BM) {
       const int row = min(q0 + (tid % KV_BM), a.Sq - 1);
-      // (scaled when stored, so that nothing waits for the load before the tile's work)
+      // (turned into its three terms when stored, so that nothing waits for the load before
+      // the tile's work)
       lpre = tid < KV_BM ? args.lse[b * args.lse_sb + h * args.lse_sh + row]
                          : args.delta[b * args.delta_sb + h * args.delta_sh + row];
     }
   };
   auto store_stats = [&](int buf) {
-    if (tid < KV_BM)
-      lse_lds[buf * KV_BM + tid] = lpre * kLog2e;
-    else if (tid < 2 * KV_BM)
-      dlt_lds[buf * KV_BM + tid - KV_BM] = lpre;
+    if (tid < 2 * KV_BM) {
+      const float c = tid < KV_BM ? -lpre * args.inv_scale : -lpre;
+      const bf16 hi = (bf16)c;
+      const bf16 mid = (bf16)(c - (float)hi);
+      const bf16 lo = (bf16)(c - (float)hi - (float)mid);
+      *reinterpret_cast<bf16x4*>(aug_lds + (((tid / KV_BM) * 2 + buf) * KV_BM + tid % KV_BM) * 16) =
+          bf16x4{hi, mid, lo, (bf16)0.f};
+    }
   };
 
   const int G16 = lane >> 4, L16 = lane & 15;
@@ -351,8 +373,8 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
     const bf16* qb_lds = q_lds + buf * KV_BM * D;
     const bf16* db_lds = do_lds + buf * KV_BM * D;
-    const float* lse_b = lse_lds + buf * KV_BM;
-    const float* dlt_b = dlt_lds + buf * KV_BM;
+    const bf16* qx_lds = aug_lds + buf * KV_BM * 16;        // Q' rows of this pair
+    const bf16* dx_lds = aug_lds + (2 + buf) * KV_BM * 16;  // dO' rows
     bool edge = q0 + KV_BM > a.Sq || n0 + KV_BN > a.Sk;
     if (CAUSAL) edge = edge || ((int64_t)n0 + KV_BN - 1 > a.q_offset + q0);
     // Rows of the tile this lane's key can see, as a bit word (bit i: row q0 + i): the
@@ -378,6 +400,10 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     // dK += dS^T Q (C). They run as A0, A1 with B0, C0 with B1, C1, so that each
     // block's vector work (B) has the other block's matrix products beside it;
     // masking is applied unconditionally (a no-op word on open blocks).
+    // the augmented chunk of row 32 qb + r32 (half g: elements 8 g .. 8 g + 7)
+    auto read_x = [&](const bf16* x_lds, int qb) {
+      return *reinterpret_cast<const bf16x8*>(x_lds + (32 * qb + r32) * 16 + 8 * g);
+    };
     auto step_a = [&](int qb, f32x16& sacc, f32x16& dpacc) {
       bf16x8 qa[DS], da[DS];
       #pragma unroll
@@ -385,6 +411,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
         qa[s] = TL::read_chunk(qb_lds, 32 * qb + r32, 2 * s + g);
         da[s] = TL::read_chunk(db_lds, 32 * qb + r32, 2 * s + g);
       }
+      const bf16x8 qx = read_x(qx_lds, qb), dx = read_x(dx_lds, qb);
       sacc = zeros16();
       dpacc = zeros16();
       #pragma unroll
@@ -392,6 +419,8 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
         mma(sacc, qa[s], kf[s]);
         mma(dpacc, da[s], vf[s]);
       }
+      mma(sacc, qx, ones3);
+      mma(dpacc, dx, ones3);
     };
     // transpose reads of dO^T / Q^T for half hh of block qb (the operands of step C):
     // registers 8 hh .. 8 hh + 7 of the score accumulators hold rows
@@ -427,7 +456,6 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     // P = 0; bit 8 rr + e of the visibility word <-> register 4 rr + e)
     struct RowStats {
       uint32_t w;
-      f32x4 l4[4], d4[4];
     };
     auto stats_b = [&](int qb, f32x16& sacc, RowStats& st) {
       if (BIAS && bias) {
@@ -439,19 +467,15 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
         }
       }
       st.w = (uint32_t)(vis >> (32 * qb + 4 * g));
-      #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        st.l4[rr] = *reinterpret_cast<const f32x4*>(lse_b + 32 * qb + 8 * rr + 4 * g);
-        st.d4[rr] = *reinterpret_cast<const f32x4*>(dlt_b + 32 * qb + 8 * rr + 4 * g);
-      }
     };
     auto slice_b = [&](int i, const RowStats& st, f32x16& sacc, f32x16& dpacc) {
       #pragma unroll
       for (int r = 2 * i; r < 2 * i + 2; ++r) {
+        // (the products already hold S - LSE / scale and dP - Delta)
         const float sv = ninf_unless_bit(sacc[r], st.w, 8 * (r >> 2) + (r & 3));
-        const float pv = fast_exp2(fmaf(sv, cs, -st.l4[r >> 2][r & 3]));
+        const float pv = fast_exp2(sv * cs);
         sacc[r] = pv;
-        dpacc[r] = pv * (dpacc[r] - st.d4[r >> 2][r & 3]);
+        dpacc[r] = pv * dpacc[r];
       }
     };
     f32x16 s0, dp0, s1, dp1;
@@ -469,18 +493,23 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
         qa[s] = TL::read_chunk(qb_lds, 32 + r32, 2 * s + g);
         da[s] = TL::read_chunk(db_lds, 32 + r32, 2 * s + g);
       }
+      const bf16x8 qx = read_x(qx_lds, 1), dx = read_x(dx_lds, 1);
       RowStats st;
       stats_b(0, s0, st);
       s1 = zeros16();
       dp1 = zeros16();
       __builtin_amdgcn_sched_barrier(0);
-      // DS product pairs spread over the 8 slices
+      // DS product pairs spread over the 8 slices, the augmented pair in the last
       #pragma unroll
       for (int i = 0; i < 8; ++i) {
         constexpr int EVERY = 8 / DS;
         if (i % EVERY == 0) {
           mma(s1, qa[i / EVERY], kf[i / EVERY]);
           mma(dp1, da[i / EVERY], vf[i / EVERY]);
+        }
+        if (i == 7) {
+          mma(s1, qx, ones3);
+          mma(dp1, dx, ones3);
         }
         slice_b(i, st, s0, dp0);
         __builtin_amdgcn_sched_barrier(0);
@@ -784,7 +813,7 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
 // which keeps that code and its registers out of the common loop.
 template <int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(NT) void bwd_bf16_kernel(const BwdArgs args, const BwdPlan plan) {
-  constexpr int KV_LDS = 2 * 2 * KV_BM * D * 2 + 4 * KV_BM * 4;
+  constexpr int KV_LDS = 2 * 2 * KV_BM * D * 2 + 2 * 2 * KV_BM * 16 * 2;
   constexpr int Q_LDS = 2 * 2 * Q_BN * D * 2;
   __shared__ __attribute__((aligned(16))) char smem[KV_LDS > Q_LDS ? KV_LDS : Q_LDS];
   const int blk = blockIdx.x;
