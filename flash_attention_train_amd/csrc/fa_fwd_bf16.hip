@@ -424,38 +424,41 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
 
 // Merge of a split forward: per row, the partial rows are rescaled to the largest base
 // and summed, O = sum / (rescaled row sums), LSE = (base + log2 sum) ln 2; a row no split
-// saw a key for (every base -inf) gets O = 0, LSE = 0. One thread per 4 columns of a row.
+// saw a key for (every base -inf) gets O = 0, LSE = 0. One pass over the splits with a
+// running base (the online softmax's own rescale), one thread per 8 columns of a row.
 template <int D>
 __global__ __launch_bounds__(256) void fwd_merge_kernel(const FwdArgs args) {
-  constexpr int TPR = D / 4;  // threads per row
+  constexpr int TPR = D / 8;  // threads per row
   const AttnShape& a = args.a;
   const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
   const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;
-  const int c = 4 * (threadIdx.x % TPR);
+  const int c = 8 * (threadIdx.x % TPR);
   if (r >= rows) return;
   const int S = args.splits;
-  const int64_t stride = rows;  // rows per split slice
-  float mx = neg_inf();
-  for (int z = 0; z < S; ++z) mx = fmaxf(mx, args.part_ml[2 * (z * stride + r)]);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float l = 0.f;
-  if (mx != neg_inf()) {
-    for (int z = 0; z < S; ++z) {
-      const float2 ml = *reinterpret_cast<const float2*>(args.part_ml + 2 * (z * stride + r));
-      if (ml.x == neg_inf()) continue;
-      const float w = fast_exp2(ml.x - mx);
-      l += w * ml.y;
-      const f32x4 po = *reinterpret_cast<const f32x4*>(args.part_o + (z * stride + r) * D + c);
-      acc += w * po;
-    }
+  float mx = neg_inf(), l = 0.f;
+  f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
+  #pragma unroll 4
+  for (int z = 0; z < S; ++z) {
+    const int64_t zr = (int64_t)z * rows + r;
+    const float2 ml = *reinterpret_cast<const float2*>(args.part_ml + 2 * zr);
+    const f32x4 plo = *reinterpret_cast<const f32x4*>(args.part_o + zr * D + c);
+    const f32x4 phi = *reinterpret_cast<const f32x4*>(args.part_o + zr * D + c + 4);
+    if (ml.x == neg_inf()) continue;  // this split saw no key of the row
+    const float nm = fmaxf(mx, ml.x);
+    const float fo = mx == neg_inf() ? 0.f : fast_exp2(mx - nm), fn = fast_exp2(ml.x - nm);
+    lo = lo * fo + plo * fn;
+    hi = hi * fo + phi * fn;
+    l = l * fo + ml.y * fn;
+    mx = nm;
   }
   const bool full = mx == neg_inf();
   const float inv = full ? 0.f : 1.f / l;
   const int i = (int)(r % a.Sq);
   const int h = (int)((r / a.Sq) % a.Hq), b = (int)(r / ((int64_t)a.Sq * a.Hq));
   bf16* O = static_cast<bf16*>(args.o) + b * args.so.b + h * args.so.h + (int64_t)i * args.so.s + c;
-  *reinterpret_cast<bf16x4*>(O) = bf16x4{(bf16)(acc[0] * inv), (bf16)(acc[1] * inv), (bf16)(acc[2] * inv),
-                                         (bf16)(acc[3] * inv)};
+  *reinterpret_cast<bf16x8*>(O) = bf16x8{(bf16)(lo[0] * inv), (bf16)(lo[1] * inv), (bf16)(lo[2] * inv),
+                                         (bf16)(lo[3] * inv), (bf16)(hi[0] * inv), (bf16)(hi[1] * inv),
+                                         (bf16)(hi[2] * inv), (bf16)(hi[3] * inv)};
   if (c == 0) args.lse[b * args.lse_sb + h * args.lse_sh + i] = full ? 0.f : (mx + log2f(l)) * kLn2;
 }
 
@@ -473,7 +476,7 @@ hipError_t launch_split_d(const FwdArgs& args, hipStream_t stream) {
     hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, 64, false, false, 1, true>), grid, dim3(256), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t threads = (int64_t)args.a.B * args.a.Hq * args.a.Sq * (D / 4);
+  const int64_t threads = (int64_t)args.a.B * args.a.Hq * args.a.Sq * (D / 8);
   hipLaunchKernelGGL((fwd_merge_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, args);
   return hipGetLastError();
 }
