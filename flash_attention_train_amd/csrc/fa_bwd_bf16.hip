@@ -186,13 +186,16 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
   constexpr int DS = D / 16, DB = D / 32;
   static_assert(8 % DS == 0 && 8 % (2 * DB) == 0, "each woven slice holds whole product pairs");
   using TL = Tile<D>;
-  bf16* q_lds = reinterpret_cast<bf16*>(smem);                 // [2][KV_BM * D]
-  bf16* do_lds = q_lds + 2 * KV_BM * D;                        // [2][KV_BM * D]
+  // three buffers: the pair being processed, the next one landing, and the one after it
+  // staged as soon as this pair starts (the buffer it overwrites was last read two pairs
+  // ago, before this pair's barrier)
+  bf16* q_lds = reinterpret_cast<bf16*>(smem);                 // [3][KV_BM * D]
+  bf16* do_lds = q_lds + 3 * KV_BM * D;                        // [3][KV_BM * D]
   // one extra 16-wide k-chunk per staged Q and dO row: (-LSE / scale) and (-Delta), each as
   // three bf16 terms (hi + mid + lo carry the fp32 value) and zeros; with K and V extended by
   // (1, 1, 1, 0 ...) the products give S - LSE / scale and dP - Delta directly, so the row
   // statistics are never broadcast to every lane through LDS
-  bf16* aug_lds = do_lds + 2 * KV_BM * D;                      // [Q', dO'][2 buffers][KV_BM][16]
+  bf16* aug_lds = do_lds + 3 * KV_BM * D;                      // [Q', dO'][3 buffers][KV_BM][16]
 
   const AttnShape& a = args.a;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -260,8 +263,8 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
   // by the thread that later writes its three terms (so no barrier orders the two)
   if (tid < 2 * KV_BM) {
     #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      bf16x8* z = reinterpret_cast<bf16x8*>(aug_lds + (((tid / KV_BM) * 2 + bb) * KV_BM + tid % KV_BM) * 16);
+    for (int bb = 0; bb < 3; ++bb) {
+      bf16x8* z = reinterpret_cast<bf16x8*>(aug_lds + (((tid / KV_BM) * 3 + bb) * KV_BM + tid % KV_BM) * 16);
       zero(z[0]);
       zero(z[1]);
     }
@@ -293,7 +296,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
       const bf16 hi = (bf16)c;
       const bf16 mid = (bf16)(c - (float)hi);
       const bf16 lo = (bf16)(c - (float)hi - (float)mid);
-      *reinterpret_cast<bf16x4*>(aug_lds + (((tid / KV_BM) * 2 + buf) * KV_BM + tid % KV_BM) * 16) =
+      *reinterpret_cast<bf16x4*>(aug_lds + (((tid / KV_BM) * 3 + buf) * KV_BM + tid % KV_BM) * 16) =
           bf16x4{hi, mid, lo, (bf16)0.f};
     }
   };
@@ -356,15 +359,28 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
   wait_vm();  // on every path: the K / V fragments are complete before the walk
   if (cur.p < npairs) store_stats(0);
   __syncthreads();
-  for (int it = 0; cur.p < npairs; ++it) {
-    const int buf = it & 1;
+  // the first block's S / dP operands (Q, dO rows and their augmented chunks) of the pair
+  // about to start, requested one pair ahead so that its products never wait on LDS
+  bf16x8 pqa[DS], pda[DS], pqx, pdx;
+  auto read_a0 = [&](int bb) {
+    #pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      pqa[s] = TL::read_chunk(q_lds + bb * KV_BM * D, r32, 2 * s + g);
+      pda[s] = TL::read_chunk(do_lds + bb * KV_BM * D, r32, 2 * s + g);
+    }
+    pqx = *reinterpret_cast<const bf16x8*>(aug_lds + bb * KV_BM * 16 + r32 * 16 + 8 * g);
+    pdx = *reinterpret_cast<const bf16x8*>(aug_lds + (3 + bb) * KV_BM * 16 + r32 * 16 + 8 * g);
+  };
+  if (cur.p < npairs) read_a0(0);
+  for (int it = 0, buf = 0; cur.p < npairs; ++it) {
+    const int nb = buf == 2 ? 0 : buf + 1;
     const Pos nxt = next_live(advance(cur));
     const bool more = nxt.p < npairs;
     ClassAhead cls_next{0u, kSelBias};
     uint64_t wb_next = ~0ull;
     if (more) {
       mask_state(nxt, cls_next, wb_next);
-      stage_pair(nxt, buf ^ 1);  // lands while this pair is being processed
+      stage_pair(nxt, nb);  // lands while this pair is being processed
     }
     int h, q0;
     pair_of(cur, h, q0);
@@ -374,7 +390,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     const bf16* qb_lds = q_lds + buf * KV_BM * D;
     const bf16* db_lds = do_lds + buf * KV_BM * D;
     const bf16* qx_lds = aug_lds + buf * KV_BM * 16;        // Q' rows of this pair
-    const bf16* dx_lds = aug_lds + (2 + buf) * KV_BM * 16;  // dO' rows
+    const bf16* dx_lds = aug_lds + (3 + buf) * KV_BM * 16;  // dO' rows
     bool edge = q0 + KV_BM > a.Sq || n0 + KV_BN > a.Sk;
     if (CAUSAL) edge = edge || ((int64_t)n0 + KV_BN - 1 > a.q_offset + q0);
     // Rows of the tile this lane's key can see, as a bit word (bit i: row q0 + i): the
@@ -398,29 +414,12 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     // The pair is two 32-row blocks, each in three steps: products S = Q K^T and
     // dP = dO V^T (A), the softmax gradient (B) and the products dV += P^T dO,
     // dK += dS^T Q (C). They run as A0, A1 with B0, C0 with B1, C1, so that each
-    // block's vector work (B) has the other block's matrix products beside it;
-    // masking is applied unconditionally (a no-op word on open blocks).
+    // block's vector work (B) has the other block's matrix products beside it; A0's
+    // operands were requested before the previous pair's C1. Masking is applied
+    // unconditionally (a no-op word on open blocks).
     // the augmented chunk of row 32 qb + r32 (half g: elements 8 g .. 8 g + 7)
     auto read_x = [&](const bf16* x_lds, int qb) {
       return *reinterpret_cast<const bf16x8*>(x_lds + (32 * qb + r32) * 16 + 8 * g);
-    };
-    auto step_a = [&](int qb, f32x16& sacc, f32x16& dpacc) {
-      bf16x8 qa[DS], da[DS];
-      #pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        qa[s] = TL::read_chunk(qb_lds, 32 * qb + r32, 2 * s + g);
-        da[s] = TL::read_chunk(db_lds, 32 * qb + r32, 2 * s + g);
-      }
-      const bf16x8 qx = read_x(qx_lds, qb), dx = read_x(dx_lds, qb);
-      sacc = zeros16();
-      dpacc = zeros16();
-      #pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        mma(sacc, qa[s], kf[s]);
-        mma(dpacc, da[s], vf[s]);
-      }
-      mma(sacc, qx, ones3);
-      mma(dpacc, dx, ones3);
     };
     // transpose reads of dO^T / Q^T for half hh of block qb (the operands of step C):
     // registers 8 hh .. 8 hh + 7 of the score accumulators hold rows
@@ -480,7 +479,15 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     };
     f32x16 s0, dp0, s1, dp1;
     bf16x8 pa0[2], ds0[2], pa1[2], ds1[2];
-    step_a(0, s0, dp0);
+    s0 = zeros16();  // step A of block 0 from the operands requested one pair ahead
+    dp0 = zeros16();
+    #pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      mma(s0, pqa[s], kf[s]);
+      mma(dp0, pda[s], vf[s]);
+    }
+    mma(s0, pqx, ones3);
+    mma(dp0, pdx, ones3);
     // Step A of block 1 woven with step B of block 0, then step C of block 0 woven with
     // step B of block 1: each two are independent, and one wave per SIMD only overlaps
     // vector work with matrix products when its instruction stream alternates them. Each
@@ -545,10 +552,14 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
         pack8(ds1[hh], dp1, 8 * hh);
       }
     }
-    step_c(1, pa1, ds1);
+    // the next pair's tiles are complete once every wave has waited for its own loads;
+    // its first block's operands are then requested before this pair's last products
     wait_vm();
-    if (more) store_stats(buf ^ 1);
+    if (more) store_stats(nb);
     __syncthreads();
+    if (more) read_a0(nb);
+    step_c(1, pa1, ds1);
+    buf = nb;
     cur = nxt;
     cls_cur = cls_next;
     wb_cur = wb_next;
@@ -813,7 +824,7 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
 // which keeps that code and its registers out of the common loop.
 template <int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(NT) void bwd_bf16_kernel(const BwdArgs args, const BwdPlan plan) {
-  constexpr int KV_LDS = 2 * 2 * KV_BM * D * 2 + 2 * 2 * KV_BM * 16 * 2;
+  constexpr int KV_LDS = 3 * 2 * KV_BM * D * 2 + 2 * 3 * KV_BM * 16 * 2;
   constexpr int Q_LDS = 2 * 2 * Q_BN * D * 2;
   __shared__ __attribute__((aligned(16))) char smem[KV_LDS > Q_LDS ? KV_LDS : Q_LDS];
   const int blk = blockIdx.x;
