@@ -187,6 +187,18 @@ def test_forward_splits(name, split):
     compare_full(c, {"O": host64(o), "LSE": host64(lse)}, {"O": O, "LSE": L}, names=("O", "LSE"))
 
 
+def test_forward_split_hint_ignored_for_fp32():
+    """The fp32 forward is never split: a split hint through the workspace entry point needs no
+    workspace and gives the unsplit results."""
+    c = CASES["f32_d64_gqa_mask"]()
+    t = upload(c)
+    assert binding.fwd_workspace_bytes(t["q"], t["k"], scale=c.scale, mask=t["mask"], split=3) == 0
+    o, lse = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, split=3)
+    o1, lse1 = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, split=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o1) and torch.equal(lse, lse1)
+
+
 @pytest.mark.parametrize("kv_split,q_split", [(1, 1), (3, 1), (1, 2), (2, 5)])
 @pytest.mark.parametrize("name", ["dit_sa_ragged", "lm_causal_gqa4", "random_bias_bcast", "d64_bf16"])
 def test_backward_decompositions(name, kv_split, q_split):
