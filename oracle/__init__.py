@@ -144,3 +144,35 @@ def cols(q, k, v, do, col_ids, mask=None, *, scale: float, causal: bool = False,
     if rc:
         raise ValueError(f"oracle rejected the problem (code {rc})")
     return out
+
+
+def structured_mask(B: int, Sq: int, Sk: int, *, key_len=None, q_len=None, window_left: int = -1,
+                    window_right: int = -1, q_offset: int = 0, causal: bool = False) -> np.ndarray:
+    """The dense additive mask [B, Sq, Sk] (0 / -inf) of a structured mask, entry by entry:
+    (b, i, j) is hidden when j >= key_len[b], when i >= q_len[b] (the whole row, which is
+    then fully masked), when window_left >= 0 and j < q_offset + i - window_left, when
+    window_right >= 0 and j > q_offset + i + window_right, or (causal) when j > q_offset + i.
+
+    This is the reading of the pages' DiT batch masks ("sa" = sliding window + padded key
+    columns, "sa_pad" = padded key columns) with the window as a band of explicit width on
+    each side of a row's position; the pages give no width. The result feeds forward() /
+    backward() like any dense mask."""
+    m = np.zeros((B, Sq, Sk), np.float64)
+    i = np.arange(Sq)[:, None]
+    j = np.arange(Sk)[None, :]
+    pos = q_offset + i
+    hidden = np.zeros((Sq, Sk), bool)
+    if window_left >= 0:
+        hidden |= j < pos - window_left
+    if window_right >= 0:
+        hidden |= j > pos + window_right
+    if causal:
+        hidden |= j > pos
+    for b in range(B):
+        h = hidden.copy()
+        if key_len is not None:
+            h |= j >= int(key_len[b])
+        if q_len is not None:
+            h |= np.broadcast_to(i >= int(q_len[b]), (Sq, Sk))
+        m[b][h] = -np.inf
+    return m

@@ -327,3 +327,64 @@ def test_sampled_rows_and_columns_match_full():
     cc = oracle.cols(q, k, v, do, cols, m, scale=c.scale, causal=True, q_offset=2)
     np.testing.assert_allclose(cc["dK"], full["dK"].reshape(-1, c.D)[cols], rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(cc["dV"], full["dV"].reshape(-1, c.D)[cols], rtol=1e-13, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# structured masks (key length, query length, sliding window): pinned to reductions
+# that do not use the structured definition (slicing, closed forms)
+# ---------------------------------------------------------------------------
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def test_structured_key_length_equals_sliced_keys():
+    B, H, Sq, Sk, D = 2, 2, 7, 9, 8
+    q, k, v, do = _rand((B, H, Sq, D), 1), _rand((B, H, Sk, D), 2), _rand((B, H, Sk, D), 3), _rand((B, H, Sq, D), 4)
+    klen = [5, 9]
+    m = oracle.structured_mask(B, Sq, Sk, key_len=klen)
+    ref = oracle.backward(q, k, v, do, m, scale=0.3)
+    for b in range(B):
+        kb = klen[b]
+        one = oracle.backward(q[b:b + 1], k[b:b + 1, :, :kb], v[b:b + 1, :, :kb], do[b:b + 1], scale=0.3)
+        for n in ("O", "LSE", "dQ"):
+            np.testing.assert_allclose(ref[n][b:b + 1], one[n], rtol=1e-12, atol=1e-12)
+        for n in ("dK", "dV"):
+            np.testing.assert_allclose(ref[n][b:b + 1, :, :kb], one[n], rtol=1e-12, atol=1e-12)
+            assert np.all(ref[n][b, :, kb:] == 0)  # keys past the length get nothing
+
+
+def test_structured_query_length_rows_are_fully_masked():
+    B, H, Sq, Sk, D = 2, 2, 6, 5, 8
+    q, k, v, do = _rand((B, H, Sq, D), 5), _rand((B, H, Sk, D), 6), _rand((B, H, Sk, D), 7), _rand((B, H, Sq, D), 8)
+    qlen = [6, 2]
+    ref = oracle.backward(q, k, v, do, oracle.structured_mask(B, Sq, Sk, q_len=qlen), scale=0.4)
+    b = 1
+    for n in ("O", "dQ"):
+        assert np.all(ref[n][b, :, 2:] == 0)
+    assert np.all(ref["LSE"][b, :, 2:] == 0)
+    one = oracle.backward(q[b:b + 1, :, :2], k[b:b + 1], v[b:b + 1], do[b:b + 1, :, :2], scale=0.4)
+    for n in ("dK", "dV"):  # the masked rows add nothing
+        np.testing.assert_allclose(ref[n][b:b + 1], one[n], rtol=1e-12, atol=1e-12)
+
+
+def test_structured_zero_width_window_closed_form():
+    # each row sees only the key at its own position: O_i = V_i, LSE_i = s <q_i, k_i>
+    B, H, S, D = 1, 2, 6, 8
+    q, k, v = _rand((B, H, S, D), 9), _rand((B, H, S, D), 10), _rand((B, H, S, D), 11)
+    m = oracle.structured_mask(B, S, S, window_left=0, window_right=0)
+    O, L = oracle.forward(q, k, v, m, scale=0.5)
+    np.testing.assert_allclose(O, v, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(L, 0.5 * np.einsum("bhsd,bhsd->bhs", q, k), rtol=1e-13, atol=1e-13)
+
+
+def test_structured_causal_window_equals_per_row_slices():
+    # a causal sliding window of w: row i sees keys max(0, i + off - w) .. i + off
+    B, H, Sq, Sk, D, w, off = 1, 2, 5, 9, 8, 3, 4
+    q, k, v = _rand((B, H, Sq, D), 12), _rand((B, H, Sk, D), 13), _rand((B, H, Sk, D), 14)
+    m = oracle.structured_mask(B, Sq, Sk, window_left=w, q_offset=off, causal=True)
+    O, L = oracle.forward(q, k, v, m, scale=0.25, causal=True, q_offset=off)
+    for i in range(Sq):
+        lo, hi = max(0, i + off - w), i + off + 1
+        Oi, Li = oracle.forward(q[:, :, i:i + 1], k[:, :, lo:hi], v[:, :, lo:hi], scale=0.25)
+        np.testing.assert_allclose(O[:, :, i], Oi[:, :, 0], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(L[:, :, i], Li[:, :, 0], rtol=1e-12, atol=1e-12)
