@@ -33,7 +33,8 @@ class FaAttnParams(ctypes.Structure):
                 ("q_offset", ctypes.c_int64), ("scale", ctypes.c_float), ("mask", ctypes.c_void_p),
                 ("mask_stride_b", ctypes.c_int64), ("mask_stride_q", ctypes.c_int64), ("mask_tiles", ctypes.c_void_p),
                 ("fwd_variant", ctypes.c_int32), ("kv_split", ctypes.c_int32), ("q_split", ctypes.c_int32),
-                ("fwd_split", ctypes.c_int32)]
+                ("fwd_split", ctypes.c_int32), ("key_len", ctypes.c_void_p), ("q_len", ctypes.c_void_p),
+                ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32)]
 
 
 class FaError(RuntimeError):
@@ -118,7 +119,9 @@ def _stream_handle(stream) -> int:
 
 def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], causal: bool,
                 q_offset: Optional[int], mask: Optional[torch.Tensor], fwd_variant: int = 0, kv_split: int = 0,
-                q_split: int = 0, mask_tiles: Optional[torch.Tensor] = None, fwd_split: int = 0) -> FaAttnParams:
+                q_split: int = 0, mask_tiles: Optional[torch.Tensor] = None, fwd_split: int = 0,
+                key_len: Optional[torch.Tensor] = None, q_len: Optional[torch.Tensor] = None,
+                window: tuple = (-1, -1)) -> FaAttnParams:
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Sk, Dk = k.shape
     if Bk != B or Dk != D:
@@ -128,7 +131,13 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
     if q_offset is None:
         q_offset = Sk - Sq if causal else 0
     p = FaAttnParams(B, Hq, Hkv, Sq, Sk, D, _dtype_code(q), int(bool(causal)), int(q_offset), float(scale),
-                     None, 0, 0, None, int(fwd_variant), int(kv_split), int(q_split), int(fwd_split))
+                     None, 0, 0, None, int(fwd_variant), int(kv_split), int(q_split), int(fwd_split), None, None,
+                     int(window[0]), int(window[1]))
+    for name, t, n in (("key_len", key_len, B), ("q_len", q_len, B)):
+        if t is not None:
+            if t.dtype != torch.int32 or t.dim() != 1 or t.shape[0] != n or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous int32 [B] tensor on the device")
+            setattr(p, name, t.data_ptr())
     if mask is not None:
         if mask.dtype != torch.float32 or mask.dim() != 3 or mask.stride(2) != 1:
             raise ValueError("mask must be an fp32 [Bm, Sq, Sk] tensor with a contiguous last dimension")
@@ -170,18 +179,20 @@ def mask_tile_count(mask: torch.Tensor) -> int:
     return Bm * ((Sq + 63) // 64) * ((Sk + 63) // 64)
 
 
-def fwd_workspace_bytes(q, k, *, scale=None, causal=False, q_offset=None, mask=None, split=0) -> int:
-    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, fwd_split=split)
+def fwd_workspace_bytes(q, k, *, scale=None, causal=False, q_offset=None, mask=None, split=0, key_len=None,
+                        q_len=None, window=(-1, -1)) -> int:
+    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, fwd_split=split,
+                    key_len=key_len, q_len=q_len, window=window)
     return int(lib().fa_train_fwd_workspace_bytes(ctypes.byref(p)))
 
 
 def fwd(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, out=None, lse=None, stream=None,
-        variant=0, mask_tiles=None, workspace=None, split=0):
+        variant=0, mask_tiles=None, workspace=None, split=0, key_len=None, q_len=None, window=(-1, -1)):
     """Forward: returns (O, LSE). O has q's dtype and shape; LSE is fp32 [B, Hq, Sq].
     Runs fa_train_fwd_ws: a short grid may split the key walks (split = 0: the library's
     choice; 1: never), with `workspace` (allocated here when None and needed)."""
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, fwd_variant=variant,
-                    mask_tiles=mask_tiles, fwd_split=split)
+                    mask_tiles=mask_tiles, fwd_split=split, key_len=key_len, q_len=q_len, window=window)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
@@ -209,9 +220,10 @@ def bwd_preprocess(o, dout, *, delta=None, stream=None):
     return delta
 
 
-def bwd_workspace_bytes(q, k, *, scale=None, causal=False, q_offset=None, mask=None, kv_split=0, q_split=0) -> int:
+def bwd_workspace_bytes(q, k, *, scale=None, causal=False, q_offset=None, mask=None, kv_split=0, q_split=0,
+                        key_len=None, q_len=None, window=(-1, -1)) -> int:
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
-                    q_split=q_split)
+                    q_split=q_split, key_len=key_len, q_len=q_len, window=window)
     return int(lib().fa_train_bwd_workspace_bytes(ctypes.byref(p)))
 
 
@@ -225,10 +237,11 @@ def _workspace(p: FaAttnParams, device, workspace):
 
 
 def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_offset=None, dq=None, dk=None,
-        dv=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None):
+        dv=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None, q_len=None,
+        window=(-1, -1)):
     """Backward: returns (dQ, dK, dV), each in q's dtype, overwritten."""
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
-                    q_split=q_split, mask_tiles=mask_tiles)
+                    q_split=q_split, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, window=window)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
@@ -243,7 +256,8 @@ BWD_SPLIT_CANDIDATES = ((0, 0), (1, 1), (2, 1), (4, 1), (8, 1), (1, 2), (2, 2), 
 
 
 def tune_bwd_splits(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_offset=None,
-                    mask_tiles=None, candidates=BWD_SPLIT_CANDIDATES, reps=5, rounds=3, stream=None):
+                    mask_tiles=None, candidates=BWD_SPLIT_CANDIDATES, reps=5, rounds=3, stream=None, key_len=None,
+                    q_len=None, window=(-1, -1)):
     """Times the backward on these inputs for each (kv_split, q_split) candidate ((0, 0):
     the library's own choice) and returns the fastest pair: `rounds` passes over the
     candidates, interleaved, each candidate keeping its best pass of `reps` calls. The
@@ -255,14 +269,15 @@ def tune_bwd_splits(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=
     s = torch.cuda.current_stream() if stream is None else stream
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     need = max(bwd_workspace_bytes(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv,
-                                   q_split=qs) for kv, qs in candidates)
+                                   q_split=qs, key_len=key_len, q_len=q_len, window=window) for kv, qs in candidates)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     best = {}
     for _ in range(rounds):
         for kv, qs in candidates:
             def call():
                 bwd(q, k, v, dout, lse, delta, mask=mask, scale=scale, causal=causal, q_offset=q_offset, dq=dq,
-                    dk=dk, dv=dv, workspace=ws, stream=s, kv_split=kv, q_split=qs, mask_tiles=mask_tiles)
+                    dk=dk, dv=dv, workspace=ws, stream=s, kv_split=kv, q_split=qs, mask_tiles=mask_tiles,
+                    key_len=key_len, q_len=q_len, window=window)
             call()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(s)
@@ -276,11 +291,13 @@ def tune_bwd_splits(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=
 
 
 def bwd_chunked(q, k, v, dout, lse, delta, dk_acc, dv_acc, *, mask=None, scale=None, causal=True, q_offset=None,
-                dq=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None):
+                dq=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None,
+                q_len=None, window=(-1, -1)):
     """Chunked backward: returns dQ for the chunk; ADDS dK/dV into the fp32 window
     accumulators ``dk_acc`` / ``dv_acc`` ([B, Hkv, >= Sk, D])."""
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
-                    q_split=q_split, mask_tiles=mask_tiles)
+                    q_split=q_split, mask_tiles=mask_tiles, key_len=key_len,
+                    q_len=q_len, window=window)
     if dk_acc.dtype != torch.float32 or dv_acc.dtype != torch.float32:
         raise TypeError("the window accumulators must be float32")
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq

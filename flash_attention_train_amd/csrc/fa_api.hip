@@ -88,6 +88,12 @@ fa_status check_params(const fa_attn_params* p) {
   if (p->kv_split < 0 || p->kv_split > 64 || p->q_split < 0 || p->q_split > 64 || p->fwd_split < 0 ||
       p->fwd_split > 64)
     return fail(FA_ERR_SHAPE, "split hints must be in 0 .. 64");
+  if (p->window_left < -1 || p->window_right < -1) return fail(FA_ERR_SHAPE, "window bounds must be >= -1");
+  if (reinterpret_cast<uintptr_t>(p->key_len) % 4 || reinterpret_cast<uintptr_t>(p->q_len) % 4)
+    return fail(FA_ERR_ALIGN, "key_len / q_len are not 4-byte aligned");
+  const bool structured = p->key_len || p->q_len || p->window_left >= 0 || p->window_right >= 0;
+  if (structured && p->dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "structured masks (key_len, q_len, window) are implemented for bf16 only");
   if (p->mask) {
     if (p->mask_stride_q < p->Sk) return fail(FA_ERR_STRIDE, "mask_stride_q (%lld) < Sk", (long long)p->mask_stride_q);
     if (p->mask_stride_b < 0) return fail(FA_ERR_STRIDE, "mask_stride_b is negative");
@@ -128,6 +134,10 @@ fa::AttnShape shape_of(const fa_attn_params* p) {
   a.colbits = a.tiles ? a.rowbits + nblk * 64 : nullptr;
   a.tiles_ncol = (int)tile_cols(p);
   a.tiles_bstride = p->mask_stride_b == 0 ? 0 : (int)(tile_rows(p) * tile_cols(p));
+  a.key_len = p->key_len;
+  a.q_len = p->q_len;
+  a.wl = p->window_left;
+  a.wr = p->window_right;
   return a;
 }
 
@@ -414,6 +424,10 @@ int choose_fwd_split(const fa_attn_params* p) {
   if (p->causal) {  // the longest walk: the last query tile's
     const int64_t last_key = p->q_offset + p->Sq - 1;
     nkt = last_key < 0 ? 0 : std::min<int64_t>(last_key / 64 + 1, nkt);
+  }
+  if (p->window_left >= 0) {  // a band: a 128-row workgroup sees at most its rows' spans
+    const int64_t right = p->window_right >= 0 ? p->window_right : (p->causal ? 0 : p->Sk);
+    nkt = std::min<int64_t>(nkt, (p->window_left + right + 128) / 64 + 2);
   }
   if (p->fwd_split) return (int)std::max<int64_t>(1, std::min<int64_t>(p->fwd_split, std::max<int64_t>(nkt, 1)));
   if (wgs >= 256) return 1;

@@ -229,15 +229,33 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     dv[db] = zeros16();
   }
 
-  // the (head, query tile) pairs this workgroup walks: query tiles qt0 .. nqt - 1 of
-  // every head of the group, pair p = (qt - qt0) * G + (h - hk G), p = split (mod kv_split)
-  const int nqt = (a.Sq + KV_BM - 1) / KV_BM;
-  int qt0 = 0;
-  if (CAUSAL) {
-    const int64_t first_row = (int64_t)n0 - a.q_offset;  // rows i >= n0 - q_offset see a key here
-    qt0 = first_row <= 0 ? 0 : (int)((first_row / KV_BM) < nqt ? first_row / KV_BM : nqt);
+  // the rows the structure lets see any of the unit's keys (sequence ends, causal diagonal,
+  // key and query lengths, window): from the first key's lower end to the last live key's
+  // upper end (both ends move down with the key)
+  const int klen = klen_of(a, b), qlen = qlen_of(a, b);
+  int qt0 = 0, qt_end = 0;
+  if (n0 < klen) {
+    int64_t lo, hi, lo1, hi1;
+    row_range(a, klen, qlen, n0, lo, hi);
+    row_range(a, klen, qlen, min(n0 + KV_BN, klen) - 1, lo1, hi1);
+    const int nqt = (a.Sq + KV_BM - 1) / KV_BM;
+    qt0 = (int)min<int64_t>(lo / KV_BM, nqt);
+    qt_end = hi1 > lo ? (int)min<int64_t>((hi1 + KV_BM - 1) / KV_BM, nqt) : qt0;
+    if (qt_end < qt0) qt_end = qt0;
   }
-  const int npairs = (nqt - qt0) * a.G;
+  // the rows every key of the unit sees: a pair tile outside [r_lo, r_hi) needs masking
+  // (as 32-bit row numbers: row bounds lie in [0, Sq])
+  int r_lo, r_hi;
+  {
+    int64_t l0, h0, l1, h1;
+    row_range(a, klen, qlen, n0, l0, h0);
+    row_range(a, klen, qlen, n0 + KV_BN - 1, l1, h1);
+    r_lo = (int)min<int64_t>(l1, a.Sq);
+    r_hi = n0 + KV_BN > klen ? r_lo : (int)min<int64_t>(h0, a.Sq);  // keys past the length see nothing
+  }
+  // the (head, query tile) pairs this workgroup walks: query tiles qt0 .. qt_end - 1 of
+  // every head of the group, pair p = (qt - qt0) * G + (h - hk G), p = split (mod kv_split)
+  const int npairs = (qt_end - qt0) * a.G;
 
   // Pair p is (query tile qt0 + p / G, head hk G + p % G); this workgroup walks
   // p = split, split + kv_split, ..., carried as a running (quotient, remainder) so that
@@ -391,23 +409,20 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     const bf16* db_lds = do_lds + buf * KV_BM * D;
     const bf16* qx_lds = aug_lds + buf * KV_BM * 16;        // Q' rows of this pair
     const bf16* dx_lds = aug_lds + (3 + buf) * KV_BM * 16;  // dO' rows
-    bool edge = q0 + KV_BM > a.Sq || n0 + KV_BN > a.Sk;
-    if (CAUSAL) edge = edge || ((int64_t)n0 + KV_BN - 1 > a.q_offset + q0);
+    const bool edge = !(q0 >= r_lo && q0 + KV_BM <= r_hi);
     // Rows of the tile this lane's key can see, as a bit word (bit i: row q0 + i): the
-    // sequence tail, the causal diagonal and the block's visibility bits (none for a
-    // dead block, whose products then contribute exact zeros: skipping them per wave
-    // costs more in registers than it saves).
+    // structure (sequence ends, lengths, causal diagonal, window) and the block's
+    // visibility bits (none for a dead block, whose products then contribute exact
+    // zeros: skipping them per wave costs more in registers than it saves).
     const bool dead = MASK && cls == kTileDead;
     const bool masked = edge || bits || dead;
     uint64_t vis = dead ? 0ull : ~0ull;
     if (masked && !dead) {
-      int qlo = 0;
-      const int qhi = key < a.Sk ? min(a.Sq - q0, KV_BM) : 0;
-      if (CAUSAL) {
-        const int64_t lo = (int64_t)key - a.q_offset - q0;  // key <= q_offset + row
-        qlo = (int)(lo < 0 ? 0 : (lo > KV_BM ? KV_BM : lo));
-      }
-      vis = bit_range64(qlo, qhi);
+      int64_t lo, hi;
+      row_range(a, klen, qlen, key, lo, hi);
+      lo -= q0;
+      hi -= q0;
+      vis = bit_range64((int)(lo < 0 ? 0 : (lo > KV_BM ? KV_BM : lo)), (int)(hi < 0 ? 0 : (hi > KV_BM ? KV_BM : hi)));
       if (bits) vis &= wb_cur;
     }
 
@@ -631,11 +646,30 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
   #pragma unroll
   for (int db = 0; db < DB; ++db) dq[db] = zeros16();
 
+  // keys the workgroup's rows can see by the structure (sequence ends, causal diagonal,
+  // key and query lengths, window): from the first row's lower end to the last visible
+  // row's upper end (both ends move right with the row)
+  const int klen = klen_of(a, b), qlen = qlen_of(a, b);
   const int nkt = (a.Sk + Q_BN - 1) / Q_BN;
-  int kt_end = nkt;
-  if (CAUSAL) {
-    const int64_t last_key = a.q_offset + q0 + Q_BM - 1;
-    kt_end = last_key < 0 ? 0 : (int)((last_key / Q_BN + 1) < nkt ? (last_key / Q_BN + 1) : nkt);
+  int kt_begin = 0, kt_end = 0;
+  if (q0 < qlen) {
+    int64_t lo, hi, lo1, hi1;
+    key_range(a, klen, qlen, q0, lo, hi);
+    key_range(a, klen, qlen, min(q0 + Q_BM, qlen) - 1, lo1, hi1);
+    kt_begin = (int)min<int64_t>(lo / Q_BN, nkt);
+    kt_end = hi1 > lo ? (int)min<int64_t>((hi1 + Q_BN - 1) / Q_BN, nkt) : kt_begin;
+    if (kt_end < kt_begin) kt_end = kt_begin;
+  }
+  // the keys every row of the wave sees: a key tile outside [w_lo, w_hi) needs masking
+  // (as 32-bit key numbers: key bounds lie in [0, Sk])
+  int w_lo, w_hi;
+  {
+    int64_t l0, h0, l1, h1;
+    key_range(a, klen, qlen, qw, l0, h0);
+    key_range(a, klen, qlen, qw + 31, l1, h1);
+    w_lo = (int)min<int64_t>(l1, a.Sk);
+    // rows in [qlen, Sq) see nothing (rows past Sq are never stored)
+    w_hi = (qlen < a.Sq && qw + 32 > qlen) ? w_lo : (int)min<int64_t>(h0, a.Sk);
   }
 
   // stage K and V rows [key0, key0 + Q_BN) straight into LDS (keys past the end repeat
@@ -651,21 +685,22 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
 
   // mask tile map: skip key tiles dead for both 64-row blocks of this workgroup
   const int nrt = (a.Sq + kMaskTile - 1) / kMaskTile;
-  // candidate j: key tile split + j q_split
+  // candidate j: key tile kt_begin + split + j q_split
   auto live = [&](int j) -> bool {
-    const int k = split + j * plan.q_split;
+    const int k = kt_begin + split + j * plan.q_split;
     for (int rt = q0 / kMaskTile; rt <= (q0 + Q_BM - 1) / kMaskTile && rt < nrt; ++rt)
       if (tile_class(a, b, rt, k) != kTileDead) return true;  // Q_BN = kMaskTile: key tile = block
     return false;
   };
   __shared__ uint64_t live_lds[kBwdWaves];
   LiveWords lw{live_lds, -NT};
-  const int ncand = kt_end > split ? (kt_end - split + plan.q_split - 1) / plan.q_split : 0;
+  const int nwalk = kt_end - kt_begin;
+  const int ncand = nwalk > split ? (nwalk - split + plan.q_split - 1) / plan.q_split : 0;
   auto next_live = [&](int j) {  // candidate j -> the first live one from j (ncand: none)
     if (j >= ncand) return ncand;
     return MASK && a.tiles ? lw.next(j, ncand, tid, live) : j;
   };
-  auto tile_of = [&](int j) { return j < ncand ? split + j * plan.q_split : kt_end; };
+  auto tile_of = [&](int j) { return j < ncand ? kt_begin + split + j * plan.q_split : kt_end; };
   const int rt_w = qw / kMaskTile;
 
   // per-tile mask state of this wave, fetched one tile ahead: the block class and this
@@ -709,22 +744,20 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
     const bf16* kb_lds = k_lds + buf * Q_BN * D;
     const bf16* vb_lds = v_lds + buf * Q_BN * D;
     const int key0 = kt * Q_BN;
-    bool edge = key0 + Q_BN > a.Sk || qw + 32 > a.Sq;
-    if (CAUSAL) edge = edge || ((int64_t)key0 + Q_BN - 1 > a.q_offset + qw);
+    const bool edge = !(key0 >= w_lo && key0 + Q_BN <= w_hi);
     // Keys of the tile this lane's row can see, as a bit word (bit j: key key0 + j):
-    // the sequence tail, the causal diagonal and the block's visibility bits (none for
-    // a dead block, computed to exact zeros like in the dK/dV walk). Blocks with none
-    // of these (wave-uniform `masked` false) skip the masking altogether.
+    // the structure (sequence ends, lengths, causal diagonal, window) and the block's
+    // visibility bits (none for a dead block, computed to exact zeros like in the dK/dV
+    // walk). Blocks with none of these (wave-uniform `masked` false) skip the masking.
     const bool dead = MASK && cls == kTileDead;
     const bool masked = edge || bits || dead;
     uint64_t vis = dead ? 0ull : ~0ull;
     if (masked && !dead) {
-      int64_t kl64 = row < a.Sq ? (int64_t)a.Sk - key0 : 0;
-      if (CAUSAL) {
-        const int64_t c = a.q_offset + row + 1 - key0;
-        kl64 = c < kl64 ? c : kl64;
-      }
-      vis = bit_range64(0, (int)(kl64 < 0 ? 0 : (kl64 > Q_BN ? Q_BN : kl64)));
+      int64_t lo, hi;
+      key_range(a, klen, qlen, row, lo, hi);
+      lo -= key0;
+      hi -= key0;
+      vis = bit_range64((int)(lo < 0 ? 0 : (lo > Q_BN ? Q_BN : lo)), (int)(hi < 0 ? 0 : (hi > Q_BN ? Q_BN : hi)));
       if (bits) vis &= wb_cur;
     }
 

@@ -98,16 +98,34 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     lsum[qb] = 0.f;
   }
 
+  // keys the workgroup's rows can see by the structure (sequence ends, causal diagonal,
+  // key and query lengths, window): from the first row's lower end to the last visible
+  // row's upper end (both ends move right with the row)
+  const int klen = klen_of(a, b), qlen = qlen_of(a, b);
   const int nkt = (a.Sk + BN - 1) / BN;
-  int kt_end = nkt;
-  if (CAUSAL) {
-    const int64_t last_key = a.q_offset + q0 + BM - 1;
-    kt_end = last_key < 0 ? 0 : (int)((last_key / BN + 1) < nkt ? (last_key / BN + 1) : nkt);
+  int kt_begin = 0, kt_end = 0;
+  if (q0 < qlen) {
+    int64_t lo, hi, lo1, hi1;
+    key_range(a, klen, qlen, q0, lo, hi);
+    key_range(a, klen, qlen, min(q0 + BM, qlen) - 1, lo1, hi1);
+    kt_begin = (int)min<int64_t>(lo / BN, nkt);
+    kt_end = hi1 > lo ? (int)min<int64_t>((hi1 + BN - 1) / BN, nkt) : 0;
+    if (kt_end < kt_begin) kt_end = kt_begin;
   }
-  int kt_begin = 0;
-  if constexpr (SPLIT) {  // this workgroup's share of [0, kt_end)
-    const int per = (kt_end + (int)gridDim.z - 1) / (int)gridDim.z;
-    kt_begin = min(kt_end, (int)blockIdx.z * per);
+  // the wave's rows: every key tile outside [w_lo, w_hi) needs per-element masking
+  // (as 32-bit key numbers: key bounds lie in [0, Sk])
+  int w_lo, w_hi;
+  {
+    int64_t l0, h0, l1, h1;
+    key_range(a, klen, qlen, qw, l0, h0);
+    key_range(a, klen, qlen, qw + QB * 32 - 1, l1, h1);
+    w_lo = (int)min<int64_t>(l1, a.Sk);  // the largest lower end
+    // rows in [qlen, Sq) see nothing (rows past Sq are never stored)
+    w_hi = (qlen < a.Sq && qw + QB * 32 > qlen) ? w_lo : (int)min<int64_t>(h0, a.Sk);
+  }
+  if constexpr (SPLIT) {  // this workgroup's share of [kt_begin, kt_end)
+    const int per = (kt_end - kt_begin + (int)gridDim.z - 1) / (int)gridDim.z;
+    kt_begin = min(kt_end, kt_begin + (int)blockIdx.z * per);
     kt_end = min(kt_end, kt_begin + per);
   }
 
@@ -236,10 +254,10 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
       }
     }
 
-    // does this tile need per-element masking (sequence tail / causal diagonal / bits)?
+    // does this tile need per-element masking (structure: sequence tail, causal diagonal,
+    // lengths, window; or the block's bits)?
     const int key0 = kt * BN;
-    bool edge = key0 + BN > a.Sk;
-    if (CAUSAL) edge = edge || ((int64_t)key0 + BN - 1 > a.q_offset + qw);
+    const bool edge = !(key0 >= w_lo && key0 + BN <= w_hi);
     const bool masked = edge || bits;
 
     bf16x8 pf[QB][KB][2];
@@ -271,12 +289,11 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
       if (masked) {
         // keys of the tile this lane's row can see (bit j: key key0 + j); masked scores
         // become -inf (bit-field insert of -inf under a sign-extended bit: two VALU ops)
-        int64_t l = (int64_t)a.Sk - key0;
-        if (CAUSAL) {
-          const int64_t c = a.q_offset + row + 1 - key0;
-          l = c < l ? c : l;
-        }
-        uint64_t vis = bit_range64(0, (int)(l < 0 ? 0 : (l > BN ? BN : l)));
+        int64_t lo, hi;
+        key_range(a, klen, qlen, row, lo, hi);
+        lo -= key0;
+        hi -= key0;
+        uint64_t vis = bit_range64((int)(lo < 0 ? 0 : (lo > BN ? BN : lo)), (int)(hi < 0 ? 0 : (hi > BN ? BN : hi)));
         if (bits) vis &= BN == 64 ? wb_cur[qb] : (wb_cur[qb] >> (key0 % kMaskTile));
         #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {

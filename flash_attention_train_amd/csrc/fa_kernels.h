@@ -28,7 +28,42 @@ struct AttnShape {
   const uint64_t* colbits;   // per block, 64 words: bit i of word j = entry (i, j) visible
   int tiles_bstride;         // blocks per mask batch entry (0 when the mask is shared)
   int tiles_ncol;            // ceil(Sk / 64)
+  // structured masks: entry (b, i, j) is hidden when j >= klen(b), i >= qlen(b),
+  // j < q_offset + i - wl (wl >= 0) or j > q_offset + i + wr (wr >= 0)
+  const int32_t* key_len;    // [B] or nullptr (Sk)
+  const int32_t* q_len;      // [B] or nullptr (Sq)
+  int wl, wr;                // window bounds, -1: none
 };
+
+// the structured lengths of batch entry b (clamped to the tensor lengths)
+__device__ __forceinline__ int klen_of(const AttnShape& a, int b) {
+  return a.key_len ? min(max(a.key_len[b], 0), a.Sk) : a.Sk;
+}
+__device__ __forceinline__ int qlen_of(const AttnShape& a, int b) {
+  return a.q_len ? min(max(a.q_len[b], 0), a.Sq) : a.Sq;
+}
+// keys [lo, hi) that query row i can see by the structure alone (sequence ends, key length,
+// causal diagonal, window); empty when the row is past the query length
+__device__ __forceinline__ void key_range(const AttnShape& a, int klen, int qlen, int64_t i, int64_t& lo,
+                                          int64_t& hi) {
+  const int64_t pos = a.q_offset + i;
+  lo = a.wl >= 0 ? pos - a.wl : 0;
+  hi = klen;
+  if (a.causal && pos + 1 < hi) hi = pos + 1;
+  if (a.wr >= 0 && pos + a.wr + 1 < hi) hi = pos + a.wr + 1;
+  if (lo < 0) lo = 0;
+  if (i >= qlen || hi < lo) hi = lo;
+}
+// rows [lo, hi) that can see key j by the structure alone
+__device__ __forceinline__ void row_range(const AttnShape& a, int klen, int qlen, int64_t j, int64_t& lo,
+                                          int64_t& hi) {
+  lo = 0;
+  hi = qlen;
+  if (a.causal && j - a.q_offset > lo) lo = j - a.q_offset;            // j <= q_offset + i
+  if (a.wr >= 0 && j - a.q_offset - a.wr > lo) lo = j - a.q_offset - a.wr;
+  if (a.wl >= 0 && j - a.q_offset + a.wl + 1 < hi) hi = j - a.q_offset + a.wl + 1;  // j >= q_offset + i - wl
+  if (j >= klen || hi < lo) hi = lo;
+}
 
 // block classes: dead = all -inf, open = all 0, bits = only 0 / -inf, bias = finite biases
 constexpr int kTileDead = 0, kTileOpen = 1, kTileBits = 2, kTileBias = 3, kMaskTile = 64;

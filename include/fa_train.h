@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FA_TRAIN_ABI_VERSION 2
+#define FA_TRAIN_ABI_VERSION 3
 
 typedef enum fa_status {
     FA_OK = 0,
@@ -116,6 +116,17 @@ typedef struct fa_attn_params {
                              128-row query tile's key walk, 1 .. 64 (> 1: each stores its
                              unnormalised fp32 rows in the workspace and a merge pass
                              combines them). fa_train_fwd never splits and rejects > 1. */
+    /* Structured masks (bf16 only; they combine with causal and with a dense mask): the
+     * per-element padding and sliding-window masks of the pages' DiT batches ("sa" =
+     * sliding window + padded key columns, "sa_pad" = padded key columns) without a
+     * dense tensor. Entry (b, i, j) is hidden when j >= key_len[b], when i >= q_len[b]
+     * (the row is then fully masked: O = 0, LSE = 0, dQ = 0, and it adds nothing to dK,
+     * dV), when j < q_offset + i - window_left, or when j > q_offset + i + window_right. */
+    const int32_t* key_len;  /* device [B] int32, each in [0, Sk] (clamped); NULL = Sk */
+    const int32_t* q_len;    /* device [B] int32, each in [0, Sq] (clamped); NULL = Sq */
+    int32_t window_left;     /* >= 0: keys at most this far before a row's position q_offset + i;
+                                -1: no bound */
+    int32_t window_right;    /* >= 0: keys at most this far after it; -1: no bound */
 } fa_attn_params;
 
 /* Forward: writes O (dtype) and LSE (fp32, natural log). Fully masked rows get

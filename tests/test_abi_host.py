@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(L, n), n
         assert n in B.SIGNATURES, f"{n} has no ctypes signature in the binding"
-    assert L.fa_train_version() == 2
+    assert L.fa_train_version() == 3
 
 
 BASE = 0x7F0000000000  # fake, 256-byte aligned device addresses
@@ -42,7 +42,8 @@ BASE = 0x7F0000000000  # fake, 256-byte aligned device addresses
 
 def params(**kw):
     a = dict(B=1, Hq=4, Hkv=2, Sq=64, Sk=64, D=64, dtype=B.FA_BF16, causal=0, q_offset=0, scale=0.125, mask=None,
-             mask_stride_b=0, mask_stride_q=0, mask_tiles=None, fwd_variant=0, kv_split=0, q_split=0, fwd_split=0)
+             mask_stride_b=0, mask_stride_q=0, mask_tiles=None, fwd_variant=0, kv_split=0, q_split=0, fwd_split=0, key_len=None, q_len=None,
+             window_left=-1, window_right=-1)
     a.update(kw)
     return B.FaAttnParams(*(a[f] for f, _ in B.FaAttnParams._fields_))
 
@@ -83,6 +84,10 @@ FWD_ERRORS = [
     ("negative scale", params(scale=-0.5), {}, 2),
     ("unknown forward variant", params(fwd_variant=9), {}, 2),
     ("split out of range", params(kv_split=65), {}, 2),
+    ("window bound -2", params(window_left=-2), {}, 2),
+    ("misaligned key_len", params(key_len=BASE + 2), {}, 5),
+    ("structured mask on fp32", params(dtype=B.FA_F32, key_len=BASE), {}, 7),
+    ("window on fp32", params(dtype=B.FA_F32, window_right=3), {}, 7),
     ("mask stride too small", params(mask=BASE + 9 * (1 << 24), mask_stride_q=32), {}, 4),
     ("row stride 2^24", params(), {"k": view(1, H=2, stride_s=1 << 24, stride_h=(1 << 24) * 64,
                                                 stride_b=(1 << 24) * 128)}, 4),
