@@ -10,7 +10,7 @@ S=1542, D=128, bf16, pad mask): mask-adjusted fwd+bwd TFLOP/s (14 * D * N FLOPs
 per step, N = unmasked score pairs). Other workloads are reported under "extra".
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload dit_sa]
-                    [--extra lm_causal,dit_ca] [--no-cpu-baseline]
+                    [--extra lm_causal,dit_ca,long_window,dit_sa_len,dit_sa_band] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dit_sa")
-    ap.add_argument("--extra", default="lm_causal,dit_ca,long_window",
+    ap.add_argument("--extra", default="lm_causal,dit_ca,long_window,dit_sa_len,dit_sa_band",
                     help="other workloads to time, comma separated ('none' for none); long_window is the "
                          "64-chunk walk over a 32768-long window")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -70,6 +70,13 @@ class Workload:
 
         self.q, self.k, self.v, self.do = up(c.q), up(c.k), up(c.v), up(c.do)
         self.mask = None if c.mask is None else torch.from_numpy(c.mask).to(dev)
+        # a structured mask (key / query lengths as device arrays, a window): given to every call
+        st = c.meta.get("structure")
+        self.sk = {}
+        if st is not None:
+            for n in ("key_len", "q_len"):
+                self.sk[n] = None if st[n] is None else torch.tensor(st[n], dtype=torch.int32, device=dev)
+            self.sk["window"] = tuple(st["window"])
         self.o = torch.empty_like(self.q)
         self.lse = torch.empty(c.B, c.Hq, c.Sq, dtype=torch.float32, device=dev)
         self.delta = torch.empty_like(self.lse)
@@ -82,7 +89,7 @@ class Workload:
             self.tiles = binding.mask_tile_map(self.mask, self.q, self.k)  # sized once, refilled every step
         # forward workspace: the split-key walk's partial rows when the grid is short
         self.fws_bytes = binding.fwd_workspace_bytes(self.q, self.k, scale=c.scale, causal=c.causal,
-                                                     q_offset=c.q_offset, mask=self.mask)
+                                                     q_offset=c.q_offset, mask=self.mask, **self.sk)
         self.fws = torch.empty(max(self.fws_bytes, 256), dtype=torch.uint8, device=dev)
         self.fwd_split = self.fws_bytes // (4 * c.B * c.Hq * c.Sq * (c.D + 2)) if self.fws_bytes else 1
         # backward split: the library's cost model, or (tune) the fastest of a few
@@ -101,9 +108,9 @@ class Workload:
             self.pre()
             self.kv_split, self.q_split = binding.tune_bwd_splits(
                 self.q, self.k, self.v, self.do, self.lse, self.delta, mask=self.mask, scale=c.scale,
-                causal=c.causal, q_offset=c.q_offset, mask_tiles=self.tiles)
+                causal=c.causal, q_offset=c.q_offset, mask_tiles=self.tiles, **self.sk)
         nws = binding.bwd_workspace_bytes(self.q, self.k, scale=c.scale, causal=c.causal, q_offset=c.q_offset,
-                                          mask=self.mask, kv_split=self.kv_split, q_split=self.q_split)
+                                          mask=self.mask, kv_split=self.kv_split, q_split=self.q_split, **self.sk)
         self.ws_bytes = nws
         self.ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
 
@@ -116,7 +123,7 @@ class Workload:
     def fwd(self):
         c = self.case
         self.B.fwd(self.q, self.k, self.v, mask=self.mask, scale=c.scale, causal=c.causal, q_offset=c.q_offset,
-                   out=self.o, lse=self.lse, mask_tiles=self.tiles, workspace=self.fws)
+                   out=self.o, lse=self.lse, mask_tiles=self.tiles, workspace=self.fws, **self.sk)
 
     def pre(self):
         self.B.bwd_preprocess(self.o, self.do, delta=self.delta)
@@ -125,7 +132,7 @@ class Workload:
         c = self.case
         self.B.bwd(self.q, self.k, self.v, self.do, self.lse, self.delta, mask=self.mask, scale=c.scale,
                    causal=c.causal, q_offset=c.q_offset, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws,
-                   kv_split=self.kv_split, q_split=self.q_split, mask_tiles=self.tiles)
+                   kv_split=self.kv_split, q_split=self.q_split, mask_tiles=self.tiles, **self.sk)
 
     def step(self):
         self.classify()

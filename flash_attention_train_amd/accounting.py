@@ -44,8 +44,35 @@ def unmasked_pairs(B: int, Hq: int, Sq: int, Sk: int, causal: bool, q_offset: in
     return total * Hq
 
 
+def structured_counts(Sq: int, Sk: int, causal: bool, q_offset: int, key_len: int, q_len: int, window_left: int,
+                      window_right: int) -> np.ndarray:
+    """Visible keys per query row of one batch entry under a structured mask: row i
+    (i < q_len) sees the keys j with max(0, pos - window_left) <= j < min(key_len,
+    pos + 1 if causal, pos + window_right + 1), pos = q_offset + i (a bound of -1 is absent)."""
+    pos = q_offset + np.arange(Sq, dtype=np.int64)
+    lo = np.maximum(pos - window_left, 0) if window_left >= 0 else np.zeros(Sq, np.int64)
+    hi = np.full(Sq, min(key_len, Sk), np.int64)
+    if causal:
+        hi = np.minimum(hi, pos + 1)
+    if window_right >= 0:
+        hi = np.minimum(hi, pos + window_right + 1)
+    n = np.maximum(hi - lo, 0)
+    n[q_len:] = 0
+    return n
+
+
 def case_pairs(c: Case) -> int:
-    return unmasked_pairs(c.B, c.Hq, c.Sq, c.Sk, c.causal, c.q_offset, c.mask)
+    st = c.meta.get("structure")
+    if st is None:
+        return unmasked_pairs(c.B, c.Hq, c.Sq, c.Sk, c.causal, c.q_offset, c.mask)
+    if c.mask is not None:
+        raise ValueError("pair counts of a structured case with a dense mask are not defined here")
+    total = 0
+    for b in range(c.B):
+        kl = c.Sk if st["key_len"] is None else int(st["key_len"][b])
+        ql = c.Sq if st["q_len"] is None else int(st["q_len"][b])
+        total += int(structured_counts(c.Sq, c.Sk, c.causal, c.q_offset, kl, ql, *st["window"]).sum())
+    return total * c.Hq
 
 
 def fwd_flops(n_pairs: int, D: int) -> float:

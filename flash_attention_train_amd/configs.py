@@ -34,7 +34,17 @@ WORKLOADS = {
     "lm_causal": Workload("lm_causal", "LM causal GQA, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 4, (2, 1)),
     "long_window": Workload("long_window",
                             "long-window chunked walk, W=32768, 64 chunks of 512, Hq=16 Hkv=4 D=128 bf16", 5),
+    # the DiT self-attention masks given by their structure instead of a dense mask:
+    # the pad as a key length, and a mixed-length batch under a sliding window
+    "dit_sa_len": Workload("dit_sa_len", "DiT self-attention, B=1 Hq=16 Hkv=8 S=1542 D=128 bf16, "
+                           "key length 1388 (the pad as a length)", 6, (2, 1)),
+    "dit_sa_band": Workload("dit_sa_band", "DiT self-attention, mixed-length batch B=2 Hq=16 Hkv=8 S=1542 D=128 "
+                            "bf16, key lengths 1542 / 1101, window 256 keys each side", 7),
 }
+
+# the sliding window of the structured DiT workload: keys within this distance on each
+# side of a row's position (the trainer's width is not given)
+DIT_WINDOW = 256
 
 LONG_WINDOW = 32768
 LONG_CHUNK = 512
@@ -68,6 +78,19 @@ def make(key: str, **shrink) -> Case:
         a = dict(B=1, Hq=32, Hkv=8, Sq=4096, Sk=4096, D=128, dtype=BF16, do_std=0.1)
         a.update(shrink)
         return make_case(key, seed=s, causal=True, q_offset=0, **a)
+    if key in ("dit_sa_len", "dit_sa_band"):
+        a = dict(B=1 if key == "dit_sa_len" else 2, Hq=16, Hkv=8, Sq=1542, Sk=1542, D=128, dtype=BF16)
+        a.update(shrink)
+        c = make_case(key, seed=s, **a)
+        n_pad = int(round(0.1 * c.Sk))  # the self-attention pad of the DiT workload
+        if key == "dit_sa_len":
+            c.meta["structure"] = {"key_len": [c.Sk - n_pad] * c.B, "q_len": None, "window": (-1, -1)}
+        else:
+            lens = [c.Sk if b % 2 == 0 else max(1, (c.Sk * 5) // 7) for b in range(c.B)]
+            w = min(DIT_WINDOW, c.Sk)
+            c.meta["structure"] = {"key_len": lens, "q_len": None, "window": (w, w)}
+        c.meta["mask_kind"] = "structured"
+        return c
     if key == "long_window":
         W = shrink.pop("W", LONG_WINDOW)
         a = dict(B=1, Hq=16, Hkv=4, Sq=W, Sk=W, D=128, dtype=BF16)

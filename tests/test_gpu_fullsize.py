@@ -50,6 +50,32 @@ def test_dit_full_size_every_element(key):
         assert full.sum() == 2 * c.B and dead.any()
 
 
+@pytest.mark.parametrize("key", ["dit_sa_len", "dit_sa_band"])
+def test_structured_dit_full_size_every_element(key):
+    """The structured DiT workloads as the bench runs them (lengths on the device, the
+    window, the table's backward decomposition): every output against the oracle given
+    the structure's dense mask."""
+    c = configs.make(key)
+    st = c.meta["structure"]
+    say(f"{key}: full size B={c.B} Hq={c.Hq} Hkv={c.Hkv} S={c.Sq} {st}; oracle running")
+    t = upload(c)
+    kl = torch.tensor(st["key_len"], dtype=torch.int32, device="cuda")
+    kv, qs = configs.WORKLOADS[key].bwd_splits or (0, 0)
+    o, lse = binding.fwd(t["q"], t["k"], t["v"], scale=c.scale, key_len=kl, window=st["window"])
+    delta = binding.bwd_preprocess(o, t["do"])
+    dq, dk, dv = binding.bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, scale=c.scale, key_len=kl,
+                             window=st["window"], kv_split=kv, q_split=qs)
+    torch.cuda.synchronize()
+    got = {"O": host64(o), "LSE": host64(lse), "Delta": host64(delta), "dQ": host64(dq), "dK": host64(dk),
+           "dV": host64(dv)}
+    m = oracle.structured_mask(c.B, c.Sq, c.Sk, key_len=st["key_len"], q_len=st["q_len"],
+                               window_left=st["window"][0], window_right=st["window"][1], q_offset=c.q_offset)
+    ref = oracle.backward(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), m, scale=c.scale, causal=c.causal,
+                          q_offset=c.q_offset)
+    c.mask = m.astype(np.float32)  # for the exact-zero checks of dead rows and columns
+    compare_full(c, got, ref)
+
+
 def _check_rows(c, got, ids, ref, tol):
     D = c.D
     full, _ = visibility(c)

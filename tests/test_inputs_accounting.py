@@ -5,6 +5,7 @@ from __future__ import annotations
 import numpy as np
 import pytest
 
+import oracle
 from flash_attention_train_amd import accounting as A
 from flash_attention_train_amd import configs
 from flash_attention_train_amd.inputs import bf16_bits_to_f32, f32_to_bf16_bits, make_case
@@ -73,3 +74,33 @@ def test_chunk_plan():
     assert plan[0] == (0, 512, 512) and plan[-1] == (32256, 512, 32768)
     with pytest.raises(ValueError):
         configs.chunk_plan(1000, 512)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_structured_pair_counts_brute_force(seed):
+    """Closed-form visible-key counts of a structured mask against an entry-by-entry count
+    of the definition on small random structures (lengths, windows, offsets, causal)."""
+    rng = np.random.default_rng(seed)
+    Sq, Sk = int(rng.integers(1, 40)), int(rng.integers(1, 40))
+    causal = bool(rng.integers(0, 2))
+    q_offset = int(rng.integers(-10, 20))
+    wl, wr = (int(x) for x in rng.integers(-1, 12, size=2))
+    kl, ql = int(rng.integers(0, Sk + 1)), int(rng.integers(0, Sq + 1))
+    n = A.structured_counts(Sq, Sk, causal, q_offset, kl, ql, wl, wr)
+    for i in range(Sq):
+        pos = q_offset + i
+        want = 0
+        for j in range(Sk):
+            ok = i < ql and j < kl and (wl < 0 or j >= pos - wl) and (wr < 0 or j <= pos + wr)
+            ok = ok and (not causal or j <= pos)
+            want += ok
+        assert n[i] == want, (i, n[i], want)
+
+
+@pytest.mark.parametrize("key", ["dit_sa_len", "dit_sa_band"])
+def test_structured_workload_pairs_match_the_dense_definition(key):
+    c = configs.make(key, Hq=1, Hkv=1, D=8)
+    st = c.meta["structure"]
+    m = oracle.structured_mask(c.B, c.Sq, c.Sk, key_len=st["key_len"], q_len=st["q_len"],
+                               window_left=st["window"][0], window_right=st["window"][1], q_offset=c.q_offset)
+    assert A.case_pairs(c) == int(np.isfinite(m).sum())
