@@ -34,7 +34,8 @@ class FaAttnParams(ctypes.Structure):
                 ("mask_stride_b", ctypes.c_int64), ("mask_stride_q", ctypes.c_int64), ("mask_tiles", ctypes.c_void_p),
                 ("fwd_variant", ctypes.c_int32), ("kv_split", ctypes.c_int32), ("q_split", ctypes.c_int32),
                 ("fwd_split", ctypes.c_int32), ("key_len", ctypes.c_void_p), ("q_len", ctypes.c_void_p),
-                ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32)]
+                ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
+                ("bwd_dq_launch", ctypes.c_int32)]
 
 
 class FaError(RuntimeError):
@@ -121,7 +122,7 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
                 q_offset: Optional[int], mask: Optional[torch.Tensor], fwd_variant: int = 0, kv_split: int = 0,
                 q_split: int = 0, mask_tiles: Optional[torch.Tensor] = None, fwd_split: int = 0,
                 key_len: Optional[torch.Tensor] = None, q_len: Optional[torch.Tensor] = None,
-                window: tuple = (-1, -1)) -> FaAttnParams:
+                window: tuple = (-1, -1), dq_launch: int = 0) -> FaAttnParams:
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Sk, Dk = k.shape
     if Bk != B or Dk != D:
@@ -132,7 +133,7 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
         q_offset = Sk - Sq if causal else 0
     p = FaAttnParams(B, Hq, Hkv, Sq, Sk, D, _dtype_code(q), int(bool(causal)), int(q_offset), float(scale),
                      None, 0, 0, None, int(fwd_variant), int(kv_split), int(q_split), int(fwd_split), None, None,
-                     int(window[0]), int(window[1]))
+                     int(window[0]), int(window[1]), int(dq_launch))
     for name, t, n in (("key_len", key_len, B), ("q_len", q_len, B)):
         if t is not None:
             if t.dtype != torch.int32 or t.dim() != 1 or t.shape[0] != n or not t.is_contiguous():
@@ -238,10 +239,11 @@ def _workspace(p: FaAttnParams, device, workspace):
 
 def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_offset=None, dq=None, dk=None,
         dv=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None, q_len=None,
-        window=(-1, -1)):
+        window=(-1, -1), dq_launch=0):
     """Backward: returns (dQ, dK, dV), each in q's dtype, overwritten."""
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
-                    q_split=q_split, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, window=window)
+                    q_split=q_split, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, window=window,
+                    dq_launch=dq_launch)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
@@ -292,12 +294,12 @@ def tune_bwd_splits(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=
 
 def bwd_chunked(q, k, v, dout, lse, delta, dk_acc, dv_acc, *, mask=None, scale=None, causal=True, q_offset=None,
                 dq=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None,
-                q_len=None, window=(-1, -1)):
+                q_len=None, window=(-1, -1), dq_launch=0):
     """Chunked backward: returns dQ for the chunk; ADDS dK/dV into the fp32 window
     accumulators ``dk_acc`` / ``dv_acc`` ([B, Hkv, >= Sk, D])."""
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len,
-                    q_len=q_len, window=window)
+                    q_len=q_len, window=window, dq_launch=dq_launch)
     if dk_acc.dtype != torch.float32 or dv_acc.dtype != torch.float32:
         raise TypeError("the window accumulators must be float32")
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq

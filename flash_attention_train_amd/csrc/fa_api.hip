@@ -89,6 +89,8 @@ fa_status check_params(const fa_attn_params* p) {
       p->fwd_split > 64)
     return fail(FA_ERR_SHAPE, "split hints must be in 0 .. 64");
   if (p->window_left < -1 || p->window_right < -1) return fail(FA_ERR_SHAPE, "window bounds must be >= -1");
+  if (p->bwd_dq_launch < 0 || p->bwd_dq_launch > 2)
+    return fail(FA_ERR_SHAPE, "bwd_dq_launch must be 0, 1 or 2 (got %d)", p->bwd_dq_launch);
   if (reinterpret_cast<uintptr_t>(p->key_len) % 4 || reinterpret_cast<uintptr_t>(p->q_len) % 4)
     return fail(FA_ERR_ALIGN, "key_len / q_len are not 4-byte aligned");
   const bool structured = p->key_len || p->q_len || p->window_left >= 0 || p->window_right >= 0;
@@ -371,7 +373,11 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
     fa::BwdPlan plan;
     int kv, q;
     choose_splits(p, accumulate, &kv, &q);
-    fa::plan_bwd_bf16(a.a, kv, q, &plan);
+    fa::plan_bwd_bf16(a.a, kv, q, 0, &plan);
+    // a large dQ grid runs as its own kernel, two workgroups per compute unit (measured on
+    // the causal LM backward: 659 -> 631 us); small grids keep one launch, whose dQ
+    // workgroups fill the compute units the dK/dV walks leave idle
+    plan.dq_separate = p->bwd_dq_launch ? p->bwd_dq_launch == 2 : plan.n_q_units >= 512;
     // split walks write every element of their fp32 slices (zeros included), so the
     // slices need no clearing; the reduce passes sum them into the outputs
     a.dq_acc = nullptr;

@@ -607,7 +607,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
 // ---------------------------------------------------------------------------
 // dQ workgroup
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool MASK, bool BIAS>
+template <int D, bool CAUSAL, bool MASK, bool BIAS, bool LOWREG = false>
 __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
   constexpr int DS = D / 16, DB = D / 32;
   using TL = Tile<D>;
@@ -641,6 +641,13 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
   }
   const float lse2 = args.lse[b * args.lse_sb + h * args.lse_sh + row_c] * kLog2e;
   const float dlt = args.delta[b * args.delta_sb + h * args.delta_sh + row_c];
+  if constexpr (LOWREG) {
+    // two workgroups per compute unit: the Q / dO fragments wait in accumulation
+    // registers (matrix instructions read their operands there), leaving the vector
+    // file to the walk
+    #pragma unroll
+    for (int s = 0; s < DS; ++s) asm volatile("" : "+a"(qf[s]), "+a"(df[s]));
+  }
 
   f32x16 dq[DB];
   #pragma unroll
@@ -765,24 +772,29 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
     #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       // S^T = K Q^T, dP^T = V dO^T: all K / V row chunks of the block requested up front
-      bf16x8 ka[DS], va[DS];
-      #pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        ka[s] = TL::read_chunk(kb_lds, 32 * kb + r32, 2 * s + g);
-        va[s] = TL::read_chunk(vb_lds, 32 * kb + r32, 2 * s + g);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      // (in halves when two workgroups share the compute unit: the other one's work
+      // covers the wait, and the operands of a half fit beside it)
+      constexpr int NH = LOWREG ? 4 : 1, PH = DS / NH;
       f32x16 st = zeros16(), dpt = zeros16();
       #pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        mma(st, ka[s], qf[s]);
-        mma(dpt, va[s], df[s]);
+      for (int half = 0; half < NH; ++half) {
+        bf16x8 ka[PH], va[PH];
+        #pragma unroll
+        for (int s = 0; s < PH; ++s) {
+          ka[s] = TL::read_chunk(kb_lds, 32 * kb + r32, 2 * (PH * half + s) + g);
+          va[s] = TL::read_chunk(vb_lds, 32 * kb + r32, 2 * (PH * half + s) + g);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        #pragma unroll
+        for (int s = 0; s < PH; ++s) {
+          mma(st, ka[s], qf[PH * half + s]);
+          mma(dpt, va[s], df[PH * half + s]);
+        }
       }
       // K operands of dQ += dS K (transpose reads), landing during the softmax: registers
       // 8 hh .. of this key block hold keys 32 kb + 16 hh + 8 t + 4 g + e
       bf16x8 kbt[2][DB];
-      #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
+      auto read_kbt = [&](int hh) {
         const int rbase = 32 * kb + 16 * hh + 4 * g + tr_row;
         #pragma unroll
         for (int db = 0; db < DB; ++db) {
@@ -790,6 +802,10 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
           const bf16x4 hi = TL::read_tr(kb_lds, rbase + 8, 32 * db + tr_col);
           kbt[hh][db] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
+      };
+      if constexpr (!LOWREG) {
+        read_kbt(0);
+        read_kbt(1);
       }
       __builtin_amdgcn_sched_barrier(0);
       // lane (query row, half g), register r -> key 32 kb + 8 (r/4) + 4 g + r%4
@@ -821,6 +837,7 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
       for (int r = 0; r < 16; ++r) st[r] = st[r] * (dpt[r] - dlt);
       #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
+        if constexpr (LOWREG) read_kbt(hh);  // (two workgroups per unit: read when needed)
         bf16x8 dsf;
         pack8(dsf, st, 8 * hh);
         #pragma unroll
@@ -880,24 +897,51 @@ __global__ __launch_bounds__(NT) void bwd_bf16_kernel(const BwdArgs args, const 
   }
 }
 
+// The dQ walk as a kernel of its own: its registers fit two workgroups per compute unit
+// (the dK/dV walk's do not), so that one workgroup's LDS and memory waits are covered by
+// the other's products. Launched after the dK/dV-only grid when the plan asks for it.
+template <int D, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(const BwdArgs args, const BwdPlan plan) {
+  constexpr int Q_LDS = 2 * 2 * Q_BN * D * 2;
+  __shared__ __attribute__((aligned(16))) char smem[Q_LDS];
+  const int unit = blockIdx.x;
+  const AttnShape& a = args.a;
+  const QUnit u = q_unit_of(a, plan, unit);
+  if (MASK && any_bias_block(a, u.b, u.qt * (Q_BM / kMaskTile), Q_BM / kMaskTile, 0,
+                             (a.Sk + kMaskTile - 1) / kMaskTile))
+    dq_unit<D, CAUSAL, MASK, true, true>(args, plan, unit, smem);
+  else
+    dq_unit<D, CAUSAL, MASK, false, true>(args, plan, unit, smem);
+}
+
+template <int D, bool CAUSAL, bool MASK>
+hipError_t launch_cm(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream) {
+  if (!plan.dq_separate) {
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, MASK>), dim3(plan.n_kv_units + plan.n_q_units), dim3(NT), 0, stream,
+                       args, plan);
+    return hipGetLastError();
+  }
+  if (plan.n_kv_units > 0)
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, MASK>), dim3(plan.n_kv_units), dim3(NT), 0, stream, args, plan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.n_q_units == 0) return e;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, MASK>), dim3(plan.n_q_units), dim3(NT), 0, stream, args, plan);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_t(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream) {
-  const dim3 grid(plan.n_kv_units + plan.n_q_units);
   const bool causal = args.a.causal != 0, mask = args.a.mask != nullptr;
-  if (causal && mask)
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, true, true>), grid, dim3(NT), 0, stream, args, plan);
-  else if (causal)
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, true, false>), grid, dim3(NT), 0, stream, args, plan);
-  else if (mask)
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, false, true>), grid, dim3(NT), 0, stream, args, plan);
-  else
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, false, false>), grid, dim3(NT), 0, stream, args, plan);
-  return hipGetLastError();
+  if (causal && mask) return launch_cm<D, true, true>(args, plan, stream);
+  if (causal) return launch_cm<D, true, false>(args, plan, stream);
+  if (mask) return launch_cm<D, false, true>(args, plan, stream);
+  return launch_cm<D, false, false>(args, plan, stream);
 }
 
 }  // namespace
 
-void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, BwdPlan* plan) {
+void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, int dq_separate, BwdPlan* plan) {
+  plan->dq_separate = dq_separate;
   const int nkt = (a.Sk + KV_BN - 1) / KV_BN;
   const int nqt = (a.Sq + Q_BM - 1) / Q_BM;
   plan->kv_split = kv_split;

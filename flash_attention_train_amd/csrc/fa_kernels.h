@@ -161,6 +161,7 @@ struct BwdPlan {
   int q_split;     // workgroups sharing one query tile's dQ walk (> 1: fp32 partial slices)
   int n_kv_units;  // dK/dV workgroups (launched first)
   int n_q_units;   // dQ workgroups
+  int dq_separate; // 1: the dQ workgroups run as a second kernel (two per compute unit)
   float* dk_part;  // fp32 [kv_split][B, Hkv, Sk, D] partial sums when kv_split > 1
   float* dv_part;
   float* dq_part;  // fp32 [q_split][B, Hq, Sq, D] partial sums when q_split > 1
@@ -201,7 +202,7 @@ hipError_t launch_bwd(const BwdArgs& args, int is_bf16, hipStream_t stream);
 hipError_t launch_dq_convert(const DqArgs& args, int is_bf16, hipStream_t stream);
 // reduces args, and args1 too when given (same shape and dtype: one launch for dK and dV)
 hipError_t launch_reduce_parts(const ReduceArgs& args, const ReduceArgs* args1, int is_bf16, hipStream_t stream);
-void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, BwdPlan* plan);
+void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, int dq_separate, BwdPlan* plan);
 hipError_t launch_bwd_bf16(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream);
 
 }  // namespace fa

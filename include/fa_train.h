@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FA_TRAIN_ABI_VERSION 3
+#define FA_TRAIN_ABI_VERSION 4
 
 typedef enum fa_status {
     FA_OK = 0,
@@ -127,6 +127,11 @@ typedef struct fa_attn_params {
     int32_t window_left;     /* >= 0: keys at most this far before a row's position q_offset + i;
                                 -1: no bound */
     int32_t window_right;    /* >= 0: keys at most this far after it; -1: no bound */
+    /* Work decomposition hint of the bf16 backward, like the split hints above (same
+     * results up to fp32 summation order): 0 = automatic, 1 = the dQ workgroups share the
+     * dK/dV workgroups' launch, 2 = they run as a second kernel after it, two per compute
+     * unit (chosen automatically for grids of at least 512 dQ workgroups). */
+    int32_t bwd_dq_launch;
 } fa_attn_params;
 
 /* Forward: writes O (dtype) and LSE (fp32, natural log). Fully masked rows get

@@ -199,21 +199,41 @@ def test_forward_split_hint_ignored_for_fp32():
     assert torch.equal(o, o1) and torch.equal(lse, lse1)
 
 
+@pytest.mark.parametrize("dq_launch", [1, 2])
 @pytest.mark.parametrize("kv_split,q_split", [(1, 1), (3, 1), (1, 2), (2, 5)])
 @pytest.mark.parametrize("name", ["dit_sa_ragged", "lm_causal_gqa4", "random_bias_bcast", "d64_bf16"])
-def test_backward_decompositions(name, kv_split, q_split):
+def test_backward_decompositions(name, kv_split, q_split, dq_launch):
     """Every split of the bf16 backward's work (direct stores, or fp32 partial slices summed by a reduce
-    pass) gives the oracle's gradients."""
+    pass), with the dQ workgroups in the dK/dV launch (1) or in a launch of their own (2), gives the
+    oracle's gradients."""
+    c = CASES[name]()
+    t = upload(c)
+    say(f"case {name}: kv_split {kv_split} q_split {q_split} dq_launch {dq_launch}")
+    o, lse = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
+                         q_offset=c.q_offset)
+    delta = binding.bwd_preprocess(o, t["do"])
+    dq, dk, dv = binding.bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, mask=t["mask"], scale=c.scale,
+                             causal=c.causal, q_offset=c.q_offset, kv_split=kv_split, q_split=q_split,
+                             dq_launch=dq_launch)
+    torch.cuda.synchronize()
+    ref = oracle_full(c)
+    compare_full(c, {"dQ": host64(dq), "dK": host64(dk), "dV": host64(dv)}, ref, names=("dQ", "dK", "dV"))
+
+
+@pytest.mark.parametrize("name", ["dit_sa_ragged", "lm_causal_gqa4"])
+def test_dq_launch_is_bitwise_neutral(name):
+    """The dQ walk in its own launch (two workgroups per compute unit) does the same arithmetic in the
+    same order as in the shared launch: identical bits for a fixed split."""
     c = CASES[name]()
     t = upload(c)
     o, lse = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
                          q_offset=c.q_offset)
     delta = binding.bwd_preprocess(o, t["do"])
-    dq, dk, dv = binding.bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, mask=t["mask"], scale=c.scale,
-                             causal=c.causal, q_offset=c.q_offset, kv_split=kv_split, q_split=q_split)
+    out = [binding.bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, mask=t["mask"], scale=c.scale,
+                       causal=c.causal, q_offset=c.q_offset, kv_split=2, q_split=1, dq_launch=m) for m in (1, 2)]
     torch.cuda.synchronize()
-    ref = oracle_full(c)
-    compare_full(c, {"dQ": host64(dq), "dK": host64(dk), "dV": host64(dv)}, ref, names=("dQ", "dK", "dV"))
+    for a, b in zip(*out):
+        assert torch.equal(a, b)
 
 
 def test_tuned_split_is_a_candidate_and_exact():
@@ -235,8 +255,8 @@ def test_tuned_split_is_a_candidate_and_exact():
     compare_full(c, {"dQ": host64(dq), "dK": host64(dk), "dV": host64(dv)}, oracle_full(c), names=("dQ", "dK", "dV"))
 
 
-@pytest.mark.parametrize("kv_split,q_split", [(1, 1), (2, 3)])
-def test_chunked_decompositions(kv_split, q_split):
+@pytest.mark.parametrize("kv_split,q_split,dq_launch", [(1, 1, 0), (2, 3, 0), (2, 1, 2)])
+def test_chunked_decompositions(kv_split, q_split, dq_launch):
     """The chunked backward adds into the window accumulators the same way for any split."""
     W, C = 512, 128
     c = configs.make("long_window", W=W, Hq=4, Hkv=1)
@@ -250,7 +270,7 @@ def test_chunked_decompositions(kv_split, q_split):
         o, lse = binding.fwd(q, kk, vv, scale=c.scale, causal=True, q_offset=p0)
         delta = binding.bwd_preprocess(o, do)
         binding.bwd_chunked(q, kk, vv, do, lse, delta, dk_acc, dv_acc, scale=c.scale, causal=True, q_offset=p0,
-                            dq=dQ[:, :, p0:p0 + n], kv_split=kv_split, q_split=q_split)
+                            dq=dQ[:, :, p0:p0 + n], kv_split=kv_split, q_split=q_split, dq_launch=dq_launch)
     torch.cuda.synchronize()
     ref = oracle_full(c)
     got = {"dQ": host64(dQ), "dK": dk_acc.cpu().numpy().astype(np.float64),
