@@ -37,7 +37,7 @@ class _Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("Sq", ctypes.c_int32), ("Sk", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("mask_b", ctypes.c_int32),
-                ("q_offset", ctypes.c_int64), ("scale", ctypes.c_double)]
+                ("q_offset", ctypes.c_int64), ("scale", ctypes.c_double), ("sinks", ctypes.c_void_p)]
 
 
 _lib = None
@@ -74,7 +74,7 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
-def _problem(q, k, mask, scale, causal, q_offset):
+def _problem(q, k, mask, scale, causal, q_offset, sinks=None):
     B, Hq, Sq, D = q.shape
     _, Hkv, Sk, _ = k.shape
     if q_offset is None:
@@ -82,14 +82,17 @@ def _problem(q, k, mask, scale, causal, q_offset):
     mb = 0 if mask is None else int(mask.shape[0])
     if mask is not None and tuple(mask.shape[1:]) != (Sq, Sk):
         raise ValueError("mask must be [Bm, Sq, Sk]")
-    return _Problem(B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), mb, int(q_offset), float(scale))
+    if sinks is not None and sinks.shape != (Hq,):
+        raise ValueError("sinks must be [Hq]")
+    return _Problem(B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), mb, int(q_offset), float(scale),
+                    None if sinks is None else sinks.ctypes.data)
 
 
 def forward(q, k, v, mask=None, *, scale: float, causal: bool = False, q_offset: Optional[int] = None,
-            threads: Optional[int] = None):
-    """Returns (O [B,Hq,Sq,D], LSE [B,Hq,Sq]) in float64."""
-    q, k, v, mask = _f64(q), _f64(k), _f64(v), _f64(mask)
-    p = _problem(q, k, mask, scale, causal, q_offset)
+            threads: Optional[int] = None, sinks=None):
+    """Returns (O [B,Hq,Sq,D], LSE [B,Hq,Sq]) in float64. ``sinks``: optional [Hq] sink logits."""
+    q, k, v, mask, sinks = _f64(q), _f64(k), _f64(v), _f64(mask), _f64(sinks)
+    p = _problem(q, k, mask, scale, causal, q_offset, sinks)
     O = np.zeros(q.shape, np.float64)
     L = np.zeros(q.shape[:3], np.float64)
     rc = _load().ora_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(O), _ptr(L),
@@ -100,10 +103,11 @@ def forward(q, k, v, mask=None, *, scale: float, causal: bool = False, q_offset:
 
 
 def backward(q, k, v, do, mask=None, *, scale: float, causal: bool = False, q_offset: Optional[int] = None,
-             threads: Optional[int] = None) -> dict:
-    """The full forward and backward. Returns a dict with O, LSE, Delta, dQ, dK, dV (float64)."""
-    q, k, v, do, mask = _f64(q), _f64(k), _f64(v), _f64(do), _f64(mask)
-    p = _problem(q, k, mask, scale, causal, q_offset)
+             threads: Optional[int] = None, sinks=None) -> dict:
+    """The full forward and backward. Returns a dict with O, LSE, Delta, dQ, dK, dV (float64), and
+    dSink [Hq] when ``sinks`` ([Hq] sink logits) is given."""
+    q, k, v, do, mask, sinks = _f64(q), _f64(k), _f64(v), _f64(do), _f64(mask), _f64(sinks)
+    p = _problem(q, k, mask, scale, causal, q_offset, sinks)
     out = {"O": np.zeros(q.shape), "LSE": np.zeros(q.shape[:3]), "Delta": np.zeros(q.shape[:3]),
            "dQ": np.zeros(q.shape), "dK": np.zeros(k.shape), "dV": np.zeros(k.shape)}
     rc = _load().ora_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(do),
@@ -111,14 +115,30 @@ def backward(q, k, v, do, mask=None, *, scale: float, causal: bool = False, q_of
                               threads or default_threads())
     if rc:
         raise ValueError(f"oracle rejected the problem (code {rc})")
+    if sinks is not None:
+        out["dSink"] = sink_grad(sinks, out["LSE"], out["Delta"])
+    return out
+
+
+def sink_grad(sinks, lse, delta) -> np.ndarray:
+    """Gradient of the loss with respect to each head's sink logit: the sink is one more softmax
+    column with no value row, so its dS is P_sink (0 - Delta_i) with P_sink = exp(sink_h - LSE_i),
+    summed over every row of the head (all batches): dSink_h = -sum_{b,i} exp(sink_h - LSE_bhi) Delta_bhi.
+    A fully masked row without a sink has no sink term; with one, its O is 0 and so is its Delta."""
+    sinks = np.asarray(sinks, np.float64)
+    lse = np.asarray(lse, np.float64)
+    delta = np.asarray(delta, np.float64)
+    out = np.zeros(sinks.shape[0])
+    for h in range(sinks.shape[0]):
+        out[h] = -np.sum(np.exp(sinks[h] - lse[:, h, :]) * delta[:, h, :])
     return out
 
 
 def rows(q, k, v, do, row_ids, mask=None, *, scale: float, causal: bool = False,
-         q_offset: Optional[int] = None, threads: Optional[int] = None) -> dict:
+         q_offset: Optional[int] = None, threads: Optional[int] = None, sinks=None) -> dict:
     """Selected rows, ids (b*Hq + h)*Sq + i. Returns O [n,D], LSE [n], Delta [n], dQ [n,D]."""
-    q, k, v, do, mask = _f64(q), _f64(k), _f64(v), _f64(do), _f64(mask)
-    p = _problem(q, k, mask, scale, causal, q_offset)
+    q, k, v, do, mask, sinks = _f64(q), _f64(k), _f64(v), _f64(do), _f64(mask), _f64(sinks)
+    p = _problem(q, k, mask, scale, causal, q_offset, sinks)
     ids = np.ascontiguousarray(row_ids, dtype=np.int64)
     n, D = ids.size, q.shape[3]
     out = {"O": np.zeros((n, D)), "LSE": np.zeros(n), "Delta": np.zeros(n), "dQ": np.zeros((n, D))}
@@ -131,10 +151,10 @@ def rows(q, k, v, do, row_ids, mask=None, *, scale: float, causal: bool = False,
 
 
 def cols(q, k, v, do, col_ids, mask=None, *, scale: float, causal: bool = False,
-         q_offset: Optional[int] = None, threads: Optional[int] = None) -> dict:
+         q_offset: Optional[int] = None, threads: Optional[int] = None, sinks=None) -> dict:
     """Selected key columns, ids (b*Hkv + g)*Sk + j. Returns dK [n,D], dV [n,D]."""
-    q, k, v, do, mask = _f64(q), _f64(k), _f64(v), _f64(do), _f64(mask)
-    p = _problem(q, k, mask, scale, causal, q_offset)
+    q, k, v, do, mask, sinks = _f64(q), _f64(k), _f64(v), _f64(do), _f64(mask), _f64(sinks)
+    p = _problem(q, k, mask, scale, causal, q_offset, sinks)
     ids = np.ascontiguousarray(col_ids, dtype=np.int64)
     n, D = ids.size, q.shape[3]
     out = {"dK": np.zeros((n, D)), "dV": np.zeros((n, D))}

@@ -9,10 +9,14 @@
  * materialised, no tiling, no online softmax):
  *
  *   S_ij   = scale * <q_i, k_g(h),j> + M_ij    or -inf where masked / causal
- *   m_i    = max_j S_ij
+ *   m_i    = max(max_j S_ij, sink_h)            (sink_h = -inf without sinks)
  *   row fully masked (m_i = -inf):  O_i = 0, LSE_i = 0, P_i. = 0
- *   otherwise: LSE_i = m_i + ln sum_j exp(S_ij - m_i),  P_ij = exp(S_ij - LSE_i),
- *              O_i = sum_j P_ij v_j
+ *   otherwise: LSE_i = m_i + ln (sum_j exp(S_ij - m_i) + exp(sink_h - m_i)),
+ *              P_ij = exp(S_ij - LSE_i),  O_i = sum_j P_ij v_j
+ *   (an attention sink is one more logit per head in the softmax's denominator,
+ *   with no value row: llama.cpp pull request 57, the list of score modifiers
+ *   whose flash backward was missing; its own gradient is formed from LSE and
+ *   Delta by the Python wrapper)
  *   Delta_i = <dO_i, O_i>
  *   dP_ij   = <dO_i, v_j>,   dS_ij = P_ij (dP_ij - Delta_i)
  *   dQ_i    = scale * sum_j dS_ij k_j
@@ -50,6 +54,7 @@ typedef struct {
     int32_t mask_b; /* 0 = no mask, 1 = shared by the batch, B = one per sample */
     int64_t q_offset;
     double scale;
+    const double *sinks; /* [Hq] logits, NULL = none */
 } ora_problem;
 
 typedef struct {
@@ -115,7 +120,8 @@ static void row_forward(const ora_inputs *in, int b, int h, int i, double *srow,
                         double *lse_out, double *delta_out) {
     const ora_problem *p = in->p;
     const int D = p->D, Sk = p->Sk, g = kv_head(p, h);
-    double m = -INFINITY;
+    const double sink = p->sinks ? p->sinks[h] : -INFINITY;
+    double m = sink;
     for (int j = 0; j < Sk; ++j) {
         srow[j] = score(in, b, h, i, j);
         if (srow[j] > m) m = srow[j];
@@ -126,7 +132,7 @@ static void row_forward(const ora_inputs *in, int b, int h, int i, double *srow,
         if (delta_out) *delta_out = 0.0;
         return;
     }
-    double l = 0.0;
+    double l = exp(sink - m);
     for (int j = 0; j < Sk; ++j) l += exp(srow[j] - m);
     const double lse = m + log(l);
     for (int j = 0; j < Sk; ++j) {

@@ -388,3 +388,106 @@ def test_structured_causal_window_equals_per_row_slices():
         Oi, Li = oracle.forward(q[:, :, i:i + 1], k[:, :, lo:hi], v[:, :, lo:hi], scale=0.25)
         np.testing.assert_allclose(O[:, :, i], Oi[:, :, 0], rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(L[:, :, i], Li[:, :, 0], rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# attention sinks (one more logit per head in the softmax denominator, no value row):
+# pinned to the same problem with the sink written as an extra key, to finite
+# differences of the loss in the sink logits, and to closed forms
+# ---------------------------------------------------------------------------
+def _sink_problem(seed, B=2, Hq=4, Hkv=2, Sq=6, Sk=7, D=5, causal=False, q_offset=None, mask=True):
+    rng = np.random.default_rng(seed)
+    q, k, v, do = (rng.standard_normal(s) for s in ((B, Hq, Sq, D), (B, Hkv, Sk, D), (B, Hkv, Sk, D), (B, Hq, Sq, D)))
+    m = None
+    if mask:  # key padding with one fully masked row per sample
+        m = np.zeros((B, Sq, Sk))
+        m[0, :, Sk - 2:] = -np.inf
+        m[1, 2, :] = -np.inf
+    sinks = rng.standard_normal(Hq) + 0.5
+    return q, k, v, do, m, sinks
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sinks_equal_an_extra_key_per_head(causal):
+    """A sink is the score of one more key whose value row is zero: per query head, append a key with
+    k = 0 (its product is 0) and the mask entry sink_h in every row, run the plain oracle on that head
+    alone, and every output must agree (dK/dV summed over the group's heads, on the real keys)."""
+    q, k, v, do, m, sinks = _sink_problem(21, causal=causal)
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    G, sc = Hq // Hkv, 0.45
+    off = Sk - Sq if causal else None
+    ref = oracle.backward(q, k, v, do, m, scale=sc, causal=causal, q_offset=off, sinks=sinks)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for h in range(Hq):
+        g = h // G
+        ke = np.concatenate([k[:, g:g + 1], np.zeros((B, 1, 1, D))], axis=2)
+        ve = np.concatenate([v[:, g:g + 1], np.zeros((B, 1, 1, D))], axis=2)
+        me = np.zeros((B, Sq, Sk + 1)) if m is None else np.concatenate([m, np.zeros((B, Sq, 1))], axis=2)
+        me[:, :, Sk] = sinks[h]
+        if causal:  # the real keys keep their causal visibility; the sink column is always visible
+            i, j = np.arange(Sq)[:, None], np.arange(Sk)[None, :]
+            me[:, :, :Sk] = np.where(j > (Sk - Sq) + i, -np.inf, me[:, :, :Sk])
+        one = oracle.backward(q[:, h:h + 1], ke, ve, do[:, h:h + 1], me, scale=sc)
+        for n in ("O", "LSE", "Delta", "dQ"):
+            np.testing.assert_allclose(ref[n][:, h:h + 1], one[n], rtol=1e-12, atol=1e-12, err_msg=n)
+        dk[:, g] += one["dK"][:, 0, :Sk]
+        dv[:, g] += one["dV"][:, 0, :Sk]
+    np.testing.assert_allclose(ref["dK"], dk, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ref["dV"], dv, rtol=1e-12, atol=1e-12)
+
+
+def test_sink_gradient_finite_differences():
+    """dSink_h against central differences of L = <O, dO> in the sink logits (float64)."""
+    q, k, v, do, m, sinks = _sink_problem(22, Sq=5, Sk=6, D=4)
+    sc = 0.6
+    ref = oracle.backward(q, k, v, do, m, scale=sc, sinks=sinks)
+    assert np.abs(ref["dSink"]).min() > 1e-6
+
+    def loss(s):
+        O, _ = oracle.forward(q, k, v, m, scale=sc, sinks=s, threads=1)
+        return float(np.sum(O * do))
+
+    h = 1e-6
+    for i in range(len(sinks)):
+        sp, sm = sinks.copy(), sinks.copy()
+        sp[i] += h
+        sm[i] -= h
+        fd = (loss(sp) - loss(sm)) / (2 * h)
+        assert abs(fd - ref["dSink"][i]) <= 1e-7 * max(1.0, abs(ref["dSink"][i])), (i, fd, ref["dSink"][i])
+    # dQ / dK / dV with sinks also match finite differences (the sink changes P through the LSE)
+    for name_t, t, grad in (("q", q, ref["dQ"]), ("v", v, ref["dV"])):
+        idx = tuple(np.unravel_index(np.argmax(np.abs(grad)), grad.shape))
+        tp, tm = t.copy(), t.copy()
+        tp[idx] += h
+        tm[idx] -= h
+        args_p = {"q": q, "k": k, "v": v, name_t: tp}
+        args_m = {"q": q, "k": k, "v": v, name_t: tm}
+        Op, _ = oracle.forward(args_p["q"], args_p["k"], args_p["v"], m, scale=sc, sinks=sinks, threads=1)
+        Om, _ = oracle.forward(args_m["q"], args_m["k"], args_m["v"], m, scale=sc, sinks=sinks, threads=1)
+        fd = (np.sum(Op * do) - np.sum(Om * do)) / (2 * h)
+        assert abs(fd - grad[idx]) <= 1e-7 * abs(grad[idx]), (name_t, fd, grad[idx])
+
+
+def test_sink_closed_forms():
+    """One key and a sink: P = sigmoid(s - sink), O = P v, LSE = log(exp(s) + exp(sink)). A row with every
+    key masked keeps only the sink: O = 0, LSE = sink exactly, and its dQ is 0. A sink of -inf is no sink."""
+    rng = np.random.default_rng(23)
+    q, k, v, do = (rng.standard_normal((1, 1, 3, 4)), rng.standard_normal((1, 1, 1, 4)),
+                   rng.standard_normal((1, 1, 1, 4)), rng.standard_normal((1, 1, 3, 4)))
+    sinks = np.array([0.7])
+    m = np.zeros((1, 3, 1))
+    m[0, 1, 0] = -np.inf
+    r = oracle.backward(q, k, v, do, m, scale=0.5, sinks=sinks)
+    for i in (0, 2):
+        s = 0.5 * float(q[0, 0, i] @ k[0, 0, 0])
+        p = 1.0 / (1.0 + math.exp(sinks[0] - s))
+        np.testing.assert_allclose(r["O"][0, 0, i], p * v[0, 0, 0], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(r["LSE"][0, 0, i], math.log(math.exp(s) + math.exp(sinks[0])), rtol=1e-14)
+    assert np.all(r["O"][0, 0, 1] == 0) and r["LSE"][0, 0, 1] == sinks[0] and np.all(r["dQ"][0, 0, 1] == 0)
+    q2, k2, v2, do2, m2, _ = _sink_problem(24)
+    a = oracle.backward(q2, k2, v2, do2, m2, scale=0.3)
+    b = oracle.backward(q2, k2, v2, do2, m2, scale=0.3, sinks=np.full(4, -np.inf))
+    for n in ("O", "LSE", "dQ", "dK", "dV"):
+        assert np.array_equal(a[n], b[n]), n
