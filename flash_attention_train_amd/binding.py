@@ -35,7 +35,7 @@ class FaAttnParams(ctypes.Structure):
                 ("fwd_variant", ctypes.c_int32), ("kv_split", ctypes.c_int32), ("q_split", ctypes.c_int32),
                 ("fwd_split", ctypes.c_int32), ("key_len", ctypes.c_void_p), ("q_len", ctypes.c_void_p),
                 ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
-                ("bwd_dq_launch", ctypes.c_int32)]
+                ("bwd_dq_launch", ctypes.c_int32), ("sinks", ctypes.c_void_p)]
 
 
 class FaError(RuntimeError):
@@ -64,6 +64,7 @@ SIGNATURES = {
     "fa_train_version": ([], ctypes.c_int),
     "fa_train_mask_tiles_bytes": ([_PP], ctypes.c_size_t),
     "fa_train_mask_tiles": ([_PP, _VP, _VP], ctypes.c_int),
+    "fa_train_bwd_sinks": ([_PP, _PV, _PV, _VP, _VP], ctypes.c_int),
     "fa_train_probe_mfma": ([ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP], ctypes.c_int),
     "fa_train_probe_ds_read_tr16": ([ctypes.c_int32, _VP, _VP, _VP], ctypes.c_int),
 }
@@ -122,7 +123,8 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
                 q_offset: Optional[int], mask: Optional[torch.Tensor], fwd_variant: int = 0, kv_split: int = 0,
                 q_split: int = 0, mask_tiles: Optional[torch.Tensor] = None, fwd_split: int = 0,
                 key_len: Optional[torch.Tensor] = None, q_len: Optional[torch.Tensor] = None,
-                window: tuple = (-1, -1), dq_launch: int = 0) -> FaAttnParams:
+                window: tuple = (-1, -1), dq_launch: int = 0,
+                sinks: Optional[torch.Tensor] = None) -> FaAttnParams:
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Sk, Dk = k.shape
     if Bk != B or Dk != D:
@@ -139,6 +141,10 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
             if t.dtype != torch.int32 or t.dim() != 1 or t.shape[0] != n or not t.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous int32 [B] tensor on the device")
             setattr(p, name, t.data_ptr())
+    if sinks is not None:
+        if sinks.dtype != torch.float32 or sinks.shape != (Hq,) or not sinks.is_contiguous():
+            raise ValueError("sinks must be a contiguous fp32 [Hq] tensor on the device")
+        p.sinks = sinks.data_ptr()
     if mask is not None:
         if mask.dtype != torch.float32 or mask.dim() != 3 or mask.stride(2) != 1:
             raise ValueError("mask must be an fp32 [Bm, Sq, Sk] tensor with a contiguous last dimension")
@@ -188,12 +194,15 @@ def fwd_workspace_bytes(q, k, *, scale=None, causal=False, q_offset=None, mask=N
 
 
 def fwd(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, out=None, lse=None, stream=None,
-        variant=0, mask_tiles=None, workspace=None, split=0, key_len=None, q_len=None, window=(-1, -1)):
+        variant=0, mask_tiles=None, workspace=None, split=0, key_len=None, q_len=None, window=(-1, -1),
+        sinks=None):
     """Forward: returns (O, LSE). O has q's dtype and shape; LSE is fp32 [B, Hq, Sq].
     Runs fa_train_fwd_ws: a short grid may split the key walks (split = 0: the library's
-    choice; 1: never), with `workspace` (allocated here when None and needed)."""
+    choice; 1: never), with `workspace` (allocated here when None and needed). ``sinks``:
+    optional fp32 [Hq] attention-sink logits."""
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, fwd_variant=variant,
-                    mask_tiles=mask_tiles, fwd_split=split, key_len=key_len, q_len=q_len, window=window)
+                    mask_tiles=mask_tiles, fwd_split=split, key_len=key_len, q_len=q_len, window=window,
+                    sinks=sinks)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
@@ -219,6 +228,22 @@ def bwd_preprocess(o, dout, *, delta=None, stream=None):
     _check("fa_train_bwd_preprocess",
            lib().fa_train_bwd_preprocess(ctypes.byref(p), view4(o), view4(dout), view3(delta), _stream_handle(stream)))
     return delta
+
+
+def bwd_sinks(lse, delta, sinks, *, dsink=None, stream=None):
+    """Gradient of the attention sinks, ADDED into ``dsink`` (fp32 [Hq]; a zeroed one is made when
+    None): dsink[h] += -sum over the head's rows of exp(sinks[h] - LSE) * Delta."""
+    B, Hq, Sq = lse.shape
+    if dsink is None:
+        dsink = torch.zeros(Hq, dtype=torch.float32, device=lse.device)
+    if sinks.dtype != torch.float32 or sinks.shape != (Hq,) or not sinks.is_contiguous():
+        raise ValueError("sinks must be a contiguous fp32 [Hq] tensor on the device")
+    p = FaAttnParams(B, Hq, Hq, Sq, Sq, 64, FA_BF16, 0, 0, 1.0)
+    p.window_left = p.window_right = -1
+    p.sinks = sinks.data_ptr()
+    _check("fa_train_bwd_sinks", lib().fa_train_bwd_sinks(ctypes.byref(p), view3(lse), view3(delta),
+                                                          dsink.data_ptr(), _stream_handle(stream)))
+    return dsink
 
 
 def bwd_workspace_bytes(q, k, *, scale=None, causal=False, q_offset=None, mask=None, kv_split=0, q_split=0,

@@ -89,6 +89,8 @@ fa_status check_params(const fa_attn_params* p) {
       p->fwd_split > 64)
     return fail(FA_ERR_SHAPE, "split hints must be in 0 .. 64");
   if (p->window_left < -1 || p->window_right < -1) return fail(FA_ERR_SHAPE, "window bounds must be >= -1");
+  if (p->sinks && p->dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "attention sinks are implemented for bf16 only");
+  if (reinterpret_cast<uintptr_t>(p->sinks) % 4) return fail(FA_ERR_ALIGN, "sinks is not 4-byte aligned");
   if (p->bwd_dq_launch < 0 || p->bwd_dq_launch > 2)
     return fail(FA_ERR_SHAPE, "bwd_dq_launch must be 0, 1 or 2 (got %d)", p->bwd_dq_launch);
   if (reinterpret_cast<uintptr_t>(p->key_len) % 4 || reinterpret_cast<uintptr_t>(p->q_len) % 4)
@@ -496,6 +498,7 @@ fa_status fwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   a.inv_scale = 1.f / p->scale;
   const uintptr_t mp = reinterpret_cast<uintptr_t>(p->mask);
   a.mask_vec4 = p->mask && mp % 16 == 0 && p->mask_stride_q % 4 == 0 && p->mask_stride_b % 4 == 0;
+  a.sinks = p->sinks;
   a.splits = splits;
   a.part_o = nullptr;
   a.part_ml = nullptr;
@@ -568,6 +571,40 @@ fa_status fa_train_bwd_preprocess(const fa_attn_params* p, const fa_view* o, con
   a.delta_sb = delta->stride_b;
   a.delta_sh = delta->stride_h;
   return hip_status(fa::launch_preprocess(a, p->dtype == FA_BF16, stream), "preprocess");
+}
+
+fa_status fa_train_bwd_sinks(const fa_attn_params* p, const fa_view* lse, const fa_view* delta, float* dsink,
+                             hipStream_t stream) {
+  g_err[0] = 0;
+  fa_status s = check_params(p);
+  if (s) return s;
+  if (!p->sinks) return fail(FA_ERR_NULL, "the params carry no sinks");
+  if (!dsink) return fail(FA_ERR_NULL, "dsink is NULL");
+  if (reinterpret_cast<uintptr_t>(dsink) % 4) return fail(FA_ERR_ALIGN, "dsink is not 4-byte aligned");
+  Extent el, ed;
+  for (const fa_view* v : {lse, delta}) {
+    if (!v) return fail(FA_ERR_NULL, "lse / delta view is NULL");
+    if (v->stride_s != 1) return fail(FA_ERR_STRIDE, "lse / delta stride_s must be 1");
+  }
+  if ((s = check_view(lse, "lse", p->B, p->Hq, p->Sq, 1, 4, false, false, &el))) return s;
+  if ((s = check_view(delta, "delta", p->B, p->Hq, p->Sq, 1, 4, false, false, &ed))) return s;
+  const uintptr_t d0 = reinterpret_cast<uintptr_t>(dsink), s0 = reinterpret_cast<uintptr_t>(p->sinks);
+  const Extent eds = {d0, d0 + (uintptr_t)p->Hq * 4}, es = {s0, s0 + (uintptr_t)p->Hq * 4};
+  if (overlaps(eds, el) || overlaps(eds, ed) || overlaps(eds, es))
+    return fail(FA_ERR_ALIAS, "dsink overlaps the LSE, Delta or the sinks");
+  fa::SinkArgs a;
+  a.B = p->B;
+  a.Hq = p->Hq;
+  a.Sq = p->Sq;
+  a.sinks = p->sinks;
+  a.lse = static_cast<const float*>(lse->data);
+  a.delta = static_cast<const float*>(delta->data);
+  a.lse_sb = lse->stride_b;
+  a.lse_sh = lse->stride_h;
+  a.delta_sb = delta->stride_b;
+  a.delta_sh = delta->stride_h;
+  a.dsink = dsink;
+  return hip_status(fa::launch_sink_grad(a, stream), "sink gradient");
 }
 
 size_t fa_train_bwd_workspace_bytes(const fa_attn_params* p) {

@@ -4,7 +4,8 @@
 //     gradients per tile);
 //   * clearing the fp32 dQ accumulator;
 //   * converting the accumulated dQ to its output dtype with the softmax scale;
-//   * classifying the additive mask's 64 x 64 blocks for the forward and backward.
+//   * classifying the additive mask's 64 x 64 blocks for the forward and backward;
+//   * the gradient of the attention sinks from the LSE and Delta.
 // The first three stream their operands once with 16-byte loads and stores.
 #include "fa_device.h"
 #include "fa_kernels.h"
@@ -192,7 +193,38 @@ hipError_t launch_dq_t(const DqArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Gradient of the attention sinks: one workgroup per (chunk of a head's B * Sq rows,
+// head); every thread sums exp(sink - LSE) * Delta over its rows, the workgroup reduces
+// the sums (lane shuffles, then one value per wave in LDS) and adds the negated total
+// to dsink[h] with one atomic.
+constexpr int kSinkRows = 2048;  // rows per workgroup
+__global__ __launch_bounds__(256) void sink_grad_kernel(const SinkArgs p) {
+  const int h = blockIdx.y;
+  const int64_t rows = (int64_t)p.B * p.Sq;
+  const float sink = p.sinks[h];
+  float acc = 0.f;
+  for (int64_t r = (int64_t)blockIdx.x * kSinkRows + threadIdx.x; r < min(rows, (int64_t)(blockIdx.x + 1) * kSinkRows);
+       r += 256) {
+    const int b = (int)(r / p.Sq), i = (int)(r % p.Sq);
+    const float lse = p.lse[b * p.lse_sb + h * p.lse_sh + i];
+    const float dl = p.delta[b * p.delta_sb + h * p.delta_sh + i];
+    acc += expf(sink - lse) * dl;
+  }
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  __shared__ float part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicAdd(p.dsink + h, -(part[0] + part[1] + part[2] + part[3]));
+}
+
 }  // namespace
+
+hipError_t launch_sink_grad(const SinkArgs& p, hipStream_t stream) {
+  const int64_t rows = (int64_t)p.B * p.Sq;
+  const dim3 grid((unsigned)((rows + kSinkRows - 1) / kSinkRows), p.Hq);
+  hipLaunchKernelGGL(sink_grad_kernel, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_preprocess(const PreArgs& p, int is_bf16, hipStream_t stream) {
   if (is_bf16) return p.D == 64 ? launch_pre_t<bf16, 64>(p, stream) : launch_pre_t<bf16, 128>(p, stream);

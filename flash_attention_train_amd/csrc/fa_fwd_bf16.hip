@@ -414,14 +414,26 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     }
     return;
   }
-  // epilogue: O = acc / l, LSE = (base + log2 l) ln 2; fully masked rows -> 0, 0
+  // epilogue: O = acc / l, LSE = (base + log2 l) ln 2; fully masked rows -> 0, 0. A sink
+  // joins the row sum as 2^(sink log2e - base) after both move to the larger base (a row
+  // with every key masked then keeps only the sink: O = 0, LSE = sink)
+  const float sb = args.sinks ? args.sinks[h] * kLog2e : neg_inf();
   #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qw + 32 * qb + r32;
-    const float lt = lsum[qb] + xor32(lsum[qb]);
-    const bool full = base[qb] == neg_inf();
-    const float inv = full ? 0.f : 1.f / lt;
-    const float lse = full ? 0.f : (base[qb] + log2f(lt)) * kLn2;
+    float lt = lsum[qb] + xor32(lsum[qb]);
+    float inv, lse;
+    if (sb != neg_inf()) {
+      const float nb = fmaxf(base[qb], sb);
+      const float fo = base[qb] == neg_inf() ? 0.f : fast_exp2(base[qb] - nb);
+      lt = lt * fo + fast_exp2(sb - nb);
+      inv = fo / lt;
+      lse = base[qb] == neg_inf() ? args.sinks[h] : (nb + log2f(lt)) * kLn2;
+    } else {
+      const bool full = base[qb] == neg_inf();
+      inv = full ? 0.f : 1.f / lt;
+      lse = full ? 0.f : (base[qb] + log2f(lt)) * kLn2;
+    }
     if (row < a.Sq) {
       bf16* O = static_cast<bf16*>(args.o) + b * args.so.b + h * args.so.h + (int64_t)row * args.so.s;
       #pragma unroll
@@ -441,7 +453,8 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
 
 // Merge of a split forward: per row, the partial rows are rescaled to the largest base
 // and summed, O = sum / (rescaled row sums), LSE = (base + log2 sum) ln 2; a row no split
-// saw a key for (every base -inf) gets O = 0, LSE = 0. One pass over the splits with a
+// saw a key for (every base -inf) gets O = 0, LSE = 0 (or LSE = its head's sink, which
+// joins the row sum here). One pass over the splits with a
 // running base (the online softmax's own rescale), one thread per 8 columns of a row.
 template <int D>
 __global__ __launch_bounds__(256) void fwd_merge_kernel(const FwdArgs args) {
@@ -468,15 +481,26 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const FwdArgs args) {
     l = l * fo + ml.y * fn;
     mx = nm;
   }
-  const bool full = mx == neg_inf();
-  const float inv = full ? 0.f : 1.f / l;
   const int i = (int)(r % a.Sq);
   const int h = (int)((r / a.Sq) % a.Hq), b = (int)(r / ((int64_t)a.Sq * a.Hq));
+  float inv, lse;
+  const float sb = args.sinks ? args.sinks[h] * kLog2e : neg_inf();
+  if (sb != neg_inf()) {  // the sink joins the row sum at the larger of the two bases
+    const float nb = fmaxf(mx, sb);
+    const float fo = mx == neg_inf() ? 0.f : fast_exp2(mx - nb);
+    l = l * fo + fast_exp2(sb - nb);
+    inv = fo / l;
+    lse = mx == neg_inf() ? args.sinks[h] : (nb + log2f(l)) * kLn2;
+  } else {
+    const bool full = mx == neg_inf();
+    inv = full ? 0.f : 1.f / l;
+    lse = full ? 0.f : (mx + log2f(l)) * kLn2;
+  }
   bf16* O = static_cast<bf16*>(args.o) + b * args.so.b + h * args.so.h + (int64_t)i * args.so.s + c;
   *reinterpret_cast<bf16x8*>(O) = bf16x8{(bf16)(lo[0] * inv), (bf16)(lo[1] * inv), (bf16)(lo[2] * inv),
                                          (bf16)(lo[3] * inv), (bf16)(hi[0] * inv), (bf16)(hi[1] * inv),
                                          (bf16)(hi[2] * inv), (bf16)(hi[3] * inv)};
-  if (c == 0) args.lse[b * args.lse_sb + h * args.lse_sh + i] = full ? 0.f : (mx + log2f(l)) * kLn2;
+  if (c == 0) args.lse[b * args.lse_sb + h * args.lse_sh + i] = lse;
 }
 
 template <int D>

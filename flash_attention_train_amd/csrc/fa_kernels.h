@@ -121,6 +121,7 @@ struct FwdArgs {
   int64_t lse_sb, lse_sh;
   float inv_scale;  // 1 / scale (scale > 0)
   int mask_vec4;    // the mask can be read 4 floats at a time (16-byte aligned rows)
+  const float* sinks;  // [Hq] sink logits (natural log) joining each row's denominator, or null
   // split key walks (splits > 1): workgroup z walks the z-th share of the key tiles and
   // stores its unnormalised fp32 O rows and (base, row sum) per row, merged afterwards
   int splits;
@@ -135,6 +136,16 @@ struct PreArgs {
   float* delta;
   Strides so, sdo;
   int64_t delta_sb, delta_sh;
+};
+
+// dsink[h] += -sum over the head's rows of exp(sinks[h] - LSE) * Delta
+struct SinkArgs {
+  int B, Hq, Sq;
+  const float* sinks;
+  const float* lse;
+  const float* delta;
+  int64_t lse_sb, lse_sh, delta_sb, delta_sh;
+  float* dsink;
 };
 
 struct BwdArgs {
@@ -202,6 +213,7 @@ hipError_t launch_bwd(const BwdArgs& args, int is_bf16, hipStream_t stream);
 hipError_t launch_dq_convert(const DqArgs& args, int is_bf16, hipStream_t stream);
 // reduces args, and args1 too when given (same shape and dtype: one launch for dK and dV)
 hipError_t launch_reduce_parts(const ReduceArgs& args, const ReduceArgs* args1, int is_bf16, hipStream_t stream);
+hipError_t launch_sink_grad(const SinkArgs& args, hipStream_t stream);
 void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, int dq_separate, BwdPlan* plan);
 hipError_t launch_bwd_bf16(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream);
 

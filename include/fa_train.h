@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FA_TRAIN_ABI_VERSION 4
+#define FA_TRAIN_ABI_VERSION 5
 
 typedef enum fa_status {
     FA_OK = 0,
@@ -132,6 +132,14 @@ typedef struct fa_attn_params {
      * dK/dV workgroups' launch, 2 = they run as a second kernel after it, two per compute
      * unit (chosen automatically for grids of at least 512 dQ workgroups). */
     int32_t bwd_dq_launch;
+    /* Attention sinks (bf16 only): one more logit per query head that joins every row's
+     * softmax denominator and has no value row (llama.cpp pull request 57 lists sinks
+     * among the score modifiers its flash backward lacked). sinks[h] is a natural-log
+     * logit, used as given (not scaled): LSE_i = ln(sum_j exp(S_ij) + exp(sinks[h])), and
+     * O_i = sum_j exp(S_ij - LSE_i) v_j. A row whose every key is masked then has
+     * O = 0 and LSE = sinks[h]. The backward is unchanged (it reads the LSE); the sinks'
+     * own gradient comes from fa_train_bwd_sinks. */
+    const float* sinks;      /* device [Hq] fp32, 4-byte aligned; NULL = none */
 } fa_attn_params;
 
 /* Forward: writes O (dtype) and LSE (fp32, natural log). Fully masked rows get
@@ -215,6 +223,17 @@ fa_status fa_train_mask_tiles(const fa_attn_params* p, uint8_t* tiles, hipStream
 const char* fa_train_status_str(fa_status s);
 /* Detail text of the calling thread's last error ("" if none). */
 const char* fa_train_last_error(void);
+/* Gradient of the attention sinks: ADDS, for every query head h,
+ *   dsink[h] += -sum_{b, i} exp(sinks[h] - LSE[b, h, i]) * Delta[b, h, i]
+ * (the sink is a softmax column with no value, so its dS is P_sink (0 - Delta_i)). LSE and
+ * Delta are the forward's and the preprocess's fp32 outputs [B, Hq, Sq] (stride_s 1); a
+ * fully masked row has Delta = 0 and adds nothing. dsink: device fp32 [Hq], never zeroed
+ * by the library (the caller clears it, or keeps adding as a gradient accumulator). The
+ * sum is reduced per workgroup and added with one fp32 atomic per workgroup and head, so
+ * its rounding order varies from run to run. Needs p->sinks. */
+fa_status fa_train_bwd_sinks(const fa_attn_params* p, const fa_view* lse, const fa_view* delta, float* dsink,
+                             hipStream_t stream);
+
 /* FA_TRAIN_ABI_VERSION of the loaded library. */
 int fa_train_version(void);
 
