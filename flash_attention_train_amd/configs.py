@@ -12,7 +12,7 @@ from __future__ import annotations
 
 from dataclasses import dataclass
 
-from .inputs import BF16, F32, Case, make_case
+from .inputs import BF16, F32, Case, make_case, sink_logits
 
 
 @dataclass(frozen=True)
@@ -40,6 +40,10 @@ WORKLOADS = {
                            "key length 1388 (the pad as a length)", 6, (2, 1)),
     "dit_sa_band": Workload("dit_sa_band", "DiT self-attention, mixed-length batch B=2 Hq=16 Hkv=8 S=1542 D=128 "
                             "bf16, key lengths 1542 / 1101, window 256 keys each side", 7),
+    # the LM layer with one attention-sink logit per query head (N(0, 1)); its step adds the
+    # sinks' gradient pass
+    "lm_sinks": Workload("lm_sinks", "LM causal GQA with attention sinks, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 8,
+                         (2, 1)),
 }
 
 # the sliding window of the structured DiT workload: keys within this distance on each
@@ -74,10 +78,13 @@ def make(key: str, **shrink) -> Case:
             lo_hi["lo"] = max(1, shrink["Sk"] // 4)
         a.update(shrink)
         return make_case(key, seed=s, mask="ca_keypad", mask_args=lo_hi, **a)
-    if key == "lm_causal":
+    if key in ("lm_causal", "lm_sinks"):
         a = dict(B=1, Hq=32, Hkv=8, Sq=4096, Sk=4096, D=128, dtype=BF16, do_std=0.1)
         a.update(shrink)
-        return make_case(key, seed=s, causal=True, q_offset=0, **a)
+        c = make_case(key, seed=s, causal=True, q_offset=0, **a)
+        if key == "lm_sinks":
+            c.meta["sinks"] = sink_logits(s, c.Hq)
+        return c
     if key in ("dit_sa_len", "dit_sa_band"):
         a = dict(B=1 if key == "dit_sa_len" else 2, Hq=16, Hkv=8, Sq=1542, Sk=1542, D=128, dtype=BF16)
         a.update(shrink)

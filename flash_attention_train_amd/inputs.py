@@ -155,6 +155,14 @@ def random_bias_mask(rng: np.random.Generator, Bm: int, Sq: int, Sk: int, p_mask
     return bias
 
 
+def sink_logits(seed: int, Hq: int, std: float = 1.0) -> np.ndarray:
+    """Seeded per-head attention-sink logits, float32 [Hq], N(0, std^2): drawn from their
+    own generator stream (seed + 7919), so that adding sinks to a case changes none of its
+    other inputs."""
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    return (std * rng.standard_normal(Hq)).astype(np.float32)
+
+
 def make_case(name: str, *, B: int, Hq: int, Hkv: int, Sq: int, Sk: int, D: int, dtype: str,
               seed: int, causal: bool = False, q_offset: Optional[int] = None, do_std: float = 1.0,
               mask: str = "none", mask_args: Optional[dict] = None, scale: Optional[float] = None) -> Case:

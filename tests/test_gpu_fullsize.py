@@ -174,3 +174,38 @@ def test_long_window_walk_full_size():
     e_k = np.abs(dk_sum).max() / np.abs(got["dK"][0]).sum(axis=1).max()
     say(f"    identities: sum dV vs sum dO {e_v:.2e}, |sum dK| / sum |dK| {e_k:.2e}")
     assert e_v <= TOL[c.dtype] and e_k <= TOL[c.dtype]
+
+
+def test_lm_sinks_full_size_sampled():
+    """The LM layer with attention sinks, as the bench runs it: sampled rows (O, LSE, Delta, dQ) and key
+    columns (dK, dV) against the oracle with the same sinks, and the sinks' gradient against its
+    definition summed on the host over every row's GPU LSE and Delta (a property at any size; the
+    LSE and Delta themselves are pinned by the sampled rows)."""
+    c = configs.make("lm_sinks")
+    say("lm_sinks: full size, sampled rows and columns, sink gradient over all rows")
+    t = upload(c)
+    sinks = torch.from_numpy(c.meta["sinks"]).to("cuda")
+    o, lse = binding.fwd(t["q"], t["k"], t["v"], scale=c.scale, causal=True, q_offset=0, sinks=sinks)
+    delta = binding.bwd_preprocess(o, t["do"])
+    dq, dk, dv = binding.bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, scale=c.scale, causal=True, q_offset=0)
+    dsink = binding.bwd_sinks(lse, delta, sinks)
+    torch.cuda.synchronize()
+    got = {"O": host64(o), "LSE": host64(lse), "Delta": host64(delta), "dQ": host64(dq), "dK": host64(dk),
+           "dV": host64(dv)}
+    s64 = c.meta["sinks"].astype(np.float64)
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, 1, c.Sq - 1, 7 * c.Sq + 2], rng.choice(c.Hq * c.Sq, 80, replace=False)])
+                     ).astype(np.int64)
+    ref = oracle.rows(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), rows, scale=c.scale, causal=True,
+                      q_offset=0, sinks=s64)
+    _check_rows(c, got, rows, ref, TOL[c.dtype])
+    cols = np.unique(np.concatenate([[0, c.Sk - 1], rng.choice(np.arange(c.Sk, 2 * c.Sk), 8, replace=False)])
+                     ).astype(np.int64)
+    refc = oracle.cols(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), cols, scale=c.scale, causal=True,
+                       q_offset=0, sinks=s64)
+    _check_cols(c, got["dK"], got["dV"], cols, refc, TOL[c.dtype])
+    terms = np.exp(s64[None, :, None] - got["LSE"]) * got["Delta"]
+    want = -terms.sum(axis=(0, 2))
+    e = np.abs(dsink.cpu().numpy().astype(np.float64) - want).max() / np.abs(terms).sum(axis=(0, 2)).max()
+    say(f"    dSink vs the host sum over all rows: {e:.2e}")
+    assert e <= 1e-5
