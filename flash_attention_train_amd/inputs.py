@@ -163,6 +163,25 @@ def sink_logits(seed: int, Hq: int, std: float = 1.0) -> np.ndarray:
     return (std * rng.standard_normal(Hq)).astype(np.float32)
 
 
+def quantize_q8_0(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Store a [..., D] array the way a q8_0 K/V cache holds it (ggml's q8_0 block: 32
+    consecutive values share one fp16 scale d = max|x| / 127, each value kept as the int8
+    q = round(x / d), halves away from zero). Returns (qs int8 [..., D], d float16
+    [..., D / 32]); the stored value is d * q. This prepares inputs: the cache arrives
+    quantized, and the op and its checker both start from (qs, d)."""
+    x = np.asarray(x, np.float32)
+    D = x.shape[-1]
+    if D % 32:
+        raise ValueError("q8_0 blocks need D to be a multiple of 32")
+    xb = x.reshape(*x.shape[:-1], D // 32, 32)
+    d = np.abs(xb).max(axis=-1) / np.float32(127)
+    inv = np.where(d > 0, np.float32(1) / np.where(d > 0, d, 1), 0).astype(np.float32)
+    v = xb * inv[..., None]
+    q = np.trunc(v + np.copysign(np.float32(0.5), v))
+    qs = np.clip(q, -127, 127).astype(np.int8).reshape(x.shape)
+    return qs, d.astype(np.float16)
+
+
 def make_case(name: str, *, B: int, Hq: int, Hkv: int, Sq: int, Sk: int, D: int, dtype: str,
               seed: int, causal: bool = False, q_offset: Optional[int] = None, do_std: float = 1.0,
               mask: str = "none", mask_args: Optional[dict] = None, scale: Optional[float] = None) -> Case:

@@ -166,6 +166,19 @@ def cols(q, k, v, do, col_ids, mask=None, *, scale: float, causal: bool = False,
     return out
 
 
+def dequant_q8_0(qs, d) -> np.ndarray:
+    """The values a q8_0 K/V window holds (llama.cpp pull request 57 trains such a quantised cache in
+    place): blocks of 32 consecutive values along the head dimension share one fp16 scale, and value
+    t of block b is d[b] * qs[32 b + t]. qs: int8 [..., D]; d: float16 [..., D / 32]; float64 out."""
+    qs = np.asarray(qs)
+    d = np.asarray(d)
+    D = qs.shape[-1]
+    out = np.empty(qs.shape, np.float64)
+    for b in range(D // 32):
+        out[..., 32 * b:32 * (b + 1)] = d[..., b:b + 1].astype(np.float64) * qs[..., 32 * b:32 * (b + 1)]
+    return out
+
+
 def structured_mask(B: int, Sq: int, Sk: int, *, key_len=None, q_len=None, window_left: int = -1,
                     window_right: int = -1, q_offset: int = 0, causal: bool = False) -> np.ndarray:
     """The dense additive mask [B, Sq, Sk] (0 / -inf) of a structured mask, entry by entry:

@@ -491,3 +491,38 @@ def test_sink_closed_forms():
     b = oracle.backward(q2, k2, v2, do2, m2, scale=0.3, sinks=np.full(4, -np.inf))
     for n in ("O", "LSE", "dQ", "dK", "dV"):
         assert np.array_equal(a[n], b[n]), n
+
+
+# ---------------------------------------------------------------------------
+# q8_0 K/V window: the stored values, pinned to a block worked by hand, and the
+# seeded quantizer's round trip on values already on the q8_0 grid
+# ---------------------------------------------------------------------------
+def test_q8_0_dequant_golden_block():
+    with open(os.path.join(GOLDEN, "q8_0_blocks.json")) as f:
+        g = json.load(f)
+    t = np.arange(32)
+    qs = np.concatenate([t - 16, 31 - 2 * t]).astype(np.int8)[None, None, None]
+    d = np.array(g["d"], np.float16)[None, None, None]
+    x = oracle.dequant_q8_0(qs, d)
+    assert x.shape == (1, 1, 1, 64)
+    for i, want in g["expect"].items():
+        assert x[0, 0, 0, int(i)] == want, (i, x[0, 0, 0, int(i)], want)
+
+
+def test_q8_0_quantizer_round_trip_on_grid_values():
+    """Values d * q with d a power of two and max |q| = 127 in every block survive quantize -> dequantize
+    exactly; values off the grid come back within half a step plus the fp16 rounding of the scale
+    (d / 2 + 127 |d - fp16(d)|, with |d - fp16(d)| <= 2^-11 d)."""
+    from flash_attention_train_amd.inputs import quantize_q8_0
+    rng = np.random.default_rng(31)
+    q = rng.integers(-127, 128, size=(2, 3, 5, 128))
+    q[..., ::32] = 127  # every block reaches the end of the range
+    d = 2.0 ** rng.integers(-6, 2, size=(2, 3, 5, 4))
+    x = (np.repeat(d, 32, axis=-1) * q).astype(np.float32)
+    qs, dh = quantize_q8_0(x)
+    np.testing.assert_array_equal(oracle.dequant_q8_0(qs, dh), x.astype(np.float64))
+    y = rng.standard_normal((3, 4, 64)).astype(np.float32)
+    qs, dh = quantize_q8_0(y)
+    back = oracle.dequant_q8_0(qs, dh)
+    step = np.repeat(dh.astype(np.float64), 32, axis=-1)
+    assert np.all(np.abs(back - y) <= step * (0.5 + 127 * 2.0 ** -11) * (1 + 1e-3))
