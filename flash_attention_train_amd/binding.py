@@ -65,6 +65,8 @@ SIGNATURES = {
     "fa_train_mask_tiles_bytes": ([_PP], ctypes.c_size_t),
     "fa_train_mask_tiles": ([_PP, _VP, _VP], ctypes.c_int),
     "fa_train_bwd_sinks": ([_PP, _PV, _PV, _VP, _VP], ctypes.c_int),
+    "fa_train_dequant_q8_0": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _PV, _PV, _PV, _VP],
+                              ctypes.c_int),
     "fa_train_probe_mfma": ([ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP], ctypes.c_int),
     "fa_train_probe_ds_read_tr16": ([ctypes.c_int32, _VP, _VP, _VP], ctypes.c_int),
 }
@@ -244,6 +246,21 @@ def bwd_sinks(lse, delta, sinks, *, dsink=None, stream=None):
     _check("fa_train_bwd_sinks", lib().fa_train_bwd_sinks(ctypes.byref(p), view3(lse), view3(delta),
                                                           dsink.data_ptr(), _stream_handle(stream)))
     return dsink
+
+
+def dequant_q8_0(qs, d, *, out=None, stream=None):
+    """bf16 values of a q8_0-stored K or V window: ``qs`` int8 [B, H, S, D], ``d`` fp16 [B, H, S, D / 32]
+    (views with a contiguous last dimension). Writes ``out`` (bf16 [B, H, S, D], made when None)."""
+    if qs.dtype != torch.int8 or d.dtype != torch.float16:
+        raise TypeError("qs must be int8 and d float16")
+    B, H, S, D = qs.shape
+    if tuple(d.shape) != (B, H, S, D // 32):
+        raise ValueError("d must be [B, H, S, D / 32]")
+    if out is None:
+        out = torch.empty(qs.shape, dtype=torch.bfloat16, device=qs.device)
+    _check("fa_train_dequant_q8_0", lib().fa_train_dequant_q8_0(B, H, S, D, view4(qs), view4(d), view4(out),
+                                                                _stream_handle(stream)))
+    return out
 
 
 def bwd_workspace_bytes(q, k, *, scale=None, causal=False, q_offset=None, mask=None, kv_split=0, q_split=0,

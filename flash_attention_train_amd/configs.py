@@ -12,7 +12,7 @@ from __future__ import annotations
 
 from dataclasses import dataclass
 
-from .inputs import BF16, F32, Case, make_case, sink_logits
+from .inputs import BF16, F32, Case, make_case, quantize_q8_0, sink_logits
 
 
 @dataclass(frozen=True)
@@ -44,6 +44,10 @@ WORKLOADS = {
     # sinks' gradient pass
     "lm_sinks": Workload("lm_sinks", "LM causal GQA with attention sinks, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 8,
                          (2, 1)),
+    # the long-window walk over a q8_0-stored K/V window (the pages train such a cache in
+    # place): the same queries and K/V values, quantised to q8_0 blocks
+    "long_window_q8": Workload("long_window_q8", "long-window chunked walk over a q8_0 K/V window, W=32768, "
+                               "64 chunks of 512, Hq=16 Hkv=4 D=128", 9),
 }
 
 # the sliding window of the structured DiT workload: keys within this distance on each
@@ -98,11 +102,14 @@ def make(key: str, **shrink) -> Case:
             c.meta["structure"] = {"key_len": lens, "q_len": None, "window": (w, w)}
         c.meta["mask_kind"] = "structured"
         return c
-    if key == "long_window":
+    if key in ("long_window", "long_window_q8"):
         W = shrink.pop("W", LONG_WINDOW)
         a = dict(B=1, Hq=16, Hkv=4, Sq=W, Sk=W, D=128, dtype=BF16)
         a.update(shrink)
-        return make_case(key, seed=s, causal=True, q_offset=0, **a)
+        c = make_case(key, seed=s, causal=True, q_offset=0, **a)
+        if key == "long_window_q8":  # the cache holds the K / V values as q8_0 blocks
+            c.meta["q8"] = {"k": quantize_q8_0(c.f64("k")), "v": quantize_q8_0(c.f64("v"))}
+        return c
     raise KeyError(key)
 
 

@@ -607,6 +607,32 @@ fa_status fa_train_bwd_sinks(const fa_attn_params* p, const fa_view* lse, const 
   return hip_status(fa::launch_sink_grad(a, stream), "sink gradient");
 }
 
+fa_status fa_train_dequant_q8_0(int32_t B, int32_t H, int32_t S, int32_t D, const fa_view* qs, const fa_view* d,
+                                const fa_view* out, hipStream_t stream) {
+  g_err[0] = 0;
+  if (B < 1 || H < 1 || S < 1) return fail(FA_ERR_SHAPE, "B, H and S must be positive");
+  if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", D);
+  Extent eq, ed, eo;
+  fa_status s;
+  if ((s = check_view(qs, "qs", B, H, S, D, 1, true, false, &eq))) return s;
+  if ((s = check_view(d, "d", B, H, S, D / 32, 2, false, false, &ed))) return s;
+  if ((s = check_view(out, "out", B, H, S, D, 2, true, true, &eo))) return s;
+  if (d->stride_s < D / 32 && S > 1) return fail(FA_ERR_STRIDE, "d: stride_s must cover the row's D / 32 scales");
+  if (overlaps(eo, eq) || overlaps(eo, ed)) return fail(FA_ERR_ALIAS, "out overlaps qs or d");
+  fa::DequantArgs a;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.D = D;
+  a.qs = static_cast<const int8_t*>(qs->data);
+  a.d = static_cast<const _Float16*>(d->data);
+  a.out = out->data;
+  a.sq = strides_of(qs);
+  a.sd = strides_of(d);
+  a.so = strides_of(out);
+  return hip_status(fa::launch_dequant_q8_0(a, stream), "q8_0 dequant");
+}
+
 size_t fa_train_bwd_workspace_bytes(const fa_attn_params* p) {
   if (check_params(p) != FA_OK) return (size_t)-1;
   return workspace_bytes(p);

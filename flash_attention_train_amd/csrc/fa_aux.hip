@@ -5,7 +5,8 @@
 //   * clearing the fp32 dQ accumulator;
 //   * converting the accumulated dQ to its output dtype with the softmax scale;
 //   * classifying the additive mask's 64 x 64 blocks for the forward and backward;
-//   * the gradient of the attention sinks from the LSE and Delta.
+//   * the gradient of the attention sinks from the LSE and Delta;
+//   * the bf16 values of a q8_0-stored K/V window.
 // The first three stream their operands once with 16-byte loads and stores.
 #include "fa_device.h"
 #include "fa_kernels.h"
@@ -217,7 +218,38 @@ __global__ __launch_bounds__(256) void sink_grad_kernel(const SinkArgs p) {
   if (threadIdx.x == 0) atomicAdd(p.dsink + h, -(part[0] + part[1] + part[2] + part[3]));
 }
 
+// q8_0 window rows to bf16: one thread per 16 consecutive values of a row (one 16-byte
+// load of quants, the block's fp16 scale, two 16-byte stores). The fp32 product of an
+// fp16 scale and an int8 quant is exact; the one rounding is to bf16 (nearest even).
+__global__ __launch_bounds__(256) void dequant_q8_0_kernel(const DequantArgs p) {
+  const int per_row = p.D / 16;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rows = (int64_t)p.B * p.H * p.S;
+  if (t >= rows * per_row) return;
+  const int64_t row = t / per_row;
+  const int c16 = (int)(t % per_row);
+  const int s = (int)(row % p.S), h = (int)((row / p.S) % p.H), b = (int)(row / ((int64_t)p.S * p.H));
+  typedef int8_t i8x16 __attribute__((ext_vector_type(16)));
+  const i8x16 q = *reinterpret_cast<const i8x16*>(p.qs + b * p.sq.b + h * p.sq.h + (int64_t)s * p.sq.s + 16 * c16);
+  const float d = (float)p.d[b * p.sd.b + h * p.sd.h + (int64_t)s * p.sd.s + c16 / 2];
+  bf16x8 lo, hi;
+  #pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    lo[e] = (bf16)(d * (float)q[e]);
+    hi[e] = (bf16)(d * (float)q[8 + e]);
+  }
+  bf16* o = static_cast<bf16*>(p.out) + b * p.so.b + h * p.so.h + (int64_t)s * p.so.s + 16 * c16;
+  *reinterpret_cast<bf16x8*>(o) = lo;
+  *reinterpret_cast<bf16x8*>(o + 8) = hi;
+}
+
 }  // namespace
+
+hipError_t launch_dequant_q8_0(const DequantArgs& p, hipStream_t stream) {
+  const int64_t threads = (int64_t)p.B * p.H * p.S * (p.D / 16);
+  hipLaunchKernelGGL(dequant_q8_0_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_sink_grad(const SinkArgs& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.B * p.Sq;

@@ -214,6 +214,16 @@ hipError_t launch_dq_convert(const DqArgs& args, int is_bf16, hipStream_t stream
 // reduces args, and args1 too when given (same shape and dtype: one launch for dK and dV)
 hipError_t launch_reduce_parts(const ReduceArgs& args, const ReduceArgs* args1, int is_bf16, hipStream_t stream);
 hipError_t launch_sink_grad(const SinkArgs& args, hipStream_t stream);
+
+// bf16 values of a q8_0 window: out[b][h][s][32 c + t] = bf16(d[b][h][s][c] * qs[b][h][s][32 c + t])
+struct DequantArgs {
+  int B, H, S, D;
+  const int8_t* qs;
+  const _Float16* d;
+  void* out;  // bf16
+  Strides sq, sd, so;  // element strides of qs, d and out
+};
+hipError_t launch_dequant_q8_0(const DequantArgs& args, hipStream_t stream);
 void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, int dq_separate, BwdPlan* plan);
 hipError_t launch_bwd_bf16(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream);
 

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FA_TRAIN_ABI_VERSION 5
+#define FA_TRAIN_ABI_VERSION 6
 
 typedef enum fa_status {
     FA_OK = 0,
@@ -233,6 +233,20 @@ const char* fa_train_last_error(void);
  * its rounding order varies from run to run. Needs p->sinks. */
 fa_status fa_train_bwd_sinks(const fa_attn_params* p, const fa_view* lse, const fa_view* delta, float* dsink,
                              hipStream_t stream);
+
+/* q8_0 K/V window (llama.cpp pull request 57 trains a q8_0-quantised cache in place): the
+ * rows of a window stored as ggml's q8_0 blocks -- 32 consecutive values along D share
+ * one fp16 scale d, each value is the int8 q, the stored value is d * q -- written out as
+ * bf16 (one rounding, to nearest even; the fp32 product is exact) into `out`, the bf16
+ * K or V view the bf16 entry points read. The exact walk calls it once per chunk for the
+ * window rows the chunk adds, so every row is converted once per walk and the gradient
+ * flows to the stored values (dK/dV accumulate in fp32 as for a bf16 window).
+ *   qs : int8 [B, H, S, D] view (element = byte strides), rows 16-byte aligned
+ *   d  : fp16 [B, H, S, D / 32] view (element strides), 2-byte aligned, stride_s >= D / 32
+ *   out: bf16 [B, H, S, D] view, rows 16-byte aligned; must not overlap qs or d
+ * D is 64 or 128. */
+fa_status fa_train_dequant_q8_0(int32_t B, int32_t H, int32_t S, int32_t D, const fa_view* qs, const fa_view* d,
+                                const fa_view* out, hipStream_t stream);
 
 /* FA_TRAIN_ABI_VERSION of the loaded library. */
 int fa_train_version(void);

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(L, n), n
         assert n in B.SIGNATURES, f"{n} has no ctypes signature in the binding"
-    assert L.fa_train_version() == 5
+    assert L.fa_train_version() == 6
 
 
 BASE = 0x7F0000000000  # fake, 256-byte aligned device addresses
