@@ -37,7 +37,8 @@ class _Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("Sq", ctypes.c_int32), ("Sk", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("mask_b", ctypes.c_int32),
-                ("q_offset", ctypes.c_int64), ("scale", ctypes.c_double), ("sinks", ctypes.c_void_p)]
+                ("q_offset", ctypes.c_int64), ("scale", ctypes.c_double), ("sinks", ctypes.c_void_p),
+                ("alibi", ctypes.c_void_p)]
 
 
 _lib = None
@@ -74,7 +75,7 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
-def _problem(q, k, mask, scale, causal, q_offset, sinks=None):
+def _problem(q, k, mask, scale, causal, q_offset, sinks=None, alibi=None):
     B, Hq, Sq, D = q.shape
     _, Hkv, Sk, _ = k.shape
     if q_offset is None:
@@ -84,15 +85,18 @@ def _problem(q, k, mask, scale, causal, q_offset, sinks=None):
         raise ValueError("mask must be [Bm, Sq, Sk]")
     if sinks is not None and sinks.shape != (Hq,):
         raise ValueError("sinks must be [Hq]")
+    if alibi is not None and alibi.shape != (Hq,):
+        raise ValueError("alibi must be [Hq]")
     return _Problem(B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), mb, int(q_offset), float(scale),
-                    None if sinks is None else sinks.ctypes.data)
+                    None if sinks is None else sinks.ctypes.data, None if alibi is None else alibi.ctypes.data)
 
 
 def forward(q, k, v, mask=None, *, scale: float, causal: bool = False, q_offset: Optional[int] = None,
-            threads: Optional[int] = None, sinks=None):
-    """Returns (O [B,Hq,Sq,D], LSE [B,Hq,Sq]) in float64. ``sinks``: optional [Hq] sink logits."""
-    q, k, v, mask, sinks = _f64(q), _f64(k), _f64(v), _f64(mask), _f64(sinks)
-    p = _problem(q, k, mask, scale, causal, q_offset, sinks)
+            threads: Optional[int] = None, sinks=None, alibi=None):
+    """Returns (O [B,Hq,Sq,D], LSE [B,Hq,Sq]) in float64. ``sinks``: optional [Hq] sink logits;
+    ``alibi``: optional [Hq] ALiBi slopes."""
+    q, k, v, mask, sinks, alibi = _f64(q), _f64(k), _f64(v), _f64(mask), _f64(sinks), _f64(alibi)
+    p = _problem(q, k, mask, scale, causal, q_offset, sinks, alibi)
     O = np.zeros(q.shape, np.float64)
     L = np.zeros(q.shape[:3], np.float64)
     rc = _load().ora_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(O), _ptr(L),
@@ -103,11 +107,11 @@ def forward(q, k, v, mask=None, *, scale: float, causal: bool = False, q_offset:
 
 
 def backward(q, k, v, do, mask=None, *, scale: float, causal: bool = False, q_offset: Optional[int] = None,
-             threads: Optional[int] = None, sinks=None) -> dict:
+             threads: Optional[int] = None, sinks=None, alibi=None) -> dict:
     """The full forward and backward. Returns a dict with O, LSE, Delta, dQ, dK, dV (float64), and
-    dSink [Hq] when ``sinks`` ([Hq] sink logits) is given."""
-    q, k, v, do, mask, sinks = _f64(q), _f64(k), _f64(v), _f64(do), _f64(mask), _f64(sinks)
-    p = _problem(q, k, mask, scale, causal, q_offset, sinks)
+    dSink [Hq] when ``sinks`` ([Hq] sink logits) is given. ``alibi``: optional [Hq] ALiBi slopes."""
+    q, k, v, do, mask, sinks, alibi = _f64(q), _f64(k), _f64(v), _f64(do), _f64(mask), _f64(sinks), _f64(alibi)
+    p = _problem(q, k, mask, scale, causal, q_offset, sinks, alibi)
     out = {"O": np.zeros(q.shape), "LSE": np.zeros(q.shape[:3]), "Delta": np.zeros(q.shape[:3]),
            "dQ": np.zeros(q.shape), "dK": np.zeros(k.shape), "dV": np.zeros(k.shape)}
     rc = _load().ora_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(do),
@@ -135,10 +139,10 @@ def sink_grad(sinks, lse, delta) -> np.ndarray:
 
 
 def rows(q, k, v, do, row_ids, mask=None, *, scale: float, causal: bool = False,
-         q_offset: Optional[int] = None, threads: Optional[int] = None, sinks=None) -> dict:
+         q_offset: Optional[int] = None, threads: Optional[int] = None, sinks=None, alibi=None) -> dict:
     """Selected rows, ids (b*Hq + h)*Sq + i. Returns O [n,D], LSE [n], Delta [n], dQ [n,D]."""
-    q, k, v, do, mask, sinks = _f64(q), _f64(k), _f64(v), _f64(do), _f64(mask), _f64(sinks)
-    p = _problem(q, k, mask, scale, causal, q_offset, sinks)
+    q, k, v, do, mask, sinks, alibi = _f64(q), _f64(k), _f64(v), _f64(do), _f64(mask), _f64(sinks), _f64(alibi)
+    p = _problem(q, k, mask, scale, causal, q_offset, sinks, alibi)
     ids = np.ascontiguousarray(row_ids, dtype=np.int64)
     n, D = ids.size, q.shape[3]
     out = {"O": np.zeros((n, D)), "LSE": np.zeros(n), "Delta": np.zeros(n), "dQ": np.zeros((n, D))}
@@ -151,10 +155,10 @@ def rows(q, k, v, do, row_ids, mask=None, *, scale: float, causal: bool = False,
 
 
 def cols(q, k, v, do, col_ids, mask=None, *, scale: float, causal: bool = False,
-         q_offset: Optional[int] = None, threads: Optional[int] = None, sinks=None) -> dict:
+         q_offset: Optional[int] = None, threads: Optional[int] = None, sinks=None, alibi=None) -> dict:
     """Selected key columns, ids (b*Hkv + g)*Sk + j. Returns dK [n,D], dV [n,D]."""
-    q, k, v, do, mask, sinks = _f64(q), _f64(k), _f64(v), _f64(do), _f64(mask), _f64(sinks)
-    p = _problem(q, k, mask, scale, causal, q_offset, sinks)
+    q, k, v, do, mask, sinks, alibi = _f64(q), _f64(k), _f64(v), _f64(do), _f64(mask), _f64(sinks), _f64(alibi)
+    p = _problem(q, k, mask, scale, causal, q_offset, sinks, alibi)
     ids = np.ascontiguousarray(col_ids, dtype=np.int64)
     n, D = ids.size, q.shape[3]
     out = {"dK": np.zeros((n, D)), "dV": np.zeros((n, D))}

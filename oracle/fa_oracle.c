@@ -13,6 +13,9 @@
  *   row fully masked (m_i = -inf):  O_i = 0, LSE_i = 0, P_i. = 0
  *   otherwise: LSE_i = m_i + ln (sum_j exp(S_ij - m_i) + exp(sink_h - m_i)),
  *              P_ij = exp(S_ij - LSE_i),  O_i = sum_j P_ij v_j
+ *   (with ALiBi slopes a_h, S_ij also gets -a_h |j - (q_offset + i)|: a linear
+ *   penalty on the distance between key and query positions, llama.cpp pull
+ *   request 57's score modifiers; under a causal mask it is a_h (j - q_offset - i))
  *   (an attention sink is one more logit per head in the softmax's denominator,
  *   with no value row: llama.cpp pull request 57, the list of score modifiers
  *   whose flash backward was missing; its own gradient is formed from LSE and
@@ -55,6 +58,7 @@ typedef struct {
     int64_t q_offset;
     double scale;
     const double *sinks; /* [Hq] logits, NULL = none */
+    const double *alibi; /* [Hq] slopes, NULL = none */
 } ora_problem;
 
 typedef struct {
@@ -110,6 +114,7 @@ static double score(const ora_inputs *in, int b, int h, int i, int j) {
         int mb = p->mask_b == 1 ? 0 : b;
         mv = in->M[((int64_t)mb * p->Sq + i) * p->Sk + j];
     }
+    if (p->alibi) mv -= p->alibi[h] * fabs((double)j - (double)(p->q_offset + i));
     int g = kv_head(p, h);
     return p->scale * dot(q_row(in, b, h, i), k_row(in, b, g, j), p->D) + mv;
 }

@@ -526,3 +526,97 @@ def test_q8_0_quantizer_round_trip_on_grid_values():
     back = oracle.dequant_q8_0(qs, dh)
     step = np.repeat(dh.astype(np.float64), 32, axis=-1)
     assert np.all(np.abs(back - y) <= step * (0.5 + 127 * 2.0 ** -11) * (1 + 1e-3))
+
+
+# ---------------------------------------------------------------------------
+# ALiBi slopes (S_ij gets -a_h |j - (q_offset + i)|): pinned to torch CPU float64
+# autograd with the bias written out, to finite differences, and to the geometric
+# series the LSE becomes when every raw score is zero
+# ---------------------------------------------------------------------------
+ALIBI_CASES = {
+    "causal_gqa": dict(B=2, Hq=4, Hkv=2, Sq=6, Sk=6, causal=True, q_offset=0),
+    "causal_offset": dict(B=1, Hq=2, Hkv=1, Sq=4, Sk=9, causal=True, q_offset=5),
+    "bidirectional_masked": dict(B=2, Hq=2, Hkv=2, Sq=5, Sk=7, causal=False, q_offset=0, mask=True),
+}
+
+
+def _alibi_problem(name, seed):
+    a = dict(ALIBI_CASES[name])
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, Sq, Sk, D = a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], 5
+    q, k, v, do = (rng.standard_normal(s) for s in ((B, Hq, Sq, D), (B, Hkv, Sk, D), (B, Hkv, Sk, D), (B, Hq, Sq, D)))
+    m = None
+    if a.get("mask"):
+        m = np.zeros((B, Sq, Sk))
+        m[1, :, Sk - 2:] = -np.inf
+        m[0, 3, :] = -np.inf
+    slopes = 2.0 ** (-8.0 * np.arange(1, Hq + 1) / Hq)
+    return q, k, v, do, m, slopes, a["causal"], a["q_offset"]
+
+
+@pytest.mark.parametrize("name", list(ALIBI_CASES))
+def test_alibi_torch_autograd_crosscheck(name):
+    torch = pytest.importorskip("torch")
+    q, k, v, do, m, slopes, causal, off = _alibi_problem(name, 51)
+    sc = 0.4
+    r = oracle.backward(q, k, v, do, m, scale=sc, causal=causal, q_offset=off, alibi=slopes)
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    pos = off + np.arange(Sq)
+    bias = -slopes[None, :, None, None] * np.abs(np.arange(Sk)[None, None, None, :] - pos[None, None, :, None])
+    bias = np.broadcast_to(bias, (B, Hq, Sq, Sk)).copy()
+    if m is not None:
+        bias = bias + m[:, None]
+    if causal:
+        bias = np.where(np.arange(Sk)[None, None, None, :] > pos[None, None, :, None], -np.inf, bias)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    s = sc * torch.matmul(tq, tk.repeat_interleave(G, dim=1).transpose(-1, -2).contiguous()) + torch.tensor(bias)
+    full = np.isinf(bias).all(axis=3)  # fully masked rows: the library gives NaN there, the oracle 0
+    s = torch.where(torch.tensor(full)[..., None], torch.zeros_like(s), s)  # (kept finite, then dropped)
+    p = torch.softmax(s, dim=-1)
+    p = torch.where(torch.tensor(full)[..., None], torch.zeros_like(p), p)
+    o = torch.matmul(p, tv.repeat_interleave(G, dim=1))
+    lse = torch.logsumexp(s, dim=-1)
+    (o * torch.tensor(do)).sum().backward()
+    np.testing.assert_allclose(r["O"], o.detach().numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["LSE"][~full], lse.detach().numpy()[~full], rtol=1e-10, atol=1e-12)
+    for n, t in (("dQ", tq), ("dK", tk), ("dV", tv)):
+        np.testing.assert_allclose(r[n], t.grad.numpy(), rtol=1e-9, atol=1e-11, err_msg=n)
+
+
+def test_alibi_finite_differences():
+    q, k, v, do, m, slopes, causal, off = _alibi_problem("causal_offset", 52)
+    sc = 0.7
+    r = oracle.backward(q, k, v, do, m, scale=sc, causal=causal, q_offset=off, alibi=slopes)
+
+    def loss(a):
+        O, _ = oracle.forward(a["q"], a["k"], a["v"], m, scale=sc, causal=causal, q_offset=off, alibi=slopes,
+                              threads=1)
+        return float(np.sum(O * do))
+
+    h = 1e-6
+    for name_t, t, grad in (("q", q, r["dQ"]), ("k", k, r["dK"]), ("v", v, r["dV"])):
+        fd = np.zeros_like(t)
+        for idx in np.ndindex(t.shape):
+            tp, tm = t.copy(), t.copy()
+            tp[idx] += h
+            tm[idx] -= h
+            fd[idx] = (loss({"q": q, "k": k, "v": v, name_t: tp}) - loss({"q": q, "k": k, "v": v, name_t: tm})) / (2 * h)
+        assert np.abs(fd - grad).max() / np.abs(grad).max() < 1e-7, name_t
+
+
+def test_alibi_zero_scores_geometric_series():
+    """Q = 0 under a causal mask: row i sees keys 0..i with scores -a (i - j), so
+    LSE_i = ln sum_{t=0}^{i} exp(-a t) = ln((1 - exp(-a (i + 1))) / (1 - exp(-a)))."""
+    rng = np.random.default_rng(53)
+    S, D = 7, 4
+    q = np.zeros((1, 2, S, D))
+    k, v = rng.standard_normal((1, 2, S, D)), rng.standard_normal((1, 2, S, D))
+    slopes = np.array([0.5, 0.125])
+    O, L = oracle.forward(q, k, v, scale=1.0, causal=True, q_offset=0, alibi=slopes)
+    for h, a in enumerate(slopes):
+        i = np.arange(S)
+        np.testing.assert_allclose(L[0, h], np.log((1 - np.exp(-a * (i + 1))) / (1 - np.exp(-a))), rtol=1e-14)
+        w = np.exp(-a * (S - 1 - np.arange(S)))  # last row's weights
+        np.testing.assert_allclose(O[0, h, S - 1], (w / w.sum()) @ v[0, h], rtol=1e-13)
