@@ -35,7 +35,7 @@ class FaAttnParams(ctypes.Structure):
                 ("fwd_variant", ctypes.c_int32), ("kv_split", ctypes.c_int32), ("q_split", ctypes.c_int32),
                 ("fwd_split", ctypes.c_int32), ("key_len", ctypes.c_void_p), ("q_len", ctypes.c_void_p),
                 ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
-                ("bwd_dq_launch", ctypes.c_int32), ("sinks", ctypes.c_void_p)]
+                ("bwd_dq_launch", ctypes.c_int32), ("sinks", ctypes.c_void_p), ("alibi", ctypes.c_void_p)]
 
 
 class FaError(RuntimeError):
@@ -126,7 +126,7 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
                 q_split: int = 0, mask_tiles: Optional[torch.Tensor] = None, fwd_split: int = 0,
                 key_len: Optional[torch.Tensor] = None, q_len: Optional[torch.Tensor] = None,
                 window: tuple = (-1, -1), dq_launch: int = 0,
-                sinks: Optional[torch.Tensor] = None) -> FaAttnParams:
+                sinks: Optional[torch.Tensor] = None, alibi: Optional[torch.Tensor] = None) -> FaAttnParams:
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Sk, Dk = k.shape
     if Bk != B or Dk != D:
@@ -143,10 +143,11 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
             if t.dtype != torch.int32 or t.dim() != 1 or t.shape[0] != n or not t.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous int32 [B] tensor on the device")
             setattr(p, name, t.data_ptr())
-    if sinks is not None:
-        if sinks.dtype != torch.float32 or sinks.shape != (Hq,) or not sinks.is_contiguous():
-            raise ValueError("sinks must be a contiguous fp32 [Hq] tensor on the device")
-        p.sinks = sinks.data_ptr()
+    for name, t in (("sinks", sinks), ("alibi", alibi)):
+        if t is not None:
+            if t.dtype != torch.float32 or t.shape != (Hq,) or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous fp32 [Hq] tensor on the device")
+            setattr(p, name, t.data_ptr())
     if mask is not None:
         if mask.dtype != torch.float32 or mask.dim() != 3 or mask.stride(2) != 1:
             raise ValueError("mask must be an fp32 [Bm, Sq, Sk] tensor with a contiguous last dimension")
@@ -197,14 +198,14 @@ def fwd_workspace_bytes(q, k, *, scale=None, causal=False, q_offset=None, mask=N
 
 def fwd(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, out=None, lse=None, stream=None,
         variant=0, mask_tiles=None, workspace=None, split=0, key_len=None, q_len=None, window=(-1, -1),
-        sinks=None):
+        sinks=None, alibi=None):
     """Forward: returns (O, LSE). O has q's dtype and shape; LSE is fp32 [B, Hq, Sq].
     Runs fa_train_fwd_ws: a short grid may split the key walks (split = 0: the library's
     choice; 1: never), with `workspace` (allocated here when None and needed). ``sinks``:
     optional fp32 [Hq] attention-sink logits."""
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, fwd_variant=variant,
                     mask_tiles=mask_tiles, fwd_split=split, key_len=key_len, q_len=q_len, window=window,
-                    sinks=sinks)
+                    sinks=sinks, alibi=alibi)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
@@ -281,11 +282,11 @@ def _workspace(p: FaAttnParams, device, workspace):
 
 def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_offset=None, dq=None, dk=None,
         dv=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None, q_len=None,
-        window=(-1, -1), dq_launch=0):
+        window=(-1, -1), dq_launch=0, alibi=None):
     """Backward: returns (dQ, dK, dV), each in q's dtype, overwritten."""
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, window=window,
-                    dq_launch=dq_launch)
+                    dq_launch=dq_launch, alibi=alibi)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
@@ -336,12 +337,12 @@ def tune_bwd_splits(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=
 
 def bwd_chunked(q, k, v, dout, lse, delta, dk_acc, dv_acc, *, mask=None, scale=None, causal=True, q_offset=None,
                 dq=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None,
-                q_len=None, window=(-1, -1), dq_launch=0):
+                q_len=None, window=(-1, -1), dq_launch=0, alibi=None):
     """Chunked backward: returns dQ for the chunk; ADDS dK/dV into the fp32 window
     accumulators ``dk_acc`` / ``dv_acc`` ([B, Hkv, >= Sk, D])."""
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len,
-                    q_len=q_len, window=window, dq_launch=dq_launch)
+                    q_len=q_len, window=window, dq_launch=dq_launch, alibi=alibi)
     if dk_acc.dtype != torch.float32 or dv_acc.dtype != torch.float32:
         raise TypeError("the window accumulators must be float32")
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq

@@ -91,6 +91,8 @@ fa_status check_params(const fa_attn_params* p) {
   if (p->window_left < -1 || p->window_right < -1) return fail(FA_ERR_SHAPE, "window bounds must be >= -1");
   if (p->sinks && p->dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "attention sinks are implemented for bf16 only");
   if (reinterpret_cast<uintptr_t>(p->sinks) % 4) return fail(FA_ERR_ALIGN, "sinks is not 4-byte aligned");
+  if (p->alibi && p->dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "ALiBi is implemented for bf16 only");
+  if (reinterpret_cast<uintptr_t>(p->alibi) % 4) return fail(FA_ERR_ALIGN, "alibi is not 4-byte aligned");
   if (p->bwd_dq_launch < 0 || p->bwd_dq_launch > 2)
     return fail(FA_ERR_SHAPE, "bwd_dq_launch must be 0, 1 or 2 (got %d)", p->bwd_dq_launch);
   if (reinterpret_cast<uintptr_t>(p->key_len) % 4 || reinterpret_cast<uintptr_t>(p->q_len) % 4)
@@ -142,6 +144,7 @@ fa::AttnShape shape_of(const fa_attn_params* p) {
   a.q_len = p->q_len;
   a.wl = p->window_left;
   a.wr = p->window_right;
+  a.alibi = p->alibi;
   return a;
 }
 

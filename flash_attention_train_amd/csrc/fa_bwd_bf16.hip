@@ -84,7 +84,7 @@ __device__ __forceinline__ QUnit q_unit_of(const AttnShape& a, const BwdPlan& pl
 // compiled without the mask-value reads, which keeps their loop free of that code.
 // Called by the whole workgroup: the threads test the blocks together.
 __device__ __forceinline__ bool any_bias_block(const AttnShape& a, int b, int rb0, int nrb, int cb0, int ncb) {
-  if (!a.tiles) return true;
+  if (!a.tiles || a.alibi) return true;
   const int nrt = (a.Sq + kMaskTile - 1) / kMaskTile, nct = (a.Sk + kMaskTile - 1) / kMaskTile;
   nrb = min(nrb, nrt - rb0);
   ncb = min(ncb, nct - cb0);
@@ -403,7 +403,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     int h, q0;
     pair_of(cur, h, q0);
     const int cls = class_of(cls_cur);
-    const bool bias = MASK && cls == kTileBias;  // read mask values
+    const bool bias = MASK && (cls == kTileBias || a.alibi);  // add mask values and / or ALiBi
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
     const bf16* qb_lds = q_lds + buf * KV_BM * D;
     const bf16* db_lds = do_lds + buf * KV_BM * D;
@@ -472,7 +472,15 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
       uint32_t w;
     };
     auto stats_b = [&](int qb, f32x16& sacc, RowStats& st) {
-      if (BIAS && bias) {
+      if (BIAS && bias && a.alibi) {
+        // ALiBi in raw score units: -(slope / scale) |key - position|; this lane's key, the
+        // register's row: key - position = (key - q_offset - q0 - 32 qb - 4 g) - 8 (r/4) - r%4
+        const float sl = a.alibi[h] * args.inv_scale;
+        const float base = (float)((int64_t)key - a.q_offset - q0 - 32 * qb - 4 * g);
+        #pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] -= sl * fabsf(base - (float)(8 * (r >> 2) + (r & 3)));
+      }
+      if (BIAS && bias && a.mask) {
         const float* mk = a.mask + b * a.mask_sb + min(key, a.Sk - 1);
         #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -746,7 +754,7 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
       stage_tile(ktn, buf ^ 1);  // lands while this tile is being processed
     }
     const int cls = class_of(cls_cur);
-    const bool bias = MASK && cls == kTileBias;  // read mask values
+    const bool bias = MASK && (cls == kTileBias || a.alibi);  // add mask values and / or ALiBi
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
     const bf16* kb_lds = k_lds + buf * Q_BN * D;
     const bf16* vb_lds = v_lds + buf * Q_BN * D;
@@ -809,7 +817,13 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
       }
       __builtin_amdgcn_sched_barrier(0);
       // lane (query row, half g), register r -> key 32 kb + 8 (r/4) + 4 g + r%4
-      if (BIAS && bias) {  // additive mask values, 4 keys at a time (keys past the end read 0)
+      if (BIAS && bias && a.alibi) {  // ALiBi, as in the forward (lane = row, register = key)
+        const float sl = a.alibi[h] * args.inv_scale;
+        const float base = (float)((int64_t)key0 + 32 * kb + 4 * g - a.q_offset - row);
+        #pragma unroll
+        for (int r = 0; r < 16; ++r) st[r] -= sl * fabsf(base + (float)(8 * (r >> 2) + (r & 3)));
+      }
+      if (BIAS && bias && a.mask) {  // additive mask values, 4 keys at a time (keys past the end read 0)
         const float* mr = a.mask + b * a.mask_sb + (int64_t)min(row, a.Sq - 1) * a.mask_sq;
         #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -931,7 +945,7 @@ hipError_t launch_cm(const BwdArgs& args, const BwdPlan& plan, hipStream_t strea
 
 template <int D>
 hipError_t launch_t(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream) {
-  const bool causal = args.a.causal != 0, mask = args.a.mask != nullptr;
+  const bool causal = args.a.causal != 0, mask = args.a.mask != nullptr || args.a.alibi != nullptr;
   if (causal && mask) return launch_cm<D, true, true>(args, plan, stream);
   if (causal) return launch_cm<D, true, false>(args, plan, stream);
   if (mask) return launch_cm<D, false, true>(args, plan, stream);

@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     const bf16* vb_lds = v_lds[kh][buf];
     const int cls = kt < kt_end ? class_of(cls_cur) : kTileDead;  // a key half may sit out the last step
     if (cls != kTileDead) {
-    const bool bias = MASK && cls == kTileBias;  // read mask values
+    const bool bias = MASK && (cls == kTileBias || a.alibi);  // add mask values and / or ALiBi
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
 
     // S^T = K Q^T for both 32-key blocks; each K fragment serves all QB query blocks
@@ -264,7 +264,18 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int row = qw + 32 * qb + r32;
-      if (MASK && bias) {
+      if (MASK && bias && a.alibi) {
+        // ALiBi in raw score units: -(slope / scale) |key - position|; this lane's row, the
+        // register's key: key - position = (key0 + 4 g - q_offset - row) + 32 kb + 8 rr + e
+        const float sl = a.alibi[h] * args.inv_scale;
+        const float base = (float)((int64_t)key0 + 4 * g - a.q_offset - row);
+        #pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          #pragma unroll
+          for (int r = 0; r < 16; ++r)
+            st[qb][kb][r] -= sl * fabsf(base + (float)(32 * kb + 8 * (r >> 2) + (r & 3)));
+      }
+      if (MASK && bias && a.mask) {
         // the mask enters the raw score as M / scale so that one fma applies both later;
         // keys past the end read 0 (the tail is masked below), rows past the end the last row
         const float* mr = a.mask + b * a.mask_sb + (int64_t)min(row, a.Sq - 1) * a.mask_sq;
@@ -506,7 +517,7 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const FwdArgs args) {
 template <int D>
 hipError_t launch_split_d(const FwdArgs& args, hipStream_t stream) {
   const dim3 grid(args.a.Hq * args.a.B, (args.a.Sq + 127) / 128, args.splits);
-  const bool causal = args.a.causal != 0, mask = args.a.mask != nullptr;
+  const bool causal = args.a.causal != 0, mask = args.a.mask != nullptr || args.a.alibi != nullptr;
   if (causal && mask)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, 64, true, true, 1, true>), grid, dim3(256), 0, stream, args);
   else if (causal)
@@ -526,7 +537,7 @@ template <int D, int QB, int BN, int KS>
 hipError_t launch_t(const FwdArgs& args, hipStream_t stream) {
   constexpr int BM = 4 / KS * QB * 32;
   const dim3 grid(args.a.Hq * args.a.B, (args.a.Sq + BM - 1) / BM);
-  const bool causal = args.a.causal != 0, mask = args.a.mask != nullptr;
+  const bool causal = args.a.causal != 0, mask = args.a.mask != nullptr || args.a.alibi != nullptr;
   if (causal && mask)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BN, true, true, KS>), grid, dim3(256), 0, stream, args);
   else if (causal)

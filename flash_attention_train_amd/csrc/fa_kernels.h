@@ -33,6 +33,9 @@ struct AttnShape {
   const int32_t* key_len;    // [B] or nullptr (Sk)
   const int32_t* q_len;      // [B] or nullptr (Sq)
   int wl, wr;                // window bounds, -1: none
+  // ALiBi: score (h, i, j) gets -alibi[h] |j - (q_offset + i)|; or nullptr. It runs in the
+  // masked kernels' bias body (every live block counts as a bias block)
+  const float* alibi;
 };
 
 // the structured lengths of batch entry b (clamped to the tensor lengths)

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FA_TRAIN_ABI_VERSION 6
+#define FA_TRAIN_ABI_VERSION 7
 
 typedef enum fa_status {
     FA_OK = 0,
@@ -140,6 +140,13 @@ typedef struct fa_attn_params {
      * O = 0 and LSE = sinks[h]. The backward is unchanged (it reads the LSE); the sinks'
      * own gradient comes from fa_train_bwd_sinks. */
     const float* sinks;      /* device [Hq] fp32, 4-byte aligned; NULL = none */
+    /* ALiBi (bf16 only; combines with every mask): a per-head linear penalty on the distance
+     * between a key and the query's position, one of the score modifiers the pull request's
+     * flash backward lacked. Score (b, h, i, j) gets -alibi[h] * |j - (q_offset + i)|, added
+     * like a mask value (after the scale); under a causal mask that is the usual
+     * alibi[h] * (j - q_offset - i). Positions are exact while |j - q_offset - i| < 2^24. It
+     * is a constant of the scores, so the backward's gradients need nothing more. */
+    const float* alibi;      /* device [Hq] fp32 slopes, 4-byte aligned; NULL = none */
 } fa_attn_params;
 
 /* Forward: writes O (dtype) and LSE (fp32, natural log). Fully masked rows get
