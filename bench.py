@@ -10,7 +10,7 @@ S=1542, D=128, bf16, pad mask): mask-adjusted fwd+bwd TFLOP/s (14 * D * N FLOPs
 per step, N = unmasked score pairs). Other workloads are reported under "extra".
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload dit_sa]
-                    [--extra lm_causal,dit_ca,long_window,dit_sa_len,dit_sa_band,lm_sinks,long_window_q8]
+                    [--extra lm_causal,dit_ca,long_window,dit_sa_len,dit_sa_band,lm_sinks,lm_alibi,long_window_q8]
                     [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dit_sa")
-    ap.add_argument("--extra", default="lm_causal,dit_ca,long_window,dit_sa_len,dit_sa_band,lm_sinks,long_window_q8",
+    ap.add_argument("--extra", default="lm_causal,dit_ca,long_window,dit_sa_len,dit_sa_band,lm_sinks,lm_alibi,long_window_q8",
                     help="other workloads to time, comma separated ('none' for none); long_window is the "
                          "64-chunk walk over a 32768-long window")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -81,6 +81,8 @@ class Workload:
         # attention sinks (per-head logits): given to the forward; the step adds their gradient
         self.sinks = None if c.meta.get("sinks") is None else torch.from_numpy(c.meta["sinks"]).to(dev)
         self.dsink = None if self.sinks is None else torch.zeros_like(self.sinks)
+        # ALiBi slopes (per head), given to the forward and the backward
+        self.alibi = None if c.meta.get("alibi") is None else torch.from_numpy(c.meta["alibi"]).to(dev)
         self.o = torch.empty_like(self.q)
         self.lse = torch.empty(c.B, c.Hq, c.Sq, dtype=torch.float32, device=dev)
         self.delta = torch.empty_like(self.lse)
@@ -127,7 +129,8 @@ class Workload:
     def fwd(self):
         c = self.case
         self.B.fwd(self.q, self.k, self.v, mask=self.mask, scale=c.scale, causal=c.causal, q_offset=c.q_offset,
-                   out=self.o, lse=self.lse, mask_tiles=self.tiles, workspace=self.fws, sinks=self.sinks, **self.sk)
+                   out=self.o, lse=self.lse, mask_tiles=self.tiles, workspace=self.fws, sinks=self.sinks,
+                   alibi=self.alibi, **self.sk)
 
     def pre(self):
         self.B.bwd_preprocess(self.o, self.do, delta=self.delta)
@@ -136,7 +139,7 @@ class Workload:
         c = self.case
         self.B.bwd(self.q, self.k, self.v, self.do, self.lse, self.delta, mask=self.mask, scale=c.scale,
                    causal=c.causal, q_offset=c.q_offset, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws,
-                   kv_split=self.kv_split, q_split=self.q_split, mask_tiles=self.tiles, **self.sk)
+                   kv_split=self.kv_split, q_split=self.q_split, mask_tiles=self.tiles, alibi=self.alibi, **self.sk)
         if self.sinks is not None:  # the sinks' gradient, added into their accumulator
             self.B.bwd_sinks(self.lse, self.delta, self.sinks, dsink=self.dsink)
 

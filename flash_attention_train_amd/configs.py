@@ -12,7 +12,7 @@ from __future__ import annotations
 
 from dataclasses import dataclass
 
-from .inputs import BF16, F32, Case, make_case, quantize_q8_0, sink_logits
+from .inputs import BF16, F32, Case, alibi_slopes, make_case, quantize_q8_0, sink_logits
 
 
 @dataclass(frozen=True)
@@ -46,6 +46,8 @@ WORKLOADS = {
                          (2, 1)),
     # the long-window walk over a q8_0-stored K/V window (the pages train such a cache in
     # place): the same queries and K/V values, quantised to q8_0 blocks
+    # the LM layer with ALiBi (slopes 2^(-8 (h + 1) / Hq)) in place of positional rotations
+    "lm_alibi": Workload("lm_alibi", "LM causal GQA with ALiBi, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 10, (2, 1)),
     "long_window_q8": Workload("long_window_q8", "long-window chunked walk over a q8_0 K/V window, W=32768, "
                                "64 chunks of 512, Hq=16 Hkv=4 D=128", 9),
 }
@@ -82,12 +84,14 @@ def make(key: str, **shrink) -> Case:
             lo_hi["lo"] = max(1, shrink["Sk"] // 4)
         a.update(shrink)
         return make_case(key, seed=s, mask="ca_keypad", mask_args=lo_hi, **a)
-    if key in ("lm_causal", "lm_sinks"):
+    if key in ("lm_causal", "lm_sinks", "lm_alibi"):
         a = dict(B=1, Hq=32, Hkv=8, Sq=4096, Sk=4096, D=128, dtype=BF16, do_std=0.1)
         a.update(shrink)
         c = make_case(key, seed=s, causal=True, q_offset=0, **a)
         if key == "lm_sinks":
             c.meta["sinks"] = sink_logits(s, c.Hq)
+        if key == "lm_alibi":
+            c.meta["alibi"] = alibi_slopes(c.Hq)
         return c
     if key in ("dit_sa_len", "dit_sa_band"):
         a = dict(B=1 if key == "dit_sa_len" else 2, Hq=16, Hkv=8, Sq=1542, Sk=1542, D=128, dtype=BF16)

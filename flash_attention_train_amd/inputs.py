@@ -163,6 +163,11 @@ def sink_logits(seed: int, Hq: int, std: float = 1.0) -> np.ndarray:
     return (std * rng.standard_normal(Hq)).astype(np.float32)
 
 
+def alibi_slopes(H: int) -> np.ndarray:
+    """The usual ALiBi slopes for H heads, 2^(-8 (h + 1) / H), float32 [H]."""
+    return (2.0 ** (-8.0 * np.arange(1, H + 1) / H)).astype(np.float32)
+
+
 def quantize_q8_0(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """Store a [..., D] array the way a q8_0 K/V cache holds it (ggml's q8_0 block: 32
     consecutive values share one fp16 scale d = max|x| / 127, each value kept as the int8

@@ -209,3 +209,32 @@ def test_lm_sinks_full_size_sampled():
     e = np.abs(dsink.cpu().numpy().astype(np.float64) - want).max() / np.abs(terms).sum(axis=(0, 2)).max()
     say(f"    dSink vs the host sum over all rows: {e:.2e}")
     assert e <= 1e-5
+
+
+def test_lm_alibi_full_size_sampled():
+    """The LM layer with ALiBi, as the bench runs it: sampled rows (O, LSE, Delta, dQ) and key columns
+    (dK, dV) against the oracle with the same slopes."""
+    c = configs.make("lm_alibi")
+    say("lm_alibi: full size, sampled rows and columns")
+    t = upload(c)
+    al = torch.from_numpy(c.meta["alibi"]).to("cuda")
+    kv, qs = configs.WORKLOADS["lm_alibi"].bwd_splits
+    o, lse = binding.fwd(t["q"], t["k"], t["v"], scale=c.scale, causal=True, q_offset=0, alibi=al)
+    delta = binding.bwd_preprocess(o, t["do"])
+    dq, dk, dv = binding.bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, scale=c.scale, causal=True, q_offset=0,
+                             alibi=al, kv_split=kv, q_split=qs)
+    torch.cuda.synchronize()
+    got = {"O": host64(o), "LSE": host64(lse), "Delta": host64(delta), "dQ": host64(dq), "dK": host64(dk),
+           "dV": host64(dv)}
+    a64 = c.meta["alibi"].astype(np.float64)
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 1, c.Sq - 1, 31 * c.Sq + 4000], rng.choice(c.Hq * c.Sq, 80, replace=False)])
+                     ).astype(np.int64)
+    ref = oracle.rows(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), rows, scale=c.scale, causal=True,
+                      q_offset=0, alibi=a64)
+    _check_rows(c, got, rows, ref, TOL[c.dtype])
+    cols = np.unique(np.concatenate([[0, c.Sk - 1], rng.choice(np.arange(7 * c.Sk, 8 * c.Sk), 8, replace=False)])
+                     ).astype(np.int64)
+    refc = oracle.cols(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), cols, scale=c.scale, causal=True,
+                       q_offset=0, alibi=a64)
+    _check_cols(c, got["dK"], got["dV"], cols, refc, TOL[c.dtype])
