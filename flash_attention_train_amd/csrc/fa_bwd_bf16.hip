@@ -346,27 +346,36 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
   };
   const int ct_w = ct0 + (32 * wave) / kMaskTile;  // this wave's 32 keys lie in one 64-key block
 
-  // Per-pair mask state of this wave, fetched one pair ahead (its loads complete under
-  // the end-of-iteration wait instead of stalling the pair): the block class and this
-  // lane's key column visibility word.
-  auto mask_state = [&](const Pos& x, ClassAhead& cls, uint64_t& w) {
-    cls = ClassAhead{0u, kSelBias};
+  // Per-pair mask state of this wave, taken one pair ahead (its load completes under the
+  // end-of-iteration wait instead of stalling the pair): the block class, from the wave's
+  // run of classes down its key column (reloaded every 64 row blocks), and, for a 0 / -inf
+  // block only, this lane's key column visibility word.
+  const int nrt_all = (a.Sq + kMaskTile - 1) / kMaskTile;
+  ClassRun run{kTileDead, -64};
+  auto load_run = [&](int qi) {
+    run.load(a, qi & ~63, ct_w < nct ? nrt_all - qt0 : 0,
+             [&](int pos) { return tile_index(a, b, qt0 + pos, ct_w); });
+  };
+  auto mask_state = [&](const Pos& x, int& cls, uint64_t& w) {
+    cls = kTileBias;
     w = ~0ull;
     if (MASK && a.tiles) {
-      cls.sel = kSelDead;
-      if (ct_w < nct) {
-        const int i = tile_index(a, b, qt0 + x.qi, ct_w);
-        cls = class_ahead(a, i);
-        w = a.colbits[(int64_t)i * kMaskTile + (key - ct_w * kMaskTile)];
-      }
+      if (x.qi >= run.base + 64) load_run(x.qi);  // (a longer walk: the next 64 row blocks)
+      cls = run.at(x.qi);
+      if (cls == kTileBits)
+        w = a.colbits[(int64_t)tile_index(a, b, qt0 + x.qi, ct_w) * kMaskTile + (key - ct_w * kMaskTile)];
     }
   };
 
   Pos cur = next_live(Pos{split, split / a.G, split % a.G, 0});
-  ClassAhead cls_cur{0u, kSelBias};
+  int cls_cur = kTileBias;
   uint64_t wb_cur = ~0ull;
   if (cur.p < npairs) {
     stage_pair(cur, 0);
+    if (MASK && a.tiles) {
+      load_run(cur.qi);
+      wait_vm();  // the run's classes, with the first pair's tiles
+    }
     mask_state(cur, cls_cur, wb_cur);
   }
   // The K / V operand fragments live in accumulation registers for the whole walk (matrix
@@ -394,7 +403,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     const int nb = buf == 2 ? 0 : buf + 1;
     const Pos nxt = next_live(advance(cur));
     const bool more = nxt.p < npairs;
-    ClassAhead cls_next{0u, kSelBias};
+    int cls_next = kTileBias;
     uint64_t wb_next = ~0ull;
     if (more) {
       mask_state(nxt, cls_next, wb_next);
@@ -402,7 +411,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     }
     int h, q0;
     pair_of(cur, h, q0);
-    const int cls = class_of(cls_cur);
+    const int cls = cls_cur;
     const bool bias = MASK && (cls == kTileBias || a.alibi);  // add mask values and / or ALiBi
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
     const bf16* qb_lds = q_lds + buf * KV_BM * D;
@@ -718,27 +727,33 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
   auto tile_of = [&](int j) { return j < ncand ? kt_begin + split + j * plan.q_split : kt_end; };
   const int rt_w = qw / kMaskTile;
 
-  // per-tile mask state of this wave, fetched one tile ahead: the block class and this
-  // lane's row visibility word
-  auto mask_state = [&](int k, ClassAhead& cls, uint64_t& w) {
-    cls = ClassAhead{0u, kSelBias};
+  // per-tile mask state of this wave, taken one tile ahead: the block class, from the
+  // wave's run of classes along its row (reloaded every 64 key blocks), and, for a 0 / -inf
+  // block only, this lane's row visibility word
+  ClassRun run{kTileDead, -64};
+  auto load_run = [&](int k) {
+    run.load(a, k & ~63, rt_w < nrt ? nkt : 0, [&](int pos) { return tile_index(a, b, rt_w, pos); });
+  };
+  auto mask_state = [&](int k, int& cls, uint64_t& w) {
+    cls = kTileBias;
     w = ~0ull;
     if (MASK && a.tiles) {
-      cls.sel = kSelDead;
-      if (rt_w < nrt) {
-        const int i = tile_index(a, b, rt_w, k);
-        cls = class_ahead(a, i);
-        w = a.rowbits[(int64_t)i * kMaskTile + (row - rt_w * kMaskTile)];
-      }
+      if (k >= run.base + 64) load_run(k);  // (a longer walk: the next 64 key blocks)
+      cls = run.at(k);
+      if (cls == kTileBits) w = a.rowbits[(int64_t)tile_index(a, b, rt_w, k) * kMaskTile + (row - rt_w * kMaskTile)];
     }
   };
 
   int kj = next_live(0);
   int kt = tile_of(kj);
-  ClassAhead cls_cur{0u, kSelBias};
+  int cls_cur = kTileBias;
   uint64_t wb_cur = ~0ull;
   if (kt < kt_end) {
     stage_tile(kt, 0);
+    if (MASK && a.tiles) {
+      load_run(kt);
+      wait_vm();  // the run's classes, with the first tile
+    }
     mask_state(kt, cls_cur, wb_cur);
   }
   wait_vm();
@@ -747,13 +762,13 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
     const int buf = it & 1;
     const int kjn = next_live(kj + 1);
     const int ktn = tile_of(kjn);
-    ClassAhead cls_next{0u, kSelBias};
+    int cls_next = kTileBias;
     uint64_t wb_next = ~0ull;
     if (ktn < kt_end) {
       mask_state(ktn, cls_next, wb_next);
       stage_tile(ktn, buf ^ 1);  // lands while this tile is being processed
     }
-    const int cls = class_of(cls_cur);
+    const int cls = cls_cur;
     const bool bias = MASK && (cls == kTileBias || a.alibi);  // add mask values and / or ALiBi
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
     const bf16* kb_lds = k_lds + buf * Q_BN * D;

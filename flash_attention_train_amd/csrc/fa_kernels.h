@@ -101,6 +101,27 @@ __device__ __forceinline__ ClassAhead class_ahead(const AttnShape& a, int i) {
   const auto* t = reinterpret_cast<const __attribute__((address_space(1))) uint8_t*>(reinterpret_cast<uintptr_t>(a.tiles));
   return ClassAhead{t[(i & ~63) + (int)(threadIdx.x & 63)], i & 63};
 }
+// The classes of 64 consecutive mask blocks along a walk (the row blocks of one key
+// column for a dK/dV wave, the key blocks of one row for a dQ wave), one per lane, fetched
+// by one vector load per 64 blocks. A step reads its block's class with one readlane and
+// loads its visibility word only when the block is 0 / -inf, instead of issuing both loads
+// (and their 64-bit address arithmetic) for every step.
+struct ClassRun {
+  int cls;   // class of block base + lane
+  int base;  // walk position of lane 0's block (a multiple of 64), or -64 before the first load
+  // lane l takes the class of block index(base + l), or dead when base + l >= n
+  template <class Index>
+  __device__ __forceinline__ void load(const AttnShape& a, int new_base, int n, Index&& index) {
+    const auto* t =
+        reinterpret_cast<const __attribute__((address_space(1))) uint8_t*>(reinterpret_cast<uintptr_t>(a.tiles));
+    const int pos = new_base + (int)(threadIdx.x & 63);
+    cls = pos < n ? (int)t[index(pos)] : kTileDead;
+    base = new_base;
+  }
+  // class of the block at walk position pos (base <= pos < base + 64), wave-uniform
+  __device__ __forceinline__ int at(int pos) const { return __builtin_amdgcn_readlane(cls, pos - base); }
+};
+
 __device__ __forceinline__ int class_of(const ClassAhead& c) {
   if (c.sel == kSelBias) return kTileBias;
   if (c.sel == kSelDead) return kTileDead;
