@@ -160,22 +160,33 @@ struct RowSink {
 struct LiveWords {
   uint64_t* words;  // [kBwdWaves] in LDS
   int base;
+  uint64_t w[kBwdWaves];  // the words of candidates base .. base + NT - 1, kept wave-uniform
   template <class F>
   __device__ __forceinline__ int next(int j, int n, int tid, F&& live) {
-    static_assert(NT == 64 * kBwdWaves && (NT & (NT - 1)) == 0, "one bit word per wave");
+    static_assert(NT == 64 * kBwdWaves && (NT & (NT - 1)) == 0 && kBwdWaves == 4, "one bit word per wave");
     while (j < n) {
       if (j >= base + NT) {
         const int c = (j & ~(NT - 1)) + tid;
-        const uint64_t w = __ballot(c < n && live(c));
+        const uint64_t bw = __ballot(c < n && live(c));
         __syncthreads();  // the previous words are no longer read
-        if ((tid & 63) == 0) words[tid >> 6] = w;
+        if ((tid & 63) == 0) words[tid >> 6] = bw;
         __syncthreads();
         base = j & ~(NT - 1);
+        // read once into scalar registers, so that a step of the walk finds its next
+        // candidate without an LDS read (whose wait would also wait for every LDS read
+        // issued before it)
+        #pragma unroll
+        for (int k = 0; k < kBwdWaves; ++k) {
+          const uint64_t x = words[k];
+          w[k] = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32) |
+                 __builtin_amdgcn_readfirstlane((uint32_t)x);
+        }
       }
-      const int off = j - base;
-      const uint64_t bits = words[off >> 6] >> (off & 63);
+      const int off = j - base, k = off >> 6;
+      const uint64_t wk = k == 0 ? w[0] : k == 1 ? w[1] : k == 2 ? w[2] : w[3];
+      const uint64_t bits = wk >> (off & 63);
       if (bits) return j + (int)__builtin_ctzll(bits);
-      j = base + 64 * ((off >> 6) + 1);
+      j = base + 64 * (k + 1);
     }
     return n;
   }
@@ -334,7 +345,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     return false;
   };
   __shared__ uint64_t live_lds[kBwdWaves];
-  LiveWords lw{live_lds, -NT};
+  LiveWords lw{live_lds, -NT, {0, 0, 0, 0}};
   const int ncand = npairs > split ? (npairs - split + plan.kv_split - 1) / plan.kv_split : 0;
   auto next_live = [&](Pos x) {
     if (!MASK || !a.tiles || x.p >= npairs) return x;
@@ -717,7 +728,7 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
     return false;
   };
   __shared__ uint64_t live_lds[kBwdWaves];
-  LiveWords lw{live_lds, -NT};
+  LiveWords lw{live_lds, -NT, {0, 0, 0, 0}};
   const int nwalk = kt_end - kt_begin;
   const int ncand = nwalk > split ? (nwalk - split + plan.q_split - 1) / plan.q_split : 0;
   auto next_live = [&](int j) {  // candidate j -> the first live one from j (ncand: none)
