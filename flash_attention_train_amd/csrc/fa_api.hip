@@ -449,7 +449,8 @@ int choose_fwd_split(const fa_attn_params* p) {
 size_t fwd_workspace_bytes(const fa_attn_params* p) {
   const int s = choose_fwd_split(p);
   if (s <= 1) return 0;
-  return round256((size_t)s * p->B * p->Hq * p->Sq * (p->D + 2) * sizeof(float));
+  // bf16 rows (2 D bytes) plus their fp32 base and row sum (8 bytes)
+  return round256((size_t)s * p->B * p->Hq * p->Sq * (2 * p->D + 8));
 }
 
 fa_status fwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,
@@ -507,8 +508,9 @@ fa_status fwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   a.part_ml = nullptr;
   if (p->dtype == FA_BF16) {
     if (splits > 1) {  // the split walk runs the default configuration
-      a.part_o = static_cast<float*>(workspace);
-      a.part_ml = a.part_o + (size_t)splits * p->B * p->Hq * p->Sq * p->D;
+      a.part_o = workspace;
+      a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           (size_t)splits * p->B * p->Hq * p->Sq * p->D * 2);
       return hip_status(fa::launch_fwd_bf16_split(a, stream), "split forward");
     }
     // variant 1 (32 query rows per wave, 64-key tiles, two waves per SIMD) measured

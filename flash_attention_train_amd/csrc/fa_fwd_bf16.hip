@@ -408,19 +408,23 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     base[0] = nb;
   }
 
-  if constexpr (SPLIT) {  // unnormalised rows, their base and row sum, for the merge
+  if constexpr (SPLIT) {  // this share's normalised rows (bf16), their base and row sum, for the merge
     static_assert(QB == 1 && KS == 1, "the split walk runs the one-block, one-half configuration");
     const int row = qw + r32;
     const float lt = lsum[0] + xor32(lsum[0]);
+    const float inv = base[0] == neg_inf() ? 0.f : 1.f / lt;  // (a share that saw no key: zeros)
     if (row < a.Sq) {
       const int64_t r = (((int64_t)blockIdx.z * a.B + b) * a.Hq + h) * a.Sq + row;
-      float* po = args.part_o + r * D;
+      bf16* po = static_cast<bf16*>(args.part_o) + r * D;
       #pragma unroll
       for (int db = 0; db < DB; ++db)
         #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          *reinterpret_cast<f32x4*>(po + 32 * db + 8 * rr + 4 * g) =
-              f32x4{oacc[0][db][4 * rr], oacc[0][db][4 * rr + 1], oacc[0][db][4 * rr + 2], oacc[0][db][4 * rr + 3]};
+        for (int rr = 0; rr < 4; ++rr) {
+          bf16x4 o4;
+          #pragma unroll
+          for (int e = 0; e < 4; ++e) o4[e] = (bf16)(oacc[0][db][4 * rr + e] * inv);
+          *reinterpret_cast<bf16x4*>(po + 32 * db + 8 * rr + 4 * g) = o4;
+        }
       if (g == 0) *reinterpret_cast<float2*>(args.part_ml + 2 * r) = float2{base[0], lt};
     }
     return;
@@ -462,8 +466,9 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
   }
 }
 
-// Merge of a split forward: per row, the partial rows are rescaled to the largest base
-// and summed, O = sum / (rescaled row sums), LSE = (base + log2 sum) ln 2; a row no split
+// Merge of a split forward: per row, each share's normalised row O_z (bf16) is weighted by
+// its row sum rescaled to the largest base, w_z = l_z 2^(b_z - b), and O = sum w_z O_z /
+// sum w_z, LSE = (b + log2 sum w_z) ln 2; a row no split
 // saw a key for (every base -inf) gets O = 0, LSE = 0 (or LSE = its head's sink, which
 // joins the row sum here). One pass over the splits with a
 // running base (the online softmax's own rescale), one thread per 8 columns of a row.
@@ -482,14 +487,16 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const FwdArgs args) {
   for (int z = 0; z < S; ++z) {
     const int64_t zr = (int64_t)z * rows + r;
     const float2 ml = *reinterpret_cast<const float2*>(args.part_ml + 2 * zr);
-    const f32x4 plo = *reinterpret_cast<const f32x4*>(args.part_o + zr * D + c);
-    const f32x4 phi = *reinterpret_cast<const f32x4*>(args.part_o + zr * D + c + 4);
+    const bf16x8 p8 = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(args.part_o) + zr * D + c);
     if (ml.x == neg_inf()) continue;  // this split saw no key of the row
     const float nm = fmaxf(mx, ml.x);
-    const float fo = mx == neg_inf() ? 0.f : fast_exp2(mx - nm), fn = fast_exp2(ml.x - nm);
+    // share z holds O_z = acc_z / l_z: its weight is l_z 2^(b_z - base)
+    const float fo = mx == neg_inf() ? 0.f : fast_exp2(mx - nm), fn = fast_exp2(ml.x - nm) * ml.y;
+    const f32x4 plo = {(float)p8[0], (float)p8[1], (float)p8[2], (float)p8[3]};
+    const f32x4 phi = {(float)p8[4], (float)p8[5], (float)p8[6], (float)p8[7]};
     lo = lo * fo + plo * fn;
     hi = hi * fo + phi * fn;
-    l = l * fo + ml.y * fn;
+    l = l * fo + fn;
     mx = nm;
   }
   const int i = (int)(r % a.Sq);

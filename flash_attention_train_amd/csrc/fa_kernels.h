@@ -147,9 +147,10 @@ struct FwdArgs {
   int mask_vec4;    // the mask can be read 4 floats at a time (16-byte aligned rows)
   const float* sinks;  // [Hq] sink logits (natural log) joining each row's denominator, or null
   // split key walks (splits > 1): workgroup z walks the z-th share of the key tiles and
-  // stores its unnormalised fp32 O rows and (base, row sum) per row, merged afterwards
+  // stores its O rows normalised by its own row sum (bf16) and (base, row sum) per row,
+  // merged afterwards
   int splits;
-  float* part_o;    // [splits][B][Hq][Sq][D]
+  void* part_o;     // bf16 [splits][B][Hq][Sq][D]: the share's rows normalised by its own row sum
   float* part_ml;   // [splits][B][Hq][Sq][2]: exponent base (log2 units, -inf: no key), row sum
 };
 

@@ -155,17 +155,19 @@ fa_status fa_train_fwd(const fa_attn_params* p, const fa_view* q, const fa_view*
                        const fa_view* o, const fa_view* lse, hipStream_t stream);
 
 /* Bytes of device workspace fa_train_fwd_ws needs for p: 0 when the forward is not
- * split, else splits * B * Hq * Sq * (D + 2) * 4 rounded up to 256 (the partial rows,
- * their exponent bases and row sums). The split is fwd_split when set, else chosen
+ * split, else splits * B * Hq * Sq * (2 D + 8) rounded up to 256 (each share's rows
+ * normalised by its own row sum, in bf16, then their fp32 exponent bases and row sums). The split is fwd_split when set, else chosen
  * from the shape: only grids with fewer than 256 query-tile workgroups and key walks of
  * at least 24 tiles of 64 keys are split. Returns (size_t)-1 if p is invalid. */
 size_t fa_train_fwd_workspace_bytes(const fa_attn_params* p);
 
-/* Forward with a caller-owned workspace: the same results as fa_train_fwd (O, LSE,
- * fully masked rows O = 0 and LSE = 0) for the same inputs, up to the order of fp32
- * summation, but a short grid may split each query tile's key walk over several
- * workgroups (the split-key reading of the pages' tiled forward; the partial rows are
- * merged exactly by rescaling to the largest exponent base). `workspace`: at least
+/* Forward with a caller-owned workspace: the results of fa_train_fwd (O, LSE, fully
+ * masked rows O = 0 and LSE = 0) for the same inputs, but a short grid may split each
+ * query tile's key walk over several workgroups (the split-key reading of the pages'
+ * tiled forward). Each share stores its rows normalised by its own row sum, rounded to
+ * bf16, and the merge weights them by their row sums rescaled to the largest exponent
+ * base: the LSE matches up to fp32 summation order, O up to one more bf16 rounding of
+ * each share's row. `workspace`: at least
  * fa_train_fwd_workspace_bytes(p) bytes of device memory, 256-byte aligned (NULL
  * allowed when 0 bytes are needed), overlapping no input or output; contents on entry
  * do not matter. Errors: those of fa_train_fwd, FA_ERR_WORKSPACE, FA_ERR_ALIGN and

@@ -109,17 +109,17 @@ def test_forward_rejects(name, p, over, code):
 
 def test_split_forward_workspace_and_rejects():
     L = B.lib()
-    # splits x B x Hq x Sq x (D + 2) fp32: the partial rows plus their base and row sum
+    # splits x B x Hq x Sq x (2 D + 8) bytes: the bf16 partial rows plus their fp32 base and row sum
     p2 = params(Sk=640, fwd_split=2)
-    assert L.fa_train_fwd_workspace_bytes(ctypes.byref(p2)) == 2 * 1 * 4 * 64 * 66 * 4
+    assert L.fa_train_fwd_workspace_bytes(ctypes.byref(p2)) == 2 * 1 * 4 * 64 * (2 * 64 + 8)
     # automatic: 4 query-tile workgroups, 64 key tiles -> 5 splits (each at least 12 tiles)
-    assert L.fa_train_fwd_workspace_bytes(ctypes.byref(params(Sk=4096))) == 5 * 1 * 4 * 64 * 66 * 4
+    assert L.fa_train_fwd_workspace_bytes(ctypes.byref(params(Sk=4096))) == 5 * 1 * 4 * 64 * (2 * 64 + 8)
     assert L.fa_train_fwd_workspace_bytes(ctypes.byref(params())) == 0  # one key tile: nothing to split
     assert L.fa_train_fwd_workspace_bytes(ctypes.byref(params(Sk=640, fwd_split=1))) == 0
     assert L.fa_train_fwd_workspace_bytes(None) == ctypes.c_size_t(-1).value
     assert L.fa_train_fwd_workspace_bytes(ctypes.byref(params(fwd_split=65))) == ctypes.c_size_t(-1).value
     kk, vv = view(1, H=2, S=640), view(2, H=2, S=640)
-    need = 2 * 1 * 4 * 64 * 66 * 4
+    need = 2 * 1 * 4 * 64 * (2 * 64 + 8)
     ws = BASE + 12 * (1 << 24)
 
     def fws(p, ws=ws, nbytes=need, **over):
