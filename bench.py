@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--splits", default="table",
                     help="backward split: 'table' (the workload's measured setting), 'tune' (time a few settings "
-                         "once at setup, untimed), 'model' (the library's cost model) or KVxQ (e.g. 2x1)")
+                         "once at setup, untimed), 'model' (the library's cost model), KVxQ (e.g. 2x1) or KVxQxTILES "
+                         "(q-way split of the first TILES 128-row query tiles only, e.g. 2x2x6)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference kernel that "
                          "scales the HBM byte counters) and exit")
@@ -100,13 +101,15 @@ class Workload:
         self.fwd_split = self.fws_bytes // (4 * c.B * c.Hq * c.Sq * (c.D + 2)) if self.fws_bytes else 1
         # backward split: the library's cost model, or (tune) the fastest of a few
         # settings timed once here on this workload, outside every timed region
-        self.kv_split = self.q_split = 0
+        self.kv_split = self.q_split = self.q_split_tiles = 0
         self.splits_from = "library cost model"
         if splits == "table" and configs.WORKLOADS[key].bwd_splits:
-            self.kv_split, self.q_split = configs.WORKLOADS[key].bwd_splits
+            self.kv_split, self.q_split, self.q_split_tiles = configs.WORKLOADS[key].bwd_splits
             self.splits_from = "workload table"
-        elif "x" in splits:
-            self.kv_split, self.q_split = (int(x) for x in splits.split("x"))
+        elif "x" in splits:  # KVxQ or KVxQxTILES
+            v = [int(x) for x in splits.split("x")]
+            self.kv_split, self.q_split = v[0], v[1]
+            self.q_split_tiles = v[2] if len(v) > 2 else 0
             self.splits_from = "given"
         elif splits == "tune":
             self.splits_from = "tuned once at setup"
@@ -116,7 +119,8 @@ class Workload:
                 self.q, self.k, self.v, self.do, self.lse, self.delta, mask=self.mask, scale=c.scale,
                 causal=c.causal, q_offset=c.q_offset, mask_tiles=self.tiles, **self.sk)
         nws = binding.bwd_workspace_bytes(self.q, self.k, scale=c.scale, causal=c.causal, q_offset=c.q_offset,
-                                          mask=self.mask, kv_split=self.kv_split, q_split=self.q_split, **self.sk)
+                                          mask=self.mask, kv_split=self.kv_split, q_split=self.q_split,
+                                          q_split_tiles=self.q_split_tiles, **self.sk)
         self.ws_bytes = nws
         self.ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
 
@@ -139,7 +143,8 @@ class Workload:
         c = self.case
         self.B.bwd(self.q, self.k, self.v, self.do, self.lse, self.delta, mask=self.mask, scale=c.scale,
                    causal=c.causal, q_offset=c.q_offset, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws,
-                   kv_split=self.kv_split, q_split=self.q_split, mask_tiles=self.tiles, alibi=self.alibi, **self.sk)
+                   kv_split=self.kv_split, q_split=self.q_split, q_split_tiles=self.q_split_tiles,
+                   mask_tiles=self.tiles, alibi=self.alibi, **self.sk)
         if self.sinks is not None:  # the sinks' gradient, added into their accumulator
             self.B.bwd_sinks(self.lse, self.delta, self.sinks, dsink=self.dsink)
 
@@ -219,7 +224,7 @@ def time_workload(w: Workload, steps: int, warmup: int, graph: bool = True) -> d
         "pre_gbs": w.pre_bytes / (pre_ms.mean() * 1e-3) / 1e9,
         "pairs": w.pairs,
         "fwd_split": w.fwd_split,
-        "bwd_splits": [w.kv_split, w.q_split],
+        "bwd_splits": [w.kv_split, w.q_split, w.q_split_tiles],
         "bwd_splits_from": w.splits_from,
         "gflop_per_step": total_flops / 1e9,
     }
@@ -435,7 +440,7 @@ def main():
                      "fa_train_bwd (bwd_bf16_kernel + reduce_parts_kernel)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(args.workload, [w.kv_split, w.q_split]),
+                     "traffic": measured_traffic(args.workload, [w.kv_split, w.q_split, w.q_split_tiles]),
                      "flop_per_launch": w.bwd_flops, "launch_ms": round(r["bwd_ms_mean"], 5)},
         "breakdown": {k: round(v, 4) if isinstance(v, float) else v for k, v in r.items()},
         "extra": extra,

@@ -35,7 +35,8 @@ class FaAttnParams(ctypes.Structure):
                 ("fwd_variant", ctypes.c_int32), ("kv_split", ctypes.c_int32), ("q_split", ctypes.c_int32),
                 ("fwd_split", ctypes.c_int32), ("key_len", ctypes.c_void_p), ("q_len", ctypes.c_void_p),
                 ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
-                ("bwd_dq_launch", ctypes.c_int32), ("sinks", ctypes.c_void_p), ("alibi", ctypes.c_void_p)]
+                ("bwd_dq_launch", ctypes.c_int32), ("sinks", ctypes.c_void_p), ("alibi", ctypes.c_void_p),
+                ("q_split_tiles", ctypes.c_int32)]
 
 
 class FaError(RuntimeError):
@@ -126,7 +127,8 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
                 q_split: int = 0, mask_tiles: Optional[torch.Tensor] = None, fwd_split: int = 0,
                 key_len: Optional[torch.Tensor] = None, q_len: Optional[torch.Tensor] = None,
                 window: tuple = (-1, -1), dq_launch: int = 0,
-                sinks: Optional[torch.Tensor] = None, alibi: Optional[torch.Tensor] = None) -> FaAttnParams:
+                sinks: Optional[torch.Tensor] = None, alibi: Optional[torch.Tensor] = None,
+                q_split_tiles: int = 0) -> FaAttnParams:
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Sk, Dk = k.shape
     if Bk != B or Dk != D:
@@ -143,6 +145,7 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
             if t.dtype != torch.int32 or t.dim() != 1 or t.shape[0] != n or not t.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous int32 [B] tensor on the device")
             setattr(p, name, t.data_ptr())
+    p.q_split_tiles = int(q_split_tiles)
     for name, t in (("sinks", sinks), ("alibi", alibi)):
         if t is not None:
             if t.dtype != torch.float32 or t.shape != (Hq,) or not t.is_contiguous():
@@ -265,9 +268,9 @@ def dequant_q8_0(qs, d, *, out=None, stream=None):
 
 
 def bwd_workspace_bytes(q, k, *, scale=None, causal=False, q_offset=None, mask=None, kv_split=0, q_split=0,
-                        key_len=None, q_len=None, window=(-1, -1)) -> int:
+                        key_len=None, q_len=None, window=(-1, -1), q_split_tiles=0) -> int:
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
-                    q_split=q_split, key_len=key_len, q_len=q_len, window=window)
+                    q_split=q_split, key_len=key_len, q_len=q_len, window=window, q_split_tiles=q_split_tiles)
     return int(lib().fa_train_bwd_workspace_bytes(ctypes.byref(p)))
 
 
@@ -282,11 +285,11 @@ def _workspace(p: FaAttnParams, device, workspace):
 
 def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_offset=None, dq=None, dk=None,
         dv=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None, q_len=None,
-        window=(-1, -1), dq_launch=0, alibi=None):
+        window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0):
     """Backward: returns (dQ, dK, dV), each in q's dtype, overwritten."""
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, window=window,
-                    dq_launch=dq_launch, alibi=alibi)
+                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
@@ -337,12 +340,12 @@ def tune_bwd_splits(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=
 
 def bwd_chunked(q, k, v, dout, lse, delta, dk_acc, dv_acc, *, mask=None, scale=None, causal=True, q_offset=None,
                 dq=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None,
-                q_len=None, window=(-1, -1), dq_launch=0, alibi=None):
+                q_len=None, window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0):
     """Chunked backward: returns dQ for the chunk; ADDS dK/dV into the fp32 window
     accumulators ``dk_acc`` / ``dv_acc`` ([B, Hkv, >= Sk, D])."""
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len,
-                    q_len=q_len, window=window, dq_launch=dq_launch, alibi=alibi)
+                    q_len=q_len, window=window, dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles)
     if dk_acc.dtype != torch.float32 or dv_acc.dtype != torch.float32:
         raise TypeError("the window accumulators must be float32")
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq

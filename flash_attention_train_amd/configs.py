@@ -20,34 +20,35 @@ class Workload:
     key: str
     title: str
     index: int
-    # the bf16 backward's (kv_split, q_split) for this workload: the fastest or within
-    # noise of the fastest on MI355X over kv in {1, 2, 4} x q in {1, 2, 4}; None: the
+    # the bf16 backward's (kv_split, q_split, q_split_tiles) for this workload: the fastest
+    # or within noise of the fastest on MI355X over kv in {1, 2, 4}, q in {1, 2, 3, 4} and
+    # the number of split query tiles (timed interleaved, best of three rounds); None: the
     # library's cost model
     bwd_splits: tuple | None = None
 
 
 WORKLOADS = {
     "tiny": Workload("tiny", "tiny parity case, fp32, B=1 H=2 S=64 D=64", 1),
-    "dit_sa": Workload("dit_sa", "DiT self-attention, B=1 Hq=16 Hkv=8 S=1542 D=128 bf16, pad mask", 2, (2, 1)),
+    "dit_sa": Workload("dit_sa", "DiT self-attention, B=1 Hq=16 Hkv=8 S=1542 D=128 bf16, pad mask", 2, (2, 2, 6)),
     "dit_ca": Workload("dit_ca", "DiT cross-attention, B=2 H=16 Sq=1542 Sk=512 D=128 bf16, key-pad mask", 3,
-                       (2, 1)),
-    "lm_causal": Workload("lm_causal", "LM causal GQA, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 4, (2, 1)),
+                       (2, 1, 0)),
+    "lm_causal": Workload("lm_causal", "LM causal GQA, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 4, (2, 1, 0)),
     "long_window": Workload("long_window",
                             "long-window chunked walk, W=32768, 64 chunks of 512, Hq=16 Hkv=4 D=128 bf16", 5),
     # the DiT self-attention masks given by their structure instead of a dense mask:
     # the pad as a key length, and a mixed-length batch under a sliding window
     "dit_sa_len": Workload("dit_sa_len", "DiT self-attention, B=1 Hq=16 Hkv=8 S=1542 D=128 bf16, "
-                           "key length 1388 (the pad as a length)", 6, (1, 1)),
+                           "key length 1388 (the pad as a length)", 6, (1, 1, 0)),
     "dit_sa_band": Workload("dit_sa_band", "DiT self-attention, mixed-length batch B=2 Hq=16 Hkv=8 S=1542 D=128 "
                             "bf16, key lengths 1542 / 1101, window 256 keys each side", 7),
     # the LM layer with one attention-sink logit per query head (N(0, 1)); its step adds the
     # sinks' gradient pass
     "lm_sinks": Workload("lm_sinks", "LM causal GQA with attention sinks, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 8,
-                         (2, 1)),
+                         (2, 1, 0)),
     # the long-window walk over a q8_0-stored K/V window (the pages train such a cache in
     # place): the same queries and K/V values, quantised to q8_0 blocks
     # the LM layer with ALiBi (slopes 2^(-8 (h + 1) / Hq)) in place of positional rotations
-    "lm_alibi": Workload("lm_alibi", "LM causal GQA with ALiBi, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 10, (2, 1)),
+    "lm_alibi": Workload("lm_alibi", "LM causal GQA with ALiBi, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 10, (2, 1, 0)),
     "long_window_q8": Workload("long_window_q8", "long-window chunked walk over a q8_0 K/V window, W=32768, "
                                "64 chunks of 512, Hq=16 Hkv=4 D=128", 9),
 }

@@ -85,6 +85,7 @@ fa_status check_params(const fa_attn_params* p) {
     return fail(FA_ERR_SHAPE, "q_offset out of range");
   if (!(p->scale > 0.f) || !isfinite(p->scale)) return fail(FA_ERR_SHAPE, "scale must be positive and finite");
   if (p->fwd_variant < 0 || p->fwd_variant > 3) return fail(FA_ERR_SHAPE, "unknown forward variant %d", p->fwd_variant);
+  if (p->q_split_tiles < 0) return fail(FA_ERR_SHAPE, "q_split_tiles must be >= 0");
   if (p->kv_split < 0 || p->kv_split > 64 || p->q_split < 0 || p->q_split > 64 || p->fwd_split < 0 ||
       p->fwd_split > 64)
     return fail(FA_ERR_SHAPE, "split hints must be in 0 .. 64");
@@ -180,7 +181,7 @@ size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 // dQ units, longest first), each costed by its walk length, and placed greedily on
 // the compute units the way the dispatcher fills whichever frees first; split
 // choices add the reduce pass over their fp32 slices.
-double predict_bwd_us(const fa_attn_params* p, int kv, int q) {
+double predict_bwd_us(const fa_attn_params* p, int kv, int q, int64_t q_tiles) {
   // fitted to MI355X timings of the three bf16 workloads over the split grid
   constexpr double kPairUs = 2.7;         // one 64-row x 128-key dK/dV step
   constexpr double kTileUs = 1.8;         // one 128-row x 64-key dQ step
@@ -210,18 +211,27 @@ double predict_bwd_us(const fa_attn_params* p, int kv, int q) {
     const double cost = kKvUnitUs + kPairUs * (double)((pairs + kv - 1) / kv);
     for (int64_t u = 0; u < (int64_t)p->B * p->Hkv * kv; ++u) place(cost);
   }
-  for (int64_t qt = nqt - 1; qt >= 0; --qt) {
-    int64_t tiles = nk64;
-    if (p->causal) {
-      const int64_t last_key = p->q_offset + (qt + 1) * U - 1;
-      tiles = last_key < 0 ? 0 : std::min<int64_t>(last_key / 64 + 1, nk64);
+  // whole query tiles first, then the q_tiles first tiles split q ways
+  if (q <= 1) q_tiles = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int64_t lo = pass == 0 ? q_tiles : 0, hi = pass == 0 ? nqt : q_tiles;
+    const int ways = pass == 0 ? 1 : q;
+    for (int64_t qt = hi - 1; qt >= lo; --qt) {
+      int64_t tiles = nk64;
+      if (p->causal) {
+        const int64_t last_key = p->q_offset + (qt + 1) * U - 1;
+        tiles = last_key < 0 ? 0 : std::min<int64_t>(last_key / 64 + 1, nk64);
+      }
+      const double cost = kTileUs * (double)((tiles + ways - 1) / ways);
+      for (int64_t u = 0; u < (int64_t)p->B * p->Hq * ways; ++u) place(cost);
     }
-    const double cost = kTileUs * (double)((tiles + q - 1) / q);
-    for (int64_t u = 0; u < (int64_t)p->B * p->Hq * q; ++u) place(cost);
   }
   const double nk = (double)p->B * p->Hkv * p->Sk * p->D, nq = (double)p->B * p->Hq * p->Sq * p->D;
   if (kv > 1) end += kPassUs + (2.0 * kv * nk * 4.0 + 2.0 * nk * 2.0) / kBytesPerUs;
-  if (q > 1) end += kPassUs + (q * nq * 4.0 + nq * 2.0) / kBytesPerUs;
+  if (q > 1 && q_tiles > 0) {
+    const double rows = std::min<double>(1.0, (double)(q_tiles * U) / p->Sq);  // share of rows reduced
+    end += kPassUs + rows * (q * nq * 4.0 + nq * 2.0) / kBytesPerUs;
+  }
   return end;
 }
 
@@ -229,15 +239,15 @@ double predict_bwd_us(const fa_attn_params* p, int kv, int q) {
 // per shape in a small per-thread cache (the prediction walks every workgroup). Calls
 // with the same shape always get the same choice, so the workspace size the caller
 // was given matches the launch.
-void choose_splits(const fa_attn_params* p, bool accumulate, int* kv_split, int* q_split) {
+void choose_splits(const fa_attn_params* p, bool accumulate, int* kv_split, int* q_split, int* q_tiles_split) {
   (void)accumulate;
-  int kv = 1, q = 1;
-  const int64_t units = (int64_t)((p->Sk + fa::kBwdUnit - 1) / fa::kBwdUnit) * p->B * p->Hkv +
-                        (int64_t)((p->Sq + fa::kBwdUnit - 1) / fa::kBwdUnit) * p->B * p->Hq;
+  const int64_t nqt = (p->Sq + fa::kBwdUnit - 1) / fa::kBwdUnit;
+  int kv = 1, q = 1, qt = 0;
+  const int64_t units = (int64_t)((p->Sk + fa::kBwdUnit - 1) / fa::kBwdUnit) * p->B * p->Hkv + nqt * p->B * p->Hq;
   if (units < 8 * 1024) {
     struct Entry {
       int64_t key[8];
-      int kv, q;
+      int kv, q, qt;
     };
     thread_local Entry cache[16];
     thread_local int next = 0;
@@ -247,22 +257,33 @@ void choose_splits(const fa_attn_params* p, bool accumulate, int* kv_split, int*
       if (e.kv > 0 && std::equal(key, key + 8, e.key)) {
         kv = e.kv;
         q = e.q;
+        qt = e.qt;
         hit = true;
         break;
       }
     if (!hit) {
       const int64_t kv_pairs = (int64_t)((p->Sq + 63) / 64) * (p->Hq / p->Hkv);  // walk length, one key tile
-      const int64_t q_tiles = (p->Sk + 63) / 64;                                  // walk length, one query tile
-      double best = predict_bwd_us(p, 1, 1);
+      const int64_t q_walk = (p->Sk + 63) / 64;                                   // walk length, one query tile
+      // split query tiles: all of them. (Splitting only the first ones, dispatched last, is
+      // left to the q_split_tiles hint: it shortened the DiT self-attention backward by
+      // 10% on MI355X, but this dispatch-order model does not rank those choices reliably:
+      // it preferred four-way tails that measured 17% slower.)
+      const int64_t step = nqt;
+      double best = predict_bwd_us(p, 1, 1, 0);
       for (int ckv : {1, 2, 4, 8})
         for (int cq : {1, 2, 4, 8, 16}) {
-          if ((ckv == 1 && cq == 1) || ckv > std::max<int64_t>(kv_pairs, 1) || cq > std::max<int64_t>(q_tiles, 1))
-            continue;
-          const double t = predict_bwd_us(p, ckv, cq);
-          if (t < 0.98 * best) {  // a split must pay for itself clearly
-            best = t;
-            kv = ckv;
-            q = cq;
+          if (ckv > std::max<int64_t>(kv_pairs, 1) || cq > std::max<int64_t>(q_walk, 1)) continue;
+          for (int64_t ct = cq > 1 ? step : 0; ct <= (cq > 1 ? nqt : 0); ct += (cq > 1 ? step : 1)) {
+            const int64_t tiles = cq > 1 && ct + step > nqt ? nqt : ct;  // (the last step takes them all)
+            if (ckv == 1 && cq == 1) continue;
+            const double t = predict_bwd_us(p, ckv, cq, tiles);
+            if (t < 0.98 * best) {  // a split must pay for itself clearly
+              best = t;
+              kv = ckv;
+              q = cq;
+              qt = (int)tiles;
+            }
+            if (cq == 1) break;
           }
         }
       Entry& e = cache[next];
@@ -270,10 +291,18 @@ void choose_splits(const fa_attn_params* p, bool accumulate, int* kv_split, int*
       std::copy(key, key + 8, e.key);
       e.kv = kv;
       e.q = q;
+      e.qt = qt;
     }
   }
   *kv_split = p->kv_split ? p->kv_split : kv;
-  *q_split = p->q_split ? p->q_split : q;
+  if (p->q_split) {  // given: all query tiles, or the q_split_tiles first ones
+    *q_split = p->q_split;
+    *q_tiles_split = (int)(p->q_split_tiles ? std::min<int64_t>(p->q_split_tiles, nqt) : nqt);
+  } else {
+    *q_split = q;
+    *q_tiles_split = p->q_split_tiles && q > 1 ? (int)std::min<int64_t>(p->q_split_tiles, nqt) : qt;
+  }
+  if (*q_split <= 1) *q_tiles_split = 0;
 }
 
 struct WsLayout {
@@ -289,9 +318,9 @@ WsLayout workspace_layout(const fa_attn_params* p, bool accumulate) {
   const size_t nk = (size_t)p->B * p->Hkv * p->Sk * p->D * sizeof(float);
   size_t dq_bytes = nq, dk_bytes = 0;
   if (p->dtype == FA_BF16) {
-    int kv, q;
-    choose_splits(p, accumulate, &kv, &q);
-    w.need_dq = q > 1;
+    int kv, q, qt;
+    choose_splits(p, accumulate, &kv, &q, &qt);
+    w.need_dq = q > 1 && qt > 0;
     w.need_dkdv = kv > 1;
     dq_bytes = w.need_dq ? q * nq : 0;
     dk_bytes = w.need_dkdv ? kv * nk : 0;
@@ -376,9 +405,9 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   if (is_bf16) {
     char* ws = static_cast<char*>(workspace);
     fa::BwdPlan plan;
-    int kv, q;
-    choose_splits(p, accumulate, &kv, &q);
-    fa::plan_bwd_bf16(a.a, kv, q, 0, &plan);
+    int kv, q, qt;
+    choose_splits(p, accumulate, &kv, &q, &qt);
+    fa::plan_bwd_bf16(a.a, kv, q, qt, 0, &plan);
     // a large dQ grid runs as its own kernel, two workgroups per compute unit (measured on
     // the causal LM backward: 659 -> 631 us); small grids keep one launch, whose dQ
     // workgroups fill the compute units the dK/dV walks leave idle
@@ -394,14 +423,18 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
     const int64_t nq = (int64_t)p->B * p->Hq * p->Sq * p->D, nk = (int64_t)p->B * p->Hkv * p->Sk * p->D;
     if ((st = hip_status(fa::launch_bwd_bf16(a, plan, stream), "backward"))) return st;
     if (wl.need_dq) {
-      fa::ReduceArgs r = {p->B, p->Hq, p->Sq, p->D, plan.dq_part, q, nq, dq->data, strides_of(dq), p->scale, 0};
+      // only the rows of the split query tiles (the first ones) have slices to sum
+      const int rows = std::min(p->Sq, plan.q_tiles_split * fa::kBwdUnit);
+      fa::ReduceArgs r = {p->B, p->Hq, rows, p->D, p->Sq, plan.dq_part, q, nq, dq->data, strides_of(dq), p->scale, 0};
       if ((st = hip_status(fa::launch_reduce_parts(r, nullptr, 1, stream), "dq reduce"))) return st;
     }
     if (wl.need_dkdv) {
       // the chunked walk adds into its fp32 window accumulators; otherwise bf16 outputs
       const int out_bf16 = accumulate ? 0 : 1, acc = accumulate ? 1 : 0;
-      fa::ReduceArgs rk = {p->B, p->Hkv, p->Sk, p->D, plan.dk_part, kv, nk, dk->data, strides_of(dk), p->scale, acc};
-      fa::ReduceArgs rv = {p->B, p->Hkv, p->Sk, p->D, plan.dv_part, kv, nk, dv->data, strides_of(dv), 1.f, acc};
+      fa::ReduceArgs rk = {p->B,      p->Hkv, p->Sk,   p->D, p->Sk, plan.dk_part, kv, nk,
+                           dk->data, strides_of(dk), p->scale, acc};
+      fa::ReduceArgs rv = {p->B,      p->Hkv, p->Sk,   p->D, p->Sk, plan.dv_part, kv, nk,
+                           dv->data, strides_of(dv), 1.f,      acc};
       if ((st = hip_status(fa::launch_reduce_parts(rk, &rv, out_bf16, stream), "dk / dv reduce"))) return st;
     }
     return FA_OK;

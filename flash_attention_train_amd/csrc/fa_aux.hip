@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void reduce_parts_kernel(const ReduceArgs p0, 
   const int i = (int)(row % p.S);
   const int h = (int)((row / p.S) % p.H);
   const int b = (int)(row / ((int64_t)p.S * p.H));
-  const float* src = p.parts + row * D + d0;
+  const float* src = p.parts + (((int64_t)b * p.H + h) * p.S_parts + i) * D + d0;
   f32x16 acc;
   #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;

@@ -67,16 +67,25 @@ __device__ __forceinline__ KvUnit kv_unit_of(const AttnShape& a, const BwdPlan& 
 
 // unit -> (query tile, batch, head, split); the last query tiles (longest under a
 // causal mask) are dispatched first
+// The whole tiles go first; the q_tiles_split first query tiles, dispatched last, are each
+// walked by q_split workgroups, so that the launch ends with short units.
 struct QUnit {
-  int qt, b, h, split;
+  int qt, b, h, split, nsplit;
 };
 __device__ __forceinline__ QUnit q_unit_of(const AttnShape& a, const BwdPlan& plan, int unit) {
   const int nqt = (a.Sq + Q_BM - 1) / Q_BM;
-  const int per_tile = a.B * a.Hq * plan.q_split;
+  const int bh = a.B * a.Hq;
+  const int n_whole = (nqt - plan.q_tiles_split) * bh;
+  if (unit < n_whole) {
+    const int rem = unit % bh;
+    return {nqt - 1 - unit / bh, rem / a.Hq, rem % a.Hq, 0, 1};
+  }
+  unit -= n_whole;
+  const int per_tile = bh * plan.q_split;
   int rem = unit % per_tile;
   const int split = rem % plan.q_split;
   rem /= plan.q_split;
-  return {nqt - 1 - unit / per_tile, rem / a.Hq, rem % a.Hq, split};
+  return {plan.q_tiles_split - 1 - unit / per_tile, rem / a.Hq, rem % a.Hq, split, plan.q_split};
 }
 
 // Does any mask block of rows [r0, r0 + nr) x keys [c0, c0 + nc) (in 64-blocks) carry
@@ -647,7 +656,7 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) from here on
   const int g = lane >> 5, r32 = lane & 31;
   const QUnit u = q_unit_of(a, plan, unit);
-  const int qt = u.qt, b = u.b, h = u.h, split = u.split;
+  const int qt = u.qt, b = u.b, h = u.h, split = u.split, nsplit = u.nsplit;
   const int hk = h / a.G;
   const int q0 = qt * Q_BM;
   const int qw = q0 + 32 * wave;
@@ -720,9 +729,9 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
 
   // mask tile map: skip key tiles dead for both 64-row blocks of this workgroup
   const int nrt = (a.Sq + kMaskTile - 1) / kMaskTile;
-  // candidate j: key tile kt_begin + split + j q_split
+  // candidate j: key tile kt_begin + split + j nsplit
   auto live = [&](int j) -> bool {
-    const int k = kt_begin + split + j * plan.q_split;
+    const int k = kt_begin + split + j * nsplit;
     for (int rt = q0 / kMaskTile; rt <= (q0 + Q_BM - 1) / kMaskTile && rt < nrt; ++rt)
       if (tile_class(a, b, rt, k) != kTileDead) return true;  // Q_BN = kMaskTile: key tile = block
     return false;
@@ -730,12 +739,12 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
   __shared__ uint64_t live_lds[kBwdWaves];
   LiveWords lw{live_lds, -NT, {0, 0, 0, 0}};
   const int nwalk = kt_end - kt_begin;
-  const int ncand = nwalk > split ? (nwalk - split + plan.q_split - 1) / plan.q_split : 0;
+  const int ncand = nwalk > split ? (nwalk - split + nsplit - 1) / nsplit : 0;
   auto next_live = [&](int j) {  // candidate j -> the first live one from j (ncand: none)
     if (j >= ncand) return ncand;
     return MASK && a.tiles ? lw.next(j, ncand, tid, live) : j;
   };
-  auto tile_of = [&](int j) { return j < ncand ? kt_begin + split + j * plan.q_split : kt_end; };
+  auto tile_of = [&](int j) { return j < ncand ? kt_begin + split + j * nsplit : kt_end; };
   const int rt_w = qw / kMaskTile;
 
   // per-tile mask state of this wave, taken one tile ahead: the block class, from the
@@ -897,7 +906,7 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
   // tile buffers stage the results once every wave has left the walk
   const int rows = max(0, min(32, a.Sq - qw));
   const RowSink sq =
-      plan.q_split > 1
+      nsplit > 1
           ? RowSink{reinterpret_cast<char*>(plan.dq_part + (int64_t)split * a.B * a.Hq * a.Sq * D +
                                             (((int64_t)b * a.Hq + h) * a.Sq + qw) * D),
                     (int64_t)D * 4, rows, 1}
@@ -906,7 +915,7 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
                     plan.sdq.s * 2, rows, 0};
   float* stage = reinterpret_cast<float*>(smem) + wave * 32 * D;
   __syncthreads();
-  store_block<D>(dq, plan.q_split > 1 ? 1.f : a.scale, stage, lane, sq);
+  store_block<D>(dq, nsplit > 1 ? 1.f : a.scale, stage, lane, sq);
 }
 
 // Units whose mask blocks carry additive values run a body compiled with the
@@ -980,14 +989,16 @@ hipError_t launch_t(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream
 
 }  // namespace
 
-void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, int dq_separate, BwdPlan* plan) {
+void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, int q_tiles_split, int dq_separate,
+                   BwdPlan* plan) {
   plan->dq_separate = dq_separate;
   const int nkt = (a.Sk + KV_BN - 1) / KV_BN;
   const int nqt = (a.Sq + Q_BM - 1) / Q_BM;
   plan->kv_split = kv_split;
   plan->q_split = q_split;
   plan->n_kv_units = nkt * a.B * a.Hkv * kv_split;
-  plan->n_q_units = nqt * a.B * a.Hq * q_split;
+  plan->q_tiles_split = q_split > 1 ? q_tiles_split : 0;
+  plan->n_q_units = (nqt - plan->q_tiles_split + plan->q_tiles_split * q_split) * a.B * a.Hq;
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream) {

@@ -194,7 +194,9 @@ struct BwdArgs {
 // Work decomposition of the bf16 backward (one launch, two kinds of workgroups).
 struct BwdPlan {
   int kv_split;    // workgroups sharing one key tile's dK/dV walk (> 1: fp32 partial slices)
-  int q_split;     // workgroups sharing one query tile's dQ walk (> 1: fp32 partial slices)
+  int q_split;     // workgroups sharing one split query tile's dQ walk (> 1: fp32 partial slices)
+  int q_tiles_split;  // how many 128-row query tiles (the first ones, dispatched last) are split
+                      // q_split ways; the others walk whole and store dQ directly
   int n_kv_units;  // dK/dV workgroups (launched first)
   int n_q_units;   // dQ workgroups
   int dq_separate; // 1: the dQ workgroups run as a second kernel (two per compute unit)
@@ -205,10 +207,12 @@ struct BwdPlan {
   Strides sdq;
 };
 
-// out = scale * sum of nparts fp32 slices [B, H, S, D] (slice s at parts + s * part_stride),
-// stored in the output dtype, or added to an fp32 output when accumulate is set
+// out = scale * sum of nparts fp32 slices [B, H, S_parts, D] (slice s at parts + s * part_stride),
+// over rows 0 .. S - 1 of every (b, h), stored in the output dtype, or added to an fp32 output
+// when accumulate is set
 struct ReduceArgs {
   int B, H, S, D;
+  int S_parts;
   const float* parts;
   int nparts;
   int64_t part_stride;
@@ -249,7 +253,8 @@ struct DequantArgs {
   Strides sq, sd, so;  // element strides of qs, d and out
 };
 hipError_t launch_dequant_q8_0(const DequantArgs& args, hipStream_t stream);
-void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, int dq_separate, BwdPlan* plan);
+void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, int q_tiles_split, int dq_separate,
+                   BwdPlan* plan);
 hipError_t launch_bwd_bf16(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream);
 
 }  // namespace fa

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FA_TRAIN_ABI_VERSION 7
+#define FA_TRAIN_ABI_VERSION 8
 
 typedef enum fa_status {
     FA_OK = 0,
@@ -110,8 +110,9 @@ typedef struct fa_attn_params {
     int32_t kv_split;     /* bf16 backward: workgroups sharing one 128-key tile's dK/dV
                              walk, 1 .. 64 (> 1: each writes an fp32 partial slice in the
                              workspace, summed by a reduce pass) */
-    int32_t q_split;      /* bf16 backward: workgroups sharing one 128-row query tile's dQ
-                             walk, 1 .. 64 (> 1: fp32 partial slices, as for kv_split) */
+    int32_t q_split;      /* bf16 backward: workgroups sharing one split 128-row query tile's
+                             dQ walk, 1 .. 64 (> 1: fp32 partial slices, as for kv_split);
+                             which tiles are split: q_split_tiles below */
     int32_t fwd_split;    /* bf16 forward through fa_train_fwd_ws: workgroups sharing one
                              128-row query tile's key walk, 1 .. 64 (> 1: each stores its
                              unnormalised fp32 rows in the workspace and a merge pass
@@ -147,6 +148,12 @@ typedef struct fa_attn_params {
      * alibi[h] * (j - q_offset - i). Positions are exact while |j - q_offset - i| < 2^24. It
      * is a constant of the scores, so the backward's gradients need nothing more. */
     const float* alibi;      /* device [Hq] fp32 slopes, 4-byte aligned; NULL = none */
+    /* Work decomposition hint of the bf16 backward (same results up to fp32 summation
+     * order): how many 128-row query tiles, counted from the first (their dQ workgroups
+     * are dispatched last), have their dQ walk split q_split ways; the other tiles walk
+     * whole. 0 = all tiles when q_split is given, else automatic. Splitting only the last
+     * units to run shortens the end of the launch, when few compute units are busy. */
+    int32_t q_split_tiles;
 } fa_attn_params;
 
 /* Forward: writes O (dtype) and LSE (fp32, natural log). Fully masked rows get

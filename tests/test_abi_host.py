@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(L, n), n
         assert n in B.SIGNATURES, f"{n} has no ctypes signature in the binding"
-    assert L.fa_train_version() == 7
+    assert L.fa_train_version() == 8
 
 
 BASE = 0x7F0000000000  # fake, 256-byte aligned device addresses
@@ -43,7 +43,8 @@ BASE = 0x7F0000000000  # fake, 256-byte aligned device addresses
 def params(**kw):
     a = dict(B=1, Hq=4, Hkv=2, Sq=64, Sk=64, D=64, dtype=B.FA_BF16, causal=0, q_offset=0, scale=0.125, mask=None,
              mask_stride_b=0, mask_stride_q=0, mask_tiles=None, fwd_variant=0, kv_split=0, q_split=0, fwd_split=0, key_len=None, q_len=None,
-             window_left=-1, window_right=-1, bwd_dq_launch=0, sinks=None, alibi=None)
+             window_left=-1, window_right=-1, bwd_dq_launch=0, sinks=None, alibi=None,
+             q_split_tiles=0)
     a.update(kw)
     return B.FaAttnParams(*(a[f] for f, _ in B.FaAttnParams._fields_))
 
@@ -86,6 +87,7 @@ FWD_ERRORS = [
     ("split out of range", params(kv_split=65), {}, 2),
     ("window bound -2", params(window_left=-2), {}, 2),
     ("unknown dQ launch hint", params(bwd_dq_launch=3), {}, 2),
+    ("negative q_split_tiles", params(q_split_tiles=-1), {}, 2),
     ("sinks on fp32", params(dtype=B.FA_F32, sinks=BASE), {}, 7),
     ("misaligned sinks", params(sinks=BASE + 2), {}, 5),
     ("ALiBi on fp32", params(dtype=B.FA_F32, alibi=BASE), {}, 7),

@@ -25,13 +25,19 @@ def _mask64(c):
     return None if c.mask is None else c.mask.astype(np.float64)
 
 
+def _splits(key):
+    """The backward decomposition the bench uses for this workload (its table entry, else automatic)."""
+    kv, qs, qt = configs.WORKLOADS[key].bwd_splits or (0, 0, 0)
+    return dict(kv_split=kv, q_split=qs, q_split_tiles=qt)
+
+
 def _run_with_tiles(c, t):
     tiles = binding.mask_tile_map(t["mask"], t["q"], t["k"]) if t["mask"] is not None else None
     o, lse = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
                          q_offset=c.q_offset, mask_tiles=tiles)
     delta = binding.bwd_preprocess(o, t["do"])
     dq, dk, dv = binding.bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, mask=t["mask"], scale=c.scale,
-                             causal=c.causal, q_offset=c.q_offset, mask_tiles=tiles)
+                             causal=c.causal, q_offset=c.q_offset, mask_tiles=tiles, **_splits(c.name))
     torch.cuda.synchronize()
     return {"O": host64(o), "LSE": host64(lse), "Delta": host64(delta), "dQ": host64(dq), "dK": host64(dk),
             "dV": host64(dv)}
@@ -60,11 +66,10 @@ def test_structured_dit_full_size_every_element(key):
     say(f"{key}: full size B={c.B} Hq={c.Hq} Hkv={c.Hkv} S={c.Sq} {st}; oracle running")
     t = upload(c)
     kl = torch.tensor(st["key_len"], dtype=torch.int32, device="cuda")
-    kv, qs = configs.WORKLOADS[key].bwd_splits or (0, 0)
     o, lse = binding.fwd(t["q"], t["k"], t["v"], scale=c.scale, key_len=kl, window=st["window"])
     delta = binding.bwd_preprocess(o, t["do"])
     dq, dk, dv = binding.bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, scale=c.scale, key_len=kl,
-                             window=st["window"], kv_split=kv, q_split=qs)
+                             window=st["window"], **_splits(key))
     torch.cuda.synchronize()
     got = {"O": host64(o), "LSE": host64(lse), "Delta": host64(delta), "dQ": host64(dq), "dK": host64(dk),
            "dV": host64(dv)}
@@ -218,11 +223,10 @@ def test_lm_alibi_full_size_sampled():
     say("lm_alibi: full size, sampled rows and columns")
     t = upload(c)
     al = torch.from_numpy(c.meta["alibi"]).to("cuda")
-    kv, qs = configs.WORKLOADS["lm_alibi"].bwd_splits
     o, lse = binding.fwd(t["q"], t["k"], t["v"], scale=c.scale, causal=True, q_offset=0, alibi=al)
     delta = binding.bwd_preprocess(o, t["do"])
     dq, dk, dv = binding.bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, scale=c.scale, causal=True, q_offset=0,
-                             alibi=al, kv_split=kv, q_split=qs)
+                             alibi=al, **_splits("lm_alibi"))
     torch.cuda.synchronize()
     got = {"O": host64(o), "LSE": host64(lse), "Delta": host64(delta), "dQ": host64(dq), "dK": host64(dk),
            "dV": host64(dv)}

@@ -220,6 +220,24 @@ def test_backward_decompositions(name, kv_split, q_split, dq_launch):
     compare_full(c, {"dQ": host64(dq), "dK": host64(dk), "dV": host64(dv)}, ref, names=("dQ", "dK", "dV"))
 
 
+@pytest.mark.parametrize("q_split,q_split_tiles,dq_launch", [(2, 1, 1), (3, 2, 1), (4, 1, 2), (2, 99, 1)])
+@pytest.mark.parametrize("name", ["dit_sa_ragged", "lm_causal_gqa4", "random_bias_bcast", "d64_bf16"])
+def test_backward_split_tail(name, q_split, q_split_tiles, dq_launch):
+    """Only the first query tiles' dQ walks split (dispatched last), the others whole: the split tiles
+    sum fp32 slices over their rows only, the whole ones store directly; the oracle's gradients either way."""
+    c = CASES[name]()
+    t = upload(c)
+    say(f"case {name}: q_split {q_split} over the first {q_split_tiles} query tiles, dq_launch {dq_launch}")
+    o, lse = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
+                         q_offset=c.q_offset)
+    delta = binding.bwd_preprocess(o, t["do"])
+    dq, dk, dv = binding.bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, mask=t["mask"], scale=c.scale,
+                             causal=c.causal, q_offset=c.q_offset, kv_split=2, q_split=q_split,
+                             q_split_tiles=q_split_tiles, dq_launch=dq_launch)
+    torch.cuda.synchronize()
+    compare_full(c, {"dQ": host64(dq), "dK": host64(dk), "dV": host64(dv)}, oracle_full(c), names=("dQ", "dK", "dV"))
+
+
 @pytest.mark.parametrize("name", ["dit_sa_ragged", "lm_causal_gqa4"])
 def test_dq_launch_is_bitwise_neutral(name):
     """The dQ walk in its own launch (two workgroups per compute unit) does the same arithmetic in the
@@ -255,8 +273,9 @@ def test_tuned_split_is_a_candidate_and_exact():
     compare_full(c, {"dQ": host64(dq), "dK": host64(dk), "dV": host64(dv)}, oracle_full(c), names=("dQ", "dK", "dV"))
 
 
-@pytest.mark.parametrize("kv_split,q_split,dq_launch", [(1, 1, 0), (2, 3, 0), (2, 1, 2)])
-def test_chunked_decompositions(kv_split, q_split, dq_launch):
+@pytest.mark.parametrize("kv_split,q_split,dq_launch,q_split_tiles", [(1, 1, 0, 0), (2, 3, 0, 0), (2, 1, 2, 0),
+                                                                      (2, 2, 0, 1)])
+def test_chunked_decompositions(kv_split, q_split, dq_launch, q_split_tiles):
     """The chunked backward adds into the window accumulators the same way for any split."""
     W, C = 512, 128
     c = configs.make("long_window", W=W, Hq=4, Hkv=1)
@@ -270,7 +289,8 @@ def test_chunked_decompositions(kv_split, q_split, dq_launch):
         o, lse = binding.fwd(q, kk, vv, scale=c.scale, causal=True, q_offset=p0)
         delta = binding.bwd_preprocess(o, do)
         binding.bwd_chunked(q, kk, vv, do, lse, delta, dk_acc, dv_acc, scale=c.scale, causal=True, q_offset=p0,
-                            dq=dQ[:, :, p0:p0 + n], kv_split=kv_split, q_split=q_split, dq_launch=dq_launch)
+                            dq=dQ[:, :, p0:p0 + n], kv_split=kv_split, q_split=q_split, dq_launch=dq_launch,
+                            q_split_tiles=q_split_tiles)
     torch.cuda.synchronize()
     ref = oracle_full(c)
     got = {"dQ": host64(dQ), "dK": dk_acc.cpu().numpy().astype(np.float64),
