@@ -38,7 +38,7 @@ WORKLOADS = {
     # the DiT self-attention masks given by their structure instead of a dense mask:
     # the pad as a key length, and a mixed-length batch under a sliding window
     "dit_sa_len": Workload("dit_sa_len", "DiT self-attention, B=1 Hq=16 Hkv=8 S=1542 D=128 bf16, "
-                           "key length 1388 (the pad as a length)", 6, (1, 1, 0)),
+                           "key length 1388 (the pad as a length)", 6, (2, 2, 6)),
     "dit_sa_band": Workload("dit_sa_band", "DiT self-attention, mixed-length batch B=2 Hq=16 Hkv=8 S=1542 D=128 "
                             "bf16, key lengths 1542 / 1101, window 256 keys each side", 7),
     # the LM layer with one attention-sink logit per query head (N(0, 1)); its step adds the
