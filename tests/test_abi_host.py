@@ -157,6 +157,9 @@ def test_backward_rejects():
     assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(p)) == 2 * (1 * 4 * 64 * 64 * 4)
     assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(params(q_split=1, kv_split=1))) == 0
     assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(params(q_split=1, kv_split=2))) == 2 * 2 * (2 * 64 * 64 * 4)
+    # a split tail keeps full-length dQ slices (only the split tiles' rows are written and summed)
+    assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(params(q_split=2, kv_split=1, q_split_tiles=1))) == \
+        B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(params(q_split=2, kv_split=1)))
     assert bwd_call(p, ws=0) == 8
     assert bwd_call(p, ws_bytes=100) == 8
     assert bwd_call(p, ws=BASE + 12 * (1 << 24) + 16) == 5
