@@ -6,7 +6,8 @@ plain float64 C implementation (``fa_oracle.c``) that materialises every score
 row, plus this thin ctypes wrapper. It shares no code with the HIP library.
 
 Every function takes float64 arrays in contiguous ``[B, H, S, D]`` layout and an
-optional additive mask ``[Bm, Sq, Sk]`` (``Bm`` 1 or B, ``-inf`` = masked).
+optional additive mask ``[Bm, Sq, Sk]`` or ``[Bm, Hm, Sq, Sk]`` (``Bm`` 1 or B, ``Hm`` 1
+or Hq: a score bias per head; ``-inf`` = masked).
 """
 from __future__ import annotations
 
@@ -38,7 +39,7 @@ class _Problem(ctypes.Structure):
                 ("Sq", ctypes.c_int32), ("Sk", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("mask_b", ctypes.c_int32),
                 ("q_offset", ctypes.c_int64), ("scale", ctypes.c_double), ("sinks", ctypes.c_void_p),
-                ("alibi", ctypes.c_void_p)]
+                ("alibi", ctypes.c_void_p), ("mask_h", ctypes.c_int32)]
 
 
 _lib = None
@@ -81,14 +82,20 @@ def _problem(q, k, mask, scale, causal, q_offset, sinks=None, alibi=None):
     if q_offset is None:
         q_offset = Sk - Sq if causal else 0
     mb = 0 if mask is None else int(mask.shape[0])
-    if mask is not None and tuple(mask.shape[1:]) != (Sq, Sk):
-        raise ValueError("mask must be [Bm, Sq, Sk]")
+    mh = 0
+    if mask is not None:
+        if mask.ndim == 4:  # [Bm, Hm, Sq, Sk]: Hm = 1 (every head) or Hq (a bias per head)
+            mh = int(mask.shape[1])
+            if mh not in (1, Hq):
+                raise ValueError("a 4-D mask must have 1 or Hq heads")
+        if tuple(mask.shape[-2:]) != (Sq, Sk) or mask.ndim not in (3, 4):
+            raise ValueError("mask must be [Bm, Sq, Sk] or [Bm, Hm, Sq, Sk]")
     if sinks is not None and sinks.shape != (Hq,):
         raise ValueError("sinks must be [Hq]")
     if alibi is not None and alibi.shape != (Hq,):
         raise ValueError("alibi must be [Hq]")
     return _Problem(B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), mb, int(q_offset), float(scale),
-                    None if sinks is None else sinks.ctypes.data, None if alibi is None else alibi.ctypes.data)
+                    None if sinks is None else sinks.ctypes.data, None if alibi is None else alibi.ctypes.data, mh)
 
 
 def forward(q, k, v, mask=None, *, scale: float, causal: bool = False, q_offset: Optional[int] = None,

@@ -42,7 +42,8 @@
  *
  * Layouts: contiguous [B, Hq, Sq, D] for Q, dO, O, dQ; [B, Hkv, Sk, D] for K, V,
  * dK, dV; [B, Hq, Sq] for LSE and Delta; the optional additive mask is
- * [mask_b, Sq, Sk] with mask_b = 1 (shared by the batch) or B.
+ * [mask_b, mask heads, Sq, Sk] with mask_b = 1 (shared by the batch) or B and mask
+ * heads 1 (shared by the heads) or Hq (a per-head score bias).
  */
 #include <math.h>
 #include <pthread.h>
@@ -59,6 +60,7 @@ typedef struct {
     double scale;
     const double *sinks; /* [Hq] logits, NULL = none */
     const double *alibi; /* [Hq] slopes, NULL = none */
+    int32_t mask_h;      /* heads of the mask: 0 or 1 = one mask for every head, Hq = one per head */
 } ora_problem;
 
 typedef struct {
@@ -93,13 +95,21 @@ static double dot(const double *a, const double *b, int n) {
     return s;
 }
 
-/* Is score (b, i, j) visible at all (neither causal- nor mask-excluded)? */
-static int visible(const ora_inputs *in, int b, int i, int j) {
+/* The mask entry of (b, h, i, j): [mask_b][mask heads][Sq][Sk], a dimension of size 1
+ * shared by every batch entry or head. */
+static double mask_at(const ora_inputs *in, int b, int h, int i, int j) {
+    const ora_problem *p = in->p;
+    const int mb = p->mask_b == 1 ? 0 : b;
+    const int hm = p->mask_h > 1 ? p->mask_h : 1, mh = p->mask_h > 1 ? h : 0;
+    return in->M[(((int64_t)mb * hm + mh) * p->Sq + i) * p->Sk + j];
+}
+
+/* Is score (b, h, i, j) visible at all (neither causal- nor mask-excluded)? */
+static int visible(const ora_inputs *in, int b, int h, int i, int j) {
     const ora_problem *p = in->p;
     if (p->causal && (int64_t)j > p->q_offset + i) return 0;
     if (p->mask_b) {
-        int mb = p->mask_b == 1 ? 0 : b;
-        double mv = in->M[((int64_t)mb * p->Sq + i) * p->Sk + j];
+        double mv = mask_at(in, b, h, i, j);
         if (isinf(mv) && mv < 0) return 0;
     }
     return 1;
@@ -108,12 +118,9 @@ static int visible(const ora_inputs *in, int b, int i, int j) {
 /* S_ij for query head h (step 1 of the definition). */
 static double score(const ora_inputs *in, int b, int h, int i, int j) {
     const ora_problem *p = in->p;
-    if (!visible(in, b, i, j)) return -INFINITY;
+    if (!visible(in, b, h, i, j)) return -INFINITY;
     double mv = 0.0;
-    if (p->mask_b) {
-        int mb = p->mask_b == 1 ? 0 : b;
-        mv = in->M[((int64_t)mb * p->Sq + i) * p->Sk + j];
-    }
+    if (p->mask_b) mv = mask_at(in, b, h, i, j);
     if (p->alibi) mv -= p->alibi[h] * fabs((double)j - (double)(p->q_offset + i));
     int g = kv_head(p, h);
     return p->scale * dot(q_row(in, b, h, i), k_row(in, b, g, j), p->D) + mv;
@@ -246,6 +253,7 @@ static int check_problem(const ora_problem *p) {
     if (p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->Sq <= 0 || p->Sk <= 0 || p->D <= 0) return 1;
     if (p->Hq % p->Hkv) return 2;
     if (p->mask_b != 0 && p->mask_b != 1 && p->mask_b != p->B) return 3;
+    if (p->mask_h < 0 || (p->mask_h > 1 && p->mask_h != p->Hq)) return 4;
     return 0;
 }
 
@@ -366,10 +374,9 @@ int ora_cols(const ora_problem *p, const double *Q, const double *K, const doubl
         const int j = (int)(cols[c] % p->Sk);
         const int g = (int)((cols[c] / p->Sk) % p->Hkv);
         const int b = (int)(cols[c] / ((int64_t)p->Sk * p->Hkv));
-        for (int i = 0; i < p->Sq; ++i) {
-            if (!visible(&in, b, i, j)) continue;
-            for (int h = g * G; h < (g + 1) * G; ++h) flag[((int64_t)b * p->Hq + h) * p->Sq + i] = 1;
-        }
+        for (int i = 0; i < p->Sq; ++i)
+            for (int h = g * G; h < (g + 1) * G; ++h)
+                if (visible(&in, b, h, i, j)) flag[((int64_t)b * p->Hq + h) * p->Sq + i] = 1;
     }
     int64_t nn = 0;
     for (int64_t r = 0; r < nrows; ++r)

@@ -620,3 +620,60 @@ def test_alibi_zero_scores_geometric_series():
         np.testing.assert_allclose(L[0, h], np.log((1 - np.exp(-a * (i + 1))) / (1 - np.exp(-a))), rtol=1e-14)
         w = np.exp(-a * (S - 1 - np.arange(S)))  # last row's weights
         np.testing.assert_allclose(O[0, h, S - 1], (w / w.sum()) @ v[0, h], rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# a score bias per head (mask [Bm, Hq, Sq, Sk]): pinned to the heads run one by one
+# with their own 3-D masks, and to finite differences
+# ---------------------------------------------------------------------------
+def _head_bias_problem(seed):
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, Sq, Sk, D = 2, 4, 2, 5, 6, 4
+    q, k, v, do = (rng.standard_normal(s) for s in ((B, Hq, Sq, D), (B, Hkv, Sk, D), (B, Hkv, Sk, D), (B, Hq, Sq, D)))
+    m = 0.7 * rng.standard_normal((B, Hq, Sq, Sk))
+    m[0, 1, :, 2] = -np.inf      # a key column hidden in one head only
+    m[1, 3, 4, :] = -np.inf      # a row fully masked in one head only
+    return q, k, v, do, m
+
+
+def test_head_bias_equals_heads_one_by_one():
+    q, k, v, do, m = _head_bias_problem(61)
+    ref = oracle.backward(q, k, v, do, m, scale=0.5)
+    G = q.shape[1] // k.shape[1]
+    dk, dv = np.zeros_like(k), np.zeros_like(v)
+    for h in range(q.shape[1]):
+        g = h // G
+        one = oracle.backward(q[:, h:h + 1], k[:, g:g + 1], v[:, g:g + 1], do[:, h:h + 1], m[:, h], scale=0.5)
+        for n in ("O", "LSE", "Delta", "dQ"):
+            np.testing.assert_allclose(ref[n][:, h:h + 1], one[n], rtol=1e-13, atol=1e-14, err_msg=n)
+        dk[:, g] += one["dK"][:, 0]
+        dv[:, g] += one["dV"][:, 0]
+    np.testing.assert_allclose(ref["dK"], dk, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ref["dV"], dv, rtol=1e-12, atol=1e-13)
+    assert np.all(ref["O"][1, 3, 4] == 0) and ref["LSE"][1, 3, 4] == 0  # fully masked in that head only
+    assert np.any(ref["O"][1, 2, 4] != 0)
+    # a per-head mask whose heads are all equal is the shared 3-D mask
+    same = np.repeat(m[:, :1], q.shape[1], axis=1)
+    a = oracle.backward(q, k, v, do, same, scale=0.5)
+    b = oracle.backward(q, k, v, do, m[:, 0], scale=0.5)
+    for n in ("O", "LSE", "dQ", "dK", "dV"):
+        assert np.array_equal(a[n], b[n]), n
+
+
+def test_head_bias_finite_differences():
+    q, k, v, do, m = _head_bias_problem(62)
+    r = oracle.backward(q, k, v, do, m, scale=0.6)
+
+    def loss(a):
+        O, _ = oracle.forward(a["q"], a["k"], a["v"], m, scale=0.6, threads=1)
+        return float(np.sum(O * do))
+
+    h = 1e-6
+    for name_t, t, grad in (("q", q, r["dQ"]), ("k", k, r["dK"]), ("v", v, r["dV"])):
+        fd = np.zeros_like(t)
+        for idx in np.ndindex(t.shape):
+            tp, tm = t.copy(), t.copy()
+            tp[idx] += h
+            tm[idx] -= h
+            fd[idx] = (loss({"q": q, "k": k, "v": v, name_t: tp}) - loss({"q": q, "k": k, "v": v, name_t: tm})) / (2 * h)
+        assert np.abs(fd - grad).max() / np.abs(grad).max() < 1e-7, name_t
