@@ -36,7 +36,7 @@ class FaAttnParams(ctypes.Structure):
                 ("fwd_split", ctypes.c_int32), ("key_len", ctypes.c_void_p), ("q_len", ctypes.c_void_p),
                 ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
                 ("bwd_dq_launch", ctypes.c_int32), ("sinks", ctypes.c_void_p), ("alibi", ctypes.c_void_p),
-                ("q_split_tiles", ctypes.c_int32)]
+                ("q_split_tiles", ctypes.c_int32), ("mask_stride_h", ctypes.c_int64)]
 
 
 class FaError(RuntimeError):
@@ -152,13 +152,17 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
                 raise ValueError(f"{name} must be a contiguous fp32 [Hq] tensor on the device")
             setattr(p, name, t.data_ptr())
     if mask is not None:
-        if mask.dtype != torch.float32 or mask.dim() != 3 or mask.stride(2) != 1:
-            raise ValueError("mask must be an fp32 [Bm, Sq, Sk] tensor with a contiguous last dimension")
-        if mask.shape[1] != Sq or mask.shape[2] != Sk or mask.shape[0] not in (1, B):
-            raise ValueError("mask must be [1 or B, Sq, Sk]")
+        if mask.dtype != torch.float32 or mask.dim() not in (3, 4) or mask.stride(-1) != 1:
+            raise ValueError("mask must be an fp32 [Bm, Sq, Sk] or [Bm, Hm, Sq, Sk] tensor with a contiguous last "
+                             "dimension")
+        if mask.dim() == 4 and mask.shape[1] not in (1, Hq):
+            raise ValueError("a per-head mask must have 1 or Hq heads")
+        if mask.shape[-2] != Sq or mask.shape[-1] != Sk or mask.shape[0] not in (1, B):
+            raise ValueError("mask must be [1 or B, (1 or Hq,) Sq, Sk]")
         p.mask = mask.data_ptr()
         p.mask_stride_b = 0 if mask.shape[0] == 1 else mask.stride(0)
-        p.mask_stride_q = mask.stride(1)
+        p.mask_stride_q = mask.stride(-2)
+        p.mask_stride_h = mask.stride(1) if mask.dim() == 4 and mask.shape[1] > 1 else 0
         if mask_tiles is not None:
             if mask_tiles.dtype != torch.uint8 or not mask_tiles.is_contiguous():
                 raise ValueError("mask_tiles must be a contiguous uint8 tensor from mask_tile_map()")

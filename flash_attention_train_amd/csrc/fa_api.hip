@@ -104,6 +104,9 @@ fa_status check_params(const fa_attn_params* p) {
   if (p->mask) {
     if (p->mask_stride_q < p->Sk) return fail(FA_ERR_STRIDE, "mask_stride_q (%lld) < Sk", (long long)p->mask_stride_q);
     if (p->mask_stride_b < 0) return fail(FA_ERR_STRIDE, "mask_stride_b is negative");
+    if (p->mask_stride_h < 0) return fail(FA_ERR_STRIDE, "mask_stride_h is negative");
+    if (p->mask_stride_h > 0 && p->mask_tiles)
+      return fail(FA_ERR_UNSUPPORTED, "the mask block map is per batch entry: a mask per head runs without one");
     if (reinterpret_cast<uintptr_t>(p->mask) % 4) return fail(FA_ERR_ALIGN, "mask pointer is not 4-byte aligned");
   }
   return FA_OK;
@@ -111,7 +114,8 @@ fa_status check_params(const fa_attn_params* p) {
 
 Extent mask_extent(const fa_attn_params* p) {
   const uintptr_t base = reinterpret_cast<uintptr_t>(p->mask);
-  const int64_t last = (int64_t)(p->B - 1) * p->mask_stride_b + (int64_t)(p->Sq - 1) * p->mask_stride_q + p->Sk;
+  const int64_t last = (int64_t)(p->B - 1) * p->mask_stride_b + (int64_t)(p->Hq - 1) * p->mask_stride_h +
+                       (int64_t)(p->Sq - 1) * p->mask_stride_q + p->Sk;
   return {base, base + (uintptr_t)(last * 4)};
 }
 
@@ -134,6 +138,7 @@ fa::AttnShape shape_of(const fa_attn_params* p) {
   a.mask = p->mask;
   a.mask_sb = p->mask_stride_b;
   a.mask_sq = p->mask_stride_q;
+  a.mask_sh = p->mask ? p->mask_stride_h : 0;
   a.tiles = p->mask ? p->mask_tiles : nullptr;
   const int64_t nblk = tile_batches(p) * tile_rows(p) * tile_cols(p);
   const int64_t rowbits_off = (nblk + 255) / 256 * 256;
@@ -399,7 +404,8 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   a.accumulate = accumulate ? 1 : 0;
   a.inv_scale = 1.f / p->scale;
   const uintptr_t mp = reinterpret_cast<uintptr_t>(p->mask);
-  a.mask_vec4 = p->mask && mp % 16 == 0 && p->mask_stride_q % 4 == 0 && p->mask_stride_b % 4 == 0;
+  a.mask_vec4 = p->mask && mp % 16 == 0 && p->mask_stride_q % 4 == 0 && p->mask_stride_b % 4 == 0 &&
+                 p->mask_stride_h % 4 == 0;
   const int is_bf16 = p->dtype == FA_BF16;
   fa_status st;
   if (is_bf16) {
@@ -534,7 +540,8 @@ fa_status fwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   a.lse_sh = lse->stride_h;
   a.inv_scale = 1.f / p->scale;
   const uintptr_t mp = reinterpret_cast<uintptr_t>(p->mask);
-  a.mask_vec4 = p->mask && mp % 16 == 0 && p->mask_stride_q % 4 == 0 && p->mask_stride_b % 4 == 0;
+  a.mask_vec4 = p->mask && mp % 16 == 0 && p->mask_stride_q % 4 == 0 && p->mask_stride_b % 4 == 0 &&
+                 p->mask_stride_h % 4 == 0;
   a.sinks = p->sinks;
   a.splits = splits;
   a.part_o = nullptr;
@@ -704,6 +711,7 @@ fa_status fa_train_mask_tiles(const fa_attn_params* p, uint8_t* tiles, hipStream
   fa_status s = check_params(p);
   if (s) return s;
   if (!p->mask) return fail(FA_ERR_NULL, "the params carry no mask");
+  if (p->mask_stride_h > 0) return fail(FA_ERR_UNSUPPORTED, "the mask block map is per batch entry, not per head");
   if (!tiles) return fail(FA_ERR_NULL, "tiles is NULL");
   const uintptr_t t = reinterpret_cast<uintptr_t>(tiles);
   if (t % 8) return fail(FA_ERR_ALIGN, "tiles is not 8-byte aligned");

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(const BwdArgs args) {
           bool vis = key < a.Sk && qi < a.Sq;
           if (CAUSAL) vis = vis && ((int64_t)key <= a.q_offset + qi);
           float x = sacc[r] * cs;
-          if (MASK && vis) x += a.mask[b * a.mask_sb + (int64_t)qi * a.mask_sq + key] * kLog2e;
+          if (MASK && vis) x += a.mask[b * a.mask_sb + h * a.mask_sh + (int64_t)qi * a.mask_sq + key] * kLog2e;
           const float p = vis ? fast_exp2(x - lse_lds[ql]) : 0.f;
           sacc[r] = p;
           dpacc[r] = p * (dpacc[r] - dlt_lds[ql]);

@@ -510,7 +510,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
         for (int r = 0; r < 16; ++r) sacc[r] -= sl * fabsf(base - (float)(8 * (r >> 2) + (r & 3)));
       }
       if (BIAS && bias && a.mask) {
-        const float* mk = a.mask + b * a.mask_sb + min(key, a.Sk - 1);
+        const float* mk = a.mask + b * a.mask_sb + h * a.mask_sh + min(key, a.Sk - 1);
         #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = min(q0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3), a.Sq - 1);
@@ -859,7 +859,7 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
         for (int r = 0; r < 16; ++r) st[r] -= sl * fabsf(base + (float)(8 * (r >> 2) + (r & 3)));
       }
       if (BIAS && bias && a.mask) {  // additive mask values, 4 keys at a time (keys past the end read 0)
-        const float* mr = a.mask + b * a.mask_sb + (int64_t)min(row, a.Sq - 1) * a.mask_sq;
+        const float* mr = a.mask + b * a.mask_sb + h * a.mask_sh + (int64_t)min(row, a.Sq - 1) * a.mask_sq;
         #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int k4 = key0 + 32 * kb + 8 * rr + 4 * g;

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(const FwdArgs args) {
   const T* K = static_cast<const T*>(args.k) + b * args.sk.b + hk * args.sk.h;
   const T* V = static_cast<const T*>(args.v) + b * args.sv.b + hk * args.sv.h;
   const float* Mrow = nullptr;
-  if (MASK && qrow < a.Sq) Mrow = a.mask + b * a.mask_sb + (int64_t)qrow * a.mask_sq;
+  if (MASK && qrow < a.Sq) Mrow = a.mask + b * a.mask_sb + h * a.mask_sh + (int64_t)qrow * a.mask_sq;
 
   // Q as the B operand of S^T = K Q^T: lane (row r32, half g) holds d = 16 s + 8 g + j
   Frag<T> qf[DS];

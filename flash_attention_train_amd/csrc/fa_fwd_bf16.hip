@@ -278,7 +278,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
       if (MASK && bias && a.mask) {
         // the mask enters the raw score as M / scale so that one fma applies both later;
         // keys past the end read 0 (the tail is masked below), rows past the end the last row
-        const float* mr = a.mask + b * a.mask_sb + (int64_t)min(row, a.Sq - 1) * a.mask_sq;
+        const float* mr = a.mask + b * a.mask_sb + h * a.mask_sh + (int64_t)min(row, a.Sq - 1) * a.mask_sq;
         #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           #pragma unroll

@@ -21,8 +21,9 @@ struct AttnShape {
   int causal;
   int64_t q_offset;  // key position of query row 0
   float scale;       // multiplies <q, k>
-  const float* mask; // additive [b][i][j] fp32 or nullptr
+  const float* mask; // additive [b][h][i][j] fp32 or nullptr (b and h strides 0: shared)
   int64_t mask_sb, mask_sq;
+  int64_t mask_sh;   // head stride of the mask: 0 = one mask for every head, else a score bias per head
   const uint8_t* tiles;      // mask block classes [Bm][ceil(Sq/64)][ceil(Sk/64)] or nullptr
   const uint64_t* rowbits;   // per block, 64 words: bit j of word i = entry (i, j) visible
   const uint64_t* colbits;   // per block, 64 words: bit i of word j = entry (i, j) visible

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FA_TRAIN_ABI_VERSION 8
+#define FA_TRAIN_ABI_VERSION 9
 
 typedef enum fa_status {
     FA_OK = 0,
@@ -154,6 +154,12 @@ typedef struct fa_attn_params {
      * whole. 0 = all tiles when q_split is given, else automatic. Splitting only the last
      * units to run shortens the end of the launch, when few compute units are busy. */
     int32_t q_split_tiles;
+    /* Head stride of the mask, in elements: 0 = one mask for every head (the layout above);
+     * > 0 = a mask per query head, entry (b, h, i, j) at mask + b * mask_stride_b +
+     * h * mask_stride_h + i * mask_stride_q + j -- an additive score bias per head (the
+     * pull request's KQ bias), with -inf still hiding entries. Its own gradient (dS) is not
+     * produced. A per-head mask takes no mask block map (mask_tiles must be NULL). */
+    int64_t mask_stride_h;
 } fa_attn_params;
 
 /* Forward: writes O (dtype) and LSE (fp32, natural log). Fully masked rows get

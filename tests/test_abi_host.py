@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(L, n), n
         assert n in B.SIGNATURES, f"{n} has no ctypes signature in the binding"
-    assert L.fa_train_version() == 8
+    assert L.fa_train_version() == 9
 
 
 BASE = 0x7F0000000000  # fake, 256-byte aligned device addresses
@@ -44,7 +44,7 @@ def params(**kw):
     a = dict(B=1, Hq=4, Hkv=2, Sq=64, Sk=64, D=64, dtype=B.FA_BF16, causal=0, q_offset=0, scale=0.125, mask=None,
              mask_stride_b=0, mask_stride_q=0, mask_tiles=None, fwd_variant=0, kv_split=0, q_split=0, fwd_split=0, key_len=None, q_len=None,
              window_left=-1, window_right=-1, bwd_dq_launch=0, sinks=None, alibi=None,
-             q_split_tiles=0)
+             q_split_tiles=0, mask_stride_h=0)
     a.update(kw)
     return B.FaAttnParams(*(a[f] for f, _ in B.FaAttnParams._fields_))
 
@@ -88,6 +88,8 @@ FWD_ERRORS = [
     ("window bound -2", params(window_left=-2), {}, 2),
     ("unknown dQ launch hint", params(bwd_dq_launch=3), {}, 2),
     ("negative q_split_tiles", params(q_split_tiles=-1), {}, 2),
+    ("per-head mask with a block map", params(mask=BASE + 9 * (1 << 24), mask_stride_q=64, mask_stride_h=64 * 64,
+                                              mask_tiles=BASE + 10 * (1 << 24)), {}, 7),
     ("sinks on fp32", params(dtype=B.FA_F32, sinks=BASE), {}, 7),
     ("misaligned sinks", params(sinks=BASE + 2), {}, 5),
     ("ALiBi on fp32", params(dtype=B.FA_F32, alibi=BASE), {}, 7),
