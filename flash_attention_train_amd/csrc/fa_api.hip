@@ -428,20 +428,25 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
     plan.sdq = strides_of(dq);
     const int64_t nq = (int64_t)p->B * p->Hq * p->Sq * p->D, nk = (int64_t)p->B * p->Hkv * p->Sk * p->D;
     if ((st = hip_status(fa::launch_bwd_bf16(a, plan, stream), "backward"))) return st;
-    if (wl.need_dq) {
-      // only the rows of the split query tiles (the first ones) have slices to sum
-      const int rows = std::min(p->Sq, plan.q_tiles_split * fa::kBwdUnit);
-      fa::ReduceArgs r = {p->B, p->Hq, rows, p->D, p->Sq, plan.dq_part, q, nq, dq->data, strides_of(dq), p->scale, 0};
-      if ((st = hip_status(fa::launch_reduce_parts(r, nullptr, 1, stream), "dq reduce"))) return st;
-    }
-    if (wl.need_dkdv) {
-      // the chunked walk adds into its fp32 window accumulators; otherwise bf16 outputs
-      const int out_bf16 = accumulate ? 0 : 1, acc = accumulate ? 1 : 0;
-      fa::ReduceArgs rk = {p->B,      p->Hkv, p->Sk,   p->D, p->Sk, plan.dk_part, kv, nk,
-                           dk->data, strides_of(dk), p->scale, acc};
-      fa::ReduceArgs rv = {p->B,      p->Hkv, p->Sk,   p->D, p->Sk, plan.dv_part, kv, nk,
-                           dv->data, strides_of(dv), 1.f,      acc};
-      if ((st = hip_status(fa::launch_reduce_parts(rk, &rv, out_bf16, stream), "dk / dv reduce"))) return st;
+    // the reduce passes: dQ over the rows of the split query tiles (the first ones), dK and dV
+    // over every key; one launch when all three go to bf16 outputs (the chunked walk adds dK / dV
+    // into its fp32 window accumulators instead)
+    const int rows = std::min(p->Sq, plan.q_tiles_split * fa::kBwdUnit);
+    const fa::ReduceArgs r = {p->B, p->Hq, rows, p->D, p->Sq, plan.dq_part, q, nq, dq->data, strides_of(dq),
+                              p->scale, 0};
+    const int out_bf16 = accumulate ? 0 : 1, acc = accumulate ? 1 : 0;
+    const fa::ReduceArgs rk = {p->B, p->Hkv, p->Sk, p->D, p->Sk, plan.dk_part, kv, nk,
+                               dk->data, strides_of(dk), p->scale, acc};
+    const fa::ReduceArgs rv = {p->B, p->Hkv, p->Sk, p->D, p->Sk, plan.dv_part, kv, nk,
+                               dv->data, strides_of(dv), 1.f, acc};
+    if (wl.need_dq && wl.need_dkdv && !accumulate) {
+      if ((st = hip_status(fa::launch_reduce_parts(rk, &rv, &r, 1, stream), "dq / dk / dv reduce"))) return st;
+    } else {
+      if (wl.need_dq && (st = hip_status(fa::launch_reduce_parts(r, nullptr, nullptr, 1, stream), "dq reduce")))
+        return st;
+      if (wl.need_dkdv &&
+          (st = hip_status(fa::launch_reduce_parts(rk, &rv, nullptr, out_bf16, stream), "dk / dv reduce")))
+        return st;
     }
     return FA_OK;
   }

@@ -8,6 +8,8 @@
 //   * the gradient of the attention sinks from the LSE and Delta;
 //   * the bf16 values of a q8_0-stored K/V window.
 // The first three stream their operands once with 16-byte loads and stores.
+#include <algorithm>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -72,8 +74,10 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const DqArgs p) {
 // Sum of the backward's fp32 partial slices, 8 consecutive elements per thread: each
 // slice element is read once, the result written once (or added to an fp32 output).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void reduce_parts_kernel(const ReduceArgs p0, const ReduceArgs p1) {
-  const ReduceArgs& p = blockIdx.y ? p1 : p0;  // one launch reduces up to two tensors (dK and dV)
+__global__ __launch_bounds__(256) void reduce_parts_kernel(const ReduceArgs p0, const ReduceArgs p1,
+                                                           const ReduceArgs p2) {
+  // one launch reduces up to three tensors of one output dtype (dK, dV and dQ)
+  const ReduceArgs& p = blockIdx.y == 0 ? p0 : blockIdx.y == 1 ? p1 : p2;
   constexpr int CPR = D / 8;
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t nrows = (int64_t)p.B * p.H * p.S;
@@ -282,17 +286,20 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream) {
 }
 
 template <typename T, int D>
-hipError_t launch_reduce_t(const ReduceArgs& p, const ReduceArgs* p1, hipStream_t stream) {
-  const int64_t chunks = (int64_t)p.B * p.H * p.S * (D / 8);  // p1 has the same shape
-  const dim3 grid((unsigned)((chunks + 255) / 256), p1 ? 2 : 1);
-  hipLaunchKernelGGL((reduce_parts_kernel<T, D>), grid, dim3(256), 0, stream, p, p1 ? *p1 : p);
+hipError_t launch_reduce_t(const ReduceArgs& p, const ReduceArgs* p1, const ReduceArgs* p2, hipStream_t stream) {
+  // blocks over the largest tensor; the others' threads past their ends return at once
+  int64_t chunks = (int64_t)p.B * p.H * p.S * (D / 8);
+  if (p2) chunks = std::max<int64_t>(chunks, (int64_t)p2->B * p2->H * p2->S * (D / 8));
+  const dim3 grid((unsigned)((chunks + 255) / 256), p2 ? 3 : p1 ? 2 : 1);
+  hipLaunchKernelGGL((reduce_parts_kernel<T, D>), grid, dim3(256), 0, stream, p, p1 ? *p1 : p, p2 ? *p2 : p);
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_parts(const ReduceArgs& p, const ReduceArgs* p1, int is_bf16, hipStream_t stream) {
+hipError_t launch_reduce_parts(const ReduceArgs& p, const ReduceArgs* p1, const ReduceArgs* p2, int is_bf16,
+                               hipStream_t stream) {
   if (is_bf16)
-    return p.D == 64 ? launch_reduce_t<bf16, 64>(p, p1, stream) : launch_reduce_t<bf16, 128>(p, p1, stream);
-  return p.D == 64 ? launch_reduce_t<float, 64>(p, p1, stream) : launch_reduce_t<float, 128>(p, p1, stream);
+    return p.D == 64 ? launch_reduce_t<bf16, 64>(p, p1, p2, stream) : launch_reduce_t<bf16, 128>(p, p1, p2, stream);
+  return p.D == 64 ? launch_reduce_t<float, 64>(p, p1, p2, stream) : launch_reduce_t<float, 128>(p, p1, p2, stream);
 }
 
 hipError_t launch_dq_convert(const DqArgs& p, int is_bf16, hipStream_t stream) {

@@ -242,7 +242,9 @@ hipError_t launch_mask_tiles(const AttnShape& a, uint8_t* tiles, hipStream_t str
 hipError_t launch_bwd(const BwdArgs& args, int is_bf16, hipStream_t stream);
 hipError_t launch_dq_convert(const DqArgs& args, int is_bf16, hipStream_t stream);
 // reduces args, and args1 too when given (same shape and dtype: one launch for dK and dV)
-hipError_t launch_reduce_parts(const ReduceArgs& args, const ReduceArgs* args1, int is_bf16, hipStream_t stream);
+// reduces args, and args1 / args2 too when given (same D and output dtype; one launch)
+hipError_t launch_reduce_parts(const ReduceArgs& args, const ReduceArgs* args1, const ReduceArgs* args2, int is_bf16,
+                               hipStream_t stream);
 hipError_t launch_sink_grad(const SinkArgs& args, hipStream_t stream);
 
 // bf16 values of a q8_0 window: out[b][h][s][32 c + t] = bf16(d[b][h][s][c] * qs[b][h][s][32 c + t])
