@@ -10,7 +10,7 @@ S=1542, D=128, bf16, pad mask): mask-adjusted fwd+bwd TFLOP/s (14 * D * N FLOPs
 per step, N = unmasked score pairs). Other workloads are reported under "extra".
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload dit_sa]
-                    [--extra lm_causal,dit_ca,long_window,dit_sa_len,dit_sa_band,lm_sinks,lm_alibi,long_window_q8]
+                    [--extra lm_causal,dit_ca,long_window,dit_sa_len,dit_sa_band,lm_sinks,lm_alibi,long_window_q8,long_window_f16]
                     [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dit_sa")
-    ap.add_argument("--extra", default="lm_causal,dit_ca,long_window,dit_sa_len,dit_sa_band,lm_sinks,lm_alibi,long_window_q8",
+    ap.add_argument("--extra", default="lm_causal,dit_ca,long_window,dit_sa_len,dit_sa_band,lm_sinks,lm_alibi,long_window_q8,long_window_f16",
                     help="other workloads to time, comma separated ('none' for none); long_window is the "
                          "64-chunk walk over a 32768-long window")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -236,8 +236,9 @@ def time_long_window(steps: int, warmup: int, key: str = "long_window") -> dict:
     (dK/dV added into fp32 window accumulators, zeroed at the start of the walk). The
     whole walk (192 launches) is captured in one HIP graph and replayed; FLOPs are the
     walk's exact causal pairs, which equal the one-shot causal run's. With
-    key = "long_window_q8" the window is stored as q8_0 and every chunk first writes the
-    bf16 values of the 512 window rows it adds (one pass over the window per walk)."""
+    key = "long_window_q8" (or "long_window_f16") the window is stored as q8_0 (fp16) and
+    every chunk first writes the bf16 values of the 512 window rows it adds (one pass over
+    the window per walk)."""
     import torch
 
     from flash_attention_train_amd import accounting, binding, configs
@@ -248,10 +249,13 @@ def time_long_window(steps: int, warmup: int, key: str = "long_window") -> dict:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda")
 
     q, k, v, do = up(c.q), up(c.k), up(c.v), up(c.do)
-    q8 = c.meta.get("q8")
-    if q8 is not None:  # the window's bf16 rows are written by the walk itself
+    q8, f16 = c.meta.get("q8"), c.meta.get("f16")
+    if q8 is not None:
         kq, kd = (torch.from_numpy(a).to("cuda") for a in q8["k"])
         vq, vd = (torch.from_numpy(a).to("cuda") for a in q8["v"])
+    if f16 is not None:
+        k16, v16 = (torch.from_numpy(f16[n]).to("cuda") for n in ("k", "v"))
+    if q8 is not None or f16 is not None:  # the window's bf16 rows are written by the walk itself
         k.zero_()
         v.zero_()
     dk_acc = torch.zeros((1, c.Hkv, W, c.D), dtype=torch.float32, device="cuda")
@@ -276,6 +280,9 @@ def time_long_window(steps: int, warmup: int, key: str = "long_window") -> dict:
             if q8 is not None:
                 binding.dequant_q8_0(kq[:, :, p0:sk], kd[:, :, p0:sk], out=k[:, :, p0:sk])
                 binding.dequant_q8_0(vq[:, :, p0:sk], vd[:, :, p0:sk], out=v[:, :, p0:sk])
+            if f16 is not None:
+                binding.convert_f16(k16[:, :, p0:sk], out=k[:, :, p0:sk])
+                binding.convert_f16(v16[:, :, p0:sk], out=v[:, :, p0:sk])
             binding.fwd(qc, kc, vc, scale=c.scale, causal=True, q_offset=p0, out=O[:, :, p0:p0 + n],
                         lse=LSE[:, :, p0:p0 + n], workspace=fws)
             binding.bwd_preprocess(O[:, :, p0:p0 + n], doc, delta=Delta[:, :, p0:p0 + n])
@@ -402,7 +409,7 @@ def main():
 
     extra = {}
     for key in [k for k in args.extra.split(",") if k and k not in (args.workload, "none")]:
-        if key in ("long_window", "long_window_q8"):
+        if key in ("long_window", "long_window_q8", "long_window_f16"):
             extra[key] = time_long_window(max(2, args.steps // 8), 1, key)
             log(f"[bench] {key}: {extra[key]['ms_per_walk']:.2f} ms/walk, {extra[key]['tflops']:.1f} TFLOP/s")
             torch.cuda.empty_cache()

@@ -68,6 +68,8 @@ SIGNATURES = {
     "fa_train_bwd_sinks": ([_PP, _PV, _PV, _VP, _VP], ctypes.c_int),
     "fa_train_dequant_q8_0": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _PV, _PV, _PV, _VP],
                               ctypes.c_int),
+    "fa_train_convert_f16": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _PV, _PV,
+                              ctypes.c_int32, _VP], ctypes.c_int),
     "fa_train_probe_mfma": ([ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP], ctypes.c_int),
     "fa_train_probe_ds_read_tr16": ([ctypes.c_int32, _VP, _VP, _VP], ctypes.c_int),
 }
@@ -268,6 +270,23 @@ def dequant_q8_0(qs, d, *, out=None, stream=None):
         out = torch.empty(qs.shape, dtype=torch.bfloat16, device=qs.device)
     _check("fa_train_dequant_q8_0", lib().fa_train_dequant_q8_0(B, H, S, D, view4(qs), view4(d), view4(out),
                                                                 _stream_handle(stream)))
+    return out
+
+
+def convert_f16(src, *, out=None, dtype=None, stream=None):
+    """Values of an f16-stored K or V window in a compute type: ``src`` float16 [B, H, S, D] (a view
+    with a contiguous last dimension). Writes ``out`` (float32 or bfloat16 [B, H, S, D]; made in
+    ``dtype``, default bfloat16, when None): exact into float32, nearest-even into bfloat16."""
+    if src.dtype != torch.float16:
+        raise TypeError("src must be float16")
+    if out is None:
+        out = torch.empty(src.shape, dtype=dtype or torch.bfloat16, device=src.device)
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be float32 or bfloat16")
+    Bn, H, S, D = src.shape
+    _check("fa_train_convert_f16", lib().fa_train_convert_f16(Bn, H, S, D, view4(src), view4(out),
+                                                              FA_F32 if out.dtype == torch.float32 else FA_BF16,
+                                                              _stream_handle(stream)))
     return out
 
 

@@ -1,4 +1,4 @@
-"""The five workloads the op is checked and measured on.
+"""The workloads the op is checked and measured on.
 
 Shapes follow the pages' two trainers: the DiT adapter trainer (self-attention
 at a 1542-token crop with GQA, cross-attention over up to 512 encoder tokens with
@@ -12,7 +12,9 @@ from __future__ import annotations
 
 from dataclasses import dataclass
 
-from .inputs import BF16, F32, Case, alibi_slopes, make_case, quantize_q8_0, sink_logits
+import numpy as np
+
+from .inputs import BF16, F32, Case, alibi_slopes, make_case, quantize_q8_0, sink_logits, stored
 
 
 @dataclass(frozen=True)
@@ -45,12 +47,15 @@ WORKLOADS = {
     # sinks' gradient pass
     "lm_sinks": Workload("lm_sinks", "LM causal GQA with attention sinks, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 8,
                          (2, 1, 0)),
-    # the long-window walk over a q8_0-stored K/V window (the pages train such a cache in
-    # place): the same queries and K/V values, quantised to q8_0 blocks
     # the LM layer with ALiBi (slopes 2^(-8 (h + 1) / Hq)) in place of positional rotations
     "lm_alibi": Workload("lm_alibi", "LM causal GQA with ALiBi, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 10, (2, 1, 0)),
+    # the long-window walk over a q8_0-stored K/V window (the pages train such a cache in
+    # place): the same queries and K/V values, quantised to q8_0 blocks
     "long_window_q8": Workload("long_window_q8", "long-window chunked walk over a q8_0 K/V window, W=32768, "
                                "64 chunks of 512, Hq=16 Hkv=4 D=128", 9),
+    # the same walk over an fp16-stored window: the K/V draws rounded once to fp16
+    "long_window_f16": Workload("long_window_f16", "long-window chunked walk over an f16 K/V window, W=32768, "
+                                "64 chunks of 512, Hq=16 Hkv=4 D=128", 11),
 }
 
 # the sliding window of the structured DiT workload: keys within this distance on each
@@ -107,13 +112,19 @@ def make(key: str, **shrink) -> Case:
             c.meta["structure"] = {"key_len": lens, "q_len": None, "window": (w, w)}
         c.meta["mask_kind"] = "structured"
         return c
-    if key in ("long_window", "long_window_q8"):
+    if key in ("long_window", "long_window_q8", "long_window_f16"):
         W = shrink.pop("W", LONG_WINDOW)
         a = dict(B=1, Hq=16, Hkv=4, Sq=W, Sk=W, D=128, dtype=BF16)
         a.update(shrink)
         c = make_case(key, seed=s, causal=True, q_offset=0, **a)
         if key == "long_window_q8":  # the cache holds the K / V values as q8_0 blocks
             c.meta["q8"] = {"k": quantize_q8_0(c.f64("k")), "v": quantize_q8_0(c.f64("v"))}
+        if key == "long_window_f16":
+            # the cache holds the K / V draws (the same normals, kept in fp32) rounded to fp16;
+            # the case's own K / V are those fp16 values in the compute dtype
+            full = make_case(key, seed=s, causal=True, q_offset=0, **dict(a, dtype=F32))
+            c.meta["f16"] = {n: full.f64(n).astype(np.float16) for n in ("k", "v")}
+            c.k, c.v = (stored(c.meta["f16"][n].astype(np.float32), c.dtype) for n in ("k", "v"))
         return c
     raise KeyError(key)
 

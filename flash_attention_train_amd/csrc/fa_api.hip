@@ -683,6 +683,30 @@ fa_status fa_train_dequant_q8_0(int32_t B, int32_t H, int32_t S, int32_t D, cons
   return hip_status(fa::launch_dequant_q8_0(a, stream), "q8_0 dequant");
 }
 
+fa_status fa_train_convert_f16(int32_t B, int32_t H, int32_t S, int32_t D, const fa_view* src, const fa_view* out,
+                               int32_t out_dtype, hipStream_t stream) {
+  g_err[0] = 0;
+  if (B < 1 || H < 1 || S < 1) return fail(FA_ERR_SHAPE, "B, H and S must be positive");
+  if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", D);
+  if (out_dtype != FA_F32 && out_dtype != FA_BF16) return fail(FA_ERR_DTYPE, "unknown out dtype %d", out_dtype);
+  Extent es, eo;
+  fa_status s;
+  if ((s = check_view(src, "src", B, H, S, D, 2, true, false, &es))) return s;
+  if ((s = check_view(out, "out", B, H, S, D, out_dtype == FA_F32 ? 4 : 2, true, true, &eo))) return s;
+  if (overlaps(eo, es)) return fail(FA_ERR_ALIAS, "out overlaps src");
+  fa::ConvertArgs a;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.D = D;
+  a.src = static_cast<const _Float16*>(src->data);
+  a.out = out->data;
+  a.to_bf16 = out_dtype == FA_BF16;
+  a.ss = strides_of(src);
+  a.so = strides_of(out);
+  return hip_status(fa::launch_convert_f16(a, stream), "f16 conversion");
+}
+
 size_t fa_train_bwd_workspace_bytes(const fa_attn_params* p) {
   if (check_params(p) != FA_OK) return (size_t)-1;
   return workspace_bytes(p);

@@ -247,7 +247,47 @@ __global__ __launch_bounds__(256) void dequant_q8_0_kernel(const DequantArgs p) 
   *reinterpret_cast<bf16x8*>(o + 8) = hi;
 }
 
+// f16 window rows to the compute type: one thread per 8 consecutive values of a row (one
+// 16-byte load). fp16 -> fp32 is exact (subnormals included); fp16 -> bf16 keeps 8 of the
+// 11 significand bits, rounding to nearest even, and loses no range (bf16 spans fp16's).
+template <bool TO_BF16>
+__global__ __launch_bounds__(256) void convert_f16_kernel(const ConvertArgs p) {
+  const int per_row = p.D / 8;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rows = (int64_t)p.B * p.H * p.S;
+  if (t >= rows * per_row) return;
+  const int64_t row = t / per_row;
+  const int c8 = (int)(t % per_row);
+  const int s = (int)(row % p.S), h = (int)((row / p.S) % p.H), b = (int)(row / ((int64_t)p.S * p.H));
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  const f16x8 x = *reinterpret_cast<const f16x8*>(p.src + b * p.ss.b + h * p.ss.h + (int64_t)s * p.ss.s + 8 * c8);
+  const int64_t o = b * p.so.b + h * p.so.h + (int64_t)s * p.so.s + 8 * c8;
+  if constexpr (TO_BF16) {
+    bf16x8 y;
+    #pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = (bf16)(float)x[e];
+    *reinterpret_cast<bf16x8*>(static_cast<bf16*>(p.out) + o) = y;
+  } else {
+    float4 lo, hi;
+    lo.x = (float)x[0], lo.y = (float)x[1], lo.z = (float)x[2], lo.w = (float)x[3];
+    hi.x = (float)x[4], hi.y = (float)x[5], hi.z = (float)x[6], hi.w = (float)x[7];
+    float* y = static_cast<float*>(p.out) + o;
+    *reinterpret_cast<float4*>(y) = lo;
+    *reinterpret_cast<float4*>(y + 4) = hi;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_convert_f16(const ConvertArgs& p, hipStream_t stream) {
+  const int64_t threads = (int64_t)p.B * p.H * p.S * (p.D / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (p.to_bf16)
+    hipLaunchKernelGGL(convert_f16_kernel<true>, grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(convert_f16_kernel<false>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_dequant_q8_0(const DequantArgs& p, hipStream_t stream) {
   const int64_t threads = (int64_t)p.B * p.H * p.S * (p.D / 16);

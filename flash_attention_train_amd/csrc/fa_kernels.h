@@ -256,6 +256,14 @@ struct DequantArgs {
   Strides sq, sd, so;  // element strides of qs, d and out
 };
 hipError_t launch_dequant_q8_0(const DequantArgs& args, hipStream_t stream);
+struct ConvertArgs {
+  int B, H, S, D;
+  const _Float16* src;
+  void* out;  // fp32 or bf16
+  int to_bf16;
+  Strides ss, so;  // element strides of src and out
+};
+hipError_t launch_convert_f16(const ConvertArgs& args, hipStream_t stream);
 void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, int q_tiles_split, int dq_separate,
                    BwdPlan* plan);
 hipError_t launch_bwd_bf16(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream);

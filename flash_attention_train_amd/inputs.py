@@ -104,8 +104,12 @@ def _normal(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
     return x.astype(np.float32)
 
 
-def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+def stored(x: np.ndarray, dtype: str) -> np.ndarray:
+    """fp32 values as a case stores them: bf16 bit patterns (nearest even) or fp32 itself."""
     return f32_to_bf16_bits(x) if dtype == BF16 else x
+
+
+_store = stored
 
 
 def sa_pad_mask(Sq: int, Sk: int, pad_frac: float = 0.1) -> tuple[np.ndarray, int]:

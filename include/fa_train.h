@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FA_TRAIN_ABI_VERSION 9
+#define FA_TRAIN_ABI_VERSION 10
 
 typedef enum fa_status {
     FA_OK = 0,
@@ -269,6 +269,19 @@ fa_status fa_train_bwd_sinks(const fa_attn_params* p, const fa_view* lse, const 
  * D is 64 or 128. */
 fa_status fa_train_dequant_q8_0(int32_t B, int32_t H, int32_t S, int32_t D, const fa_view* qs, const fa_view* d,
                                 const fa_view* out, hipStream_t stream);
+
+/* f16 K/V window (llama.cpp pull request 57 trains an f16 cache in place; its backward casts
+ * each tile of the cache to F32): the rows of a window stored as IEEE fp16 written out in the
+ * compute type of the entry points that read them. out_dtype FA_F32 is exact (every fp16
+ * value, subnormals included, is an fp32 value); FA_BF16 rounds to nearest even (bf16 keeps
+ * 8 of fp16's 11 significand bits and spans its whole range). The exact walk calls it once
+ * per chunk for the window rows the chunk adds, as for q8_0; dK/dV accumulate in fp32.
+ *   src: fp16 [B, H, S, D] view, rows 16-byte aligned
+ *   out: [B, H, S, D] view of out_dtype, rows 16-byte aligned; must not overlap src
+ * D is 64 or 128. Errors: FA_ERR_SHAPE, FA_ERR_UNSUPPORTED (D), FA_ERR_DTYPE, the view
+ * errors (FA_ERR_NULL, FA_ERR_STRIDE, FA_ERR_ALIGN), FA_ERR_ALIAS, FA_ERR_HIP. */
+fa_status fa_train_convert_f16(int32_t B, int32_t H, int32_t S, int32_t D, const fa_view* src, const fa_view* out,
+                               int32_t out_dtype, hipStream_t stream);
 
 /* FA_TRAIN_ABI_VERSION of the loaded library. */
 int fa_train_version(void);

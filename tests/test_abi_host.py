@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(L, n), n
         assert n in B.SIGNATURES, f"{n} has no ctypes signature in the binding"
-    assert L.fa_train_version() == 9
+    assert L.fa_train_version() == 10
 
 
 BASE = 0x7F0000000000  # fake, 256-byte aligned device addresses
@@ -203,3 +203,21 @@ def test_probe_rejects_bad_arguments():
     assert L.fa_train_probe_mfma(0, 0, BASE, BASE, BASE, None) == 2
     assert L.fa_train_probe_mfma(0, 1, None, BASE, BASE, None) == 1
     assert L.fa_train_probe_ds_read_tr16(0, BASE, BASE, None) == 2
+
+
+def test_window_conversions_reject():
+    L = B.lib()
+    # f16 -> fp32 / bf16
+    assert L.fa_train_convert_f16(1, 4, 64, 64, view(0), view(0), B.FA_F32, None) == 6  # out overlaps src
+    assert L.fa_train_convert_f16(1, 4, 64, 64, view(0), view(2, elt=4), 2, None) == 3
+    assert L.fa_train_convert_f16(1, 4, 64, 96, view(0, D=96), view(2, D=96), B.FA_BF16, None) == 7
+    assert L.fa_train_convert_f16(0, 4, 64, 64, view(0), view(2), B.FA_BF16, None) == 2
+    assert L.fa_train_convert_f16(1, 4, 64, 64, None, view(2), B.FA_BF16, None) == 1
+    assert L.fa_train_convert_f16(1, 4, 64, 64, view(0, stride_s=68), view(2), B.FA_BF16, None) == 5
+    assert L.fa_train_convert_f16(1, 4, 64, 64, view(0), view(2, stride_s=32), B.FA_BF16, None) == 4
+    # q8_0 -> bf16: quants [1, 4, 64, 64] int8, scales [1, 4, 64, 2] fp16
+    qs = B.FaView(BASE, 4 * 64 * 64, 64 * 64, 64)
+    d = B.FaView(BASE + (1 << 24), 4 * 64 * 2, 64 * 2, 2)
+    assert L.fa_train_dequant_q8_0(1, 4, 64, 64, qs, B.FaView(BASE + (1 << 24), 4 * 64, 64, 1), view(2), None) == 4
+    assert L.fa_train_dequant_q8_0(1, 4, 64, 64, qs, d, view(0), None) == 6  # out overlaps qs
+    assert L.fa_train_dequant_q8_0(1, 4, 64, 48, qs, d, view(2), None) == 7
