@@ -39,7 +39,7 @@ class _Problem(ctypes.Structure):
                 ("Sq", ctypes.c_int32), ("Sk", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("mask_b", ctypes.c_int32),
                 ("q_offset", ctypes.c_int64), ("scale", ctypes.c_double), ("sinks", ctypes.c_void_p),
-                ("alibi", ctypes.c_void_p), ("mask_h", ctypes.c_int32)]
+                ("alibi", ctypes.c_void_p), ("mask_h", ctypes.c_int32), ("softcap", ctypes.c_double)]
 
 
 _lib = None
@@ -76,7 +76,7 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
-def _problem(q, k, mask, scale, causal, q_offset, sinks=None, alibi=None):
+def _problem(q, k, mask, scale, causal, q_offset, sinks=None, alibi=None, softcap=None):
     B, Hq, Sq, D = q.shape
     _, Hkv, Sk, _ = k.shape
     if q_offset is None:
@@ -95,15 +95,16 @@ def _problem(q, k, mask, scale, causal, q_offset, sinks=None, alibi=None):
     if alibi is not None and alibi.shape != (Hq,):
         raise ValueError("alibi must be [Hq]")
     return _Problem(B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), mb, int(q_offset), float(scale),
-                    None if sinks is None else sinks.ctypes.data, None if alibi is None else alibi.ctypes.data, mh)
+                    None if sinks is None else sinks.ctypes.data, None if alibi is None else alibi.ctypes.data, mh,
+                    float(softcap or 0.0))
 
 
 def forward(q, k, v, mask=None, *, scale: float, causal: bool = False, q_offset: Optional[int] = None,
-            threads: Optional[int] = None, sinks=None, alibi=None):
+            threads: Optional[int] = None, sinks=None, alibi=None, softcap: Optional[float] = None):
     """Returns (O [B,Hq,Sq,D], LSE [B,Hq,Sq]) in float64. ``sinks``: optional [Hq] sink logits;
-    ``alibi``: optional [Hq] ALiBi slopes."""
+    ``alibi``: optional [Hq] ALiBi slopes; ``softcap``: optional logit softcap c > 0."""
     q, k, v, mask, sinks, alibi = _f64(q), _f64(k), _f64(v), _f64(mask), _f64(sinks), _f64(alibi)
-    p = _problem(q, k, mask, scale, causal, q_offset, sinks, alibi)
+    p = _problem(q, k, mask, scale, causal, q_offset, sinks, alibi, softcap)
     O = np.zeros(q.shape, np.float64)
     L = np.zeros(q.shape[:3], np.float64)
     rc = _load().ora_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(O), _ptr(L),
@@ -114,11 +115,12 @@ def forward(q, k, v, mask=None, *, scale: float, causal: bool = False, q_offset:
 
 
 def backward(q, k, v, do, mask=None, *, scale: float, causal: bool = False, q_offset: Optional[int] = None,
-             threads: Optional[int] = None, sinks=None, alibi=None) -> dict:
+             threads: Optional[int] = None, sinks=None, alibi=None, softcap: Optional[float] = None) -> dict:
     """The full forward and backward. Returns a dict with O, LSE, Delta, dQ, dK, dV (float64), and
-    dSink [Hq] when ``sinks`` ([Hq] sink logits) is given. ``alibi``: optional [Hq] ALiBi slopes."""
+    dSink [Hq] when ``sinks`` ([Hq] sink logits) is given. ``alibi``: optional [Hq] ALiBi slopes;
+    ``softcap``: optional logit softcap c > 0."""
     q, k, v, do, mask, sinks, alibi = _f64(q), _f64(k), _f64(v), _f64(do), _f64(mask), _f64(sinks), _f64(alibi)
-    p = _problem(q, k, mask, scale, causal, q_offset, sinks, alibi)
+    p = _problem(q, k, mask, scale, causal, q_offset, sinks, alibi, softcap)
     out = {"O": np.zeros(q.shape), "LSE": np.zeros(q.shape[:3]), "Delta": np.zeros(q.shape[:3]),
            "dQ": np.zeros(q.shape), "dK": np.zeros(k.shape), "dV": np.zeros(k.shape)}
     rc = _load().ora_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(do),
@@ -146,10 +148,11 @@ def sink_grad(sinks, lse, delta) -> np.ndarray:
 
 
 def rows(q, k, v, do, row_ids, mask=None, *, scale: float, causal: bool = False,
-         q_offset: Optional[int] = None, threads: Optional[int] = None, sinks=None, alibi=None) -> dict:
+         q_offset: Optional[int] = None, threads: Optional[int] = None, sinks=None, alibi=None,
+         softcap: Optional[float] = None) -> dict:
     """Selected rows, ids (b*Hq + h)*Sq + i. Returns O [n,D], LSE [n], Delta [n], dQ [n,D]."""
     q, k, v, do, mask, sinks, alibi = _f64(q), _f64(k), _f64(v), _f64(do), _f64(mask), _f64(sinks), _f64(alibi)
-    p = _problem(q, k, mask, scale, causal, q_offset, sinks, alibi)
+    p = _problem(q, k, mask, scale, causal, q_offset, sinks, alibi, softcap)
     ids = np.ascontiguousarray(row_ids, dtype=np.int64)
     n, D = ids.size, q.shape[3]
     out = {"O": np.zeros((n, D)), "LSE": np.zeros(n), "Delta": np.zeros(n), "dQ": np.zeros((n, D))}
@@ -162,10 +165,11 @@ def rows(q, k, v, do, row_ids, mask=None, *, scale: float, causal: bool = False,
 
 
 def cols(q, k, v, do, col_ids, mask=None, *, scale: float, causal: bool = False,
-         q_offset: Optional[int] = None, threads: Optional[int] = None, sinks=None, alibi=None) -> dict:
+         q_offset: Optional[int] = None, threads: Optional[int] = None, sinks=None, alibi=None,
+         softcap: Optional[float] = None) -> dict:
     """Selected key columns, ids (b*Hkv + g)*Sk + j. Returns dK [n,D], dV [n,D]."""
     q, k, v, do, mask, sinks, alibi = _f64(q), _f64(k), _f64(v), _f64(do), _f64(mask), _f64(sinks), _f64(alibi)
-    p = _problem(q, k, mask, scale, causal, q_offset, sinks, alibi)
+    p = _problem(q, k, mask, scale, causal, q_offset, sinks, alibi, softcap)
     ids = np.ascontiguousarray(col_ids, dtype=np.int64)
     n, D = ids.size, q.shape[3]
     out = {"dK": np.zeros((n, D)), "dV": np.zeros((n, D))}

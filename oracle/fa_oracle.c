@@ -8,7 +8,10 @@
  * What it computes (plain definition, float64 throughout, every score row
  * materialised, no tiling, no online softmax):
  *
- *   S_ij   = scale * <q_i, k_g(h),j> + M_ij    or -inf where masked / causal
+ *   S_ij   = cap(scale * <q_i, k_g(h),j>) + M_ij    or -inf where masked / causal
+ *   cap(x) = x, or c tanh(x / c) with a logit softcap c > 0 (a score modifier of
+ *            llama.cpp pull request 57's list; the cap bounds the product, and the
+ *            mask and ALiBi terms are added after it)
  *   m_i    = max(max_j S_ij, sink_h)            (sink_h = -inf without sinks)
  *   row fully masked (m_i = -inf):  O_i = 0, LSE_i = 0, P_i. = 0
  *   otherwise: LSE_i = m_i + ln (sum_j exp(S_ij - m_i) + exp(sink_h - m_i)),
@@ -21,7 +24,8 @@
  *   whose flash backward was missing; its own gradient is formed from LSE and
  *   Delta by the Python wrapper)
  *   Delta_i = <dO_i, O_i>
- *   dP_ij   = <dO_i, v_j>,   dS_ij = P_ij (dP_ij - Delta_i)
+ *   dP_ij   = <dO_i, v_j>,   dS_ij = P_ij (dP_ij - Delta_i) cap'(scale <q_i, k_j>)
+ *             (cap' = 1, or 1 - tanh^2 under a softcap)
  *   dQ_i    = scale * sum_j dS_ij k_j
  *   dK_j    = scale * sum_{h in group} sum_i dS_ij q_i
  *   dV_j    =         sum_{h in group} sum_i P_ij dO_i
@@ -61,6 +65,7 @@ typedef struct {
     const double *sinks; /* [Hq] logits, NULL = none */
     const double *alibi; /* [Hq] slopes, NULL = none */
     int32_t mask_h;      /* heads of the mask: 0 or 1 = one mask for every head, Hq = one per head */
+    double softcap;      /* logit softcap c, 0 = none */
 } ora_problem;
 
 typedef struct {
@@ -115,16 +120,25 @@ static int visible(const ora_inputs *in, int b, int h, int i, int j) {
     return 1;
 }
 
-/* S_ij for query head h (step 1 of the definition). */
-static double score(const ora_inputs *in, int b, int h, int i, int j) {
+/* S_ij for query head h (step 1 of the definition). If dcap is not NULL it receives
+ * cap' at the scaled product, the factor dS_ij carries back to the product. */
+static double score_d(const ora_inputs *in, int b, int h, int i, int j, double *dcap) {
     const ora_problem *p = in->p;
+    if (dcap) *dcap = 1.0;
     if (!visible(in, b, h, i, j)) return -INFINITY;
     double mv = 0.0;
     if (p->mask_b) mv = mask_at(in, b, h, i, j);
     if (p->alibi) mv -= p->alibi[h] * fabs((double)j - (double)(p->q_offset + i));
     int g = kv_head(p, h);
-    return p->scale * dot(q_row(in, b, h, i), k_row(in, b, g, j), p->D) + mv;
+    double x = p->scale * dot(q_row(in, b, h, i), k_row(in, b, g, j), p->D);
+    if (p->softcap > 0.0) {
+        const double t = tanh(x / p->softcap);
+        x = p->softcap * t;
+        if (dcap) *dcap = 1.0 - t * t;
+    }
+    return x + mv;
 }
+static double score(const ora_inputs *in, int b, int h, int i, int j) { return score_d(in, b, h, i, j, NULL); }
 
 /* Steps 1-4 for one query row: materialise the row of scores, then LSE, O and
  * Delta (Delta only if dO is given). srow is caller scratch of Sk doubles. */
@@ -164,11 +178,12 @@ static void row_dq(const ora_inputs *in, int b, int h, int i, double lse, double
     for (int d = 0; d < D; ++d) dq_out[d] = 0.0;
     const double *doi = do_row(in, b, h, i);
     for (int j = 0; j < Sk; ++j) {
-        const double s = score(in, b, h, i, j);
+        double dcap;
+        const double s = score_d(in, b, h, i, j, &dcap);
         if (s == -INFINITY) continue;
         const double pij = exp(s - lse);
         const double dpij = dot(doi, v_row(in, b, g, j), D);
-        const double dsij = pij * (dpij - delta);
+        const double dsij = pij * (dpij - delta) * dcap;
         const double *kj = k_row(in, b, g, j);
         for (int d = 0; d < D; ++d) dq_out[d] += p->scale * dsij * kj[d];
     }
@@ -184,12 +199,13 @@ static void col_dkdv(const ora_inputs *in, int b, int g, int j, const double *LS
     const double *vj = v_row(in, b, g, j);
     for (int h = g * G; h < (g + 1) * G; ++h) {
         for (int i = 0; i < p->Sq; ++i) {
-            const double s = score(in, b, h, i, j);
+            double dcap;
+            const double s = score_d(in, b, h, i, j, &dcap);
             if (s == -INFINITY) continue;
             const int64_t r = ((int64_t)b * p->Hq + h) * p->Sq + i;
             const double pij = exp(s - LSE[r]);
             const double *doi = do_row(in, b, h, i);
-            const double dsij = pij * (dot(doi, vj, D) - Delta[r]);
+            const double dsij = pij * (dot(doi, vj, D) - Delta[r]) * dcap;
             const double *qi = q_row(in, b, h, i);
             for (int d = 0; d < D; ++d) {
                 dk_out[d] += p->scale * dsij * qi[d];
@@ -254,6 +270,7 @@ static int check_problem(const ora_problem *p) {
     if (p->Hq % p->Hkv) return 2;
     if (p->mask_b != 0 && p->mask_b != 1 && p->mask_b != p->B) return 3;
     if (p->mask_h < 0 || (p->mask_h > 1 && p->mask_h != p->Hq)) return 4;
+    if (!(p->softcap >= 0.0) || isinf(p->softcap)) return 5;
     return 0;
 }
 

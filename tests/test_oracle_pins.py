@@ -677,3 +677,107 @@ def test_head_bias_finite_differences():
             tm[idx] -= h
             fd[idx] = (loss({"q": q, "k": k, "v": v, name_t: tp}) - loss({"q": q, "k": k, "v": v, name_t: tm})) / (2 * h)
         assert np.abs(fd - grad).max() / np.abs(grad).max() < 1e-7, name_t
+
+
+# ---------------------------------------------------------------------------
+# logit softcap, S = c tanh(scale <q, k> / c) + mask: pinned to torch autograd on the
+# materialised scores, to finite differences, and to its two limits (no cap as c grows;
+# as c -> 0 the products vanish and the softmax runs over the mask alone, which also
+# pins that the mask is added after the cap)
+# ---------------------------------------------------------------------------
+def _softcap_problem(seed, causal, mask):
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, Sq, Sk, D = 2, 4, 2, 6, 7, 5
+    q, k, v, do = (rng.standard_normal(s) for s in ((B, Hq, Sq, D), (B, Hkv, Sk, D), (B, Hkv, Sk, D), (B, Hq, Sq, D)))
+    q *= 2.0  # products of a few units: well inside tanh's bend for c = 1.5
+    m = None
+    if mask:
+        m = rng.standard_normal((B, Sq, Sk))  # finite biases, plus hidden entries
+        m[1, :, Sk - 2:] = -np.inf
+        m[0, 3, :] = -np.inf
+    return q, k, v, do, m, causal, (Sk - Sq if causal else 0)
+
+
+@pytest.mark.parametrize("causal,mask", [(False, False), (True, True)])
+def test_softcap_torch_autograd_crosscheck(causal, mask):
+    torch = pytest.importorskip("torch")
+    q, k, v, do, m, causal, off = _softcap_problem(61, causal, mask)
+    sc, cap = 0.6, 1.5
+    r = oracle.backward(q, k, v, do, m, scale=sc, causal=causal, q_offset=off, softcap=cap)
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    bias = np.zeros((B, Hq, Sq, Sk))
+    if m is not None:
+        bias = bias + m[:, None]
+    if causal:
+        pos = off + np.arange(Sq)
+        bias = np.where(np.arange(Sk)[None, None, None, :] > pos[None, None, :, None], -np.inf, bias)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    x = sc * torch.matmul(tq, tk.repeat_interleave(G, dim=1).transpose(-1, -2).contiguous())
+    s = cap * torch.tanh(x / cap) + torch.tensor(bias)
+    full = np.isinf(bias).all(axis=3)
+    s = torch.where(torch.tensor(full)[..., None], torch.zeros_like(s), s)  # (kept finite, then dropped)
+    p = torch.softmax(s, dim=-1)
+    p = torch.where(torch.tensor(full)[..., None], torch.zeros_like(p), p)
+    o = torch.matmul(p, tv.repeat_interleave(G, dim=1))
+    lse = torch.logsumexp(s, dim=-1)
+    (o * torch.tensor(do)).sum().backward()
+    assert np.abs(x.detach().numpy()).max() > 2 * cap  # the cap is active
+    np.testing.assert_allclose(r["O"], o.detach().numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["LSE"][~full], lse.detach().numpy()[~full], rtol=1e-10, atol=1e-12)
+    for n, t in (("dQ", tq), ("dK", tk), ("dV", tv)):
+        np.testing.assert_allclose(r[n], t.grad.numpy(), rtol=1e-9, atol=1e-11, err_msg=n)
+
+
+def test_softcap_finite_differences():
+    q, k, v, do, m, causal, off = _softcap_problem(62, True, True)
+    sc, cap = 0.6, 1.5
+    r = oracle.backward(q, k, v, do, m, scale=sc, causal=causal, q_offset=off, softcap=cap)
+
+    def loss(a):
+        O, _ = oracle.forward(a["q"], a["k"], a["v"], m, scale=sc, causal=causal, q_offset=off, softcap=cap,
+                              threads=1)
+        return float(np.sum(O * do))
+
+    h = 1e-6
+    for name_t, t, grad in (("q", q, r["dQ"]), ("k", k, r["dK"]), ("v", v, r["dV"])):
+        fd = np.zeros_like(t)
+        for idx in np.ndindex(t.shape):
+            tp, tm = t.copy(), t.copy()
+            tp[idx] += h
+            tm[idx] -= h
+            fd[idx] = (loss({"q": q, "k": k, "v": v, name_t: tp}) - loss({"q": q, "k": k, "v": v, name_t: tm})) / (2 * h)
+        assert np.abs(fd - grad).max() / np.abs(grad).max() < 1e-7, name_t
+
+
+def test_softcap_limits():
+    q, k, v, do, m, causal, off = _softcap_problem(63, True, True)
+    sc = 0.6
+    plain = oracle.backward(q, k, v, do, m, scale=sc, causal=causal, q_offset=off)
+    wide = oracle.backward(q, k, v, do, m, scale=sc, causal=causal, q_offset=off, softcap=1e7)
+    for n in ("O", "LSE", "Delta", "dQ", "dK", "dV"):
+        np.testing.assert_allclose(wide[n], plain[n], rtol=1e-10, atol=1e-12, err_msg=n)
+    # c -> 0: S_ij -> M_ij, P = softmax of the visible mask values, and the product's gradient
+    # carries a factor c, so dQ and dK vanish with it
+    c = 1e-9
+    r = oracle.backward(q, k, v, do, m, scale=sc, causal=causal, q_offset=off, softcap=c)
+    B, Hq, Sq, _ = q.shape
+    Sk = k.shape[2]
+    G = Hq // k.shape[1]
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(Sq):
+                mv = m[b, i].copy()
+                mv[np.arange(Sk) > off + i] = -np.inf
+                if np.isinf(mv).all():
+                    assert r["LSE"][b, h, i] == 0 and np.all(r["O"][b, h, i] == 0)
+                    continue
+                mx = mv[np.isfinite(mv)].max()
+                w = np.where(np.isfinite(mv), np.exp(mv - mx), 0.0)
+                np.testing.assert_allclose(r["LSE"][b, h, i], mx + np.log(w.sum()), rtol=0, atol=1e-8)
+                np.testing.assert_allclose(r["O"][b, h, i], (w / w.sum()) @ v[b, h // G], rtol=0, atol=1e-8)
+    assert np.abs(r["dQ"]).max() < 1e-7 and np.abs(r["dK"]).max() < 1e-7
+    assert np.abs(r["dV"]).max() > 0.1
+    with pytest.raises(ValueError):
+        oracle.forward(q, k, v, scale=sc, softcap=-1.0)
