@@ -10,7 +10,7 @@ S=1542, D=128, bf16, pad mask): mask-adjusted fwd+bwd TFLOP/s (14 * D * N FLOPs
 per step, N = unmasked score pairs). Other workloads are reported under "extra".
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload dit_sa]
-                    [--extra lm_causal,dit_ca,long_window,dit_sa_len,dit_sa_band,lm_sinks,lm_alibi,long_window_q8,long_window_f16]
+                    [--extra lm_causal,dit_ca,long_window,dit_sa_len,dit_sa_band,lm_sinks,lm_alibi,lm_softcap,long_window_q8,long_window_f16]
                     [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -27,6 +27,11 @@ import numpy as np
 METRIC = "attention fwd+bwd TFLOP/s (mask-adjusted) and % of MI355X bf16 MFMA peak"
 
 
+# the other workloads timed by default, beside the headline one
+DEFAULT_EXTRA = ("lm_causal", "dit_ca", "long_window", "dit_sa_len", "dit_sa_band", "lm_sinks", "lm_alibi",
+                 "lm_softcap", "long_window_q8", "long_window_f16")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -37,7 +42,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dit_sa")
-    ap.add_argument("--extra", default="lm_causal,dit_ca,long_window,dit_sa_len,dit_sa_band,lm_sinks,lm_alibi,long_window_q8,long_window_f16",
+    ap.add_argument("--extra", default=",".join(DEFAULT_EXTRA),
                     help="other workloads to time, comma separated ('none' for none); long_window is the "
                          "64-chunk walk over a 32768-long window")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -84,6 +89,8 @@ class Workload:
         self.dsink = None if self.sinks is None else torch.zeros_like(self.sinks)
         # ALiBi slopes (per head), given to the forward and the backward
         self.alibi = None if c.meta.get("alibi") is None else torch.from_numpy(c.meta["alibi"]).to(dev)
+        # a logit softcap, given to the forward and the backward (0 = none)
+        self.softcap = float(c.meta.get("softcap", 0.0))
         self.o = torch.empty_like(self.q)
         self.lse = torch.empty(c.B, c.Hq, c.Sq, dtype=torch.float32, device=dev)
         self.delta = torch.empty_like(self.lse)
@@ -96,7 +103,8 @@ class Workload:
             self.tiles = binding.mask_tile_map(self.mask, self.q, self.k)  # sized once, refilled every step
         # forward workspace: the split-key walk's partial rows when the grid is short
         self.fws_bytes = binding.fwd_workspace_bytes(self.q, self.k, scale=c.scale, causal=c.causal,
-                                                     q_offset=c.q_offset, mask=self.mask, **self.sk)
+                                                     q_offset=c.q_offset, mask=self.mask, softcap=self.softcap,
+                                                     **self.sk)
         self.fws = torch.empty(max(self.fws_bytes, 256), dtype=torch.uint8, device=dev)
         self.fwd_split = self.fws_bytes // (4 * c.B * c.Hq * c.Sq * (c.D + 2)) if self.fws_bytes else 1
         # backward split: the library's cost model, or (tune) the fastest of a few
@@ -120,7 +128,7 @@ class Workload:
                 causal=c.causal, q_offset=c.q_offset, mask_tiles=self.tiles, **self.sk)
         nws = binding.bwd_workspace_bytes(self.q, self.k, scale=c.scale, causal=c.causal, q_offset=c.q_offset,
                                           mask=self.mask, kv_split=self.kv_split, q_split=self.q_split,
-                                          q_split_tiles=self.q_split_tiles, **self.sk)
+                                          q_split_tiles=self.q_split_tiles, softcap=self.softcap, **self.sk)
         self.ws_bytes = nws
         self.ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
 
@@ -134,7 +142,7 @@ class Workload:
         c = self.case
         self.B.fwd(self.q, self.k, self.v, mask=self.mask, scale=c.scale, causal=c.causal, q_offset=c.q_offset,
                    out=self.o, lse=self.lse, mask_tiles=self.tiles, workspace=self.fws, sinks=self.sinks,
-                   alibi=self.alibi, **self.sk)
+                   alibi=self.alibi, softcap=self.softcap, **self.sk)
 
     def pre(self):
         self.B.bwd_preprocess(self.o, self.do, delta=self.delta)
@@ -144,7 +152,7 @@ class Workload:
         self.B.bwd(self.q, self.k, self.v, self.do, self.lse, self.delta, mask=self.mask, scale=c.scale,
                    causal=c.causal, q_offset=c.q_offset, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws,
                    kv_split=self.kv_split, q_split=self.q_split, q_split_tiles=self.q_split_tiles,
-                   mask_tiles=self.tiles, alibi=self.alibi, **self.sk)
+                   mask_tiles=self.tiles, alibi=self.alibi, softcap=self.softcap, **self.sk)
         if self.sinks is not None:  # the sinks' gradient, added into their accumulator
             self.B.bwd_sinks(self.lse, self.delta, self.sinks, dsink=self.dsink)
 

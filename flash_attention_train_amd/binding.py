@@ -36,7 +36,7 @@ class FaAttnParams(ctypes.Structure):
                 ("fwd_split", ctypes.c_int32), ("key_len", ctypes.c_void_p), ("q_len", ctypes.c_void_p),
                 ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
                 ("bwd_dq_launch", ctypes.c_int32), ("sinks", ctypes.c_void_p), ("alibi", ctypes.c_void_p),
-                ("q_split_tiles", ctypes.c_int32), ("mask_stride_h", ctypes.c_int64)]
+                ("q_split_tiles", ctypes.c_int32), ("mask_stride_h", ctypes.c_int64), ("softcap", ctypes.c_float)]
 
 
 class FaError(RuntimeError):
@@ -130,7 +130,7 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
                 key_len: Optional[torch.Tensor] = None, q_len: Optional[torch.Tensor] = None,
                 window: tuple = (-1, -1), dq_launch: int = 0,
                 sinks: Optional[torch.Tensor] = None, alibi: Optional[torch.Tensor] = None,
-                q_split_tiles: int = 0) -> FaAttnParams:
+                q_split_tiles: int = 0, softcap: float = 0.0) -> FaAttnParams:
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Sk, Dk = k.shape
     if Bk != B or Dk != D:
@@ -148,6 +148,7 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
                 raise ValueError(f"{name} must be a contiguous int32 [B] tensor on the device")
             setattr(p, name, t.data_ptr())
     p.q_split_tiles = int(q_split_tiles)
+    p.softcap = float(softcap)
     for name, t in (("sinks", sinks), ("alibi", alibi)):
         if t is not None:
             if t.dtype != torch.float32 or t.shape != (Hq,) or not t.is_contiguous():
@@ -199,22 +200,23 @@ def mask_tile_count(mask: torch.Tensor) -> int:
 
 
 def fwd_workspace_bytes(q, k, *, scale=None, causal=False, q_offset=None, mask=None, split=0, key_len=None,
-                        q_len=None, window=(-1, -1)) -> int:
+                        q_len=None, window=(-1, -1), softcap=0.0) -> int:
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, fwd_split=split,
-                    key_len=key_len, q_len=q_len, window=window)
+                    key_len=key_len, q_len=q_len, window=window, softcap=softcap)
     return int(lib().fa_train_fwd_workspace_bytes(ctypes.byref(p)))
 
 
 def fwd(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, out=None, lse=None, stream=None,
         variant=0, mask_tiles=None, workspace=None, split=0, key_len=None, q_len=None, window=(-1, -1),
-        sinks=None, alibi=None):
+        sinks=None, alibi=None, softcap=0.0):
     """Forward: returns (O, LSE). O has q's dtype and shape; LSE is fp32 [B, Hq, Sq].
     Runs fa_train_fwd_ws: a short grid may split the key walks (split = 0: the library's
     choice; 1: never), with `workspace` (allocated here when None and needed). ``sinks``:
-    optional fp32 [Hq] attention-sink logits."""
+    optional fp32 [Hq] attention-sink logits; ``alibi``: fp32 [Hq] slopes; ``softcap``: a
+    logit softcap c > 0 (0 = none)."""
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, fwd_variant=variant,
                     mask_tiles=mask_tiles, fwd_split=split, key_len=key_len, q_len=q_len, window=window,
-                    sinks=sinks, alibi=alibi)
+                    sinks=sinks, alibi=alibi, softcap=softcap)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
@@ -291,9 +293,10 @@ def convert_f16(src, *, out=None, dtype=None, stream=None):
 
 
 def bwd_workspace_bytes(q, k, *, scale=None, causal=False, q_offset=None, mask=None, kv_split=0, q_split=0,
-                        key_len=None, q_len=None, window=(-1, -1), q_split_tiles=0) -> int:
+                        key_len=None, q_len=None, window=(-1, -1), q_split_tiles=0, softcap=0.0) -> int:
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
-                    q_split=q_split, key_len=key_len, q_len=q_len, window=window, q_split_tiles=q_split_tiles)
+                    q_split=q_split, key_len=key_len, q_len=q_len, window=window, q_split_tiles=q_split_tiles,
+                    softcap=softcap)
     return int(lib().fa_train_bwd_workspace_bytes(ctypes.byref(p)))
 
 
@@ -308,11 +311,11 @@ def _workspace(p: FaAttnParams, device, workspace):
 
 def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_offset=None, dq=None, dk=None,
         dv=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None, q_len=None,
-        window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0):
+        window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0):
     """Backward: returns (dQ, dK, dV), each in q's dtype, overwritten."""
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, window=window,
-                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles)
+                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles, softcap=softcap)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
@@ -363,12 +366,13 @@ def tune_bwd_splits(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=
 
 def bwd_chunked(q, k, v, dout, lse, delta, dk_acc, dv_acc, *, mask=None, scale=None, causal=True, q_offset=None,
                 dq=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None,
-                q_len=None, window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0):
+                q_len=None, window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0):
     """Chunked backward: returns dQ for the chunk; ADDS dK/dV into the fp32 window
     accumulators ``dk_acc`` / ``dv_acc`` ([B, Hkv, >= Sk, D])."""
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len,
-                    q_len=q_len, window=window, dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles)
+                    q_len=q_len, window=window, dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles,
+                    softcap=softcap)
     if dk_acc.dtype != torch.float32 or dv_acc.dtype != torch.float32:
         raise TypeError("the window accumulators must be float32")
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq

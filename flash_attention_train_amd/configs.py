@@ -54,6 +54,10 @@ WORKLOADS = {
     "long_window_q8": Workload("long_window_q8", "long-window chunked walk over a q8_0 K/V window, W=32768, "
                                "64 chunks of 512, Hq=16 Hkv=4 D=128", 9),
     # the same walk over an fp16-stored window: the K/V draws rounded once to fp16
+    # the LM layer with a logit softcap of 50 (the pages give no value; the cost does not depend
+    # on it): it runs on the generic kernels
+    "lm_softcap": Workload("lm_softcap", "LM causal GQA with logit softcap 50, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16",
+                           12),
     "long_window_f16": Workload("long_window_f16", "long-window chunked walk over an f16 K/V window, W=32768, "
                                 "64 chunks of 512, Hq=16 Hkv=4 D=128", 11),
 }
@@ -90,7 +94,7 @@ def make(key: str, **shrink) -> Case:
             lo_hi["lo"] = max(1, shrink["Sk"] // 4)
         a.update(shrink)
         return make_case(key, seed=s, mask="ca_keypad", mask_args=lo_hi, **a)
-    if key in ("lm_causal", "lm_sinks", "lm_alibi"):
+    if key in ("lm_causal", "lm_sinks", "lm_alibi", "lm_softcap"):
         a = dict(B=1, Hq=32, Hkv=8, Sq=4096, Sk=4096, D=128, dtype=BF16, do_std=0.1)
         a.update(shrink)
         c = make_case(key, seed=s, causal=True, q_offset=0, **a)
@@ -98,6 +102,8 @@ def make(key: str, **shrink) -> Case:
             c.meta["sinks"] = sink_logits(s, c.Hq)
         if key == "lm_alibi":
             c.meta["alibi"] = alibi_slopes(c.Hq)
+        if key == "lm_softcap":
+            c.meta["softcap"] = 50.0
         return c
     if key in ("dit_sa_len", "dit_sa_band"):
         a = dict(B=1 if key == "dit_sa_len" else 2, Hq=16, Hkv=8, Sq=1542, Sk=1542, D=128, dtype=BF16)

@@ -101,6 +101,10 @@ fa_status check_params(const fa_attn_params* p) {
   const bool structured = p->key_len || p->q_len || p->window_left >= 0 || p->window_right >= 0;
   if (structured && p->dtype != FA_BF16)
     return fail(FA_ERR_UNSUPPORTED, "structured masks (key_len, q_len, window) are implemented for bf16 only");
+  if (!(p->softcap >= 0.f) || isinf(p->softcap)) return fail(FA_ERR_SHAPE, "softcap must be >= 0 and finite");
+  if (p->softcap > 0.f && (p->sinks || p->alibi || structured))
+    return fail(FA_ERR_UNSUPPORTED, "the logit softcap combines with causal and dense masks only "
+                                    "(not with sinks, ALiBi or structured masks)");
   if (p->mask) {
     if (p->mask_stride_q < p->Sk) return fail(FA_ERR_STRIDE, "mask_stride_q (%lld) < Sk", (long long)p->mask_stride_q);
     if (p->mask_stride_b < 0) return fail(FA_ERR_STRIDE, "mask_stride_b is negative");
@@ -151,8 +155,13 @@ fa::AttnShape shape_of(const fa_attn_params* p) {
   a.wl = p->window_left;
   a.wr = p->window_right;
   a.alibi = p->alibi;
+  a.softcap = p->softcap;
   return a;
 }
+
+// The generic kernels (fa_fwd.hip, fa_bwd.hip) run fp32 problems and every problem with a
+// logit softcap; the bf16 MFMA kernels run the rest.
+bool generic_path(const fa_attn_params* p) { return p->dtype != FA_BF16 || p->softcap > 0.f; }
 
 fa::Strides strides_of(const fa_view* v) { return {v->stride_b, v->stride_h, v->stride_s}; }
 
@@ -322,7 +331,7 @@ WsLayout workspace_layout(const fa_attn_params* p, bool accumulate) {
   const size_t nq = (size_t)p->B * p->Hq * p->Sq * p->D * sizeof(float);
   const size_t nk = (size_t)p->B * p->Hkv * p->Sk * p->D * sizeof(float);
   size_t dq_bytes = nq, dk_bytes = 0;
-  if (p->dtype == FA_BF16) {
+  if (!generic_path(p)) {
     int kv, q, qt;
     choose_splits(p, accumulate, &kv, &q, &qt);
     w.need_dq = q > 1 && qt > 0;
@@ -408,7 +417,7 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
                  p->mask_stride_h % 4 == 0;
   const int is_bf16 = p->dtype == FA_BF16;
   fa_status st;
-  if (is_bf16) {
+  if (!generic_path(p)) {
     char* ws = static_cast<char*>(workspace);
     fa::BwdPlan plan;
     int kv, q, qt;
@@ -473,7 +482,7 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
 // (measured: 16 heads x 1542 rows gains 10% at 2 splits and loses at 3; a 512-row
 // chunk over a 32768-key window runs 4x faster at 8).
 int choose_fwd_split(const fa_attn_params* p) {
-  if (p->dtype != FA_BF16) return 1;
+  if (generic_path(p)) return 1;
   const int64_t wgs = (int64_t)p->B * p->Hq * ((p->Sq + 127) / 128);
   int64_t nkt = (p->Sk + 63) / 64;
   if (p->causal) {  // the longest walk: the last query tile's
@@ -551,7 +560,7 @@ fa_status fwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   a.splits = splits;
   a.part_o = nullptr;
   a.part_ml = nullptr;
-  if (p->dtype == FA_BF16) {
+  if (!generic_path(p)) {
     if (splits > 1) {  // the split walk runs the default configuration
       a.part_o = workspace;
       a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
@@ -564,7 +573,7 @@ fa_status fwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
     const int variant = p->fwd_variant ? p->fwd_variant : 1;
     return hip_status(fa::launch_fwd_bf16(a, variant, stream), "forward");
   }
-  return hip_status(fa::launch_fwd(a, 0, stream), "forward");
+  return hip_status(fa::launch_fwd(a, p->dtype == FA_BF16, stream), "forward");
 }
 
 }  // namespace

@@ -14,6 +14,8 @@
 //   S  = Q K^T        (A: Q rows from LDS,  B: K rows in registers)
 //   dP = dO V^T       (A: dO rows from LDS, B: V rows in registers)
 //   P  = exp2(S c + M log2e - LSE log2e),  dS = P (dP - Delta)
+//   (with a logit softcap c': S c becomes c' tanh(S scale / c') log2e, and dS carries
+//   the derivative of the cap, 1 - tanh^2)
 //   dV += P^T dO      (A: P straight from the accumulator, B: dO^T from LDS)
 //   dK += dS^T Q      (A: dS from the accumulator,        B: Q^T from LDS)
 // The accumulator layout puts one key and 16 query rows in each lane, which is
@@ -74,6 +76,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(const BwdArgs args) {
   const int n0 = blockIdx.x * BN;
   const int key = n0 + 32 * wave + r32;  // this lane's key in S / dP accumulators
   const float cs = a.scale * kLog2e;
+  const bool capped = a.softcap > 0.f;
+  const float cap_in = capped ? a.scale / a.softcap : 0.f, cap_out = a.softcap * kLog2e;
 
   const T* K = static_cast<const T*>(args.k) + b * args.sk.b + hk * args.sk.h;
   const T* V = static_cast<const T*>(args.v) + b * args.sv.b + hk * args.sv.h;
@@ -163,11 +167,16 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(const BwdArgs args) {
           const int qi = q0 + ql;
           bool vis = key < a.Sk && qi < a.Sq;
           if (CAUSAL) vis = vis && ((int64_t)key <= a.q_offset + qi);
-          float x = sacc[r] * cs;
+          float x = sacc[r] * cs, dcap = 1.f;
+          if (capped) {
+            const float t = tanhf(sacc[r] * cap_in);
+            x = t * cap_out;
+            dcap = 1.f - t * t;
+          }
           if (MASK && vis) x += a.mask[b * a.mask_sb + h * a.mask_sh + (int64_t)qi * a.mask_sq + key] * kLog2e;
           const float p = vis ? fast_exp2(x - lse_lds[ql]) : 0.f;
           sacc[r] = p;
-          dpacc[r] = p * (dpacc[r] - dlt_lds[ql]);
+          dpacc[r] = p * (dpacc[r] - dlt_lds[ql]) * dcap;
         }
         // dV += P^T dO and dK += dS^T Q over this 32-row block, 16 rows per step:
         // registers 8 hh .. 8 hh + 7 hold rows 16 hh + {4 g .. 4 g + 3} and

@@ -17,7 +17,8 @@
 // per-lane scalar.
 //
 // Numerics: scores are scaled by scale * log2(e) and exponentiated with the
-// hardware exp2; the LSE is converted back to natural log on output. A row that
+// hardware exp2 (with a logit softcap c, the scaled product x first becomes
+// c tanh(x / c), before the mask is added); the LSE is converted back to natural log on output. A row that
 // has seen no visible key keeps m = -inf; its exponent base is taken as 0 so that
 // exp2(-inf) = 0 flows through without NaN, and the epilogue writes O = 0 and
 // LSE = 0 for it (skill page, section 6, trap 9).
@@ -59,6 +60,8 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(const FwdArgs args) {
   const int qrow = q0 + wave * 32 + r32;
   const int hk = h / a.G;
   const float cs = a.scale * kLog2e;
+  const bool capped = a.softcap > 0.f;
+  const float cap_in = capped ? a.scale / a.softcap : 0.f, cap_out = a.softcap * kLog2e;
 
   const T* Q = static_cast<const T*>(args.q) + b * args.sq.b + h * args.sq.h;
   const T* K = static_cast<const T*>(args.k) + b * args.sk.b + hk * args.sk.h;
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(const FwdArgs args) {
     for (int kb = 0; kb < 2; ++kb) {
       for (int r = 0; r < 16; ++r) {
         const int key = kt * BN + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-        float x = st[kb][r] * cs;
+        float x = capped ? tanhf(st[kb][r] * cap_in) * cap_out : st[kb][r] * cs;
         bool vis = key < a.Sk;
         if (CAUSAL) vis = vis && ((int64_t)key <= a.q_offset + qrow);
         if (MASK && vis && Mrow) x += Mrow[key] * kLog2e;

@@ -37,6 +37,9 @@ struct AttnShape {
   // ALiBi: score (h, i, j) gets -alibi[h] |j - (q_offset + i)|; or nullptr. It runs in the
   // masked kernels' bias body (every live block counts as a bias block)
   const float* alibi;
+  // logit softcap c (> 0) or 0: the scaled product x becomes c tanh(x / c) before the mask;
+  // read by the generic kernels only
+  float softcap;
 };
 
 // the structured lengths of batch entry b (clamped to the tensor lengths)

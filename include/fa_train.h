@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FA_TRAIN_ABI_VERSION 10
+#define FA_TRAIN_ABI_VERSION 11
 
 typedef enum fa_status {
     FA_OK = 0,
@@ -160,6 +160,14 @@ typedef struct fa_attn_params {
      * pull request's KQ bias), with -inf still hiding entries. Its own gradient (dS) is not
      * produced. A per-head mask takes no mask block map (mask_tiles must be NULL). */
     int64_t mask_stride_h;
+    /* Logit softcap (0 = none; else > 0 and finite), a score modifier the pull request's flash
+     * backward lacked: score (b, h, i, j) = c * tanh(scale * <q_i, k_j> / c) + the mask value,
+     * so the product is bounded by c before the mask is added; the backward carries
+     * 1 - tanh^2 into dS. It runs on the generic kernels for both dtypes (no split walks,
+     * no workspace in the forward; the mask block map is not read) and combines with causal
+     * masking and dense masks (per-head ones included), not with sinks, ALiBi or structured
+     * masks (FA_ERR_UNSUPPORTED). */
+    float softcap;
 } fa_attn_params;
 
 /* Forward: writes O (dtype) and LSE (fp32, natural log). Fully masked rows get

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(L, n), n
         assert n in B.SIGNATURES, f"{n} has no ctypes signature in the binding"
-    assert L.fa_train_version() == 10
+    assert L.fa_train_version() == 11
 
 
 BASE = 0x7F0000000000  # fake, 256-byte aligned device addresses
@@ -44,7 +44,7 @@ def params(**kw):
     a = dict(B=1, Hq=4, Hkv=2, Sq=64, Sk=64, D=64, dtype=B.FA_BF16, causal=0, q_offset=0, scale=0.125, mask=None,
              mask_stride_b=0, mask_stride_q=0, mask_tiles=None, fwd_variant=0, kv_split=0, q_split=0, fwd_split=0, key_len=None, q_len=None,
              window_left=-1, window_right=-1, bwd_dq_launch=0, sinks=None, alibi=None,
-             q_split_tiles=0, mask_stride_h=0)
+             q_split_tiles=0, mask_stride_h=0, softcap=0.0)
     a.update(kw)
     return B.FaAttnParams(*(a[f] for f, _ in B.FaAttnParams._fields_))
 
@@ -221,3 +221,22 @@ def test_window_conversions_reject():
     assert L.fa_train_dequant_q8_0(1, 4, 64, 64, qs, B.FaView(BASE + (1 << 24), 4 * 64, 64, 1), view(2), None) == 4
     assert L.fa_train_dequant_q8_0(1, 4, 64, 64, qs, d, view(0), None) == 6  # out overlaps qs
     assert L.fa_train_dequant_q8_0(1, 4, 64, 48, qs, d, view(2), None) == 7
+
+
+def test_softcap_params_rejected():
+    L = B.lib()
+    lse, dlt = lse_view(5), lse_view(6)
+    bad = [(dict(softcap=-1.0), 2), (dict(softcap=float("inf")), 2), (dict(softcap=float("nan")), 2),
+           (dict(softcap=30.0, sinks=BASE + 7 * (1 << 24)), 7), (dict(softcap=30.0, alibi=BASE + 7 * (1 << 24)), 7),
+           (dict(softcap=30.0, window_left=8), 7), (dict(softcap=30.0, key_len=BASE + 7 * (1 << 24)), 7)]
+    for kw, code in bad:
+        p = params(**kw)
+        assert L.fa_train_fwd(ctypes.byref(p), view(0), view(1, H=2), view(2, H=2), view(3), lse, None) == code, kw
+        assert L.fa_train_bwd(ctypes.byref(p), view(0), view(1, H=2), view(2, H=2), view(3), lse, dlt, view(8),
+                              view(9, H=2), view(10, H=2), None, 0, None) == code, kw
+    # a softcap problem runs on the generic kernels: no forward split workspace, and the
+    # backward's workspace is the fp32 dQ accumulator for both dtypes
+    for dt in (B.FA_BF16, B.FA_F32):
+        p = params(softcap=30.0, dtype=dt)
+        assert L.fa_train_fwd_workspace_bytes(ctypes.byref(params(softcap=30.0, dtype=dt, Sk=4096))) == 0
+        assert L.fa_train_bwd_workspace_bytes(ctypes.byref(p)) == 1 * 4 * 64 * 64 * 4

@@ -242,3 +242,30 @@ def test_lm_alibi_full_size_sampled():
     refc = oracle.cols(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), cols, scale=c.scale, causal=True,
                        q_offset=0, alibi=a64)
     _check_cols(c, got["dK"], got["dV"], cols, refc, TOL[c.dtype])
+
+
+def test_lm_softcap_full_size_sampled():
+    """The LM layer with a logit softcap, as the bench runs it (the generic kernels): sampled rows
+    (O, LSE, Delta, dQ) and key columns (dK, dV) against the oracle with the same cap."""
+    c = configs.make("lm_softcap")
+    cap = c.meta["softcap"]
+    say(f"lm_softcap: full size, softcap {cap}, sampled rows and columns")
+    t = upload(c)
+    o, lse = binding.fwd(t["q"], t["k"], t["v"], scale=c.scale, causal=True, q_offset=0, softcap=cap)
+    delta = binding.bwd_preprocess(o, t["do"])
+    dq, dk, dv = binding.bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, scale=c.scale, causal=True, q_offset=0,
+                             softcap=cap)
+    torch.cuda.synchronize()
+    got = {"O": host64(o), "LSE": host64(lse), "Delta": host64(delta), "dQ": host64(dq), "dK": host64(dk),
+           "dV": host64(dv)}
+    rng = np.random.default_rng(8)
+    rows = np.unique(np.concatenate([[0, 1, c.Sq - 1, 17 * c.Sq + 2049], rng.choice(c.Hq * c.Sq, 60, replace=False)])
+                     ).astype(np.int64)
+    ref = oracle.rows(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), rows, scale=c.scale, causal=True,
+                      q_offset=0, softcap=cap)
+    _check_rows(c, got, rows, ref, TOL[c.dtype])
+    cols = np.unique(np.concatenate([[0, c.Sk - 1], rng.choice(np.arange(5 * c.Sk, 6 * c.Sk), 8, replace=False)])
+                     ).astype(np.int64)
+    refc = oracle.cols(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), cols, scale=c.scale, causal=True,
+                       q_offset=0, softcap=cap)
+    _check_cols(c, got["dK"], got["dV"], cols, refc, TOL[c.dtype])

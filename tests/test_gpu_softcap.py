@@ -1,0 +1,83 @@
+"""GPU parity of the logit softcap (score (b, h, i, j) = c tanh(scale <q_i, k_j> / c) + the
+mask value) against the oracle, in fp32 and bf16: every output element by element, with the
+exact-zero checks for fully masked rows and dead key columns. Cases: the causal GQA layer, a
+dense key-padding mask with fully masked rows, a score bias per head, and the chunked walk
+over a window (each chunk adding into the fp32 dK / dV accumulators). The caps are small
+enough (1 to 4 score units) that tanh is well inside its bend for N(0, 1) inputs."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from flash_attention_train_amd import binding, configs
+from flash_attention_train_amd.inputs import BF16, F32, make_case
+from parity_util import compare_full, host64, say, upload
+from test_gpu_head_bias import _case as head_bias_case, compare as head_bias_compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(name, dtype):
+    if name == "lm_causal_gqa4":
+        return make_case(name, B=1, Hq=8, Hkv=2, Sq=300, Sk=300, D=128, dtype=dtype, seed=131, causal=True), 1.0
+    if name == "ca_keypad_rows_d64":
+        return make_case(name, B=2, Hq=4, Hkv=4, Sq=200, Sk=150, D=64, dtype=dtype, seed=132, mask="ca_keypad",
+                         mask_args={"lo": 40, "hi": 150, "masked_rows": 2}), 2.0
+    if name == "head_bias":  # [B, Hq, Sq, Sk] biases with rows and key columns hidden per head
+        return head_bias_case(name, B=2, Hq=4, Hkv=2, Sq=130, Sk=190, D=128, dtype=dtype, seed=133), 4.0
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("name", ["lm_causal_gqa4", "ca_keypad_rows_d64", "head_bias"])
+def test_softcap_parity(name, dtype):
+    c, cap = _case(name, dtype)
+    say(f"case {name} ({dtype}): softcap {cap}")
+    bias = c.meta.get("bias")
+    m = bias if bias is not None else c.mask
+    ref = oracle.backward(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), None if m is None else m.astype(np.float64),
+                          scale=c.scale, causal=c.causal, q_offset=c.q_offset, softcap=cap)
+    t = upload(c)
+    if bias is not None:
+        t["mask"] = torch.from_numpy(bias).cuda()
+    o, lse = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
+                         q_offset=c.q_offset, softcap=cap)
+    delta = binding.bwd_preprocess(o, t["do"])
+    dq, dk, dv = binding.bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, mask=t["mask"], scale=c.scale,
+                             causal=c.causal, q_offset=c.q_offset, softcap=cap)
+    torch.cuda.synchronize()
+    got = {"O": host64(o), "LSE": host64(lse), "Delta": host64(delta), "dQ": host64(dq), "dK": host64(dk),
+           "dV": host64(dv)}
+    if bias is not None:
+        head_bias_compare(c, got, ref)
+    else:
+        compare_full(c, got, ref)
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_softcap_chunked_window(dtype):
+    W, C, cap = 512, 128, 1.5
+    c = configs.make("long_window", W=W, Hq=4, Hkv=1, D=64, dtype=dtype)
+    say(f"softcap chunked walk ({dtype}): W={W}, chunks of {C}, softcap {cap}")
+    t = upload(c)
+    dk_acc = torch.zeros((1, c.Hkv, W, c.D), dtype=torch.float32, device="cuda")
+    dv_acc = torch.zeros_like(dk_acc)
+    O, dQ = torch.empty_like(t["q"]), torch.empty_like(t["q"])
+    LSE = torch.empty((1, c.Hq, W), dtype=torch.float32, device="cuda")
+    Delta = torch.empty_like(LSE)
+    for p0, n, sk in configs.chunk_plan(W, C):
+        q, do = t["q"][:, :, p0:p0 + n], t["do"][:, :, p0:p0 + n]
+        kk, vv = t["k"][:, :, :sk], t["v"][:, :, :sk]
+        o, lse = binding.fwd(q, kk, vv, scale=c.scale, causal=True, q_offset=p0, out=O[:, :, p0:p0 + n],
+                             lse=LSE[:, :, p0:p0 + n], softcap=cap)
+        delta = binding.bwd_preprocess(o, do, delta=Delta[:, :, p0:p0 + n])
+        binding.bwd_chunked(q, kk, vv, do, lse, delta, dk_acc, dv_acc, scale=c.scale, causal=True, q_offset=p0,
+                            dq=dQ[:, :, p0:p0 + n], softcap=cap)
+    torch.cuda.synchronize()
+    ref = oracle.backward(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), scale=c.scale, causal=True, q_offset=0,
+                          softcap=cap)
+    got = {"O": host64(O), "LSE": host64(LSE), "Delta": host64(Delta), "dQ": host64(dQ),
+           "dK": dk_acc.cpu().numpy().astype(np.float64), "dV": dv_acc.cpu().numpy().astype(np.float64)}
+    compare_full(c, got, ref)
