@@ -159,8 +159,8 @@ fa::AttnShape shape_of(const fa_attn_params* p) {
   return a;
 }
 
-// The generic kernels (fa_fwd.hip, fa_bwd.hip) run fp32 problems and every problem with a
-// logit softcap; the bf16 MFMA kernels run the rest.
+// The generic backward (fa_bwd.hip) runs fp32 problems and every problem with a logit
+// softcap; the bf16 MFMA backward runs the rest. (The bf16 forward takes the softcap itself.)
 bool generic_path(const fa_attn_params* p) { return p->dtype != FA_BF16 || p->softcap > 0.f; }
 
 fa::Strides strides_of(const fa_view* v) { return {v->stride_b, v->stride_h, v->stride_s}; }
@@ -482,7 +482,7 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
 // (measured: 16 heads x 1542 rows gains 10% at 2 splits and loses at 3; a 512-row
 // chunk over a 32768-key window runs 4x faster at 8).
 int choose_fwd_split(const fa_attn_params* p) {
-  if (generic_path(p)) return 1;
+  if (p->dtype != FA_BF16) return 1;
   const int64_t wgs = (int64_t)p->B * p->Hq * ((p->Sq + 127) / 128);
   int64_t nkt = (p->Sk + 63) / 64;
   if (p->causal) {  // the longest walk: the last query tile's
@@ -560,7 +560,7 @@ fa_status fwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   a.splits = splits;
   a.part_o = nullptr;
   a.part_ml = nullptr;
-  if (!generic_path(p)) {
+  if (p->dtype == FA_BF16) {
     if (splits > 1) {  // the split walk runs the default configuration
       a.part_o = workspace;
       a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
@@ -573,7 +573,7 @@ fa_status fwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
     const int variant = p->fwd_variant ? p->fwd_variant : 1;
     return hip_status(fa::launch_fwd_bf16(a, variant, stream), "forward");
   }
-  return hip_status(fa::launch_fwd(a, p->dtype == FA_BF16, stream), "forward");
+  return hip_status(fa::launch_fwd(a, 0, stream), "forward");
 }
 
 }  // namespace

@@ -71,6 +71,12 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
   const int qw = q0 + rb * QB * 32;            // first row of this wave
   const int hk = h / a.G;
   const float cs = a.scale * kLog2e;           // scale > 0 (checked on the host)
+  // logit softcap c in raw score units: S -> (c / scale) tanh(S scale / c), with
+  // tanh(x) = 1 - 2 / (e^(2x) + 1) from the hardware exp2 and reciprocal (absolute error a
+  // few ulp of 1; e^(2x) overflowing to inf gives 1, underflowing to 0 gives -1)
+  const bool capped = a.softcap > 0.f;
+  const float cap_k = capped ? 2.f * kLog2e * a.scale / a.softcap : 0.f;
+  const float cap_raw = a.softcap * args.inv_scale;
 
   const bf16* Q = static_cast<const bf16*>(args.q) + b * args.sq.b + h * args.sq.h;
   const bf16* K = static_cast<const bf16*>(args.k) + b * args.sk.b + hk * args.sk.h;
@@ -264,6 +270,15 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int row = qw + 32 * qb + r32;
+      if (capped) {
+        #pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = fast_exp2(st[qb][kb][r] * cap_k);
+            st[qb][kb][r] = cap_raw * (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f));
+          }
+      }
       if (MASK && bias && a.alibi) {
         // ALiBi in raw score units: -(slope / scale) |key - position|; this lane's row, the
         // register's key: key - position = (key0 + 4 g - q_offset - row) + 32 kb + 8 rr + e

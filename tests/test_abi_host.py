@@ -234,9 +234,12 @@ def test_softcap_params_rejected():
         assert L.fa_train_fwd(ctypes.byref(p), view(0), view(1, H=2), view(2, H=2), view(3), lse, None) == code, kw
         assert L.fa_train_bwd(ctypes.byref(p), view(0), view(1, H=2), view(2, H=2), view(3), lse, dlt, view(8),
                               view(9, H=2), view(10, H=2), None, 0, None) == code, kw
-    # a softcap problem runs on the generic kernels: no forward split workspace, and the
-    # backward's workspace is the fp32 dQ accumulator for both dtypes
+    # a softcap backward runs on the generic kernels: its workspace is the fp32 dQ accumulator
+    # for both dtypes; the bf16 forward keeps its split walks
     for dt in (B.FA_BF16, B.FA_F32):
         p = params(softcap=30.0, dtype=dt)
-        assert L.fa_train_fwd_workspace_bytes(ctypes.byref(params(softcap=30.0, dtype=dt, Sk=4096))) == 0
         assert L.fa_train_bwd_workspace_bytes(ctypes.byref(p)) == 1 * 4 * 64 * 64 * 4
+    long_keys = dict(softcap=30.0, Sk=4096)
+    assert L.fa_train_fwd_workspace_bytes(ctypes.byref(params(**long_keys))) == \
+        L.fa_train_fwd_workspace_bytes(ctypes.byref(params(Sk=4096))) > 0
+    assert L.fa_train_fwd_workspace_bytes(ctypes.byref(params(dtype=B.FA_F32, **long_keys))) == 0

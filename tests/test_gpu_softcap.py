@@ -1,6 +1,7 @@
 """GPU parity of the logit softcap (score (b, h, i, j) = c tanh(scale <q_i, k_j> / c) + the
 mask value) against the oracle, in fp32 and bf16: every output element by element, with the
-exact-zero checks for fully masked rows and dead key columns. Cases: the causal GQA layer, a
+exact-zero checks for fully masked rows and dead key columns. The bf16 forward runs the cap in
+its MFMA kernel (whole and split key walks), the backward on the generic kernels. Cases: the causal GQA layer, a
 dense key-padding mask with fully masked rows, a score bias per head, and the chunked walk
 over a window (each chunk adding into the fp32 dK / dV accumulators). The caps are small
 enough (1 to 4 score units) that tanh is well inside its bend for N(0, 1) inputs."""
@@ -32,9 +33,10 @@ def _case(name, dtype):
 
 @pytest.mark.parametrize("dtype", [F32, BF16])
 @pytest.mark.parametrize("name", ["lm_causal_gqa4", "ca_keypad_rows_d64", "head_bias"])
-def test_softcap_parity(name, dtype):
+@pytest.mark.parametrize("split", [0, 3])
+def test_softcap_parity(name, dtype, split):
     c, cap = _case(name, dtype)
-    say(f"case {name} ({dtype}): softcap {cap}")
+    say(f"case {name} ({dtype}): softcap {cap}, forward split {split}")
     bias = c.meta.get("bias")
     m = bias if bias is not None else c.mask
     ref = oracle.backward(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), None if m is None else m.astype(np.float64),
@@ -43,7 +45,7 @@ def test_softcap_parity(name, dtype):
     if bias is not None:
         t["mask"] = torch.from_numpy(bias).cuda()
     o, lse = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
-                         q_offset=c.q_offset, softcap=cap)
+                         q_offset=c.q_offset, softcap=cap, split=split)
     delta = binding.bwd_preprocess(o, t["do"])
     dq, dk, dv = binding.bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, mask=t["mask"], scale=c.scale,
                              causal=c.causal, q_offset=c.q_offset, softcap=cap)
@@ -81,3 +83,18 @@ def test_softcap_chunked_window(dtype):
     got = {"O": host64(O), "LSE": host64(LSE), "Delta": host64(Delta), "dQ": host64(dQ),
            "dK": dk_acc.cpu().numpy().astype(np.float64), "dV": dv_acc.cpu().numpy().astype(np.float64)}
     compare_full(c, got, ref)
+
+
+@pytest.mark.parametrize("variant", [2, 3])
+def test_softcap_forward_variants(variant):
+    """The other configurations of the bf16 forward kernel (64 rows per wave with 32-key tiles;
+    keys split over two halves of the workgroup) apply the cap the same way."""
+    c, cap = _case("ca_keypad_rows_d64", BF16)
+    say(f"case ca_keypad_rows_d64 (bf16): softcap {cap}, forward variant {variant}")
+    ref = oracle.backward(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), c.mask.astype(np.float64), scale=c.scale,
+                          causal=c.causal, q_offset=c.q_offset, softcap=cap)
+    t = upload(c)
+    o, lse = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
+                         q_offset=c.q_offset, softcap=cap, split=1, variant=variant)
+    torch.cuda.synchronize()
+    compare_full(c, {"O": host64(o), "LSE": host64(lse)}, ref, names=("O", "LSE"))
