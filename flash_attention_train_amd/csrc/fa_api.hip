@@ -159,9 +159,10 @@ fa::AttnShape shape_of(const fa_attn_params* p) {
   return a;
 }
 
-// The generic backward (fa_bwd.hip) runs fp32 problems and every problem with a logit
-// softcap; the bf16 MFMA backward runs the rest. (The bf16 forward takes the softcap itself.)
-bool generic_path(const fa_attn_params* p) { return p->dtype != FA_BF16 || p->softcap > 0.f; }
+// The generic backward (fa_bwd.hip) runs fp32 problems and logit softcaps over a dense
+// mask; the bf16 MFMA backward runs the rest (a softcap without a dense mask in a variant of
+// its own). The bf16 forward takes every softcap itself.
+bool generic_path(const fa_attn_params* p) { return p->dtype != FA_BF16 || (p->softcap > 0.f && p->mask); }
 
 fa::Strides strides_of(const fa_view* v) { return {v->stride_b, v->stride_h, v->stride_s}; }
 

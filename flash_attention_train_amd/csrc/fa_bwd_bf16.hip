@@ -201,7 +201,12 @@ struct LiveWords {
   }
 };
 
-template <int D, bool CAUSAL, bool MASK, bool BIAS>
+// CAP: a logit softcap (no dense mask). The scores then leave the product raw: the cap's
+// tanh sits between the product and the LSE, so the S half of the augmented k-chunk is not
+// applied, and each slice reads -LSE / scale of its rows from the augmented rows in LDS.
+// tanh(x) = 1 - 2 / (e^(2x) + 1) from the hardware exp2 and reciprocal, as in the forward;
+// dS carries the cap's derivative 1 - tanh^2.
+template <int D, bool CAUSAL, bool MASK, bool BIAS, bool CAP = false>
 __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
   constexpr int DS = D / 16, DB = D / 32;
   static_assert(8 % DS == 0 && 8 % (2 * DB) == 0, "each woven slice holds whole product pairs");
@@ -226,6 +231,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
   const int n0 = kt * KV_BN;
   const int key = n0 + 32 * wave + r32;
   const float cs = a.scale * kLog2e;
+  const float cap_k = CAP ? 2.f * kLog2e * a.scale / a.softcap : 0.f, cap_raw = a.softcap * args.inv_scale;
 
   const bf16* K = static_cast<const bf16*>(args.k) + b * args.sk.b + hk * args.sk.h;
   const bf16* V = static_cast<const bf16*>(args.v) + b * args.sv.b + hk * args.sv.h;
@@ -499,6 +505,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     // P = 0; bit 8 rr + e of the visibility word <-> register 4 rr + e)
     struct RowStats {
       uint32_t w;
+      const bf16* x;  // (CAP) the augmented row of register 0's query row
     };
     auto stats_b = [&](int qb, f32x16& sacc, RowStats& st) {
       if (BIAS && bias && a.alibi) {
@@ -518,8 +525,23 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
         }
       }
       st.w = (uint32_t)(vis >> (32 * qb + 4 * g));
+      st.x = qx_lds + (32 * qb + 4 * g) * 16;
     };
     auto slice_b = [&](int i, const RowStats& st, f32x16& sacc, f32x16& dpacc) {
+      if constexpr (CAP) {
+        #pragma unroll
+        for (int r = 2 * i; r < 2 * i + 2; ++r) {
+          // -LSE / scale of the register's row: the three terms of its augmented row
+          const bf16x4 c3 = *reinterpret_cast<const bf16x4*>(st.x + (8 * (r >> 2) + (r & 3)) * 16);
+          const float nl = (float)c3[0] + (float)c3[1] + (float)c3[2];
+          const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(fast_exp2(sacc[r] * cap_k) + 1.f);
+          const float sv = ninf_unless_bit(fmaf(cap_raw, t, nl), st.w, 8 * (r >> 2) + (r & 3));
+          const float pv = fast_exp2(sv * cs);
+          sacc[r] = pv;
+          dpacc[r] = pv * dpacc[r] * (1.f - t * t);
+        }
+        return;
+      }
       #pragma unroll
       for (int r = 2 * i; r < 2 * i + 2; ++r) {
         // (the products already hold S - LSE / scale and dP - Delta)
@@ -538,7 +560,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
       mma(s0, pqa[s], kf[s]);
       mma(dp0, pda[s], vf[s]);
     }
-    mma(s0, pqx, ones3);
+    if constexpr (!CAP) mma(s0, pqx, ones3);
     mma(dp0, pdx, ones3);
     // Step A of block 1 woven with step B of block 0, then step C of block 0 woven with
     // step B of block 1: each two are independent, and one wave per SIMD only overlaps
@@ -567,7 +589,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
           mma(dp1, da[i / EVERY], vf[i / EVERY]);
         }
         if (i == 7) {
-          mma(s1, qx, ones3);
+          if constexpr (!CAP) mma(s1, qx, ones3);
           mma(dp1, dx, ones3);
         }
         slice_b(i, st, s0, dp0);
@@ -644,7 +666,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
 // ---------------------------------------------------------------------------
 // dQ workgroup
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool MASK, bool BIAS, bool LOWREG = false>
+template <int D, bool CAUSAL, bool MASK, bool BIAS, bool LOWREG = false, bool CAP = false>
 __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
   constexpr int DS = D / 16, DB = D / 32;
   using TL = Tile<D>;
@@ -662,6 +684,7 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
   const int qw = q0 + 32 * wave;
   const int row = qw + r32;
   const float cs = a.scale * kLog2e;
+  const float cap_k = CAP ? 2.f * kLog2e * a.scale / a.softcap : 0.f, cap_raw = a.softcap * args.inv_scale;
 
   const bf16* Q = static_cast<const bf16*>(args.q) + b * args.sq.b + h * args.sq.h;
   const bf16* dO = static_cast<const bf16*>(args.dout) + b * args.sdo.b + h * args.sdo.h;
@@ -875,6 +898,16 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
           for (int e = 0; e < 4; ++e) st[4 * rr + e] += mv[e] * args.inv_scale;
         }
       }
+      if constexpr (CAP) {  // (no dense mask) the capped score, P and dS element by element
+        const uint32_t w = (uint32_t)(vis >> (32 * kb + 4 * g));
+        #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(fast_exp2(st[r] * cap_k) + 1.f);
+          float x = cap_raw * t;
+          if (masked) x = ninf_unless_bit(x, w, 8 * (r >> 2) + (r & 3));
+          st[r] = fast_exp2(fmaf(x, cs, -lse2)) * (dpt[r] - dlt) * (1.f - t * t);
+        }
+      } else {
       if (masked) {  // hidden scores -> -inf (P = 0); bit 8 rr + e of w <-> register 4 rr + e
         const uint32_t w = (uint32_t)(vis >> (32 * kb + 4 * g));
         #pragma unroll
@@ -884,6 +917,7 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
       for (int r = 0; r < 16; ++r) st[r] = fast_exp2(fmaf(st[r], cs, -lse2));
       #pragma unroll
       for (int r = 0; r < 16; ++r) st[r] = st[r] * (dpt[r] - dlt);
+      }
       #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         if constexpr (LOWREG) read_kbt(hh);  // (two workgroups per unit: read when needed)
@@ -921,7 +955,7 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
 // Units whose mask blocks carry additive values run a body compiled with the
 // mask-value reads; all others (dead / open / 0-or--inf blocks) a body without them,
 // which keeps that code and its registers out of the common loop.
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool CAP = false>
 __global__ __launch_bounds__(NT) void bwd_bf16_kernel(const BwdArgs args, const BwdPlan plan) {
   constexpr int KV_LDS = 3 * 2 * KV_BM * D * 2 + 2 * 3 * KV_BM * 16 * 2;
   constexpr int Q_LDS = 2 * 2 * Q_BN * D * 2;
@@ -932,24 +966,24 @@ __global__ __launch_bounds__(NT) void bwd_bf16_kernel(const BwdArgs args, const 
     const KvUnit u = kv_unit_of(a, plan, blk);
     if (MASK && any_bias_block(a, u.b, 0, (a.Sq + kMaskTile - 1) / kMaskTile, u.kt * (KV_BN / kMaskTile),
                                KV_BN / kMaskTile))
-      dkdv_unit<D, CAUSAL, MASK, true>(args, plan, blk, smem);
+      dkdv_unit<D, CAUSAL, MASK, true, CAP>(args, plan, blk, smem);
     else
-      dkdv_unit<D, CAUSAL, MASK, false>(args, plan, blk, smem);
+      dkdv_unit<D, CAUSAL, MASK, false, CAP>(args, plan, blk, smem);
   } else {
     const int unit = blk - plan.n_kv_units;
     const QUnit u = q_unit_of(a, plan, unit);
     if (MASK && any_bias_block(a, u.b, u.qt * (Q_BM / kMaskTile), Q_BM / kMaskTile, 0,
                                (a.Sk + kMaskTile - 1) / kMaskTile))
-      dq_unit<D, CAUSAL, MASK, true>(args, plan, unit, smem);
+      dq_unit<D, CAUSAL, MASK, true, false, CAP>(args, plan, unit, smem);
     else
-      dq_unit<D, CAUSAL, MASK, false>(args, plan, unit, smem);
+      dq_unit<D, CAUSAL, MASK, false, false, CAP>(args, plan, unit, smem);
   }
 }
 
 // The dQ walk as a kernel of its own: its registers fit two workgroups per compute unit
 // (the dK/dV walk's do not), so that one workgroup's LDS and memory waits are covered by
 // the other's products. Launched after the dK/dV-only grid when the plan asks for it.
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool CAP = false>
 __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(const BwdArgs args, const BwdPlan plan) {
   constexpr int Q_LDS = 2 * 2 * Q_BN * D * 2;
   __shared__ __attribute__((aligned(16))) char smem[Q_LDS];
@@ -958,29 +992,32 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(const BwdArgs args, const
   const QUnit u = q_unit_of(a, plan, unit);
   if (MASK && any_bias_block(a, u.b, u.qt * (Q_BM / kMaskTile), Q_BM / kMaskTile, 0,
                              (a.Sk + kMaskTile - 1) / kMaskTile))
-    dq_unit<D, CAUSAL, MASK, true, true>(args, plan, unit, smem);
+    dq_unit<D, CAUSAL, MASK, true, true, CAP>(args, plan, unit, smem);
   else
-    dq_unit<D, CAUSAL, MASK, false, true>(args, plan, unit, smem);
+    dq_unit<D, CAUSAL, MASK, false, true, CAP>(args, plan, unit, smem);
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool CAP = false>
 hipError_t launch_cm(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream) {
   if (!plan.dq_separate) {
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, MASK>), dim3(plan.n_kv_units + plan.n_q_units), dim3(NT), 0, stream,
-                       args, plan);
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, MASK, CAP>), dim3(plan.n_kv_units + plan.n_q_units), dim3(NT), 0,
+                       stream, args, plan);
     return hipGetLastError();
   }
   if (plan.n_kv_units > 0)
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, MASK>), dim3(plan.n_kv_units), dim3(NT), 0, stream, args, plan);
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, MASK, CAP>), dim3(plan.n_kv_units), dim3(NT), 0, stream, args,
+                       plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.n_q_units == 0) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, MASK>), dim3(plan.n_q_units), dim3(NT), 0, stream, args, plan);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, MASK, CAP>), dim3(plan.n_q_units), dim3(NT), 0, stream, args, plan);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_t(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream) {
   const bool causal = args.a.causal != 0, mask = args.a.mask != nullptr || args.a.alibi != nullptr;
+  if (args.a.softcap > 0.f && !mask)  // (a softcap with a dense mask runs on the generic kernels)
+    return causal ? launch_cm<D, true, false, true>(args, plan, stream) : launch_cm<D, false, false, true>(args, plan, stream);
   if (causal && mask) return launch_cm<D, true, true>(args, plan, stream);
   if (causal) return launch_cm<D, true, false>(args, plan, stream);
   if (mask) return launch_cm<D, false, true>(args, plan, stream);

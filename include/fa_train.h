@@ -164,10 +164,11 @@ typedef struct fa_attn_params {
      * backward lacked: score (b, h, i, j) = c * tanh(scale * <q_i, k_j> / c) + the mask value,
      * so the product is bounded by c before the mask is added; the backward carries
      * 1 - tanh^2 into dS. The bf16 forward applies it in its MFMA kernel (split walks
-     * included); the backward runs on the generic kernels for both dtypes (its workspace is
-     * then the fp32 dQ accumulator, and the mask block map is not read). It combines with
-     * causal masking and dense masks (per-head ones included), not with sinks, ALiBi or
-     * structured masks (FA_ERR_UNSUPPORTED). */
+     * included), and so does the bf16 backward without a dense mask (every work
+     * decomposition); over a dense mask, and for fp32, the backward runs on the generic
+     * kernels (its workspace is then the fp32 dQ accumulator, and the mask block map is not
+     * read). It combines with causal masking and dense masks (per-head ones included), not
+     * with sinks, ALiBi or structured masks (FA_ERR_UNSUPPORTED). */
     float softcap;
 } fa_attn_params;
 

@@ -234,11 +234,14 @@ def test_softcap_params_rejected():
         assert L.fa_train_fwd(ctypes.byref(p), view(0), view(1, H=2), view(2, H=2), view(3), lse, None) == code, kw
         assert L.fa_train_bwd(ctypes.byref(p), view(0), view(1, H=2), view(2, H=2), view(3), lse, dlt, view(8),
                               view(9, H=2), view(10, H=2), None, 0, None) == code, kw
-    # a softcap backward runs on the generic kernels: its workspace is the fp32 dQ accumulator
-    # for both dtypes; the bf16 forward keeps its split walks
+    # a softcap backward over a dense mask runs on the generic kernels, whose workspace is the
+    # fp32 dQ accumulator for both dtypes; without a mask the bf16 one keeps the MFMA kernels'
+    # plan (no workspace for this unsplit shape); the bf16 forward keeps its split walks
+    masked = dict(softcap=30.0, mask=BASE + 11 * (1 << 24), mask_stride_q=64)
     for dt in (B.FA_BF16, B.FA_F32):
-        p = params(softcap=30.0, dtype=dt)
-        assert L.fa_train_bwd_workspace_bytes(ctypes.byref(p)) == 1 * 4 * 64 * 64 * 4
+        assert L.fa_train_bwd_workspace_bytes(ctypes.byref(params(dtype=dt, **masked))) == 1 * 4 * 64 * 64 * 4
+    assert L.fa_train_bwd_workspace_bytes(ctypes.byref(params(softcap=30.0))) == \
+        L.fa_train_bwd_workspace_bytes(ctypes.byref(params())) == 0
     long_keys = dict(softcap=30.0, Sk=4096)
     assert L.fa_train_fwd_workspace_bytes(ctypes.byref(params(**long_keys))) == \
         L.fa_train_fwd_workspace_bytes(ctypes.byref(params(Sk=4096))) > 0

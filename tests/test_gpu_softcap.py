@@ -1,7 +1,8 @@
 """GPU parity of the logit softcap (score (b, h, i, j) = c tanh(scale <q_i, k_j> / c) + the
 mask value) against the oracle, in fp32 and bf16: every output element by element, with the
 exact-zero checks for fully masked rows and dead key columns. The bf16 forward runs the cap in
-its MFMA kernel (whole and split key walks), the backward on the generic kernels. Cases: the causal GQA layer, a
+its MFMA kernel (whole and split key walks); the bf16 backward in its MFMA kernels when there is
+no dense mask (every work decomposition), else on the generic kernels, as fp32 does. Cases: the causal GQA layer, a
 dense key-padding mask with fully masked rows, a score bias per head, and the chunked walk
 over a window (each chunk adding into the fp32 dK / dV accumulators). The caps are small
 enough (1 to 4 score units) that tanh is well inside its bend for N(0, 1) inputs."""
@@ -26,13 +27,15 @@ def _case(name, dtype):
     if name == "ca_keypad_rows_d64":
         return make_case(name, B=2, Hq=4, Hkv=4, Sq=200, Sk=150, D=64, dtype=dtype, seed=132, mask="ca_keypad",
                          mask_args={"lo": 40, "hi": 150, "masked_rows": 2}), 2.0
+    if name == "plain_d64":  # no mask, not causal, ragged tiles
+        return make_case(name, B=2, Hq=4, Hkv=2, Sq=190, Sk=250, D=64, dtype=dtype, seed=135), 2.0
     if name == "head_bias":  # [B, Hq, Sq, Sk] biases with rows and key columns hidden per head
         return head_bias_case(name, B=2, Hq=4, Hkv=2, Sq=130, Sk=190, D=128, dtype=dtype, seed=133), 4.0
     raise KeyError(name)
 
 
 @pytest.mark.parametrize("dtype", [F32, BF16])
-@pytest.mark.parametrize("name", ["lm_causal_gqa4", "ca_keypad_rows_d64", "head_bias"])
+@pytest.mark.parametrize("name", ["lm_causal_gqa4", "plain_d64", "ca_keypad_rows_d64", "head_bias"])
 @pytest.mark.parametrize("split", [0, 3])
 def test_softcap_parity(name, dtype, split):
     c, cap = _case(name, dtype)
@@ -98,3 +101,25 @@ def test_softcap_forward_variants(variant):
                          q_offset=c.q_offset, softcap=cap, split=1, variant=variant)
     torch.cuda.synchronize()
     compare_full(c, {"O": host64(o), "LSE": host64(lse)}, ref, names=("O", "LSE"))
+
+
+@pytest.mark.parametrize("kv_split,q_split,q_split_tiles,dq_launch", [(1, 1, 0, 1), (2, 1, 0, 2), (3, 2, 0, 1),
+                                                                      (2, 2, 1, 1), (1, 3, 2, 2)])
+@pytest.mark.parametrize("name", ["lm_causal_gqa4", "plain_d64"])
+def test_softcap_backward_decompositions(name, kv_split, q_split, q_split_tiles, dq_launch):
+    """The capped bf16 backward in the MFMA kernels: split dK/dV and dQ walks (with their reduce
+    passes), the split tail, and the dQ walk in the shared or its own launch."""
+    c, cap = _case(name, BF16)
+    say(f"case {name} (bf16): softcap {cap}, splits {kv_split}x{q_split}x{q_split_tiles}, dq launch {dq_launch}")
+    ref = oracle.backward(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), scale=c.scale, causal=c.causal,
+                          q_offset=c.q_offset, softcap=cap)
+    t = upload(c)
+    o, lse = binding.fwd(t["q"], t["k"], t["v"], scale=c.scale, causal=c.causal, q_offset=c.q_offset, softcap=cap)
+    delta = binding.bwd_preprocess(o, t["do"])
+    dq, dk, dv = binding.bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, scale=c.scale, causal=c.causal,
+                             q_offset=c.q_offset, softcap=cap, kv_split=kv_split, q_split=q_split,
+                             q_split_tiles=q_split_tiles, dq_launch=dq_launch)
+    torch.cuda.synchronize()
+    got = {"O": host64(o), "LSE": host64(lse), "Delta": host64(delta), "dQ": host64(dq), "dK": host64(dk),
+           "dV": host64(dv)}
+    compare_full(c, got, ref)
