@@ -8,7 +8,7 @@ import pytest
 import oracle
 from flash_attention_train_amd import accounting as A
 from flash_attention_train_amd import configs
-from flash_attention_train_amd.inputs import bf16_bits_to_f32, f32_to_bf16_bits, make_case
+from flash_attention_train_amd.inputs import F32, bf16_bits_to_f32, f32_to_bf16_bits, make_case
 
 
 def test_bf16_rounding_matches_torch():
@@ -104,3 +104,34 @@ def test_structured_workload_pairs_match_the_dense_definition(key):
     m = oracle.structured_mask(c.B, c.Sq, c.Sk, key_len=st["key_len"], q_len=st["q_len"],
                                window_left=st["window"][0], window_right=st["window"][1], q_offset=c.q_offset)
     assert A.case_pairs(c) == int(np.isfinite(m).sum())
+
+
+def test_every_workload_draws_deterministically_at_a_small_size():
+    """Each entry of the workload table can be drawn at a small size, twice with the same values,
+    and the bench's default workloads all come from the table."""
+    import bench
+    assert set(bench.DEFAULT_EXTRA) <= set(configs.WORKLOADS)
+    small = {"long_window": dict(W=256, Hq=2, Hkv=1, D=64), "lm": dict(Sq=96, Sk=96, Hq=4, Hkv=2, D=64),
+             "dit": dict(Hq=2, Hkv=1, D=64)}
+    for key in configs.WORKLOADS:
+        kw = small["long_window"] if key.startswith("long_window") else small["lm"] if key.startswith("lm") \
+            else small["dit"]
+        a, b = configs.make(key, **kw), configs.make(key, **kw)
+        for n in ("q", "k", "v", "do"):
+            assert np.array_equal(getattr(a, n), getattr(b, n)), (key, n)
+        assert a.q.shape[1] == kw["Hq"] and a.k.shape[1] == kw["Hkv"], key
+
+
+def test_f16_window_holds_the_draws_rounded_once():
+    c = configs.make("long_window_f16", W=256, Hq=2, Hkv=1, D=64)
+    full = configs.make("long_window_f16", W=256, Hq=2, Hkv=1, D=64, dtype=F32)
+    for n in ("k", "v"):
+        w = c.meta["f16"][n]
+        assert w.dtype == np.float16
+        x = full.f64(n)
+        # nearest fp16: within half a unit in the last place of the value (normal range)
+        ulp = np.spacing(np.abs(w).astype(np.float16)).astype(np.float64)
+        assert np.all(np.abs(w.astype(np.float64) - x) <= 0.5 * ulp + 1e-30)
+        # the case's own bf16 K / V are those fp16 values rounded to bf16
+        np.testing.assert_array_equal(getattr(c, n), f32_to_bf16_bits(w.astype(np.float32)))
+    assert configs.make("lm_softcap", Sq=64, Sk=64, Hq=2, Hkv=1, D=64).meta["softcap"] == 50.0
