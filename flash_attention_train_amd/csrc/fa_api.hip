@@ -102,9 +102,11 @@ fa_status check_params(const fa_attn_params* p) {
   if (structured && p->dtype != FA_BF16)
     return fail(FA_ERR_UNSUPPORTED, "structured masks (key_len, q_len, window) are implemented for bf16 only");
   if (!(p->softcap >= 0.f) || isinf(p->softcap)) return fail(FA_ERR_SHAPE, "softcap must be >= 0 and finite");
-  if (p->softcap > 0.f && (p->sinks || p->alibi || structured))
-    return fail(FA_ERR_UNSUPPORTED, "the logit softcap combines with causal and dense masks only "
-                                    "(not with sinks, ALiBi or structured masks)");
+  // (sinks and structured masks are bf16-only, checked above; the capped MFMA backward runs
+  // without a dense mask)
+  if (p->softcap > 0.f && (p->alibi || ((p->sinks || structured) && p->mask)))
+    return fail(FA_ERR_UNSUPPORTED, "the logit softcap does not combine with ALiBi, nor with sinks or "
+                                    "structured masks over a dense mask");
   if (p->mask) {
     if (p->mask_stride_q < p->Sk) return fail(FA_ERR_STRIDE, "mask_stride_q (%lld) < Sk", (long long)p->mask_stride_q);
     if (p->mask_stride_b < 0) return fail(FA_ERR_STRIDE, "mask_stride_b is negative");

@@ -167,8 +167,9 @@ typedef struct fa_attn_params {
      * included), and so does the bf16 backward without a dense mask (every work
      * decomposition); over a dense mask, and for fp32, the backward runs on the generic
      * kernels (its workspace is then the fp32 dQ accumulator, and the mask block map is not
-     * read). It combines with causal masking and dense masks (per-head ones included), not
-     * with sinks, ALiBi or structured masks (FA_ERR_UNSUPPORTED). */
+     * read). It combines with causal masking and dense masks (per-head ones included), and
+     * without a dense mask with sinks and structured masks; not with ALiBi, nor with sinks or
+     * structured masks over a dense mask (FA_ERR_UNSUPPORTED). */
     float softcap;
 } fa_attn_params;
 

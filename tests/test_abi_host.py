@@ -226,9 +226,10 @@ def test_window_conversions_reject():
 def test_softcap_params_rejected():
     L = B.lib()
     lse, dlt = lse_view(5), lse_view(6)
+    m = dict(mask=BASE + 11 * (1 << 24), mask_stride_q=64)
     bad = [(dict(softcap=-1.0), 2), (dict(softcap=float("inf")), 2), (dict(softcap=float("nan")), 2),
-           (dict(softcap=30.0, sinks=BASE + 7 * (1 << 24)), 7), (dict(softcap=30.0, alibi=BASE + 7 * (1 << 24)), 7),
-           (dict(softcap=30.0, window_left=8), 7), (dict(softcap=30.0, key_len=BASE + 7 * (1 << 24)), 7)]
+           (dict(softcap=30.0, alibi=BASE + 7 * (1 << 24)), 7), (dict(softcap=30.0, sinks=BASE + 7 * (1 << 24), **m), 7),
+           (dict(softcap=30.0, window_left=8, **m), 7), (dict(softcap=30.0, key_len=BASE + 7 * (1 << 24), **m), 7)]
     for kw, code in bad:
         p = params(**kw)
         assert L.fa_train_fwd(ctypes.byref(p), view(0), view(1, H=2), view(2, H=2), view(3), lse, None) == code, kw

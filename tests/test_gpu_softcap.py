@@ -123,3 +123,35 @@ def test_softcap_backward_decompositions(name, kv_split, q_split, q_split_tiles,
     got = {"O": host64(o), "LSE": host64(lse), "Delta": host64(delta), "dQ": host64(dq), "dK": host64(dk),
            "dV": host64(dv)}
     compare_full(c, got, ref)
+
+
+def test_softcap_with_sinks_and_structured_masks():
+    """Without a dense mask the cap combines with attention sinks and with structured masks (key
+    lengths, a sliding window): the capped MFMA kernels, against the oracle with the same sinks and
+    the structured mask written out densely."""
+    from flash_attention_train_amd.inputs import sink_logits
+    c = make_case("sinks_band", B=2, Hq=4, Hkv=2, Sq=200, Sk=200, D=128, dtype=BF16, seed=136)
+    cap, sinks = 2.0, sink_logits(137, 4)
+    key_len, window = [200, 160], (48, 48)  # every row keeps a visible key; keys past 160 are dead
+    say(f"case sinks_band (bf16): softcap {cap}, sinks {sinks}, key lengths {key_len}, window {window}")
+    dense = oracle.structured_mask(c.B, c.Sq, c.Sk, key_len=key_len, window_left=window[0], window_right=window[1])
+    ref = oracle.backward(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), dense, scale=c.scale, softcap=cap,
+                          sinks=sinks.astype(np.float64))
+    t = upload(c)
+    kl = torch.tensor(key_len, dtype=torch.int32, device="cuda")
+    sk = torch.from_numpy(sinks).cuda()
+    o, lse = binding.fwd(t["q"], t["k"], t["v"], scale=c.scale, softcap=cap, sinks=sk, key_len=kl, window=window)
+    delta = binding.bwd_preprocess(o, t["do"])
+    dq, dk, dv = binding.bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, scale=c.scale, softcap=cap, key_len=kl,
+                             window=window)
+    dsink = binding.bwd_sinks(lse, delta, sk)
+    torch.cuda.synchronize()
+    c.mask = dense.astype(np.float32)  # the dense form, for the exact-zero checks
+    got = {"O": host64(o), "LSE": host64(lse), "Delta": host64(delta), "dQ": host64(dq), "dK": host64(dk),
+           "dV": host64(dv)}
+    compare_full(c, got, ref)
+    # the sink gradient: a sum of terms of both signs, measured against the sum of their sizes
+    terms = np.exp(sinks.astype(np.float64)[None, :, None] - ref["LSE"]) * np.abs(ref["Delta"])
+    err = np.abs(dsink.cpu().numpy() - ref["dSink"]) / terms.sum(axis=(0, 2))
+    say(f"  dSink error against sum |terms|: {err.max():.2e}")
+    assert err.max() <= 2e-2
