@@ -70,6 +70,7 @@ class Workload:
         self.fwd_flops = accounting.fwd_flops(self.pairs, c.D)
         self.bwd_flops = accounting.bwd_flops(self.pairs, c.D)
         self.pre_bytes = accounting.preprocess_bytes(c.B, c.Hq, c.Sq, c.D, c.dtype)
+        self.step_bytes = accounting.step_bytes(c)
         dev = "cuda"
 
         def up(a):
@@ -106,7 +107,9 @@ class Workload:
                                                      q_offset=c.q_offset, mask=self.mask, softcap=self.softcap,
                                                      **self.sk)
         self.fws = torch.empty(max(self.fws_bytes, 256), dtype=torch.uint8, device=dev)
-        self.fwd_split = self.fws_bytes // (4 * c.B * c.Hq * c.Sq * (c.D + 2)) if self.fws_bytes else 1
+        # the split the library chose: its workspace holds splits * B * Hq * Sq * (2 D + 8) bytes,
+        # rounded up to 256
+        self.fwd_split = self.fws_bytes // (c.B * c.Hq * c.Sq * (2 * c.D + 8)) if self.fws_bytes else 1
         # backward split: the library's cost model, or (tune) the fastest of a few
         # settings timed once here on this workload, outside every timed region
         self.kv_split = self.q_split = self.q_split_tiles = 0
@@ -163,11 +166,12 @@ class Workload:
         self.bwd()
 
 
-def time_graph(w: Workload, steps: int, warmup: int) -> float:
+def time_graph(w: Workload, steps: int, warmup: int) -> dict:
     """Captures one whole step (mask map, forward, preprocess, backward: the same launches
-    as the eager step) in a HIP graph and times `steps` replays between synchronizes.
-    Returns ms per step. The graph removes the host's per-launch cost, which a training
-    loop that captures its attention layer does not pay either."""
+    as the eager step) in a HIP graph and times `steps` replays between synchronizes
+    (`ms`: wall clock over all of them), each replay also bracketed by HIP events on the
+    replay stream (`median_ms`, `min_ms`). The graph removes the host's per-launch cost,
+    which a training loop that captures its attention layer does not pay either."""
     import torch
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -181,11 +185,17 @@ def time_graph(w: Workload, steps: int, warmup: int) -> float:
     for _ in range(warmup):
         graph.replay()
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for e0, e1 in ev:
+        e0.record(stream)
         graph.replay()
+        e1.record(stream)
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    per = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    return {"ms": ms, "median_ms": float(np.median(per)), "min_ms": float(per.min())}
 
 
 def time_workload(w: Workload, steps: int, warmup: int, graph: bool = True) -> dict:
@@ -216,10 +226,13 @@ def time_workload(w: Workload, steps: int, warmup: int, graph: bool = True) -> d
     pre_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     bwd_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
     eager_ms = wall * 1e3 / steps
-    step_ms = time_graph(w, steps, warmup) if graph else eager_ms
+    g = time_graph(w, steps, warmup) if graph else {"ms": eager_ms, "median_ms": eager_ms, "min_ms": eager_ms}
+    step_ms = g["ms"]
     total_flops = w.fwd_flops + w.bwd_flops
     return {
         "ms_per_step": step_ms,
+        "step_ms_median": g["median_ms"], "step_ms_min": g["min_ms"],
+        "tflops_at_median": total_flops / (g["median_ms"] * 1e-3) / 1e12,
         "timing": "hip graph replay of the whole step" if graph else "eager launches",
         "eager_ms_per_step": eager_ms,
         "eager_tflops": total_flops / (eager_ms * 1e-3) / 1e12,
@@ -230,6 +243,9 @@ def time_workload(w: Workload, steps: int, warmup: int, graph: bool = True) -> d
         "bwd_tflops": w.bwd_flops / (bwd_ms.mean() * 1e-3) / 1e12,
         "fwdbwd_event_tflops": total_flops / ((fwd_ms + pre_ms + bwd_ms).mean() * 1e-3) / 1e12,
         "pre_gbs": w.pre_bytes / (pre_ms.mean() * 1e-3) / 1e9,
+        "pre_hbm_frac": w.pre_bytes / (pre_ms.mean() * 1e-3) / 1e9 / 8000.0,
+        "step_bytes": w.step_bytes,
+        "step_hbm_frac": w.step_bytes / (step_ms * 1e-3) / 8e12,
         "pairs": w.pairs,
         "fwd_split": w.fwd_split,
         "bwd_splits": [w.kv_split, w.q_split, w.q_split_tiles],
@@ -377,6 +393,13 @@ def cpu_baseline(key: str, min_seconds: float = 10.0, max_reps: int = 8) -> dict
         oracle.backward(*args, scale=c.scale, causal=c.causal, q_offset=c.q_offset, threads=threads)
         dt += time.perf_counter() - t0
         reps += 1
+    # the forward alone (O and LSE), timed the same way over a shorter budget
+    freps, fdt = 0, 0.0
+    while freps < max_reps and (freps == 0 or fdt < min_seconds / 3):
+        t0 = time.perf_counter()
+        oracle.forward(*args[:3], args[4], scale=c.scale, causal=c.causal, q_offset=c.q_offset, threads=threads)
+        fdt += time.perf_counter() - t0
+        freps += 1
     n = accounting.case_pairs(c)
     flops = reps * (accounting.fwd_flops(n, c.D) + accounting.bwd_flops(n, c.D))
     cpu = platform.processor() or "unknown"
@@ -389,8 +412,10 @@ def cpu_baseline(key: str, min_seconds: float = 10.0, max_reps: int = 8) -> dict
     except OSError:
         pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} whole fwd+bwd step(s) of the {key} workload (all heads), float64, {dt:.1f} s",
-            "seconds": dt, "cpu": cpu}
+            "sample": f"{reps} whole fwd+bwd step(s) of the {key} workload (all heads), float64, {dt:.1f} s; "
+                      f"forward alone: {freps} call(s), {fdt:.1f} s",
+            "seconds": dt, "fwd_value": freps * accounting.fwd_flops(n, c.D) / fdt / 1e12,
+            "fwd_seconds": fdt, "cpu": cpu}
 
 
 def main():
@@ -425,6 +450,10 @@ def main():
         we = Workload(key, args.splits if "x" not in args.splits else "table")
         re_ = time_workload(we, max(5, args.steps // 2), args.warmup, graph=not args.eager)
         re_["pct_of_peak"] = 100.0 * re_["tflops"] / accounting.MI355X_BF16_DENSE_TFLOPS
+        # near the ridge (few keys per row): the step against the HBM roofline as well
+        re_["hbm_roofline"] = {"bytes_per_step": we.step_bytes, "achieved_gbs": we.step_bytes / (re_["ms_per_step"] * 1e-3) / 1e9,
+                               "peak_gbs": accounting.MI355X_HBM_GBS,
+                               "frac": we.step_bytes / (re_["ms_per_step"] * 1e-3) / 1e9 / accounting.MI355X_HBM_GBS}
         extra[key] = re_
         log(f"[bench] {key}: {re_['ms_per_step']:.3f} ms/step, {re_['tflops']:.1f} TFLOP/s")
         del we

@@ -96,3 +96,21 @@ def chunked_pairs(Hq: int, W: int, chunk: int) -> int:
     """Unmasked pairs of the causal walk over a W-long window in chunks (equals one-shot causal)."""
     return Hq * sum(int(np.clip(np.arange(chunk) + p0 + 1, 0, p0 + chunk).sum())
                     for p0 in range(0, W, chunk))
+
+
+def step_bytes(c: Case, mask_passes: int = 3) -> int:
+    """Algorithmic HBM bytes of one training step of the op as it is split into passes:
+    the forward reads Q, K, V and writes O and the LSE; the preprocess reads O and dO and
+    writes Delta; the backward reads Q, K, V, dO, the LSE and Delta and writes dQ, dK and
+    dV. A dense mask is read once by each of `mask_passes` passes (the block map, the
+    forward, the backward). Each tensor counts once per pass that needs it; nothing a
+    kernel re-reads counts twice."""
+    e = elt_bytes(c.dtype)
+    q = c.B * c.Hq * c.Sq * c.D * e
+    kv = c.B * c.Hkv * c.Sk * c.D * e
+    row = 4 * c.B * c.Hq * c.Sq
+    mask = 0 if c.mask is None else int(np.prod(c.mask.shape)) * 4
+    fwd = q + 2 * kv + q + row
+    pre = 2 * q + row
+    bwd = q + 2 * kv + q + 2 * row + q + 2 * kv
+    return int(fwd + pre + bwd + mask_passes * mask)

@@ -119,6 +119,47 @@ def view3(t: torch.Tensor) -> FaView:
     return FaView(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
 
 
+def _expect(name: str, t, *, dtype=None, shape=None) -> None:
+    """Type, dtype and shape of one tensor argument. The C ABI takes bare pointers and
+    cannot see a tensor's size, type or residency, so a short or mistyped tensor would
+    reach the kernels as an out-of-bounds address: every entry point checks its
+    arguments here, then their residency (`_resident`), before any launch."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _resident(device, **named) -> None:
+    """Every given tensor (None skipped) is device memory on `device`."""
+    for name, t in named.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor (it is on {t.device})")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
+
+
+def _check_qkv(q, k, v) -> None:
+    """q [B, Hq, Sq, D] in bf16 or fp32; k and v [B, Hkv, Sk, D] in q's dtype."""
+    _expect("q", q, dtype=(torch.bfloat16, torch.float32))
+    if q.dim() != 4:
+        raise ValueError("q must be [B, Hq, Sq, D]")
+    _expect("k", k, dtype=q.dtype)
+    if k.dim() != 4 or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected [B={q.shape[0]}, Hkv, Sk, D={q.shape[3]}]")
+    _expect("v", v, dtype=q.dtype, shape=k.shape)
+
+
+def _check_rowstats(q, **named) -> None:
+    """fp32 [B, Hq, Sq] row statistics (LSE, Delta) beside q."""
+    for name, t in named.items():
+        _expect(name, t, dtype=torch.float32, shape=q.shape[:3])
+
+
 def _stream_handle(stream) -> int:
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
@@ -169,6 +210,9 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
         if mask_tiles is not None:
             if mask_tiles.dtype != torch.uint8 or not mask_tiles.is_contiguous():
                 raise ValueError("mask_tiles must be a contiguous uint8 tensor from mask_tile_map()")
+            need = int(lib().fa_train_mask_tiles_bytes(ctypes.byref(p)))
+            if mask_tiles.numel() < need:
+                raise ValueError(f"mask_tiles holds {mask_tiles.numel()} bytes; this mask's map needs {need}")
             p.mask_tiles = mask_tiles.data_ptr()
     elif mask_tiles is not None:
         raise ValueError("mask_tiles given without a mask")
@@ -182,10 +226,12 @@ def mask_tile_map(mask: torch.Tensor, q: torch.Tensor, k: torch.Tensor, *, strea
     through their ``mask_tiles`` argument. The first ``mask_tile_count`` bytes are the classes.
     ``out`` (uint8, at least the map's size) is filled instead of a new tensor."""
     p = make_params(q, k, scale=None, causal=False, q_offset=0, mask=mask)
+    _resident(q.device, q=q, k=k, mask=mask)
     n = int(lib().fa_train_mask_tiles_bytes(ctypes.byref(p)))
     if out is not None:
         if out.dtype != torch.uint8 or not out.is_contiguous() or out.numel() < n:
             raise ValueError(f"out must be a contiguous uint8 tensor of at least {n} bytes")
+        _resident(q.device, out=out)
         tiles = out
     else:
         tiles = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
@@ -214,6 +260,7 @@ def fwd(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, out=None
     choice; 1: never), with `workspace` (allocated here when None and needed). ``sinks``:
     optional fp32 [Hq] attention-sink logits; ``alibi``: fp32 [Hq] slopes; ``softcap``: a
     logit softcap c > 0 (0 = none)."""
+    _check_qkv(q, k, v)
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, fwd_variant=variant,
                     mask_tiles=mask_tiles, fwd_split=split, key_len=key_len, q_len=q_len, window=window,
                     sinks=sinks, alibi=alibi, softcap=softcap)
@@ -221,6 +268,10 @@ def fwd(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, out=None
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _expect("out", out, dtype=q.dtype, shape=q.shape)
+    _check_rowstats(q, lse=lse)
+    _resident(q.device, q=q, k=k, v=v, out=out, lse=lse, workspace=workspace, mask=mask, mask_tiles=mask_tiles,
+              key_len=key_len, q_len=q_len, sinks=sinks, alibi=alibi)
     need = int(lib().fa_train_fwd_workspace_bytes(ctypes.byref(p)))
     if need == ctypes.c_size_t(-1).value:
         need = 0  # invalid parameters: the call itself reports why
@@ -233,11 +284,39 @@ def fwd(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, out=None
     return out, lse
 
 
+def fwd_unsplit(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, out=None, lse=None, stream=None,
+                variant=0, mask_tiles=None, key_len=None, q_len=None, window=(-1, -1), sinks=None, alibi=None,
+                softcap=0.0):
+    """Forward through fa_train_fwd, the entry point without a workspace: the same results as
+    fwd() (O, LSE), but every query tile's key walk stays in one workgroup."""
+    _check_qkv(q, k, v)
+    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, fwd_variant=variant,
+                    mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, window=window, sinks=sinks, alibi=alibi,
+                    softcap=softcap)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _expect("out", out, dtype=q.dtype, shape=q.shape)
+    _check_rowstats(q, lse=lse)
+    _resident(q.device, q=q, k=k, v=v, out=out, lse=lse, mask=mask, mask_tiles=mask_tiles, key_len=key_len,
+              q_len=q_len, sinks=sinks, alibi=alibi)
+    _check("fa_train_fwd", lib().fa_train_fwd(ctypes.byref(p), view4(q), view4(k), view4(v), view4(out), view3(lse),
+                                              _stream_handle(stream)))
+    return out, lse
+
+
 def bwd_preprocess(o, dout, *, delta=None, stream=None):
     """Delta = rowsum(dO * O) in fp32, [B, Hq, Sq]."""
+    _expect("o", o, dtype=(torch.bfloat16, torch.float32))
+    if o.dim() != 4:
+        raise ValueError("o must be [B, Hq, Sq, D]")
+    _expect("dout", dout, dtype=o.dtype, shape=o.shape)
     B, Hq, Sq, D = o.shape
     if delta is None:
         delta = torch.empty((B, Hq, Sq), dtype=torch.float32, device=o.device)
+    _check_rowstats(o, delta=delta)
+    _resident(o.device, o=o, dout=dout, delta=delta)
     p = FaAttnParams(B, Hq, Hq, Sq, Sq, D, _dtype_code(o), 0, 0, 1.0, None, 0, 0, None, 0, 0, 0)
     _check("fa_train_bwd_preprocess",
            lib().fa_train_bwd_preprocess(ctypes.byref(p), view4(o), view4(dout), view3(delta), _stream_handle(stream)))
@@ -247,11 +326,17 @@ def bwd_preprocess(o, dout, *, delta=None, stream=None):
 def bwd_sinks(lse, delta, sinks, *, dsink=None, stream=None):
     """Gradient of the attention sinks, ADDED into ``dsink`` (fp32 [Hq]; a zeroed one is made when
     None): dsink[h] += -sum over the head's rows of exp(sinks[h] - LSE) * Delta."""
+    _expect("lse", lse, dtype=torch.float32)
+    if lse.dim() != 3:
+        raise ValueError("lse must be [B, Hq, Sq]")
+    _expect("delta", delta, dtype=torch.float32, shape=lse.shape)
     B, Hq, Sq = lse.shape
     if dsink is None:
         dsink = torch.zeros(Hq, dtype=torch.float32, device=lse.device)
     if sinks.dtype != torch.float32 or sinks.shape != (Hq,) or not sinks.is_contiguous():
         raise ValueError("sinks must be a contiguous fp32 [Hq] tensor on the device")
+    _expect("dsink", dsink, dtype=torch.float32, shape=(Hq,))
+    _resident(lse.device, lse=lse, delta=delta, sinks=sinks, dsink=dsink)
     p = FaAttnParams(B, Hq, Hq, Sq, Sq, 64, FA_BF16, 0, 0, 1.0)
     p.window_left = p.window_right = -1
     p.sinks = sinks.data_ptr()
@@ -265,11 +350,15 @@ def dequant_q8_0(qs, d, *, out=None, stream=None):
     (views with a contiguous last dimension). Writes ``out`` (bf16 [B, H, S, D], made when None)."""
     if qs.dtype != torch.int8 or d.dtype != torch.float16:
         raise TypeError("qs must be int8 and d float16")
+    if qs.dim() != 4:
+        raise ValueError("qs must be [B, H, S, D]")
     B, H, S, D = qs.shape
     if tuple(d.shape) != (B, H, S, D // 32):
         raise ValueError("d must be [B, H, S, D / 32]")
     if out is None:
         out = torch.empty(qs.shape, dtype=torch.bfloat16, device=qs.device)
+    _expect("out", out, dtype=torch.bfloat16, shape=qs.shape)
+    _resident(qs.device, qs=qs, d=d, out=out)
     _check("fa_train_dequant_q8_0", lib().fa_train_dequant_q8_0(B, H, S, D, view4(qs), view4(d), view4(out),
                                                                 _stream_handle(stream)))
     return out
@@ -285,6 +374,10 @@ def convert_f16(src, *, out=None, dtype=None, stream=None):
         out = torch.empty(src.shape, dtype=dtype or torch.bfloat16, device=src.device)
     if out.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out must be float32 or bfloat16")
+    if src.dim() != 4:
+        raise ValueError("src must be [B, H, S, D]")
+    _expect("out", out, shape=src.shape)
+    _resident(src.device, src=src, out=out)
     Bn, H, S, D = src.shape
     _check("fa_train_convert_f16", lib().fa_train_convert_f16(Bn, H, S, D, view4(src), view4(out),
                                                               FA_F32 if out.dtype == torch.float32 else FA_BF16,
@@ -306,6 +399,8 @@ def _workspace(p: FaAttnParams, device, workspace):
         need = 0  # invalid parameters: the call itself reports why
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    else:
+        _resident(device, workspace=workspace)
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -313,12 +408,20 @@ def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_off
         dv=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None, q_len=None,
         window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0):
     """Backward: returns (dQ, dK, dV), each in q's dtype, overwritten."""
+    _check_qkv(q, k, v)
+    _expect("dout", dout, dtype=q.dtype, shape=q.shape)
+    _check_rowstats(q, lse=lse, delta=delta)
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, window=window,
                     dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles, softcap=softcap)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    _expect("dq", dq, dtype=q.dtype, shape=q.shape)
+    _expect("dk", dk, dtype=q.dtype, shape=k.shape)
+    _expect("dv", dv, dtype=q.dtype, shape=k.shape)
+    _resident(q.device, q=q, k=k, v=v, dout=dout, lse=lse, delta=delta, dq=dq, dk=dk, dv=dv, mask=mask,
+              mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, alibi=alibi)
     ws, nbytes = _workspace(p, q.device, workspace)
     _check("fa_train_bwd", lib().fa_train_bwd(ctypes.byref(p), view4(q), view4(k), view4(v), view4(dout), view3(lse),
                                               view3(delta), view4(dq), view4(dk), view4(dv), ws.data_ptr(), nbytes,
@@ -369,13 +472,23 @@ def bwd_chunked(q, k, v, dout, lse, delta, dk_acc, dv_acc, *, mask=None, scale=N
                 q_len=None, window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0):
     """Chunked backward: returns dQ for the chunk; ADDS dK/dV into the fp32 window
     accumulators ``dk_acc`` / ``dv_acc`` ([B, Hkv, >= Sk, D])."""
+    _check_qkv(q, k, v)
+    _expect("dout", dout, dtype=q.dtype, shape=q.shape)
+    _check_rowstats(q, lse=lse, delta=delta)
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len,
                     q_len=q_len, window=window, dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles,
                     softcap=softcap)
     if dk_acc.dtype != torch.float32 or dv_acc.dtype != torch.float32:
         raise TypeError("the window accumulators must be float32")
+    B, Hkv, Sk, D = k.shape
+    for name, acc in (("dk_acc", dk_acc), ("dv_acc", dv_acc)):
+        if acc.dim() != 4 or acc.shape[0] != B or acc.shape[1] != Hkv or acc.shape[2] < Sk or acc.shape[3] != D:
+            raise ValueError(f"{name} has shape {tuple(acc.shape)}, expected [{B}, {Hkv}, >= {Sk}, {D}]")
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    _expect("dq", dq, dtype=q.dtype, shape=q.shape)
+    _resident(q.device, q=q, k=k, v=v, dout=dout, lse=lse, delta=delta, dq=dq, dk_acc=dk_acc, dv_acc=dv_acc,
+              mask=mask, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, alibi=alibi)
     ws, nbytes = _workspace(p, q.device, workspace)
     _check("fa_train_bwd_chunked",
            lib().fa_train_bwd_chunked(ctypes.byref(p), view4(q), view4(k), view4(v), view4(dout), view3(lse),

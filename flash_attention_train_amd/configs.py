@@ -55,7 +55,7 @@ WORKLOADS = {
                                "64 chunks of 512, Hq=16 Hkv=4 D=128", 9),
     # the same walk over an fp16-stored window: the K/V draws rounded once to fp16
     # the LM layer with a logit softcap of 50 (the pages give no value; the cost does not depend
-    # on it): it runs on the generic kernels
+    # on it): the bf16 MFMA forward and backward with their cap variants
     "lm_softcap": Workload("lm_softcap", "LM causal GQA with logit softcap 50, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16",
                            12),
     "long_window_f16": Workload("long_window_f16", "long-window chunked walk over an f16 K/V window, W=32768, "

@@ -191,8 +191,9 @@ fa_status check_alias(const Extent* outs, int n_out, const char* const* out_name
 size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
 // Split factors of the bf16 backward. Each split > 1 spreads one tile's walk over
-// several workgroups whose partial sums meet in fp32 atomics, so splits are only
-// used when the unsplit grid would leave compute units idle.
+// several workgroups, each storing its fp32 partial sums into a slice of its own in the
+// workspace; a reduce pass then sums the slices. Splits are only used when the unsplit
+// grid would leave compute units idle.
 // Predicted time (us) of the bf16 backward for one split choice. The workgroups are
 // taken in dispatch order (dK/dV units by key tile, longest causal walks first, then
 // dQ units, longest first), each costed by its walk length, and placed greedily on

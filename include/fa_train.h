@@ -115,7 +115,8 @@ typedef struct fa_attn_params {
                              which tiles are split: q_split_tiles below */
     int32_t fwd_split;    /* bf16 forward through fa_train_fwd_ws: workgroups sharing one
                              128-row query tile's key walk, 1 .. 64 (> 1: each stores its
-                             unnormalised fp32 rows in the workspace and a merge pass
+                             rows normalised by its own row sum, in bf16, with their fp32
+                             exponent base and row sum, in the workspace, and a merge pass
                              combines them). fa_train_fwd never splits and rejects > 1. */
     /* Structured masks (bf16 only; they combine with causal and with a dense mask): the
      * per-element padding and sliding-window masks of the pages' DiT batches ("sa" =

@@ -2,11 +2,12 @@
 times (automatic decomposition, mask tile maps for masked workloads):
 
 * DiT self-attention and DiT cross-attention: every output against the whole oracle;
-* LM causal: sampled query rows (O, LSE, Delta, dQ) and sampled key columns (dK, dV)
-  that the oracle computes one by one;
+* LM causal: every output against the whole oracle;
 * long-window chunked walk (64 chunks of 512 over a 32768-key window, fp32 dK/dV
-  accumulators): sampled rows of every chunk, sampled late key columns, and the
-  column-sum identities sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i, which hold at any size.
+  accumulators): a row of every chunk, key columns spread over the whole window (so
+  that each sums the contributions of many chunks), and the column-sum identities
+  sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i, which hold at any size;
+* the LM layer with sinks, ALiBi or a softcap: sampled rows and key columns.
 """
 from __future__ import annotations
 
@@ -109,24 +110,16 @@ def _check_cols(c, got_dk, got_dv, ids, ref, tol):
         assert e <= tol, n
 
 
-def test_lm_causal_full_size_sampled():
+def test_lm_causal_full_size_every_element():
+    """The LM layer (B=1, Hq=32, Hkv=8, S=4096, D=128, causal) as the bench runs it: every output
+    against the whole oracle (about 0.5 TFLOP of float64 work on the host cores)."""
     c = configs.make("lm_causal")
-    say("lm_causal: full size, sampled rows and columns")
+    say(f"lm_causal: full size B={c.B} Hq={c.Hq} Hkv={c.Hkv} S={c.Sq}; GPU step")
     got = _run_with_tiles(c, upload(c))
-    rng = np.random.default_rng(4)
-    rows = np.unique(np.concatenate([
-        [0, 1, c.Sq - 1],                                   # first rows (one visible key), last row
-        [(h * c.Sq) + i for h in (5, 31) for i in (0, 63, 64, 4095)],
-        rng.choice(c.Hq * c.Sq, 120, replace=False)]).astype(np.int64))
-    ref = oracle.rows(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), rows, scale=c.scale, causal=True,
-                      q_offset=0)
-    _check_rows(c, got, rows, ref, TOL[c.dtype])
-    cols = np.unique(np.concatenate([
-        [0, 1, c.Sk - 1, 3 * c.Sk + 2047],                  # KV head 0 and 3
-        rng.choice(np.arange(2 * c.Sk, 3 * c.Sk), 12, replace=False)]).astype(np.int64))  # KV head 2
-    refc = oracle.cols(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), cols, scale=c.scale, causal=True,
-                       q_offset=0)
-    _check_cols(c, got["dK"], got["dV"], cols, refc, TOL[c.dtype])
+    say("lm_causal: whole oracle running (tens of seconds)")
+    ref = oracle.backward(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), None, scale=c.scale, causal=True,
+                          q_offset=0)
+    compare_full(c, got, ref)
 
 
 def run_walk(c, t, W, C):
@@ -151,24 +144,33 @@ def run_walk(c, t, W, C):
 
 
 def test_long_window_walk_full_size():
+    """The 64-chunk walk over the 32768-key window against the one-shot oracle: a query row from every
+    chunk in two heads plus random rows (O, LSE, Delta, dQ); key columns spread over the whole window
+    in two KV heads, one in every 2048 keys, so that early columns hold fp32 sums over up to 64 chunks
+    (dK, dV); and the column-sum identities over the whole window."""
     W, C = configs.LONG_WINDOW, configs.LONG_CHUNK
     c = configs.make("long_window")
-    say(f"long_window: 64-chunk walk over W={W}, sampled rows/columns + column-sum identities")
+    say(f"long_window: 64-chunk walk over W={W}; GPU walk")
     got = run_walk(c, upload(c), W, C)
     rng = np.random.default_rng(5)
+    nchunk = W // C
+    every_chunk = [h * W + C * k + int(rng.integers(C)) for h in (0, 13) for k in range(nchunk)]
     rows = np.unique(np.concatenate([
-        [0, 511, 512, 32767, 5 * W + 16384],
+        [0, 511, 512, 32767, 5 * W + 16384], every_chunk,
         rng.choice(c.Hq * W, 96, replace=False)]).astype(np.int64))
+    say(f"    oracle rows ({rows.size})")
     ref = oracle.rows(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), rows, scale=c.scale, causal=True,
                       q_offset=0)
     _check_rows(c, got, rows, ref, TOL[c.dtype])
-    cols = np.unique(np.concatenate([
-        [W - 1, W - 512, 3 * W + W - 1],
-        rng.choice(np.arange(W - 384, W), 6, replace=False),
-        rng.choice(np.arange(2 * W + W - 256, 3 * W), 4, replace=False)]).astype(np.int64))
-    refc = oracle.cols(c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do"), cols, scale=c.scale, causal=True,
-                       q_offset=0)
-    _check_cols(c, got["dK"], got["dV"], cols, refc, TOL[c.dtype])
+    q64, k64, v64, do64 = c.f64("q"), c.f64("k"), c.f64("v"), c.f64("do")
+    for g in (0, 3):
+        # column 0 (seen by every row of the group), one column in each 2048 keys, the last key
+        js = np.unique(np.concatenate([[0, W - 1], 2048 * np.arange(W // 2048) + rng.integers(2048, size=W // 2048)]))
+        cols = (g * W + js).astype(np.int64)
+        say(f"    oracle key columns of KV head {g} ({cols.size}, from key {js.min()} to {js.max()}; "
+            f"about a minute of host time)")
+        refc = oracle.cols(q64, k64, v64, do64, cols, scale=c.scale, causal=True, q_offset=0)
+        _check_cols(c, got["dK"], got["dV"], cols, refc, TOL[c.dtype])
     # identities over the whole window, per KV head and feature
     do = c.f64("do")
     G = c.Hq // c.Hkv
@@ -245,7 +247,7 @@ def test_lm_alibi_full_size_sampled():
 
 
 def test_lm_softcap_full_size_sampled():
-    """The LM layer with a logit softcap, as the bench runs it (the generic kernels): sampled rows
+    """The LM layer with a logit softcap, as the bench runs it (the MFMA kernels' cap variants): sampled rows
     (O, LSE, Delta, dQ) and key columns (dK, dV) against the oracle with the same cap."""
     c = configs.make("lm_softcap")
     cap = c.meta["softcap"]

@@ -60,8 +60,8 @@ def test_parity_small(name):
 
 
 def test_deterministic_outputs():
-    """With unsplit backward work nothing is written with atomics: two runs agree bitwise
-    on every output (split work sums partials with fp32 atomics, in any order)."""
+    """With unsplit backward work every output is stored once by one workgroup: two runs
+    agree bitwise on every output (split work also sums fixed fp32 slices in a fixed order)."""
     c = CASES["dit_ca_ragged"]()
     t = upload(c)
 
@@ -185,6 +185,26 @@ def test_forward_splits(name, split):
     O, L = oracle.forward(c.f64("q"), c.f64("k"), c.f64("v"), m, scale=c.scale, causal=c.causal,
                           q_offset=c.q_offset)
     compare_full(c, {"O": host64(o), "LSE": host64(lse)}, {"O": O, "LSE": L}, names=("O", "LSE"))
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "d128_f32_causal", "f32_d64_gqa_mask", "dit_sa_ragged", "dit_ca_ragged",
+                                  "lm_causal_gqa4", "chunk_offset", "single_query_single_key"])
+def test_forward_entry_without_workspace(name):
+    """fa_train_fwd itself (the forward entry point that takes no workspace), bf16 and fp32, against
+    the oracle; and the same bits as fa_train_fwd_ws with the split pinned to 1."""
+    c = CASES[name]()
+    say(f"case {name}: fa_train_fwd, B={c.B} Hq={c.Hq} Hkv={c.Hkv} Sq={c.Sq} Sk={c.Sk} D={c.D} {c.dtype}")
+    t = upload(c)
+    o, lse = binding.fwd_unsplit(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
+                                 q_offset=c.q_offset)
+    o1, lse1 = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
+                           q_offset=c.q_offset, split=1)
+    torch.cuda.synchronize()
+    m = None if c.mask is None else c.mask.astype(np.float64)
+    O, L = oracle.forward(c.f64("q"), c.f64("k"), c.f64("v"), m, scale=c.scale, causal=c.causal,
+                          q_offset=c.q_offset)
+    compare_full(c, {"O": host64(o), "LSE": host64(lse)}, {"O": O, "LSE": L}, names=("O", "LSE"))
+    assert torch.equal(o, o1) and torch.equal(lse, lse1)
 
 
 def test_forward_split_hint_ignored_for_fp32():
