@@ -60,6 +60,7 @@ SIGNATURES = {
     "fa_train_bwd": ([_PP, _PV, _PV, _PV, _PV, _PV, _PV, _PV, _PV, _PV, _VP, ctypes.c_size_t, _VP], ctypes.c_int),
     "fa_train_bwd_chunked": ([_PP, _PV, _PV, _PV, _PV, _PV, _PV, _PV, _PV, _PV, _VP, ctypes.c_size_t, _VP],
                              ctypes.c_int),
+    "fa_train_bwd_noalloc": ([_PP, _PV, _PV, _PV, _PV, _PV, _PV, _PV, _PV, _PV, _VP], ctypes.c_int),
     "fa_train_status_str": ([ctypes.c_int], ctypes.c_char_p),
     "fa_train_last_error": ([], ctypes.c_char_p),
     "fa_train_version": ([], ctypes.c_int),
@@ -427,6 +428,35 @@ def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_off
                                               view3(delta), view4(dq), view4(dk), view4(dv), ws.data_ptr(), nbytes,
                                               _stream_handle(stream)))
     return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_offset=None, dq=None,
+                dk=None, dv=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None, q_len=None,
+                window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0):
+    """Backward through fa_train_bwd_noalloc: the results of bwd(), with the workspace taken from
+    the library's static device scratch instead of an allocation (dQ, dK and dV are still the
+    caller's; pass them to allocate nothing here either)."""
+    _check_qkv(q, k, v)
+    _expect("dout", dout, dtype=q.dtype, shape=q.shape)
+    _check_rowstats(q, lse=lse, delta=delta)
+    p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
+                    q_split=q_split, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, window=window,
+                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles, softcap=softcap)
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    _expect("dq", dq, dtype=q.dtype, shape=q.shape)
+    _expect("dk", dk, dtype=q.dtype, shape=k.shape)
+    _expect("dv", dv, dtype=q.dtype, shape=k.shape)
+    _resident(q.device, q=q, k=k, v=v, dout=dout, lse=lse, delta=delta, dq=dq, dk=dk, dv=dv, mask=mask,
+              mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, alibi=alibi)
+    _check("fa_train_bwd_noalloc",
+           lib().fa_train_bwd_noalloc(ctypes.byref(p), view4(q), view4(k), view4(v), view4(dout), view3(lse),
+                                      view3(delta), view4(dq), view4(dk), view4(dv), _stream_handle(stream)))
+    return dq, dk, dv
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # FA_TRAIN_NOALLOC_SCRATCH_BYTES
 
 
 BWD_SPLIT_CANDIDATES = ((0, 0), (1, 1), (2, 1), (4, 1), (8, 1), (1, 2), (2, 2), (4, 2))

@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <functional>
+#include <mutex>
 #include <queue>
 #include <vector>
 
@@ -355,11 +356,44 @@ WsLayout workspace_layout(const fa_attn_params* p, bool accumulate) {
 
 size_t workspace_bytes(const fa_attn_params* p) { return workspace_layout(p, false).total; }
 
-// Shared body of the two backward entry points.
+// Scratch memory of fa_train_bwd_noalloc, for callers that cannot allocate: the
+// workspace of the backward (split walks' fp32 slices, or the fp32 path's dQ
+// accumulator) lives in this static device array instead of a caller-owned buffer.
+// Every device the library runs on holds its own copy until the process ends. In host
+// code `scratch` names a host-side stand-in, not the device copy: the device address
+// is looked up once per device with hipGetSymbolAddress and only that address is ever
+// handed to kernels.
+static __device__ __align__(256) char scratch[FA_TRAIN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the first call on
+// that device, with it current).
+fa_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_HIP, "device %d beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(FA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+// Shared body of the backward entry points. use_scratch: the workspace is the current
+// device's static scratch array (fa_train_bwd_noalloc), looked up after every host check.
 fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,
                      const fa_view* dout, const fa_view* lse, const fa_view* delta, const fa_view* dq,
                      const fa_view* dk, const fa_view* dv, void* workspace, size_t workspace_bytes_given,
-                     hipStream_t stream, bool accumulate) {
+                     hipStream_t stream, bool accumulate, bool use_scratch = false) {
   fa_status s = check_params(p);
   if (s) return s;
   const int elt = elt_of(p);
@@ -378,14 +412,18 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   if ((s = check_view(dv, accumulate ? "dv_acc" : "dv", p->B, p->Hkv, p->Sk, p->D, gelt, true, true, &edv))) return s;
   const WsLayout wl = workspace_layout(p, accumulate);
   const size_t need = wl.total;
-  if (need > 0) {
+  if (use_scratch) {
+    if (need > (size_t)FA_TRAIN_NOALLOC_SCRATCH_BYTES)
+      return fail(FA_ERR_WORKSPACE, "this backward needs %zu bytes of scratch; the static array holds %zu",
+                  need, (size_t)FA_TRAIN_NOALLOC_SCRATCH_BYTES);
+  } else if (need > 0) {
     if (!workspace) return fail(FA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
     if (workspace_bytes_given < need)
       return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_given, need);
     if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(FA_ERR_ALIGN, "workspace is not 256-byte aligned");
   }
   const uintptr_t wlo = reinterpret_cast<uintptr_t>(workspace);
-  Extent ews = {wlo, wlo + need};
+  Extent ews = {wlo, use_scratch ? wlo : wlo + need};  // (the static array is nobody else's memory)
   Extent ins[8] = {eq, ek, ev, edo, el, ed, {0, 0}, {0, 0}};
   const char* in_names[8] = {"q", "k", "v", "dout", "lse", "delta", "mask", "-"};
   int n_in = 6;
@@ -393,6 +431,10 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   Extent outs[4] = {edq, edk, edv, ews};
   const char* out_names[4] = {"dq", accumulate ? "dk_acc" : "dk", accumulate ? "dv_acc" : "dv", "workspace"};
   if ((s = check_alias(outs, 4, out_names, ins, n_in, in_names))) return s;
+  if (use_scratch && need > 0) {
+    if ((s = scratch_of_current_device(&workspace))) return s;
+    workspace_bytes_given = FA_TRAIN_NOALLOC_SCRATCH_BYTES;
+  }
 
   fa::BwdArgs a;
   a.a = shape_of(p);
@@ -731,6 +773,13 @@ fa_status fa_train_bwd(const fa_attn_params* p, const fa_view* q, const fa_view*
                        hipStream_t stream) {
   g_err[0] = 0;
   return bwd_common(p, q, k, v, dout, lse, delta, dq, dk, dv, workspace, workspace_bytes_given, stream, false);
+}
+
+fa_status fa_train_bwd_noalloc(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,
+                               const fa_view* dout, const fa_view* lse, const fa_view* delta, const fa_view* dq,
+                               const fa_view* dk, const fa_view* dv, hipStream_t stream) {
+  g_err[0] = 0;
+  return bwd_common(p, q, k, v, dout, lse, delta, dq, dk, dv, nullptr, 0, stream, false, true);
 }
 
 fa_status fa_train_bwd_chunked(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,

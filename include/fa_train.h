@@ -231,6 +231,27 @@ fa_status fa_train_bwd_chunked(const fa_attn_params* p, const fa_view* q, const 
                                const fa_view* dq, const fa_view* dk_acc, const fa_view* dv_acc,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Size of the static scratch array behind fa_train_bwd_noalloc (64 MiB per device). */
+#define FA_TRAIN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* fa_train_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight training loops, harnesses that forbid allocation): the same
+ * arguments, checks and results, but no workspace argument. The backward's workspace
+ * (see fa_train_bwd_workspace_bytes: the split walks' fp32 slices, or the fp32 path's
+ * dQ accumulator, which it clears itself with a kernel) is taken from a static device
+ * array of FA_TRAIN_NOALLOC_SCRATCH_BYTES bytes that the library holds on every device
+ * it runs on until the process ends; its device address is looked up on the first
+ * call on each device, with that device current. Nothing is allocated or freed, by
+ * the library or by any library it calls. A problem whose workspace would exceed the
+ * array is rejected with FA_ERR_WORKSPACE before anything is launched (a smaller
+ * kv_split / q_split hint, or fa_train_bwd with a caller-owned workspace, serves it).
+ * Every call on one device shares that device's array and the array keeps the last
+ * call's contents, so calls that may overlap on one device (on different streams, or
+ * from different host threads without ordering) race: order them on one stream. */
+fa_status fa_train_bwd_noalloc(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,
+                               const fa_view* dout, const fa_view* lse, const fa_view* delta, const fa_view* dq,
+                               const fa_view* dk, const fa_view* dv, hipStream_t stream);
+
 /* Mask block classes written by fa_train_mask_tiles. */
 #define FA_TILE_DEAD 0  /* every entry of the block is -inf */
 #define FA_TILE_OPEN 1  /* every entry of the block is exactly 0 */

@@ -247,3 +247,30 @@ def test_softcap_params_rejected():
     assert L.fa_train_fwd_workspace_bytes(ctypes.byref(params(**long_keys))) == \
         L.fa_train_fwd_workspace_bytes(ctypes.byref(params(Sk=4096))) > 0
     assert L.fa_train_fwd_workspace_bytes(ctypes.byref(params(dtype=B.FA_F32, **long_keys))) == 0
+
+
+def test_backward_noalloc_rejects_before_any_launch():
+    """fa_train_bwd_noalloc runs fa_train_bwd's checks, and rejects a problem whose workspace
+    exceeds its static scratch, all on the host before it looks up the scratch or launches."""
+    L = B.lib()
+    far = 1 << 34  # fake regions far enough apart for LM-sized views
+
+    def v(i, H, S, D=128):
+        return view(0, H=H, S=S, D=D, data=BASE + i * far)
+
+    def call(p, **over):
+        a = {"q": v(0, 32, 4096), "k": v(1, 8, 4096), "v": v(2, 8, 4096), "do": v(3, 32, 4096),
+             "lse": B.FaView(BASE + 4 * far, 32 * 4096, 4096, 1), "delta": B.FaView(BASE + 5 * far, 32 * 4096, 4096, 1),
+             "dq": v(6, 32, 4096), "dk": v(7, 8, 4096), "dv": v(8, 8, 4096)}
+        a.update(over)
+        return L.fa_train_bwd_noalloc(ctypes.byref(p) if p is not None else None, a["q"], a["k"], a["v"], a["do"],
+                                      a["lse"], a["delta"], a["dq"], a["dk"], a["dv"], None)
+
+    lm = dict(Hq=32, Hkv=8, Sq=4096, Sk=4096, D=128, causal=1)
+    big = params(kv_split=8, q_split=8, **lm)
+    assert L.fa_train_bwd_workspace_bytes(ctypes.byref(big)) > B.NOALLOC_SCRATCH_BYTES
+    assert call(big) == 8, B.lib().fa_train_last_error()
+    assert b"scratch" in B.lib().fa_train_last_error()
+    assert call(None) == 1
+    assert call(params(Hkv=3, **{k: x for k, x in lm.items() if k != "Hkv"})) == 2
+    assert call(params(kv_split=2, **lm), dq=v(0, 32, 4096)) == 6  # dQ over Q
