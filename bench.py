@@ -51,6 +51,8 @@ def parse():
                     help="backward split: 'table' (the workload's measured setting), 'tune' (time a few settings "
                          "once at setup, untimed), 'model' (the library's cost model), KVxQ (e.g. 2x1) or KVxQxTILES "
                          "(q-way split of the first TILES 128-row query tiles only, e.g. 2x2x6)")
+    ap.add_argument("--kv-walk", type=int, default=0,
+                    help="bf16 backward dK/dV walk: 0 the library's choice, 1 one wave per 32 keys, 2 split by role")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference kernel that "
                          "scales the HBM byte counters) and exit")
@@ -60,11 +62,12 @@ def parse():
 class Workload:
     """Device buffers and the three calls of one step for a seeded case."""
 
-    def __init__(self, key: str, splits: str = "table"):
+    def __init__(self, key: str, splits: str = "table", kv_walk: int = 0):
         import torch
 
         from flash_attention_train_amd import accounting, binding, configs
         self.key = key
+        self.kv_walk = kv_walk
         self.case = c = configs.make(key)
         self.pairs = accounting.case_pairs(c)
         self.fwd_flops = accounting.fwd_flops(self.pairs, c.D)
@@ -155,7 +158,7 @@ class Workload:
         self.B.bwd(self.q, self.k, self.v, self.do, self.lse, self.delta, mask=self.mask, scale=c.scale,
                    causal=c.causal, q_offset=c.q_offset, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws,
                    kv_split=self.kv_split, q_split=self.q_split, q_split_tiles=self.q_split_tiles,
-                   mask_tiles=self.tiles, alibi=self.alibi, softcap=self.softcap, **self.sk)
+                   mask_tiles=self.tiles, alibi=self.alibi, softcap=self.softcap, kv_walk=self.kv_walk, **self.sk)
         if self.sinks is not None:  # the sinks' gradient, added into their accumulator
             self.B.bwd_sinks(self.lse, self.delta, self.sinks, dsink=self.dsink)
 
@@ -436,7 +439,7 @@ def main():
         return
 
     log(f"[bench] device {torch.cuda.get_device_name(0)}; workload {args.workload}")
-    w = Workload(args.workload, args.splits)
+    w = Workload(args.workload, args.splits, args.kv_walk)
     r = time_workload(w, args.steps, args.warmup, graph=not args.eager)
     log(f"[bench] {args.workload}: {r['ms_per_step']:.3f} ms/step, {r['tflops']:.1f} TFLOP/s")
 
@@ -447,7 +450,7 @@ def main():
             log(f"[bench] {key}: {extra[key]['ms_per_walk']:.2f} ms/walk, {extra[key]['tflops']:.1f} TFLOP/s")
             torch.cuda.empty_cache()
             continue
-        we = Workload(key, args.splits if "x" not in args.splits else "table")
+        we = Workload(key, args.splits if "x" not in args.splits else "table", args.kv_walk)
         re_ = time_workload(we, max(5, args.steps // 2), args.warmup, graph=not args.eager)
         re_["pct_of_peak"] = 100.0 * re_["tflops"] / accounting.MI355X_BF16_DENSE_TFLOPS
         # near the ridge (few keys per row): the step against the HBM roofline as well

@@ -36,7 +36,8 @@ class FaAttnParams(ctypes.Structure):
                 ("fwd_split", ctypes.c_int32), ("key_len", ctypes.c_void_p), ("q_len", ctypes.c_void_p),
                 ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
                 ("bwd_dq_launch", ctypes.c_int32), ("sinks", ctypes.c_void_p), ("alibi", ctypes.c_void_p),
-                ("q_split_tiles", ctypes.c_int32), ("mask_stride_h", ctypes.c_int64), ("softcap", ctypes.c_float)]
+                ("q_split_tiles", ctypes.c_int32), ("mask_stride_h", ctypes.c_int64), ("softcap", ctypes.c_float),
+                ("bwd_kv_walk", ctypes.c_int32)]
 
 
 class FaError(RuntimeError):
@@ -172,7 +173,7 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
                 key_len: Optional[torch.Tensor] = None, q_len: Optional[torch.Tensor] = None,
                 window: tuple = (-1, -1), dq_launch: int = 0,
                 sinks: Optional[torch.Tensor] = None, alibi: Optional[torch.Tensor] = None,
-                q_split_tiles: int = 0, softcap: float = 0.0) -> FaAttnParams:
+                q_split_tiles: int = 0, softcap: float = 0.0, kv_walk: int = 0) -> FaAttnParams:
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Sk, Dk = k.shape
     if Bk != B or Dk != D:
@@ -191,6 +192,7 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
             setattr(p, name, t.data_ptr())
     p.q_split_tiles = int(q_split_tiles)
     p.softcap = float(softcap)
+    p.bwd_kv_walk = int(kv_walk)
     for name, t in (("sinks", sinks), ("alibi", alibi)):
         if t is not None:
             if t.dtype != torch.float32 or t.shape != (Hq,) or not t.is_contiguous():
@@ -407,14 +409,14 @@ def _workspace(p: FaAttnParams, device, workspace):
 
 def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_offset=None, dq=None, dk=None,
         dv=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None, q_len=None,
-        window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0):
+        window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0):
     """Backward: returns (dQ, dK, dV), each in q's dtype, overwritten."""
     _check_qkv(q, k, v)
     _expect("dout", dout, dtype=q.dtype, shape=q.shape)
     _check_rowstats(q, lse=lse, delta=delta)
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, window=window,
-                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles, softcap=softcap)
+                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles, softcap=softcap, kv_walk=kv_walk)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
@@ -432,7 +434,7 @@ def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_off
 
 def bwd_noalloc(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_offset=None, dq=None,
                 dk=None, dv=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None, q_len=None,
-                window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0):
+                window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0):
     """Backward through fa_train_bwd_noalloc: the results of bwd(), with the workspace taken from
     the library's static device scratch instead of an allocation (dQ, dK and dV are still the
     caller's; pass them to allocate nothing here either)."""
@@ -441,7 +443,7 @@ def bwd_noalloc(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=Fals
     _check_rowstats(q, lse=lse, delta=delta)
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, window=window,
-                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles, softcap=softcap)
+                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles, softcap=softcap, kv_walk=kv_walk)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
@@ -499,7 +501,7 @@ def tune_bwd_splits(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=
 
 def bwd_chunked(q, k, v, dout, lse, delta, dk_acc, dv_acc, *, mask=None, scale=None, causal=True, q_offset=None,
                 dq=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None,
-                q_len=None, window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0):
+                q_len=None, window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0):
     """Chunked backward: returns dQ for the chunk; ADDS dK/dV into the fp32 window
     accumulators ``dk_acc`` / ``dv_acc`` ([B, Hkv, >= Sk, D])."""
     _check_qkv(q, k, v)
@@ -508,7 +510,7 @@ def bwd_chunked(q, k, v, dout, lse, delta, dk_acc, dv_acc, *, mask=None, scale=N
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len,
                     q_len=q_len, window=window, dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles,
-                    softcap=softcap)
+                    softcap=softcap, kv_walk=kv_walk)
     if dk_acc.dtype != torch.float32 or dv_acc.dtype != torch.float32:
         raise TypeError("the window accumulators must be float32")
     B, Hkv, Sk, D = k.shape

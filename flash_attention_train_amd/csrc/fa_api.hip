@@ -87,6 +87,7 @@ fa_status check_params(const fa_attn_params* p) {
   if (!(p->scale > 0.f) || !isfinite(p->scale)) return fail(FA_ERR_SHAPE, "scale must be positive and finite");
   if (p->fwd_variant < 0 || p->fwd_variant > 3) return fail(FA_ERR_SHAPE, "unknown forward variant %d", p->fwd_variant);
   if (p->q_split_tiles < 0) return fail(FA_ERR_SHAPE, "q_split_tiles must be >= 0");
+  if (p->bwd_kv_walk < 0 || p->bwd_kv_walk > 2) return fail(FA_ERR_SHAPE, "bwd_kv_walk %d (0, 1 or 2)", p->bwd_kv_walk);
   if (p->kv_split < 0 || p->kv_split > 64 || p->q_split < 0 || p->q_split > 64 || p->fwd_split < 0 ||
       p->fwd_split > 64)
     return fail(FA_ERR_SHAPE, "split hints must be in 0 .. 64");
@@ -468,7 +469,12 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
     fa::BwdPlan plan;
     int kv, q, qt;
     choose_splits(p, accumulate, &kv, &q, &qt);
-    fa::plan_bwd_bf16(a.a, kv, q, qt, 0, &plan);
+    // the one-wave dK/dV walk unless the hint asks for the role-split one (which has no
+    // softcap variant): measured on MI355X, the role-split walk waits on its barriers and P
+    // hand-over 55% of the time and stages a pair's tiles per 64 keys instead of 128, and was
+    // 20-60% slower on the DiT and LM workloads
+    const int kv_role = p->softcap > 0.f ? 0 : (p->bwd_kv_walk == 2 ? 1 : 0);
+    fa::plan_bwd_bf16(a.a, kv, q, qt, 0, &plan, kv_role);
     // a large dQ grid runs as its own kernel, two workgroups per compute unit (measured on
     // the causal LM backward: 659 -> 631 us); small grids keep one launch, whose dQ
     // workgroups fill the compute units the dK/dV walks leave idle

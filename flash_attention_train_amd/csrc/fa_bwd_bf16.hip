@@ -29,6 +29,8 @@
 // window accumulators). Unsplit work stores its results directly. Masked entries get P = 0 exactly, so fully masked rows and key
 // columns end with exactly zero gradients ("Flash Attn Training" skill page,
 // section 6, traps 8 and 9).
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 #include "fa_tile.h"
@@ -664,6 +666,384 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
 }
 
 // ---------------------------------------------------------------------------
+// dK / dV workgroup with the work split by role (two workgroups per compute unit)
+// ---------------------------------------------------------------------------
+// A 64-key tile of one KV head, walked by four waves: for each 32-key group, one wave
+// computes S = Q K^T, P and dV += P^T dO (role 0) and another dP = dO V^T, dS and
+// dK += dS^T Q (role 1). Each wave holds one operand (K or V) and one accumulator (dV or
+// dK) of its 32 keys, about half the registers of a wave doing all four products, so
+// two workgroups share a compute unit and each one's waits are covered by the other's
+// products. P reaches the dS wave through LDS in bf16, in the accumulator layout both
+// waves share (lane = key, register = query row), 2 KB per block; dS is then formed from
+// it (one more bf16 rounding of P inside the products, as dV already uses it). Per
+// (head, 64-row query tile) pair:
+//   role 0: S0, P0 -> LDS; S1, P1 -> LDS | barrier | dV += P0^T dO0, P1^T dO1
+//   role 1: dP0, dP1                     | barrier | dS0 -> dK += dS0^T Q0; dS1 -> dK
+// The structure, the mask's block classes and visibility bits, its additive values and
+// ALiBi are applied by role 0 (P = 0 exactly where hidden, so role 1's dS is 0 there).
+// The rest is the one-wave walk's: pairs of a split walk, the live-candidate words, the
+// Q / dO tiles copied straight into LDS one pair ahead (two buffers), LSE and Delta
+// folded into an extra k-chunk of the products, results stored through LDS.
+template <int D, bool CAUSAL, bool MASK, bool BIAS>
+__device__ __forceinline__ void dkdv_role_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
+  constexpr int DS = D / 16, DB = D / 32;
+  constexpr int BN = kBwdRoleKeys, BM = KV_BM;
+  using TL = Tile<D>;
+  bf16* q_lds = reinterpret_cast<bf16*>(smem);     // [2][BM * D]
+  bf16* do_lds = q_lds + 2 * BM * D;               // [2][BM * D]
+  // augmented k-chunk rows: (-LSE / scale) and (-Delta) as three bf16 terms (hi + mid + lo
+  // carry the fp32 value), 8 elements per row; both lane halves read them and the K / V
+  // extension (1, 1, 1, 0 ...) is zero in half 1, so only half 0's copy counts
+  bf16* aug_lds = do_lds + 2 * BM * D;             // [Q', dO'][2 buffers][BM][8]
+  bf16* x_lds = aug_lds + 2 * 2 * BM * 8;          // P exchange [2 blocks][2 key groups][64 lanes][16]
+
+  const AttnShape& a = args.a;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int role = wave >> 1, kg = wave & 1;  // role 0: S, P, dV; role 1: dP, dS, dK
+  const int g = lane >> 5, r32 = lane & 31;
+  const KvUnit u = kv_unit_of(a, plan, unit);
+  const int kt = u.kt, b = u.b, hk = u.hk, split = u.split;
+  const int n0 = kt * BN;
+  const int key = n0 + 32 * kg + r32;
+  const float cs = a.scale * kLog2e;
+
+  // this wave's operand: K (role 0) or V (role 1), rows of its 32 keys (keys past the end
+  // read the last key: their scores are hidden on the tail tile, their rows never stored)
+  const bf16* KV = role == 0 ? static_cast<const bf16*>(args.k) + b * args.sk.b + hk * args.sk.h
+                             : static_cast<const bf16*>(args.v) + b * args.sv.b + hk * args.sv.h;
+  const int64_t kv_s = role == 0 ? args.sk.s : args.sv.s;
+  const int64_t key_c = min(key, a.Sk - 1);
+  bf16x8 ones3;
+  #pragma unroll
+  for (int e = 0; e < 8; ++e) ones3[e] = (bf16)(g == 0 && e < 3 ? 1.f : 0.f);
+  bf16x8 kvf[DS];
+  #pragma unroll
+  for (int s = 0; s < DS; ++s) kvf[s] = *reinterpret_cast<const bf16x8*>(KV + key_c * kv_s + 16 * s + 8 * g);
+  f32x16 acc[DB];  // dV (role 0) or dK (role 1)
+  #pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = zeros16();
+
+  // the rows that can see any of the unit's keys, and the rows every key sees (a pair
+  // tile outside [r_lo, r_hi) needs masking), as in the one-wave walk
+  const int klen = klen_of(a, b), qlen = qlen_of(a, b);
+  int qt0 = 0, qt_end = 0;
+  if (n0 < klen) {
+    int64_t lo, hi, lo1, hi1;
+    row_range(a, klen, qlen, n0, lo, hi);
+    row_range(a, klen, qlen, min(n0 + BN, klen) - 1, lo1, hi1);
+    const int nqt = (a.Sq + BM - 1) / BM;
+    qt0 = (int)min<int64_t>(lo / BM, nqt);
+    qt_end = hi1 > lo ? (int)min<int64_t>((hi1 + BM - 1) / BM, nqt) : qt0;
+    if (qt_end < qt0) qt_end = qt0;
+  }
+  int r_lo, r_hi;
+  {
+    int64_t l0, h0, l1, h1;
+    row_range(a, klen, qlen, n0, l0, h0);
+    row_range(a, klen, qlen, n0 + BN - 1, l1, h1);
+    r_lo = (int)min<int64_t>(l1, a.Sq);
+    r_hi = n0 + BN > klen ? r_lo : (int)min<int64_t>(h0, a.Sq);
+  }
+  const int npairs = (qt_end - qt0) * a.G;
+  struct Pos {
+    int p, qi, hi, j;
+  };
+  const int step_q = plan.kv_split / a.G, step_h = plan.kv_split % a.G;
+  auto advance = [&](Pos x) {
+    x.p += plan.kv_split;
+    ++x.j;
+    x.qi += step_q;
+    x.hi += step_h;
+    if (x.hi >= a.G) {
+      x.hi -= a.G;
+      ++x.qi;
+    }
+    return x;
+  };
+  auto pair_of = [&](const Pos& x, int& h, int& q0) {
+    h = hk * a.G + x.hi;
+    q0 = (qt0 + x.qi) * BM;
+  };
+  float lpre = 0.f;
+  auto stage_pair = [&](const Pos& x, int buf) {
+    int h, q0;
+    pair_of(x, h, q0);
+    const bf16* Q = static_cast<const bf16*>(args.q) + b * args.sq.b + h * args.sq.h + (int64_t)q0 * args.sq.s;
+    const bf16* dO = static_cast<const bf16*>(args.dout) + b * args.sdo.b + h * args.sdo.h + (int64_t)q0 * args.sdo.s;
+    TL::template stage<BM, NT, false>(q_lds + buf * BM * D, Q, args.sq.s, a.Sq - q0);
+    TL::template stage<BM, NT, false>(do_lds + buf * BM * D, dO, args.sdo.s, a.Sq - q0);
+    if (tid < 2 * BM) {
+      const int row = min(q0 + (tid % BM), a.Sq - 1);
+      lpre = tid < BM ? args.lse[b * args.lse_sb + h * args.lse_sh + row]
+                      : args.delta[b * args.delta_sb + h * args.delta_sh + row];
+    }
+  };
+  auto store_stats = [&](int buf) {
+    if (tid < 2 * BM) {
+      const float c = tid < BM ? -lpre * args.inv_scale : -lpre;
+      const bf16 hi = (bf16)c;
+      const bf16 mid = (bf16)(c - (float)hi);
+      const bf16 lo = (bf16)(c - (float)hi - (float)mid);
+      *reinterpret_cast<bf16x8*>(aug_lds + (((tid / BM) * 2 + buf) * BM + tid % BM) * 8) =
+          bf16x8{hi, mid, lo, (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    }
+  };
+
+  const int G16 = lane >> 4, L16 = lane & 15;
+  const int tr_row = L16 >> 2, tr_col = 16 * (G16 & 1) + 4 * (L16 & 3);
+
+  // pairs whose mask block is dead are skipped by the whole workgroup; per pair, role 0
+  // takes the block class and, for a 0 / -inf block, its key's visibility word
+  const int nct = (a.Sk + kMaskTile - 1) / kMaskTile;
+  const int ct0 = n0 / kMaskTile;  // the unit's keys are one mask block column
+  auto live = [&](int j) -> bool {
+    const int rt = qt0 + (split + j * plan.kv_split) / a.G;
+    return ct0 < nct && tile_class(a, b, rt, ct0) != kTileDead;
+  };
+  __shared__ uint64_t live_lds[kBwdWaves];
+  LiveWords lw{live_lds, -NT, {0, 0, 0, 0}};
+  const int ncand = npairs > split ? (npairs - split + plan.kv_split - 1) / plan.kv_split : 0;
+  auto next_live = [&](Pos x) {
+    if (!MASK || !a.tiles || x.p >= npairs) return x;
+    const int j = lw.next(x.j, ncand, tid, live);
+    if (j == x.j) return x;
+    if (j >= ncand) return Pos{npairs, 0, 0, ncand};
+    const int p = split + j * plan.kv_split;
+    return Pos{p, p / a.G, p % a.G, j};
+  };
+  const int nrt_all = (a.Sq + kMaskTile - 1) / kMaskTile;
+  ClassRun run{kTileDead, -64};
+  auto load_run = [&](int qi) {
+    run.load(a, qi & ~63, ct0 < nct ? nrt_all - qt0 : 0, [&](int pos) { return tile_index(a, b, qt0 + pos, ct0); });
+  };
+  auto mask_state = [&](const Pos& x, int& cls, uint64_t& w) {
+    cls = kTileBias;
+    w = ~0ull;
+    if (MASK && a.tiles) {
+      if (x.qi >= run.base + 64) load_run(x.qi);
+      cls = run.at(x.qi);
+      if (cls == kTileBits)
+        w = a.colbits[(int64_t)tile_index(a, b, qt0 + x.qi, ct0) * kMaskTile + (key - ct0 * kMaskTile)];
+    }
+  };
+
+  Pos cur = next_live(Pos{split, split / a.G, split % a.G, 0});
+  int cls_cur = kTileBias;
+  uint64_t wb_cur = ~0ull;
+  if (cur.p < npairs) {
+    stage_pair(cur, 0);
+    if (MASK && a.tiles) {
+      load_run(cur.qi);
+      wait_vm();
+    }
+    mask_state(cur, cls_cur, wb_cur);
+  }
+  // (everything stays in the arch VGPRs: about 200 per lane, so that with no AGPRs in use the
+  // compiler may give this walk all 256 registers of a two-workgroups-per-unit wave)
+  wait_vm();
+  if (cur.p < npairs) store_stats(0);
+  __syncthreads();
+  bf16* xw = x_lds + (kg * 64 + lane) * 16;  // this lane's P slot, block 0 (block 1: + 2 * 64 * 16)
+
+  // the pair loop, compiled once per role so that each wave's loop carries only its own
+  // role's operands and addresses (both loops take the same barriers in the same order)
+  auto walk = [&](auto role_c) {
+  constexpr int ROLE = decltype(role_c)::value;
+  for (int buf = 0; cur.p < npairs;) {
+    const int nb = buf ^ 1;
+    const Pos nxt = next_live(advance(cur));
+    const bool more = nxt.p < npairs;
+    int cls_next = kTileBias;
+    uint64_t wb_next = ~0ull;
+    if (more) {
+      mask_state(nxt, cls_next, wb_next);
+      stage_pair(nxt, nb);  // lands while this pair is processed
+    }
+    int h, q0;
+    pair_of(cur, h, q0);
+    const bf16* qb_lds = q_lds + buf * BM * D;
+    const bf16* db_lds = do_lds + buf * BM * D;
+    // Three phases per pair, separated by workgroup barriers, each with about the same
+    // matrix work for both roles (role 0 | role 1):
+    //   S0, P0 -> LDS          | dP0
+    //   dV += P0^T dO0; S1, P1 | dS0 (P0 from LDS), dK += dS0^T Q0; dP1
+    //   dV += P1^T dO1         | dS1, dK += dS1^T Q1
+    if constexpr (ROLE == 0) {
+      const int cls = cls_cur;
+      const bool bias = BIAS && MASK && (cls == kTileBias || a.alibi);
+      const bool bits = MASK && cls == kTileBits;
+      const bool dead = MASK && cls == kTileDead;
+      const bool edge = !(q0 >= r_lo && q0 + BM <= r_hi);
+      const bool masked = edge || bits || dead;
+      uint64_t vis = dead ? 0ull : ~0ull;
+      if (masked && !dead) {
+        int64_t lo, hi;
+        row_range(a, klen, qlen, key, lo, hi);
+        lo -= q0;
+        hi -= q0;
+        vis = bit_range64((int)(lo < 0 ? 0 : (lo > BM ? BM : lo)), (int)(hi < 0 ? 0 : (hi > BM ? BM : hi)));
+        if (bits) vis &= wb_cur;
+      }
+      const bf16* qx_lds = aug_lds + buf * BM * 8;
+      // S and P of block qb (lane = key, half g; register r = query row 32 qb + 8 (r/4) + 4 g + r%4),
+      // stored to this lane's P slot and kept for dV
+      auto s_block = [&](int qb, bf16x8 (&pa)[2]) {
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 qa[DS];
+        #pragma unroll
+        for (int s = 0; s < DS; ++s) qa[s] = TL::read_chunk(qb_lds, 32 * qb + r32, 2 * s + g);
+        const bf16x8 qx = *reinterpret_cast<const bf16x8*>(qx_lds + (32 * qb + r32) * 8);
+        f32x16 sacc = zeros16();
+        #pragma unroll
+        for (int s = 0; s < DS; ++s) mma(sacc, qa[s], kvf[s]);
+        mma(sacc, qx, ones3);  // S - LSE / scale
+        if (bias && a.alibi) {
+          const float sl = a.alibi[h] * args.inv_scale;
+          const float base = (float)((int64_t)key - a.q_offset - q0 - 32 * qb - 4 * g);
+          #pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[r] -= sl * fabsf(base - (float)(8 * (r >> 2) + (r & 3)));
+        }
+        if (bias && a.mask) {  // four rows' values in flight at a time (registers)
+          const float* mk = a.mask + b * a.mask_sb + h * a.mask_sh + min(key, a.Sk - 1);
+          #pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            float mv[4];
+            #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int row = min(q0 + 32 * qb + 8 * rr + 4 * g + e, a.Sq - 1);
+              mv[e] = mk[(int64_t)row * a.mask_sq];
+            }
+            #pragma unroll
+            for (int e = 0; e < 4; ++e) sacc[4 * rr + e] += mv[e] * args.inv_scale;
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        if (masked) {  // hidden scores -> -inf (P = 0); bit 8 rr + e of w <-> register 4 rr + e
+          const uint32_t w = (uint32_t)(vis >> (32 * qb + 4 * g));
+          #pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[r] = ninf_unless_bit(sacc[r], w, 8 * (r >> 2) + (r & 3));
+        }
+        #pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(sacc[r] * cs);
+        pack8(pa[0], sacc, 0);
+        pack8(pa[1], sacc, 8);
+        *reinterpret_cast<bf16x8*>(xw + qb * 2 * 64 * 16) = pa[0];
+        *reinterpret_cast<bf16x8*>(xw + qb * 2 * 64 * 16 + 8) = pa[1];
+      };
+      // dV += P^T dO for block qb: registers 8 hh .. of P hold rows 32 qb + 16 hh + 8 t + 4 g + e,
+      // the rows each pair of dO^T transpose reads returns
+      // (the reads of one half, 8 transposes, are issued before its 4 products and fenced from
+      // the other half's, so that at most 16 operand registers are in flight)
+      auto dv_block = [&](int qb, const bf16x8 (&pa)[2]) {
+        #pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int rbase = 32 * qb + 16 * hh + 4 * g + tr_row;
+          bf16x8 dob[DB];
+          #pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x4 d0 = TL::read_tr(db_lds, rbase, 32 * db + tr_col);
+            const bf16x4 d1 = TL::read_tr(db_lds, rbase + 8, 32 * db + tr_col);
+            dob[db] = bf16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+          }
+          #pragma unroll
+          for (int db = 0; db < DB; ++db) mma(acc[db], pa[hh], dob[db]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      bf16x8 p0[2], p1[2];
+      s_block(0, p0);
+      __syncthreads();
+      dv_block(0, p0);
+      s_block(1, p1);
+      __syncthreads();
+      dv_block(1, p1);
+    } else {
+      const bf16* dx_lds = aug_lds + (2 + buf) * BM * 8;
+      auto dp_block = [&](int qb) {  // dP - Delta of block qb
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 da[DS];
+        #pragma unroll
+        for (int s = 0; s < DS; ++s) da[s] = TL::read_chunk(db_lds, 32 * qb + r32, 2 * s + g);
+        const bf16x8 dx = *reinterpret_cast<const bf16x8*>(dx_lds + (32 * qb + r32) * 8);
+        f32x16 dp = zeros16();
+        #pragma unroll
+        for (int s = 0; s < DS; ++s) mma(dp, da[s], kvf[s]);
+        mma(dp, dx, ones3);
+        return dp;
+      };
+      // dS = P (dP - Delta) from role 0's P of block qb, then dK += dS^T Q
+      auto dk_block = [&](int qb, f32x16& dp) {
+        const bf16x8 pv0 = *reinterpret_cast<const bf16x8*>(xw + qb * 2 * 64 * 16);
+        const bf16x8 pv1 = *reinterpret_cast<const bf16x8*>(xw + qb * 2 * 64 * 16 + 8);
+        #pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          dp[r] *= (float)pv0[r];
+          dp[8 + r] *= (float)pv1[r];
+        }
+        bf16x8 dsa[2];
+        pack8(dsa[0], dp, 0);
+        pack8(dsa[1], dp, 8);
+        #pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int rbase = 32 * qb + 16 * hh + 4 * g + tr_row;
+          bf16x8 qbt[DB];
+          #pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x4 q0v = TL::read_tr(qb_lds, rbase, 32 * db + tr_col);
+            const bf16x4 q1v = TL::read_tr(qb_lds, rbase + 8, 32 * db + tr_col);
+            qbt[db] = bf16x8{q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
+          }
+          #pragma unroll
+          for (int db = 0; db < DB; ++db) mma(acc[db], dsa[hh], qbt[db]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      f32x16 dp0 = dp_block(0);
+      __syncthreads();  // role 0 has stored P0
+      dk_block(0, dp0);
+      f32x16 dp1 = dp_block(1);
+      __syncthreads();  // role 0 has stored P1
+      dk_block(1, dp1);
+    }
+    // the next pair's tiles are complete once every wave has waited for its own loads;
+    // every read of this pair's buffers and P slots is done after this barrier
+    wait_vm();
+    if (more) store_stats(nb);
+    __syncthreads();
+    buf = nb;
+    cur = nxt;
+    cls_cur = cls_next;
+    wb_cur = wb_next;
+  }
+  };
+  if (role == 0)
+    walk(std::integral_constant<int, 0>{});
+  else
+    walk(std::integral_constant<int, 1>{});
+
+  const bool part = plan.kv_split > 1;
+  const int kbase = n0 + 32 * kg;
+  const int rows = max(0, min(32, a.Sk - kbase));
+  float* part_base = role == 0 ? plan.dv_part : plan.dk_part;
+  void* out = role == 0 ? args.dv : args.dk;
+  const Strides so = role == 0 ? args.sdv : args.sdk;
+  RowSink sink;
+  if (part) {
+    sink = RowSink{reinterpret_cast<char*>(part_base + (int64_t)split * a.B * a.Hkv * a.Sk * D +
+                                           (((int64_t)b * a.Hkv + hk) * a.Sk + kbase) * D),
+                   (int64_t)D * 4, rows, 1};
+  } else {
+    const int64_t esz = args.accumulate ? 4 : 2;
+    sink = RowSink{static_cast<char*>(out) + (b * so.b + hk * so.h + (int64_t)kbase * so.s) * esz, so.s * esz, rows,
+                   args.accumulate ? 2 : 0};
+  }
+  float* stage = reinterpret_cast<float*>(smem) + wave * 32 * D;
+  __syncthreads();
+  store_block<D>(acc, (role == 1 && !part) ? a.scale : 1.f, stage, lane, sink);
+}
+
+// ---------------------------------------------------------------------------
 // dQ workgroup
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool MASK, bool BIAS, bool LOWREG = false, bool CAP = false>
@@ -980,6 +1360,23 @@ __global__ __launch_bounds__(NT) void bwd_bf16_kernel(const BwdArgs args, const 
   }
 }
 
+// The role-split dK/dV walk as a kernel of its own, two workgroups per compute unit; the
+// dQ walk follows as bwd_dq_kernel. (One launch for both would need the two walks'
+// registers together, beyond the 256 a wave gets at two workgroups per unit.)
+template <int D, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(NT, 2) void bwd_role_kernel(const BwdArgs args, const BwdPlan plan) {
+  constexpr int KV_LDS = (4 * KV_BM * D + 2 * 2 * KV_BM * 8 + 2 * 2 * 64 * 16) * 2;
+  __shared__ __attribute__((aligned(16))) char smem[KV_LDS];
+  const int blk = blockIdx.x;
+  const AttnShape& a = args.a;
+  const KvUnit u = kv_unit_of(a, plan, blk);
+  if (MASK && any_bias_block(a, u.b, 0, (a.Sq + kMaskTile - 1) / kMaskTile, u.kt * (kBwdRoleKeys / kMaskTile),
+                             kBwdRoleKeys / kMaskTile))
+    dkdv_role_unit<D, CAUSAL, MASK, true>(args, plan, blk, smem);
+  else
+    dkdv_role_unit<D, CAUSAL, MASK, false>(args, plan, blk, smem);
+}
+
 // The dQ walk as a kernel of its own: its registers fit two workgroups per compute unit
 // (the dK/dV walk's do not), so that one workgroup's LDS and memory waits are covered by
 // the other's products. Launched after the dK/dV-only grid when the plan asks for it.
@@ -999,6 +1396,17 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(const BwdArgs args, const
 
 template <int D, bool CAUSAL, bool MASK, bool CAP = false>
 hipError_t launch_cm(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream) {
+  if constexpr (!CAP) {
+    if (plan.kv_role) {
+      if (plan.n_kv_units > 0)
+        hipLaunchKernelGGL((bwd_role_kernel<D, CAUSAL, MASK>), dim3(plan.n_kv_units), dim3(NT), 0, stream, args, plan);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess || plan.n_q_units == 0) return e;
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, MASK, CAP>), dim3(plan.n_q_units), dim3(NT), 0, stream, args,
+                         plan);
+      return hipGetLastError();
+    }
+  }
   if (!plan.dq_separate) {
     hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, MASK, CAP>), dim3(plan.n_kv_units + plan.n_q_units), dim3(NT), 0,
                        stream, args, plan);
@@ -1027,9 +1435,11 @@ hipError_t launch_t(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream
 }  // namespace
 
 void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, int q_tiles_split, int dq_separate,
-                   BwdPlan* plan) {
+                   BwdPlan* plan, int kv_role) {
   plan->dq_separate = dq_separate;
-  const int nkt = (a.Sk + KV_BN - 1) / KV_BN;
+  plan->kv_role = kv_role;
+  const int kvb = kv_role ? kBwdRoleKeys : KV_BN;
+  const int nkt = (a.Sk + kvb - 1) / kvb;
   const int nqt = (a.Sq + Q_BM - 1) / Q_BM;
   plan->kv_split = kv_split;
   plan->q_split = q_split;

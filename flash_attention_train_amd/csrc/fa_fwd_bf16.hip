@@ -44,8 +44,12 @@ __device__ __forceinline__ f32x16 zeros16() {
 // alternate live key tiles, and merge their (max, sum, O) in LDS at the end.
 // SPLIT: workgroup blockIdx.z walks only the blockIdx.z-th contiguous share of the live
 // range's key tiles and leaves its unnormalised rows to the merge pass.
-template <int D, int QB, int BN, bool CAUSAL, bool MASK, int KS, bool SPLIT = false>
+// KVF: K and V stored as bf16 (0), fp16 (1) or q8_0 (2); the last two are converted to bf16
+// on their way into LDS (their tiles' loads issued one tile ahead into registers, converted
+// and written after the current tile's products), so a quantised window is read in place.
+template <int D, int QB, int BN, bool CAUSAL, bool MASK, int KS, bool SPLIT = false, int KVF = 0>
 __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const FwdArgs args) {
+  static_assert(KVF == 0 || (KS == 1 && QB == 1 && BN == 64), "stored K / V formats take the default walk");
   constexpr int NW = 4;
   constexpr int RB = NW / KS;       // waves (row blocks) per key half
   constexpr int BM = RB * QB * 32;  // query rows per workgroup
@@ -143,6 +147,24 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     TL::template stage<BN, NTS, KS == 1>(k_lds[kh][buf], K + (int64_t)key0 * args.sk.s, args.sk.s, a.Sk - key0, rb);
     TL::template stage<BN, NTS, KS == 1>(v_lds[kh][buf], V + (int64_t)key0 * args.sv.s, args.sv.s, a.Sk - key0, rb);
   };
+  // stored fp16 / q8_0 tiles: loads one tile ahead, conversion into LDS after the products
+  constexpr int KVE = KVF == kKvQ8 ? 1 : 2;  // bytes per stored element
+  const char* Kst = static_cast<const char*>(args.k) + (b * args.sk.b + hk * args.sk.h) * KVE;
+  const char* Vst = static_cast<const char*>(args.v) + (b * args.sv.b + hk * args.sv.h) * KVE;
+  const _Float16* Ksc = a.kscale ? a.kscale + b * a.sks.b + hk * a.sks.h : nullptr;
+  const _Float16* Vsc = a.vscale ? a.vscale + b * a.svs.b + hk * a.svs.h : nullptr;
+  CvtStage<D, BN, NTS, KVF == 0 ? 1 : KVF> kcs, vcs;
+  auto load_tile = [&](int kt) {
+    const int64_t key0 = (int64_t)kt * BN;
+    kcs.load(Kst + key0 * args.sk.s * KVE, args.sk.s, Ksc ? Ksc + key0 * a.sks.s : nullptr, a.sks.s,
+             a.Sk - (int)key0, rb);
+    vcs.load(Vst + key0 * args.sv.s * KVE, args.sv.s, Vsc ? Vsc + key0 * a.svs.s : nullptr, a.svs.s,
+             a.Sk - (int)key0, rb);
+  };
+  auto commit_tile = [&](int buf) {
+    kcs.commit(k_lds[kh][buf], rb);
+    vcs.commit(v_lds[kh][buf], rb);
+  };
 
   // With a mask tile map, key tiles whose mask blocks are dead for every row block
   // of this workgroup are skipped outright (no load, no products); per wave, a dead
@@ -211,7 +233,12 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
   #pragma unroll
   for (int qb = 0; qb < QB; ++qb) wb_cur[qb] = ~0ull;
   if (kt < kt_end) {
-    stage_tile(kt, 0);
+    if constexpr (KVF == 0) {
+      stage_tile(kt, 0);
+    } else {
+      load_tile(kt);
+      commit_tile(0);
+    }
     mask_state(kt, cls_cur, wb_cur);
   }
   wait_vm();
@@ -235,7 +262,10 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     for (int qb = 0; qb < QB; ++qb) wb_next[qb] = ~0ull;
     if (more) {
       mask_state(ktn, cls_next, wb_next);
-      stage_tile(ktn, buf ^ 1);  // lands while this tile is being processed
+      if constexpr (KVF == 0)
+        stage_tile(ktn, buf ^ 1);  // lands while this tile is being processed
+      else
+        load_tile(ktn);  // (converted into the other buffer after this tile's products)
     }
     const bf16* kb_lds = k_lds[kh][buf];
     const bf16* vb_lds = v_lds[kh][buf];
@@ -384,6 +414,9 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     }
 
     }  // cls != dead
+    if constexpr (KVF != 0) {
+      if (more) commit_tile(buf ^ 1);
+    }
     wait_vm();
     __syncthreads();
     #pragma unroll
@@ -536,11 +569,29 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const FwdArgs args) {
   if (c == 0) args.lse[b * args.lse_sb + h * args.lse_sh + i] = lse;
 }
 
+// stored fp16 / q8_0 K and V: the default walk without a dense mask or ALiBi (checked on the host)
+template <int D, bool SPLIT>
+hipError_t launch_kvf(const FwdArgs& args, dim3 grid, hipStream_t stream) {
+  const bool causal = args.a.causal != 0, q8 = args.a.kvf == kKvQ8;
+  if (causal && q8)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, 64, true, false, 1, SPLIT, kKvQ8>), grid, dim3(256), 0, stream, args);
+  else if (causal)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, 64, true, false, 1, SPLIT, kKvF16>), grid, dim3(256), 0, stream, args);
+  else if (q8)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, 64, false, false, 1, SPLIT, kKvQ8>), grid, dim3(256), 0, stream, args);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, 64, false, false, 1, SPLIT, kKvF16>), grid, dim3(256), 0, stream, args);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_split_d(const FwdArgs& args, hipStream_t stream) {
   const dim3 grid(args.a.Hq * args.a.B, (args.a.Sq + 127) / 128, args.splits);
   const bool causal = args.a.causal != 0, mask = args.a.mask != nullptr || args.a.alibi != nullptr;
-  if (causal && mask)
+  if (args.a.kvf != kKvBf16) {
+    hipError_t e = launch_kvf<D, true>(args, grid, stream);
+    if (e != hipSuccess) return e;
+  } else if (causal && mask)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, 64, true, true, 1, true>), grid, dim3(256), 0, stream, args);
   else if (causal)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, 64, true, false, 1, true>), grid, dim3(256), 0, stream, args);
@@ -573,6 +624,8 @@ hipError_t launch_t(const FwdArgs& args, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_d(const FwdArgs& args, int variant, hipStream_t stream) {
+  if (args.a.kvf != kKvBf16)
+    return launch_kvf<D, false>(args, dim3(args.a.Hq * args.a.B, (args.a.Sq + 127) / 128), stream);
   if (variant == 2) return launch_t<D, 2, 32, 1>(args, stream);
   if (variant == 3) return launch_t<D, 1, 32, 2>(args, stream);
   return launch_t<D, 1, 64, 1>(args, stream);

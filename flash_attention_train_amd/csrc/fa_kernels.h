@@ -40,7 +40,15 @@ struct AttnShape {
   // logit softcap c (> 0) or 0: the scaled product x becomes c tanh(x / c) before the mask;
   // read by the generic kernels only
   float softcap;
+  // storage of K and V for the bf16 kernels: kKvBf16 (the compute dtype), kKvF16 (fp16), or
+  // kKvQ8 (q8_0: int8 quants, one fp16 scale per 32 values along D at kscale / vscale,
+  // element strides sks / svs); the walks convert each tile to bf16 as they read it
+  int kvf;
+  const _Float16* kscale;
+  const _Float16* vscale;
+  Strides sks, svs;
 };
+constexpr int kKvBf16 = 0, kKvF16 = 1, kKvQ8 = 2;
 
 // the structured lengths of batch entry b (clamped to the tensor lengths)
 __device__ __forceinline__ int klen_of(const AttnShape& a, int b) {
@@ -137,6 +145,8 @@ __device__ __forceinline__ int class_of(const ClassAhead& c) {
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kBwdUnit = 32 * kBwdWaves;
+// keys per dK/dV workgroup of the role-split walk (two 32-key groups, two roles each)
+constexpr int kBwdRoleKeys = 64;
 
 struct FwdArgs {
   AttnShape a;
@@ -204,6 +214,7 @@ struct BwdPlan {
   int n_kv_units;  // dK/dV workgroups (launched first)
   int n_q_units;   // dQ workgroups
   int dq_separate; // 1: the dQ workgroups run as a second kernel (two per compute unit)
+  int kv_role;     // 1: the role-split dK/dV walk (64-key workgroups, two per compute unit)
   float* dk_part;  // fp32 [kv_split][B, Hkv, Sk, D] partial sums when kv_split > 1
   float* dv_part;
   float* dq_part;  // fp32 [q_split][B, Hq, Sq, D] partial sums when q_split > 1
@@ -268,7 +279,7 @@ struct ConvertArgs {
 };
 hipError_t launch_convert_f16(const ConvertArgs& args, hipStream_t stream);
 void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, int q_tiles_split, int dq_separate,
-                   BwdPlan* plan);
+                   BwdPlan* plan, int kv_role);
 hipError_t launch_bwd_bf16(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream);
 
 }  // namespace fa

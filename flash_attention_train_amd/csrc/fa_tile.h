@@ -14,6 +14,8 @@
 //     times 16 columns (swz >> 2 differs across the 4 rows).
 #pragma once
 
+#include <type_traits>
+
 #include "fa_device.h"
 
 namespace fa {
@@ -100,6 +102,84 @@ struct Tile {
         __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) bf16*)dst);
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
                  : "memory", "m0");
+  }
+};
+
+// ---------------------------------------------------------------------------
+// K / V stored as fp16 or q8_0, read in place: 8 consecutive values of a row to bf16
+// ---------------------------------------------------------------------------
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// fp16 -> bf16: the fp32 widening is exact; one rounding to nearest even
+__device__ __forceinline__ bf16x8 cvt8_f16(const f16x8& h) {
+  bf16x8 o;
+  #pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = (bf16)(float)h[j];
+  return o;
+}
+// q8_0 -> bf16: value = d * q, the fp32 product of an fp16 scale and an int8 quant is exact
+// (at most 11 + 7 significant bits); one rounding to nearest even
+__device__ __forceinline__ bf16x8 cvt8_q8(uint2 q, _Float16 d) {
+  const float df = (float)d;
+  bf16x8 o;
+  #pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t w = j < 4 ? q.x : q.y;
+    const int v = __builtin_amdgcn_sbfe((int)w, 8 * (j & 3), 8);
+    o[j] = (bf16)((float)v * df);
+  }
+  return o;
+}
+// 8 values of a stored row (element j0 .. j0 + 7, j0 a multiple of 8) as bf16: `row` points at
+// the row's first stored element (fp16 or int8), `srow` at its first q8_0 scale
+template <int KVF>
+__device__ __forceinline__ bf16x8 load_cvt8(const void* row, const _Float16* srow, int j0) {
+  if constexpr (KVF == 1) {
+    return cvt8_f16(*reinterpret_cast<const f16x8*>(static_cast<const _Float16*>(row) + j0));
+  } else {
+    return cvt8_q8(*reinterpret_cast<const uint2*>(static_cast<const int8_t*>(row) + j0), srow[j0 >> 5]);
+  }
+}
+
+// A [ROWS][D] K or V tile stored as fp16 (KVF 1) or q8_0 (KVF 2), staged into LDS in the
+// same swizzled bf16 layout as Tile<D>::stage: load() issues this thread's global loads
+// (row `valid - 1` repeated past the end), commit() converts them and writes LDS. Between
+// the two the raw values wait in registers, so the loads of the next tile can be issued
+// before the current tile's products and written after them.
+template <int D, int ROWS, int NT, int KVF>
+struct CvtStage {
+  static constexpr int NCH = D / 8, W = NT / 64, PER = ROWS * NCH / NT;
+  static_assert((ROWS * NCH) % NT == 0, "tile must split evenly over the threads");
+  typedef typename std::conditional<KVF == 1, f16x8, uint2>::type Raw;
+  Raw raw[PER];
+  _Float16 sc[PER];
+  __device__ __forceinline__ void load(const void* src, int64_t stride, const _Float16* scale, int64_t sstride,
+                                       int valid, int group_wave = -1) {
+    const int lane = threadIdx.x & 63, wave = group_wave < 0 ? (int)(threadIdx.x >> 6) : group_wave;
+    #pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int n = 64 * (wave + W * i) + lane;
+      const int row = n / NCH, p = n % NCH;
+      const int c = p ^ Tile<D>::swz(row);
+      const int64_t grow = row < valid ? row : valid - 1;
+      if constexpr (KVF == 1) {
+        raw[i] = *reinterpret_cast<const f16x8*>(static_cast<const _Float16*>(src) + grow * stride + 8 * c);
+      } else {
+        raw[i] = *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(src) + grow * stride + 8 * c);
+        sc[i] = scale[grow * sstride + (c >> 2)];
+      }
+    }
+  }
+  __device__ __forceinline__ void commit(bf16* lds, int group_wave = -1) const {
+    const int lane = threadIdx.x & 63, wave = group_wave < 0 ? (int)(threadIdx.x >> 6) : group_wave;
+    #pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int n = 64 * (wave + W * i) + lane;
+      bf16x8 v;
+      if constexpr (KVF == 1) v = cvt8_f16(raw[i]);
+      else v = cvt8_q8(raw[i], sc[i]);
+      *reinterpret_cast<bf16x8*>(lds + 8 * n) = v;
+    }
   }
 };
 

@@ -172,6 +172,13 @@ typedef struct fa_attn_params {
      * without a dense mask with sinks and structured masks; not with ALiBi, nor with sinks or
      * structured masks over a dense mask (FA_ERR_UNSUPPORTED). */
     float softcap;
+    /* Work decomposition hint of the bf16 backward's dK/dV walk (same results up to fp32
+     * summation order and one bf16 rounding of P inside dS): 0 = automatic (walk 1); 1 = one
+     * wave per 32 keys computes S, dP, dV and dK (128-key workgroups, one per compute unit);
+     * 2 = the work split by role, one wave computing S, P and dV and another dP, dS and dK for
+     * each 32 keys (64-key workgroups, two per compute unit, P passed between them in bf16;
+     * the dQ walk then runs as its own kernel). A logit softcap always takes walk 1. */
+    int32_t bwd_kv_walk;
 } fa_attn_params;
 
 /* Forward: writes O (dtype) and LSE (fp32, natural log). Fully masked rows get

@@ -44,7 +44,7 @@ def params(**kw):
     a = dict(B=1, Hq=4, Hkv=2, Sq=64, Sk=64, D=64, dtype=B.FA_BF16, causal=0, q_offset=0, scale=0.125, mask=None,
              mask_stride_b=0, mask_stride_q=0, mask_tiles=None, fwd_variant=0, kv_split=0, q_split=0, fwd_split=0, key_len=None, q_len=None,
              window_left=-1, window_right=-1, bwd_dq_launch=0, sinks=None, alibi=None,
-             q_split_tiles=0, mask_stride_h=0, softcap=0.0)
+             q_split_tiles=0, mask_stride_h=0, softcap=0.0, bwd_kv_walk=0)
     a.update(kw)
     return B.FaAttnParams(*(a[f] for f, _ in B.FaAttnParams._fields_))
 
@@ -274,3 +274,8 @@ def test_backward_noalloc_rejects_before_any_launch():
     assert call(None) == 1
     assert call(params(Hkv=3, **{k: x for k, x in lm.items() if k != "Hkv"})) == 2
     assert call(params(kv_split=2, **lm), dq=v(0, 32, 4096)) == 6  # dQ over Q
+
+
+def test_kv_walk_hint_range():
+    assert fwd_call(params(bwd_kv_walk=3)) == 2
+    assert fwd_call(params(bwd_kv_walk=-1)) == 2

@@ -240,6 +240,47 @@ def test_backward_decompositions(name, kv_split, q_split, dq_launch):
     compare_full(c, {"dQ": host64(dq), "dK": host64(dk), "dV": host64(dv)}, ref, names=("dQ", "dK", "dV"))
 
 
+@pytest.mark.parametrize("kv_split,q_split", [(1, 1), (3, 2)])
+@pytest.mark.parametrize("name", ["tiny_f32", "dit_sa_ragged", "dit_ca_ragged", "lm_causal_gqa4", "chunk_offset",
+                                  "random_bias_bcast", "d64_bf16", "single_query_single_key", "causal_q_before_keys"])
+def test_backward_role_split_walk(name, kv_split, q_split):
+    """The dK/dV walk split by role (one wave S, P and dV, another dP, dS and dK per 32 keys, P passed
+    through LDS in bf16; bwd_kv_walk = 2) gives the oracle's gradients, fully masked rows and dead key
+    columns exactly zero; fp32 problems ignore the hint."""
+    c = CASES[name]()
+    t = upload(c)
+    say(f"case {name}: role-split dK/dV walk, kv_split {kv_split} q_split {q_split}")
+    o, lse = binding.fwd(t["q"], t["k"], t["v"], mask=t["mask"], scale=c.scale, causal=c.causal,
+                         q_offset=c.q_offset)
+    delta = binding.bwd_preprocess(o, t["do"])
+    dq, dk, dv = binding.bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, mask=t["mask"], scale=c.scale,
+                             causal=c.causal, q_offset=c.q_offset, kv_split=kv_split, q_split=q_split, kv_walk=2)
+    torch.cuda.synchronize()
+    ref = oracle_full(c)
+    compare_full(c, {"dQ": host64(dq), "dK": host64(dk), "dV": host64(dv)}, ref, names=("dQ", "dK", "dV"),
+                 zero_ok=("dQ", "dK") if c.Sk == 1 else ())
+
+
+def test_role_split_walk_chunked():
+    """The role-split walk adding into the window accumulators over a 4-chunk walk equals the one-shot oracle."""
+    W, C = 512, 128
+    c = make_case("role_walk", B=1, Hq=4, Hkv=2, Sq=W, Sk=W, D=128, dtype="bf16", seed=71, causal=True)
+    t = upload(c)
+    dk_acc = torch.zeros((1, c.Hkv, W, c.D), dtype=torch.float32, device="cuda")
+    dv_acc = torch.zeros_like(dk_acc)
+    for p0, n, sk in configs.chunk_plan(W, C):
+        q, do = t["q"][:, :, p0:p0 + n], t["do"][:, :, p0:p0 + n]
+        kk, vv = t["k"][:, :, :sk], t["v"][:, :, :sk]
+        o, lse = binding.fwd(q, kk, vv, scale=c.scale, causal=True, q_offset=p0)
+        delta = binding.bwd_preprocess(o, do)
+        binding.bwd_chunked(q, kk, vv, do, lse, delta, dk_acc, dv_acc, scale=c.scale, causal=True, q_offset=p0,
+                            kv_walk=2)
+    torch.cuda.synchronize()
+    ref = oracle_full(c)
+    compare_full(c, {"dK": dk_acc.cpu().numpy().astype(np.float64), "dV": dv_acc.cpu().numpy().astype(np.float64)},
+                 ref, names=("dK", "dV"))
+
+
 @pytest.mark.parametrize("q_split,q_split_tiles,dq_launch", [(2, 1, 1), (3, 2, 1), (4, 1, 2), (2, 99, 1)])
 @pytest.mark.parametrize("name", ["dit_sa_ragged", "lm_causal_gqa4", "random_bias_bcast", "d64_bf16"])
 def test_backward_split_tail(name, q_split, q_split_tiles, dq_launch):
