@@ -264,8 +264,8 @@ def time_long_window(steps: int, warmup: int, key: str = "long_window") -> dict:
     whole walk (192 launches) is captured in one HIP graph and replayed; FLOPs are the
     walk's exact causal pairs, which equal the one-shot causal run's. With
     key = "long_window_q8" (or "long_window_f16") the window is stored as q8_0 (fp16) and
-    every chunk first writes the bf16 values of the 512 window rows it adds (one pass over
-    the window per walk)."""
+    read in place: the kernels convert each K / V tile to bf16 as they load it, and no
+    bf16 copy of the window exists."""
     import torch
 
     from flash_attention_train_amd import accounting, binding, configs
@@ -275,27 +275,31 @@ def time_long_window(steps: int, warmup: int, key: str = "long_window") -> dict:
     def up(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda")
 
-    q, k, v, do = up(c.q), up(c.k), up(c.v), up(c.do)
+    q, do = up(c.q), up(c.do)
     q8, f16 = c.meta.get("q8"), c.meta.get("f16")
-    if q8 is not None:
-        kq, kd = (torch.from_numpy(a).to("cuda") for a in q8["k"])
-        vq, vd = (torch.from_numpy(a).to("cuda") for a in q8["v"])
-    if f16 is not None:
-        k16, v16 = (torch.from_numpy(f16[n]).to("cuda") for n in ("k", "v"))
-    if q8 is not None or f16 is not None:  # the window's bf16 rows are written by the walk itself
-        k.zero_()
-        v.zero_()
+    sc = {}  # the q8_0 scale planes
+    if q8 is not None:  # the window as stored: int8 quants and their fp16 scales
+        k, sc["k_scale"] = (torch.from_numpy(a).to("cuda") for a in q8["k"])
+        v, sc["v_scale"] = (torch.from_numpy(a).to("cuda") for a in q8["v"])
+    elif f16 is not None:
+        k, v = (torch.from_numpy(f16[n]).to("cuda") for n in ("k", "v"))
+    else:
+        k, v = up(c.k), up(c.v)
     dk_acc = torch.zeros((1, c.Hkv, W, c.D), dtype=torch.float32, device="cuda")
     dv_acc = torch.zeros_like(dk_acc)
     O, dQ = torch.empty_like(q), torch.empty_like(q)
     LSE = torch.empty((1, c.Hq, W), dtype=torch.float32, device="cuda")
     Delta = torch.empty_like(LSE)
     plan = configs.chunk_plan(W, C)
-    need = max(binding.bwd_workspace_bytes(q[:, :, p0:p0 + n], k[:, :, :sk], scale=c.scale, causal=True,
-                                           q_offset=p0) for p0, n, sk in plan)
+
+    def window(sk):  # the K / V rows (and q8_0 scales) the chunk sees
+        return k[:, :, :sk], v[:, :, :sk], {n: x[:, :, :sk] for n, x in sc.items()}
+
+    need = max(binding.bwd_workspace_bytes(q[:, :, p0:p0 + n], window(sk)[0], scale=c.scale, causal=True,
+                                           q_offset=p0, **window(sk)[2]) for p0, n, sk in plan)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
-    fneed = max(binding.fwd_workspace_bytes(q[:, :, p0:p0 + n], k[:, :, :sk], scale=c.scale, causal=True,
-                                            q_offset=p0) for p0, n, sk in plan)
+    fneed = max(binding.fwd_workspace_bytes(q[:, :, p0:p0 + n], window(sk)[0], scale=c.scale, causal=True,
+                                            q_offset=p0, **window(sk)[2]) for p0, n, sk in plan)
     fws = torch.empty(max(fneed, 256), dtype=torch.uint8, device="cuda")
 
     def walk():
@@ -303,18 +307,13 @@ def time_long_window(steps: int, warmup: int, key: str = "long_window") -> dict:
         dv_acc.zero_()
         for p0, n, sk in plan:
             qc, doc = q[:, :, p0:p0 + n], do[:, :, p0:p0 + n]
-            kc, vc = k[:, :, :sk], v[:, :, :sk]
-            if q8 is not None:
-                binding.dequant_q8_0(kq[:, :, p0:sk], kd[:, :, p0:sk], out=k[:, :, p0:sk])
-                binding.dequant_q8_0(vq[:, :, p0:sk], vd[:, :, p0:sk], out=v[:, :, p0:sk])
-            if f16 is not None:
-                binding.convert_f16(k16[:, :, p0:sk], out=k[:, :, p0:sk])
-                binding.convert_f16(v16[:, :, p0:sk], out=v[:, :, p0:sk])
+            kc, vc, skw = window(sk)
             binding.fwd(qc, kc, vc, scale=c.scale, causal=True, q_offset=p0, out=O[:, :, p0:p0 + n],
-                        lse=LSE[:, :, p0:p0 + n], workspace=fws)
+                        lse=LSE[:, :, p0:p0 + n], workspace=fws, **skw)
             binding.bwd_preprocess(O[:, :, p0:p0 + n], doc, delta=Delta[:, :, p0:p0 + n])
             binding.bwd_chunked(qc, kc, vc, doc, LSE[:, :, p0:p0 + n], Delta[:, :, p0:p0 + n], dk_acc, dv_acc,
-                                scale=c.scale, causal=True, q_offset=p0, dq=dQ[:, :, p0:p0 + n], workspace=ws)
+                                scale=c.scale, causal=True, q_offset=p0, dq=dQ[:, :, p0:p0 + n], workspace=ws,
+                                **skw)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

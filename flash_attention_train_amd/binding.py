@@ -20,6 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa_train.so")
 
 FA_F32, FA_BF16 = 0, 1
+FA_KV_DTYPE, FA_KV_F16, FA_KV_Q8_0 = 0, 1, 2
 
 
 class FaView(ctypes.Structure):
@@ -37,7 +38,8 @@ class FaAttnParams(ctypes.Structure):
                 ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
                 ("bwd_dq_launch", ctypes.c_int32), ("sinks", ctypes.c_void_p), ("alibi", ctypes.c_void_p),
                 ("q_split_tiles", ctypes.c_int32), ("mask_stride_h", ctypes.c_int64), ("softcap", ctypes.c_float),
-                ("bwd_kv_walk", ctypes.c_int32)]
+                ("bwd_kv_walk", ctypes.c_int32), ("kv_format", ctypes.c_int32), ("k_scale", FaView),
+                ("v_scale", FaView)]
 
 
 class FaError(RuntimeError):
@@ -145,15 +147,26 @@ def _resident(device, **named) -> None:
             raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
 
 
-def _check_qkv(q, k, v) -> None:
-    """q [B, Hq, Sq, D] in bf16 or fp32; k and v [B, Hkv, Sk, D] in q's dtype."""
+def _check_qkv(q, k, v, k_scale=None, v_scale=None) -> None:
+    """q [B, Hq, Sq, D] in bf16 or fp32; k and v [B, Hkv, Sk, D] in q's dtype, or (bf16 q) a
+    K/V window stored in place: fp16 values, or q8_0 int8 quants with fp16 scale planes
+    k_scale / v_scale [B, Hkv, Sk, D / 32]."""
     _expect("q", q, dtype=(torch.bfloat16, torch.float32))
     if q.dim() != 4:
         raise ValueError("q must be [B, Hq, Sq, D]")
-    _expect("k", k, dtype=q.dtype)
+    stored = (torch.float16, torch.int8) if q.dtype == torch.bfloat16 else ()
+    _expect("k", k, dtype=(q.dtype,) + stored)
     if k.dim() != 4 or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
         raise ValueError(f"k has shape {tuple(k.shape)}, expected [B={q.shape[0]}, Hkv, Sk, D={q.shape[3]}]")
-    _expect("v", v, dtype=q.dtype, shape=k.shape)
+    _expect("v", v, dtype=k.dtype, shape=k.shape)
+    if k.dtype == torch.int8:
+        if k_scale is None or v_scale is None:
+            raise ValueError("a q8_0 K/V window needs k_scale and v_scale")
+        B, H, S, D = k.shape
+        _expect("k_scale", k_scale, dtype=torch.float16, shape=(B, H, S, D // 32))
+        _expect("v_scale", v_scale, dtype=torch.float16, shape=(B, H, S, D // 32))
+    elif k_scale is not None or v_scale is not None:
+        raise ValueError("k_scale / v_scale belong to an int8 (q8_0) K/V window")
 
 
 def _check_rowstats(q, **named) -> None:
@@ -173,7 +186,8 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
                 key_len: Optional[torch.Tensor] = None, q_len: Optional[torch.Tensor] = None,
                 window: tuple = (-1, -1), dq_launch: int = 0,
                 sinks: Optional[torch.Tensor] = None, alibi: Optional[torch.Tensor] = None,
-                q_split_tiles: int = 0, softcap: float = 0.0, kv_walk: int = 0) -> FaAttnParams:
+                q_split_tiles: int = 0, softcap: float = 0.0, kv_walk: int = 0,
+                k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None) -> FaAttnParams:
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Sk, Dk = k.shape
     if Bk != B or Dk != D:
@@ -193,6 +207,12 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
     p.q_split_tiles = int(q_split_tiles)
     p.softcap = float(softcap)
     p.bwd_kv_walk = int(kv_walk)
+    p.kv_format = {torch.float16: FA_KV_F16, torch.int8: FA_KV_Q8_0}.get(k.dtype, FA_KV_DTYPE)
+    if p.kv_format == FA_KV_Q8_0:
+        if k_scale is None or v_scale is None:
+            raise ValueError("a q8_0 K/V window needs k_scale and v_scale")
+        p.k_scale = view4(k_scale)
+        p.v_scale = view4(v_scale)
     for name, t in (("sinks", sinks), ("alibi", alibi)):
         if t is not None:
             if t.dtype != torch.float32 or t.shape != (Hq,) or not t.is_contiguous():
@@ -249,31 +269,31 @@ def mask_tile_count(mask: torch.Tensor) -> int:
 
 
 def fwd_workspace_bytes(q, k, *, scale=None, causal=False, q_offset=None, mask=None, split=0, key_len=None,
-                        q_len=None, window=(-1, -1), softcap=0.0) -> int:
+                        q_len=None, window=(-1, -1), softcap=0.0, k_scale=None, v_scale=None) -> int:
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, fwd_split=split,
-                    key_len=key_len, q_len=q_len, window=window, softcap=softcap)
+                    key_len=key_len, q_len=q_len, window=window, softcap=softcap, k_scale=k_scale, v_scale=v_scale)
     return int(lib().fa_train_fwd_workspace_bytes(ctypes.byref(p)))
 
 
 def fwd(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, out=None, lse=None, stream=None,
         variant=0, mask_tiles=None, workspace=None, split=0, key_len=None, q_len=None, window=(-1, -1),
-        sinks=None, alibi=None, softcap=0.0):
+        sinks=None, alibi=None, softcap=0.0, k_scale=None, v_scale=None):
     """Forward: returns (O, LSE). O has q's dtype and shape; LSE is fp32 [B, Hq, Sq].
     Runs fa_train_fwd_ws: a short grid may split the key walks (split = 0: the library's
     choice; 1: never), with `workspace` (allocated here when None and needed). ``sinks``:
     optional fp32 [Hq] attention-sink logits; ``alibi``: fp32 [Hq] slopes; ``softcap``: a
     logit softcap c > 0 (0 = none)."""
-    _check_qkv(q, k, v)
+    _check_qkv(q, k, v, k_scale, v_scale)
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, fwd_variant=variant,
                     mask_tiles=mask_tiles, fwd_split=split, key_len=key_len, q_len=q_len, window=window,
-                    sinks=sinks, alibi=alibi, softcap=softcap)
+                    sinks=sinks, alibi=alibi, softcap=softcap, k_scale=k_scale, v_scale=v_scale)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     _expect("out", out, dtype=q.dtype, shape=q.shape)
     _check_rowstats(q, lse=lse)
-    _resident(q.device, q=q, k=k, v=v, out=out, lse=lse, workspace=workspace, mask=mask, mask_tiles=mask_tiles,
+    _resident(q.device, q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, out=out, lse=lse, workspace=workspace, mask=mask, mask_tiles=mask_tiles,
               key_len=key_len, q_len=q_len, sinks=sinks, alibi=alibi)
     need = int(lib().fa_train_fwd_workspace_bytes(ctypes.byref(p)))
     if need == ctypes.c_size_t(-1).value:
@@ -289,20 +309,20 @@ def fwd(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, out=None
 
 def fwd_unsplit(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, out=None, lse=None, stream=None,
                 variant=0, mask_tiles=None, key_len=None, q_len=None, window=(-1, -1), sinks=None, alibi=None,
-                softcap=0.0):
+                softcap=0.0, k_scale=None, v_scale=None):
     """Forward through fa_train_fwd, the entry point without a workspace: the same results as
     fwd() (O, LSE), but every query tile's key walk stays in one workgroup."""
-    _check_qkv(q, k, v)
+    _check_qkv(q, k, v, k_scale, v_scale)
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, fwd_variant=variant,
                     mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, window=window, sinks=sinks, alibi=alibi,
-                    softcap=softcap)
+                    softcap=softcap, k_scale=k_scale, v_scale=v_scale)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     _expect("out", out, dtype=q.dtype, shape=q.shape)
     _check_rowstats(q, lse=lse)
-    _resident(q.device, q=q, k=k, v=v, out=out, lse=lse, mask=mask, mask_tiles=mask_tiles, key_len=key_len,
+    _resident(q.device, q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, out=out, lse=lse, mask=mask, mask_tiles=mask_tiles, key_len=key_len,
               q_len=q_len, sinks=sinks, alibi=alibi)
     _check("fa_train_fwd", lib().fa_train_fwd(ctypes.byref(p), view4(q), view4(k), view4(v), view4(out), view3(lse),
                                               _stream_handle(stream)))
@@ -389,10 +409,11 @@ def convert_f16(src, *, out=None, dtype=None, stream=None):
 
 
 def bwd_workspace_bytes(q, k, *, scale=None, causal=False, q_offset=None, mask=None, kv_split=0, q_split=0,
-                        key_len=None, q_len=None, window=(-1, -1), q_split_tiles=0, softcap=0.0) -> int:
+                        key_len=None, q_len=None, window=(-1, -1), q_split_tiles=0, softcap=0.0, k_scale=None,
+                        v_scale=None) -> int:
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, key_len=key_len, q_len=q_len, window=window, q_split_tiles=q_split_tiles,
-                    softcap=softcap)
+                    softcap=softcap, k_scale=k_scale, v_scale=v_scale)
     return int(lib().fa_train_bwd_workspace_bytes(ctypes.byref(p)))
 
 
@@ -409,21 +430,22 @@ def _workspace(p: FaAttnParams, device, workspace):
 
 def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_offset=None, dq=None, dk=None,
         dv=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None, q_len=None,
-        window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0):
+        window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0, k_scale=None, v_scale=None):
     """Backward: returns (dQ, dK, dV), each in q's dtype, overwritten."""
-    _check_qkv(q, k, v)
+    _check_qkv(q, k, v, k_scale, v_scale)
     _expect("dout", dout, dtype=q.dtype, shape=q.shape)
     _check_rowstats(q, lse=lse, delta=delta)
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, window=window,
-                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles, softcap=softcap, kv_walk=kv_walk)
+                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles, softcap=softcap, kv_walk=kv_walk, k_scale=k_scale, v_scale=v_scale)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
-    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
-    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    # (dK / dV in the compute dtype also for a K/V window stored as fp16 or q8_0)
+    dk = torch.empty(k.shape, dtype=q.dtype, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=q.dtype, device=q.device) if dv is None else dv
     _expect("dq", dq, dtype=q.dtype, shape=q.shape)
     _expect("dk", dk, dtype=q.dtype, shape=k.shape)
     _expect("dv", dv, dtype=q.dtype, shape=k.shape)
-    _resident(q.device, q=q, k=k, v=v, dout=dout, lse=lse, delta=delta, dq=dq, dk=dk, dv=dv, mask=mask,
+    _resident(q.device, q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, dout=dout, lse=lse, delta=delta, dq=dq, dk=dk, dv=dv, mask=mask,
               mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, alibi=alibi)
     ws, nbytes = _workspace(p, q.device, workspace)
     _check("fa_train_bwd", lib().fa_train_bwd(ctypes.byref(p), view4(q), view4(k), view4(v), view4(dout), view3(lse),
@@ -434,23 +456,24 @@ def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_off
 
 def bwd_noalloc(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_offset=None, dq=None,
                 dk=None, dv=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None, q_len=None,
-                window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0):
+                window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0, k_scale=None, v_scale=None):
     """Backward through fa_train_bwd_noalloc: the results of bwd(), with the workspace taken from
     the library's static device scratch instead of an allocation (dQ, dK and dV are still the
     caller's; pass them to allocate nothing here either)."""
-    _check_qkv(q, k, v)
+    _check_qkv(q, k, v, k_scale, v_scale)
     _expect("dout", dout, dtype=q.dtype, shape=q.shape)
     _check_rowstats(q, lse=lse, delta=delta)
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, window=window,
-                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles, softcap=softcap, kv_walk=kv_walk)
+                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles, softcap=softcap, kv_walk=kv_walk, k_scale=k_scale, v_scale=v_scale)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
-    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
-    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    # (dK / dV in the compute dtype also for a K/V window stored as fp16 or q8_0)
+    dk = torch.empty(k.shape, dtype=q.dtype, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=q.dtype, device=q.device) if dv is None else dv
     _expect("dq", dq, dtype=q.dtype, shape=q.shape)
     _expect("dk", dk, dtype=q.dtype, shape=k.shape)
     _expect("dv", dv, dtype=q.dtype, shape=k.shape)
-    _resident(q.device, q=q, k=k, v=v, dout=dout, lse=lse, delta=delta, dq=dq, dk=dk, dv=dv, mask=mask,
+    _resident(q.device, q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, dout=dout, lse=lse, delta=delta, dq=dq, dk=dk, dv=dv, mask=mask,
               mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, alibi=alibi)
     _check("fa_train_bwd_noalloc",
            lib().fa_train_bwd_noalloc(ctypes.byref(p), view4(q), view4(k), view4(v), view4(dout), view3(lse),
@@ -501,16 +524,16 @@ def tune_bwd_splits(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=
 
 def bwd_chunked(q, k, v, dout, lse, delta, dk_acc, dv_acc, *, mask=None, scale=None, causal=True, q_offset=None,
                 dq=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None,
-                q_len=None, window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0):
+                q_len=None, window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0, k_scale=None, v_scale=None):
     """Chunked backward: returns dQ for the chunk; ADDS dK/dV into the fp32 window
     accumulators ``dk_acc`` / ``dv_acc`` ([B, Hkv, >= Sk, D])."""
-    _check_qkv(q, k, v)
+    _check_qkv(q, k, v, k_scale, v_scale)
     _expect("dout", dout, dtype=q.dtype, shape=q.shape)
     _check_rowstats(q, lse=lse, delta=delta)
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len,
                     q_len=q_len, window=window, dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles,
-                    softcap=softcap, kv_walk=kv_walk)
+                    softcap=softcap, kv_walk=kv_walk, k_scale=k_scale, v_scale=v_scale)
     if dk_acc.dtype != torch.float32 or dv_acc.dtype != torch.float32:
         raise TypeError("the window accumulators must be float32")
     B, Hkv, Sk, D = k.shape
@@ -519,7 +542,7 @@ def bwd_chunked(q, k, v, dout, lse, delta, dk_acc, dv_acc, *, mask=None, scale=N
             raise ValueError(f"{name} has shape {tuple(acc.shape)}, expected [{B}, {Hkv}, >= {Sk}, {D}]")
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     _expect("dq", dq, dtype=q.dtype, shape=q.shape)
-    _resident(q.device, q=q, k=k, v=v, dout=dout, lse=lse, delta=delta, dq=dq, dk_acc=dk_acc, dv_acc=dv_acc,
+    _resident(q.device, q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, dout=dout, lse=lse, delta=delta, dq=dq, dk_acc=dk_acc, dv_acc=dv_acc,
               mask=mask, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, alibi=alibi)
     ws, nbytes = _workspace(p, q.device, workspace)
     _check("fa_train_bwd_chunked",

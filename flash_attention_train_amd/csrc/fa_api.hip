@@ -88,6 +88,13 @@ fa_status check_params(const fa_attn_params* p) {
   if (p->fwd_variant < 0 || p->fwd_variant > 3) return fail(FA_ERR_SHAPE, "unknown forward variant %d", p->fwd_variant);
   if (p->q_split_tiles < 0) return fail(FA_ERR_SHAPE, "q_split_tiles must be >= 0");
   if (p->bwd_kv_walk < 0 || p->bwd_kv_walk > 2) return fail(FA_ERR_SHAPE, "bwd_kv_walk %d (0, 1 or 2)", p->bwd_kv_walk);
+  if (p->kv_format < FA_KV_DTYPE || p->kv_format > FA_KV_Q8_0)
+    return fail(FA_ERR_DTYPE, "unknown kv_format %d", p->kv_format);
+  if (p->kv_format != FA_KV_DTYPE) {
+    if (p->dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "stored K / V formats need bf16 problems");
+    if (p->mask || p->alibi || p->softcap != 0.f)
+      return fail(FA_ERR_UNSUPPORTED, "stored K / V formats take no dense mask, ALiBi or softcap");
+  }
   if (p->kv_split < 0 || p->kv_split > 64 || p->q_split < 0 || p->q_split > 64 || p->fwd_split < 0 ||
       p->fwd_split > 64)
     return fail(FA_ERR_SHAPE, "split hints must be in 0 .. 64");
@@ -160,7 +167,43 @@ fa::AttnShape shape_of(const fa_attn_params* p) {
   a.wr = p->window_right;
   a.alibi = p->alibi;
   a.softcap = p->softcap;
+  a.kvf = p->kv_format == FA_KV_F16 ? fa::kKvF16 : p->kv_format == FA_KV_Q8_0 ? fa::kKvQ8 : fa::kKvBf16;
+  const bool q8 = p->kv_format == FA_KV_Q8_0;
+  a.kscale = q8 ? static_cast<const _Float16*>(p->k_scale.data) : nullptr;
+  a.vscale = q8 ? static_cast<const _Float16*>(p->v_scale.data) : nullptr;
+  a.sks = q8 ? fa::Strides{p->k_scale.stride_b, p->k_scale.stride_h, p->k_scale.stride_s} : fa::Strides{0, 0, 0};
+  a.svs = q8 ? fa::Strides{p->v_scale.stride_b, p->v_scale.stride_h, p->v_scale.stride_s} : fa::Strides{0, 0, 0};
   return a;
+}
+
+// Bytes per stored K / V element, and the checks of the K / V views and (q8_0) their scale
+// planes; `ins` receives their extents for the alias checks.
+int kv_elt(const fa_attn_params* p) {
+  return p->kv_format == FA_KV_Q8_0 ? 1 : p->kv_format == FA_KV_F16 ? 2 : (p->dtype == FA_BF16 ? 2 : 4);
+}
+fa_status check_kv(const fa_attn_params* p, const fa_view* k, const fa_view* v, Extent* ins, int* n_in,
+                   const char** in_names) {
+  fa_status s;
+  const int e = kv_elt(p);
+  Extent ek, ev;
+  if ((s = check_view(k, "k", p->B, p->Hkv, p->Sk, p->D, e, true, false, &ek))) return s;
+  if ((s = check_view(v, "v", p->B, p->Hkv, p->Sk, p->D, e, true, false, &ev))) return s;
+  ins[*n_in] = ek;
+  in_names[(*n_in)++] = "k";
+  ins[*n_in] = ev;
+  in_names[(*n_in)++] = "v";
+  if (p->kv_format == FA_KV_Q8_0) {
+    Extent eks, evs;
+    if ((s = check_view(&p->k_scale, "k_scale", p->B, p->Hkv, p->Sk, p->D / 32, 2, false, false, &eks))) return s;
+    if ((s = check_view(&p->v_scale, "v_scale", p->B, p->Hkv, p->Sk, p->D / 32, 2, false, false, &evs))) return s;
+    if (p->Sk > 1 && (p->k_scale.stride_s < p->D / 32 || p->v_scale.stride_s < p->D / 32))
+      return fail(FA_ERR_STRIDE, "k_scale / v_scale: stride_s must cover a row's D / 32 scales");
+    ins[*n_in] = eks;
+    in_names[(*n_in)++] = "k_scale";
+    ins[*n_in] = evs;
+    in_names[(*n_in)++] = "v_scale";
+  }
+  return FA_OK;
 }
 
 // The generic backward (fa_bwd.hip) runs fp32 problems and logit softcaps over a dense
@@ -398,10 +441,12 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   fa_status s = check_params(p);
   if (s) return s;
   const int elt = elt_of(p);
-  Extent eq, ek, ev, edo, el, ed, edq, edk, edv;
+  Extent eq, edo, el, ed, edq, edk, edv;
+  Extent kvx[4];
+  const char* kv_names[4];
+  int n_kv = 0;
   if ((s = check_view(q, "q", p->B, p->Hq, p->Sq, p->D, elt, true, false, &eq))) return s;
-  if ((s = check_view(k, "k", p->B, p->Hkv, p->Sk, p->D, elt, true, false, &ek))) return s;
-  if ((s = check_view(v, "v", p->B, p->Hkv, p->Sk, p->D, elt, true, false, &ev))) return s;
+  if ((s = check_kv(p, k, v, kvx, &n_kv, kv_names))) return s;
   if ((s = check_view(dout, "dout", p->B, p->Hq, p->Sq, p->D, elt, true, false, &edo))) return s;
   if (!lse || !delta) return fail(FA_ERR_NULL, "lse or delta view is NULL");
   if (lse->stride_s != 1 || delta->stride_s != 1) return fail(FA_ERR_STRIDE, "lse / delta stride_s must be 1");
@@ -425,10 +470,17 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   }
   const uintptr_t wlo = reinterpret_cast<uintptr_t>(workspace);
   Extent ews = {wlo, use_scratch ? wlo : wlo + need};  // (the static array is nobody else's memory)
-  Extent ins[8] = {eq, ek, ev, edo, el, ed, {0, 0}, {0, 0}};
-  const char* in_names[8] = {"q", "k", "v", "dout", "lse", "delta", "mask", "-"};
-  int n_in = 6;
-  if (p->mask) ins[n_in++] = mask_extent(p);
+  Extent ins[10] = {eq, edo, el, ed};
+  const char* in_names[10] = {"q", "dout", "lse", "delta"};
+  int n_in = 4;
+  for (int i = 0; i < n_kv; ++i) {
+    in_names[n_in] = kv_names[i];
+    ins[n_in++] = kvx[i];
+  }
+  if (p->mask) {
+    in_names[n_in] = "mask";
+    ins[n_in++] = mask_extent(p);
+  }
   Extent outs[4] = {edq, edk, edv, ews};
   const char* out_names[4] = {"dq", accumulate ? "dk_acc" : "dk", accumulate ? "dv_acc" : "dv", "workspace"};
   if ((s = check_alias(outs, 4, out_names, ins, n_in, in_names))) return s;
@@ -473,7 +525,7 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
     // softcap variant): measured on MI355X, the role-split walk waits on its barriers and P
     // hand-over 55% of the time and stages a pair's tiles per 64 keys instead of 128, and was
     // 20-60% slower on the DiT and LM workloads
-    const int kv_role = p->softcap > 0.f ? 0 : (p->bwd_kv_walk == 2 ? 1 : 0);
+    const int kv_role = p->softcap > 0.f || p->kv_format != FA_KV_DTYPE ? 0 : (p->bwd_kv_walk == 2 ? 1 : 0);
     fa::plan_bwd_bf16(a.a, kv, q, qt, 0, &plan, kv_role);
     // a large dQ grid runs as its own kernel, two workgroups per compute unit (measured on
     // the causal LM backward: 659 -> 631 us); small grids keep one launch, whose dQ
@@ -566,18 +618,21 @@ fa_status fwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   if (!with_ws && p->fwd_split > 1)
     return fail(FA_ERR_WORKSPACE, "fwd_split %d needs a workspace: call fa_train_fwd_ws", p->fwd_split);
   const int elt = elt_of(p);
-  Extent eq, ek, ev, eo, el;
+  Extent eq, eo, el;
+  Extent ins[6];
+  const char* in_names[6] = {"q"};
+  int n_in = 1;
   if ((s = check_view(q, "q", p->B, p->Hq, p->Sq, p->D, elt, true, false, &eq))) return s;
-  if ((s = check_view(k, "k", p->B, p->Hkv, p->Sk, p->D, elt, true, false, &ek))) return s;
-  if ((s = check_view(v, "v", p->B, p->Hkv, p->Sk, p->D, elt, true, false, &ev))) return s;
+  ins[0] = eq;
+  if ((s = check_kv(p, k, v, ins, &n_in, in_names))) return s;
   if ((s = check_view(o, "o", p->B, p->Hq, p->Sq, p->D, elt, true, true, &eo))) return s;
   if (!lse) return fail(FA_ERR_NULL, "lse view is NULL");
   if (lse->stride_s != 1) return fail(FA_ERR_STRIDE, "lse stride_s must be 1");
   if ((s = check_view(lse, "lse", p->B, p->Hq, p->Sq, 1, 4, false, true, &el))) return s;
-  Extent ins[4] = {eq, ek, ev, {0, 0}};
-  const char* in_names[4] = {"q", "k", "v", "mask"};
-  int n_in = 3;
-  if (p->mask) ins[n_in++] = mask_extent(p);
+  if (p->mask) {
+    in_names[n_in] = "mask";
+    ins[n_in++] = mask_extent(p);
+  }
   const int splits = with_ws ? choose_fwd_split(p) : 1;
   const size_t need = splits > 1 ? fwd_workspace_bytes(p) : 0;
   if (need > 0) {

@@ -208,7 +208,7 @@ struct LiveWords {
 // applied, and each slice reads -LSE / scale of its rows from the augmented rows in LDS.
 // tanh(x) = 1 - 2 / (e^(2x) + 1) from the hardware exp2 and reciprocal, as in the forward;
 // dS carries the cap's derivative 1 - tanh^2.
-template <int D, bool CAUSAL, bool MASK, bool BIAS, bool CAP = false>
+template <int D, bool CAUSAL, bool MASK, bool BIAS, bool CAP = false, int KVF = 0>
 __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
   constexpr int DS = D / 16, DB = D / 32;
   static_assert(8 % DS == 0 && 8 % (2 * DB) == 0, "each woven slice holds whole product pairs");
@@ -245,10 +245,23 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
   #pragma unroll
   for (int e = 0; e < 8; ++e) ones3[e] = (bf16)(g == 0 && e < 3 ? 1.f : 0.f);
   bf16x8 kf[DS], vf[DS];
-  #pragma unroll
-  for (int s = 0; s < DS; ++s) {
-    kf[s] = *reinterpret_cast<const bf16x8*>(K + key_c * args.sk.s + 16 * s + 8 * g);
-    vf[s] = *reinterpret_cast<const bf16x8*>(V + key_c * args.sv.s + 16 * s + 8 * g);
+  if constexpr (KVF == kKvBf16) {
+    #pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      kf[s] = *reinterpret_cast<const bf16x8*>(K + key_c * args.sk.s + 16 * s + 8 * g);
+      vf[s] = *reinterpret_cast<const bf16x8*>(V + key_c * args.sv.s + 16 * s + 8 * g);
+    }
+  } else {  // a stored fp16 / q8_0 window: this lane's key row converted to bf16 in registers
+    constexpr int KVE = KVF == kKvQ8 ? 1 : 2;
+    const char* Kr = static_cast<const char*>(args.k) + (b * args.sk.b + hk * args.sk.h + key_c * args.sk.s) * KVE;
+    const char* Vr = static_cast<const char*>(args.v) + (b * args.sv.b + hk * args.sv.h + key_c * args.sv.s) * KVE;
+    const _Float16* Ks = a.kscale ? a.kscale + b * a.sks.b + hk * a.sks.h + key_c * a.sks.s : nullptr;
+    const _Float16* Vs = a.vscale ? a.vscale + b * a.svs.b + hk * a.svs.h + key_c * a.svs.s : nullptr;
+    #pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      kf[s] = load_cvt8<KVF>(Kr, Ks, 16 * s + 8 * g);
+      vf[s] = load_cvt8<KVF>(Vr, Vs, 16 * s + 8 * g);
+    }
   }
   f32x16 dk[DB], dv[DB];
   #pragma unroll
@@ -1046,7 +1059,7 @@ __device__ __forceinline__ void dkdv_role_unit(const BwdArgs& args, const BwdPla
 // ---------------------------------------------------------------------------
 // dQ workgroup
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool MASK, bool BIAS, bool LOWREG = false, bool CAP = false>
+template <int D, bool CAUSAL, bool MASK, bool BIAS, bool LOWREG = false, bool CAP = false, int KVF = 0>
 __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
   constexpr int DS = D / 16, DB = D / 32;
   using TL = Tile<D>;
@@ -1126,6 +1139,25 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
     TL::template stage<Q_BN, NT, false>(k_lds + buf * Q_BN * D, K + (int64_t)key0 * args.sk.s, args.sk.s, a.Sk - key0);
     TL::template stage<Q_BN, NT, false>(v_lds + buf * Q_BN * D, V + (int64_t)key0 * args.sv.s, args.sv.s, a.Sk - key0);
   };
+  // a stored fp16 / q8_0 window: each tile's loads issued one tile ahead into registers,
+  // converted to bf16 into LDS after the current tile's products
+  constexpr int KVE = KVF == kKvQ8 ? 1 : 2;
+  const char* Kst = static_cast<const char*>(args.k) + (b * args.sk.b + hk * args.sk.h) * KVE;
+  const char* Vst = static_cast<const char*>(args.v) + (b * args.sv.b + hk * args.sv.h) * KVE;
+  const _Float16* Ksc = a.kscale ? a.kscale + b * a.sks.b + hk * a.sks.h : nullptr;
+  const _Float16* Vsc = a.vscale ? a.vscale + b * a.svs.b + hk * a.svs.h : nullptr;
+  CvtStage<D, Q_BN, NT, KVF == 0 ? 1 : KVF> kcs, vcs;
+  auto load_tile = [&](int kt) {
+    const int64_t key0 = (int64_t)kt * Q_BN;
+    kcs.load(Kst + key0 * args.sk.s * KVE, args.sk.s, Ksc ? Ksc + key0 * a.sks.s : nullptr, a.sks.s,
+             a.Sk - (int)key0);
+    vcs.load(Vst + key0 * args.sv.s * KVE, args.sv.s, Vsc ? Vsc + key0 * a.svs.s : nullptr, a.svs.s,
+             a.Sk - (int)key0);
+  };
+  auto commit_tile = [&](int buf) {
+    kcs.commit(k_lds + buf * Q_BN * D);
+    vcs.commit(v_lds + buf * Q_BN * D);
+  };
 
   const int G16 = lane >> 4, L16 = lane & 15;
   const int tr_row = L16 >> 2, tr_col = 16 * (G16 & 1) + 4 * (L16 & 3);
@@ -1172,7 +1204,12 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
   int cls_cur = kTileBias;
   uint64_t wb_cur = ~0ull;
   if (kt < kt_end) {
-    stage_tile(kt, 0);
+    if constexpr (KVF == kKvBf16) {
+      stage_tile(kt, 0);
+    } else {
+      load_tile(kt);
+      commit_tile(0);
+    }
     if (MASK && a.tiles) {
       load_run(kt);
       wait_vm();  // the run's classes, with the first tile
@@ -1189,7 +1226,10 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
     uint64_t wb_next = ~0ull;
     if (ktn < kt_end) {
       mask_state(ktn, cls_next, wb_next);
-      stage_tile(ktn, buf ^ 1);  // lands while this tile is being processed
+      if constexpr (KVF == kKvBf16)
+        stage_tile(ktn, buf ^ 1);  // lands while this tile is being processed
+      else
+        load_tile(ktn);
     }
     const int cls = cls_cur;
     const bool bias = MASK && (cls == kTileBias || a.alibi);  // add mask values and / or ALiBi
@@ -1307,6 +1347,9 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
         for (int db = 0; db < DB; ++db) mma_acc(dq[db], dsf, kbt[hh][db]);
       }
     }
+    if constexpr (KVF != kKvBf16) {
+      if (ktn < kt_end) commit_tile(buf ^ 1);
+    }
     wait_vm();
     __syncthreads();
     kt = ktn;
@@ -1335,7 +1378,7 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
 // Units whose mask blocks carry additive values run a body compiled with the
 // mask-value reads; all others (dead / open / 0-or--inf blocks) a body without them,
 // which keeps that code and its registers out of the common loop.
-template <int D, bool CAUSAL, bool MASK, bool CAP = false>
+template <int D, bool CAUSAL, bool MASK, bool CAP = false, int KVF = 0>
 __global__ __launch_bounds__(NT) void bwd_bf16_kernel(const BwdArgs args, const BwdPlan plan) {
   constexpr int KV_LDS = 3 * 2 * KV_BM * D * 2 + 2 * 3 * KV_BM * 16 * 2;
   constexpr int Q_LDS = 2 * 2 * Q_BN * D * 2;
@@ -1346,17 +1389,17 @@ __global__ __launch_bounds__(NT) void bwd_bf16_kernel(const BwdArgs args, const 
     const KvUnit u = kv_unit_of(a, plan, blk);
     if (MASK && any_bias_block(a, u.b, 0, (a.Sq + kMaskTile - 1) / kMaskTile, u.kt * (KV_BN / kMaskTile),
                                KV_BN / kMaskTile))
-      dkdv_unit<D, CAUSAL, MASK, true, CAP>(args, plan, blk, smem);
+      dkdv_unit<D, CAUSAL, MASK, true, CAP, KVF>(args, plan, blk, smem);
     else
-      dkdv_unit<D, CAUSAL, MASK, false, CAP>(args, plan, blk, smem);
+      dkdv_unit<D, CAUSAL, MASK, false, CAP, KVF>(args, plan, blk, smem);
   } else {
     const int unit = blk - plan.n_kv_units;
     const QUnit u = q_unit_of(a, plan, unit);
     if (MASK && any_bias_block(a, u.b, u.qt * (Q_BM / kMaskTile), Q_BM / kMaskTile, 0,
                                (a.Sk + kMaskTile - 1) / kMaskTile))
-      dq_unit<D, CAUSAL, MASK, true, false, CAP>(args, plan, unit, smem);
+      dq_unit<D, CAUSAL, MASK, true, false, CAP, KVF>(args, plan, unit, smem);
     else
-      dq_unit<D, CAUSAL, MASK, false, false, CAP>(args, plan, unit, smem);
+      dq_unit<D, CAUSAL, MASK, false, false, CAP, KVF>(args, plan, unit, smem);
   }
 }
 
@@ -1380,7 +1423,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_role_kernel(const BwdArgs args, con
 // The dQ walk as a kernel of its own: its registers fit two workgroups per compute unit
 // (the dK/dV walk's do not), so that one workgroup's LDS and memory waits are covered by
 // the other's products. Launched after the dK/dV-only grid when the plan asks for it.
-template <int D, bool CAUSAL, bool MASK, bool CAP = false>
+template <int D, bool CAUSAL, bool MASK, bool CAP = false, int KVF = 0>
 __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(const BwdArgs args, const BwdPlan plan) {
   constexpr int Q_LDS = 2 * 2 * Q_BN * D * 2;
   __shared__ __attribute__((aligned(16))) char smem[Q_LDS];
@@ -1389,41 +1432,47 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(const BwdArgs args, const
   const QUnit u = q_unit_of(a, plan, unit);
   if (MASK && any_bias_block(a, u.b, u.qt * (Q_BM / kMaskTile), Q_BM / kMaskTile, 0,
                              (a.Sk + kMaskTile - 1) / kMaskTile))
-    dq_unit<D, CAUSAL, MASK, true, true, CAP>(args, plan, unit, smem);
+    dq_unit<D, CAUSAL, MASK, true, true, CAP, KVF>(args, plan, unit, smem);
   else
-    dq_unit<D, CAUSAL, MASK, false, true, CAP>(args, plan, unit, smem);
+    dq_unit<D, CAUSAL, MASK, false, true, CAP, KVF>(args, plan, unit, smem);
 }
 
-template <int D, bool CAUSAL, bool MASK, bool CAP = false>
+template <int D, bool CAUSAL, bool MASK, bool CAP = false, int KVF = 0>
 hipError_t launch_cm(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream) {
-  if constexpr (!CAP) {
+  if constexpr (!CAP && KVF == 0) {
     if (plan.kv_role) {
       if (plan.n_kv_units > 0)
         hipLaunchKernelGGL((bwd_role_kernel<D, CAUSAL, MASK>), dim3(plan.n_kv_units), dim3(NT), 0, stream, args, plan);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess || plan.n_q_units == 0) return e;
-      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, MASK, CAP>), dim3(plan.n_q_units), dim3(NT), 0, stream, args,
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, MASK, CAP, KVF>), dim3(plan.n_q_units), dim3(NT), 0, stream, args,
                          plan);
       return hipGetLastError();
     }
   }
   if (!plan.dq_separate) {
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, MASK, CAP>), dim3(plan.n_kv_units + plan.n_q_units), dim3(NT), 0,
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, MASK, CAP, KVF>), dim3(plan.n_kv_units + plan.n_q_units), dim3(NT), 0,
                        stream, args, plan);
     return hipGetLastError();
   }
   if (plan.n_kv_units > 0)
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, MASK, CAP>), dim3(plan.n_kv_units), dim3(NT), 0, stream, args,
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, MASK, CAP, KVF>), dim3(plan.n_kv_units), dim3(NT), 0, stream, args,
                        plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.n_q_units == 0) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, MASK, CAP>), dim3(plan.n_q_units), dim3(NT), 0, stream, args, plan);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, MASK, CAP, KVF>), dim3(plan.n_q_units), dim3(NT), 0, stream, args, plan);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_t(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream) {
   const bool causal = args.a.causal != 0, mask = args.a.mask != nullptr || args.a.alibi != nullptr;
+  if (args.a.kvf == kKvQ8)  // a stored window: no dense mask, ALiBi or softcap (checked on the host)
+    return causal ? launch_cm<D, true, false, false, kKvQ8>(args, plan, stream)
+                  : launch_cm<D, false, false, false, kKvQ8>(args, plan, stream);
+  if (args.a.kvf == kKvF16)
+    return causal ? launch_cm<D, true, false, false, kKvF16>(args, plan, stream)
+                  : launch_cm<D, false, false, false, kKvF16>(args, plan, stream);
   if (args.a.softcap > 0.f && !mask)  // (a softcap with a dense mask runs on the generic kernels)
     return causal ? launch_cm<D, true, false, true>(args, plan, stream) : launch_cm<D, false, false, true>(args, plan, stream);
   if (causal && mask) return launch_cm<D, true, true>(args, plan, stream);

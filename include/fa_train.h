@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FA_TRAIN_ABI_VERSION 11
+#define FA_TRAIN_ABI_VERSION 12
 
 typedef enum fa_status {
     FA_OK = 0,
@@ -179,7 +179,25 @@ typedef struct fa_attn_params {
      * each 32 keys (64-key workgroups, two per compute unit, P passed between them in bf16;
      * the dQ walk then runs as its own kernel). A logit softcap always takes walk 1. */
     int32_t bwd_kv_walk;
+    /* Storage of K and V (bf16 problems only): FA_KV_DTYPE = the dtype above; FA_KV_F16 = fp16
+     * values; FA_KV_Q8_0 = ggml's q8_0 blocks held as two planes, int8 quants in the k / v views
+     * (element = byte strides) and one fp16 scale per 32 consecutive values along D in
+     * k_scale / v_scale ([B, Hkv, Sk, D / 32], element strides), the stored value being
+     * scale * quant. The kernels convert every K / V value they read to bf16 (fp16 widened
+     * exactly, the q8_0 product exact in fp32, then one rounding to nearest even), so a
+     * quantised or fp16 K/V window is attended to and trained in place, with no bf16 copy
+     * (llama.cpp pull request 57: a q8_0 cache trains in place). dK and dV are the gradients
+     * of the stored values, in the output dtype (bf16) or added into fp32 accumulators by
+     * fa_train_bwd_chunked. Not combined with a dense mask, ALiBi or a logit softcap
+     * (FA_ERR_UNSUPPORTED). */
+    int32_t kv_format;
+    fa_view k_scale;
+    fa_view v_scale;
 } fa_attn_params;
+
+#define FA_KV_DTYPE 0
+#define FA_KV_F16 1
+#define FA_KV_Q8_0 2
 
 /* Forward: writes O (dtype) and LSE (fp32, natural log). Fully masked rows get
  * O = 0 and LSE = 0. O must not overlap Q, K or V. */

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(L, n), n
         assert n in B.SIGNATURES, f"{n} has no ctypes signature in the binding"
-    assert L.fa_train_version() == 11
+    assert L.fa_train_version() == 12
 
 
 BASE = 0x7F0000000000  # fake, 256-byte aligned device addresses
@@ -44,7 +44,8 @@ def params(**kw):
     a = dict(B=1, Hq=4, Hkv=2, Sq=64, Sk=64, D=64, dtype=B.FA_BF16, causal=0, q_offset=0, scale=0.125, mask=None,
              mask_stride_b=0, mask_stride_q=0, mask_tiles=None, fwd_variant=0, kv_split=0, q_split=0, fwd_split=0, key_len=None, q_len=None,
              window_left=-1, window_right=-1, bwd_dq_launch=0, sinks=None, alibi=None,
-             q_split_tiles=0, mask_stride_h=0, softcap=0.0, bwd_kv_walk=0)
+             q_split_tiles=0, mask_stride_h=0, softcap=0.0, bwd_kv_walk=0, kv_format=0, k_scale=B.FaView(),
+             v_scale=B.FaView())
     a.update(kw)
     return B.FaAttnParams(*(a[f] for f, _ in B.FaAttnParams._fields_))
 
@@ -279,3 +280,30 @@ def test_backward_noalloc_rejects_before_any_launch():
 def test_kv_walk_hint_range():
     assert fwd_call(params(bwd_kv_walk=3)) == 2
     assert fwd_call(params(bwd_kv_walk=-1)) == 2
+
+
+def test_stored_kv_formats_rejected_where_unsupported():
+    """K / V stored as fp16 or q8_0: bf16 problems only, no dense mask, ALiBi or softcap; q8_0 needs
+    its fp16 scale planes, [B, Hkv, Sk, D / 32] with rows covering their D / 32 scales."""
+    def kv8(i):  # int8 quants [1, 2, 64, 64]
+        return view(i, H=2, elt=1)
+
+    def scales(i, **kw):
+        a = dict(data=BASE + i * (1 << 24), stride_b=2 * 64 * 2, stride_h=64 * 2, stride_s=2)
+        a.update(kw)
+        return B.FaView(a["data"], a["stride_b"], a["stride_h"], a["stride_s"])
+
+    q8 = dict(kv_format=2, k_scale=scales(10), v_scale=scales(11))
+    assert fwd_call(params(kv_format=3)) == 3
+    assert fwd_call(params(dtype=B.FA_F32, kv_format=1)) == 7
+    assert fwd_call(params(kv_format=1, mask=BASE + 9 * (1 << 24), mask_stride_q=64)) == 7
+    assert fwd_call(params(kv_format=1, alibi=BASE + 9 * (1 << 24))) == 7
+    assert fwd_call(params(kv_format=1, softcap=30.0)) == 7
+    assert fwd_call(params(kv_format=2), k=kv8(1), v=kv8(2)) == 1  # no scale planes
+    assert fwd_call(params(kv_format=2, k_scale=scales(10, stride_s=1), v_scale=scales(11)), k=kv8(1), v=kv8(2)) == 4
+    assert fwd_call(params(kv_format=2, k_scale=scales(10, data=BASE + 10 * (1 << 24) + 1), v_scale=scales(11)),
+                    k=kv8(1), v=kv8(2)) == 5
+    assert fwd_call(params(kv_format=2, k_scale=scales(3), v_scale=scales(11)), k=kv8(1), v=kv8(2)) == 6  # over O
+    p = params(**q8)
+    assert B.lib().fa_train_bwd(ctypes.byref(p), view(0), kv8(1), kv8(2), view(3), lse_view(4), lse_view(5),
+                                view(6), view(7, H=2), view(11, H=2), None, 0, None) == 6  # dV over v_scale
