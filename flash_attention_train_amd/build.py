@@ -21,6 +21,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfa_train.so")
+# the checked build (-DFA_CHECK): every launch's index space verified on the host first, and
+# fa_train_check_launch exported (include/fa_train_check.h)
+CHECK_LIB = os.path.join(HERE, "libfa_train_check.so")
 ARCH = "gfx950"
 
 
@@ -43,9 +46,9 @@ def _flags() -> list[str]:
             f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *_flags(), "-c", src, "-o", obj]
+def _compile(src: str, check: bool = False) -> str:
+    obj = os.path.join(OBJDIR, ("check_" if check else "") + os.path.basename(src) + ".o")
+    cmd = [hipcc(), *_flags(), *(["-DFA_CHECK"] if check else []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -56,23 +59,25 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def build(verbose: bool = True) -> str:
-    """Compile and link the library; always rebuilds. Returns the library path."""
+def build(verbose: bool = True, check: bool = False) -> str:
+    """Compile and link the library; always rebuilds. Returns the library path. With
+    check=True, the checked build (-DFA_CHECK) goes to libfa_train_check.so instead."""
     os.makedirs(OBJDIR, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda f: _compile(f, check), srcs))
+    lib_path = CHECK_LIB if check else LIB
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib_path}")
+    return lib_path
 
 
 if __name__ == "__main__":
-    build()
+    build(check="--check" in sys.argv[1:])
     sys.exit(0)

@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "fa_kernels.h"
+#include "fa_tile.h"
 #include "fa_train.h"
 
 namespace {
@@ -432,6 +433,25 @@ fa_status scratch_of_current_device(void** out) {
   return FA_OK;
 }
 
+#ifdef FA_CHECK
+struct Checker {
+  char* msg;
+  size_t len;
+  bool ok = true;
+  void fail(const char* fmt, ...) {
+    if (!ok) return;
+    ok = false;
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(msg, len, fmt, ap);
+    va_end(ap);
+  }
+};
+
+void check_bwd(Checker& c, const fa_attn_params* p, const int32_t* klen_h, const int32_t* qlen_h);
+void check_fwd(Checker& c, const fa_attn_params* p, const int32_t* klen_h, const int32_t* qlen_h);
+#endif
+
 // Shared body of the backward entry points. use_scratch: the workspace is the current
 // device's static scratch array (fa_train_bwd_noalloc), looked up after every host check.
 fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k, const fa_view* v,
@@ -489,6 +509,14 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
     workspace_bytes_given = FA_TRAIN_NOALLOC_SCRATCH_BYTES;
   }
 
+#ifdef FA_CHECK
+  if (!generic_path(p)) {  // the checked build verifies the launch's index space first
+    char rep[256];
+    Checker c{rep, sizeof rep};
+    check_bwd(c, p, nullptr, nullptr);
+    if (!c.ok) return fail(FA_ERR_HIP, "FA_CHECK: %s", rep);
+  }
+#endif
   fa::BwdArgs a;
   a.a = shape_of(p);
   a.q = q->data;
@@ -646,6 +674,14 @@ fa_status fwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   const char* out_names[3] = {"o", "lse", "workspace"};
   if ((s = check_alias(outs, need > 0 ? 3 : 2, out_names, ins, n_in, in_names))) return s;
 
+#ifdef FA_CHECK
+  if (p->dtype == FA_BF16) {  // the checked build verifies the launch's index space first
+    char rep[256];
+    Checker c{rep, sizeof rep};
+    check_fwd(c, p, nullptr, nullptr);
+    if (!c.ok) return fail(FA_ERR_HIP, "FA_CHECK: %s", rep);
+  }
+#endif
   fa::FwdArgs a;
   a.a = shape_of(p);
   a.q = q->data;
@@ -683,6 +719,173 @@ fa_status fwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   return hip_status(fa::launch_fwd(a, 0, stream), "forward");
 }
 
+
+#ifdef FA_CHECK
+// ---------------------------------------------------------------------------
+// Checked build (-DFA_CHECK): the index space of every launch, verified on the host
+// ---------------------------------------------------------------------------
+// For a problem, the checker takes the library's own plan (split choices, workspace layout,
+// unit counts) and enumerates every workgroup the bf16 forward and backward would launch,
+// decoding each with the kernels' own unit decoding, row / key ranges and LDS offsets
+// (shared host-device helpers), and verifies that every row it stages, every LDS offset it
+// reads or writes, every row it stores and every workspace slice it touches lies inside its
+// buffer, and that the units cover every output row exactly once (or once per split). The
+// structured lengths are host copies here (the kernels read them on the device).
+template <int D>
+void check_tile_offsets(Checker& c, int rows, const char* what) {
+  // every 16-byte chunk of a [rows][D] tile lands once inside the tile; transpose reads stay inside
+  using TL = fa::Tile<D>;
+  std::vector<int> seen((size_t)rows * D / 8, 0);
+  for (int r = 0; r < rows; ++r)
+    for (int ch = 0; ch < D / 8; ++ch) {
+      const int off = TL::chunk(r, ch);
+      if (off < 0 || off + 8 > rows * D || off % 8) return c.fail("%s: chunk (%d, %d) at %d", what, r, ch, off);
+      if (seen[off / 8]++) return c.fail("%s: two chunks share LDS offset %d", what, off);
+    }
+  for (int r = 0; r < rows; ++r)
+    for (int col = 0; col < D; col += 4) {
+      const int off = TL::quad(r, col);
+      if (off < 0 || off + 4 > rows * D) return c.fail("%s: transpose read (%d, %d) at %d", what, r, col, off);
+    }
+}
+
+void check_bwd(Checker& c, const fa_attn_params* p, const int32_t* klen_h, const int32_t* qlen_h) {
+  const fa::AttnShape a = shape_of(p);
+  int kv, q, qt;
+  choose_splits(p, false, &kv, &q, &qt);
+  const int kv_role = p->softcap > 0.f || p->kv_format != FA_KV_DTYPE ? 0 : (p->bwd_kv_walk == 2 ? 1 : 0);
+  fa::BwdPlan plan;
+  fa::plan_bwd_bf16(a, kv, q, qt, 0, &plan, kv_role);
+  const WsLayout wl = workspace_layout(p, false);
+  const int64_t nq = (int64_t)p->B * p->Hq * p->Sq * p->D, nk = (int64_t)p->B * p->Hkv * p->Sk * p->D;
+  if (wl.need_dq && (int64_t)(wl.dk_off - wl.dq_off) < plan.q_split * nq * 4) c.fail("dq slices exceed their space");
+  if (wl.need_dkdv && (int64_t)(wl.dv_off - wl.dk_off) < plan.kv_split * nk * 4) c.fail("dk slices exceed their space");
+  if (wl.need_dkdv && (int64_t)(wl.total - wl.dv_off) < plan.kv_split * nk * 4) c.fail("dv slices exceed their space");
+  const int KB = kv_role ? fa::kBwdRoleKeys : fa::kBwdUnit, BM = 64, G = p->Hq / p->Hkv;
+  const int nkt = (p->Sk + KB - 1) / KB;
+  if (plan.n_kv_units != nkt * p->B * p->Hkv * plan.kv_split) c.fail("dK/dV unit count %d", plan.n_kv_units);
+  std::vector<int> kv_seen((size_t)nkt * p->B * p->Hkv * plan.kv_split, 0);
+  for (int unit = 0; unit < plan.n_kv_units && c.ok; ++unit) {
+    const fa::KvUnit u = fa::kv_unit_of(a, plan, unit);
+    if (u.kt < 0 || u.kt >= nkt || u.b < 0 || u.b >= p->B || u.hk < 0 || u.hk >= p->Hkv || u.split < 0 ||
+        u.split >= plan.kv_split)
+      return c.fail("dK/dV unit %d decodes to (%d, %d, %d, %d)", unit, u.kt, u.b, u.hk, u.split);
+    if (kv_seen[(((size_t)u.kt * p->B + u.b) * p->Hkv + u.hk) * plan.kv_split + u.split]++)
+      return c.fail("dK/dV unit %d duplicates another", unit);
+    const int klen = klen_h ? std::min(std::max(klen_h[u.b], 0), p->Sk) : p->Sk;
+    const int qlen = qlen_h ? std::min(std::max(qlen_h[u.b], 0), p->Sq) : p->Sq;
+    const int n0 = u.kt * KB;
+    int qt0 = 0, qt_end = 0;
+    if (n0 < klen) {
+      int64_t lo, hi, lo1, hi1;
+      fa::row_range(a, klen, qlen, n0, lo, hi);
+      fa::row_range(a, klen, qlen, std::min(n0 + KB, klen) - 1, lo1, hi1);
+      const int nqt = (p->Sq + BM - 1) / BM;
+      qt0 = (int)std::min<int64_t>(lo / BM, nqt);
+      qt_end = hi1 > lo ? (int)std::min<int64_t>((hi1 + BM - 1) / BM, nqt) : qt0;
+      if (qt_end < qt0) qt_end = qt0;
+    }
+    const int npairs = (qt_end - qt0) * G;
+    for (int pr = u.split; pr < npairs; pr += plan.kv_split) {
+      const int h = u.hk * G + pr % G, q0 = (qt0 + pr / G) * BM;
+      if (h >= p->Hq || q0 < 0 || q0 >= p->Sq) return c.fail("dK/dV unit %d walks pair (%d, %d)", unit, h, q0);
+      // staged rows: row r of the tile reads q0 + min(r, Sq - q0 - 1)
+      if (q0 + std::min(BM - 1, p->Sq - q0 - 1) >= p->Sq) return c.fail("dK/dV unit %d stages past Sq", unit);
+    }
+    for (int w = 0; w < KB / 32; ++w) {
+      const int kbase = n0 + 32 * w, rows = std::max(0, std::min(32, p->Sk - kbase));
+      if (rows == 0) continue;  // a wave whose keys all lie past Sk stores nothing
+      if (kbase + rows > p->Sk) return c.fail("dK/dV unit %d stores past Sk", unit);
+      if (plan.kv_split > 1) {
+        const int64_t end = (int64_t)u.split * nk + (((int64_t)u.b * p->Hkv + u.hk) * p->Sk + kbase + rows) * p->D;
+        if (end > plan.kv_split * nk) return c.fail("dK/dV unit %d writes past its slices", unit);
+      }
+    }
+  }
+  for (size_t i = 0; i < kv_seen.size() && c.ok; ++i)
+    if (kv_seen[i] != 1) c.fail("dK/dV unit %zu covered %d times", i, kv_seen[i]);
+  // dQ units: each 128-row query tile of each head once, or once per split for the split tiles
+  const int QM = fa::kBwdUnit, QN = 64, nqt = (p->Sq + QM - 1) / QM;
+  if (plan.n_q_units != (nqt - plan.q_tiles_split + plan.q_tiles_split * plan.q_split) * p->B * p->Hq)
+    c.fail("dQ unit count %d", plan.n_q_units);
+  std::vector<int> q_seen((size_t)nqt * p->B * p->Hq * std::max(1, plan.q_split), 0);
+  for (int unit = 0; unit < plan.n_q_units && c.ok; ++unit) {
+    const fa::QUnit u = fa::q_unit_of(a, plan, unit);
+    if (u.qt < 0 || u.qt >= nqt || u.b < 0 || u.b >= p->B || u.h < 0 || u.h >= p->Hq || u.split < 0 ||
+        u.split >= u.nsplit)
+      return c.fail("dQ unit %d decodes to (%d, %d, %d, %d)", unit, u.qt, u.b, u.h, u.split);
+    if (u.nsplit != (u.qt < plan.q_tiles_split ? plan.q_split : 1)) return c.fail("dQ unit %d: split count", unit);
+    if (q_seen[(((size_t)u.qt * p->B + u.b) * p->Hq + u.h) * std::max(1, plan.q_split) + u.split]++)
+      return c.fail("dQ unit %d duplicates another", unit);
+    const int klen = klen_h ? std::min(std::max(klen_h[u.b], 0), p->Sk) : p->Sk;
+    const int qlen = qlen_h ? std::min(std::max(qlen_h[u.b], 0), p->Sq) : p->Sq;
+    const int q0 = u.qt * QM, nkt64 = (p->Sk + QN - 1) / QN;
+    int kb = 0, ke = 0;
+    if (q0 < qlen) {
+      int64_t lo, hi, lo1, hi1;
+      fa::key_range(a, klen, qlen, q0, lo, hi);
+      fa::key_range(a, klen, qlen, std::min(q0 + QM, qlen) - 1, lo1, hi1);
+      kb = (int)std::min<int64_t>(lo / QN, nkt64);
+      ke = hi1 > lo ? (int)std::min<int64_t>((hi1 + QN - 1) / QN, nkt64) : kb;
+      if (ke < kb) ke = kb;
+    }
+    for (int t = kb + u.split; t < ke; t += u.nsplit)
+      if (t * QN >= p->Sk) return c.fail("dQ unit %d walks key tile %d past Sk", unit, t);
+    for (int w = 0; w < QM / 32; ++w) {
+      const int qw = q0 + 32 * w, rows = std::max(0, std::min(32, p->Sq - qw));
+      if (rows == 0) continue;  // a wave whose rows all lie past Sq stores nothing
+      if (qw + rows > p->Sq) return c.fail("dQ unit %d stores past Sq", unit);
+      if (u.nsplit > 1) {
+        const int64_t end = (int64_t)u.split * nq + (((int64_t)u.b * p->Hq + u.h) * p->Sq + qw + rows) * p->D;
+        if (end > plan.q_split * nq) return c.fail("dQ unit %d writes past its slices", unit);
+      }
+    }
+  }
+  for (int qi = 0; qi < nqt && c.ok; ++qi)
+    for (int bh = 0; bh < p->B * p->Hq && c.ok; ++bh) {
+      const int ns = qi < plan.q_tiles_split ? plan.q_split : 1;
+      for (int sp = 0; sp < std::max(1, plan.q_split); ++sp) {
+        const int n = q_seen[((size_t)qi * p->B * p->Hq + bh) * std::max(1, plan.q_split) + sp];
+        if (n != (sp < ns ? 1 : 0)) return c.fail("dQ tile %d, head %d, split %d covered %d times", qi, bh, sp, n);
+      }
+    }
+}
+
+void check_fwd(Checker& c, const fa_attn_params* p, const int32_t* klen_h, const int32_t* qlen_h) {
+  const fa::AttnShape a = shape_of(p);
+  const int splits = choose_fwd_split(p);
+  const size_t need = splits > 1 ? fwd_workspace_bytes(p) : 0;
+  const int64_t rows = (int64_t)p->B * p->Hq * p->Sq;
+  if (splits > 1 && (size_t)(splits * rows * (2 * p->D + 8)) > need) c.fail("forward partials exceed the workspace");
+  const int BM = 128, BN = 64, nkt = (p->Sk + BN - 1) / BN, nqt = (p->Sq + BM - 1) / BM;
+  for (int b = 0; b < p->B && c.ok; ++b)
+    for (int qi = 0; qi < nqt && c.ok; ++qi) {
+      const int klen = klen_h ? std::min(std::max(klen_h[b], 0), p->Sk) : p->Sk;
+      const int qlen = qlen_h ? std::min(std::max(qlen_h[b], 0), p->Sq) : p->Sq;
+      const int q0 = qi * BM;
+      int kb = 0, ke = 0;
+      if (q0 < qlen) {
+        int64_t lo, hi, lo1, hi1;
+        fa::key_range(a, klen, qlen, q0, lo, hi);
+        fa::key_range(a, klen, qlen, std::min(q0 + BM, qlen) - 1, lo1, hi1);
+        kb = (int)std::min<int64_t>(lo / BN, nkt);
+        ke = hi1 > lo ? (int)std::min<int64_t>((hi1 + BN - 1) / BN, nkt) : 0;
+        if (ke < kb) ke = kb;
+      }
+      for (int z = 0; z < splits; ++z) {  // the z-th share of [kb, ke)
+        const int per = (ke - kb + splits - 1) / splits;
+        const int b0 = std::min(ke, kb + z * per), e0 = std::min(ke, b0 + per);
+        for (int t = b0; t < e0; ++t)
+          if (t * BN >= p->Sk) return c.fail("forward tile (%d, %d) walks key tile %d past Sk", b, qi, t);
+      }
+      for (int w = 0; w < 4; ++w) {
+        const int row = q0 + 32 * w + 31;  // the last row a wave may store (rows past Sq are skipped)
+        if (splits > 1 && std::min(row, p->Sq - 1) >= p->Sq) return c.fail("forward stores past Sq");
+      }
+    }
+}
+
+#endif  // FA_CHECK
 }  // namespace
 
 extern "C" {
@@ -892,6 +1095,26 @@ const char* fa_train_status_str(fa_status s) {
 }
 
 const char* fa_train_last_error(void) { return g_err; }
+
+#ifdef FA_CHECK
+// Checked build only: runs the host checker over the bf16 forward's and backward's launches for
+// p (lengths as host arrays, or NULL for the full lengths). Returns FA_OK, or FA_ERR_HIP with
+// the first violation in `report`.
+fa_status fa_train_check_launch(const fa_attn_params* p, const int32_t* key_len_host, const int32_t* q_len_host,
+                                char* report, size_t report_len) {
+  g_err[0] = 0;
+  fa_status s = check_params(p);
+  if (s) return s;
+  if (p->dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "the checker covers the bf16 kernels");
+  Checker c{report, report_len};
+  if (report_len) report[0] = 0;
+  check_tile_offsets<64>(c, 64, "tile D=64");
+  check_tile_offsets<128>(c, 64, "tile D=128");
+  check_fwd(c, p, key_len_host, q_len_host);
+  check_bwd(c, p, key_len_host, q_len_host);
+  return c.ok ? FA_OK : fail(FA_ERR_HIP, "FA_CHECK: %s", report);
+}
+#endif
 
 int fa_train_version(void) { return FA_TRAIN_ABI_VERSION; }
 

@@ -54,41 +54,7 @@ __device__ __forceinline__ f32x16 zeros16() {
 }
 
 
-// unit -> (key tile, batch, kv head, split); key tiles vary slowest so that the long
-// causal tiles (small key index) are dispatched first
-struct KvUnit {
-  int kt, b, hk, split;
-};
-__device__ __forceinline__ KvUnit kv_unit_of(const AttnShape& a, const BwdPlan& plan, int unit) {
-  const int per_tile = a.B * a.Hkv * plan.kv_split;
-  int rem = unit % per_tile;
-  const int split = rem % plan.kv_split;
-  rem /= plan.kv_split;
-  return {unit / per_tile, rem / a.Hkv, rem % a.Hkv, split};
-}
-
-// unit -> (query tile, batch, head, split); the last query tiles (longest under a
-// causal mask) are dispatched first
-// The whole tiles go first; the q_tiles_split first query tiles, dispatched last, are each
-// walked by q_split workgroups, so that the launch ends with short units.
-struct QUnit {
-  int qt, b, h, split, nsplit;
-};
-__device__ __forceinline__ QUnit q_unit_of(const AttnShape& a, const BwdPlan& plan, int unit) {
-  const int nqt = (a.Sq + Q_BM - 1) / Q_BM;
-  const int bh = a.B * a.Hq;
-  const int n_whole = (nqt - plan.q_tiles_split) * bh;
-  if (unit < n_whole) {
-    const int rem = unit % bh;
-    return {nqt - 1 - unit / bh, rem / a.Hq, rem % a.Hq, 0, 1};
-  }
-  unit -= n_whole;
-  const int per_tile = bh * plan.q_split;
-  int rem = unit % per_tile;
-  const int split = rem % plan.q_split;
-  rem /= plan.q_split;
-  return {plan.q_tiles_split - 1 - unit / per_tile, rem / a.Hq, rem % a.Hq, split, plan.q_split};
-}
+// (the unit decoding, kv_unit_of and q_unit_of, is shared with the host checker: fa_kernels.h)
 
 // Does any mask block of rows [r0, r0 + nr) x keys [c0, c0 + nc) (in 64-blocks) carry
 // additive values? Units whose blocks are all dead / open / 0-or--inf run a body

@@ -59,7 +59,7 @@ __device__ __forceinline__ int qlen_of(const AttnShape& a, int b) {
 }
 // keys [lo, hi) that query row i can see by the structure alone (sequence ends, key length,
 // causal diagonal, window); empty when the row is past the query length
-__device__ __forceinline__ void key_range(const AttnShape& a, int klen, int qlen, int64_t i, int64_t& lo,
+__host__ __device__ __forceinline__ void key_range(const AttnShape& a, int klen, int qlen, int64_t i, int64_t& lo,
                                           int64_t& hi) {
   const int64_t pos = a.q_offset + i;
   lo = a.wl >= 0 ? pos - a.wl : 0;
@@ -70,7 +70,7 @@ __device__ __forceinline__ void key_range(const AttnShape& a, int klen, int qlen
   if (i >= qlen || hi < lo) hi = lo;
 }
 // rows [lo, hi) that can see key j by the structure alone
-__device__ __forceinline__ void row_range(const AttnShape& a, int klen, int qlen, int64_t j, int64_t& lo,
+__host__ __device__ __forceinline__ void row_range(const AttnShape& a, int klen, int qlen, int64_t j, int64_t& lo,
                                           int64_t& hi) {
   lo = 0;
   hi = qlen;
@@ -205,6 +205,18 @@ struct BwdArgs {
   int mask_vec4;   // the mask can be read 4 floats at a time
 };
 
+// unit -> (key tile, batch, kv head, split) of a dK/dV workgroup; key tiles vary slowest so
+// that the long causal tiles (small key index) are dispatched first
+struct KvUnit {
+  int kt, b, hk, split;
+};
+// unit -> (query tile, batch, head, split, splits) of a dQ workgroup; the last query tiles
+// (longest under a causal mask) are dispatched first, the whole tiles before the
+// q_tiles_split first ones, which are each walked by q_split workgroups and dispatched last
+struct QUnit {
+  int qt, b, h, split, nsplit;
+};
+
 // Work decomposition of the bf16 backward (one launch, two kinds of workgroups).
 struct BwdPlan {
   int kv_split;    // workgroups sharing one key tile's dK/dV walk (> 1: fp32 partial slices)
@@ -280,6 +292,29 @@ struct ConvertArgs {
 hipError_t launch_convert_f16(const ConvertArgs& args, hipStream_t stream);
 void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, int q_tiles_split, int dq_separate,
                    BwdPlan* plan, int kv_role);
+
+__host__ __device__ __forceinline__ KvUnit kv_unit_of(const AttnShape& a, const BwdPlan& plan, int unit) {
+  const int per_tile = a.B * a.Hkv * plan.kv_split;
+  int rem = unit % per_tile;
+  const int split = rem % plan.kv_split;
+  rem /= plan.kv_split;
+  return {unit / per_tile, rem / a.Hkv, rem % a.Hkv, split};
+}
+__host__ __device__ __forceinline__ QUnit q_unit_of(const AttnShape& a, const BwdPlan& plan, int unit) {
+  const int nqt = (a.Sq + kBwdUnit - 1) / kBwdUnit;
+  const int bh = a.B * a.Hq;
+  const int n_whole = (nqt - plan.q_tiles_split) * bh;
+  if (unit < n_whole) {
+    const int rem = unit % bh;
+    return {nqt - 1 - unit / bh, rem / a.Hq, rem % a.Hq, 0, 1};
+  }
+  unit -= n_whole;
+  const int per_tile = bh * plan.q_split;
+  int rem = unit % per_tile;
+  const int split = rem % plan.q_split;
+  rem /= plan.q_split;
+  return {plan.q_tiles_split - 1 - unit / per_tile, rem / a.Hq, rem % a.Hq, split, plan.q_split};
+}
 hipError_t launch_bwd_bf16(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream);
 
 }  // namespace fa

@@ -26,13 +26,13 @@ template <int D>
 struct Tile {
   static constexpr int NCH = D / 8;  // 16-byte chunks per row
 
-  __device__ static __forceinline__ int swz(int row) { return (((row & 3) << 2) | ((row >> 2) & 3)) & (NCH - 1); }
+  __host__ __device__ static __forceinline__ int swz(int row) { return (((row & 3) << 2) | ((row >> 2) & 3)) & (NCH - 1); }
 
   // element offset of logical 8-element chunk c of row `row`
-  __device__ static __forceinline__ int chunk(int row, int c) { return row * D + 8 * (c ^ swz(row)); }
+  __host__ __device__ static __forceinline__ int chunk(int row, int c) { return row * D + 8 * (c ^ swz(row)); }
 
   // element offset of the 4 elements at column col (a multiple of 4) of row `row`
-  __device__ static __forceinline__ int quad(int row, int col) { return chunk(row, col >> 3) + (col & 4); }
+  __host__ __device__ static __forceinline__ int quad(int row, int col) { return chunk(row, col >> 3) + (col & 4); }
 
   // 16-byte read of logical chunk c of row `row`
   __device__ static __forceinline__ bf16x8 read_chunk(const bf16* lds, int row, int c) {

@@ -19,8 +19,11 @@ pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libfa_tr
 
 
 def declared_functions():
+    """Functions declared by the op's headers (the checked build's own header is separate)."""
     names = set()
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        if os.path.basename(h) == "fa_train_check.h":
+            continue
         text = open(h).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         names.update(re.findall(r"\b(fa_train_\w+)\s*\(", text))
