@@ -789,8 +789,10 @@ void check_bwd(Checker& c, const fa_attn_params* p, const int32_t* klen_h, const
     for (int pr = u.split; pr < npairs; pr += plan.kv_split) {
       const int h = u.hk * G + pr % G, q0 = (qt0 + pr / G) * BM;
       if (h >= p->Hq || q0 < 0 || q0 >= p->Sq) return c.fail("dK/dV unit %d walks pair (%d, %d)", unit, h, q0);
-      // staged rows: row r of the tile reads q0 + min(r, Sq - q0 - 1)
-      if (q0 + std::min(BM - 1, p->Sq - q0 - 1) >= p->Sq) return c.fail("dK/dV unit %d stages past Sq", unit);
+      // staged rows: the tile's buffer resource ends after row q0 + v - 1, v = min(BM, Sq - q0)
+      // (later rows arrive as zeros)
+      const int v = std::min(BM, p->Sq - q0);
+      if (v < 1 || q0 + v - 1 >= p->Sq) return c.fail("dK/dV unit %d stages past Sq", unit);
     }
     for (int w = 0; w < KB / 32; ++w) {
       const int kbase = n0 + 32 * w, rows = std::max(0, std::min(32, p->Sk - kbase));
@@ -829,7 +831,7 @@ void check_bwd(Checker& c, const fa_attn_params* p, const int32_t* klen_h, const
       ke = hi1 > lo ? (int)std::min<int64_t>((hi1 + QN - 1) / QN, nkt64) : kb;
       if (ke < kb) ke = kb;
     }
-    for (int t = kb + u.split; t < ke; t += u.nsplit)
+    for (int t = kb + u.split; t < ke; t += u.nsplit)  // (a tile's resource ends at key min(t QN + QN, Sk) - 1)
       if (t * QN >= p->Sk) return c.fail("dQ unit %d walks key tile %d past Sk", unit, t);
     for (int w = 0; w < QM / 32; ++w) {
       const int qw = q0 + 32 * w, rows = std::max(0, std::min(32, p->Sq - qw));

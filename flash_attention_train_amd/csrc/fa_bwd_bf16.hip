@@ -298,15 +298,15 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     h = hk * a.G + x.hi;
     q0 = (qt0 + x.qi) * KV_BM;
   };
-  // stage a pair's Q and dO tiles straight into LDS (rows past the end repeat the last
-  // row, masked out on the tail tile) and fetch its LSE / Delta into a register
+  // stage a pair's Q and dO tiles straight into LDS (rows past the end arrive as zeros,
+  // masked out on the tail tile) and fetch its LSE / Delta into a register
   auto stage_pair = [&](const Pos& x, int buf) {
     int h, q0;
     pair_of(x, h, q0);
     const bf16* Q = static_cast<const bf16*>(args.q) + b * args.sq.b + h * args.sq.h + (int64_t)q0 * args.sq.s;
     const bf16* dO = static_cast<const bf16*>(args.dout) + b * args.sdo.b + h * args.sdo.h + (int64_t)q0 * args.sdo.s;
-    TL::template stage<KV_BM, NT, false>(q_lds + buf * KV_BM * D, Q, args.sq.s, a.Sq - q0);
-    TL::template stage<KV_BM, NT, false>(do_lds + buf * KV_BM * D, dO, args.sdo.s, a.Sq - q0);
+    TL::template stage_rows<KV_BM, NT>(q_lds + buf * KV_BM * D, Q, args.sq.s, a.Sq - q0);
+    TL::template stage_rows<KV_BM, NT>(do_lds + buf * KV_BM * D, dO, args.sdo.s, a.Sq - q0);
     if (tid < 2 * KV_BM) {
       const int row = min(q0 + (tid % KV_BM), a.Sq - 1);
       // (turned into its three terms when stored, so that nothing waits for the load before
@@ -1098,12 +1098,12 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
     w_hi = (qlen < a.Sq && qw + 32 > qlen) ? w_lo : (int)min<int64_t>(h0, a.Sk);
   }
 
-  // stage K and V rows [key0, key0 + Q_BN) straight into LDS (keys past the end repeat
-  // the last key, masked out on the tail tile)
+  // stage K and V rows [key0, key0 + Q_BN) straight into LDS (keys past the end arrive as
+  // zeros, masked out on the tail tile)
   auto stage_tile = [&](int kt, int buf) {
     const int key0 = kt * Q_BN;
-    TL::template stage<Q_BN, NT, false>(k_lds + buf * Q_BN * D, K + (int64_t)key0 * args.sk.s, args.sk.s, a.Sk - key0);
-    TL::template stage<Q_BN, NT, false>(v_lds + buf * Q_BN * D, V + (int64_t)key0 * args.sv.s, args.sv.s, a.Sk - key0);
+    TL::template stage_rows<Q_BN, NT>(k_lds + buf * Q_BN * D, K + (int64_t)key0 * args.sk.s, args.sk.s, a.Sk - key0);
+    TL::template stage_rows<Q_BN, NT>(v_lds + buf * Q_BN * D, V + (int64_t)key0 * args.sv.s, args.sv.s, a.Sk - key0);
   };
   // a stored fp16 / q8_0 window: each tile's loads issued one tile ahead into registers,
   // converted to bf16 into LDS after the current tile's products

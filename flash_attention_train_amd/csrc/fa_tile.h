@@ -21,6 +21,22 @@
 namespace fa {
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// A raw buffer resource (stride 0, no swizzle) over the `bytes` bytes at `base`. The range
+// check of a load through it covers the scalar and the per-lane offset together: a lane
+// whose offset is `bytes` or more reads no memory and returns zeros (for a load into LDS,
+// zeros are written there). The fourth word is the gfx9 data-format default that raw loads
+// use.
+__device__ __forceinline__ u32x4 raw_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
 
 template <int D>
 struct Tile {
@@ -85,6 +101,30 @@ struct Tile {
     }
   }
 
+  // Stage rows [0, ROWS) of a tile whose row i starts at src + i * stride (elements); rows
+  // at or beyond `valid` arrive as zeros. The loads go through a buffer resource that ends
+  // after row valid - 1, whose range check turns every later row into zeros without a
+  // memory access, so the last tile needs no clamping. A thread loads the same chunk of
+  // every row it touches (RSTEP rows apart; the swizzle repeats every 16 rows): one per-lane
+  // byte offset serves all its loads and the row step is the scalar offset, so a load costs
+  // no vector work. The row stride is below 2^24 elements (checked on the host): the
+  // offsets within a tile fit in 32 bits.
+  template <int ROWS, int NT>
+  __device__ static __forceinline__ void stage_rows(bf16* lds, const bf16* src, int64_t stride, int valid) {
+    constexpr int W = NT / 64, PER = ROWS * NCH / NT, RSTEP = 64 * W / NCH;
+    static_assert((ROWS * NCH) % NT == 0, "tile must split evenly over the threads");
+    static_assert(RSTEP % 16 == 0, "a thread's rows must share their swizzle");
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t st = (uint32_t)stride;
+    const int row0 = (64 * (int)(threadIdx.x >> 6) + lane) / NCH;
+    const uint32_t voff = ((uint32_t)row0 * st + 8u * (uint32_t)((lane % NCH) ^ swz(row0))) * 2u;
+    const int v = valid < ROWS ? valid : ROWS;
+    const u32x4 rsrc = raw_rsrc(src, v > 0 ? ((uint32_t)(v - 1) * st + (uint32_t)D) * 2u : 0u);
+    #pragma unroll
+    for (int i = 0; i < PER; ++i)
+      dma16(rsrc, voff, (uint32_t)(RSTEP * i) * st * 2u, lds + 8 * 64 * (wave + W * i));
+  }
+
   // One wave-instruction of global_load_lds_dwordx4: lane l's 16 bytes from g land at
   // LDS byte address m0 + 16 l, m0 = dst (wave-uniform). Written as asm so that the
   // compiler does not treat the asynchronous LDS write as possibly aliasing every later
@@ -101,6 +141,16 @@ struct Tile {
     const uint32_t m0 =
         __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) bf16*)dst);
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+                 : "memory", "m0");
+  }
+  // the same through a buffer resource: lane l's 16 bytes at byte offset soff + voff (zeros
+  // where that is past the resource's end)
+  // (a flat address into LDS is the shared aperture's base, whose low 32 bits are zero, plus
+  // the LDS byte address: its low word is the LDS address, with no null check to emit)
+  __device__ static __forceinline__ void dma16(const u32x4& rsrc, uint32_t voff, uint32_t soff, bf16* dst) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds" ::"v"(voff), "s"(rsrc),
+                 "s"(m0), "s"(__builtin_amdgcn_readfirstlane(soff))
                  : "memory", "m0");
   }
 };
