@@ -140,8 +140,18 @@ __device__ __forceinline__ float from_f32<float>(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// swap with the lane 32 positions away (the other half of the wave)
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// x combined with the value of the lane 32 positions away (the other half of the wave),
+// the same result in both lanes: one v_permlane32_swap of x with itself leaves the lower
+// half's values in one register and the upper half's in the other, across the whole wave
+// (no LDS round trip)
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 

@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(const FwdArgs args) {
         mx = fmaxf(mx, x);
       }
     }
-    mx = fmaxf(mx, xor32(mx));
+    mx = halves_max(mx);
     const float m_new = fmaxf(m, mx);
     const float base = (m_new == neg_inf()) ? 0.f : m_new;
     const float alpha = fast_exp2(m - base);  // 0 while nothing was visible yet
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(const FwdArgs args) {
   }
 
   // epilogue: O = acc / l, LSE = ln(sum) + max; fully masked rows -> 0 and 0
-  const float lt = l + xor32(l);
+  const float lt = halves_sum(l);
   const bool full = (m == neg_inf());
   const float inv = full ? 0.f : 1.f / lt;
   const float lse = full ? 0.f : (m + log2f(lt)) * kLn2;

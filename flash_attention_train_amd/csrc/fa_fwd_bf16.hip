@@ -140,12 +140,12 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
   }
 
   // tile staging: K and V rows [key0, key0 + BN) straight into LDS; keys past the end
-  // repeat the last key (masked out, P = 0, on the tail tile)
+  // arrive as zeros (masked out, P = 0, on the tail tile)
   // (with KS = 2 each key half stages its own tile with its own two waves)
   auto stage_tile = [&](int kt, int buf) {
     const int key0 = kt * BN;
-    TL::template stage<BN, NTS, KS == 1>(k_lds[kh][buf], K + (int64_t)key0 * args.sk.s, args.sk.s, a.Sk - key0, rb);
-    TL::template stage<BN, NTS, KS == 1>(v_lds[kh][buf], V + (int64_t)key0 * args.sv.s, args.sv.s, a.Sk - key0, rb);
+    TL::template stage_rows<BN, NTS>(k_lds[kh][buf], K + (int64_t)key0 * args.sk.s, args.sk.s, a.Sk - key0, rb);
+    TL::template stage_rows<BN, NTS>(v_lds[kh][buf], V + (int64_t)key0 * args.sv.s, args.sv.s, a.Sk - key0, rb);
   };
   // stored fp16 / q8_0 tiles: loads one tile ahead, conversion into LDS after the products
   constexpr int KVE = KVF == kKvQ8 ? 1 : 2;  // bytes per stored element
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
       for (int kb = 0; kb < KB; ++kb)
         #pragma unroll
         for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(st[qb][kb][r], st[qb][kb][r + 1]));
-      mx = fmaxf(mx, xor32(mx));
+      mx = halves_max(mx);
       const float mscaled = mx * cs;
       const bool need = mscaled > base[qb] + 8.f;
       if (__any(need)) {
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
   if constexpr (SPLIT) {  // this share's normalised rows (bf16), their base and row sum, for the merge
     static_assert(QB == 1 && KS == 1, "the split walk runs the one-block, one-half configuration");
     const int row = qw + r32;
-    const float lt = lsum[0] + xor32(lsum[0]);
+    const float lt = halves_sum(lsum[0]);
     const float inv = base[0] == neg_inf() ? 0.f : 1.f / lt;  // (a share that saw no key: zeros)
     if (row < a.Sq) {
       const int64_t r = (((int64_t)blockIdx.z * a.B + b) * a.Hq + h) * a.Sq + row;
@@ -484,7 +484,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
   #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qw + 32 * qb + r32;
-    float lt = lsum[qb] + xor32(lsum[qb]);
+    float lt = halves_sum(lsum[qb]);
     float inv, lse;
     if (sb != neg_inf()) {
       const float nb = fmaxf(base[qb], sb);

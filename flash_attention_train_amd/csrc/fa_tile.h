@@ -109,20 +109,32 @@ struct Tile {
   // byte offset serves all its loads and the row step is the scalar offset, so a load costs
   // no vector work. The row stride is below 2^24 elements (checked on the host): the
   // offsets within a tile fit in 32 bits.
+  // NT threads (NT / 64 waves) stage the tile; group_wave is this wave's index among them
+  // (default: its index in the workgroup).
   template <int ROWS, int NT>
-  __device__ static __forceinline__ void stage_rows(bf16* lds, const bf16* src, int64_t stride, int valid) {
+  __device__ static __forceinline__ void stage_rows(bf16* lds, const bf16* src, int64_t stride, int valid,
+                                                    int group_wave = -1) {
     constexpr int W = NT / 64, PER = ROWS * NCH / NT, RSTEP = 64 * W / NCH;
     static_assert((ROWS * NCH) % NT == 0, "tile must split evenly over the threads");
-    static_assert(RSTEP % 16 == 0, "a thread's rows must share their swizzle");
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(group_wave < 0 ? (int)(threadIdx.x >> 6) : group_wave);
     const uint32_t st = (uint32_t)stride;
-    const int row0 = (64 * (int)(threadIdx.x >> 6) + lane) / NCH;
-    const uint32_t voff = ((uint32_t)row0 * st + 8u * (uint32_t)((lane % NCH) ^ swz(row0))) * 2u;
+    const int row0 = (64 * wave + lane) / NCH;
     const int v = valid < ROWS ? valid : ROWS;
     const u32x4 rsrc = raw_rsrc(src, v > 0 ? ((uint32_t)(v - 1) * st + (uint32_t)D) * 2u : 0u);
-    #pragma unroll
-    for (int i = 0; i < PER; ++i)
-      dma16(rsrc, voff, (uint32_t)(RSTEP * i) * st * 2u, lds + 8 * 64 * (wave + W * i));
+    if constexpr (RSTEP % 16 == 0) {
+      const uint32_t voff = ((uint32_t)row0 * st + 8u * (uint32_t)((lane % NCH) ^ swz(row0))) * 2u;
+      #pragma unroll
+      for (int i = 0; i < PER; ++i)
+        dma16(rsrc, voff, (uint32_t)(RSTEP * i) * st * 2u, lds + 8 * 64 * (wave + W * i));
+    } else {  // (fewer staging waves: a thread's rows differ in their swizzle, one offset each)
+      #pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int row = row0 + RSTEP * i;
+        const uint32_t voff = ((uint32_t)row * st + 8u * (uint32_t)((lane % NCH) ^ swz(row))) * 2u;
+        dma16(rsrc, voff, 0u, lds + 8 * 64 * (wave + W * i));
+      }
+    }
   }
 
   // One wave-instruction of global_load_lds_dwordx4: lane l's 16 bytes from g land at
