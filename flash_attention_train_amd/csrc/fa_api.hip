@@ -100,23 +100,13 @@ fa_status check_params(const fa_attn_params* p) {
       p->fwd_split > 64)
     return fail(FA_ERR_SHAPE, "split hints must be in 0 .. 64");
   if (p->window_left < -1 || p->window_right < -1) return fail(FA_ERR_SHAPE, "window bounds must be >= -1");
-  if (p->sinks && p->dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "attention sinks are implemented for bf16 only");
   if (reinterpret_cast<uintptr_t>(p->sinks) % 4) return fail(FA_ERR_ALIGN, "sinks is not 4-byte aligned");
-  if (p->alibi && p->dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "ALiBi is implemented for bf16 only");
   if (reinterpret_cast<uintptr_t>(p->alibi) % 4) return fail(FA_ERR_ALIGN, "alibi is not 4-byte aligned");
   if (p->bwd_dq_launch < 0 || p->bwd_dq_launch > 2)
     return fail(FA_ERR_SHAPE, "bwd_dq_launch must be 0, 1 or 2 (got %d)", p->bwd_dq_launch);
   if (reinterpret_cast<uintptr_t>(p->key_len) % 4 || reinterpret_cast<uintptr_t>(p->q_len) % 4)
     return fail(FA_ERR_ALIGN, "key_len / q_len are not 4-byte aligned");
-  const bool structured = p->key_len || p->q_len || p->window_left >= 0 || p->window_right >= 0;
-  if (structured && p->dtype != FA_BF16)
-    return fail(FA_ERR_UNSUPPORTED, "structured masks (key_len, q_len, window) are implemented for bf16 only");
   if (!(p->softcap >= 0.f) || isinf(p->softcap)) return fail(FA_ERR_SHAPE, "softcap must be >= 0 and finite");
-  // (sinks and structured masks are bf16-only, checked above; the capped MFMA backward runs
-  // without a dense mask)
-  if (p->softcap > 0.f && (p->alibi || ((p->sinks || structured) && p->mask)))
-    return fail(FA_ERR_UNSUPPORTED, "the logit softcap does not combine with ALiBi, nor with sinks or "
-                                    "structured masks over a dense mask");
   if (p->mask) {
     if (p->mask_stride_q < p->Sk) return fail(FA_ERR_STRIDE, "mask_stride_q (%lld) < Sk", (long long)p->mask_stride_q);
     if (p->mask_stride_b < 0) return fail(FA_ERR_STRIDE, "mask_stride_b is negative");
@@ -210,7 +200,11 @@ fa_status check_kv(const fa_attn_params* p, const fa_view* k, const fa_view* v, 
 // The generic backward (fa_bwd.hip) runs fp32 problems and logit softcaps over a dense
 // mask; the bf16 MFMA backward runs the rest (a softcap without a dense mask in a variant of
 // its own). The bf16 forward takes every softcap itself.
-bool generic_path(const fa_attn_params* p) { return p->dtype != FA_BF16 || (p->softcap > 0.f && p->mask); }
+// the backward's generic kernels: every fp32 problem, and a bf16 logit softcap under additive
+// scores (a dense mask or ALiBi), which the bf16 walks' capped variants do not add after the cap
+bool generic_path(const fa_attn_params* p) {
+  return p->dtype != FA_BF16 || (p->softcap > 0.f && (p->mask || p->alibi));
+}
 
 fa::Strides strides_of(const fa_view* v) { return {v->stride_b, v->stride_h, v->stride_s}; }
 
@@ -1113,7 +1107,7 @@ fa_status fa_train_check_launch(const fa_attn_params* p, const int32_t* key_len_
   check_tile_offsets<64>(c, 64, "tile D=64");
   check_tile_offsets<128>(c, 64, "tile D=128");
   check_fwd(c, p, key_len_host, q_len_host);
-  check_bwd(c, p, key_len_host, q_len_host);
+  if (!generic_path(p)) check_bwd(c, p, key_len_host, q_len_host);  // (the generic kernels have no plan)
   return c.ok ? FA_OK : fail(FA_ERR_HIP, "FA_CHECK: %s", report);
 }
 #endif

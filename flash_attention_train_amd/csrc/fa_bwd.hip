@@ -26,7 +26,10 @@
 //
 // Masked entries get P = 0 exactly (so dS = 0): a fully masked query row (LSE 0)
 // contributes nothing, and a key column no query can see ends with dK = dV = 0
-// exactly (skill page, section 6, trap 8).
+// exactly (skill page, section 6, trap 8). The rows that see a key by the structure
+// (sequence end, key and query lengths, causal diagonal, window) come from the range helper
+// the bf16 kernels share; ALiBi adds -slope |key - position| after the cap, like the mask;
+// an attention sink only enters through the LSE (its own gradient is a separate pass).
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -47,7 +50,7 @@ __device__ __forceinline__ void atomic_add_f32(float* p, float v) {
   __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <typename T, int D, int NW, bool CAUSAL, bool MASK>
+template <typename T, int D, int NW, bool MASK>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(const BwdArgs args) {
   constexpr int NT = NW * 64;
   constexpr int BN = 32 * NW;                     // keys per workgroup
@@ -110,12 +113,19 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(const BwdArgs args) {
     dv[db] = zeros16();
   }
 
+  // the rows this lane's key sees by the structure, and the query tiles any key of the
+  // workgroup's tile sees (both ends of a key's row range move down with the key)
+  const int klen = klen_of(a, b), qlen = qlen_of(a, b);
+  int64_t rlo, rhi;
+  row_range(a, klen, qlen, key, rlo, rhi);
   const int nqt = (a.Sq + BM - 1) / BM;
-  int qt_begin = 0;
-  if (CAUSAL) {
-    // rows i with q_offset + i >= n0 can see a key of this tile
-    const int64_t first_row = (int64_t)n0 - a.q_offset;
-    qt_begin = first_row <= 0 ? 0 : (int)((first_row / BM) < nqt ? first_row / BM : nqt);
+  int qt_begin = 0, qt_end = 0;
+  if (n0 < klen) {
+    int64_t lo0, hi0, lo1, hi1;
+    row_range(a, klen, qlen, n0, lo0, hi0);
+    row_range(a, klen, qlen, min(n0 + BN, klen) - 1, lo1, hi1);
+    qt_begin = (int)min<int64_t>(lo0 / BM, nqt);
+    qt_end = hi1 > lo0 ? (int)min<int64_t>((hi1 + BM - 1) / BM, nqt) : qt_begin;
   }
 
   for (int h = hk * a.G; h < (hk + 1) * a.G; ++h) {
@@ -125,7 +135,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(const BwdArgs args) {
     const float* DLT = args.delta + b * args.delta_sb + h * args.delta_sh;
     float* dQacc = args.dq_acc + ((int64_t)b * a.Hq + h) * a.Sq * D;
 
-    for (int qt = qt_begin; qt < nqt; ++qt) {
+    // ALiBi in log2 units: -slope log2(e) |key - position|
+    const float al2 = a.alibi ? a.alibi[h] * kLog2e : 0.f;
+    for (int qt = qt_begin; qt < qt_end; ++qt) {
       const int q0 = qt * BM;
       __syncthreads();  // the previous tile's LDS readers are done
       for (int c = tid; c < BM * D / 8; c += NT) {
@@ -165,8 +177,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(const BwdArgs args) {
         for (int r = 0; r < 16; ++r) {
           const int ql = 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
           const int qi = q0 + ql;
-          bool vis = key < a.Sk && qi < a.Sq;
-          if (CAUSAL) vis = vis && ((int64_t)key <= a.q_offset + qi);
+          const bool vis = qi >= rlo && qi < rhi;
           float x = sacc[r] * cs, dcap = 1.f;
           if (capped) {
             const float t = tanhf(sacc[r] * cap_in);
@@ -174,6 +185,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(const BwdArgs args) {
             dcap = 1.f - t * t;
           }
           if (MASK && vis) x += a.mask[b * a.mask_sb + h * a.mask_sh + (int64_t)qi * a.mask_sq + key] * kLog2e;
+          if (a.alibi) x -= al2 * fabsf((float)((int64_t)key - a.q_offset - qi));
           const float p = vis ? fast_exp2(x - lse_lds[ql]) : 0.f;
           sacc[r] = p;
           dpacc[r] = p * (dpacc[r] - dlt_lds[ql]) * dcap;
@@ -250,15 +262,10 @@ template <typename T, int D, int NW>
 hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t stream) {
   const dim3 grid((args.a.Sk + 32 * NW - 1) / (32 * NW), args.a.Hkv, args.a.B);
   const dim3 block(NW * 64);
-  const bool causal = args.a.causal != 0, mask = args.a.mask != nullptr;
-  if (causal && mask)
-    hipLaunchKernelGGL((bwd_kernel<T, D, NW, true, true>), grid, block, 0, stream, args);
-  else if (causal)
-    hipLaunchKernelGGL((bwd_kernel<T, D, NW, true, false>), grid, block, 0, stream, args);
-  else if (mask)
-    hipLaunchKernelGGL((bwd_kernel<T, D, NW, false, true>), grid, block, 0, stream, args);
+  if (args.a.mask != nullptr)
+    hipLaunchKernelGGL((bwd_kernel<T, D, NW, true>), grid, block, 0, stream, args);
   else
-    hipLaunchKernelGGL((bwd_kernel<T, D, NW, false, false>), grid, block, 0, stream, args);
+    hipLaunchKernelGGL((bwd_kernel<T, D, NW, false>), grid, block, 0, stream, args);
   return hipGetLastError();
 }
 

@@ -18,10 +18,14 @@
 //
 // Numerics: scores are scaled by scale * log2(e) and exponentiated with the
 // hardware exp2 (with a logit softcap c, the scaled product x first becomes
-// c tanh(x / c), before the mask is added); the LSE is converted back to natural log on output. A row that
+// c tanh(x / c), before the mask and ALiBi are added); the LSE is converted back to natural
+// log on output. The keys a row sees by the structure (sequence end, key and query lengths,
+// causal diagonal, window) come from the same range helper the bf16 kernels use. A row that
 // has seen no visible key keeps m = -inf; its exponent base is taken as 0 so that
 // exp2(-inf) = 0 flows through without NaN, and the epilogue writes O = 0 and
-// LSE = 0 for it (skill page, section 6, trap 9).
+// LSE = 0 for it (skill page, section 6, trap 9). An attention sink (one more logit per head
+// with no value row, llama.cpp pull request 57's list of score modifiers) joins the row sum
+// in the epilogue; a row that saw no key then has O = 0 and LSE = the sink.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -38,7 +42,7 @@ __device__ __forceinline__ f32x16 zeros16() {
 __device__ __forceinline__ bf16 elem_t(const bf16x8& f, int j) { return f[j]; }
 __device__ __forceinline__ float elem_t(const f32x8& f, int j) { return j < 4 ? f.lo[j] : f.hi[j - 4]; }
 
-template <typename T, int D, bool CAUSAL, bool MASK>
+template <typename T, int D, bool MASK>
 __global__ __launch_bounds__(256, 1) void fwd_kernel(const FwdArgs args) {
   constexpr int BM = 128;              // query rows per workgroup (32 per wave)
   constexpr int BN = 64;               // keys per tile
@@ -68,6 +72,13 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(const FwdArgs args) {
   const T* V = static_cast<const T*>(args.v) + b * args.sv.b + hk * args.sv.h;
   const float* Mrow = nullptr;
   if (MASK && qrow < a.Sq) Mrow = a.mask + b * a.mask_sb + h * a.mask_sh + (int64_t)qrow * a.mask_sq;
+  // ALiBi in log2 units: -slope log2(e) |key - position|
+  const float al2 = a.alibi ? a.alibi[h] * kLog2e : 0.f;
+  const int64_t pos = a.q_offset + qrow;
+  // the keys this lane's row sees by the structure, and the tiles the workgroup's rows see
+  const int klen = klen_of(a, b), qlen = qlen_of(a, b);
+  int64_t lo, hi;
+  key_range(a, klen, qlen, qrow, lo, hi);
 
   // Q as the B operand of S^T = K Q^T: lane (row r32, half g) holds d = 16 s + 8 g + j
   Frag<T> qf[DS];
@@ -84,13 +95,16 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(const FwdArgs args) {
   float l = 0.f;        // this lane's share of the running row sum
 
   const int nkt = (a.Sk + BN - 1) / BN;
-  int kt_end = nkt;
-  if (CAUSAL) {
-    const int64_t last_key = a.q_offset + q0 + BM - 1;  // highest key the tile can see
-    kt_end = last_key < 0 ? 0 : (int)((last_key / BN + 1) < nkt ? (last_key / BN + 1) : nkt);
+  int kt_begin = 0, kt_end = 0;
+  if (q0 < qlen) {  // from the first row's lower end to the last visible row's upper end
+    int64_t lo0, hi0, lo1, hi1;
+    key_range(a, klen, qlen, q0, lo0, hi0);
+    key_range(a, klen, qlen, min(q0 + BM, qlen) - 1, lo1, hi1);
+    kt_begin = (int)min<int64_t>(lo0 / BN, nkt);
+    kt_end = hi1 > lo0 ? (int)min<int64_t>((hi1 + BN - 1) / BN, nkt) : kt_begin;
   }
 
-  for (int kt = 0; kt < kt_end; ++kt) {
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
     __syncthreads();  // every wave is done with the previous tile
     for (int c = tid; c < BN * D / 8; c += 256) {
       const int key = c / (D / 8), d0 = (c % (D / 8)) * 8;
@@ -124,9 +138,9 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(const FwdArgs args) {
       for (int r = 0; r < 16; ++r) {
         const int key = kt * BN + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
         float x = capped ? tanhf(st[kb][r] * cap_in) * cap_out : st[kb][r] * cs;
-        bool vis = key < a.Sk;
-        if (CAUSAL) vis = vis && ((int64_t)key <= a.q_offset + qrow);
+        const bool vis = key >= lo && key < hi;
         if (MASK && vis && Mrow) x += Mrow[key] * kLog2e;
+        if (a.alibi) x -= al2 * fabsf((float)(key - pos));
         x = vis ? x : neg_inf();
         st[kb][r] = x;
         mx = fmaxf(mx, x);
@@ -167,11 +181,21 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(const FwdArgs args) {
     }
   }
 
-  // epilogue: O = acc / l, LSE = ln(sum) + max; fully masked rows -> 0 and 0
-  const float lt = halves_sum(l);
-  const bool full = (m == neg_inf());
-  const float inv = full ? 0.f : 1.f / lt;
-  const float lse = full ? 0.f : (m + log2f(lt)) * kLn2;
+  // epilogue: O = acc / l, LSE = ln(sum) + max; fully masked rows -> 0 and 0 (the sink, when
+  // there is one, joins the sum at the larger of its logit and the row max)
+  float lt = halves_sum(l), inv, lse;
+  const float sb = args.sinks ? args.sinks[h] * kLog2e : neg_inf();
+  if (sb != neg_inf()) {
+    const float nb = fmaxf(m, sb);
+    const float fo = m == neg_inf() ? 0.f : fast_exp2(m - nb);
+    lt = lt * fo + fast_exp2(sb - nb);
+    inv = fo / lt;
+    lse = m == neg_inf() ? args.sinks[h] : (nb + log2f(lt)) * kLn2;
+  } else {
+    const bool full = (m == neg_inf());
+    inv = full ? 0.f : 1.f / lt;
+    lse = full ? 0.f : (m + log2f(lt)) * kLn2;
+  }
   if (qrow < a.Sq) {
     T* O = static_cast<T*>(args.o) + b * args.so.b + h * args.so.h + (int64_t)qrow * args.so.s;
     for (int db = 0; db < DB; ++db)
@@ -184,15 +208,10 @@ template <typename T, int D>
 hipError_t launch_fwd_t(const FwdArgs& args, hipStream_t stream) {
   const dim3 grid((args.a.Sq + 127) / 128, args.a.Hq, args.a.B);
   const dim3 block(256);
-  const bool causal = args.a.causal != 0, mask = args.a.mask != nullptr;
-  if (causal && mask)
-    hipLaunchKernelGGL((fwd_kernel<T, D, true, true>), grid, block, 0, stream, args);
-  else if (causal)
-    hipLaunchKernelGGL((fwd_kernel<T, D, true, false>), grid, block, 0, stream, args);
-  else if (mask)
-    hipLaunchKernelGGL((fwd_kernel<T, D, false, true>), grid, block, 0, stream, args);
+  if (args.a.mask != nullptr)
+    hipLaunchKernelGGL((fwd_kernel<T, D, true>), grid, block, 0, stream, args);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, D, false, false>), grid, block, 0, stream, args);
+    hipLaunchKernelGGL((fwd_kernel<T, D, false>), grid, block, 0, stream, args);
   return hipGetLastError();
 }
 

@@ -66,6 +66,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) from here on
   const int rb = wave % RB, kh = wave / RB;                    // row block, key half
+  const uint32_t k_lds32 = TL::lds_addr(k_lds[kh][0]), v_lds32 = TL::lds_addr(v_lds[kh][0]);  // (staging destinations)
   const int g = lane >> 5, r32 = lane & 31;
   // Workgroups are dispatched in linear order with x fastest: x walks (batch, head) and y
   // the query tiles from the last, so every head's longest causal walks go out first.
@@ -144,8 +145,10 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
   // (with KS = 2 each key half stages its own tile with its own two waves)
   auto stage_tile = [&](int kt, int buf) {
     const int key0 = kt * BN;
-    TL::template stage_rows<BN, NTS>(k_lds[kh][buf], K + (int64_t)key0 * args.sk.s, args.sk.s, a.Sk - key0, rb);
-    TL::template stage_rows<BN, NTS>(v_lds[kh][buf], V + (int64_t)key0 * args.sv.s, args.sv.s, a.Sk - key0, rb);
+    TL::template stage_rows<BN, NTS>(k_lds32 + (uint32_t)buf * (BN * D * 2), K + (int64_t)key0 * args.sk.s, args.sk.s,
+                                     a.Sk - key0, rb);
+    TL::template stage_rows<BN, NTS>(v_lds32 + (uint32_t)buf * (BN * D * 2), V + (int64_t)key0 * args.sv.s, args.sv.s,
+                                     a.Sk - key0, rb);
   };
   // stored fp16 / q8_0 tiles: loads one tile ahead, conversion into LDS after the products
   constexpr int KVE = KVF == kKvQ8 ? 1 : 2;  // bytes per stored element

@@ -110,9 +110,9 @@ struct Tile {
   // no vector work. The row stride is below 2^24 elements (checked on the host): the
   // offsets within a tile fit in 32 bits.
   // NT threads (NT / 64 waves) stage the tile; group_wave is this wave's index among them
-  // (default: its index in the workgroup).
+  // (default: its index in the workgroup). `lds` is the tile's LDS byte address.
   template <int ROWS, int NT>
-  __device__ static __forceinline__ void stage_rows(bf16* lds, const bf16* src, int64_t stride, int valid,
+  __device__ static __forceinline__ void stage_rows(uint32_t lds, const bf16* src, int64_t stride, int valid,
                                                     int group_wave = -1) {
     constexpr int W = NT / 64, PER = ROWS * NCH / NT, RSTEP = 64 * W / NCH;
     static_assert((ROWS * NCH) % NT == 0, "tile must split evenly over the threads");
@@ -126,16 +126,26 @@ struct Tile {
       const uint32_t voff = ((uint32_t)row0 * st + 8u * (uint32_t)((lane % NCH) ^ swz(row0))) * 2u;
       #pragma unroll
       for (int i = 0; i < PER; ++i)
-        dma16(rsrc, voff, (uint32_t)(RSTEP * i) * st * 2u, lds + 8 * 64 * (wave + W * i));
+        dma16(rsrc, voff, (uint32_t)(RSTEP * i) * st * 2u, lds + 1024u * (uint32_t)(wave + W * i));
     } else {  // (fewer staging waves: a thread's rows differ in their swizzle, one offset each)
       #pragma unroll
       for (int i = 0; i < PER; ++i) {
         const int row = row0 + RSTEP * i;
         const uint32_t voff = ((uint32_t)row * st + 8u * (uint32_t)((lane % NCH) ^ swz(row))) * 2u;
-        dma16(rsrc, voff, 0u, lds + 8 * 64 * (wave + W * i));
+        dma16(rsrc, voff, 0u, lds + 1024u * (uint32_t)(wave + W * i));
       }
     }
   }
+  template <int ROWS, int NT>
+  __device__ static __forceinline__ void stage_rows(bf16* lds, const bf16* src, int64_t stride, int valid,
+                                                    int group_wave = -1) {
+    stage_rows<ROWS, NT>(lds_addr(lds), src, stride, valid, group_wave);
+  }
+
+  // the LDS byte address of a pointer into LDS: a flat address into LDS is the shared
+  // aperture's base, whose low 32 bits are zero, plus the LDS address, so its low word is
+  // the LDS address (with no null check to emit)
+  __device__ static __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
   // One wave-instruction of global_load_lds_dwordx4: lane l's 16 bytes from g land at
   // LDS byte address m0 + 16 l, m0 = dst (wave-uniform). Written as asm so that the
@@ -157,10 +167,9 @@ struct Tile {
   }
   // the same through a buffer resource: lane l's 16 bytes at byte offset soff + voff (zeros
   // where that is past the resource's end)
-  // (a flat address into LDS is the shared aperture's base, whose low 32 bits are zero, plus
-  // the LDS byte address: its low word is the LDS address, with no null check to emit)
-  __device__ static __forceinline__ void dma16(const u32x4& rsrc, uint32_t voff, uint32_t soff, bf16* dst) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  // (dst: the LDS byte address, wave-uniform)
+  __device__ static __forceinline__ void dma16(const u32x4& rsrc, uint32_t voff, uint32_t soff, uint32_t dst) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(dst);
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds" ::"v"(voff), "s"(rsrc),
                  "s"(m0), "s"(__builtin_amdgcn_readfirstlane(soff))
                  : "memory", "m0");

@@ -94,13 +94,9 @@ FWD_ERRORS = [
     ("negative q_split_tiles", params(q_split_tiles=-1), {}, 2),
     ("per-head mask with a block map", params(mask=BASE + 9 * (1 << 24), mask_stride_q=64, mask_stride_h=64 * 64,
                                               mask_tiles=BASE + 10 * (1 << 24)), {}, 7),
-    ("sinks on fp32", params(dtype=B.FA_F32, sinks=BASE), {}, 7),
     ("misaligned sinks", params(sinks=BASE + 2), {}, 5),
-    ("ALiBi on fp32", params(dtype=B.FA_F32, alibi=BASE), {}, 7),
     ("misaligned alibi", params(alibi=BASE + 2), {}, 5),
     ("misaligned key_len", params(key_len=BASE + 2), {}, 5),
-    ("structured mask on fp32", params(dtype=B.FA_F32, key_len=BASE), {}, 7),
-    ("window on fp32", params(dtype=B.FA_F32, window_right=3), {}, 7),
     ("mask stride too small", params(mask=BASE + 9 * (1 << 24), mask_stride_q=32), {}, 4),
     ("row stride 2^24", params(), {"k": view(1, H=2, stride_s=1 << 24, stride_h=(1 << 24) * 64,
                                                 stride_b=(1 << 24) * 128)}, 4),
@@ -230,21 +226,21 @@ def test_window_conversions_reject():
 def test_softcap_params_rejected():
     L = B.lib()
     lse, dlt = lse_view(5), lse_view(6)
-    m = dict(mask=BASE + 11 * (1 << 24), mask_stride_q=64)
-    bad = [(dict(softcap=-1.0), 2), (dict(softcap=float("inf")), 2), (dict(softcap=float("nan")), 2),
-           (dict(softcap=30.0, alibi=BASE + 7 * (1 << 24)), 7), (dict(softcap=30.0, sinks=BASE + 7 * (1 << 24), **m), 7),
-           (dict(softcap=30.0, window_left=8, **m), 7), (dict(softcap=30.0, key_len=BASE + 7 * (1 << 24), **m), 7)]
+    bad = [(dict(softcap=-1.0), 2), (dict(softcap=float("inf")), 2), (dict(softcap=float("nan")), 2)]
     for kw, code in bad:
         p = params(**kw)
         assert L.fa_train_fwd(ctypes.byref(p), view(0), view(1, H=2), view(2, H=2), view(3), lse, None) == code, kw
         assert L.fa_train_bwd(ctypes.byref(p), view(0), view(1, H=2), view(2, H=2), view(3), lse, dlt, view(8),
                               view(9, H=2), view(10, H=2), None, 0, None) == code, kw
-    # a softcap backward over a dense mask runs on the generic kernels, whose workspace is the
-    # fp32 dQ accumulator for both dtypes; without a mask the bf16 one keeps the MFMA kernels'
-    # plan (no workspace for this unsplit shape); the bf16 forward keeps its split walks
+    # a softcap backward under additive scores (a dense mask or ALiBi) runs on the generic
+    # kernels, whose workspace is the fp32 dQ accumulator for both dtypes; without them the
+    # bf16 one keeps the MFMA kernels' plan (no workspace for this unsplit shape); the bf16
+    # forward keeps its split walks
     masked = dict(softcap=30.0, mask=BASE + 11 * (1 << 24), mask_stride_q=64)
+    slopes = dict(softcap=30.0, alibi=BASE + 11 * (1 << 24))
     for dt in (B.FA_BF16, B.FA_F32):
-        assert L.fa_train_bwd_workspace_bytes(ctypes.byref(params(dtype=dt, **masked))) == 1 * 4 * 64 * 64 * 4
+        for kw in (masked, slopes):
+            assert L.fa_train_bwd_workspace_bytes(ctypes.byref(params(dtype=dt, **kw))) == 1 * 4 * 64 * 64 * 4
     assert L.fa_train_bwd_workspace_bytes(ctypes.byref(params(softcap=30.0))) == \
         L.fa_train_bwd_workspace_bytes(ctypes.byref(params())) == 0
     long_keys = dict(softcap=30.0, Sk=4096)
