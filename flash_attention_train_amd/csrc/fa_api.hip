@@ -200,11 +200,8 @@ fa_status check_kv(const fa_attn_params* p, const fa_view* k, const fa_view* v, 
 // The generic backward (fa_bwd.hip) runs fp32 problems and logit softcaps over a dense
 // mask; the bf16 MFMA backward runs the rest (a softcap without a dense mask in a variant of
 // its own). The bf16 forward takes every softcap itself.
-// the backward's generic kernels: every fp32 problem, and a bf16 logit softcap under additive
-// scores (a dense mask or ALiBi), which the bf16 walks' capped variants do not add after the cap
-bool generic_path(const fa_attn_params* p) {
-  return p->dtype != FA_BF16 || (p->softcap > 0.f && (p->mask || p->alibi));
-}
+// the backward's generic kernels: the fp32 problems (bf16 runs on the matrix-core walks)
+bool generic_path(const fa_attn_params* p) { return p->dtype != FA_BF16; }
 
 fa::Strides strides_of(const fa_view* v) { return {v->stride_b, v->stride_h, v->stride_s}; }
 

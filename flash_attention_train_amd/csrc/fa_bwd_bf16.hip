@@ -169,11 +169,13 @@ struct LiveWords {
   }
 };
 
-// CAP: a logit softcap (no dense mask). The scores then leave the product raw: the cap's
-// tanh sits between the product and the LSE, so the S half of the augmented k-chunk is not
-// applied, and each slice reads -LSE / scale of its rows from the augmented rows in LDS.
-// tanh(x) = 1 - 2 / (e^(2x) + 1) from the hardware exp2 and reciprocal, as in the forward;
-// dS carries the cap's derivative 1 - tanh^2.
+// CAP: a logit softcap. The scores then leave the product raw: the cap's tanh sits between
+// the product and the LSE, so the S half of the augmented k-chunk is not applied, and each
+// slice reads -LSE / scale of its rows from the augmented rows in LDS. tanh(x) = 1 - 2 /
+// (e^(2x) + 1) from the hardware exp2 and reciprocal, as in the forward; dS carries the
+// cap's derivative 1 - tanh^2. Under additive scores (a dense mask's values or ALiBi, BIAS)
+// the cap is applied to a whole block before they are added, with its derivative folded into
+// dP - Delta; otherwise inside the woven slices.
 template <int D, bool CAUSAL, bool MASK, bool BIAS, bool CAP = false, int KVF = 0>
 __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
   constexpr int DS = D / 16, DB = D / 32;
@@ -488,7 +490,19 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
       uint32_t w;
       const bf16* x;  // (CAP) the augmented row of register 0's query row
     };
-    auto stats_b = [&](int qb, f32x16& sacc, RowStats& st) {
+    auto stats_b = [&](int qb, f32x16& sacc, f32x16& dpacc, RowStats& st) {
+      if constexpr (CAP && BIAS) {
+        // a softcap under additive scores: the cap goes first (the mask and ALiBi add to the
+        // capped score), its derivative 1 - tanh^2 joins dP - Delta here, and the slices then
+        // only add -LSE / scale
+        #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(fast_exp2(sacc[r] * cap_k) + 1.f);
+          sacc[r] = cap_raw * t;
+          dpacc[r] *= 1.f - t * t;
+          if (r % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // (a few registers in flight at a time)
+        }
+      }
       if (BIAS && bias && a.alibi) {
         // ALiBi in raw score units: -(slope / scale) |key - position|; this lane's key, the
         // register's row: key - position = (key - q_offset - q0 - 32 qb - 4 g) - 8 (r/4) - r%4
@@ -509,6 +523,18 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
       st.x = qx_lds + (32 * qb + 4 * g) * 16;
     };
     auto slice_b = [&](int i, const RowStats& st, f32x16& sacc, f32x16& dpacc) {
+      if constexpr (CAP && BIAS) {  // (capped, with the additive values and the derivative, in stats_b)
+        #pragma unroll
+        for (int r = 2 * i; r < 2 * i + 2; ++r) {
+          const bf16x4 c3 = *reinterpret_cast<const bf16x4*>(st.x + (8 * (r >> 2) + (r & 3)) * 16);
+          const float nl = (float)c3[0] + (float)c3[1] + (float)c3[2];
+          const float sv = ninf_unless_bit(sacc[r] + nl, st.w, 8 * (r >> 2) + (r & 3));
+          const float pv = fast_exp2(sv * cs);
+          sacc[r] = pv;
+          dpacc[r] = pv * dpacc[r];
+        }
+        return;
+      }
       if constexpr (CAP) {
         #pragma unroll
         for (int r = 2 * i; r < 2 * i + 2; ++r) {
@@ -557,7 +583,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
       }
       const bf16x8 qx = read_x(qx_lds, 1), dx = read_x(dx_lds, 1);
       RowStats st;
-      stats_b(0, s0, st);
+      stats_b(0, s0, dp0, st);
       s1 = zeros16();
       dp1 = zeros16();
       __builtin_amdgcn_sched_barrier(0);
@@ -587,7 +613,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
       read_c(0, 0, dob[0], qbt[0]);
       read_c(0, 1, dob[1], qbt[1]);
       RowStats st;
-      stats_b(1, s1, st);
+      stats_b(1, s1, dp1, st);
       __builtin_amdgcn_sched_barrier(0);
       // 2 DB product pairs spread over the 8 slices
       #pragma unroll
@@ -1261,6 +1287,16 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
       }
       __builtin_amdgcn_sched_barrier(0);
       // lane (query row, half g), register r -> key 32 kb + 8 (r/4) + 4 g + r%4
+      if constexpr (CAP) {
+        // the capped score (the mask and ALiBi add to it below) and dP - Delta times the cap's
+        // derivative 1 - tanh^2
+        #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(fast_exp2(st[r] * cap_k) + 1.f);
+          st[r] = cap_raw * t;
+          dpt[r] = (dpt[r] - dlt) * (1.f - t * t);
+        }
+      }
       if (BIAS && bias && a.alibi) {  // ALiBi, as in the forward (lane = row, register = key)
         const float sl = a.alibi[h] * args.inv_scale;
         const float base = (float)((int64_t)key0 + 32 * kb + 4 * g - a.q_offset - row);
@@ -1284,16 +1320,6 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
           for (int e = 0; e < 4; ++e) st[4 * rr + e] += mv[e] * args.inv_scale;
         }
       }
-      if constexpr (CAP) {  // (no dense mask) the capped score, P and dS element by element
-        const uint32_t w = (uint32_t)(vis >> (32 * kb + 4 * g));
-        #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(fast_exp2(st[r] * cap_k) + 1.f);
-          float x = cap_raw * t;
-          if (masked) x = ninf_unless_bit(x, w, 8 * (r >> 2) + (r & 3));
-          st[r] = fast_exp2(fmaf(x, cs, -lse2)) * (dpt[r] - dlt) * (1.f - t * t);
-        }
-      } else {
       if (masked) {  // hidden scores -> -inf (P = 0); bit 8 rr + e of w <-> register 4 rr + e
         const uint32_t w = (uint32_t)(vis >> (32 * kb + 4 * g));
         #pragma unroll
@@ -1302,8 +1328,7 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
       #pragma unroll
       for (int r = 0; r < 16; ++r) st[r] = fast_exp2(fmaf(st[r], cs, -lse2));
       #pragma unroll
-      for (int r = 0; r < 16; ++r) st[r] = st[r] * (dpt[r] - dlt);
-      }
+      for (int r = 0; r < 16; ++r) st[r] = st[r] * (CAP ? dpt[r] : dpt[r] - dlt);
       #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         if constexpr (LOWREG) read_kbt(hh);  // (two workgroups per unit: read when needed)
@@ -1439,8 +1464,10 @@ hipError_t launch_t(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream
   if (args.a.kvf == kKvF16)
     return causal ? launch_cm<D, true, false, false, kKvF16>(args, plan, stream)
                   : launch_cm<D, false, false, false, kKvF16>(args, plan, stream);
-  if (args.a.softcap > 0.f && !mask)  // (a softcap with a dense mask runs on the generic kernels)
+  if (args.a.softcap > 0.f) {  // the capped walks (with a dense mask or ALiBi, added after the cap)
+    if (mask) return causal ? launch_cm<D, true, true, true>(args, plan, stream) : launch_cm<D, false, true, true>(args, plan, stream);
     return causal ? launch_cm<D, true, false, true>(args, plan, stream) : launch_cm<D, false, false, true>(args, plan, stream);
+  }
   if (causal && mask) return launch_cm<D, true, true>(args, plan, stream);
   if (causal) return launch_cm<D, true, false>(args, plan, stream);
   if (mask) return launch_cm<D, false, true>(args, plan, stream);
