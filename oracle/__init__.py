@@ -56,7 +56,8 @@ def _load():
         _lib.ora_backward.argtypes = [pp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
         _lib.ora_rows.argtypes = [pp, dp, dp, dp, dp, dp, ctypes.c_int64, ip, dp, dp, dp, dp, ctypes.c_int]
         _lib.ora_cols.argtypes = [pp, dp, dp, dp, dp, dp, ctypes.c_int64, ip, dp, dp, ctypes.c_int]
-        for f in (_lib.ora_forward, _lib.ora_backward, _lib.ora_rows, _lib.ora_cols):
+        _lib.ora_score_grad.argtypes = [pp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+        for f in (_lib.ora_forward, _lib.ora_backward, _lib.ora_rows, _lib.ora_cols, _lib.ora_score_grad):
             f.restype = ctypes.c_int
     return _lib
 
@@ -131,6 +132,31 @@ def backward(q, k, v, do, mask=None, *, scale: float, causal: bool = False, q_of
     if sinks is not None:
         out["dSink"] = sink_grad(sinks, out["LSE"], out["Delta"])
     return out
+
+
+def bias_grad(q, k, v, do, mask, *, scale: float, causal: bool = False, q_offset: Optional[int] = None,
+              threads: Optional[int] = None, sinks=None, alibi=None, softcap: Optional[float] = None) -> np.ndarray:
+    """Gradient of L = <O, dO> with respect to the additive mask, shaped like the mask: each
+    score's dM = P (dP - Delta) (the mask is added after the cap, so no cap' factor; 0 where an
+    entry is hidden), summed over the batch entries / heads the mask is broadcast over."""
+    q, k, v, do, mask, sinks, alibi = _f64(q), _f64(k), _f64(v), _f64(do), _f64(mask), _f64(sinks), _f64(alibi)
+    if mask is None:
+        raise ValueError("bias_grad needs the mask it differentiates")
+    p = _problem(q, k, mask, scale, causal, q_offset, sinks, alibi, softcap)
+    B, Hq, Sq, _ = q.shape
+    Sk = k.shape[2]
+    dm = np.zeros((B, Hq, Sq, Sk), np.float64)
+    rc = _load().ora_score_grad(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(do), _ptr(dm),
+                                threads or default_threads())
+    if rc:
+        raise ValueError(f"oracle rejected the problem (code {rc})")
+    if mask.ndim == 3:  # shared by the heads
+        dm = dm.sum(axis=1)
+    elif mask.shape[1] == 1:
+        dm = dm.sum(axis=1, keepdims=True)
+    if mask.shape[0] == 1 and B > 1:  # shared by the batch
+        dm = dm.sum(axis=0, keepdims=True)
+    return dm
 
 
 def sink_grad(sinks, lse, delta) -> np.ndarray:

@@ -29,6 +29,9 @@
  *   dQ_i    = scale * sum_j dS_ij k_j
  *   dK_j    = scale * sum_{h in group} sum_i dS_ij q_i
  *   dV_j    =         sum_{h in group} sum_i P_ij dO_i
+ *   dM_ij   = P_ij (dP_ij - Delta_i)   (the gradient of the additive term M_ij, which
+ *             enters S after the cap: a learnable KQ bias, another modifier on the pull
+ *             request's list; 0 where the entry is hidden)
  *
  * Sources on the pages:
  *   - fully masked query rows give O = 0 and LSE = 0, where a plain softmax
@@ -407,4 +410,46 @@ int ora_cols(const ora_problem *p, const double *Q, const double *K, const doubl
     run_parallel(col_item, &c, n, 1, nthreads);
     free(flag); free(LSE); free(Delta); free(need);
     return 0;
+}
+
+typedef struct {
+    ora_inputs in;
+    double *dM; /* [B, Hq, Sq, Sk] */
+} bias_job;
+
+static void bias_item(void *vctx, int64_t idx, double *scratch) {
+    bias_job *c = (bias_job *)vctx;
+    const ora_problem *p = c->in.p;
+    const int i = (int)(idx % p->Sq);
+    const int h = (int)((idx / p->Sq) % p->Hq);
+    const int b = (int)(idx / ((int64_t)p->Sq * p->Hq));
+    const int g = kv_head(p, h);
+    /* scratch holds the score row (Sk) followed by the output row (D) */
+    double lse = 0.0, delta = 0.0;
+    row_forward(&c->in, b, h, i, scratch, scratch + p->Sk, &lse, &delta);
+    double *out = c->dM + idx * p->Sk;
+    const double *doi = do_row(&c->in, b, h, i);
+    for (int j = 0; j < p->Sk; ++j) {
+        const double s = score(&c->in, b, h, i, j);
+        if (s == -INFINITY) {
+            out[j] = 0.0;
+            continue;
+        }
+        const double pij = exp(s - lse);
+        out[j] = pij * (dot(doi, v_row(&c->in, b, g, j), p->D) - delta);
+    }
+}
+
+/* The gradient of every additive score term, dM [B, Hq, Sq, Sk] = P (dP - Delta) per
+ * entry (no cap' factor: the term is added after the cap). The Python wrapper sums it
+ * over the mask's broadcast dimensions. */
+int ora_score_grad(const ora_problem *p, const double *Q, const double *K, const double *V, const double *M,
+                   const double *dO, double *dM, int nthreads) {
+    int e = check_problem(p);
+    if (e) return e;
+    bias_job c;
+    memset(&c, 0, sizeof c);
+    c.in.p = p; c.in.Q = Q; c.in.K = K; c.in.V = V; c.in.M = M; c.in.dO = dO;
+    c.dM = dM;
+    return run_parallel(bias_item, &c, (int64_t)p->B * p->Hq * p->Sq, p->Sk + p->D, nthreads);
 }

@@ -781,3 +781,64 @@ def test_softcap_limits():
     assert np.abs(r["dV"]).max() > 0.1
     with pytest.raises(ValueError):
         oracle.forward(q, k, v, scale=sc, softcap=-1.0)
+
+
+# ---------------------------------------------------------------------------
+# gradient of the additive mask (a learnable KQ bias): dM = P (dP - Delta) per entry,
+# summed over the dimensions the mask is broadcast over
+# ---------------------------------------------------------------------------
+def _bias_problem(seed, B=2, Hq=4, Hkv=2, Sq=5, Sk=6, D=4, heads=True):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, Sq, D))
+    k = rng.standard_normal((B, Hkv, Sk, D))
+    v = rng.standard_normal((B, Hkv, Sk, D))
+    do = rng.standard_normal((B, Hq, Sq, D))
+    m = 0.7 * rng.standard_normal((B, Hq, Sq, Sk) if heads else (1, Sq, Sk))
+    if heads:
+        m[0, 1, 2, 3] = -np.inf
+        m[1, 3, 4, :] = -np.inf  # a fully masked row in one head
+    else:
+        m[0, 2, 3] = -np.inf
+    return q, k, v, do, m
+
+
+@pytest.mark.parametrize("heads,causal,cap", [(True, False, None), (False, False, None), (True, True, 2.5),
+                                             (False, True, None)])
+def test_bias_gradient_finite_differences(heads, causal, cap):
+    """dM against central differences of L = <O, dO> in every finite mask entry (float64), with a
+    per-head and a batch- and head-shared mask (whose gradient sums over both), causal masking,
+    a logit softcap (the mask is added after the cap: no cap' factor) and ALiBi."""
+    q, k, v, do, m = _bias_problem(31 + int(heads) + 2 * int(causal), heads=heads)
+    sc = 0.45
+    al = np.array([0.1, 0.2, 0.05, 0.3])
+    g = oracle.bias_grad(q, k, v, do, m, scale=sc, causal=causal, alibi=al, softcap=cap)
+    assert g.shape == m.shape
+    assert np.all(g[~np.isfinite(m)] == 0)
+
+    def loss(mm):
+        O, _ = oracle.forward(q, k, v, mm, scale=sc, causal=causal, alibi=al, softcap=cap, threads=1)
+        return float(np.sum(O * do))
+
+    h = 1e-6
+    fd = np.zeros_like(g)
+    for idx in zip(*np.nonzero(np.isfinite(m))):
+        mp, mn = m.copy(), m.copy()
+        mp[idx] += h
+        mn[idx] -= h
+        fd[idx] = (loss(mp) - loss(mn)) / (2 * h)
+    err = np.abs(fd - g).max() / np.abs(g).max()
+    assert err < 1e-6, err
+
+
+def test_bias_gradient_rows_sum_to_zero_and_match_dq():
+    """Two closed forms of dM = P (dP - Delta) without a sink: every row of one head sums to 0
+    (sum_j P_ij dP_ij = Delta_i and sum_j P_ij = 1), and for a per-head mask without a cap,
+    dQ_i = scale sum_j dM_ij k_j, which the oracle's backward computes by a separate route."""
+    q, k, v, do, m = _bias_problem(41, heads=True)
+    sc = 0.6
+    g = oracle.bias_grad(q, k, v, do, m, scale=sc)
+    ref = oracle.backward(q, k, v, do, m, scale=sc)
+    np.testing.assert_allclose(g.sum(axis=-1), 0.0, atol=1e-12)
+    G = q.shape[1] // k.shape[1]
+    dq = sc * np.einsum("bhij,bhjd->bhid", g, np.repeat(k, G, axis=1))
+    np.testing.assert_allclose(dq, ref["dQ"], rtol=1e-10, atol=1e-12)
