@@ -39,7 +39,8 @@ class FaAttnParams(ctypes.Structure):
                 ("bwd_dq_launch", ctypes.c_int32), ("sinks", ctypes.c_void_p), ("alibi", ctypes.c_void_p),
                 ("q_split_tiles", ctypes.c_int32), ("mask_stride_h", ctypes.c_int64), ("softcap", ctypes.c_float),
                 ("bwd_kv_walk", ctypes.c_int32), ("kv_format", ctypes.c_int32), ("k_scale", FaView),
-                ("v_scale", FaView)]
+                ("v_scale", FaView), ("dbias", ctypes.c_void_p), ("dbias_stride_b", ctypes.c_int64),
+                ("dbias_stride_h", ctypes.c_int64), ("dbias_stride_q", ctypes.c_int64)]
 
 
 class FaError(RuntimeError):
@@ -187,7 +188,8 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
                 window: tuple = (-1, -1), dq_launch: int = 0,
                 sinks: Optional[torch.Tensor] = None, alibi: Optional[torch.Tensor] = None,
                 q_split_tiles: int = 0, softcap: float = 0.0, kv_walk: int = 0,
-                k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None) -> FaAttnParams:
+                k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                dbias: Optional[torch.Tensor] = None) -> FaAttnParams:
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Sk, Dk = k.shape
     if Bk != B or Dk != D:
@@ -239,6 +241,15 @@ def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: Optional[float], cau
             p.mask_tiles = mask_tiles.data_ptr()
     elif mask_tiles is not None:
         raise ValueError("mask_tiles given without a mask")
+    if dbias is not None:  # the mask's gradient: the mask's shape and broadcast
+        if mask is None:
+            raise ValueError("dbias is the gradient of the mask: pass the mask")
+        if dbias.dtype != torch.float32 or tuple(dbias.shape) != tuple(mask.shape) or dbias.stride(-1) != 1:
+            raise ValueError("dbias must be an fp32 tensor of the mask's shape with a contiguous last dimension")
+        p.dbias = dbias.data_ptr()
+        p.dbias_stride_b = 0 if dbias.shape[0] == 1 else dbias.stride(0)
+        p.dbias_stride_q = dbias.stride(-2)
+        p.dbias_stride_h = dbias.stride(1) if dbias.dim() == 4 and dbias.shape[1] > 1 else 0
     return p
 
 
@@ -430,14 +441,17 @@ def _workspace(p: FaAttnParams, device, workspace):
 
 def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_offset=None, dq=None, dk=None,
         dv=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None, q_len=None,
-        window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0, k_scale=None, v_scale=None):
-    """Backward: returns (dQ, dK, dV), each in q's dtype, overwritten."""
+        window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0, k_scale=None, v_scale=None,
+        dbias=None):
+    """Backward: returns (dQ, dK, dV), each in q's dtype, overwritten. ``dbias``: optional fp32
+    tensor of the mask's shape that receives the mask's gradient, added in (zero it first)."""
     _check_qkv(q, k, v, k_scale, v_scale)
     _expect("dout", dout, dtype=q.dtype, shape=q.shape)
     _check_rowstats(q, lse=lse, delta=delta)
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, window=window,
-                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles, softcap=softcap, kv_walk=kv_walk, k_scale=k_scale, v_scale=v_scale)
+                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles, softcap=softcap, kv_walk=kv_walk, k_scale=k_scale, v_scale=v_scale,
+                    dbias=dbias)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     # (dK / dV in the compute dtype also for a K/V window stored as fp16 or q8_0)
     dk = torch.empty(k.shape, dtype=q.dtype, device=q.device) if dk is None else dk
@@ -446,7 +460,7 @@ def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_off
     _expect("dk", dk, dtype=q.dtype, shape=k.shape)
     _expect("dv", dv, dtype=q.dtype, shape=k.shape)
     _resident(q.device, q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, dout=dout, lse=lse, delta=delta, dq=dq, dk=dk, dv=dv, mask=mask,
-              mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, alibi=alibi)
+              mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, alibi=alibi, dbias=dbias)
     ws, nbytes = _workspace(p, q.device, workspace)
     _check("fa_train_bwd", lib().fa_train_bwd(ctypes.byref(p), view4(q), view4(k), view4(v), view4(dout), view3(lse),
                                               view3(delta), view4(dq), view4(dk), view4(dv), ws.data_ptr(), nbytes,
@@ -456,7 +470,8 @@ def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_off
 
 def bwd_noalloc(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_offset=None, dq=None,
                 dk=None, dv=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None, q_len=None,
-                window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0, k_scale=None, v_scale=None):
+                window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0, k_scale=None, v_scale=None,
+                dbias=None):
     """Backward through fa_train_bwd_noalloc: the results of bwd(), with the workspace taken from
     the library's static device scratch instead of an allocation (dQ, dK and dV are still the
     caller's; pass them to allocate nothing here either)."""
@@ -465,7 +480,8 @@ def bwd_noalloc(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=Fals
     _check_rowstats(q, lse=lse, delta=delta)
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, window=window,
-                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles, softcap=softcap, kv_walk=kv_walk, k_scale=k_scale, v_scale=v_scale)
+                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles, softcap=softcap, kv_walk=kv_walk, k_scale=k_scale, v_scale=v_scale,
+                    dbias=dbias)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     # (dK / dV in the compute dtype also for a K/V window stored as fp16 or q8_0)
     dk = torch.empty(k.shape, dtype=q.dtype, device=q.device) if dk is None else dk
@@ -474,7 +490,7 @@ def bwd_noalloc(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=Fals
     _expect("dk", dk, dtype=q.dtype, shape=k.shape)
     _expect("dv", dv, dtype=q.dtype, shape=k.shape)
     _resident(q.device, q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, dout=dout, lse=lse, delta=delta, dq=dq, dk=dk, dv=dv, mask=mask,
-              mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, alibi=alibi)
+              mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, alibi=alibi, dbias=dbias)
     _check("fa_train_bwd_noalloc",
            lib().fa_train_bwd_noalloc(ctypes.byref(p), view4(q), view4(k), view4(v), view4(dout), view3(lse),
                                       view3(delta), view4(dq), view4(dk), view4(dv), _stream_handle(stream)))
@@ -524,16 +540,18 @@ def tune_bwd_splits(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=
 
 def bwd_chunked(q, k, v, dout, lse, delta, dk_acc, dv_acc, *, mask=None, scale=None, causal=True, q_offset=None,
                 dq=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None,
-                q_len=None, window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0, k_scale=None, v_scale=None):
+                q_len=None, window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0, k_scale=None, v_scale=None,
+                dbias=None):
     """Chunked backward: returns dQ for the chunk; ADDS dK/dV into the fp32 window
-    accumulators ``dk_acc`` / ``dv_acc`` ([B, Hkv, >= Sk, D])."""
+    accumulators ``dk_acc`` / ``dv_acc`` ([B, Hkv, >= Sk, D]) and, when given, the mask's
+    gradient into ``dbias`` (the mask's shape, fp32)."""
     _check_qkv(q, k, v, k_scale, v_scale)
     _expect("dout", dout, dtype=q.dtype, shape=q.shape)
     _check_rowstats(q, lse=lse, delta=delta)
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len,
                     q_len=q_len, window=window, dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles,
-                    softcap=softcap, kv_walk=kv_walk, k_scale=k_scale, v_scale=v_scale)
+                    softcap=softcap, kv_walk=kv_walk, k_scale=k_scale, v_scale=v_scale, dbias=dbias)
     if dk_acc.dtype != torch.float32 or dv_acc.dtype != torch.float32:
         raise TypeError("the window accumulators must be float32")
     B, Hkv, Sk, D = k.shape
@@ -543,7 +561,7 @@ def bwd_chunked(q, k, v, dout, lse, delta, dk_acc, dv_acc, *, mask=None, scale=N
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     _expect("dq", dq, dtype=q.dtype, shape=q.shape)
     _resident(q.device, q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, dout=dout, lse=lse, delta=delta, dq=dq, dk_acc=dk_acc, dv_acc=dv_acc,
-              mask=mask, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, alibi=alibi)
+              mask=mask, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, alibi=alibi, dbias=dbias)
     ws, nbytes = _workspace(p, q.device, workspace)
     _check("fa_train_bwd_chunked",
            lib().fa_train_bwd_chunked(ctypes.byref(p), view4(q), view4(k), view4(v), view4(dout), view3(lse),

@@ -107,6 +107,18 @@ fa_status check_params(const fa_attn_params* p) {
   if (reinterpret_cast<uintptr_t>(p->key_len) % 4 || reinterpret_cast<uintptr_t>(p->q_len) % 4)
     return fail(FA_ERR_ALIGN, "key_len / q_len are not 4-byte aligned");
   if (!(p->softcap >= 0.f) || isinf(p->softcap)) return fail(FA_ERR_SHAPE, "softcap must be >= 0 and finite");
+  if (p->dbias) {
+    if (!p->mask) return fail(FA_ERR_SHAPE, "dbias is the gradient of a dense mask: mask is NULL");
+    if (p->dtype == FA_BF16 && p->softcap > 0.f)
+      return fail(FA_ERR_UNSUPPORTED, "the mask gradient is not produced under a logit softcap in bf16");
+    if (p->dbias_stride_b < 0 || p->dbias_stride_h < 0 || p->dbias_stride_q < p->Sk)
+      return fail(FA_ERR_STRIDE, "dbias strides must be >= 0 with dbias_stride_q >= Sk");
+    if (p->B > 1 && (p->dbias_stride_b == 0) != (p->mask_stride_b == 0))
+      return fail(FA_ERR_STRIDE, "dbias must be shared by the batch exactly when the mask is");
+    if (p->Hq > 1 && (p->dbias_stride_h == 0) != (p->mask_stride_h == 0))
+      return fail(FA_ERR_STRIDE, "dbias must be shared by the heads exactly when the mask is");
+    if (reinterpret_cast<uintptr_t>(p->dbias) % 4) return fail(FA_ERR_ALIGN, "dbias is not 4-byte aligned");
+  }
   if (p->mask) {
     if (p->mask_stride_q < p->Sk) return fail(FA_ERR_STRIDE, "mask_stride_q (%lld) < Sk", (long long)p->mask_stride_q);
     if (p->mask_stride_b < 0) return fail(FA_ERR_STRIDE, "mask_stride_b is negative");
@@ -492,9 +504,16 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
     in_names[n_in] = "mask";
     ins[n_in++] = mask_extent(p);
   }
-  Extent outs[4] = {edq, edk, edv, ews};
-  const char* out_names[4] = {"dq", accumulate ? "dk_acc" : "dk", accumulate ? "dv_acc" : "dv", "workspace"};
-  if ((s = check_alias(outs, 4, out_names, ins, n_in, in_names))) return s;
+  Extent outs[5] = {edq, edk, edv, ews};
+  const char* out_names[5] = {"dq", accumulate ? "dk_acc" : "dk", accumulate ? "dv_acc" : "dv", "workspace", "dbias"};
+  int n_out = 4;
+  if (p->dbias) {  // rows of Sk fp32 entries, one plane per batch entry / head unless shared
+    const fa_view dbv = {p->dbias, p->dbias_stride_b, p->dbias_stride_h, p->dbias_stride_q};
+    if ((s = check_view(&dbv, "dbias", p->dbias_stride_b ? p->B : 1, p->dbias_stride_h ? p->Hq : 1, p->Sq, p->Sk, 4,
+                        false, true, &outs[n_out++])))
+      return s;
+  }
+  if ((s = check_alias(outs, n_out, out_names, ins, n_in, in_names))) return s;
   if (use_scratch && need > 0) {
     if ((s = scratch_of_current_device(&workspace))) return s;
     workspace_bytes_given = FA_TRAIN_NOALLOC_SCRATCH_BYTES;
@@ -530,6 +549,13 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   a.delta_sh = delta->stride_h;
   a.accumulate = accumulate ? 1 : 0;
   a.inv_scale = 1.f / p->scale;
+  a.dbias = p->dbias;
+  a.dbias_sb = p->dbias_stride_b;
+  a.dbias_sh = p->dbias_stride_h;
+  a.dbias_sq = p->dbias_stride_q;
+  a.dbias_atomic = (p->B > 1 && p->dbias_stride_b == 0) || (p->Hq > 1 && p->dbias_stride_h == 0);
+  a.dbias_vec4 = reinterpret_cast<uintptr_t>(p->dbias) % 16 == 0 && p->dbias_stride_b % 4 == 0 &&
+                 p->dbias_stride_h % 4 == 0 && p->dbias_stride_q % 4 == 0;
   const uintptr_t mp = reinterpret_cast<uintptr_t>(p->mask);
   a.mask_vec4 = p->mask && mp % 16 == 0 && p->mask_stride_q % 4 == 0 && p->mask_stride_b % 4 == 0 &&
                  p->mask_stride_h % 4 == 0;

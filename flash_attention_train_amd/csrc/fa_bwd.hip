@@ -187,8 +187,16 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(const BwdArgs args) {
           if (MASK && vis) x += a.mask[b * a.mask_sb + h * a.mask_sh + (int64_t)qi * a.mask_sq + key] * kLog2e;
           if (a.alibi) x -= al2 * fabsf((float)((int64_t)key - a.q_offset - qi));
           const float p = vis ? fast_exp2(x - lse_lds[ql]) : 0.f;
+          const float dm = p * (dpacc[r] - dlt_lds[ql]);  // the gradient of the additive term
           sacc[r] = p;
-          dpacc[r] = p * (dpacc[r] - dlt_lds[ql]) * dcap;
+          dpacc[r] = dm * dcap;
+          if (MASK && args.dbias && vis) {  // the mask's gradient (a learnable score bias), added in
+            float* db = args.dbias + b * args.dbias_sb + h * args.dbias_sh + (int64_t)qi * args.dbias_sq + key;
+            if (args.dbias_atomic)
+              __hip_atomic_fetch_add(db, dm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+              *db += dm;
+          }
         }
         // dV += P^T dO and dK += dS^T Q over this 32-row block, 16 rows per step:
         // registers 8 hh .. 8 hh + 7 hold rows 16 hh + {4 g .. 4 g + 3} and

@@ -109,6 +109,32 @@ __device__ __forceinline__ void store_block(const f32x16 (&acc)[D / 32], float m
   for (int i = 0; i < N; ++i) sink.put(r0 + i * (64 / CH), col, v[i]);
 }
 
+// The mask's gradient (a learnable score bias) for one lane's 16 scores: dS = P (dP - Delta)
+// of query row `row` at keys k0 + 8 rr + e (register 4 rr + e), added into dbias; by atomics
+// where several heads or batch entries share the entries, else as 16-byte read-add-writes.
+__device__ __forceinline__ void add_mask_grad(const BwdArgs& args, int b, int h, int row, int k0, const f32x16& ds) {
+  const AttnShape& a = args.a;
+  if (row >= a.Sq) return;
+  float* db = args.dbias + b * args.dbias_sb + h * args.dbias_sh + (int64_t)row * args.dbias_sq;
+  #pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int k4 = k0 + 8 * rr;
+    if (!args.dbias_atomic && args.dbias_vec4 && k4 + 3 < a.Sk) {
+      f32x4* p = reinterpret_cast<f32x4*>(db + k4);
+      *p = *p + f32x4{ds[4 * rr], ds[4 * rr + 1], ds[4 * rr + 2], ds[4 * rr + 3]};
+      continue;
+    }
+    #pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (k4 + e >= a.Sk) continue;
+      if (args.dbias_atomic)
+        __hip_atomic_fetch_add(db + k4 + e, ds[4 * rr + e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        db[k4 + e] += ds[4 * rr + e];
+    }
+  }
+}
+
 // Destination of a wave's 32-row result block: row 0's address and the row pitch in
 // bytes, the rows that exist, and the element kind: bf16 (stored), fp32 (stored, a
 // partial slice) or fp32 added to (an accumulator). Built once before the stores, so
@@ -1051,7 +1077,9 @@ __device__ __forceinline__ void dkdv_role_unit(const BwdArgs& args, const BwdPla
 // ---------------------------------------------------------------------------
 // dQ workgroup
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool MASK, bool BIAS, bool LOWREG = false, bool CAP = false, int KVF = 0>
+// MG: the mask's gradient is requested (a masked, uncapped problem; kernels of their own, so that
+// the others carry none of its code)
+template <int D, bool CAUSAL, bool MASK, bool BIAS, bool LOWREG = false, bool CAP = false, int KVF = 0, bool MG = false>
 __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
   constexpr int DS = D / 16, DB = D / 32;
   using TL = Tile<D>;
@@ -1329,6 +1357,7 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
       for (int r = 0; r < 16; ++r) st[r] = fast_exp2(fmaf(st[r], cs, -lse2));
       #pragma unroll
       for (int r = 0; r < 16; ++r) st[r] = st[r] * (CAP ? dpt[r] : dpt[r] - dlt);
+      if constexpr (MG) add_mask_grad(args, b, h, row, key0 + 32 * kb + 4 * g, st);
       #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         if constexpr (LOWREG) read_kbt(hh);  // (two workgroups per unit: read when needed)
@@ -1369,7 +1398,7 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
 // Units whose mask blocks carry additive values run a body compiled with the
 // mask-value reads; all others (dead / open / 0-or--inf blocks) a body without them,
 // which keeps that code and its registers out of the common loop.
-template <int D, bool CAUSAL, bool MASK, bool CAP = false, int KVF = 0>
+template <int D, bool CAUSAL, bool MASK, bool CAP = false, int KVF = 0, bool MG = false>
 __global__ __launch_bounds__(NT) void bwd_bf16_kernel(const BwdArgs args, const BwdPlan plan) {
   constexpr int KV_LDS = 3 * 2 * KV_BM * D * 2 + 2 * 3 * KV_BM * 16 * 2;
   constexpr int Q_LDS = 2 * 2 * Q_BN * D * 2;
@@ -1388,9 +1417,9 @@ __global__ __launch_bounds__(NT) void bwd_bf16_kernel(const BwdArgs args, const 
     const QUnit u = q_unit_of(a, plan, unit);
     if (MASK && any_bias_block(a, u.b, u.qt * (Q_BM / kMaskTile), Q_BM / kMaskTile, 0,
                                (a.Sk + kMaskTile - 1) / kMaskTile))
-      dq_unit<D, CAUSAL, MASK, true, false, CAP, KVF>(args, plan, unit, smem);
+      dq_unit<D, CAUSAL, MASK, true, false, CAP, KVF, MG>(args, plan, unit, smem);
     else
-      dq_unit<D, CAUSAL, MASK, false, false, CAP, KVF>(args, plan, unit, smem);
+      dq_unit<D, CAUSAL, MASK, false, false, CAP, KVF, MG>(args, plan, unit, smem);
   }
 }
 
@@ -1414,7 +1443,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_role_kernel(const BwdArgs args, con
 // The dQ walk as a kernel of its own: its registers fit two workgroups per compute unit
 // (the dK/dV walk's do not), so that one workgroup's LDS and memory waits are covered by
 // the other's products. Launched after the dK/dV-only grid when the plan asks for it.
-template <int D, bool CAUSAL, bool MASK, bool CAP = false, int KVF = 0>
+template <int D, bool CAUSAL, bool MASK, bool CAP = false, int KVF = 0, bool MG = false>
 __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(const BwdArgs args, const BwdPlan plan) {
   constexpr int Q_LDS = 2 * 2 * Q_BN * D * 2;
   __shared__ __attribute__((aligned(16))) char smem[Q_LDS];
@@ -1423,12 +1452,12 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(const BwdArgs args, const
   const QUnit u = q_unit_of(a, plan, unit);
   if (MASK && any_bias_block(a, u.b, u.qt * (Q_BM / kMaskTile), Q_BM / kMaskTile, 0,
                              (a.Sk + kMaskTile - 1) / kMaskTile))
-    dq_unit<D, CAUSAL, MASK, true, true, CAP, KVF>(args, plan, unit, smem);
+    dq_unit<D, CAUSAL, MASK, true, true, CAP, KVF, MG>(args, plan, unit, smem);
   else
-    dq_unit<D, CAUSAL, MASK, false, true, CAP, KVF>(args, plan, unit, smem);
+    dq_unit<D, CAUSAL, MASK, false, true, CAP, KVF, MG>(args, plan, unit, smem);
 }
 
-template <int D, bool CAUSAL, bool MASK, bool CAP = false, int KVF = 0>
+template <int D, bool CAUSAL, bool MASK, bool CAP = false, int KVF = 0, bool MG = false>
 hipError_t launch_cm(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream) {
   if constexpr (!CAP && KVF == 0) {
     if (plan.kv_role) {
@@ -1436,22 +1465,22 @@ hipError_t launch_cm(const BwdArgs& args, const BwdPlan& plan, hipStream_t strea
         hipLaunchKernelGGL((bwd_role_kernel<D, CAUSAL, MASK>), dim3(plan.n_kv_units), dim3(NT), 0, stream, args, plan);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess || plan.n_q_units == 0) return e;
-      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, MASK, CAP, KVF>), dim3(plan.n_q_units), dim3(NT), 0, stream, args,
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, MASK, CAP, KVF, MG>), dim3(plan.n_q_units), dim3(NT), 0, stream, args,
                          plan);
       return hipGetLastError();
     }
   }
   if (!plan.dq_separate) {
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, MASK, CAP, KVF>), dim3(plan.n_kv_units + plan.n_q_units), dim3(NT), 0,
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, MASK, CAP, KVF, MG>), dim3(plan.n_kv_units + plan.n_q_units), dim3(NT), 0,
                        stream, args, plan);
     return hipGetLastError();
   }
   if (plan.n_kv_units > 0)
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, MASK, CAP, KVF>), dim3(plan.n_kv_units), dim3(NT), 0, stream, args,
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, MASK, CAP, KVF, MG>), dim3(plan.n_kv_units), dim3(NT), 0, stream, args,
                        plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.n_q_units == 0) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, MASK, CAP, KVF>), dim3(plan.n_q_units), dim3(NT), 0, stream, args, plan);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, MASK, CAP, KVF, MG>), dim3(plan.n_q_units), dim3(NT), 0, stream, args, plan);
   return hipGetLastError();
 }
 
@@ -1468,6 +1497,9 @@ hipError_t launch_t(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream
     if (mask) return causal ? launch_cm<D, true, true, true>(args, plan, stream) : launch_cm<D, false, true, true>(args, plan, stream);
     return causal ? launch_cm<D, true, false, true>(args, plan, stream) : launch_cm<D, false, false, true>(args, plan, stream);
   }
+  if (args.dbias)  // (a dense mask, no softcap: checked on the host)
+    return causal ? launch_cm<D, true, true, false, 0, true>(args, plan, stream)
+                  : launch_cm<D, false, true, false, 0, true>(args, plan, stream);
   if (causal && mask) return launch_cm<D, true, true>(args, plan, stream);
   if (causal) return launch_cm<D, true, false>(args, plan, stream);
   if (mask) return launch_cm<D, false, true>(args, plan, stream);

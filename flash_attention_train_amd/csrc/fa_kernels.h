@@ -203,6 +203,11 @@ struct BwdArgs {
   int accumulate;  // 1: dK/dV are fp32 accumulators and receive +=, 0: overwrite in dtype
   float inv_scale; // 1 / scale
   int mask_vec4;   // the mask can be read 4 floats at a time
+  // the mask's gradient (fp32, added into, broadcast like the mask) or null; dbias_atomic:
+  // several heads or batch entries add into one entry; dbias_vec4: 16-byte rows of 4 entries
+  float* dbias;
+  int64_t dbias_sb, dbias_sh, dbias_sq;
+  int dbias_atomic, dbias_vec4;
 };
 
 // unit -> (key tile, batch, kv head, split) of a dK/dV workgroup; key tiles vary slowest so

@@ -117,9 +117,10 @@ struct Tile {
     constexpr int W = NT / 64, PER = ROWS * NCH / NT, RSTEP = 64 * W / NCH;
     static_assert((ROWS * NCH) % NT == 0, "tile must split evenly over the threads");
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(group_wave < 0 ? (int)(threadIdx.x >> 6) : group_wave);
+    const int gw = group_wave < 0 ? (int)(threadIdx.x >> 6) : group_wave;
+    const int wave = __builtin_amdgcn_readfirstlane(gw);  // (for the LDS destinations)
     const uint32_t st = (uint32_t)stride;
-    const int row0 = (64 * wave + lane) / NCH;
+    const int row0 = (64 * gw + lane) / NCH;
     const int v = valid < ROWS ? valid : ROWS;
     const u32x4 rsrc = raw_rsrc(src, v > 0 ? ((uint32_t)(v - 1) * st + (uint32_t)D) * 2u : 0u);
     if constexpr (RSTEP % 16 == 0) {

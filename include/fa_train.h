@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FA_TRAIN_ABI_VERSION 12
+#define FA_TRAIN_ABI_VERSION 13
 
 typedef enum fa_status {
     FA_OK = 0,
@@ -193,6 +193,19 @@ typedef struct fa_attn_params {
     int32_t kv_format;
     fa_view k_scale;
     fa_view v_scale;
+    /* The gradient of the additive mask, for a learnable score bias (the pull request's KQ
+     * bias): an optional fp32 output of the backward entry points (fa_train_bwd,
+     * fa_train_bwd_chunked, fa_train_bwd_noalloc). For every score it adds
+     * dL/dM_ij = P_ij (dP_ij - Delta_i) (0 where the entry is hidden) into
+     * dbias + b * dbias_stride_b + h * dbias_stride_h + i * dbias_stride_q + j: the caller
+     * zeroes it before the first call, and the chunked walk's chunks sum into it. Its broadcast
+     * follows the mask's: dbias_stride_b is 0 exactly when mask_stride_b is 0 (the batch
+     * entries then add into one plane), dbias_stride_h is 0 exactly when mask_stride_h is 0
+     * (the heads add into one plane); dbias_stride_q >= Sk; rows must not overlap. Needs a
+     * dense mask (FA_ERR_SHAPE without one); a bf16 problem with a logit softcap does not take
+     * it (FA_ERR_UNSUPPORTED). NULL: not computed. */
+    float* dbias;
+    int64_t dbias_stride_b, dbias_stride_h, dbias_stride_q;
 } fa_attn_params;
 
 #define FA_KV_DTYPE 0

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(L, n), n
         assert n in B.SIGNATURES, f"{n} has no ctypes signature in the binding"
-    assert L.fa_train_version() == 12
+    assert L.fa_train_version() == 13
 
 
 BASE = 0x7F0000000000  # fake, 256-byte aligned device addresses
@@ -48,7 +48,7 @@ def params(**kw):
              mask_stride_b=0, mask_stride_q=0, mask_tiles=None, fwd_variant=0, kv_split=0, q_split=0, fwd_split=0, key_len=None, q_len=None,
              window_left=-1, window_right=-1, bwd_dq_launch=0, sinks=None, alibi=None,
              q_split_tiles=0, mask_stride_h=0, softcap=0.0, bwd_kv_walk=0, kv_format=0, k_scale=B.FaView(),
-             v_scale=B.FaView())
+             v_scale=B.FaView(), dbias=None, dbias_stride_b=0, dbias_stride_h=0, dbias_stride_q=0)
     a.update(kw)
     return B.FaAttnParams(*(a[f] for f, _ in B.FaAttnParams._fields_))
 
@@ -232,15 +232,14 @@ def test_softcap_params_rejected():
         assert L.fa_train_fwd(ctypes.byref(p), view(0), view(1, H=2), view(2, H=2), view(3), lse, None) == code, kw
         assert L.fa_train_bwd(ctypes.byref(p), view(0), view(1, H=2), view(2, H=2), view(3), lse, dlt, view(8),
                               view(9, H=2), view(10, H=2), None, 0, None) == code, kw
-    # a softcap backward under additive scores (a dense mask or ALiBi) runs on the generic
-    # kernels, whose workspace is the fp32 dQ accumulator for both dtypes; without them the
-    # bf16 one keeps the MFMA kernels' plan (no workspace for this unsplit shape); the bf16
-    # forward keeps its split walks
+    # a softcap backward keeps the bf16 matrix-core kernels' plan also under a dense mask or ALiBi
+    # (no workspace for this unsplit shape); fp32 runs on the generic kernels, whose workspace is
+    # the fp32 dQ accumulator; the bf16 forward keeps its split walks
     masked = dict(softcap=30.0, mask=BASE + 11 * (1 << 24), mask_stride_q=64)
     slopes = dict(softcap=30.0, alibi=BASE + 11 * (1 << 24))
-    for dt in (B.FA_BF16, B.FA_F32):
-        for kw in (masked, slopes):
-            assert L.fa_train_bwd_workspace_bytes(ctypes.byref(params(dtype=dt, **kw))) == 1 * 4 * 64 * 64 * 4
+    for kw in (masked, slopes):
+        assert L.fa_train_bwd_workspace_bytes(ctypes.byref(params(dtype=B.FA_BF16, **kw))) == 0
+        assert L.fa_train_bwd_workspace_bytes(ctypes.byref(params(dtype=B.FA_F32, **kw))) == 1 * 4 * 64 * 64 * 4
     assert L.fa_train_bwd_workspace_bytes(ctypes.byref(params(softcap=30.0))) == \
         L.fa_train_bwd_workspace_bytes(ctypes.byref(params())) == 0
     long_keys = dict(softcap=30.0, Sk=4096)
@@ -306,3 +305,35 @@ def test_stored_kv_formats_rejected_where_unsupported():
     p = params(**q8)
     assert B.lib().fa_train_bwd(ctypes.byref(p), view(0), kv8(1), kv8(2), view(3), lse_view(4), lse_view(5),
                                 view(6), view(7, H=2), view(11, H=2), None, 0, None) == 6  # dV over v_scale
+
+
+def test_mask_gradient_params_rejected():
+    """dbias (the mask's gradient) needs a dense mask, fp32-aligned rows of at least Sk entries, the
+    mask's broadcast over batch and heads, no overlap with the inputs, and no softcap in bf16; all
+    checked before any launch."""
+    L = B.lib()
+    lse, dlt = lse_view(5), lse_view(6)
+    m = dict(mask=BASE + 11 * (1 << 24), mask_stride_q=64)
+    db = dict(dbias=BASE + 12 * (1 << 24), dbias_stride_q=64)
+    bad = [(dict(**db), 2),                                         # no mask
+           (dict(**m, **db, softcap=30.0), 7),                      # bf16 softcap
+           (dict(**m, dbias=BASE + 12 * (1 << 24), dbias_stride_q=32), 4),  # rows shorter than Sk
+           (dict(**m, **db, dbias_stride_h=64 * 64), 4),            # per-head gradient of a shared mask
+           (dict(**m, mask_stride_h=64 * 64, **db), 4),             # shared gradient of a per-head mask
+           (dict(**m, dbias=BASE + 12 * (1 << 24) + 2, dbias_stride_q=64), 5),  # misaligned
+           (dict(**m, dbias=BASE + 11 * (1 << 24), dbias_stride_q=64), 6)]      # the mask itself
+    for kw, code in bad:
+        p = params(**kw)
+        got = L.fa_train_bwd(ctypes.byref(p), view(0), view(1, H=2), view(2, H=2), view(3), lse, dlt, view(8),
+                             view(9, H=2), view(10, H=2), None, 0, None)
+        assert got == code, (kw, got)
+    # accepted on the host: fp32 with a softcap, and a per-head gradient of a per-head mask (the
+    # problem stops at the missing workspace of the fp32 path, after every other check)
+    ok = [dict(**m, **db, dtype=B.FA_F32, softcap=30.0),
+          dict(**m, mask_stride_h=64 * 64, dbias=BASE + 12 * (1 << 24), dbias_stride_h=64 * 64, dbias_stride_q=64,
+               dtype=B.FA_F32)]
+    for kw in ok:
+        p = params(**kw)
+        got = L.fa_train_bwd(ctypes.byref(p), view(0, elt=4), view(1, H=2), view(2, H=2), view(3), lse, dlt,
+                             view(8), view(9, H=2), view(10, H=2), None, 0, None)
+        assert got == 8, (kw, got)  # FA_ERR_WORKSPACE

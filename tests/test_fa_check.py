@@ -35,7 +35,7 @@ def params(**kw):
              mask_stride_b=0, mask_stride_q=0, mask_tiles=None, fwd_variant=0, kv_split=0, q_split=0, fwd_split=0,
              key_len=None, q_len=None, window_left=-1, window_right=-1, bwd_dq_launch=0, sinks=None, alibi=None,
              q_split_tiles=0, mask_stride_h=0, softcap=0.0, bwd_kv_walk=0, kv_format=0, k_scale=B.FaView(),
-             v_scale=B.FaView())
+             v_scale=B.FaView(), dbias=None, dbias_stride_b=0, dbias_stride_h=0, dbias_stride_q=0)
     a.update(kw)
     if a["causal"] and "q_offset" not in kw:
         a["q_offset"] = a["Sk"] - a["Sq"]
