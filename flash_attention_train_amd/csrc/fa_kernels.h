@@ -37,8 +37,8 @@ struct AttnShape {
   // ALiBi: score (h, i, j) gets -alibi[h] |j - (q_offset + i)|; or nullptr. It runs in the
   // masked kernels' bias body (every live block counts as a bias block)
   const float* alibi;
-  // logit softcap c (> 0) or 0: the scaled product x becomes c tanh(x / c) before the mask;
-  // read by the generic kernels only
+  // logit softcap c (> 0) or 0: the scaled product x becomes c tanh(x / c) before the mask
+  // and ALiBi are added
   float softcap;
   // storage of K and V for the bf16 kernels: kKvBf16 (the compute dtype), kKvF16 (fp16), or
   // kKvQ8 (q8_0: int8 quants, one fp16 scale per 32 values along D at kscale / vscale,

@@ -118,7 +118,7 @@ typedef struct fa_attn_params {
                              rows normalised by its own row sum, in bf16, with their fp32
                              exponent base and row sum, in the workspace, and a merge pass
                              combines them). fa_train_fwd never splits and rejects > 1. */
-    /* Structured masks (bf16 only; they combine with causal and with a dense mask): the
+    /* Structured masks (both dtypes; they combine with causal and with a dense mask): the
      * per-element padding and sliding-window masks of the pages' DiT batches ("sa" =
      * sliding window + padded key columns, "sa_pad" = padded key columns) without a
      * dense tensor. Entry (b, i, j) is hidden when j >= key_len[b], when i >= q_len[b]
@@ -134,7 +134,7 @@ typedef struct fa_attn_params {
      * dK/dV workgroups' launch, 2 = they run as a second kernel after it, two per compute
      * unit (chosen automatically for grids of at least 512 dQ workgroups). */
     int32_t bwd_dq_launch;
-    /* Attention sinks (bf16 only): one more logit per query head that joins every row's
+    /* Attention sinks (both dtypes): one more logit per query head that joins every row's
      * softmax denominator and has no value row (llama.cpp pull request 57 lists sinks
      * among the score modifiers its flash backward lacked). sinks[h] is a natural-log
      * logit, used as given (not scaled): LSE_i = ln(sum_j exp(S_ij) + exp(sinks[h])), and
@@ -142,7 +142,7 @@ typedef struct fa_attn_params {
      * O = 0 and LSE = sinks[h]. The backward is unchanged (it reads the LSE); the sinks'
      * own gradient comes from fa_train_bwd_sinks. */
     const float* sinks;      /* device [Hq] fp32, 4-byte aligned; NULL = none */
-    /* ALiBi (bf16 only; combines with every mask): a per-head linear penalty on the distance
+    /* ALiBi (both dtypes; combines with every mask): a per-head linear penalty on the distance
      * between a key and the query's position, one of the score modifiers the pull request's
      * flash backward lacked. Score (b, h, i, j) gets -alibi[h] * |j - (q_offset + i)|, added
      * like a mask value (after the scale); under a causal mask that is the usual
@@ -158,19 +158,15 @@ typedef struct fa_attn_params {
     /* Head stride of the mask, in elements: 0 = one mask for every head (the layout above);
      * > 0 = a mask per query head, entry (b, h, i, j) at mask + b * mask_stride_b +
      * h * mask_stride_h + i * mask_stride_q + j -- an additive score bias per head (the
-     * pull request's KQ bias), with -inf still hiding entries. Its own gradient (dS) is not
-     * produced. A per-head mask takes no mask block map (mask_tiles must be NULL). */
+     * pull request's KQ bias), with -inf still hiding entries; its gradient comes out through
+     * dbias below. A per-head mask takes no mask block map (mask_tiles must be NULL). */
     int64_t mask_stride_h;
     /* Logit softcap (0 = none; else > 0 and finite), a score modifier the pull request's flash
      * backward lacked: score (b, h, i, j) = c * tanh(scale * <q_i, k_j> / c) + the mask value,
-     * so the product is bounded by c before the mask is added; the backward carries
-     * 1 - tanh^2 into dS. The bf16 forward applies it in its MFMA kernel (split walks
-     * included), and so does the bf16 backward without a dense mask (every work
-     * decomposition); over a dense mask, and for fp32, the backward runs on the generic
-     * kernels (its workspace is then the fp32 dQ accumulator, and the mask block map is not
-     * read). It combines with causal masking and dense masks (per-head ones included), and
-     * without a dense mask with sinks and structured masks; not with ALiBi, nor with sinks or
-     * structured masks over a dense mask (FA_ERR_UNSUPPORTED). */
+     * so the product is bounded by c before the mask and ALiBi are added; the backward
+     * carries 1 - tanh^2 into dS. The bf16 kernels apply it in their MFMA walks (every work
+     * decomposition); fp32 runs on the generic kernels. It combines with every mask (dense,
+     * per head, structured), with sinks and with ALiBi. */
     float softcap;
     /* Work decomposition hint of the bf16 backward's dK/dV walk (same results up to fp32
      * summation order and one bf16 rounding of P inside dS): 0 = automatic (walk 1); 1 = one

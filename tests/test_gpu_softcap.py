@@ -1,8 +1,8 @@
 """GPU parity of the logit softcap (score (b, h, i, j) = c tanh(scale <q_i, k_j> / c) + the
 mask value) against the oracle, in fp32 and bf16: every output element by element, with the
-exact-zero checks for fully masked rows and dead key columns. The bf16 forward runs the cap in
-its MFMA kernel (whole and split key walks); the bf16 backward in its MFMA kernels when there is
-no dense mask (every work decomposition), else on the generic kernels, as fp32 does. Cases: the causal GQA layer, a
+exact-zero checks for fully masked rows and dead key columns. The bf16 forward and backward run
+the cap in their MFMA kernels (every work decomposition; under a dense mask the backward caps a
+whole block before adding the mask values); fp32 runs on the generic kernels. Cases: the causal GQA layer, a
 dense key-padding mask with fully masked rows, a score bias per head, and the chunked walk
 over a window (each chunk adding into the fp32 dK / dV accumulators). The caps are small
 enough (1 to 4 score units) that tanh is well inside its bend for N(0, 1) inputs."""
