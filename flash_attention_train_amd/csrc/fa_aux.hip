@@ -17,28 +17,47 @@ namespace fa {
 
 namespace {
 
-// One query row per D/8 consecutive lanes, 8 elements per lane, fp32 products,
-// reduced with lane shuffles inside the row's lane group.
+// One query row per D/8 consecutive lanes, 8 elements per lane, fp32 products, reduced with
+// lane shuffles inside the row's lane group. A workgroup takes kPreRows rows of one (batch,
+// head), each thread kPreRows / (256 / (D / 8)) of them with all their loads in flight.
+constexpr int kPreRows = 64;
 template <typename T, int D>
 __global__ __launch_bounds__(256) void preprocess_kernel(const PreArgs p) {
-  constexpr int LPR = D / 8;       // lanes per row
-  constexpr int RPB = 256 / LPR;   // rows per workgroup
+  constexpr int LPR = D / 8;              // lanes per row
+  constexpr int RPB = 256 / LPR;          // rows per pass of the workgroup
+  constexpr int RPT = kPreRows / RPB;     // rows per thread
   const int sub = threadIdx.x % LPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int64_t nrows = (int64_t)p.B * p.Hq * p.Sq;
-  float acc = 0.f;
-  int b = 0, h = 0, i = 0;
-  if (row < nrows) {
-    i = (int)(row % p.Sq);
-    h = (int)((row / p.Sq) % p.Hq);
-    b = (int)(row / ((int64_t)p.Sq * p.Hq));
-    Frag<T> o, d;
-    load8(o, static_cast<const T*>(p.o) + b * p.so.b + h * p.so.h + (int64_t)i * p.so.s + 8 * sub);
-    load8(d, static_cast<const T*>(p.dout) + b * p.sdo.b + h * p.sdo.h + (int64_t)i * p.sdo.s + 8 * sub);
-    for (int j = 0; j < 8; ++j) acc += elem(o, j) * elem(d, j);
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int i0 = blockIdx.x * kPreRows + threadIdx.x / LPR;
+  const T* O = static_cast<const T*>(p.o) + b * p.so.b + h * p.so.h + 8 * sub;
+  const T* dO = static_cast<const T*>(p.dout) + b * p.sdo.b + h * p.sdo.h + 8 * sub;
+  Frag<T> o[RPT], d[RPT];
+  #pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int i = i0 + j * RPB;
+    if (i < p.Sq) {
+      load8(o[j], O + (int64_t)i * p.so.s);
+      load8(d[j], dO + (int64_t)i * p.sdo.s);
+    } else {
+      zero(o[j]);
+      zero(d[j]);
+    }
   }
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < nrows && sub == 0) p.delta[b * p.delta_sb + h * p.delta_sh + i] = acc;
+  float acc[RPT];
+  #pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    acc[j] = 0.f;
+    for (int e = 0; e < 8; ++e) acc[j] += elem(o[j], e) * elem(d[j], e);
+  }
+  #pragma unroll
+  for (int j = 0; j < RPT; ++j)
+    for (int off = LPR / 2; off > 0; off >>= 1) acc[j] += __shfl_xor(acc[j], off, 64);
+  if (sub == 0) {
+    float* delta = p.delta + b * p.delta_sb + h * p.delta_sh;
+    #pragma unroll
+    for (int j = 0; j < RPT; ++j)
+      if (i0 + j * RPB < p.Sq) delta[i0 + j * RPB] = acc[j];
+  }
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(f32x4* p, int64_t n4) {
@@ -72,21 +91,20 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const DqArgs p) {
 }
 
 // Sum of the backward's fp32 partial slices, 8 consecutive elements per thread: each
-// slice element is read once, the result written once (or added to an fp32 output).
+// slice element is read once, the result written once (or added to an fp32 output). A
+// workgroup takes 256 / (D / 8) rows of one (batch, head) of one of up to three tensors.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void reduce_parts_kernel(const ReduceArgs p0, const ReduceArgs p1,
-                                                           const ReduceArgs p2) {
-  // one launch reduces up to three tensors of one output dtype (dK, dV and dQ)
-  const ReduceArgs& p = blockIdx.y == 0 ? p0 : blockIdx.y == 1 ? p1 : p2;
+                                                           const ReduceArgs p2, const int ntiles) {
+  // one launch reduces up to three tensors of one output dtype (dK, dV and dQ): grid
+  // (batch entries x ntiles row tiles, heads, tensors)
+  const int b = blockIdx.x / ntiles, tile = blockIdx.x % ntiles, h = blockIdx.y;
+  const ReduceArgs& p = blockIdx.z == 0 ? p0 : blockIdx.z == 1 ? p1 : p2;
   constexpr int CPR = D / 8;
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t nrows = (int64_t)p.B * p.H * p.S;
-  if (c >= nrows * CPR) return;
-  const int64_t row = c / CPR;
-  const int d0 = (int)(c % CPR) * 8;
-  const int i = (int)(row % p.S);
-  const int h = (int)((row / p.S) % p.H);
-  const int b = (int)(row / ((int64_t)p.S * p.H));
+  if (b >= p.B || h >= p.H) return;
+  const int i = tile * (256 / CPR) + threadIdx.x / CPR;
+  if (i >= p.S) return;
+  const int d0 = (threadIdx.x % CPR) * 8;
   const float* src = p.parts + (((int64_t)b * p.H + h) * p.S_parts + i) * D + d0;
   f32x16 acc;
   #pragma unroll
@@ -183,9 +201,7 @@ __global__ __launch_bounds__(256) void mask_tiles_kernel(const AttnShape a, uint
 
 template <typename T, int D>
 hipError_t launch_pre_t(const PreArgs& p, hipStream_t stream) {
-  constexpr int RPB = 256 / (D / 8);
-  const int64_t nrows = (int64_t)p.B * p.Hq * p.Sq;
-  const dim3 grid((unsigned)((nrows + RPB - 1) / RPB));
+  const dim3 grid((unsigned)((p.Sq + kPreRows - 1) / kPreRows), p.Hq, p.B);
   hipLaunchKernelGGL((preprocess_kernel<T, D>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
@@ -327,11 +343,19 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream) {
 
 template <typename T, int D>
 hipError_t launch_reduce_t(const ReduceArgs& p, const ReduceArgs* p1, const ReduceArgs* p2, hipStream_t stream) {
-  // blocks over the largest tensor; the others' threads past their ends return at once
-  int64_t chunks = (int64_t)p.B * p.H * p.S * (D / 8);
-  if (p2) chunks = std::max<int64_t>(chunks, (int64_t)p2->B * p2->H * p2->S * (D / 8));
-  const dim3 grid((unsigned)((chunks + 255) / 256), p2 ? 3 : p1 ? 2 : 1);
-  hipLaunchKernelGGL((reduce_parts_kernel<T, D>), grid, dim3(256), 0, stream, p, p1 ? *p1 : p, p2 ? *p2 : p);
+  // the grid covers the largest of the tensors; the others' workgroups past their ends return
+  // at once
+  int S = p.S, H = p.H, B = p.B;
+  for (const ReduceArgs* q : {p1, p2})
+    if (q) {
+      S = std::max(S, q->S);
+      H = std::max(H, q->H);
+      B = std::max(B, q->B);
+    }
+  const int rows_per_wg = 256 / (D / 8), n = p2 ? 3 : p1 ? 2 : 1, ntiles = (S + rows_per_wg - 1) / rows_per_wg;
+  const dim3 grid((unsigned)((int64_t)ntiles * B), H, n);
+  hipLaunchKernelGGL((reduce_parts_kernel<T, D>), grid, dim3(256), 0, stream, p, p1 ? *p1 : p, p2 ? *p2 : p,
+                     ntiles);
   return hipGetLastError();
 }
 

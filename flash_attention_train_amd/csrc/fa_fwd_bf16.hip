@@ -522,23 +522,47 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
 // sum w_z, LSE = (b + log2 sum w_z) ln 2; a row no split
 // saw a key for (every base -inf) gets O = 0, LSE = 0 (or LSE = its head's sink, which
 // joins the row sum here). One pass over the splits with a
-// running base (the online softmax's own rescale), one thread per 8 columns of a row.
+// running base (the online softmax's own rescale), one thread per 8 columns of a row; a
+// workgroup takes 256 / (D / 8) rows of one (batch, head), with the first kMergeAhead shares'
+// loads issued before any is used.
+constexpr int kMergeAhead = 4;
 template <int D>
 __global__ __launch_bounds__(256) void fwd_merge_kernel(const FwdArgs args) {
   constexpr int TPR = D / 8;  // threads per row
   const AttnShape& a = args.a;
   const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
-  const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int i = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   const int c = 8 * (threadIdx.x % TPR);
-  if (r >= rows) return;
+  if (i >= a.Sq) return;
+  const int64_t r = ((int64_t)b * a.Hq + h) * a.Sq + i;
   const int S = args.splits;
+  float2 mls[kMergeAhead];
+  bf16x8 p8s[kMergeAhead];
+  #pragma unroll
+  for (int z = 0; z < kMergeAhead; ++z) {
+    if (z >= S) break;
+    const int64_t zr = (int64_t)z * rows + r;
+    mls[z] = *reinterpret_cast<const float2*>(args.part_ml + 2 * zr);
+    p8s[z] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(args.part_o) + zr * D + c);
+  }
   float mx = neg_inf(), l = 0.f;
   f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
-  #pragma unroll 4
   for (int z = 0; z < S; ++z) {
-    const int64_t zr = (int64_t)z * rows + r;
-    const float2 ml = *reinterpret_cast<const float2*>(args.part_ml + 2 * zr);
-    const bf16x8 p8 = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(args.part_o) + zr * D + c);
+    float2 ml;
+    bf16x8 p8;
+    if (z < kMergeAhead) {
+      #pragma unroll
+      for (int y = 0; y < kMergeAhead; ++y)
+        if (y == z) {
+          ml = mls[y];
+          p8 = p8s[y];
+        }
+    } else {
+      const int64_t zr = (int64_t)z * rows + r;
+      ml = *reinterpret_cast<const float2*>(args.part_ml + 2 * zr);
+      p8 = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(args.part_o) + zr * D + c);
+    }
     if (ml.x == neg_inf()) continue;  // this split saw no key of the row
     const float nm = fmaxf(mx, ml.x);
     // share z holds O_z = acc_z / l_z: its weight is l_z 2^(b_z - base)
@@ -550,8 +574,6 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const FwdArgs args) {
     l = l * fo + fn;
     mx = nm;
   }
-  const int i = (int)(r % a.Sq);
-  const int h = (int)((r / a.Sq) % a.Hq), b = (int)(r / ((int64_t)a.Sq * a.Hq));
   float inv, lse;
   const float sb = args.sinks ? args.sinks[h] * kLog2e : neg_inf();
   if (sb != neg_inf()) {  // the sink joins the row sum at the larger of the two bases
@@ -604,8 +626,9 @@ hipError_t launch_split_d(const FwdArgs& args, hipStream_t stream) {
     hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, 64, false, false, 1, true>), grid, dim3(256), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t threads = (int64_t)args.a.B * args.a.Hq * args.a.Sq * (D / 8);
-  hipLaunchKernelGGL((fwd_merge_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, args);
+  const int rows_per_wg = 256 / (D / 8);
+  hipLaunchKernelGGL((fwd_merge_kernel<D>), dim3((args.a.Sq + rows_per_wg - 1) / rows_per_wg, args.a.Hq, args.a.B),
+                     dim3(256), 0, stream, args);
   return hipGetLastError();
 }
 
