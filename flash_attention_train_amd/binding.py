@@ -421,10 +421,10 @@ def convert_f16(src, *, out=None, dtype=None, stream=None):
 
 def bwd_workspace_bytes(q, k, *, scale=None, causal=False, q_offset=None, mask=None, kv_split=0, q_split=0,
                         key_len=None, q_len=None, window=(-1, -1), q_split_tiles=0, softcap=0.0, k_scale=None,
-                        v_scale=None) -> int:
+                        v_scale=None, dq_launch=0) -> int:
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, key_len=key_len, q_len=q_len, window=window, q_split_tiles=q_split_tiles,
-                    softcap=softcap, k_scale=k_scale, v_scale=v_scale)
+                    softcap=softcap, k_scale=k_scale, v_scale=v_scale, dq_launch=dq_launch)
     return int(lib().fa_train_bwd_workspace_bytes(ctypes.byref(p)))
 
 
@@ -444,7 +444,9 @@ def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_off
         window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0, k_scale=None, v_scale=None,
         dbias=None):
     """Backward: returns (dQ, dK, dV), each in q's dtype, overwritten. ``dbias``: optional fp32
-    tensor of the mask's shape that receives the mask's gradient, added in (zero it first)."""
+    tensor of the mask's shape that receives the mask's gradient, added in (zero it first).
+    ``dq_launch``: 0 automatic, 1 / 2 the dQ walk in the dK/dV launch / its own, 3 dQ from the dS
+    the dK/dV walk stores (a larger workspace)."""
     _check_qkv(q, k, v, k_scale, v_scale)
     _expect("dout", dout, dtype=q.dtype, shape=q.shape)
     _check_rowstats(q, lse=lse, delta=delta)

@@ -102,8 +102,8 @@ fa_status check_params(const fa_attn_params* p) {
   if (p->window_left < -1 || p->window_right < -1) return fail(FA_ERR_SHAPE, "window bounds must be >= -1");
   if (reinterpret_cast<uintptr_t>(p->sinks) % 4) return fail(FA_ERR_ALIGN, "sinks is not 4-byte aligned");
   if (reinterpret_cast<uintptr_t>(p->alibi) % 4) return fail(FA_ERR_ALIGN, "alibi is not 4-byte aligned");
-  if (p->bwd_dq_launch < 0 || p->bwd_dq_launch > 2)
-    return fail(FA_ERR_SHAPE, "bwd_dq_launch must be 0, 1 or 2 (got %d)", p->bwd_dq_launch);
+  if (p->bwd_dq_launch < 0 || p->bwd_dq_launch > 3)
+    return fail(FA_ERR_SHAPE, "bwd_dq_launch must be 0, 1, 2 or 3 (got %d)", p->bwd_dq_launch);
   if (reinterpret_cast<uintptr_t>(p->key_len) % 4 || reinterpret_cast<uintptr_t>(p->q_len) % 4)
     return fail(FA_ERR_ALIGN, "key_len / q_len are not 4-byte aligned");
   if (!(p->softcap >= 0.f) || isinf(p->softcap)) return fail(FA_ERR_SHAPE, "softcap must be >= 0 and finite");
@@ -373,9 +373,20 @@ void choose_splits(const fa_attn_params* p, bool accumulate, int* kv_split, int*
 }
 
 struct WsLayout {
-  size_t dq_off, dk_off, dv_off, total;
-  bool need_dq, need_dkdv;
+  size_t dq_off, dk_off, dv_off, ds_off, total;
+  bool need_dq, need_dkdv, need_ds;
 };
+
+// Does the bf16 backward take dQ from the dS the dK/dV walk stores (instead of the dQ walk
+// recomputing S and dP)? Not for a stored K/V window, the mask's gradient (added by the dQ
+// walk) or the role-split dK/dV walk.
+bool dq_from_ds(const fa_attn_params* p) {
+  if (generic_path(p) || p->kv_format != FA_KV_DTYPE || p->dbias || p->bwd_kv_walk == 2) return false;
+  return p->bwd_dq_launch == 3;
+}
+size_t ds_bytes(const fa_attn_params* p) {
+  return (size_t)p->B * p->Hq * ((p->Sq + 63) / 64) * ((p->Sk + fa::kBwdUnit - 1) / fa::kBwdUnit) * fa::kDsBlock;
+}
 
 // Workspace of the backward: the fp32 partial slices of the chosen split (bf16), or the
 // fp32 dQ accumulator (fp32 inputs).
@@ -395,10 +406,12 @@ WsLayout workspace_layout(const fa_attn_params* p, bool accumulate) {
     w.need_dq = true;
     w.need_dkdv = false;
   }
+  w.need_ds = dq_from_ds(p);
   w.dq_off = 0;
   w.dk_off = w.need_dq ? round256(dq_bytes) : 0;
   w.dv_off = w.dk_off + (w.need_dkdv ? round256(dk_bytes) : 0);
-  w.total = w.dv_off + (w.need_dkdv ? round256(dk_bytes) : 0);
+  w.ds_off = w.dv_off + (w.need_dkdv ? round256(dk_bytes) : 0);
+  w.total = w.ds_off + (w.need_ds ? round256(ds_bytes(p)) : 0);
   return w;
 }
 
@@ -571,7 +584,7 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
     // hand-over 55% of the time and stages a pair's tiles per 64 keys instead of 128, and was
     // 20-60% slower on the DiT and LM workloads
     const int kv_role = p->softcap > 0.f || p->kv_format != FA_KV_DTYPE ? 0 : (p->bwd_kv_walk == 2 ? 1 : 0);
-    fa::plan_bwd_bf16(a.a, kv, q, qt, 0, &plan, kv_role);
+    fa::plan_bwd_bf16(a.a, kv, q, qt, 0, &plan, kv_role, wl.need_ds ? 1 : 0);
     // a large dQ grid runs as its own kernel, two workgroups per compute unit (measured on
     // the causal LM backward: 659 -> 631 us); small grids keep one launch, whose dQ
     // workgroups fill the compute units the dK/dV walks leave idle
@@ -584,12 +597,13 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
     plan.dv_part = wl.need_dkdv ? reinterpret_cast<float*>(ws + wl.dv_off) : nullptr;
     plan.dq = dq->data;
     plan.sdq = strides_of(dq);
+    if (wl.need_ds) plan.ds = ws + wl.ds_off;
     const int64_t nq = (int64_t)p->B * p->Hq * p->Sq * p->D, nk = (int64_t)p->B * p->Hkv * p->Sk * p->D;
     if ((st = hip_status(fa::launch_bwd_bf16(a, plan, stream), "backward"))) return st;
     // the reduce passes: dQ over the rows of the split query tiles (the first ones), dK and dV
     // over every key; one launch when all three go to bf16 outputs (the chunked walk adds dK / dV
     // into its fp32 window accumulators instead)
-    const int rows = std::min(p->Sq, plan.q_tiles_split * fa::kBwdUnit);
+    const int rows = std::min(p->Sq, plan.q_tiles_split * plan.q_bm);
     const fa::ReduceArgs r = {p->B, p->Hq, rows, p->D, p->Sq, plan.dq_part, q, nq, dq->data, strides_of(dq),
                               p->scale, 0};
     const int out_bf16 = accumulate ? 0 : 1, acc = accumulate ? 1 : 0;
@@ -772,12 +786,15 @@ void check_bwd(Checker& c, const fa_attn_params* p, const int32_t* klen_h, const
   choose_splits(p, false, &kv, &q, &qt);
   const int kv_role = p->softcap > 0.f || p->kv_format != FA_KV_DTYPE ? 0 : (p->bwd_kv_walk == 2 ? 1 : 0);
   fa::BwdPlan plan;
-  fa::plan_bwd_bf16(a, kv, q, qt, 0, &plan, kv_role);
   const WsLayout wl = workspace_layout(p, false);
+  fa::plan_bwd_bf16(a, kv, q, qt, 0, &plan, kv_role, wl.need_ds ? 1 : 0);
   const int64_t nq = (int64_t)p->B * p->Hq * p->Sq * p->D, nk = (int64_t)p->B * p->Hkv * p->Sk * p->D;
   if (wl.need_dq && (int64_t)(wl.dk_off - wl.dq_off) < plan.q_split * nq * 4) c.fail("dq slices exceed their space");
   if (wl.need_dkdv && (int64_t)(wl.dv_off - wl.dk_off) < plan.kv_split * nk * 4) c.fail("dk slices exceed their space");
-  if (wl.need_dkdv && (int64_t)(wl.total - wl.dv_off) < plan.kv_split * nk * 4) c.fail("dv slices exceed their space");
+  if (wl.need_dkdv && (int64_t)(wl.ds_off - wl.dv_off) < plan.kv_split * nk * 4) c.fail("dv slices exceed their space");
+  if (wl.need_ds && wl.total - wl.ds_off < ds_bytes(p)) c.fail("stored dS exceeds its space");
+  if (wl.need_ds && (plan.ds_nrt != (p->Sq + 63) / 64 || plan.ds_nku != (p->Sk + fa::kBwdUnit - 1) / fa::kBwdUnit))
+    c.fail("stored dS block grid %d x %d", plan.ds_nrt, plan.ds_nku);
   const int KB = kv_role ? fa::kBwdRoleKeys : fa::kBwdUnit, BM = 64, G = p->Hq / p->Hkv;
   const int nkt = (p->Sk + KB - 1) / KB;
   if (plan.n_kv_units != nkt * p->B * p->Hkv * plan.kv_split) c.fail("dK/dV unit count %d", plan.n_kv_units);
@@ -810,6 +827,11 @@ void check_bwd(Checker& c, const fa_attn_params* p, const int32_t* klen_h, const
       // (later rows arrive as zeros)
       const int v = std::min(BM, p->Sq - q0);
       if (v < 1 || q0 + v - 1 >= p->Sq) return c.fail("dK/dV unit %d stages past Sq", unit);
+      if (wl.need_ds) {  // the pair's stored dS block lies inside the workspace's dS region
+        const int64_t blk = (((int64_t)u.b * p->Hq + h) * plan.ds_nrt + q0 / BM) * plan.ds_nku + u.kt;
+        if (q0 / BM >= plan.ds_nrt || u.kt >= plan.ds_nku || (size_t)(blk + 1) * fa::kDsBlock > ds_bytes(p))
+          return c.fail("dK/dV unit %d stores dS block %lld past its region", unit, (long long)blk);
+      }
     }
     for (int w = 0; w < KB / 32; ++w) {
       const int kbase = n0 + 32 * w, rows = std::max(0, std::min(32, p->Sk - kbase));
@@ -824,7 +846,7 @@ void check_bwd(Checker& c, const fa_attn_params* p, const int32_t* klen_h, const
   for (size_t i = 0; i < kv_seen.size() && c.ok; ++i)
     if (kv_seen[i] != 1) c.fail("dK/dV unit %zu covered %d times", i, kv_seen[i]);
   // dQ units: each 128-row query tile of each head once, or once per split for the split tiles
-  const int QM = fa::kBwdUnit, QN = 64, nqt = (p->Sq + QM - 1) / QM;
+  const int QM = plan.q_bm, QN = 64, nqt = (p->Sq + QM - 1) / QM;
   if (plan.n_q_units != (nqt - plan.q_tiles_split + plan.q_tiles_split * plan.q_split) * p->B * p->Hq)
     c.fail("dQ unit count %d", plan.n_q_units);
   std::vector<int> q_seen((size_t)nqt * p->B * p->Hq * std::max(1, plan.q_split), 0);
@@ -848,8 +870,18 @@ void check_bwd(Checker& c, const fa_attn_params* p, const int32_t* klen_h, const
       ke = hi1 > lo ? (int)std::min<int64_t>((hi1 + QN - 1) / QN, nkt64) : kb;
       if (ke < kb) ke = kb;
     }
-    for (int t = kb + u.split; t < ke; t += u.nsplit)  // (a tile's resource ends at key min(t QN + QN, Sk) - 1)
+    for (int t = kb + u.split; t < ke; t += u.nsplit) {  // (a tile's resource ends at key min(t QN + QN, Sk) - 1)
       if (t * QN >= p->Sk) return c.fail("dQ unit %d walks key tile %d past Sk", unit, t);
+      if (wl.need_ds)  // the half blocks it copies (row tiles past the last copy nothing)
+        for (int w = 0; w < QM / 64; ++w) {
+          const int rt = q0 / 64 + w;
+          if (rt >= plan.ds_nrt) continue;
+          const int64_t end = ((((int64_t)u.b * p->Hq + u.h) * plan.ds_nrt + rt) * plan.ds_nku + t / 2) * fa::kDsBlock +
+                              (t % 2 + 1) * (fa::kDsBlock / 2);
+          if (t / 2 >= plan.ds_nku || (size_t)end > ds_bytes(p))
+            return c.fail("dQ unit %d reads dS past its region (tile %d)", unit, t);
+        }
+    }
     for (int w = 0; w < QM / 32; ++w) {
       const int qw = q0 + 32 * w, rows = std::max(0, std::min(32, p->Sq - qw));
       if (rows == 0) continue;  // a wave whose rows all lie past Sq stores nothing

@@ -56,6 +56,24 @@ __device__ __forceinline__ f32x16 zeros16() {
 
 // (the unit decoding, kv_unit_of and q_unit_of, is shared with the host checker: fa_kernels.h)
 
+// The 64-row query tiles [qt0, qt_end) a dK/dV walk over keys [n0, n0 + KV_BN) visits by the
+// structure (sequence ends, causal diagonal, key and query lengths, window): from the first
+// key's lower row end to the last live key's upper end (both ends move down with the key).
+// The dQ walk over stored dS asks the same question to know which dS blocks were written.
+__device__ __forceinline__ void kv_row_tiles(const AttnShape& a, int klen, int qlen, int n0, int& qt0, int& qt_end) {
+  qt0 = 0;
+  qt_end = 0;
+  if (n0 < klen) {
+    int64_t lo, hi, lo1, hi1;
+    row_range(a, klen, qlen, n0, lo, hi);
+    row_range(a, klen, qlen, min(n0 + KV_BN, klen) - 1, lo1, hi1);
+    const int nqt = (a.Sq + KV_BM - 1) / KV_BM;
+    qt0 = (int)min<int64_t>(lo / KV_BM, nqt);
+    qt_end = hi1 > lo ? (int)min<int64_t>((hi1 + KV_BM - 1) / KV_BM, nqt) : qt0;
+    if (qt_end < qt0) qt_end = qt0;
+  }
+}
+
 // Does any mask block of rows [r0, r0 + nr) x keys [c0, c0 + nc) (in 64-blocks) carry
 // additive values? Units whose blocks are all dead / open / 0-or--inf run a body
 // compiled without the mask-value reads, which keeps their loop free of that code.
@@ -202,7 +220,9 @@ struct LiveWords {
 // cap's derivative 1 - tanh^2. Under additive scores (a dense mask's values or ALiBi, BIAS)
 // the cap is applied to a whole block before they are added, with its derivative folded into
 // dP - Delta; otherwise inside the woven slices.
-template <int D, bool CAUSAL, bool MASK, bool BIAS, bool CAP = false, int KVF = 0>
+// ST: the walk also stores each pair's dS (bf16, as the dK product takes it) into the pair's
+// block of plan.ds, for a dQ pass that multiplies it by K instead of recomputing S and dP.
+template <int D, bool CAUSAL, bool MASK, bool BIAS, bool CAP = false, int KVF = 0, bool ST = false>
 __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
   constexpr int DS = D / 16, DB = D / 32;
   static_assert(8 % DS == 0 && 8 % (2 * DB) == 0, "each woven slice holds whole product pairs");
@@ -264,20 +284,10 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     dv[db] = zeros16();
   }
 
-  // the rows the structure lets see any of the unit's keys (sequence ends, causal diagonal,
-  // key and query lengths, window): from the first key's lower end to the last live key's
-  // upper end (both ends move down with the key)
+  // the rows the structure lets see any of the unit's keys
   const int klen = klen_of(a, b), qlen = qlen_of(a, b);
-  int qt0 = 0, qt_end = 0;
-  if (n0 < klen) {
-    int64_t lo, hi, lo1, hi1;
-    row_range(a, klen, qlen, n0, lo, hi);
-    row_range(a, klen, qlen, min(n0 + KV_BN, klen) - 1, lo1, hi1);
-    const int nqt = (a.Sq + KV_BM - 1) / KV_BM;
-    qt0 = (int)min<int64_t>(lo / KV_BM, nqt);
-    qt_end = hi1 > lo ? (int)min<int64_t>((hi1 + KV_BM - 1) / KV_BM, nqt) : qt0;
-    if (qt_end < qt0) qt_end = qt0;
-  }
+  int qt0, qt_end;
+  kv_row_tiles(a, klen, qlen, n0, qt0, qt_end);
   // the rows every key of the unit sees: a pair tile outside [r_lo, r_hi) needs masking
   // (as 32-bit row numbers: row bounds lie in [0, Sq])
   int r_lo, r_hi;
@@ -434,6 +444,12 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     pdx = *reinterpret_cast<const bf16x8*>(aug_lds + (3 + bb) * KV_BM * 16 + r32 * 16 + 8 * g);
   };
   if (cur.p < npairs) read_a0(0);
+  // (ST) this lane's two 16-byte chunks of a 32-row block in the wave's 4 KB of a dS block:
+  // chunk (block qb, half hh, key k, lane half g) at ((2 qb + hh) 32 + (k ^ 4 hh)) 2 + g.
+  // Stored after the pair's wait, except under a softcap with additive scores, whose walk has
+  // no registers to keep dS until then (stored as soon as formed)
+  constexpr bool ST_LATE = !(CAP && BIAS);
+  const uint32_t ds_off0 = (uint32_t)(r32 * 2 + g) * 16u, ds_off1 = 1024u + (uint32_t)((r32 ^ 4) * 2 + g) * 16u;
   for (int it = 0, buf = 0; cur.p < npairs; ++it) {
     const int nb = buf == 2 ? 0 : buf + 1;
     const Pos nxt = next_live(advance(cur));
@@ -446,6 +462,10 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     }
     int h, q0;
     pair_of(cur, h, q0);
+    char* dsw = nullptr;  // (ST) the wave's 4 KB of this pair's dS block
+    if constexpr (ST)
+      dsw = plan.ds + ((((int64_t)b * a.Hq + h) * plan.ds_nrt + q0 / KV_BM) * plan.ds_nku + kt) * kDsBlock +
+            wave * (kDsBlock / kBwdWaves);
     const int cls = cls_cur;
     const bool bias = MASK && (cls == kTileBias || a.alibi);  // add mask values and / or ALiBi
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits
@@ -633,6 +653,10 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
         pack8(pa0[hh], s0, 8 * hh);
         pack8(ds0[hh], dp0, 8 * hh);
       }
+      if constexpr (ST && !ST_LATE) {
+        *reinterpret_cast<bf16x8*>(dsw + ds_off0) = ds0[0];
+        *reinterpret_cast<bf16x8*>(dsw + ds_off1) = ds0[1];
+      }
     }
     {
       bf16x8 dob[2][DB], qbt[2][DB];
@@ -658,6 +682,10 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
         pack8(pa1[hh], s1, 8 * hh);
         pack8(ds1[hh], dp1, 8 * hh);
       }
+      if constexpr (ST && !ST_LATE) {
+        *reinterpret_cast<bf16x8*>(dsw + 2048 + ds_off0) = ds1[0];
+        *reinterpret_cast<bf16x8*>(dsw + 2048 + ds_off1) = ds1[1];
+      }
     }
     // the next pair's tiles are complete once every wave has waited for its own loads;
     // its first block's operands are then requested before this pair's last products
@@ -666,6 +694,14 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     __syncthreads();
     if (more) read_a0(nb);
     step_c(1, pa1, ds1);
+    if constexpr (ST && ST_LATE) {
+      // (after this pair's wait: the stores complete under the next pair, whose end-of-pair
+      // wait would otherwise also wait for them)
+      *reinterpret_cast<bf16x8*>(dsw + ds_off0) = ds0[0];
+      *reinterpret_cast<bf16x8*>(dsw + ds_off1) = ds0[1];
+      *reinterpret_cast<bf16x8*>(dsw + 2048 + ds_off0) = ds1[0];
+      *reinterpret_cast<bf16x8*>(dsw + 2048 + ds_off1) = ds1[1];
+    }
     buf = nb;
     cur = nxt;
     cls_cur = cls_next;
@@ -1395,10 +1431,211 @@ __device__ __forceinline__ void dq_unit(const BwdArgs& args, const BwdPlan& plan
   store_block<D>(dq, nsplit > 1 ? 1.f : a.scale, stage, lane, sq);
 }
 
+// ---------------------------------------------------------------------------
+// dQ workgroup over stored dS
+// ---------------------------------------------------------------------------
+// dQ = scale dS K from the dS blocks the dK/dV walk stored (dS = P (dP - Delta) is the same
+// quantity the dQ walk recomputes from S and dP, already rounded to bf16 the way both walks
+// feed it to their products). What is left per key tile is one product reading dS once from
+// memory, so the pass streams dS: a workgroup owns 256 query rows (each wave one 64-row tile,
+// the rows of one dS block) and keeps two 64-key tiles in flight through a ring of three
+// stages in LDS, each a K tile (read by all four waves) and, per wave, the half block of
+// its row tile holding the tile's keys (read by that wave only). The dS operand of a 16-key
+// product is two transpose reads of the stored chunks (each 16-lane group reads 128
+// contiguous bytes). A wave uses a block only if the dK/dV walk visited it (the same row
+// range and mask block test): a block it skipped holds no data, and its scores are all
+// hidden, so the wave's products for it are skipped.
+template <int D, bool MASK>
+__device__ __forceinline__ void dqds_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
+  constexpr int DB = D / 32;
+  constexpr int SB = kDsBlock / 2;            // half a dS block: 64 rows x 64 keys
+  constexpr int QM = kDsRows;                 // query rows per workgroup
+  constexpr int KT = Q_BN * D * 2;            // bytes of a staged K tile
+  constexpr int STAGE = KT + kBwdWaves * SB;  // one ring stage
+  constexpr int NS = 3;                       // ring stages: two tiles in flight
+  // VMEM instructions per thread and stage (K tile rows, then the wave's 8 KB of dS): the
+  // wait for a stage lets the next stage's loads stay outstanding
+  constexpr int KLOADS = Q_BN * (D / 8) / NT, SLOADS = SB / 1024;
+  static_assert(QM == 64 * kBwdWaves, "one 64-row dS tile per wave");
+  using TL = Tile<D>;
+
+  const AttnShape& a = args.a;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) from here on
+  const int g = lane >> 5;
+  const QUnit u = q_unit_of(a, plan, unit);
+  const int qt = u.qt, b = u.b, h = u.h, split = u.split, nsplit = u.nsplit;
+  const int hk = h / a.G;
+  const int q0 = qt * QM;
+  const int qw = q0 + KV_BM * wave;  // the wave's 64 rows: dS row tile rt_w
+  const int rt_w = qw / KV_BM;
+  const bf16* K = static_cast<const bf16*>(args.k) + b * args.sk.b + hk * args.sk.h;
+  const char* dsw = plan.ds + (((int64_t)b * a.Hq + h) * plan.ds_nrt + rt_w) * plan.ds_nku * kDsBlock;
+  const uint32_t ds_bytes = rt_w < plan.ds_nrt ? (uint32_t)SB : 0u;  // (no row tile: zeros, never used)
+
+  // (accumulators in arch VGPRs: the products sit under a wave-uniform branch, across which
+  // accumulators in AGPRs would be copied out and back every tile)
+  f32x16 dq[2][DB];
+  #pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+    #pragma unroll
+    for (int db = 0; db < DB; ++db) dq[qb][db] = zeros16();
+
+  // the key tiles the workgroup's rows can see by the structure (as in the dQ walk)
+  const int klen = klen_of(a, b), qlen = qlen_of(a, b);
+  const int nkt = (a.Sk + Q_BN - 1) / Q_BN;
+  int kt_begin = 0, kt_end = 0;
+  if (q0 < qlen) {
+    int64_t lo, hi, lo1, hi1;
+    key_range(a, klen, qlen, q0, lo, hi);
+    key_range(a, klen, qlen, min(q0 + QM, qlen) - 1, lo1, hi1);
+    kt_begin = (int)min<int64_t>(lo / Q_BN, nkt);
+    kt_end = hi1 > lo ? (int)min<int64_t>((hi1 + Q_BN - 1) / Q_BN, nkt) : kt_begin;
+    if (kt_end < kt_begin) kt_end = kt_begin;
+  }
+
+  // stage key tile kt into ring slot `slot`: its K rows (keys past the end arrive as zeros)
+  // and this wave's half of dS block (rt_w, kt / 2)
+  auto stage_tile = [&](int kt, int slot) {
+    char* base = smem + slot * STAGE;
+    const int key0 = kt * Q_BN;
+    TL::template stage_rows<Q_BN, NT>(TL::lds_addr(base), K + (int64_t)key0 * args.sk.s, args.sk.s, a.Sk - key0);
+    const u32x4 rsrc = raw_rsrc(dsw + (int64_t)(kt >> 1) * kDsBlock + (kt & 1) * SB, ds_bytes);
+    const uint32_t dst = TL::lds_addr(base + KT + wave * SB);
+    #pragma unroll
+    for (int i = 0; i < SLOADS; ++i) TL::dma16(rsrc, (uint32_t)(1024 * i + 16 * lane), 0u, dst + 1024u * i);
+  };
+
+  // did the dK/dV walk store block (rt_w, ku)?
+  const int nct = (a.Sk + kMaskTile - 1) / kMaskTile;
+  auto visited = [&](int ku) -> bool {
+    int t0, t1;
+    kv_row_tiles(a, klen, qlen, ku * KV_BN, t0, t1);
+    if (rt_w < t0 || rt_w >= t1) return false;
+    if (MASK && a.tiles) {
+      for (int ct = ku * (KV_BN / kMaskTile); ct < (ku + 1) * (KV_BN / kMaskTile) && ct < nct; ++ct)
+        if (tile_class(a, b, rt_w, ct) != kTileDead) return true;
+      return false;
+    }
+    return true;
+  };
+
+  // mask tile map: skip key tiles dead for every 64-row block of this workgroup
+  const int nrt = (a.Sq + kMaskTile - 1) / kMaskTile;
+  auto live = [&](int j) -> bool {  // candidate j: key tile kt_begin + split + j nsplit
+    const int k = kt_begin + split + j * nsplit;
+    for (int rt = q0 / kMaskTile; rt <= (q0 + QM - 1) / kMaskTile && rt < nrt; ++rt)
+      if (tile_class(a, b, rt, k) != kTileDead) return true;
+    return false;
+  };
+  __shared__ uint64_t live_lds[kBwdWaves];
+  LiveWords lw{live_lds, -NT, {0, 0, 0, 0}};
+  const int nwalk = kt_end - kt_begin;
+  const int ncand = nwalk > split ? (nwalk - split + nsplit - 1) / nsplit : 0;
+  auto next_live = [&](int j) {
+    if (j >= ncand) return ncand;
+    return MASK && a.tiles ? lw.next(j, ncand, tid, live) : j;
+  };
+  auto tile_of = [&](int j) { return j < ncand ? kt_begin + split + j * nsplit : kt_end; };
+
+  // the dS operand: lane L of 16-lane group G reads keys 4 g + L / 4 (+ 8) of a 16-key step,
+  // rows 16 (G & 1) + 4 (L & 3) .. + 3 of a 32-row block; in the stored order that is chunk
+  // (qb, G & 1, key, L & 1), byte 8 ((L >> 1) & 1)
+  const int G16 = lane >> 4, L16 = lane & 15, hs = G16 & 1;
+  const uint32_t a_off =
+      (uint32_t)(((hs * 32 + ((4 * g + (L16 >> 2)) ^ (4 * hs))) * 2 + (L16 & 1)) * 16 + ((L16 >> 1) & 1) * 8);
+  const int tr_row = L16 >> 2, tr_col = 16 * (G16 & 1) + 4 * (L16 & 3);
+  auto read_tr_at = [](const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(__attribute__((address_space(3))) char*)p);
+  };
+
+  int kj = next_live(0);
+  int kt = tile_of(kj);
+  int kjn = next_live(kj + 1);
+  int ktn = tile_of(kjn);
+  if (kt < kt_end) stage_tile(kt, 0);
+  if (ktn < kt_end) {
+    stage_tile(ktn, 1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_enc(KLOADS + SLOADS));  // the first stage
+  } else {
+    wait_vm();
+  }
+  __syncthreads();
+  int ku_c = -1;
+  bool ok = false;
+  for (int slot = 0, slot_n = 1, slot_f = 2; kt < kt_end;) {
+    const int kjf = next_live(kjn + 1);
+    const int ktf = tile_of(kjf);
+    if (ktf < kt_end) stage_tile(ktf, slot_f);  // two tiles ahead (its slot was read last tile)
+    if ((kt >> 1) != ku_c) {
+      ku_c = kt >> 1;
+      ok = visited(ku_c);
+    }
+    if (ok) {
+      const bf16* kb_lds = reinterpret_cast<const bf16*>(smem + slot * STAGE);
+      const char* sa = smem + slot * STAGE + KT + wave * SB + a_off;
+      #pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        #pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          // K operands (transpose reads): keys 32 kb + 16 hh + 4 g + e and + 8
+          const int rbase = 32 * kb + 16 * hh + 4 * g + tr_row;
+          bf16x8 kbt[DB];
+          #pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x4 lo = TL::read_tr(kb_lds, rbase, 32 * db + tr_col);
+            const bf16x4 hi = TL::read_tr(kb_lds, rbase + 8, 32 * db + tr_col);
+            kbt[db] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+          #pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            const char* p = sa + 2048 * qb + 4096 * kb + 512 * hh;
+            const bf16x4 lo = read_tr_at(p), hi = read_tr_at(p + 256);
+            const bf16x8 dsf = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            #pragma unroll
+            for (int db = 0; db < DB; ++db) mma(dq[qb][db], dsf, kbt[db]);
+          }
+        }
+      }
+    }
+    if (ktf < kt_end)
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc(KLOADS + SLOADS));  // the next stage (not the one after)
+    else
+      wait_vm();
+    __syncthreads();
+    kt = ktn;
+    kj = kjn;
+    ktn = ktf;
+    kjn = kjf;
+    const int s0 = slot;
+    slot = slot_n;
+    slot_n = slot_f;
+    slot_f = s0;
+  }
+
+  // split walks store this split's fp32 slice (unscaled), summed by a reduce pass; the ring
+  // stages the results once every wave has left the walk
+  float* stage = reinterpret_cast<float*>(smem) + wave * 32 * D;
+  #pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r0 = qw + 32 * qb;
+    const int rows = max(0, min(32, a.Sq - r0));
+    const RowSink sq =
+        nsplit > 1
+            ? RowSink{reinterpret_cast<char*>(plan.dq_part + (int64_t)split * a.B * a.Hq * a.Sq * D +
+                                              (((int64_t)b * a.Hq + h) * a.Sq + r0) * D),
+                      (int64_t)D * 4, rows, 1}
+            : RowSink{reinterpret_cast<char*>(static_cast<bf16*>(plan.dq) + b * plan.sdq.b + h * plan.sdq.h +
+                                              (int64_t)r0 * plan.sdq.s),
+                      plan.sdq.s * 2, rows, 0};
+    store_block<D>(dq[qb], nsplit > 1 ? 1.f : a.scale, stage, lane, sq);
+  }
+}
+
 // Units whose mask blocks carry additive values run a body compiled with the
 // mask-value reads; all others (dead / open / 0-or--inf blocks) a body without them,
 // which keeps that code and its registers out of the common loop.
-template <int D, bool CAUSAL, bool MASK, bool CAP = false, int KVF = 0, bool MG = false>
+template <int D, bool CAUSAL, bool MASK, bool CAP = false, int KVF = 0, bool MG = false, bool ST = false>
 __global__ __launch_bounds__(NT) void bwd_bf16_kernel(const BwdArgs args, const BwdPlan plan) {
   constexpr int KV_LDS = 3 * 2 * KV_BM * D * 2 + 2 * 3 * KV_BM * 16 * 2;
   constexpr int Q_LDS = 2 * 2 * Q_BN * D * 2;
@@ -1409,10 +1646,10 @@ __global__ __launch_bounds__(NT) void bwd_bf16_kernel(const BwdArgs args, const 
     const KvUnit u = kv_unit_of(a, plan, blk);
     if (MASK && any_bias_block(a, u.b, 0, (a.Sq + kMaskTile - 1) / kMaskTile, u.kt * (KV_BN / kMaskTile),
                                KV_BN / kMaskTile))
-      dkdv_unit<D, CAUSAL, MASK, true, CAP, KVF>(args, plan, blk, smem);
+      dkdv_unit<D, CAUSAL, MASK, true, CAP, KVF, ST>(args, plan, blk, smem);
     else
-      dkdv_unit<D, CAUSAL, MASK, false, CAP, KVF>(args, plan, blk, smem);
-  } else {
+      dkdv_unit<D, CAUSAL, MASK, false, CAP, KVF, ST>(args, plan, blk, smem);
+  } else if constexpr (!ST) {
     const int unit = blk - plan.n_kv_units;
     const QUnit u = q_unit_of(a, plan, unit);
     if (MASK && any_bias_block(a, u.b, u.qt * (Q_BM / kMaskTile), Q_BM / kMaskTile, 0,
@@ -1457,8 +1694,27 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(const BwdArgs args, const
     dq_unit<D, CAUSAL, MASK, false, true, CAP, KVF, MG>(args, plan, unit, smem);
 }
 
+// dQ over the dS blocks the dK/dV-only grid stored before it (one workgroup per compute
+// unit, its loads two tiles ahead)
+template <int D, bool MASK>
+__global__ __launch_bounds__(NT, 1) void bwd_dqds_kernel(const BwdArgs args, const BwdPlan plan) {
+  __shared__ __attribute__((aligned(16))) char smem[3 * (Q_BN * D * 2 + kBwdWaves * kDsBlock / 2)];
+  dqds_unit<D, MASK>(args, plan, blockIdx.x, smem);
+}
+
 template <int D, bool CAUSAL, bool MASK, bool CAP = false, int KVF = 0, bool MG = false>
 hipError_t launch_cm(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream) {
+  if constexpr (KVF == 0 && !MG) {
+    if (plan.ds) {  // the dK/dV walk stores dS, then the dQ pass over it
+      if (plan.n_kv_units > 0)
+        hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, MASK, CAP, 0, false, true>), dim3(plan.n_kv_units), dim3(NT), 0,
+                           stream, args, plan);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess || plan.n_q_units == 0) return e;
+      hipLaunchKernelGGL((bwd_dqds_kernel<D, MASK>), dim3(plan.n_q_units), dim3(NT), 0, stream, args, plan);
+      return hipGetLastError();
+    }
+  }
   if constexpr (!CAP && KVF == 0) {
     if (plan.kv_role) {
       if (plan.n_kv_units > 0)
@@ -1509,12 +1765,17 @@ hipError_t launch_t(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream
 }  // namespace
 
 void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, int q_tiles_split, int dq_separate,
-                   BwdPlan* plan, int kv_role) {
+                   BwdPlan* plan, int kv_role, int dq_ds) {
   plan->dq_separate = dq_separate;
   plan->kv_role = kv_role;
+  plan->ds = nullptr;  // (set by the caller for the dQ pass over stored dS)
+  plan->ds_nrt = (a.Sq + KV_BM - 1) / KV_BM;
+  plan->ds_nku = (a.Sk + KV_BN - 1) / KV_BN;
   const int kvb = kv_role ? kBwdRoleKeys : KV_BN;
   const int nkt = (a.Sk + kvb - 1) / kvb;
-  const int nqt = (a.Sq + Q_BM - 1) / Q_BM;
+  plan->q_bm = dq_ds ? kDsRows : Q_BM;
+  const int nqt = (a.Sq + plan->q_bm - 1) / plan->q_bm;
+  if (dq_ds) q_tiles_split = min((q_tiles_split * Q_BM + kDsRows - 1) / kDsRows, nqt);
   plan->kv_split = kv_split;
   plan->q_split = q_split;
   plan->n_kv_units = nkt * a.B * a.Hkv * kv_split;

@@ -147,6 +147,10 @@ constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kBwdUnit = 32 * kBwdWaves;
 // keys per dK/dV workgroup of the role-split walk (two 32-key groups, two roles each)
 constexpr int kBwdRoleKeys = 64;
+// bytes of one stored dS block: a 64-row query tile times a dK/dV workgroup's keys, bf16
+constexpr int kDsBlock = 64 * kBwdUnit * 2;
+// query rows per workgroup of the dQ pass over stored dS (one 64-row tile per wave)
+constexpr int kDsRows = 64 * kBwdWaves;
 
 struct FwdArgs {
   AttnShape a;
@@ -226,7 +230,8 @@ struct QUnit {
 struct BwdPlan {
   int kv_split;    // workgroups sharing one key tile's dK/dV walk (> 1: fp32 partial slices)
   int q_split;     // workgroups sharing one split query tile's dQ walk (> 1: fp32 partial slices)
-  int q_tiles_split;  // how many 128-row query tiles (the first ones, dispatched last) are split
+  int q_bm;           // query rows per dQ workgroup (kBwdUnit, or kDsRows over stored dS)
+  int q_tiles_split;  // how many q_bm-row query tiles (the first ones, dispatched last) are split
                       // q_split ways; the others walk whole and store dQ directly
   int n_kv_units;  // dK/dV workgroups (launched first)
   int n_q_units;   // dQ workgroups
@@ -237,6 +242,11 @@ struct BwdPlan {
   float* dq_part;  // fp32 [q_split][B, Hq, Sq, D] partial sums when q_split > 1
   void* dq;        // dQ output (dtype) written directly when q_split == 1
   Strides sdq;
+  // dQ from stored dS (or null: the dQ walk recomputes S and dP): the dK/dV walk stores
+  // every pair's dS, block (b, h, 64-row tile rt, key tile kt) of kDsBlock bytes at
+  // ((b Hq + h) ds_nrt + rt) ds_nku + kt, and the dQ workgroups multiply it by K
+  char* ds;
+  int ds_nrt, ds_nku;
 };
 
 // out = scale * sum of nparts fp32 slices [B, H, S_parts, D] (slice s at parts + s * part_stride),
@@ -295,8 +305,10 @@ struct ConvertArgs {
   Strides ss, so;  // element strides of src and out
 };
 hipError_t launch_convert_f16(const ConvertArgs& args, hipStream_t stream);
+// dq_ds: dQ from stored dS (dQ units of kDsRows rows; q_tiles_split counts kBwdUnit-row tiles
+// and is rounded up to whole units)
 void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, int q_tiles_split, int dq_separate,
-                   BwdPlan* plan, int kv_role);
+                   BwdPlan* plan, int kv_role, int dq_ds = 0);
 
 __host__ __device__ __forceinline__ KvUnit kv_unit_of(const AttnShape& a, const BwdPlan& plan, int unit) {
   const int per_tile = a.B * a.Hkv * plan.kv_split;
@@ -306,7 +318,7 @@ __host__ __device__ __forceinline__ KvUnit kv_unit_of(const AttnShape& a, const 
   return {unit / per_tile, rem / a.Hkv, rem % a.Hkv, split};
 }
 __host__ __device__ __forceinline__ QUnit q_unit_of(const AttnShape& a, const BwdPlan& plan, int unit) {
-  const int nqt = (a.Sq + kBwdUnit - 1) / kBwdUnit;
+  const int nqt = (a.Sq + plan.q_bm - 1) / plan.q_bm;
   const int bh = a.B * a.Hq;
   const int n_whole = (nqt - plan.q_tiles_split) * bh;
   if (unit < n_whole) {

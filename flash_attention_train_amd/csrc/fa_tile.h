@@ -258,4 +258,10 @@ struct CvtStage {
 // wait for this wave's outstanding global loads (including loads into LDS)
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0); }
 
+// s_waitcnt operand (gfx9 encoding) that waits until at most n vector memory instructions of
+// this wave are outstanding, and for nothing else. Loads complete in issue order, so waiting
+// down to n leaves exactly the n most recent ones in flight (no stores may be among those
+// counted).
+constexpr int vmcnt_enc(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 }  // namespace fa

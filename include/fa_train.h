@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FA_TRAIN_ABI_VERSION 13
+#define FA_TRAIN_ABI_VERSION 14
 
 typedef enum fa_status {
     FA_OK = 0,
@@ -132,7 +132,14 @@ typedef struct fa_attn_params {
     /* Work decomposition hint of the bf16 backward, like the split hints above (same
      * results up to fp32 summation order): 0 = automatic, 1 = the dQ workgroups share the
      * dK/dV workgroups' launch, 2 = they run as a second kernel after it, two per compute
-     * unit (chosen automatically for grids of at least 512 dQ workgroups). */
+     * unit (chosen automatically for grids of at least 512 dQ workgroups), 3 = dQ from
+     * stored dS: the dK/dV walk also writes every dS = P (dP - Delta) it forms (bf16, as its
+     * dK product takes it) into the workspace, and a second kernel forms dQ = scale dS K
+     * from it instead of recomputing S and dP (fewer matrix products, 2 bytes of traffic
+     * each way per visible score; dK and dV are bitwise those of the other settings, dQ
+     * differs only by the rounding of dS). The workspace then holds 16 KB per (batch entry,
+     * query head, 64-row query tile, 128-key tile). Value 3 is taken as 0 with a stored
+     * K/V window (kv_format), a mask gradient (dbias) or bwd_kv_walk = 2. */
     int32_t bwd_dq_launch;
     /* Attention sinks (both dtypes): one more logit per query head that joins every row's
      * softmax denominator and has no value row (llama.cpp pull request 57 lists sinks
@@ -241,7 +248,8 @@ fa_status fa_train_bwd_preprocess(const fa_attn_params* p, const fa_view* o, con
                                   const fa_view* delta, hipStream_t stream);
 
 /* Bytes of device workspace fa_train_bwd / fa_train_bwd_chunked need for p (fp32
- * accumulators for split work; may be 0). Returns (size_t)-1 if p is invalid. */
+ * accumulators for split work, the stored dS with bwd_dq_launch = 3; may be 0). Returns
+ * (size_t)-1 if p is invalid. */
 size_t fa_train_bwd_workspace_bytes(const fa_attn_params* p);
 
 /* Backward: OVERWRITES dQ, dK, dV (dtype). Reads Q, K, V, dO, the forward's LSE and

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(L, n), n
         assert n in B.SIGNATURES, f"{n} has no ctypes signature in the binding"
-    assert L.fa_train_version() == 13
+    assert L.fa_train_version() == 14
 
 
 BASE = 0x7F0000000000  # fake, 256-byte aligned device addresses
@@ -90,7 +90,7 @@ FWD_ERRORS = [
     ("unknown forward variant", params(fwd_variant=9), {}, 2),
     ("split out of range", params(kv_split=65), {}, 2),
     ("window bound -2", params(window_left=-2), {}, 2),
-    ("unknown dQ launch hint", params(bwd_dq_launch=3), {}, 2),
+    ("unknown dQ launch hint", params(bwd_dq_launch=4), {}, 2),
     ("negative q_split_tiles", params(q_split_tiles=-1), {}, 2),
     ("per-head mask with a block map", params(mask=BASE + 9 * (1 << 24), mask_stride_q=64, mask_stride_h=64 * 64,
                                               mask_tiles=BASE + 10 * (1 << 24)), {}, 7),
@@ -162,6 +162,16 @@ def test_backward_rejects():
     # a split tail keeps full-length dQ slices (only the split tiles' rows are written and summed)
     assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(params(q_split=2, kv_split=1, q_split_tiles=1))) == \
         B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(params(q_split=2, kv_split=1)))
+    # dQ from stored dS: 16 KB per (batch entry, query head, 64-row tile, 128-key tile) after the
+    # slices; ignored (the dQ walk, no dS) for a stored K/V window, a mask gradient or the role walk
+    ds = 1 * 4 * 1 * 1 * 16384
+    assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(params(q_split=1, kv_split=1, bwd_dq_launch=3))) == ds
+    assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(params(q_split=2, kv_split=1, bwd_dq_launch=3))) == \
+        2 * (1 * 4 * 64 * 64 * 4) + ds
+    big = params(B=2, Hq=4, Sq=300, Sk=260, q_split=1, kv_split=1, bwd_dq_launch=3)
+    assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(big)) == 2 * 4 * 5 * 3 * 16384
+    assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(params(q_split=1, kv_split=1, bwd_dq_launch=3,
+                                                                    bwd_kv_walk=2))) == 0
     assert bwd_call(p, ws=0) == 8
     assert bwd_call(p, ws_bytes=100) == 8
     assert bwd_call(p, ws=BASE + 12 * (1 << 24) + 16) == 5

@@ -61,7 +61,8 @@ SHAPES = {
     "d64": dict(B=2, Hq=4, Hkv=4, Sq=200, Sk=129, D=64),
 }
 SPLITS = [dict(), dict(kv_split=2, q_split=2, q_split_tiles=6), dict(kv_split=3, q_split=5),
-          dict(kv_split=1, q_split=4, q_split_tiles=1), dict(fwd_split=7), dict(bwd_kv_walk=2, kv_split=2)]
+          dict(kv_split=1, q_split=4, q_split_tiles=1), dict(fwd_split=7), dict(bwd_kv_walk=2, kv_split=2),
+          dict(bwd_dq_launch=3), dict(bwd_dq_launch=3, kv_split=2, q_split=3, q_split_tiles=3)]
 
 
 @pytest.mark.parametrize("split", range(len(SPLITS)))
@@ -71,19 +72,22 @@ def test_launch_index_space(name, split):
     assert st == 0, rep
 
 
+@pytest.mark.parametrize("dq_launch", [0, 3])
 @pytest.mark.parametrize("window", [(-1, -1), (256, 256), (0, 0), (100, -1)])
-def test_structured_lengths_and_windows(window):
-    p = params(B=2, Hq=16, Hkv=8, Sq=1542, Sk=1542, window_left=window[0], window_right=window[1])
+def test_structured_lengths_and_windows(window, dq_launch):
+    p = params(B=2, Hq=16, Hkv=8, Sq=1542, Sk=1542, window_left=window[0], window_right=window[1],
+               bwd_dq_launch=dq_launch)
     for kl, ql in (([1388, 1388], None), ([1542, 1101], [1542, 700]), ([0, 1], [5, 0])):
         st, rep = check(p, key_len=kl, q_len=ql)
         assert st == 0, (kl, ql, rep)
 
 
-def test_long_window_chunks():
+@pytest.mark.parametrize("dq_launch", [0, 3])
+def test_long_window_chunks(dq_launch):
     W, C = 32768, 512
     for c in range(W // C):
         p0 = c * C
-        st, rep = check(params(B=1, Hq=16, Hkv=4, Sq=C, Sk=p0 + C, causal=1, q_offset=p0))
+        st, rep = check(params(B=1, Hq=16, Hkv=4, Sq=C, Sk=p0 + C, causal=1, q_offset=p0, bwd_dq_launch=dq_launch))
         assert st == 0, (c, rep)
 
 
