@@ -53,6 +53,9 @@ def parse():
                          "(q-way split of the first TILES 128-row query tiles only, e.g. 2x2x6)")
     ap.add_argument("--kv-walk", type=int, default=0,
                     help="bf16 backward dK/dV walk: 0 the library's choice, 1 one wave per 32 keys, 2 split by role")
+    ap.add_argument("--dq-launch", type=int, default=-1,
+                    help="bf16 backward dQ: -1 the workload table's setting, 0 the library's choice, 1 / 2 the dQ "
+                         "walk in the dK/dV launch / its own, 3 dQ from stored dS")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference kernel that "
                          "scales the HBM byte counters) and exit")
@@ -62,12 +65,13 @@ def parse():
 class Workload:
     """Device buffers and the three calls of one step for a seeded case."""
 
-    def __init__(self, key: str, splits: str = "table", kv_walk: int = 0):
+    def __init__(self, key: str, splits: str = "table", kv_walk: int = 0, dq_launch: int = -1):
         import torch
 
         from flash_attention_train_amd import accounting, binding, configs
         self.key = key
         self.kv_walk = kv_walk
+        self.dq_launch = configs.WORKLOADS[key].bwd_dq_launch if dq_launch < 0 else dq_launch
         self.case = c = configs.make(key)
         self.pairs = accounting.case_pairs(c)
         self.fwd_flops = accounting.fwd_flops(self.pairs, c.D)
@@ -134,7 +138,8 @@ class Workload:
                 causal=c.causal, q_offset=c.q_offset, mask_tiles=self.tiles, **self.sk)
         nws = binding.bwd_workspace_bytes(self.q, self.k, scale=c.scale, causal=c.causal, q_offset=c.q_offset,
                                           mask=self.mask, kv_split=self.kv_split, q_split=self.q_split,
-                                          q_split_tiles=self.q_split_tiles, softcap=self.softcap, **self.sk)
+                                          q_split_tiles=self.q_split_tiles, softcap=self.softcap,
+                                          dq_launch=self.dq_launch, **self.sk)
         self.ws_bytes = nws
         self.ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
 
@@ -158,7 +163,8 @@ class Workload:
         self.B.bwd(self.q, self.k, self.v, self.do, self.lse, self.delta, mask=self.mask, scale=c.scale,
                    causal=c.causal, q_offset=c.q_offset, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws,
                    kv_split=self.kv_split, q_split=self.q_split, q_split_tiles=self.q_split_tiles,
-                   mask_tiles=self.tiles, alibi=self.alibi, softcap=self.softcap, kv_walk=self.kv_walk, **self.sk)
+                   mask_tiles=self.tiles, alibi=self.alibi, softcap=self.softcap, kv_walk=self.kv_walk,
+                   dq_launch=self.dq_launch, **self.sk)
         if self.sinks is not None:  # the sinks' gradient, added into their accumulator
             self.B.bwd_sinks(self.lse, self.delta, self.sinks, dsink=self.dsink)
 
@@ -253,6 +259,7 @@ def time_workload(w: Workload, steps: int, warmup: int, graph: bool = True) -> d
         "fwd_split": w.fwd_split,
         "bwd_splits": [w.kv_split, w.q_split, w.q_split_tiles],
         "bwd_splits_from": w.splits_from,
+        "bwd_dq_launch": w.dq_launch,
         "gflop_per_step": total_flops / 1e9,
     }
 
@@ -438,7 +445,7 @@ def main():
         return
 
     log(f"[bench] device {torch.cuda.get_device_name(0)}; workload {args.workload}")
-    w = Workload(args.workload, args.splits, args.kv_walk)
+    w = Workload(args.workload, args.splits, args.kv_walk, args.dq_launch)
     r = time_workload(w, args.steps, args.warmup, graph=not args.eager)
     log(f"[bench] {args.workload}: {r['ms_per_step']:.3f} ms/step, {r['tflops']:.1f} TFLOP/s")
 
@@ -449,7 +456,7 @@ def main():
             log(f"[bench] {key}: {extra[key]['ms_per_walk']:.2f} ms/walk, {extra[key]['tflops']:.1f} TFLOP/s")
             torch.cuda.empty_cache()
             continue
-        we = Workload(key, args.splits if "x" not in args.splits else "table", args.kv_walk)
+        we = Workload(key, args.splits if "x" not in args.splits else "table", args.kv_walk, args.dq_launch)
         re_ = time_workload(we, max(5, args.steps // 2), args.warmup, graph=not args.eager)
         re_["pct_of_peak"] = 100.0 * re_["tflops"] / accounting.MI355X_BF16_DENSE_TFLOPS
         # near the ridge (few keys per row): the step against the HBM roofline as well

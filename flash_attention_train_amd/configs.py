@@ -27,6 +27,9 @@ class Workload:
     # the number of split query tiles (timed interleaved, best of three rounds); None: the
     # library's cost model
     bwd_splits: tuple | None = None
+    # the bf16 backward's dQ formation (bwd_dq_launch): 0 the library's choice, 3 dQ from the dS
+    # the dK/dV walk stores, where that measured faster on MI355X
+    bwd_dq_launch: int = 0
 
 
 WORKLOADS = {
@@ -34,7 +37,7 @@ WORKLOADS = {
     "dit_sa": Workload("dit_sa", "DiT self-attention, B=1 Hq=16 Hkv=8 S=1542 D=128 bf16, pad mask", 2, (2, 2, 6)),
     "dit_ca": Workload("dit_ca", "DiT cross-attention, B=2 H=16 Sq=1542 Sk=512 D=128 bf16, key-pad mask", 3,
                        (2, 1, 0)),
-    "lm_causal": Workload("lm_causal", "LM causal GQA, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 4, (2, 1, 0)),
+    "lm_causal": Workload("lm_causal", "LM causal GQA, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 4, (2, 1, 0), 3),
     "long_window": Workload("long_window",
                             "long-window chunked walk, W=32768, 64 chunks of 512, Hq=16 Hkv=4 D=128 bf16", 5),
     # the DiT self-attention masks given by their structure instead of a dense mask:
@@ -46,9 +49,9 @@ WORKLOADS = {
     # the LM layer with one attention-sink logit per query head (N(0, 1)); its step adds the
     # sinks' gradient pass
     "lm_sinks": Workload("lm_sinks", "LM causal GQA with attention sinks, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 8,
-                         (2, 1, 0)),
+                         (2, 1, 0), 3),
     # the LM layer with ALiBi (slopes 2^(-8 (h + 1) / Hq)) in place of positional rotations
-    "lm_alibi": Workload("lm_alibi", "LM causal GQA with ALiBi, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 10, (2, 1, 0)),
+    "lm_alibi": Workload("lm_alibi", "LM causal GQA with ALiBi, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 10, (2, 1, 0), 3),
     # the long-window walk over a q8_0-stored K/V window (the pages train such a cache in
     # place): the same queries and K/V values, quantised to q8_0 blocks
     "long_window_q8": Workload("long_window_q8", "long-window chunked walk over a q8_0 K/V window, W=32768, "
@@ -57,7 +60,7 @@ WORKLOADS = {
     # the LM layer with a logit softcap of 50 (the pages give no value; the cost does not depend
     # on it): the bf16 MFMA forward and backward with their cap variants
     "lm_softcap": Workload("lm_softcap", "LM causal GQA with logit softcap 50, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16",
-                           12),
+                           12, None, 3),
     "long_window_f16": Workload("long_window_f16", "long-window chunked walk over an f16 K/V window, W=32768, "
                                 "64 chunks of 512, Hq=16 Hkv=4 D=128", 11),
 }
