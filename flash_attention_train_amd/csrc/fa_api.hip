@@ -378,11 +378,17 @@ struct WsLayout {
 };
 
 // Does the bf16 backward take dQ from the dS the dK/dV walk stores (instead of the dQ walk
-// recomputing S and dP)? Not for a stored K/V window, the mask's gradient (added by the dQ
-// walk) or the role-split dK/dV walk.
-bool dq_from_ds(const fa_attn_params* p) {
+// recomputing S and dP)? When asked (bwd_dq_launch 3), or automatically (0) for a dQ grid of
+// at least 512 128-row workgroups (measured on MI355X over graph replays: the causal LM layer,
+// 1024 workgroups, gains 3% plain, 4-6% with ALiBi or a softcap; the DiT workloads, 208 to 416,
+// gain nothing, their dQ walk filling the compute units the dK/dV walk leaves idle), except
+// for callers that cannot allocate (the static scratch is too small to hold dS). Never for a
+// stored K/V window, the mask's gradient (added by the dQ walk) or the role-split dK/dV walk.
+bool dq_from_ds(const fa_attn_params* p, bool noalloc = false) {
   if (generic_path(p) || p->kv_format != FA_KV_DTYPE || p->dbias || p->bwd_kv_walk == 2) return false;
-  return p->bwd_dq_launch == 3;
+  if (p->bwd_dq_launch == 3) return true;
+  if (p->bwd_dq_launch != 0 || noalloc) return false;
+  return (int64_t)((p->Sq + fa::kBwdUnit - 1) / fa::kBwdUnit) * p->B * p->Hq >= 512;
 }
 size_t ds_bytes(const fa_attn_params* p) {
   return (size_t)p->B * p->Hq * ((p->Sq + 63) / 64) * ((p->Sk + fa::kBwdUnit - 1) / fa::kBwdUnit) * fa::kDsBlock;
@@ -390,7 +396,7 @@ size_t ds_bytes(const fa_attn_params* p) {
 
 // Workspace of the backward: the fp32 partial slices of the chosen split (bf16), or the
 // fp32 dQ accumulator (fp32 inputs).
-WsLayout workspace_layout(const fa_attn_params* p, bool accumulate) {
+WsLayout workspace_layout(const fa_attn_params* p, bool accumulate, bool noalloc = false) {
   WsLayout w;
   const size_t nq = (size_t)p->B * p->Hq * p->Sq * p->D * sizeof(float);
   const size_t nk = (size_t)p->B * p->Hkv * p->Sk * p->D * sizeof(float);
@@ -406,7 +412,7 @@ WsLayout workspace_layout(const fa_attn_params* p, bool accumulate) {
     w.need_dq = true;
     w.need_dkdv = false;
   }
-  w.need_ds = dq_from_ds(p);
+  w.need_ds = dq_from_ds(p, noalloc);
   w.dq_off = 0;
   w.dk_off = w.need_dq ? round256(dq_bytes) : 0;
   w.dv_off = w.dk_off + (w.need_dkdv ? round256(dk_bytes) : 0);
@@ -492,7 +498,7 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
   const int gelt = accumulate ? 4 : elt;
   if ((s = check_view(dk, accumulate ? "dk_acc" : "dk", p->B, p->Hkv, p->Sk, p->D, gelt, true, true, &edk))) return s;
   if ((s = check_view(dv, accumulate ? "dv_acc" : "dv", p->B, p->Hkv, p->Sk, p->D, gelt, true, true, &edv))) return s;
-  const WsLayout wl = workspace_layout(p, accumulate);
+  const WsLayout wl = workspace_layout(p, accumulate, use_scratch);
   const size_t need = wl.total;
   if (use_scratch) {
     if (need > (size_t)FA_TRAIN_NOALLOC_SCRATCH_BYTES)

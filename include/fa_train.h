@@ -130,9 +130,11 @@ typedef struct fa_attn_params {
                                 -1: no bound */
     int32_t window_right;    /* >= 0: keys at most this far after it; -1: no bound */
     /* Work decomposition hint of the bf16 backward, like the split hints above (same
-     * results up to fp32 summation order): 0 = automatic, 1 = the dQ workgroups share the
-     * dK/dV workgroups' launch, 2 = they run as a second kernel after it, two per compute
-     * unit (chosen automatically for grids of at least 512 dQ workgroups), 3 = dQ from
+     * results up to fp32 summation order): 0 = automatic (3 when the dQ grid has at least
+     * 512 128-row tiles, except in fa_train_bwd_noalloc; otherwise 1 or 2), 1 = the dQ
+     * workgroups share the dK/dV workgroups' launch, 2 = they run as a second kernel after
+     * it, two per compute unit (chosen automatically for grids of at least 512 dQ
+     * workgroups when dS is not stored), 3 = dQ from
      * stored dS: the dK/dV walk also writes every dS = P (dP - Delta) it forms (bf16, as its
      * dK product takes it) into the workspace, and a second kernel forms dQ = scale dS K
      * from it instead of recomputing S and dP (fewer matrix products, 2 bytes of traffic
