@@ -361,9 +361,9 @@ def source_digest(paths=KERNEL_SOURCES) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, splits):
+def measured_traffic(workload: str, splits, dq_launch: int = 0):
     """HBM bytes per backward call from the committed counter summary, or None when
-    there is none for this workload and split, or the kernel source changed since."""
+    there is none for this workload, split and dQ formation, or the kernel source changed since."""
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic_bwd.json")
     try:
         with open(path) as f:
@@ -371,7 +371,8 @@ def measured_traffic(workload: str, splits):
     except (OSError, ValueError):
         return None
     entry = rec.get("workloads", {}).get(workload)
-    if not entry or rec.get("source_sha256") != source_digest() or entry.get("bwd_splits") != list(splits):
+    if not entry or rec.get("source_sha256") != source_digest() or entry.get("bwd_splits") != list(splits) or \
+            entry.get("bwd_dq_launch", 0) != dq_launch:
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -490,10 +491,10 @@ def main():
                    "seq_len": w.case.Sq, "unmasked_pairs": w.pairs, "gflop_per_step": round(r["gflop_per_step"], 3)},
         "pct_of_peak": round(100.0 * r["tflops"] / peak, 2),
         "roofline": {"kernel": "bwd_bf16_kernel (fa_train_bwd)" if single else
-                     "fa_train_bwd (bwd_bf16_kernel + reduce_parts_kernel)", "bound": "mfma",
+                     "fa_train_bwd (its dK/dV walk, dQ walk or pass, and reduce passes)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(args.workload, [w.kv_split, w.q_split, w.q_split_tiles]),
+                     "traffic": measured_traffic(args.workload, [w.kv_split, w.q_split, w.q_split_tiles], w.dq_launch),
                      "flop_per_launch": w.bwd_flops, "launch_ms": round(r["bwd_ms_mean"], 5)},
         "breakdown": {k: round(v, 4) if isinstance(v, float) else v for k, v in r.items()},
         "extra": extra,
