@@ -248,10 +248,12 @@ def test_softcap_params_rejected():
     masked = dict(softcap=30.0, mask=BASE + 11 * (1 << 24), mask_stride_q=64)
     slopes = dict(softcap=30.0, alibi=BASE + 11 * (1 << 24))
     for kw in (masked, slopes):
-        assert L.fa_train_bwd_workspace_bytes(ctypes.byref(params(dtype=B.FA_BF16, **kw))) == 0
+        assert L.fa_train_bwd_workspace_bytes(ctypes.byref(params(dtype=B.FA_BF16, kv_split=1, q_split=1, **kw))) == 0
         assert L.fa_train_bwd_workspace_bytes(ctypes.byref(params(dtype=B.FA_F32, **kw))) == 1 * 4 * 64 * 64 * 4
-    assert L.fa_train_bwd_workspace_bytes(ctypes.byref(params(softcap=30.0))) == \
-        L.fa_train_bwd_workspace_bytes(ctypes.byref(params())) == 0
+    assert L.fa_train_bwd_workspace_bytes(ctypes.byref(params(softcap=30.0, kv_split=1, q_split=1))) == \
+        L.fa_train_bwd_workspace_bytes(ctypes.byref(params(kv_split=1, q_split=1))) == 0
+    # (the automatic split of this small non-causal grid: dK/dV walks two ways, fp32 dK and dV slices)
+    assert L.fa_train_bwd_workspace_bytes(ctypes.byref(params())) == 2 * 2 * (1 * 2 * 64 * 64 * 4)
     long_keys = dict(softcap=30.0, Sk=4096)
     assert L.fa_train_fwd_workspace_bytes(ctypes.byref(params(**long_keys))) == \
         L.fa_train_fwd_workspace_bytes(ctypes.byref(params(Sk=4096))) > 0
@@ -301,7 +303,7 @@ def test_stored_kv_formats_rejected_where_unsupported():
         a.update(kw)
         return B.FaView(a["data"], a["stride_b"], a["stride_h"], a["stride_s"])
 
-    q8 = dict(kv_format=2, k_scale=scales(10), v_scale=scales(11))
+    q8 = dict(kv_format=2, k_scale=scales(10), v_scale=scales(11), kv_split=1, q_split=1)  # (unsplit: no workspace)
     assert fwd_call(params(kv_format=3)) == 3
     assert fwd_call(params(dtype=B.FA_F32, kv_format=1)) == 7
     assert fwd_call(params(kv_format=1, mask=BASE + 9 * (1 << 24), mask_stride_q=64)) == 7
@@ -333,7 +335,7 @@ def test_mask_gradient_params_rejected():
            (dict(**m, dbias=BASE + 12 * (1 << 24) + 2, dbias_stride_q=64), 5),  # misaligned
            (dict(**m, dbias=BASE + 11 * (1 << 24), dbias_stride_q=64), 6)]      # the mask itself
     for kw, code in bad:
-        p = params(**kw)
+        p = params(kv_split=1, q_split=1, **kw)  # (unsplit: no workspace)
         got = L.fa_train_bwd(ctypes.byref(p), view(0), view(1, H=2), view(2, H=2), view(3), lse, dlt, view(8),
                              view(9, H=2), view(10, H=2), None, 0, None)
         assert got == code, (kw, got)
