@@ -446,7 +446,8 @@ def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_off
     """Backward: returns (dQ, dK, dV), each in q's dtype, overwritten. ``dbias``: optional fp32
     tensor of the mask's shape that receives the mask's gradient, added in (zero it first).
     ``dq_launch``: 0 automatic, 1 / 2 the dQ walk in the dK/dV launch / its own, 3 dQ from the dS
-    the dK/dV walk stores (a larger workspace)."""
+    the dK/dV walk stores (a larger workspace), 4 the dQ walk's own kernel on a second stream
+    beside the dK/dV kernel."""
     _check_qkv(q, k, v, k_scale, v_scale)
     _expect("dout", dout, dtype=q.dtype, shape=q.shape)
     _check_rowstats(q, lse=lse, delta=delta)

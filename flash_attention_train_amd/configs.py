@@ -28,7 +28,8 @@ class Workload:
     # library's cost model
     bwd_splits: tuple | None = None
     # the bf16 backward's dQ formation (bwd_dq_launch): 0 the library's choice, 3 dQ from the dS
-    # the dK/dV walk stores, where that measured faster on MI355X
+    # the dK/dV walk stores, 4 the dQ walk's own kernel on a second stream beside the dK/dV
+    # kernel, where that measured faster on MI355X
     bwd_dq_launch: int = 0
 
 
@@ -36,7 +37,7 @@ WORKLOADS = {
     "tiny": Workload("tiny", "tiny parity case, fp32, B=1 H=2 S=64 D=64", 1),
     "dit_sa": Workload("dit_sa", "DiT self-attention, B=1 Hq=16 Hkv=8 S=1542 D=128 bf16, pad mask", 2, (2, 2, 6)),
     "dit_ca": Workload("dit_ca", "DiT cross-attention, B=2 H=16 Sq=1542 Sk=512 D=128 bf16, key-pad mask", 3,
-                       (2, 1, 0)),
+                       (2, 1, 0), 4),
     "lm_causal": Workload("lm_causal", "LM causal GQA, B=1 Hq=32 Hkv=8 S=4096 D=128 bf16", 4, (2, 1, 0), 3),
     "long_window": Workload("long_window",
                             "long-window chunked walk, W=32768, 64 chunks of 512, Hq=16 Hkv=4 D=128 bf16", 5),

@@ -102,8 +102,8 @@ fa_status check_params(const fa_attn_params* p) {
   if (p->window_left < -1 || p->window_right < -1) return fail(FA_ERR_SHAPE, "window bounds must be >= -1");
   if (reinterpret_cast<uintptr_t>(p->sinks) % 4) return fail(FA_ERR_ALIGN, "sinks is not 4-byte aligned");
   if (reinterpret_cast<uintptr_t>(p->alibi) % 4) return fail(FA_ERR_ALIGN, "alibi is not 4-byte aligned");
-  if (p->bwd_dq_launch < 0 || p->bwd_dq_launch > 3)
-    return fail(FA_ERR_SHAPE, "bwd_dq_launch must be 0, 1, 2 or 3 (got %d)", p->bwd_dq_launch);
+  if (p->bwd_dq_launch < 0 || p->bwd_dq_launch > 4)
+    return fail(FA_ERR_SHAPE, "bwd_dq_launch must be 0 to 4 (got %d)", p->bwd_dq_launch);
   if (reinterpret_cast<uintptr_t>(p->key_len) % 4 || reinterpret_cast<uintptr_t>(p->q_len) % 4)
     return fail(FA_ERR_ALIGN, "key_len / q_len are not 4-byte aligned");
   if (!(p->softcap >= 0.f) || isinf(p->softcap)) return fail(FA_ERR_SHAPE, "softcap must be >= 0 and finite");
@@ -474,6 +474,35 @@ fa_status scratch_of_current_device(void** out) {
   return FA_OK;
 }
 
+// A second stream per device for the dQ kernel that runs beside the dK/dV kernel, with the two
+// events that fork it from the caller's stream and join it back. Created on first use (default
+// priority); the mutex makes each call's record / wait / launch sequence atomic, so calls from
+// several host threads cannot join on each other's events.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+SideStream g_side[kMaxDevices];
+std::mutex g_side_init_mu;
+
+fa_status side_of_current_device(SideStream** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_HIP, "device %d beyond the stream table", dev);
+  std::lock_guard<std::mutex> lock(g_side_init_mu);
+  SideStream& ss = g_side[dev];
+  if (!ss.s) {
+    if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess)
+      return fail(FA_ERR_HIP, "creating the dQ stream on device %d: %s", dev, hipGetErrorString(e));
+  }
+  *out = &ss;
+  return FA_OK;
+}
+
 #ifdef FA_CHECK
 struct Checker {
   char* msg;
@@ -613,7 +642,11 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
     // a large dQ grid runs as its own kernel, two workgroups per compute unit (measured on
     // the causal LM backward: 659 -> 631 us); small grids keep one launch, whose dQ
     // workgroups fill the compute units the dK/dV walks leave idle
-    plan.dq_separate = p->bwd_dq_launch ? p->bwd_dq_launch == 2 : plan.n_q_units >= 512;
+    plan.dq_separate = p->bwd_dq_launch ? p->bwd_dq_launch >= 2 : plan.n_q_units >= 512;
+    // the separate dQ kernel on a second stream, beside the dK/dV kernel (not for callers that
+    // cannot allocate, and not over stored dS, which the dQ pass reads after the walk)
+    const bool beside = !use_scratch && p->bwd_dq_launch == 4 && !wl.need_ds && plan.n_kv_units > 0 &&
+                        plan.n_q_units > 0;
     // split walks write every element of their fp32 slices (zeros included), so the
     // slices need no clearing; the reduce passes sum them into the outputs
     a.dq_acc = nullptr;
@@ -624,7 +657,21 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
     plan.sdq = strides_of(dq);
     if (wl.need_ds) plan.ds = ws + wl.ds_off;
     const int64_t nq = (int64_t)p->B * p->Hq * p->Sq * p->D, nk = (int64_t)p->B * p->Hkv * p->Sk * p->D;
-    if ((st = hip_status(fa::launch_bwd_bf16(a, plan, stream), "backward"))) return st;
+    if (beside) {
+      SideStream* ss = nullptr;
+      if ((st = side_of_current_device(&ss))) return st;
+      std::lock_guard<std::mutex> lock(ss->mu);
+      if ((st = hip_status(hipEventRecord(ss->fork, stream), "dQ stream fork")) ||
+          (st = hip_status(hipStreamWaitEvent(ss->s, ss->fork, 0), "dQ stream fork")))
+        return st;
+      plan.dq_stream = ss->s;
+      if ((st = hip_status(fa::launch_bwd_bf16(a, plan, stream), "backward"))) return st;
+      if ((st = hip_status(hipEventRecord(ss->join, ss->s), "dQ stream join")) ||
+          (st = hip_status(hipStreamWaitEvent(stream, ss->join, 0), "dQ stream join")))
+        return st;
+    } else if ((st = hip_status(fa::launch_bwd_bf16(a, plan, stream), "backward"))) {
+      return st;
+    }
     // the reduce passes: dQ over the rows of the split query tiles (the first ones), dK and dV
     // over every key; one launch when all three go to bf16 outputs (the chunked walk adds dK / dV
     // into its fp32 window accumulators instead)

@@ -1704,6 +1704,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_dqds_kernel(const BwdArgs args, con
 
 template <int D, bool CAUSAL, bool MASK, bool CAP = false, int KVF = 0, bool MG = false>
 hipError_t launch_cm(const BwdArgs& args, const BwdPlan& plan, hipStream_t stream) {
+  // (a separate dQ kernel may go to a second stream, joined by the caller)
+  hipStream_t dq_stream = plan.dq_stream ? plan.dq_stream : stream;
   if constexpr (KVF == 0 && !MG) {
     if (plan.ds) {  // the dK/dV walk stores dS, then the dQ pass over it
       if (plan.n_kv_units > 0)
@@ -1721,7 +1723,7 @@ hipError_t launch_cm(const BwdArgs& args, const BwdPlan& plan, hipStream_t strea
         hipLaunchKernelGGL((bwd_role_kernel<D, CAUSAL, MASK>), dim3(plan.n_kv_units), dim3(NT), 0, stream, args, plan);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess || plan.n_q_units == 0) return e;
-      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, MASK, CAP, KVF, MG>), dim3(plan.n_q_units), dim3(NT), 0, stream, args,
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, MASK, CAP, KVF, MG>), dim3(plan.n_q_units), dim3(NT), 0, dq_stream, args,
                          plan);
       return hipGetLastError();
     }
@@ -1736,7 +1738,7 @@ hipError_t launch_cm(const BwdArgs& args, const BwdPlan& plan, hipStream_t strea
                        plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.n_q_units == 0) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, MASK, CAP, KVF, MG>), dim3(plan.n_q_units), dim3(NT), 0, stream, args, plan);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, MASK, CAP, KVF, MG>), dim3(plan.n_q_units), dim3(NT), 0, dq_stream, args, plan);
   return hipGetLastError();
 }
 
@@ -1769,6 +1771,7 @@ void plan_bwd_bf16(const AttnShape& a, int kv_split, int q_split, int q_tiles_sp
   plan->dq_separate = dq_separate;
   plan->kv_role = kv_role;
   plan->ds = nullptr;  // (set by the caller for the dQ pass over stored dS)
+  plan->dq_stream = nullptr;  // (set by the caller to run the dQ kernel beside the dK/dV kernel)
   plan->ds_nrt = (a.Sq + KV_BM - 1) / KV_BM;
   plan->ds_nku = (a.Sk + KV_BN - 1) / KV_BN;
   const int kvb = kv_role ? kBwdRoleKeys : KV_BN;

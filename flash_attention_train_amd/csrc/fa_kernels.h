@@ -247,6 +247,8 @@ struct BwdPlan {
   // ((b Hq + h) ds_nrt + rt) ds_nku + kt, and the dQ workgroups multiply it by K
   char* ds;
   int ds_nrt, ds_nku;
+  // (host side) the stream of the separate dQ kernel, or null for the launch stream
+  hipStream_t dq_stream;
 };
 
 // out = scale * sum of nparts fp32 slices [B, H, S_parts, D] (slice s at parts + s * part_stride),

@@ -141,7 +141,12 @@ typedef struct fa_attn_params {
      * each way per visible score; dK and dV are bitwise those of the other settings, dQ
      * differs only by the rounding of dS). The workspace then holds 16 KB per (batch entry,
      * query head, 64-row query tile, 128-key tile). Value 3 is taken as 0 with a stored
-     * K/V window (kv_format), a mask gradient (dbias) or bwd_kv_walk = 2. */
+     * K/V window (kv_format), a mask gradient (dbias) or bwd_kv_walk = 2. 4 = as 2, with the
+     * dQ kernel on a second stream of the library's (one per device, default priority),
+     * forked from and joined back to the caller's stream by events, so that it runs beside
+     * the dK/dV kernel on the compute units that one leaves free (the call stays ordered on the
+     * caller's stream, and HIP graph capture records the fork and join); in
+     * fa_train_bwd_noalloc it is taken as 2. */
     int32_t bwd_dq_launch;
     /* Attention sinks (both dtypes): one more logit per query head that joins every row's
      * softmax denominator and has no value row (llama.cpp pull request 57 lists sinks

@@ -90,7 +90,7 @@ FWD_ERRORS = [
     ("unknown forward variant", params(fwd_variant=9), {}, 2),
     ("split out of range", params(kv_split=65), {}, 2),
     ("window bound -2", params(window_left=-2), {}, 2),
-    ("unknown dQ launch hint", params(bwd_dq_launch=4), {}, 2),
+    ("unknown dQ launch hint", params(bwd_dq_launch=5), {}, 2),
     ("negative q_split_tiles", params(q_split_tiles=-1), {}, 2),
     ("per-head mask with a block map", params(mask=BASE + 9 * (1 << 24), mask_stride_q=64, mask_stride_h=64 * 64,
                                               mask_tiles=BASE + 10 * (1 << 24)), {}, 7),

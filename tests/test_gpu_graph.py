@@ -3,7 +3,8 @@ and replayed: every replay, with eager work and synchronizations between replays
 reproduce the eager step's outputs bit for bit (split walks sum fixed fp32 slices in a
 fixed order, so a fixed decomposition is reproducible), and the eager step itself matches
 the oracle. This is the launch sequence the benchmark times, including a split tail of
-dQ walks with its two reduce passes."""
+dQ walks with its two reduce passes, dQ from stored dS, and the dQ kernel on the library's second
+stream (forked from and joined back to the captured stream)."""
 from __future__ import annotations
 
 import numpy as np
@@ -19,9 +20,10 @@ pytestmark = pytest.mark.gpu
 
 
 class Step:
-    def __init__(self, c, t, fwd_split=0, bwd_splits=(1, 1, 0)):
+    def __init__(self, c, t, fwd_split=0, bwd_splits=(1, 1, 0), dq_launch=0):
         self.c, self.t = c, t
         self.bwd_splits = bwd_splits
+        self.dq_launch = dq_launch
         q = t["q"]
         self.fwd_split = fwd_split
         self.fws = torch.empty(max(256, binding.fwd_workspace_bytes(q, t["k"], scale=c.scale, causal=c.causal,
@@ -35,7 +37,8 @@ class Step:
         kv, qs, qt = bwd_splits
         self.ws = torch.empty(max(1 << 20, binding.bwd_workspace_bytes(q, t["k"], scale=c.scale, causal=c.causal,
                                                                        q_offset=c.q_offset, mask=t["mask"],
-                                                                       kv_split=kv, q_split=qs, q_split_tiles=qt)),
+                                                                       kv_split=kv, q_split=qs, q_split_tiles=qt,
+                                                                       dq_launch=dq_launch)),
                               dtype=torch.uint8, device="cuda")
         self.tiles = None if t["mask"] is None else binding.mask_tile_map(t["mask"], q, t["k"])
 
@@ -49,27 +52,30 @@ class Step:
         binding.bwd(t["q"], t["k"], t["v"], t["do"], self.lse, self.delta, mask=t["mask"], scale=c.scale,
                     causal=c.causal, q_offset=c.q_offset, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws,
                     kv_split=self.bwd_splits[0], q_split=self.bwd_splits[1], q_split_tiles=self.bwd_splits[2],
-                    mask_tiles=self.tiles)
+                    mask_tiles=self.tiles, dq_launch=self.dq_launch)
 
     def outputs(self):
         return [x.clone() for x in (self.o, self.lse, self.delta, self.dq, self.dk, self.dv)]
 
 
-@pytest.mark.parametrize("key,shrink,fwd_split,bwd_splits", [
-    ("dit_sa", dict(Hq=4, Hkv=2, Sq=300, Sk=300), 0, (1, 1, 0)),
-    ("dit_sa", dict(Hq=4, Hkv=2, Sq=300, Sk=300), 0, (2, 2, 1)),  # the split tail the bench runs
-    ("dit_ca", dict(B=2, Hq=2, Hkv=2, Sq=300, Sk=160), 0, (1, 1, 0)),
-    ("lm_causal", dict(Hq=4, Hkv=1, Sq=333, Sk=333), 0, (1, 1, 0)),
-    ("chunk", None, 4, (1, 1, 0))])
-def test_graph_replays_match_eager(key, shrink, fwd_split, bwd_splits):
+@pytest.mark.parametrize("key,shrink,fwd_split,bwd_splits,dq_launch", [
+    ("dit_sa", dict(Hq=4, Hkv=2, Sq=300, Sk=300), 0, (1, 1, 0), 0),
+    ("dit_sa", dict(Hq=4, Hkv=2, Sq=300, Sk=300), 0, (2, 2, 1), 0),  # the split tail the bench runs
+    ("dit_ca", dict(B=2, Hq=2, Hkv=2, Sq=300, Sk=160), 0, (1, 1, 0), 0),
+    ("lm_causal", dict(Hq=4, Hkv=1, Sq=333, Sk=333), 0, (1, 1, 0), 0),
+    ("chunk", None, 4, (1, 1, 0), 0),
+    ("lm_causal", dict(Hq=4, Hkv=1, Sq=333, Sk=333), 0, (2, 1, 0), 3),  # dQ from stored dS
+    ("dit_ca", dict(B=2, Hq=2, Hkv=2, Sq=300, Sk=160), 0, (2, 1, 0), 4),  # dQ kernel on the second stream
+    ("dit_sa", dict(Hq=4, Hkv=2, Sq=300, Sk=300), 0, (2, 2, 1), 4)])
+def test_graph_replays_match_eager(key, shrink, fwd_split, bwd_splits, dq_launch):
     if key == "chunk":  # a query chunk late in a causal window: the split-key forward and its merge
         c = make_case("graph_chunk", B=1, Hq=4, Hkv=2, Sq=200, Sk=1800, D=128, dtype="bf16", seed=71, causal=True,
                       q_offset=1600)
     else:
         c = configs.make(key, **shrink)
     say(f"{key}: graph capture of the whole step, B={c.B} Hq={c.Hq} Sq={c.Sq} Sk={c.Sk} fwd_split={fwd_split} "
-        f"bwd_splits={bwd_splits}")
-    step = Step(c, upload(c), fwd_split, bwd_splits)
+        f"bwd_splits={bwd_splits} dq_launch={dq_launch}")
+    step = Step(c, upload(c), fwd_split, bwd_splits, dq_launch)
     step()
     torch.cuda.synchronize()
     eager = step.outputs()

@@ -219,13 +219,14 @@ def test_forward_split_hint_ignored_for_fp32():
     assert torch.equal(o, o1) and torch.equal(lse, lse1)
 
 
-@pytest.mark.parametrize("dq_launch", [1, 2, 3])
+@pytest.mark.parametrize("dq_launch", [1, 2, 3, 4])
 @pytest.mark.parametrize("kv_split,q_split", [(1, 1), (3, 1), (1, 2), (2, 5)])
 @pytest.mark.parametrize("name", ["dit_sa_ragged", "lm_causal_gqa4", "random_bias_bcast", "d64_bf16"])
 def test_backward_decompositions(name, kv_split, q_split, dq_launch):
     """Every split of the bf16 backward's work (direct stores, or fp32 partial slices summed by a reduce
-    pass), with the dQ workgroups in the dK/dV launch (1), in a launch of their own (2), or forming dQ
-    from the dS the dK/dV walk stored (3), gives the oracle's gradients."""
+    pass), with the dQ workgroups in the dK/dV launch (1), in a launch of their own (2), forming dQ
+    from the dS the dK/dV walk stored (3), or in their own launch on a second stream beside the dK/dV
+    launch (4), gives the oracle's gradients."""
     c = CASES[name]()
     t = upload(c)
     say(f"case {name}: kv_split {kv_split} q_split {q_split} dq_launch {dq_launch}")
