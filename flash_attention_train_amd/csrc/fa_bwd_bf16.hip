@@ -91,6 +91,22 @@ __device__ __forceinline__ bool any_bias_block(const AttnShape& a, int b, int rb
   return __syncthreads_or(any) != 0;
 }
 
+// Are all mask blocks of rows [r0, r0 + nr) x keys [c0, c0 + nc) (in 64-blocks) open (every
+// entry 0)? Units over open blocks only run the body compiled without a mask, which has no
+// block-class and visibility-word handling. Called by the whole workgroup.
+__device__ __forceinline__ bool all_open_blocks(const AttnShape& a, int b, int rb0, int nrb, int cb0, int ncb) {
+  if (!a.tiles || a.alibi) return false;
+  const int nrt = (a.Sq + kMaskTile - 1) / kMaskTile, nct = (a.Sk + kMaskTile - 1) / kMaskTile;
+  nrb = min(nrb, nrt - rb0);
+  ncb = min(ncb, nct - cb0);
+  int other = 0;
+  for (int i = threadIdx.x; i < nrb * ncb; i += NT) {
+    const int rt = rb0 + i / ncb, ct = cb0 + i % ncb;
+    other |= tile_class(a, b, rt, ct) != kTileOpen;
+  }
+  return __syncthreads_or(other) == 0;
+}
+
 // ---------------------------------------------------------------------------
 // dK / dV workgroup
 // ---------------------------------------------------------------------------
@@ -1644,9 +1660,11 @@ __global__ __launch_bounds__(NT) void bwd_bf16_kernel(const BwdArgs args, const 
   const AttnShape& a = args.a;
   if (blk < plan.n_kv_units) {
     const KvUnit u = kv_unit_of(a, plan, blk);
-    if (MASK && any_bias_block(a, u.b, 0, (a.Sq + kMaskTile - 1) / kMaskTile, u.kt * (KV_BN / kMaskTile),
-                               KV_BN / kMaskTile))
+    const int nrb = (a.Sq + kMaskTile - 1) / kMaskTile, cb0 = u.kt * (KV_BN / kMaskTile);
+    if (MASK && any_bias_block(a, u.b, 0, nrb, cb0, KV_BN / kMaskTile))
       dkdv_unit<D, CAUSAL, MASK, true, CAP, KVF, ST>(args, plan, blk, smem);
+    else if (MASK && all_open_blocks(a, u.b, 0, nrb, cb0, KV_BN / kMaskTile))
+      dkdv_unit<D, CAUSAL, false, false, CAP, KVF, ST>(args, plan, blk, smem);
     else
       dkdv_unit<D, CAUSAL, MASK, false, CAP, KVF, ST>(args, plan, blk, smem);
   } else if constexpr (!ST) {
