@@ -716,8 +716,27 @@ fa_status bwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
 // merge and each workgroup's first loads cost about as much as 12 tiles of walk
 // (measured: 16 heads x 1542 rows gains 10% at 2 splits and loses at 3; a 512-row
 // chunk over a 32768-key window runs 4x faster at 8).
+int split_walk_shares(const fa_attn_params* p);
+
+// Where the split walk would take two shares, a grid with no dense mask, ALiBi, causal diagonal
+// or window (a key or query length at most) takes instead the forward variant whose workgroup
+// splits its keys between its two wave pairs (64-row query tiles, the halves merged in LDS), with
+// no merge pass: measured on MI355X, DiT self-attention with the pad given as a key length
+// 37.4 -> 31.6 us; with a dense mask, under a band, for cross-attention and for causal chunks the
+// split walk stayed faster.
+bool fwd_key_halves(const fa_attn_params* p) {
+  if (p->dtype != FA_BF16 || p->fwd_variant || p->fwd_split || p->mask || p->alibi || p->causal ||
+      p->window_left >= 0 || p->window_right >= 0 || p->kv_format != FA_KV_DTYPE)
+    return false;
+  return split_walk_shares(p) == 2;
+}
+
 int choose_fwd_split(const fa_attn_params* p) {
-  if (p->dtype != FA_BF16) return 1;
+  if (p->dtype != FA_BF16 || fwd_key_halves(p)) return 1;
+  return split_walk_shares(p);
+}
+
+int split_walk_shares(const fa_attn_params* p) {
   const int64_t wgs = (int64_t)p->B * p->Hq * ((p->Sq + 127) / 128);
   int64_t nkt = (p->Sk + 63) / 64;
   if (p->causal) {  // the longest walk: the last query tile's
@@ -816,7 +835,7 @@ fa_status fwd_common(const fa_attn_params* p, const fa_view* q, const fa_view* k
     // variant 1 (32 query rows per wave, 64-key tiles, two waves per SIMD) measured
     // faster than variant 2 (64 rows per wave, 32-key tiles, one wave per SIMD) on
     // every workload shape tried; variant 2 stays selectable for tuning
-    const int variant = p->fwd_variant ? p->fwd_variant : 1;
+    const int variant = p->fwd_variant ? p->fwd_variant : (fwd_key_halves(p) ? 3 : 1);
     return hip_status(fa::launch_fwd_bf16(a, variant, stream), "forward");
   }
   return hip_status(fa::launch_fwd(a, 0, stream), "forward");
