@@ -403,14 +403,17 @@ struct WsLayout {
 // gain nothing, their dQ walk filling the compute units the dK/dV walk leaves idle), except
 // for callers that cannot allocate (the static scratch is too small to hold dS). Never for a
 // stored K/V window, the mask's gradient (added by the dQ walk) or the role-split dK/dV walk.
+size_t ds_bytes(const fa_attn_params* p) {
+  return (size_t)p->B * p->Hq * ((p->Sq + 63) / 64) * ((p->Sk + fa::kBwdUnit - 1) / fa::kBwdUnit) * fa::kDsBlock;
+}
+// (the automatic choice also keeps the stored dS within 2 GB of workspace: one block per
+// (head, 64-row tile, 128-key tile), causal or not)
+constexpr size_t kAutoDsBytes = size_t(2) << 30;
 bool dq_from_ds(const fa_attn_params* p, bool noalloc = false) {
   if (generic_path(p) || p->kv_format != FA_KV_DTYPE || p->dbias || p->bwd_kv_walk == 2) return false;
   if (p->bwd_dq_launch == 3) return true;
   if (p->bwd_dq_launch != 0 || noalloc) return false;
-  return (int64_t)((p->Sq + fa::kBwdUnit - 1) / fa::kBwdUnit) * p->B * p->Hq >= 512;
-}
-size_t ds_bytes(const fa_attn_params* p) {
-  return (size_t)p->B * p->Hq * ((p->Sq + 63) / 64) * ((p->Sk + fa::kBwdUnit - 1) / fa::kBwdUnit) * fa::kDsBlock;
+  return (int64_t)((p->Sq + fa::kBwdUnit - 1) / fa::kBwdUnit) * p->B * p->Hq >= 512 && ds_bytes(p) <= kAutoDsBytes;
 }
 
 // Workspace of the backward: the fp32 partial slices of the chosen split (bf16), or the

@@ -131,7 +131,8 @@ typedef struct fa_attn_params {
     int32_t window_right;    /* >= 0: keys at most this far after it; -1: no bound */
     /* Work decomposition hint of the bf16 backward, like the split hints above (same
      * results up to fp32 summation order): 0 = automatic (3 when the dQ grid has at least
-     * 512 128-row tiles, except in fa_train_bwd_noalloc; otherwise 1 or 2), 1 = the dQ
+     * 512 128-row tiles and the stored dS fits 2 GB, except in fa_train_bwd_noalloc; otherwise
+     * 1 or 2), 1 = the dQ
      * workgroups share the dK/dV workgroups' launch, 2 = they run as a second kernel after
      * it, two per compute unit (chosen automatically for grids of at least 512 dQ
      * workgroups when dS is not stored), 3 = dQ from

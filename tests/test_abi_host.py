@@ -172,6 +172,13 @@ def test_backward_rejects():
     assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(big)) == 2 * 4 * 5 * 3 * 16384
     assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(params(q_split=1, kv_split=1, bwd_dq_launch=3,
                                                                     bwd_kv_walk=2))) == 0
+    # the automatic choice takes stored dS from 512 128-row tiles on, while dS fits 2 GB
+    lm = params(Hq=32, Hkv=8, Sq=4096, Sk=4096, causal=1, q_split=1, kv_split=1)
+    assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(lm)) == 32 * 64 * 32 * 16384
+    long = params(Hq=32, Hkv=8, Sq=32768, Sk=32768, causal=1, q_split=1, kv_split=1)
+    assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(long)) == 0
+    long.bwd_dq_launch = 3
+    assert B.lib().fa_train_bwd_workspace_bytes(ctypes.byref(long)) == 32 * 512 * 256 * 16384
     assert bwd_call(p, ws=0) == 8
     assert bwd_call(p, ws_bytes=100) == 8
     assert bwd_call(p, ws=BASE + 12 * (1 << 24) + 16) == 5
