@@ -45,6 +45,7 @@ constexpr int KV_BM = 64;        // query rows per staged tile of the dK/dV walk
 constexpr int Q_BM = kBwdUnit;   // query rows per dQ workgroup
 constexpr int Q_BN = 64;         // keys per staged tile of the dQ walk
 static_assert(2 * KV_BM <= NT, "one thread per LSE / Delta value of a staged tile");
+static_assert(NT == LiveWords::kThreads, "one live-candidate bit word per wave");
 
 __device__ __forceinline__ f32x16 zeros16() {
   f32x16 z;
@@ -187,45 +188,6 @@ struct RowSink {
       f32x4* q = reinterpret_cast<f32x4*>(p + 4 * col);
       *q = kind == 2 ? *q + v : v;
     }
-  }
-};
-
-// The live candidates of a walk (candidate j = 0 .. n - 1), NT at a time as bit words in
-// LDS: every thread tests one candidate, so that no step of the walk waits on a class
-// load. The walk is workgroup-uniform, and every call is made by the whole workgroup at
-// the same point.
-struct LiveWords {
-  uint64_t* words;  // [kBwdWaves] in LDS
-  int base;
-  uint64_t w[kBwdWaves];  // the words of candidates base .. base + NT - 1, kept wave-uniform
-  template <class F>
-  __device__ __forceinline__ int next(int j, int n, int tid, F&& live) {
-    static_assert(NT == 64 * kBwdWaves && (NT & (NT - 1)) == 0 && kBwdWaves == 4, "one bit word per wave");
-    while (j < n) {
-      if (j >= base + NT) {
-        const int c = (j & ~(NT - 1)) + tid;
-        const uint64_t bw = __ballot(c < n && live(c));
-        __syncthreads();  // the previous words are no longer read
-        if ((tid & 63) == 0) words[tid >> 6] = bw;
-        __syncthreads();
-        base = j & ~(NT - 1);
-        // read once into scalar registers, so that a step of the walk finds its next
-        // candidate without an LDS read (whose wait would also wait for every LDS read
-        // issued before it)
-        #pragma unroll
-        for (int k = 0; k < kBwdWaves; ++k) {
-          const uint64_t x = words[k];
-          w[k] = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32) |
-                 __builtin_amdgcn_readfirstlane((uint32_t)x);
-        }
-      }
-      const int off = j - base, k = off >> 6;
-      const uint64_t wk = k == 0 ? w[0] : k == 1 ? w[1] : k == 2 ? w[2] : w[3];
-      const uint64_t bits = wk >> (off & 63);
-      if (bits) return j + (int)__builtin_ctzll(bits);
-      j = base + 64 * (k + 1);
-    }
-    return n;
   }
 };
 

@@ -181,44 +181,35 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
       if (tile_class(a, b, rt, ct) != kTileDead) return true;
     return false;
   };
-  // The live key tiles of the workgroup, 256 at a time, as bit words in LDS: found by
-  // all threads at once, so that the walk never waits on a class load per tile.
-  __shared__ uint64_t live_lds[4];
-  int live_base = -256;
-  auto refill = [&](int base) {  // called by the whole workgroup at the same point
-    const int t = base + tid;
-    const uint64_t w = __ballot(t < kt_end && live(t));
-    __syncthreads();  // the previous words are no longer read
-    if (lane == 0) live_lds[wave] = w;
-    __syncthreads();
-    live_base = base;
-  };
+  // The live key tiles of the workgroup, 256 at a time, as bit words: found by all threads
+  // at once and kept in scalar registers, so that a step of the walk waits on neither a
+  // class load nor an LDS read.
+  __shared__ uint64_t live_lds[LiveWords::kWaves];
+  LiveWords lw{live_lds, -LiveWords::kThreads, {0, 0, 0, 0}};
   auto next_live = [&](int kt) {
     if (!MASK || !a.tiles) return kt < kt_end ? kt : kt_end;
-    while (kt < kt_end) {
-      if (kt >= live_base + 256) refill(kt & ~255);
-      const int off = kt - live_base;
-      const uint64_t bits = live_lds[off >> 6] >> (off & 63);
-      if (bits) return kt + (int)__builtin_ctzll(bits);
-      kt = live_base + 64 * ((off >> 6) + 1);
-    }
-    return kt_end;
+    return lw.next(kt, kt_end, tid, live);
   };
 
-  // Per-tile mask state of this wave, fetched one tile ahead (its loads then complete
-  // under the end-of-iteration wait instead of stalling the tile): the block class and
-  // this lane's row visibility words.
-  auto mask_state = [&](int kt, ClassAhead& cls, uint64_t (&w)[QB]) {
-    cls = ClassAhead{0u, kSelBias};
+  // Per-tile mask state of this wave. The classes of its row block along the keys come as
+  // a run, one per lane and 64 key blocks per load (a longer walk reloads when it gets
+  // there), so a tile's class is one readlane; the row visibility words are loaded only
+  // for a 0 / -inf block, one tile ahead (they complete under the end-of-iteration wait).
+  const int nct = (a.Sk + kMaskTile - 1) / kMaskTile;
+  ClassRun run{kTileDead, -64};
+  auto load_run = [&](int ct) {
+    run.load(a, ct & ~63, rt_w < nrt ? nct : 0, [&](int pos) { return tile_index(a, b, rt_w, pos); });
+  };
+  auto mask_state = [&](int kt, int& cls, uint64_t (&w)[QB]) {
+    cls = kTileBias;
     #pragma unroll
     for (int qb = 0; qb < QB; ++qb) w[qb] = ~0ull;
     if (MASK && a.tiles) {
       const int ct = (kt * BN) / kMaskTile;
-      cls.sel = kSelDead;
-      if (rt_w < nrt) {
-        const int i = tile_index(a, b, rt_w, ct);
-        cls = class_ahead(a, i);
-        const int64_t base = (int64_t)i * kMaskTile - rt_w * kMaskTile;
+      if (ct >= run.base + 64) load_run(ct);
+      cls = run.at(ct);
+      if (cls == kTileBits) {
+        const int64_t base = (int64_t)tile_index(a, b, rt_w, ct) * kMaskTile - rt_w * kMaskTile;
         #pragma unroll
         for (int qb = 0; qb < QB; ++qb) w[qb] = a.rowbits[base + qw + 32 * qb + r32];
       }
@@ -226,12 +217,14 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
   };
 
   // The walk goes in steps of KS live tiles (tk[0] < tk[1] ...); this wave's tile is tk[kh].
+  // (the first run of classes lands under the wait of the first search for live tiles)
+  if (MASK && a.tiles) load_run((kt_begin * BN) / kMaskTile);
   int tk[KS];
   tk[0] = next_live(kt_begin);
   #pragma unroll
   for (int j = 1; j < KS; ++j) tk[j] = tk[j - 1] < kt_end ? next_live(tk[j - 1] + 1) : kt_end;
   int kt = tk[kh];
-  ClassAhead cls_cur{0u, kSelBias};
+  int cls_cur = kTileBias;
   uint64_t wb_cur[QB];
   #pragma unroll
   for (int qb = 0; qb < QB; ++qb) wb_cur[qb] = ~0ull;
@@ -259,7 +252,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     for (int j = 1; j < KS; ++j) tn[j] = tn[j - 1] < kt_end ? next_live(tn[j - 1] + 1) : kt_end;
     const int ktn = tn[kh];
     const bool more = ktn < kt_end;
-    ClassAhead cls_next{0u, kSelBias};
+    int cls_next = kTileBias;
     uint64_t wb_next[QB];
     #pragma unroll
     for (int qb = 0; qb < QB; ++qb) wb_next[qb] = ~0ull;
@@ -272,7 +265,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(const Fw
     }
     const bf16* kb_lds = k_lds[kh][buf];
     const bf16* vb_lds = v_lds[kh][buf];
-    const int cls = kt < kt_end ? class_of(cls_cur) : kTileDead;  // a key half may sit out the last step
+    const int cls = kt < kt_end ? cls_cur : kTileDead;  // a key half may sit out the last step
     if (cls != kTileDead) {
     const bool bias = MASK && (cls == kTileBias || a.alibi);  // add mask values and / or ALiBi
     const bool bits = MASK && cls == kTileBits;  // 0 / -inf block: use its visibility bits

@@ -99,25 +99,11 @@ __device__ __forceinline__ int tile_class(const AttnShape& a, int b, int rt, int
   return (int)((*w >> (8 * (i & 3))) & 0xffu);
 }
 
-// A block class fetched ahead of its use by a vector load: every lane loads one byte of
-// the 64-block window holding block i (inside the class array's 256-byte padding), and
-// class_of() takes lane i % 64's byte, wave-uniform, after the walk's wait for its tile
-// loads. (A scalar load shares its counter with the LDS reads and completes out of
-// order, so every LDS wait until it landed would have to wait for it as well.)
-constexpr int kSelDead = -1, kSelBias = -2;
-struct ClassAhead {
-  uint32_t win;
-  int sel;  // i % 64, or kSelDead / kSelBias
-};
-__device__ __forceinline__ ClassAhead class_ahead(const AttnShape& a, int i) {
-  const auto* t = reinterpret_cast<const __attribute__((address_space(1))) uint8_t*>(reinterpret_cast<uintptr_t>(a.tiles));
-  return ClassAhead{t[(i & ~63) + (int)(threadIdx.x & 63)], i & 63};
-}
 // The classes of 64 consecutive mask blocks along a walk (the row blocks of one key
-// column for a dK/dV wave, the key blocks of one row for a dQ wave), one per lane, fetched
-// by one vector load per 64 blocks. A step reads its block's class with one readlane and
-// loads its visibility word only when the block is 0 / -inf, instead of issuing both loads
-// (and their 64-bit address arithmetic) for every step.
+// column for a dK/dV wave, the key blocks of one row block for a forward or dQ wave), one
+// per lane, fetched by one vector load per 64 blocks. A step reads its block's class with
+// one readlane and loads its visibility word only when the block is 0 / -inf, instead of
+// issuing both loads (and their 64-bit address arithmetic) for every step.
 struct ClassRun {
   int cls;   // class of block base + lane
   int base;  // walk position of lane 0's block (a multiple of 64), or -64 before the first load
@@ -134,11 +120,45 @@ struct ClassRun {
   __device__ __forceinline__ int at(int pos) const { return __builtin_amdgcn_readlane(cls, pos - base); }
 };
 
-__device__ __forceinline__ int class_of(const ClassAhead& c) {
-  if (c.sel == kSelBias) return kTileBias;
-  if (c.sel == kSelDead) return kTileDead;
-  return __builtin_amdgcn_readlane((int)c.win, c.sel);
-}
+
+// The live candidates of a walk (candidate j = 0 .. n - 1), 256 at a time as bit words
+// in LDS: every thread tests one candidate, so that no step of the walk waits on a class
+// load. The walk is workgroup-uniform, and every call is made by the whole workgroup at
+// the same point.
+struct LiveWords {
+  static constexpr int kThreads = 256, kWaves = 4;  // the workgroup: four waves
+  uint64_t* words;  // [kWaves] in LDS
+  int base;
+  uint64_t w[kWaves];  // the words of candidates base .. base + kThreads - 1, kept wave-uniform
+  template <class F>
+  __device__ __forceinline__ int next(int j, int n, int tid, F&& live) {
+    while (j < n) {
+      if (j >= base + kThreads) {
+        const int c = (j & ~(kThreads - 1)) + tid;
+        const uint64_t bw = __ballot(c < n && live(c));
+        __syncthreads();  // the previous words are no longer read
+        if ((tid & 63) == 0) words[tid >> 6] = bw;
+        __syncthreads();
+        base = j & ~(kThreads - 1);
+        // read once into scalar registers, so that a step of the walk finds its next
+        // candidate without an LDS read (whose wait would also wait for every LDS read
+        // issued before it)
+        #pragma unroll
+        for (int k = 0; k < kWaves; ++k) {
+          const uint64_t x = words[k];
+          w[k] = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32) |
+                 __builtin_amdgcn_readfirstlane((uint32_t)x);
+        }
+      }
+      const int off = j - base, k = off >> 6;
+      const uint64_t wk = k == 0 ? w[0] : k == 1 ? w[1] : k == 2 ? w[2] : w[3];
+      const uint64_t bits = wk >> (off & 63);
+      if (bits) return j + (int)__builtin_ctzll(bits);
+      j = base + 64 * (k + 1);
+    }
+    return n;
+  }
+};
 
 // bf16 backward decomposition: waves per workgroup (one wave per SIMD: 1024 / kBwdWaves
 // workgroups fill the GPU), keys per dK/dV workgroup and query rows per dQ workgroup
