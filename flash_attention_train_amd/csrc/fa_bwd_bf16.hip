@@ -200,7 +200,10 @@ struct RowSink {
 // dP - Delta; otherwise inside the woven slices.
 // ST: the walk also stores each pair's dS (bf16, as the dK product takes it) into the pair's
 // block of plan.ds, for a dQ pass that multiplies it by K instead of recomputing S and dP.
-template <int D, bool CAUSAL, bool MASK, bool BIAS, bool CAP = false, int KVF = 0, bool ST = false>
+// NV: every pair is whole for the unit's keys (no causal diagonal or window, every key below
+// the key length, no mask block other than open), so no score is masked per element: rows
+// past the query length or the sequence end get P = 0 from their -inf statistic alone.
+template <int D, bool CAUSAL, bool MASK, bool BIAS, bool CAP = false, int KVF = 0, bool ST = false, bool NV = false>
 __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& plan, int unit, char* smem) {
   constexpr int DS = D / 16, DB = D / 32;
   static_assert(8 % DS == 0 && 8 % (2 * DB) == 0, "each woven slice holds whole product pairs");
@@ -300,6 +303,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
   };
 
   float lpre = 0.f;
+  bool lrow = true;  // the staged statistic's row is below the query length
   // each of the first 2 KV_BM threads owns one augmented row in both buffers: zeroed once here
   // by the thread that later writes its three terms (so no barrier orders the two)
   if (tid < 2 * KV_BM) {
@@ -329,14 +333,17 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
       // the tile's work)
       lpre = tid < KV_BM ? args.lse[b * args.lse_sb + h * args.lse_sh + row]
                          : args.delta[b * args.delta_sb + h * args.delta_sh + row];
+      lrow = q0 + (tid % KV_BM) < qlen;
     }
   };
+  // (a row past the query length or the sequence end gets -LSE / scale = -inf, as one term:
+  // its scores are then -inf and P = 0 with or without the per-element masking)
   auto store_stats = [&](int buf) {
     if (tid < 2 * KV_BM) {
-      const float c = tid < KV_BM ? -lpre * args.inv_scale : -lpre;
+      const float c = tid < KV_BM ? (lrow ? -lpre * args.inv_scale : neg_inf()) : -lpre;
       const bf16 hi = (bf16)c;
-      const bf16 mid = (bf16)(c - (float)hi);
-      const bf16 lo = (bf16)(c - (float)hi - (float)mid);
+      const bf16 mid = lrow || tid >= KV_BM ? (bf16)(c - (float)hi) : (bf16)0.f;
+      const bf16 lo = lrow || tid >= KV_BM ? (bf16)(c - (float)hi - (float)mid) : (bf16)0.f;
       *reinterpret_cast<bf16x4*>(aug_lds + (((tid / KV_BM) * 3 + buf) * KV_BM + tid % KV_BM) * 16) =
           bf16x4{hi, mid, lo, (bf16)0.f};
     }
@@ -457,7 +464,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     // visibility bits (none for a dead block, whose products then contribute exact
     // zeros: skipping them per wave costs more in registers than it saves).
     const bool dead = MASK && cls == kTileDead;
-    const bool masked = edge || bits || dead;
+    const bool masked = !NV && (edge || bits || dead);
     uint64_t vis = dead ? 0ull : ~0ull;
     if (masked && !dead) {
       int64_t lo, hi;
@@ -576,7 +583,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
       #pragma unroll
       for (int r = 2 * i; r < 2 * i + 2; ++r) {
         // (the products already hold S - LSE / scale and dP - Delta)
-        const float sv = ninf_unless_bit(sacc[r], st.w, 8 * (r >> 2) + (r & 3));
+        const float sv = NV ? sacc[r] : ninf_unless_bit(sacc[r], st.w, 8 * (r >> 2) + (r & 3));
         const float pv = fast_exp2(sv * cs);
         sacc[r] = pv;
         dpacc[r] = pv * dpacc[r];
@@ -1623,12 +1630,20 @@ __global__ __launch_bounds__(NT) void bwd_bf16_kernel(const BwdArgs args, const 
   if (blk < plan.n_kv_units) {
     const KvUnit u = kv_unit_of(a, plan, blk);
     const int nrb = (a.Sq + kMaskTile - 1) / kMaskTile, cb0 = u.kt * (KV_BN / kMaskTile);
-    if (MASK && any_bias_block(a, u.b, 0, nrb, cb0, KV_BN / kMaskTile))
+    // whole pairs by the structure: no causal diagonal or window, every key below the length
+    const bool whole = !CAUSAL && !CAP && a.wl < 0 && a.wr < 0 && (u.kt + 1) * KV_BN <= klen_of(a, u.b);
+    if (MASK && any_bias_block(a, u.b, 0, nrb, cb0, KV_BN / kMaskTile)) {
       dkdv_unit<D, CAUSAL, MASK, true, CAP, KVF, ST>(args, plan, blk, smem);
-    else if (MASK && all_open_blocks(a, u.b, 0, nrb, cb0, KV_BN / kMaskTile))
-      dkdv_unit<D, CAUSAL, false, false, CAP, KVF, ST>(args, plan, blk, smem);
-    else
+    } else if (MASK && all_open_blocks(a, u.b, 0, nrb, cb0, KV_BN / kMaskTile)) {
+      if (whole)
+        dkdv_unit<D, CAUSAL, false, false, CAP, KVF, ST, !CAUSAL && !CAP>(args, plan, blk, smem);
+      else
+        dkdv_unit<D, CAUSAL, false, false, CAP, KVF, ST>(args, plan, blk, smem);
+    } else if (!MASK && whole) {
+      dkdv_unit<D, CAUSAL, false, false, CAP, KVF, ST, !CAUSAL && !CAP>(args, plan, blk, smem);
+    } else {
       dkdv_unit<D, CAUSAL, MASK, false, CAP, KVF, ST>(args, plan, blk, smem);
+    }
   } else if constexpr (!ST) {
     const int unit = blk - plan.n_kv_units;
     const QUnit u = q_unit_of(a, plan, unit);
