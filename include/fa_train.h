@@ -342,10 +342,10 @@ fa_status fa_train_bwd_sinks(const fa_attn_params* p, const fa_view* lse, const 
 /* q8_0 K/V window (llama.cpp pull request 57 trains a q8_0-quantised cache in place): the
  * rows of a window stored as ggml's q8_0 blocks -- 32 consecutive values along D share
  * one fp16 scale d, each value is the int8 q, the stored value is d * q -- written out as
- * bf16 (one rounding, to nearest even; the fp32 product is exact) into `out`, the bf16
- * K or V view the bf16 entry points read. The exact walk calls it once per chunk for the
- * window rows the chunk adds, so every row is converted once per walk and the gradient
- * flows to the stored values (dK/dV accumulate in fp32 as for a bf16 window).
+ * bf16 (one rounding, to nearest even; the fp32 product is exact) into `out`, a bf16 K or V
+ * view. The bf16 entry points read such a window in place (kv_format = FA_KV_Q8_0, the same
+ * conversion per tile on its way into LDS); this standalone conversion is for callers that
+ * want a bf16 copy, and gives the values the in-place walk computes with.
  *   qs : int8 [B, H, S, D] view (element = byte strides), rows 16-byte aligned
  *   d  : fp16 [B, H, S, D / 32] view (element strides), 2-byte aligned, stride_s >= D / 32
  *   out: bf16 [B, H, S, D] view, rows 16-byte aligned; must not overlap qs or d
@@ -357,8 +357,9 @@ fa_status fa_train_dequant_q8_0(int32_t B, int32_t H, int32_t S, int32_t D, cons
  * each tile of the cache to F32): the rows of a window stored as IEEE fp16 written out in the
  * compute type of the entry points that read them. out_dtype FA_F32 is exact (every fp16
  * value, subnormals included, is an fp32 value); FA_BF16 rounds to nearest even (bf16 keeps
- * 8 of fp16's 11 significand bits and spans its whole range). The exact walk calls it once
- * per chunk for the window rows the chunk adds, as for q8_0; dK/dV accumulate in fp32.
+ * 8 of fp16's 11 significand bits and spans its whole range). The bf16 entry points read an
+ * f16 window in place (kv_format = FA_KV_F16); this conversion serves callers that want a copy,
+ * such as the fp32 entry points, which read fp32 K / V.
  *   src: fp16 [B, H, S, D] view, rows 16-byte aligned
  *   out: [B, H, S, D] view of out_dtype, rows 16-byte aligned; must not overlap src
  * D is 64 or 128. Errors: FA_ERR_SHAPE, FA_ERR_UNSUPPORTED (D), FA_ERR_DTYPE, the view
