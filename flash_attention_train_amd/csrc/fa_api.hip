@@ -922,7 +922,7 @@ void check_bwd(Checker& c, const fa_attn_params* p, const int32_t* klen_h, const
       const int v = std::min(BM, p->Sq - q0);
       if (v < 1 || q0 + v - 1 >= p->Sq) return c.fail("dK/dV unit %d stages past Sq", unit);
       if (wl.need_ds) {  // the pair's stored dS block lies inside the workspace's dS region
-        const int64_t blk = (((int64_t)u.b * p->Hq + h) * plan.ds_nrt + q0 / BM) * plan.ds_nku + u.kt;
+        const int64_t blk = (((int64_t)u.b * p->Hq + h) * plan.ds_nku + u.kt) * plan.ds_nrt + q0 / BM;
         if (q0 / BM >= plan.ds_nrt || u.kt >= plan.ds_nku || (size_t)(blk + 1) * fa::kDsBlock > ds_bytes(p))
           return c.fail("dK/dV unit %d stores dS block %lld past its region", unit, (long long)blk);
       }
@@ -970,7 +970,7 @@ void check_bwd(Checker& c, const fa_attn_params* p, const int32_t* klen_h, const
         for (int w = 0; w < QM / 64; ++w) {
           const int rt = q0 / 64 + w;
           if (rt >= plan.ds_nrt) continue;
-          const int64_t end = ((((int64_t)u.b * p->Hq + u.h) * plan.ds_nrt + rt) * plan.ds_nku + t / 2) * fa::kDsBlock +
+          const int64_t end = ((((int64_t)u.b * p->Hq + u.h) * plan.ds_nku + t / 2) * plan.ds_nrt + rt) * fa::kDsBlock +
                               (t % 2 + 1) * (fa::kDsBlock / 2);
           if (t / 2 >= plan.ds_nku || (size_t)end > ds_bytes(p))
             return c.fail("dQ unit %d reads dS past its region (tile %d)", unit, t);

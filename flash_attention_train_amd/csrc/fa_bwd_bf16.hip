@@ -449,7 +449,7 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     pair_of(cur, h, q0);
     char* dsw = nullptr;  // (ST) the wave's 4 KB of this pair's dS block
     if constexpr (ST)
-      dsw = plan.ds + ((((int64_t)b * a.Hq + h) * plan.ds_nrt + q0 / KV_BM) * plan.ds_nku + kt) * kDsBlock +
+      dsw = plan.ds + ((((int64_t)b * a.Hq + h) * plan.ds_nku + kt) * plan.ds_nrt + q0 / KV_BM) * kDsBlock +
             wave * (kDsBlock / kBwdWaves);
     const int cls = cls_cur;
     const bool bias = MASK && (cls == kTileBias || a.alibi);  // add mask values and / or ALiBi
@@ -1455,7 +1455,7 @@ __device__ __forceinline__ void dqds_unit(const BwdArgs& args, const BwdPlan& pl
   const int qw = q0 + KV_BM * wave;  // the wave's 64 rows: dS row tile rt_w
   const int rt_w = qw / KV_BM;
   const bf16* K = static_cast<const bf16*>(args.k) + b * args.sk.b + hk * args.sk.h;
-  const char* dsw = plan.ds + (((int64_t)b * a.Hq + h) * plan.ds_nrt + rt_w) * plan.ds_nku * kDsBlock;
+  const char* dsw = plan.ds + (((int64_t)b * a.Hq + h) * plan.ds_nku * plan.ds_nrt + rt_w) * kDsBlock;
   const uint32_t ds_bytes = rt_w < plan.ds_nrt ? (uint32_t)SB : 0u;  // (no row tile: zeros, never used)
 
   // (accumulators in arch VGPRs: the products sit under a wave-uniform branch, across which
@@ -1485,7 +1485,7 @@ __device__ __forceinline__ void dqds_unit(const BwdArgs& args, const BwdPlan& pl
     char* base = smem + slot * STAGE;
     const int key0 = kt * Q_BN;
     TL::template stage_rows<Q_BN, NT>(TL::lds_addr(base), K + (int64_t)key0 * args.sk.s, args.sk.s, a.Sk - key0);
-    const u32x4 rsrc = raw_rsrc(dsw + (int64_t)(kt >> 1) * kDsBlock + (kt & 1) * SB, ds_bytes);
+    const u32x4 rsrc = raw_rsrc(dsw + (int64_t)(kt >> 1) * plan.ds_nrt * kDsBlock + (kt & 1) * SB, ds_bytes);
     const uint32_t dst = TL::lds_addr(base + KT + wave * SB);
     #pragma unroll
     for (int i = 0; i < SLOADS; ++i) TL::dma16(rsrc, (uint32_t)(1024 * i + 16 * lane), 0u, dst + 1024u * i);

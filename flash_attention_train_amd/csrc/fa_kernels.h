@@ -264,7 +264,9 @@ struct BwdPlan {
   Strides sdq;
   // dQ from stored dS (or null: the dQ walk recomputes S and dP): the dK/dV walk stores
   // every pair's dS, block (b, h, 64-row tile rt, key tile kt) of kDsBlock bytes at
-  // ((b Hq + h) ds_nrt + rt) ds_nku + kt, and the dQ workgroups multiply it by K
+  // ((b Hq + h) ds_nku + kt) ds_nrt + rt (a key tile's row tiles adjacent: the walk that
+  // writes them and the four waves of a dQ workgroup that read them both stay within one
+  // key tile's run), and the dQ workgroups multiply it by K
   char* ds;
   int ds_nrt, ds_nku;
   // (host side) the stream of the separate dQ kernel, or null for the launch stream
