@@ -23,6 +23,10 @@ padded query rows):
   ``L_b`` encoder keys, ``L_b`` uniform on ``[lo, hi]``; on top of that a few query
   rows per sample are masked completely, which exercises the convention that a
   fully masked row yields O = 0 and LSE = 0.
+
+Two test-only families: ``random`` (finite biases with ``-inf`` holes and a few fully
+masked rows and columns) and ``blocks`` (64 x 64 blocks drawn whole as hidden, open,
+0 / ``-inf`` or finite biases, so long walks cross every block class).
 """
 from __future__ import annotations
 
@@ -159,6 +163,28 @@ def random_bias_mask(rng: np.random.Generator, Bm: int, Sq: int, Sk: int, p_mask
     return bias
 
 
+def block_mask(rng: np.random.Generator, Bm: int, Sq: int, Sk: int, block: int = 64,
+               p: tuple = (0.3, 0.3, 0.2, 0.2)) -> np.ndarray:
+    """A mask made of ``block`` x ``block`` blocks, each drawn as all -inf, all 0, a 0 / -inf
+    pattern (half the entries hidden) or finite N(0, 1) biases with probabilities ``p``, so
+    that every block class appears along long rows and columns."""
+    m = np.zeros((Bm, Sq, Sk), dtype=np.float32)
+    nrb, ncb = -(-Sq // block), -(-Sk // block)
+    kinds = rng.choice(4, size=(Bm, nrb, ncb), p=np.asarray(p, dtype=np.float64))
+    for b in range(Bm):
+        for i in range(nrb):
+            for j in range(ncb):
+                r0, c0 = i * block, j * block
+                blk = m[b, r0:r0 + block, c0:c0 + block]
+                if kinds[b, i, j] == 0:
+                    blk[...] = -np.inf
+                elif kinds[b, i, j] == 2:
+                    blk[rng.random(blk.shape) < 0.5] = -np.inf
+                elif kinds[b, i, j] == 3:
+                    blk[...] = _normal(rng, blk.shape)
+    return m
+
+
 def sink_logits(seed: int, Hq: int, std: float = 1.0) -> np.ndarray:
     """Seeded per-head attention-sink logits, float32 [Hq], N(0, std^2): drawn from their
     own generator stream (seed + 7919), so that adding sinks to a case changes none of its
@@ -194,7 +220,7 @@ def quantize_q8_0(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
 def make_case(name: str, *, B: int, Hq: int, Hkv: int, Sq: int, Sk: int, D: int, dtype: str,
               seed: int, causal: bool = False, q_offset: Optional[int] = None, do_std: float = 1.0,
               mask: str = "none", mask_args: Optional[dict] = None, scale: Optional[float] = None) -> Case:
-    """Draw one seeded case. ``mask`` is one of none | sa_pad | ca_keypad | random."""
+    """Draw one seeded case. ``mask`` is one of none | sa_pad | ca_keypad | random | blocks."""
     rng = np.random.Generator(np.random.PCG64(seed))
     q = _store(_normal(rng, (B, Hq, Sq, D)), dtype)
     k = _store(_normal(rng, (B, Hkv, Sk, D)), dtype)
@@ -215,6 +241,8 @@ def make_case(name: str, *, B: int, Hq: int, Hkv: int, Sq: int, Sk: int, D: int,
         m = random_bias_mask(rng, mask_args.get("Bm", B), Sq, Sk, mask_args.get("p_masked", 0.2),
                              mask_args.get("bias_std", 1.0), mask_args.get("full_rows", 1),
                              mask_args.get("full_cols", 1))
+    elif mask == "blocks":
+        m = block_mask(rng, mask_args.get("Bm", B), Sq, Sk)
     elif mask != "none":
         raise ValueError(f"unknown mask kind {mask!r}")
     if q_offset is None:
