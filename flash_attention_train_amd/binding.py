@@ -269,7 +269,8 @@ def mask_tile_map(mask: torch.Tensor, q: torch.Tensor, k: torch.Tensor, *, strea
         tiles = out
     else:
         tiles = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
-    _check("fa_train_mask_tiles", lib().fa_train_mask_tiles(ctypes.byref(p), tiles.data_ptr(), _stream_handle(stream)))
+    _check("fa_train_mask_tiles",
+           lib().fa_train_mask_tiles(ctypes.byref(p), tiles.data_ptr(), _stream_handle(stream)))
     return tiles
 
 
@@ -304,7 +305,8 @@ def fwd(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, out=None
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     _expect("out", out, dtype=q.dtype, shape=q.shape)
     _check_rowstats(q, lse=lse)
-    _resident(q.device, q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, out=out, lse=lse, workspace=workspace, mask=mask, mask_tiles=mask_tiles,
+    _resident(q.device, q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, out=out, lse=lse, workspace=workspace,
+              mask=mask, mask_tiles=mask_tiles,
               key_len=key_len, q_len=q_len, sinks=sinks, alibi=alibi)
     need = int(lib().fa_train_fwd_workspace_bytes(ctypes.byref(p)))
     if need == ctypes.c_size_t(-1).value:
@@ -333,7 +335,8 @@ def fwd_unsplit(q, k, v, *, mask=None, scale=None, causal=False, q_offset=None, 
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     _expect("out", out, dtype=q.dtype, shape=q.shape)
     _check_rowstats(q, lse=lse)
-    _resident(q.device, q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, out=out, lse=lse, mask=mask, mask_tiles=mask_tiles, key_len=key_len,
+    _resident(q.device, q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, out=out, lse=lse, mask=mask,
+              mask_tiles=mask_tiles, key_len=key_len,
               q_len=q_len, sinks=sinks, alibi=alibi)
     _check("fa_train_fwd", lib().fa_train_fwd(ctypes.byref(p), view4(q), view4(k), view4(v), view4(out), view3(lse),
                                               _stream_handle(stream)))
@@ -353,7 +356,8 @@ def bwd_preprocess(o, dout, *, delta=None, stream=None):
     _resident(o.device, o=o, dout=dout, delta=delta)
     p = FaAttnParams(B, Hq, Hq, Sq, Sq, D, _dtype_code(o), 0, 0, 1.0, None, 0, 0, None, 0, 0, 0)
     _check("fa_train_bwd_preprocess",
-           lib().fa_train_bwd_preprocess(ctypes.byref(p), view4(o), view4(dout), view3(delta), _stream_handle(stream)))
+           lib().fa_train_bwd_preprocess(ctypes.byref(p), view4(o), view4(dout), view3(delta),
+                                         _stream_handle(stream)))
     return delta
 
 
@@ -453,7 +457,8 @@ def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_off
     _check_rowstats(q, lse=lse, delta=delta)
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, window=window,
-                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles, softcap=softcap, kv_walk=kv_walk, k_scale=k_scale, v_scale=v_scale,
+                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles, softcap=softcap, kv_walk=kv_walk,
+                    k_scale=k_scale, v_scale=v_scale,
                     dbias=dbias)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     # (dK / dV in the compute dtype also for a K/V window stored as fp16 or q8_0)
@@ -462,7 +467,8 @@ def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_off
     _expect("dq", dq, dtype=q.dtype, shape=q.shape)
     _expect("dk", dk, dtype=q.dtype, shape=k.shape)
     _expect("dv", dv, dtype=q.dtype, shape=k.shape)
-    _resident(q.device, q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, dout=dout, lse=lse, delta=delta, dq=dq, dk=dk, dv=dv, mask=mask,
+    _resident(q.device, q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, dout=dout, lse=lse, delta=delta, dq=dq,
+              dk=dk, dv=dv, mask=mask,
               mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, alibi=alibi, dbias=dbias)
     ws, nbytes = _workspace(p, q.device, workspace)
     _check("fa_train_bwd", lib().fa_train_bwd(ctypes.byref(p), view4(q), view4(k), view4(v), view4(dout), view3(lse),
@@ -473,7 +479,8 @@ def bwd(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_off
 
 def bwd_noalloc(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=False, q_offset=None, dq=None,
                 dk=None, dv=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None, q_len=None,
-                window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0, k_scale=None, v_scale=None,
+                window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0, k_scale=None,
+                v_scale=None,
                 dbias=None):
     """Backward through fa_train_bwd_noalloc: the results of bwd(), with the workspace taken from
     the library's static device scratch instead of an allocation (dQ, dK and dV are still the
@@ -483,7 +490,8 @@ def bwd_noalloc(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=Fals
     _check_rowstats(q, lse=lse, delta=delta)
     p = make_params(q, k, scale=scale, causal=causal, q_offset=q_offset, mask=mask, kv_split=kv_split,
                     q_split=q_split, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, window=window,
-                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles, softcap=softcap, kv_walk=kv_walk, k_scale=k_scale, v_scale=v_scale,
+                    dq_launch=dq_launch, alibi=alibi, q_split_tiles=q_split_tiles, softcap=softcap, kv_walk=kv_walk,
+                    k_scale=k_scale, v_scale=v_scale,
                     dbias=dbias)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     # (dK / dV in the compute dtype also for a K/V window stored as fp16 or q8_0)
@@ -492,7 +500,8 @@ def bwd_noalloc(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=Fals
     _expect("dq", dq, dtype=q.dtype, shape=q.shape)
     _expect("dk", dk, dtype=q.dtype, shape=k.shape)
     _expect("dv", dv, dtype=q.dtype, shape=k.shape)
-    _resident(q.device, q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, dout=dout, lse=lse, delta=delta, dq=dq, dk=dk, dv=dv, mask=mask,
+    _resident(q.device, q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, dout=dout, lse=lse, delta=delta, dq=dq,
+              dk=dk, dv=dv, mask=mask,
               mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, alibi=alibi, dbias=dbias)
     _check("fa_train_bwd_noalloc",
            lib().fa_train_bwd_noalloc(ctypes.byref(p), view4(q), view4(k), view4(v), view4(dout), view3(lse),
@@ -543,7 +552,8 @@ def tune_bwd_splits(q, k, v, dout, lse, delta, *, mask=None, scale=None, causal=
 
 def bwd_chunked(q, k, v, dout, lse, delta, dk_acc, dv_acc, *, mask=None, scale=None, causal=True, q_offset=None,
                 dq=None, workspace=None, stream=None, kv_split=0, q_split=0, mask_tiles=None, key_len=None,
-                q_len=None, window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0, k_scale=None, v_scale=None,
+                q_len=None, window=(-1, -1), dq_launch=0, alibi=None, q_split_tiles=0, softcap=0.0, kv_walk=0,
+                k_scale=None, v_scale=None,
                 dbias=None):
     """Chunked backward: returns dQ for the chunk; ADDS dK/dV into the fp32 window
     accumulators ``dk_acc`` / ``dv_acc`` ([B, Hkv, >= Sk, D]) and, when given, the mask's
@@ -563,7 +573,8 @@ def bwd_chunked(q, k, v, dout, lse, delta, dk_acc, dv_acc, *, mask=None, scale=N
             raise ValueError(f"{name} has shape {tuple(acc.shape)}, expected [{B}, {Hkv}, >= {Sk}, {D}]")
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     _expect("dq", dq, dtype=q.dtype, shape=q.shape)
-    _resident(q.device, q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, dout=dout, lse=lse, delta=delta, dq=dq, dk_acc=dk_acc, dv_acc=dv_acc,
+    _resident(q.device, q=q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, dout=dout, lse=lse, delta=delta, dq=dq,
+              dk_acc=dk_acc, dv_acc=dv_acc,
               mask=mask, mask_tiles=mask_tiles, key_len=key_len, q_len=q_len, alibi=alibi, dbias=dbias)
     ws, nbytes = _workspace(p, q.device, workspace)
     _check("fa_train_bwd_chunked",
