@@ -36,6 +36,8 @@ CASES = {
                               mask_args={"pad_frac": 0.1}), {"softcap": 15.0}, {}),
     "splits": (dict(B=1, Hq=4, Hkv=2, Sq=600, Sk=600, D=128, dtype="bf16", seed=509, causal=True), {},
                dict(kv_split=2, q_split=3, q_split_tiles=2)),
+    # whole dK/dV units over a single query row: the other 63 rows of its dS block are zeros
+    "one_row": (dict(B=1, Hq=2, Hkv=1, Sq=1, Sk=300, D=128, dtype="bf16", seed=511), {}, {}),
 }
 
 

@@ -46,6 +46,12 @@ CASES = {
                                                  seed=66),
     "causal_q_before_keys": lambda: make_case("causal_negative_offset", B=1, Hq=2, Hkv=2, Sq=80, Sk=40, D=64,
                                               dtype="f32", seed=67, causal=True),  # q_offset = -40
+    # whole dK/dV units (no per-element masking) whose only row tile holds one row, or ends one
+    # row into a second tile: the rows past the end must contribute nothing
+    "one_query_many_keys": lambda: make_case("one_many", B=1, Hq=2, Hkv=1, Sq=1, Sk=300, D=128, dtype="bf16",
+                                             seed=68),
+    "row_tail_of_one": lambda: make_case("row_tail_one", B=2, Hq=2, Hkv=2, Sq=65, Sk=256, D=64, dtype="bf16",
+                                         seed=69),
 }
 
 
