@@ -431,6 +431,8 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
   if (cur.p < npairs) read_a0(0);
   // (ST) this lane's two 16-byte chunks of a 32-row block in the wave's 4 KB of a dS block:
   // chunk (block qb, half hh, key k, lane half g) at ((2 qb + hh) 32 + (k ^ 4 hh)) 2 + g.
+  // Non-temporal stores: the blocks are read once, by the dQ pass, and not keeping them in
+  // the caches leaves the next forward's operands there (whole LM step 2.5% faster).
   // Stored after the pair's wait, except under a softcap with additive scores, whose walk has
   // no registers to keep dS until then (stored as soon as formed)
   constexpr bool ST_LATE = !(CAP && BIAS);
@@ -639,8 +641,8 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
         pack8(ds0[hh], dp0, 8 * hh);
       }
       if constexpr (ST && !ST_LATE) {
-        *reinterpret_cast<bf16x8*>(dsw + ds_off0) = ds0[0];
-        *reinterpret_cast<bf16x8*>(dsw + ds_off1) = ds0[1];
+        __builtin_nontemporal_store(ds0[0], reinterpret_cast<bf16x8*>(dsw + ds_off0));
+        __builtin_nontemporal_store(ds0[1], reinterpret_cast<bf16x8*>(dsw + ds_off1));
       }
     }
     {
@@ -668,8 +670,8 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
         pack8(ds1[hh], dp1, 8 * hh);
       }
       if constexpr (ST && !ST_LATE) {
-        *reinterpret_cast<bf16x8*>(dsw + 2048 + ds_off0) = ds1[0];
-        *reinterpret_cast<bf16x8*>(dsw + 2048 + ds_off1) = ds1[1];
+        __builtin_nontemporal_store(ds1[0], reinterpret_cast<bf16x8*>(dsw + 2048 + ds_off0));
+        __builtin_nontemporal_store(ds1[1], reinterpret_cast<bf16x8*>(dsw + 2048 + ds_off1));
       }
     }
     // the next pair's tiles are complete once every wave has waited for its own loads;
@@ -682,10 +684,10 @@ __device__ __forceinline__ void dkdv_unit(const BwdArgs& args, const BwdPlan& pl
     if constexpr (ST && ST_LATE) {
       // (after this pair's wait: the stores complete under the next pair, whose end-of-pair
       // wait would otherwise also wait for them)
-      *reinterpret_cast<bf16x8*>(dsw + ds_off0) = ds0[0];
-      *reinterpret_cast<bf16x8*>(dsw + ds_off1) = ds0[1];
-      *reinterpret_cast<bf16x8*>(dsw + 2048 + ds_off0) = ds1[0];
-      *reinterpret_cast<bf16x8*>(dsw + 2048 + ds_off1) = ds1[1];
+      __builtin_nontemporal_store(ds0[0], reinterpret_cast<bf16x8*>(dsw + ds_off0));
+      __builtin_nontemporal_store(ds0[1], reinterpret_cast<bf16x8*>(dsw + ds_off1));
+      __builtin_nontemporal_store(ds1[0], reinterpret_cast<bf16x8*>(dsw + 2048 + ds_off0));
+      __builtin_nontemporal_store(ds1[1], reinterpret_cast<bf16x8*>(dsw + 2048 + ds_off1));
     }
     buf = nb;
     cur = nxt;
