@@ -175,6 +175,14 @@ struct Tile {
                  "s"(m0), "s"(__builtin_amdgcn_readfirstlane(soff))
                  : "memory", "m0");
   }
+  // the same with the non-temporal hint, for data read once (it then displaces less of what
+  // the caches hold for later work)
+  __device__ static __forceinline__ void dma16nt(const u32x4& rsrc, uint32_t voff, uint32_t soff, uint32_t dst) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(dst);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen nt lds" ::"v"(voff), "s"(rsrc),
+                 "s"(m0), "s"(__builtin_amdgcn_readfirstlane(soff))
+                 : "memory", "m0");
+  }
 };
 
 // ---------------------------------------------------------------------------
