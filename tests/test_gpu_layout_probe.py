@@ -7,7 +7,8 @@ The kernels assume, for the 32x32 matrix-core family:
   B (K x 32): lane l holds column l % 32, register slot j carries the same k-slot
   C (32 x 32): lane l, register r holds (row 8 (r // 4) + 4 (l // 32) + r % 4, col l % 32)
 The test loads random small-integer matrices under that assumption and requires
-the exact product back. Probe results are also written to gpurun_out/ for reading.
+the exact product back. Probe results are also written as JSON to the folder named by
+FA_PROBE_OUT, when that is set, for reading.
 """
 from __future__ import annotations
 
@@ -22,7 +23,7 @@ from parity_util import say
 
 pytestmark = pytest.mark.gpu
 
-OUT = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
+OUT = os.environ.get("FA_PROBE_OUT")  # optional folder for the probes' JSON records
 
 
 def _binding():
@@ -58,9 +59,10 @@ def test_mfma_32x32_layouts(kind, kper):
     for l in range(64):
         for r in range(16):
             want[:, l, r] = C[:, _c_row_32(l, r), l % 32]
-    os.makedirs(OUT, exist_ok=True)
-    with open(os.path.join(OUT, f"probe_mfma_kind{kind}.json"), "w") as f:
-        json.dump({"c_wave0": c[0].tolist(), "want_wave0": want[0].tolist()}, f)
+    if OUT:
+        os.makedirs(OUT, exist_ok=True)
+        with open(os.path.join(OUT, f"probe_mfma_kind{kind}.json"), "w") as f:
+            json.dump({"c_wave0": c[0].tolist(), "want_wave0": want[0].tolist()}, f)
     say(f"mfma kind {kind}: max |c - want| = {np.abs(c - want).max()}")
     assert np.array_equal(c, want)
 
@@ -101,10 +103,11 @@ def test_ds_read_tr16_record():
     }
     addr = torch.tensor([patterns[k] for k in patterns], dtype=torch.int32).cuda()
     out = _binding().probe_ds_read_tr16(addr).cpu().numpy()
-    os.makedirs(OUT, exist_ok=True)
-    rec = {k: {"addr": patterns[k], "out": out[i].tolist()} for i, k in enumerate(patterns)}
-    with open(os.path.join(OUT, "probe_ds_read_tr16.json"), "w") as f:
-        json.dump(rec, f)
+    if OUT:
+        os.makedirs(OUT, exist_ok=True)
+        rec = {k: {"addr": patterns[k], "out": out[i].tolist()} for i, k in enumerate(patterns)}
+        with open(os.path.join(OUT, "probe_ds_read_tr16.json"), "w") as f:
+            json.dump(rec, f)
     for i, k in enumerate(patterns):
         say(f"tr16 {k}: lanes 0..7 -> {out[i][:8].tolist()}")
     assert (out >= 0).all() and (out < 4096).all()
